@@ -1,0 +1,165 @@
+/*
+ * KDA reference oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain, slow, sequential fp64 evaluation of Kimi Delta Attention (KDA), the
+ * channel-wise gated delta rule.  Only the test suite, the package smoke check
+ * and the CPU-baseline leg of the benchmark may load this code; the GPU library
+ * never links or calls it, and it shares no source with it.
+ *
+ * Sources (cited by page title and section):
+ *  [A] "Kimi K3 -- the architecture and infrastructure, explained",
+ *      section "How the delta rule actually works": the delta-rule update
+ *      S <- S - beta (S k - v) k^T with the recall v_hat = S k (S there is
+ *      d_v x d_k; here it is stored transposed, d_k x d_v).
+ *  [B] same page, section "Kimi Delta Attention: the load-bearing choice":
+ *      the gate is channel-wise, each state dimension decays on its own.
+ *  [C] "Inside Kimi K3: How Moonshot AI Built the Largest Open-Source Model",
+ *      section "Technical Details": per head 128 forgetting dials, beta is the
+ *      writing strength, alpha the forgetting factor, "erase then write".
+ *  [D] marketersindex.com Kimi K3 article, section "Architectural Innovations:
+ *      Kimi Delta Attention (KDA)": recall / compare / correct, and channels
+ *      (rows of the memory state) decaying at different speeds.
+ *
+ * What it computes, for every sequence n and head h independently:
+ *     S <- initial state (or zeros)                       d_k x d_v
+ *     for each token t of the sequence, in order:
+ *       a_i = exp(log_alpha[t,h,i])        forgetting factor per channel [B][C]
+ *       S   = Diag(a) S                    channel-wise decay, rows = channels [D]
+ *       p   = S^T k_t                      recall [A][D]
+ *       u   = beta_t (v_t - p)             compare, scaled by the write strength [A][C]
+ *       S   = S + k_t u^T                  correct [A][D]
+ *       o_t = S^T q_t                      read-out from the updated state
+ *     final state <- S
+ * i.e. S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T.
+ * Readings where the pages are silent: decay comes before the erase/write;
+ * beta is one scalar per (token, head) and alpha the per-channel gate; no
+ * query scaling and no normalisation happen inside the operation; the
+ * read-out uses the state after the token's update.
+ *
+ * Addressing.  Inputs are "token rows": a row holds H heads, each head holding
+ * d_k (q, k, log_alpha), d_v (v, o) or 1 (beta) values, contiguous.  Token t
+ * of sequence n lives in row  row0[n] + t * row_step.  This one scheme covers
+ * a dense [B,T,H,*] batch (row0[n] = n*T, step 1), a packed variable-length
+ * batch (row0[n] = cu_seqlens[n], step 1) and a chain of single-token decode
+ * steps stored [steps, N, H, *] (row0[n] = n, step N).
+ *
+ * Inputs arrive as fp32 (bf16 inputs are widened exactly by the caller) and
+ * are widened to fp64 here; all arithmetic is fp64 in the order written.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int kda_oracle_abi_version(void) { return 1; }
+
+/* Returns the number of threads the parallel loop over (sequence, head) units
+ * may use, for reporting. */
+int kda_oracle_max_threads(int n_threads)
+{
+#ifdef _OPENMP
+    if (n_threads > 0) return n_threads;
+    return omp_get_max_threads();
+#else
+    (void)n_threads;
+    return 1;
+#endif
+}
+
+/* One (sequence, head) unit, token by token.  S is a dk*dv scratch matrix. */
+static void run_unit(int64_t n, int64_t h, const int64_t *row0, const int64_t *len,
+                     int64_t row_step, int64_t H, int64_t dk, int64_t dv,
+                     const float *q, const float *k, const float *v,
+                     const float *beta, const float *log_alpha,
+                     const double *s0, double *o, double *s_final,
+                     double *S, double *a, double *p, double *u)
+{
+    const int64_t unit = n * H + h;
+    if (s0) memcpy(S, s0 + unit * dk * dv, (size_t)(dk * dv) * sizeof(double));
+    else memset(S, 0, (size_t)(dk * dv) * sizeof(double));
+
+    for (int64_t t = 0; t < len[n]; ++t) {
+        const int64_t row = row0[n] + t * row_step;
+        const float *qt = q + (row * H + h) * dk;
+        const float *kt = k + (row * H + h) * dk;
+        const float *lat = log_alpha + (row * H + h) * dk;
+        const float *vt = v + (row * H + h) * dv;
+        const double bt = (double)beta[row * H + h];
+        double *ot = o + (row * H + h) * dv;
+
+        /* forgetting factors, one per channel (row of S) */
+        for (int64_t i = 0; i < dk; ++i) a[i] = exp((double)lat[i]);
+
+        /* decay: S <- Diag(a) S */
+        for (int64_t i = 0; i < dk; ++i)
+            for (int64_t j = 0; j < dv; ++j) S[i * dv + j] *= a[i];
+
+        /* recall: p = S^T k */
+        for (int64_t j = 0; j < dv; ++j) p[j] = 0.0;
+        for (int64_t i = 0; i < dk; ++i)
+            for (int64_t j = 0; j < dv; ++j) p[j] += S[i * dv + j] * (double)kt[i];
+
+        /* compare: u = beta (v - p) */
+        for (int64_t j = 0; j < dv; ++j) u[j] = bt * ((double)vt[j] - p[j]);
+
+        /* correct: S <- S + k u^T */
+        for (int64_t i = 0; i < dk; ++i)
+            for (int64_t j = 0; j < dv; ++j) S[i * dv + j] += (double)kt[i] * u[j];
+
+        /* read-out: o = S^T q */
+        for (int64_t j = 0; j < dv; ++j) ot[j] = 0.0;
+        for (int64_t i = 0; i < dk; ++i)
+            for (int64_t j = 0; j < dv; ++j) ot[j] += S[i * dv + j] * (double)qt[i];
+    }
+    memcpy(s_final + unit * dk * dv, S, (size_t)(dk * dv) * sizeof(double));
+}
+
+/*
+ * Run the recurrence for n_seq sequences x H heads.
+ *   row0[n_seq], len[n_seq] : token-row addressing (see above)
+ *   q, k, log_alpha : rows x H x dk  (fp32)
+ *   v               : rows x H x dv  (fp32)
+ *   beta            : rows x H       (fp32)
+ *   s0              : [n_seq, H, dk, dv] fp64, or NULL for zeros
+ *   o               : rows x H x dv  fp64, written for every token visited
+ *   s_final         : [n_seq, H, dk, dv] fp64
+ *   n_threads       : <= 0 means the OpenMP default
+ * Returns 0 on success, -1 on bad sizes, -2 on allocation failure.
+ */
+int kda_oracle_run(int64_t n_seq, const int64_t *row0, const int64_t *len, int64_t row_step,
+                   int64_t H, int64_t dk, int64_t dv,
+                   const float *q, const float *k, const float *v,
+                   const float *beta, const float *log_alpha,
+                   const double *s0, double *o, double *s_final, int n_threads)
+{
+    if (n_seq < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+    for (int64_t n = 0; n < n_seq; ++n)
+        if (len[n] < 0 || row0[n] < 0) return -1;
+
+    const int64_t units = n_seq * H;
+    int failed = 0;
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#pragma omp parallel reduction(| : failed)
+#endif
+    {
+        double *S = (double *)malloc((size_t)(dk * dv) * sizeof(double));
+        double *a = (double *)malloc((size_t)dk * sizeof(double));
+        double *p = (double *)malloc((size_t)dv * sizeof(double));
+        double *u = (double *)malloc((size_t)dv * sizeof(double));
+        const int ok = S && a && p && u;
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int64_t w = 0; w < units; ++w) {
+            if (!ok) { failed = 1; continue; }
+            run_unit(w / H, w % H, row0, len, row_step, H, dk, dv, q, k, v, beta,
+                     log_alpha, s0, o, s_final, S, a, p, u);
+        }
+        free(S); free(a); free(p); free(u);
+    }
+    return failed ? -2 : 0;
+}
