@@ -1,0 +1,259 @@
+#!/usr/bin/env python3
+"""KDA benchmark on one MI355X.
+
+Headline workload (one "step" = one pass of the hot path over one batch):
+batched decode, B = 64 sequences x H = 32 heads, d_k = d_v = 128, bf16
+q/k/v/beta, fp32 log_alpha and fp32 state; one step advances every sequence
+by one token (kda_decode_step over all 2048 head states).  The default run
+times 1024 consecutive steps, the length of the workload.  ``value`` is decode
+tokens/s (64 tokens per step) with all inputs already resident in HBM.
+
+Also reported (same JSON line): the chunked-prefill workload (B = 1, H = 32,
+T = 32768, bf16 inputs, gated channel mix) timed with HIP events, its
+tokens/s and roofline; the roofline of the decode kernel (algorithmic bytes
+per launch over the measured average launch duration, against 8 TB/s); and
+the CPU oracle timed on a bounded sample of the decode workload on the host
+cores.
+
+    python bench.py [--gpus 1] [--steps 1024] [--warmup 32] [--no-prefill]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/sec & decode tokens/sec; % MFMA peak / % HBM BW peak"
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+D = 128
+
+# Algorithmic bytes per head of one decode step: the fp32 state read once and
+# written once (2 x 64 KiB), q and k (bf16, 256 B each), v (bf16, 256 B),
+# beta (bf16, 2 B), log_alpha (fp32, 512 B), o (fp32, 512 B).
+DECODE_BYTES_PER_HEAD = 2 * D * D * 4 + 2 * D * 2 + D * 2 + 2 + D * 4 + D * 4
+# Prefill, per head-token: q, k, v (bf16), beta (bf16), log_alpha (fp32), o (fp32);
+# plus the final state once per head.
+PREFILL_BYTES_PER_HEAD_TOKEN = 3 * D * 2 + 2 + D * 4 + D * 4
+# Chunked-algorithm flops per head-token at chunk 64 (d_k = d_v = 128).
+PREFILL_FLOPS_PER_HEAD_TOKEN = 9_024_853 / 64
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1024, help="timed decode steps")
+    ap.add_argument("--warmup", type=int, default=32, help="untimed decode steps first")
+    ap.add_argument("--batch", type=int, default=64)
+    ap.add_argument("--heads", type=int, default=32)
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
+    ap.add_argument("--prefill-T", type=int, default=32768)
+    ap.add_argument("--prefill-reps", type=int, default=5)
+    ap.add_argument("--cpu-steps", type=int, default=1024,
+                    help="decode steps of the workload the CPU oracle runs (all heads)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="first run one plain device-to-device copy of this many MiB "
+                         "(a reference kernel for the HBM byte counters)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads and sequences would shard with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_113_amd as kda
+    import kda_inputs as ki
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    kda.load_library()
+    B, H, K, W = args.batch, args.heads, args.steps, args.warmup
+
+    # ---------------- decode: inputs resident in HBM -----------------------
+    n_gen = max(K, W, 1)
+    log(f"generating {n_gen} decode steps for B={B} H={H}")
+    t0 = time.time()
+    inp = ki.decode_steps(1, steps=n_gen, N=B, H=H)
+    log(f"generated in {time.time() - t0:.1f}s; uploading")
+
+    def up(x, bf16):
+        if bf16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    q, k, v, beta = (up(x, True) for x in (inp.q, inp.k, inp.v, inp.beta))
+    la = up(inp.log_alpha, False)
+    state0 = up(inp.initial_state, False)
+    state = state0.clone()
+    o = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    if args.copy_mib > 0:
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"reference copy: {args.copy_mib} MiB read + {args.copy_mib} MiB written")
+        del src, dst
+
+    def step(s, st):
+        kda.kda_decode_step(q[s], k[s], v[s], beta[s], la[s], st, out=o)
+
+    log(f"warmup {W} steps")
+    for s in range(W):
+        step(s % n_gen, state)
+    torch.cuda.synchronize()
+    state.copy_(state0)
+    torch.cuda.synchronize()
+
+    log(f"timing {K} steps")
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for s in range(K):
+        step(s % n_gen, state)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = ev0.elapsed_time(ev1)
+    ms_per_step = total_ms / K
+    tokens_per_s = B * K / (total_ms / 1e3)
+    bytes_per_launch = DECODE_BYTES_PER_HEAD * B * H
+    achieved = bytes_per_launch / (ms_per_step / 1e3) / 1e9
+    if not bool(torch.isfinite(state).all()):
+        raise RuntimeError("decode produced non-finite states")
+    log(f"decode: {ms_per_step * 1e3:.2f} us/step, {tokens_per_s / 1e6:.3f} M tokens/s, "
+        f"{achieved:.0f} GB/s")
+
+    # per-launch kernel duration with an event pair around each launch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(min(K, 64))]
+    state.copy_(state0)
+    torch.cuda.synchronize()
+    for s, (a, b) in enumerate(evs):
+        a.record(stream)
+        step(s % n_gen, state)
+        b.record(stream)
+    torch.cuda.synchronize()
+    launch_ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+
+    result = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded: bf16 L2-normalised q/k, N(0,1) v, sigmoid beta, "
+                "-softplus log_alpha, N(0,0.02^2) fp32 states)",
+        "config": {
+            "workload": f"batched KDA decode: B={B} sequences x H={H} heads, d_k=d_v=128, "
+                        "bf16 q/k/v/beta, fp32 log_alpha/state/o, consecutive single-token steps",
+            "global_batch": B, "heads": H, "d_k": D, "d_v": D, "seq_len": 1,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "kernel": "decode_step_kernel<bf16_t>",
+            "algorithmic_bytes_per_launch": bytes_per_launch,
+            "avg_launch_ms_timed_region": ms_per_step,
+            "median_launch_ms_event_pairs": launch_ms,
+        },
+    }
+
+    # ---------------- prefill (secondary) ---------------------------------
+    if not args.no_prefill:
+        T = args.prefill_T
+        log(f"generating prefill inputs B=1 H={H} T={T}")
+        pin = ki.workload_chunked(T=T, H=H)
+        pq, pk, pv, pb = (up(x, True) for x in (pin.q, pin.k, pin.v, pin.beta))
+        pla = up(pin.log_alpha, False)
+        po = torch.empty((1, T, H, D), dtype=torch.float32, device=dev)
+        ps = torch.empty((1, H, D, D), dtype=torch.float32, device=dev)
+        kda.kda_prefill(pq, pk, pv, pb, pla, None, out=po, final_state=ps)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(args.prefill_reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            kda.kda_prefill(pq, pk, pv, pb, pla, None, out=po, final_state=ps)
+            b.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        pms = float(np.median(times))
+        pbytes = PREFILL_BYTES_PER_HEAD_TOKEN * T * H + H * D * D * 4
+        pflops = PREFILL_FLOPS_PER_HEAD_TOKEN * T * H
+        pgbs = pbytes / (pms / 1e3) / 1e9
+        ptf = pflops / (pms / 1e3) / 1e12
+        log(f"prefill: {pms:.3f} ms, {T / pms * 1e3 / 1e6:.2f} M tokens/s, {pgbs:.0f} GB/s")
+        result["prefill"] = {
+            "workload": f"chunked KDA prefill: B=1, H={H}, T={T}, d_k=d_v=128, bf16 q/k/v/beta, "
+                        "fp32 log_alpha/state/o, gated channel mix, zero initial state",
+            "ms": pms,
+            "tokens_per_s": T / (pms / 1e3),
+            "head_tokens_per_s": T * H / (pms / 1e3),
+            "roofline": {"bound": "hbm", "achieved": pgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": pgbs / HBM_PEAK_GBS, "traffic": None,
+                         "algorithmic_bytes_per_launch": pbytes},
+            "mfma": {"algorithmic_tflops": ptf, "peak_tflops_bf16": BF16_MFMA_PEAK_TFLOPS,
+                     "frac": ptf / BF16_MFMA_PEAK_TFLOPS,
+                     "algorithmic_flops_per_launch": pflops},
+        }
+        del pq, pk, pv, pb, pla, po, ps
+
+    # ---------------- CPU oracle baseline ---------------------------------
+    if not args.no_cpu:
+        import oracle
+
+        S = min(args.cpu_steps, n_gen)
+        qf, kf, vf, bf, laf = (x[:S] for x in inp.widened())
+        threads = len(os.sched_getaffinity(0))
+        log(f"cpu oracle: {S} decode steps x {B * H} heads on {threads} threads")
+        t0 = time.time()
+        oracle.decode_chain(qf, kf, vf, bf, laf, inp.initial_state, n_threads=threads)
+        dt = time.time() - t0
+        result["cpu_baseline"] = {
+            "value": B * S / dt,
+            "unit": "tokens/s",
+            "cores": oracle.max_threads(threads),
+            "kind": "oracle",
+            "sample": f"the first {S} of the workload's decode steps, all {B}x{H} heads, "
+                      f"fp64 token-by-token recurrence, {dt:.1f} s wall",
+        }
+        log(f"cpu oracle: {B * S / dt:.1f} tokens/s in {dt:.1f}s")
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

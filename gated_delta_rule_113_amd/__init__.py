@@ -1,0 +1,24 @@
+"""Kimi Delta Attention (KDA) on AMD Instinct MI355X (gfx950).
+
+The computation lives in ``libkda.so`` (hand-written HIP kernels behind the C
+ABI of ``include/kda.h``); this package is its thin Python binding:
+
+    kda_prefill(q, k, v, beta, log_alpha, initial_state=None) -> (o, final_state)
+    kda_varlen_prefill(q, k, v, beta, log_alpha, cu_seqlens, initial_state=None)
+        -> (o, final_state)
+    kda_decode_step(q, k, v, beta, log_alpha, state) -> o      (state in place)
+
+PyTorch is used only for device memory and the current stream.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTS,
+    KDA_BF16,
+    KDA_F32,
+    KDAError,
+    kda_decode_step,
+    kda_prefill,
+    kda_varlen_prefill,
+    load_library,
+)
+
+__all__ = ["kda_prefill", "kda_varlen_prefill", "kda_decode_step", "KDAError", "load_library"]

@@ -1,0 +1,208 @@
+"""ctypes binding of libkda.so (include/kda.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, outputs are allocated with torch, and the C entry point is called
+on the current HIP stream.  Every step of the computation runs in the HIP
+kernels; if the library is missing this module raises -- there is no other
+path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(PKG, "libkda.so")
+
+KDA_F32, KDA_BF16 = 0, 1
+STATUS_NAMES = {
+    0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
+    4: "KDA_ERR_ALIGN", 5: "KDA_ERR_UNSUPPORTED", 6: "KDA_ERR_HIP",
+}
+EXPORTS = ("kda_prefill", "kda_varlen_prefill", "kda_decode_step", "kda_status_str",
+           "kda_abi_version")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class KDAError(RuntimeError):
+    """A non-OK kda_status returned by the library."""
+
+    def __init__(self, fn, code, text):
+        super().__init__(f"{fn}: {text} (status {code})")
+        self.code = code
+
+
+def load_library(path: str | None = None):
+    """Load libkda.so and declare the C signatures.  Raises if it is not built."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        target = path or LIBRARY
+        if not os.path.exists(target):
+            raise ImportError(
+                f"{target} is missing: build the KDA HIP library first "
+                "(python -m gated_delta_rule_113_amd.build)")
+        lib = ctypes.CDLL(target)
+        vp, i64, f32p = ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p
+        lib.kda_prefill.argtypes = [vp, vp, vp, vp, f32p, f32p, f32p, f32p,
+                                    i64, i64, i64, i64, i64, ctypes.c_int, vp]
+        lib.kda_prefill.restype = ctypes.c_int
+        lib.kda_varlen_prefill.argtypes = [vp, vp, vp, vp, f32p, vp, i64, i64,
+                                           f32p, f32p, f32p, i64, i64, i64, ctypes.c_int, vp]
+        lib.kda_varlen_prefill.restype = ctypes.c_int
+        lib.kda_decode_step.argtypes = [vp, vp, vp, vp, f32p, f32p, f32p,
+                                        i64, i64, i64, i64, ctypes.c_int, vp]
+        lib.kda_decode_step.restype = ctypes.c_int
+        lib.kda_status_str.argtypes = [ctypes.c_int]
+        lib.kda_status_str.restype = ctypes.c_char_p
+        lib.kda_abi_version.argtypes = []
+        lib.kda_abi_version.restype = ctypes.c_int
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def _check(lib, fn, code):
+    if code != 0:
+        raise KDAError(fn, code, lib.kda_status_str(code).decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _in_dtype(*ts):
+    torch = _torch()
+    dt = ts[0].dtype
+    for t in ts:
+        if t.dtype != dt:
+            raise TypeError("q, k, v and beta must share one dtype")
+    if dt == torch.float32:
+        return KDA_F32
+    if dt == torch.bfloat16:
+        return KDA_BF16
+    raise TypeError(f"q, k, v, beta must be float32 or bfloat16, got {dt}")
+
+
+def _require(t, name, dtype=None, shape=None, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def kda_prefill(q, k, v, beta, log_alpha, initial_state=None, *, out=None, final_state=None):
+    """Dense prefill.  q, k, log_alpha [B, T, H, 128]; v [B, T, H, 128];
+    beta [B, T, H]; initial_state [B, H, 128, 128] fp32 or None.
+
+    Returns (o [B, T, H, 128] fp32, final_state [B, H, 128, 128] fp32).
+    ``final_state`` may be passed (and may be ``initial_state``) to write in place.
+    """
+    torch = _torch()
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _require(q, "q", device=dev)
+    _require(k, "k", q.dtype, (B, T, H, dk), dev)
+    _require(v, "v", q.dtype, (B, T, H, dv), dev)
+    _require(beta, "beta", q.dtype, (B, T, H), dev)
+    _require(log_alpha, "log_alpha", torch.float32, (B, T, H, dk), dev)
+    if initial_state is not None:
+        _require(initial_state, "initial_state", torch.float32, (B, H, dk, dv), dev)
+    o = out if out is not None else torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    _require(o, "out", torch.float32, (B, T, H, dv), dev)
+    if final_state is None:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    _require(final_state, "final_state", torch.float32, (B, H, dk, dv), dev)
+    code = lib.kda_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
+                           _ptr(initial_state), _ptr(o), _ptr(final_state),
+                           B, T, H, dk, dv, _in_dtype(q, k, v, beta), _stream(dev))
+    _check(lib, "kda_prefill", code)
+    return o, final_state
+
+
+def kda_varlen_prefill(q, k, v, beta, log_alpha, cu_seqlens, initial_state=None, *,
+                       out=None, final_state=None):
+    """Packed prefill.  q, k, log_alpha [1, T_total, H, 128] (or [T_total, H, 128]);
+    cu_seqlens int32 [N + 1] on the GPU; initial_state [N, H, 128, 128] or None.
+
+    Returns (o shaped like v but fp32, final_state [N, H, 128, 128] fp32).
+    """
+    torch = _torch()
+    lib = load_library()
+    dev = q.device
+    lead = q.shape[:-3]
+    if lead not in ((), (1,)):
+        raise ValueError("packed inputs must be [T_total, H, d] or [1, T_total, H, d]")
+    Tt, H, dk = q.shape[-3:]
+    dv = v.shape[-1]
+    _require(q, "q", device=dev)
+    _require(k, "k", q.dtype, (*lead, Tt, H, dk), dev)
+    _require(v, "v", q.dtype, (*lead, Tt, H, dv), dev)
+    _require(beta, "beta", q.dtype, (*lead, Tt, H), dev)
+    _require(log_alpha, "log_alpha", torch.float32, (*lead, Tt, H, dk), dev)
+    _require(cu_seqlens, "cu_seqlens", torch.int32, None, dev)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor of N + 1 offsets")
+    N = cu_seqlens.numel() - 1
+    if initial_state is not None:
+        _require(initial_state, "initial_state", torch.float32, (N, H, dk, dv), dev)
+    o = out if out is not None else torch.empty((*lead, Tt, H, dv), dtype=torch.float32, device=dev)
+    _require(o, "out", torch.float32, (*lead, Tt, H, dv), dev)
+    if final_state is None:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    _require(final_state, "final_state", torch.float32, (N, H, dk, dv), dev)
+    code = lib.kda_varlen_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
+                                  _ptr(cu_seqlens), N, Tt, _ptr(initial_state), _ptr(o),
+                                  _ptr(final_state), H, dk, dv, _in_dtype(q, k, v, beta),
+                                  _stream(dev))
+    _check(lib, "kda_varlen_prefill", code)
+    return o, final_state
+
+
+def kda_decode_step(q, k, v, beta, log_alpha, state, *, out=None):
+    """One decode step.  q, k, log_alpha [N, H, 128]; v [N, H, 128]; beta [N, H];
+    state [N, H, 128, 128] fp32, updated in place.  Returns o [N, H, 128] fp32."""
+    torch = _torch()
+    lib = load_library()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _require(q, "q", device=dev)
+    _require(k, "k", q.dtype, (N, H, dk), dev)
+    _require(v, "v", q.dtype, (N, H, dv), dev)
+    _require(beta, "beta", q.dtype, (N, H), dev)
+    _require(log_alpha, "log_alpha", torch.float32, (N, H, dk), dev)
+    _require(state, "state", torch.float32, (N, H, dk, dv), dev)
+    o = out if out is not None else torch.empty((N, H, dv), dtype=torch.float32, device=dev)
+    _require(o, "out", torch.float32, (N, H, dv), dev)
+    code = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
+                               _ptr(state), _ptr(o), N, H, dk, dv, _in_dtype(q, k, v, beta),
+                               _stream(dev))
+    _check(lib, "kda_decode_step", code)
+    return o

@@ -1,0 +1,145 @@
+// C ABI of libkda.so (declared in include/kda.h): host-side validation, then
+// one asynchronous launch on the caller's stream.  Nothing here allocates,
+// synchronises or touches device memory; every check happens before a launch
+// so that on error nothing is enqueued.
+#include "kda.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <initializer_list>
+
+#include "kda_internal.hpp"
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 46;  // keeps every index product in int64
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+kda_status check_dtype(kda_dtype d)
+{
+    return (d == KDA_F32 || d == KDA_BF16) ? KDA_OK : KDA_ERR_DTYPE;
+}
+
+kda_status check_dims(int64_t H, int64_t d_k, int64_t d_v)
+{
+    if (H < 1 || d_k < 1 || d_v < 1) return KDA_ERR_SHAPE;
+    if (d_k != kda::kDim || d_v != kda::kDim) return KDA_ERR_UNSUPPORTED;
+    return KDA_OK;
+}
+
+// rows * H * 128 must stay far from int64 overflow and grid limits.
+kda_status check_rows(int64_t rows, int64_t H)
+{
+    if (rows < 0) return KDA_ERR_SHAPE;
+    if (rows > 0 && (rows > kMaxElems / H / kda::kDim)) return KDA_ERR_SHAPE;
+    return KDA_OK;
+}
+
+kda_status check_ptrs(std::initializer_list<const void*> required,
+                      std::initializer_list<const void*> optional)
+{
+    for (const void* p : required)
+        if (!p) return KDA_ERR_NULL;
+    for (const void* p : required)
+        if (misaligned(p)) return KDA_ERR_ALIGN;
+    for (const void* p : optional)
+        if (p && misaligned(p)) return KDA_ERR_ALIGN;
+    return KDA_OK;
+}
+
+kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_prefill(const void* q, const void* k, const void* v, const void* beta,
+                       const float* log_alpha, const float* initial_state, float* o,
+                       float* final_state, int64_t B, int64_t T, int64_t H, int64_t d_k,
+                       int64_t d_v, kda_dtype in_dtype, void* stream)
+{
+    kda_status st;
+    if ((st = check_dtype(in_dtype)) != KDA_OK) return st;
+    if ((st = check_dims(H, d_k, d_v)) != KDA_OK) return st;
+    if (B < 0 || T < 0) return KDA_ERR_SHAPE;
+    if (B > 0 && T > kMaxElems / B) return KDA_ERR_SHAPE;
+    if ((st = check_rows(B * T, H)) != KDA_OK) return st;
+    if (B > int64_t(1) << 24 || B * H > int64_t(1) << 30) return KDA_ERR_SHAPE;
+    if (B == 0) return KDA_OK;
+    if (T > 0) {
+        if ((st = check_ptrs({q, k, v, beta, log_alpha, o}, {initial_state, final_state})) != KDA_OK)
+            return st;
+    } else if ((st = check_ptrs({}, {initial_state, final_state})) != KDA_OK) {
+        return st;
+    }
+    if (T == 0 && !final_state) return KDA_OK;
+    return from_hip(kda::launch_prefill_recurrent(q, k, v, beta, log_alpha, nullptr, B, T, H,
+                                                  initial_state, o, final_state,
+                                                  in_dtype == KDA_BF16,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+kda_status kda_varlen_prefill(const void* q, const void* k, const void* v, const void* beta,
+                              const float* log_alpha, const int32_t* cu_seqlens, int64_t N,
+                              int64_t T_total, const float* initial_state, float* o,
+                              float* final_state, int64_t H, int64_t d_k, int64_t d_v,
+                              kda_dtype in_dtype, void* stream)
+{
+    kda_status st;
+    if ((st = check_dtype(in_dtype)) != KDA_OK) return st;
+    if ((st = check_dims(H, d_k, d_v)) != KDA_OK) return st;
+    if (N < 0 || T_total < 0) return KDA_ERR_SHAPE;
+    // cu_seqlens holds int32 row indices
+    if (T_total > INT32_MAX || N > int64_t(1) << 24 || N * H > int64_t(1) << 30) return KDA_ERR_SHAPE;
+    if ((st = check_rows(T_total, H)) != KDA_OK) return st;
+    if (N == 0) return KDA_OK;
+    if (!cu_seqlens) return KDA_ERR_NULL;
+    if (misaligned(cu_seqlens)) return KDA_ERR_ALIGN;
+    if (T_total > 0) {
+        if ((st = check_ptrs({q, k, v, beta, log_alpha, o}, {initial_state, final_state})) != KDA_OK)
+            return st;
+    } else if ((st = check_ptrs({}, {initial_state, final_state})) != KDA_OK) {
+        return st;
+    }
+    if (T_total == 0 && !final_state) return KDA_OK;
+    return from_hip(kda::launch_prefill_recurrent(q, k, v, beta, log_alpha, cu_seqlens, N, 0, H,
+                                                  initial_state, o, final_state,
+                                                  in_dtype == KDA_BF16,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* beta,
+                           const float* log_alpha, float* state, float* o, int64_t N, int64_t H,
+                           int64_t d_k, int64_t d_v, kda_dtype in_dtype, void* stream)
+{
+    kda_status st;
+    if ((st = check_dtype(in_dtype)) != KDA_OK) return st;
+    if ((st = check_dims(H, d_k, d_v)) != KDA_OK) return st;
+    if (N < 0) return KDA_ERR_SHAPE;
+    if (N > int64_t(1) << 24 || N * H > INT32_MAX) return KDA_ERR_SHAPE;
+    if (N == 0) return KDA_OK;
+    if ((st = check_ptrs({q, k, v, beta, log_alpha, state, o}, {})) != KDA_OK) return st;
+    return from_hip(kda::launch_decode_step(q, k, v, beta, log_alpha, state, o, N * H,
+                                            in_dtype == KDA_BF16,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+const char* kda_status_str(kda_status status)
+{
+    switch (status) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_NULL: return "KDA_ERR_NULL: a required pointer is NULL";
+        case KDA_ERR_SHAPE: return "KDA_ERR_SHAPE: a size is negative, zero where it may not be, or too large";
+        case KDA_ERR_DTYPE: return "KDA_ERR_DTYPE: unknown input dtype";
+        case KDA_ERR_ALIGN: return "KDA_ERR_ALIGN: a pointer is not 16-byte aligned";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: only d_k = d_v = 128 is supported";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP: the HIP runtime rejected a launch";
+    }
+    return "KDA_ERR_UNKNOWN: not a kda_status value";
+}
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+}  // extern "C"

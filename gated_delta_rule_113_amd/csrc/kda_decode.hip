@@ -1,0 +1,110 @@
+// Fused KDA decode step: one token per head, state streamed through HBM once.
+//
+// Per head (S is d_k x d_v = 128 x 128 fp32, rows = forgetting channels):
+//   a = exp(log_alpha)                     channel-wise forgetting
+//   S' = Diag(a) S                         (never stored)
+//   p = S'^T k,  r = S'^T q                both reductions over the rows of S'
+//   u = beta (v - p)                       the delta-rule correction
+//   S <- S' + k u^T                        erase-then-write, stored in place
+//   o = S^T q = r + (k . q) u
+// The pages define the update ("Kimi K3 -- the architecture and infrastructure,
+// explained", section "How the delta rule actually works", with the per-channel
+// gate of section "Kimi Delta Attention: the load-bearing choice") and say the
+// decode phase is bound by memory bandwidth, its cost per token constant; here
+// each state byte is read once and written once per token.
+//
+// Mapping: one workgroup of 256 threads per head.  Wave w owns columns
+// [32w, 32w+32).  Lane l owns columns 32w + 4*(l & 7) .. +3 and rows
+// (l >> 3) + 8m, m = 0..15: 16 float4 = 64 state values in registers.  Each
+// load instruction of a wave covers 8 rows x 128 contiguous bytes.  The column
+// reductions finish across the 8 row groups of the wave with lane shuffles;
+// no LDS and no barrier are needed, and the four waves are independent.
+#include "kda_device.hpp"
+#include "kda_internal.hpp"
+
+namespace kda {
+namespace {
+
+template <typename InT>
+__global__ __launch_bounds__(256) void decode_step_kernel(
+    const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
+    const InT* __restrict__ beta, const float* __restrict__ log_alpha,
+    float* __restrict__ state, float* __restrict__ o)
+{
+    const int64_t unit = blockIdx.x;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int rg = lane >> 3;
+    const int col = wave * 32 + (lane & 7) * 4;
+
+    float* S = state + unit * (kDim * kDim);
+    const int64_t vec = unit * kDim;
+
+    float4 s[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m)
+        s[m] = *reinterpret_cast<const float4*>(S + (rg + 8 * m) * kDim + col);
+
+    float a[16], kk[16], qq[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        const int i = rg + 8 * m;
+        a[m] = exp_gate(log_alpha[vec + i]);
+        kk[m] = widen(k[vec + i]);
+        qq[m] = widen(q[vec + i]);
+    }
+    const float bt = widen(beta[unit]);
+    const float4 vv = load4(v + vec + col);
+
+    float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+    float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
+    float kq = 0.f;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        s[m].x *= a[m]; s[m].y *= a[m]; s[m].z *= a[m]; s[m].w *= a[m];
+        p0 += kk[m] * s[m].x; p1 += kk[m] * s[m].y; p2 += kk[m] * s[m].z; p3 += kk[m] * s[m].w;
+        r0 += qq[m] * s[m].x; r1 += qq[m] * s[m].y; r2 += qq[m] * s[m].z; r3 += qq[m] * s[m].w;
+        kq += kk[m] * qq[m];
+    }
+    p0 = xor_sum_rows(p0); p1 = xor_sum_rows(p1); p2 = xor_sum_rows(p2); p3 = xor_sum_rows(p3);
+    r0 = xor_sum_rows(r0); r1 = xor_sum_rows(r1); r2 = xor_sum_rows(r2); r3 = xor_sum_rows(r3);
+    kq = xor_sum_rows(kq);
+
+    const float u0 = bt * (vv.x - p0), u1 = bt * (vv.y - p1);
+    const float u2 = bt * (vv.z - p2), u3 = bt * (vv.w - p3);
+    if (rg == 0) {
+        *reinterpret_cast<float4*>(o + vec + col) =
+            make_float4(r0 + kq * u0, r1 + kq * u1, r2 + kq * u2, r3 + kq * u3);
+    }
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        float4 t = s[m];
+        t.x += kk[m] * u0; t.y += kk[m] * u1; t.z += kk[m] * u2; t.w += kk[m] * u3;
+        *reinterpret_cast<float4*>(S + (rg + 8 * m) * kDim + col) = t;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode_step(const void* q, const void* k, const void* v, const void* beta,
+                              const float* log_alpha, float* state, float* o, int64_t units,
+                              bool bf16, hipStream_t stream)
+{
+    if (units <= 0) return hipSuccess;
+    const dim3 grid(static_cast<unsigned>(units)), block(256);
+    if (bf16) {
+        using T = bf16_t;
+        hipLaunchKernelGGL(decode_step_kernel<T>, grid, block, 0, stream,
+                           static_cast<const T*>(q), static_cast<const T*>(k),
+                           static_cast<const T*>(v), static_cast<const T*>(beta), log_alpha,
+                           state, o);
+    } else {
+        hipLaunchKernelGGL(decode_step_kernel<float>, grid, block, 0, stream,
+                           static_cast<const float*>(q), static_cast<const float*>(k),
+                           static_cast<const float*>(v), static_cast<const float*>(beta),
+                           log_alpha, state, o);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kda

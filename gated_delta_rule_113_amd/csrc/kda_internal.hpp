@@ -1,0 +1,25 @@
+// Host-side launchers of the KDA kernels (implemented next to each kernel).
+// Sizes have been validated by the C-ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int kDim = 128;  // d_k = d_v handled by the kernels
+
+// One fused decode step for `units` = N * H heads.
+hipError_t launch_decode_step(const void* q, const void* k, const void* v, const void* beta,
+                              const float* log_alpha, float* state, float* o, int64_t units,
+                              bool bf16, hipStream_t stream);
+
+// Token-by-token prefill with the state held in registers.  Dense when
+// cu_seqlens == nullptr (sequence n = rows n*T .. n*T+T-1), packed otherwise.
+hipError_t launch_prefill_recurrent(const void* q, const void* k, const void* v,
+                                    const void* beta, const float* log_alpha,
+                                    const int32_t* cu_seqlens, int64_t n_seq, int64_t T,
+                                    int64_t H, const float* initial_state, float* o,
+                                    float* final_state, bool bf16, hipStream_t stream);
+
+}  // namespace kda

@@ -1,0 +1,139 @@
+/*
+ * kda.h -- C ABI of libkda.so: Kimi Delta Attention (KDA) prefill and decode
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * KDA keeps, per head, a fixed-size fp32 memory S of d_k x d_v (rows are the
+ * d_k = 128 forgetting channels) and updates it once per token with the delta
+ * rule under a channel-wise forgetting gate:
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t,            alpha_t = exp(log_alpha_t)  (one per channel)
+ *
+ * Sources, by page title and section:
+ *  - "Kimi K3 -- the architecture and infrastructure, explained", section
+ *    "How the delta rule actually works": the update S <- S - beta (S k - v) k^T
+ *    (printed with S as d_v x d_k; stored here transposed, d_k x d_v).
+ *  - same page, section "Kimi Delta Attention: the load-bearing choice": the
+ *    gate is per channel; the computation is blockwise so it maps onto matrix
+ *    units; decode cost per token is constant.
+ *  - same page, section "Serving infrastructure: supernodes and the prefill
+ *    cache": a cached prefill state is restored and only the new suffix is
+ *    processed (hence the optional initial state and the returned final state).
+ *  - "Inside Kimi K3: How Moonshot AI Built the Largest Open-Source Model",
+ *    section "Technical Details": 128 forgetting dials per head, beta = writing
+ *    strength, alpha = forgetting factor, erase then write.
+ * Readings where the pages are silent: the decay is applied before the
+ * erase/write; beta is one scalar per (token, head); the read-out uses the
+ * updated state; there is no query scaling and no normalisation inside the op.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers (e.g. torch CUDA tensors), owned by
+ *    the caller.  The library allocates nothing and keeps no mutable global
+ *    state; calls are re-entrant and thread-safe.
+ *  - Layouts are dense row-major, innermost dimension last:
+ *        q, k, log_alpha : [rows, H, d_k]      v, o : [rows, H, d_v]
+ *        beta            : [rows, H]
+ *        states          : [units, H, d_k, d_v]  (d_v contiguous)
+ *    where a "row" is one token position (see each call).
+ *  - q, k, v and beta share one storage type, `in_dtype` (KDA_F32 or
+ *    KDA_BF16); log_alpha, states and o are always fp32.  Arithmetic is fp32
+ *    with fp32 state; bf16 inputs are widened exactly.
+ *  - Supported sizes: d_k = d_v = 128 (anything else -> KDA_ERR_UNSUPPORTED).
+ *  - Every pointer must be 16-byte aligned (KDA_ERR_ALIGN).
+ *  - Preconditions not checked (device data): log_alpha finite and <= 0;
+ *    cu_seqlens[0] = 0, non-decreasing, cu_seqlens[N] = T_total.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call is
+ *    asynchronous on it: arguments are validated on the host first, and on any
+ *    error nothing is enqueued.  No call synchronises.  A fault inside a
+ *    kernel surfaces at the caller's next synchronisation.
+ *  - Inputs must not overlap outputs, except where stated.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_NULL = 1,         /* a required pointer is NULL                    */
+    KDA_ERR_SHAPE = 2,        /* a size is negative, zero where it may not be, or too large */
+    KDA_ERR_DTYPE = 3,        /* in_dtype is not a kda_dtype value             */
+    KDA_ERR_ALIGN = 4,        /* a pointer is not 16-byte aligned              */
+    KDA_ERR_UNSUPPORTED = 5,  /* d_k or d_v other than 128                      */
+    KDA_ERR_HIP = 6           /* the HIP runtime rejected a launch             */
+} kda_status;
+
+typedef enum kda_dtype {
+    KDA_F32 = 0,
+    KDA_BF16 = 1
+} kda_dtype;
+
+/*
+ * Dense prefill of B sequences of T tokens each, all H heads.
+ *   q, k        : [B, T, H, d_k]  in_dtype
+ *   v           : [B, T, H, d_v]  in_dtype
+ *   beta        : [B, T, H]       in_dtype   (write strength per token and head)
+ *   log_alpha   : [B, T, H, d_k]  fp32       (log forgetting factor per channel)
+ *   initial_state : [B, H, d_k, d_v] fp32, or NULL for zeros (a restored
+ *                 prefill cache; only the given tokens are processed)
+ *   o           : [B, T, H, d_v]  fp32, written
+ *   final_state : [B, H, d_k, d_v] fp32, written, or NULL to skip; it MAY be
+ *                 the same pointer as initial_state (in-place resume)
+ * B = 0 is a no-op.  T = 0 writes final_state = initial_state (or zeros).
+ * Requires H >= 1.
+ */
+kda_status kda_prefill(const void *q, const void *k, const void *v, const void *beta,
+                       const float *log_alpha, const float *initial_state,
+                       float *o, float *final_state,
+                       int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v,
+                       kda_dtype in_dtype, void *stream);
+
+/*
+ * Packed variable-length prefill of N sequences stored back to back.
+ *   q, k, log_alpha : [T_total, H, d_k];  v, o : [T_total, H, d_v];  beta : [T_total, H]
+ *   cu_seqlens  : [N + 1] int32, DEVICE memory: sequence n owns token rows
+ *                 cu_seqlens[n] .. cu_seqlens[n+1]-1.  Read on the device, so
+ *                 the call needs no host synchronisation.
+ *   initial_state / final_state : [N, H, d_k, d_v] fp32 as in kda_prefill
+ *                 (NULL initial state = zeros for every sequence; the two may
+ *                 alias).  No state crosses a sequence boundary; an empty
+ *                 sequence returns its initial state.
+ * N = 0 is a no-op.  T_total may be 0 (then every sequence is empty).
+ */
+kda_status kda_varlen_prefill(const void *q, const void *k, const void *v, const void *beta,
+                              const float *log_alpha, const int32_t *cu_seqlens,
+                              int64_t N, int64_t T_total,
+                              const float *initial_state, float *o, float *final_state,
+                              int64_t H, int64_t d_k, int64_t d_v,
+                              kda_dtype in_dtype, void *stream);
+
+/*
+ * One decode step: one new token for each of N sequences, all H heads.
+ *   q, k, log_alpha : [N, H, d_k];  v : [N, H, d_v];  beta : [N, H]
+ *   state : [N, H, d_k, d_v] fp32, read and updated IN PLACE (S_{t-1} -> S_t)
+ *   o     : [N, H, d_v] fp32, written (o_t = S_t^T q_t)
+ * Each head's state is read once and written once.  N = 0 is a no-op.
+ */
+kda_status kda_decode_step(const void *q, const void *k, const void *v, const void *beta,
+                           const float *log_alpha, float *state, float *o,
+                           int64_t N, int64_t H, int64_t d_k, int64_t d_v,
+                           kda_dtype in_dtype, void *stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *kda_status_str(kda_status status);
+
+/* KDA_ABI_VERSION of the loaded library. */
+int kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

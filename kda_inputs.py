@@ -25,8 +25,10 @@ widening of the same bits.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 
 import numpy as np
 
@@ -42,8 +44,8 @@ N_SPECIAL = 13  # round(0.10 * 128)
 def bf16_bits(x) -> np.ndarray:
     """Round to bfloat16 (nearest, ties to even, via float32); return uint16 bits."""
     f = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
-    u = f.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = f.view(np.uint32)
+    u = (u + (np.uint32(0x7FFF) + ((u >> 16) & np.uint32(1)))) >> 16  # finite inputs only
     return u.astype(np.uint16)
 
 
@@ -51,6 +53,17 @@ def bf16_to_f32(bits) -> np.ndarray:
     """Exact widening of bfloat16 bits (uint16) to float32."""
     b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
     return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def _workers() -> int:
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _run_parallel(fn, jobs):
+    """Run fn(job) for every job on a thread pool (numpy releases the GIL)."""
+    with concurrent.futures.ThreadPoolExecutor(max_workers=_workers()) as ex:
+        for _ in ex.map(fn, jobs):
+            pass
 
 
 def _rng(*key) -> np.random.Generator:
@@ -154,14 +167,16 @@ def dense_prefill(workload: int, B: int, T: int, H: int, dk: int = 128, dv: int 
     la = np.empty((B, T, Hs, dk), np.float32)
     v = np.empty((B, T, Hs, dv), q.dtype)
     beta = np.empty((B, T, Hs), q.dtype)
-    for b in range(B):
-        for j, h in enumerate(heads):
-            hq, hk, hv, hb, hla = draw_head(workload, h, T, dk, dv, gated, key=(b,))
-            q[b, :, j] = _store(hq, dtype)
-            k[b, :, j] = _store(hk, dtype)
-            v[b, :, j] = _store(hv, dtype)
-            beta[b, :, j] = _store(hb, dtype)
-            la[b, :, j] = hla.astype(np.float32)
+    def one(job):
+        b, j, h = job
+        hq, hk, hv, hb, hla = draw_head(workload, h, T, dk, dv, gated, key=(b,))
+        q[b, :, j] = _store(hq, dtype)
+        k[b, :, j] = _store(hk, dtype)
+        v[b, :, j] = _store(hv, dtype)
+        beta[b, :, j] = _store(hb, dtype)
+        la[b, :, j] = hla
+
+    _run_parallel(one, [(b, j, h) for b in range(B) for j, h in enumerate(heads)])
     s0 = draw_state(workload, (B, H, dk, dv))[:, heads] if initial_state else None
     return KDAInputs(q, k, v, beta, la, dtype, s0)
 
@@ -190,15 +205,17 @@ def varlen_prefill(workload: int, lengths, H: int, dk: int = 128, dv: int = 128,
     v = np.empty((1, Tt, H, dv), sdt)
     beta = np.empty((1, Tt, H), sdt)
     la = np.empty((1, Tt, H, dk), np.float32)
-    for s in range(n):
+    def one(job):
+        s, h = job
         a, b = int(cu[s]), int(cu[s + 1])
-        for h in range(H):
-            hq, hk, hv, hb, hla = draw_head(workload, h, b - a, dk, dv, gated, key=(s,))
-            q[0, a:b, h] = _store(hq, dtype)
-            k[0, a:b, h] = _store(hk, dtype)
-            v[0, a:b, h] = _store(hv, dtype)
-            beta[0, a:b, h] = _store(hb, dtype)
-            la[0, a:b, h] = hla.astype(np.float32)
+        hq, hk, hv, hb, hla = draw_head(workload, h, b - a, dk, dv, gated, key=(s,))
+        q[0, a:b, h] = _store(hq, dtype)
+        k[0, a:b, h] = _store(hk, dtype)
+        v[0, a:b, h] = _store(hv, dtype)
+        beta[0, a:b, h] = _store(hb, dtype)
+        la[0, a:b, h] = hla
+
+    _run_parallel(one, [(s, h) for s in range(n) for h in range(H)])
     s0 = draw_state(workload, (n, H, dk, dv))
     if resumed == "even":
         s0[1::2] = 0.0
@@ -212,23 +229,23 @@ def varlen_prefill(workload: int, lengths, H: int, dk: int = 128, dv: int = 128,
 def decode_steps(workload: int, steps: int, N: int, H: int, dk: int = 128, dv: int = 128,
                  dtype: str = "bf16", first_step: int = 0) -> KDAInputs:
     """Inputs for a chain of single-token decode steps, [steps, N, H, *], plus
-    the N(0, 0.02^2) initial states [N, H, dk, dv].  Step s is drawn from the
-    streams keyed (workload, tensor, s, h)."""
+    the N(0, 0.02^2) initial states [N, H, dk, dv].  Step s draws all N x H
+    token vectors at once from the streams keyed (workload, tensor, s)."""
     sdt = np.float32 if dtype == "f32" else np.uint16
     q = np.empty((steps, N, H, dk), sdt)
     k = np.empty_like(q)
     v = np.empty((steps, N, H, dv), sdt)
     beta = np.empty((steps, N, H), sdt)
     la = np.empty((steps, N, H, dk), np.float32)
-    for i in range(steps):
+    def one(i):
         s = first_step + i
-        for h in range(H):
-            hq, hk, hv, hb, hla = draw_head(workload, h, N, dk, dv, False, key=(s,))
-            q[i, :, h] = _store(hq, dtype)
-            k[i, :, h] = _store(hk, dtype)
-            v[i, :, h] = _store(hv, dtype)
-            beta[i, :, h] = _store(hb, dtype)
-            la[i, :, h] = hla.astype(np.float32)
+        q[i] = _store(_unit_rows(_rng(workload, Q, s).standard_normal((N, H, dk))), dtype)
+        k[i] = _store(_unit_rows(_rng(workload, K, s).standard_normal((N, H, dk))), dtype)
+        v[i] = _store(_rng(workload, V, s).standard_normal((N, H, dv)), dtype)
+        beta[i] = _store(_sigmoid(_rng(workload, BETA, s).standard_normal((N, H))), dtype)
+        la[i] = -_softplus(_rng(workload, LOG_ALPHA, s).standard_normal((N, H, dk)))
+
+    _run_parallel(one, range(steps))
     s0 = draw_state(workload, (N, H, dk, dv))
     return KDAInputs(q, k, v, beta, la, dtype, s0)
 

@@ -1,0 +1,128 @@
+"""The C ABI on the CPU: the library loads, exports every function that
+include/kda.h declares, and rejects bad arguments before any launch.
+
+No call here reaches a kernel: every call carries an argument the host-side
+validation refuses (pointers are fake, never dereferenced)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import gated_delta_rule_113_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, HIP = range(7)
+P = 0x10000          # a 16-byte aligned fake device address
+MIS = 0x10008        # 8-byte aligned only
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda._binding.LIBRARY):
+        from gated_delta_rule_113_amd import build
+        build.build()
+    return kda.load_library()
+
+
+def _declared():
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text))
+
+
+def test_exports_match_header(lib):
+    declared = _declared()
+    assert declared == {"kda_prefill", "kda_varlen_prefill", "kda_decode_step",
+                        "kda_status_str", "kda_abi_version"}
+    out = subprocess.run(["nm", "-D", "--defined-only", kda._binding.LIBRARY],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r" T (kda_\w+)", out))
+    assert declared <= exported, declared - exported
+    for name in declared:
+        assert hasattr(lib, name)
+    assert set(kda.EXPORTS) == declared
+
+
+def test_version_and_status_strings(lib):
+    assert lib.kda_abi_version() == 1
+    for code in range(7):
+        s = lib.kda_status_str(code).decode()
+        assert s.startswith(kda._binding.STATUS_NAMES[code])
+    assert lib.kda_status_str(99).decode().startswith("KDA_ERR_UNKNOWN")
+
+
+def prefill(lib, q=P, k=P, v=P, beta=P, la=P, s0=None, o=P, s1=P, B=1, T=4, H=2,
+            dk=128, dv=128, dt=1):
+    return lib.kda_prefill(q, k, v, beta, la, s0, o, s1, B, T, H, dk, dv, dt, None)
+
+
+def varlen(lib, q=P, k=P, v=P, beta=P, la=P, cu=P, N=2, Tt=8, s0=None, o=P, s1=P, H=2,
+           dk=128, dv=128, dt=1):
+    return lib.kda_varlen_prefill(q, k, v, beta, la, cu, N, Tt, s0, o, s1, H, dk, dv, dt, None)
+
+
+def decode(lib, q=P, k=P, v=P, beta=P, la=P, st=P, o=P, N=2, H=2, dk=128, dv=128, dt=1):
+    return lib.kda_decode_step(q, k, v, beta, la, st, o, N, H, dk, dv, dt, None)
+
+
+def test_prefill_validation(lib):
+    assert prefill(lib, q=None) == NULL
+    assert prefill(lib, o=None) == NULL
+    assert prefill(lib, la=None) == NULL
+    assert prefill(lib, k=MIS) == ALIGN
+    assert prefill(lib, s0=MIS) == ALIGN
+    assert prefill(lib, s1=MIS) == ALIGN
+    assert prefill(lib, dk=64) == UNSUP
+    assert prefill(lib, dv=256) == UNSUP
+    assert prefill(lib, dk=0) == SHAPE
+    assert prefill(lib, H=0) == SHAPE
+    assert prefill(lib, B=-1) == SHAPE
+    assert prefill(lib, T=-5) == SHAPE
+    assert prefill(lib, T=1 << 40) == SHAPE
+    assert prefill(lib, dt=2) == DTYPE
+    assert prefill(lib, dt=-1) == DTYPE
+    # B = 0 is a no-op and needs no pointers at all
+    assert prefill(lib, B=0, q=None, k=None, v=None, beta=None, la=None, o=None, s1=None) == OK
+    # T = 0 without a final state has nothing to write
+    assert prefill(lib, T=0, q=None, k=None, v=None, beta=None, la=None, o=None, s1=None) == OK
+
+
+def test_varlen_validation(lib):
+    assert varlen(lib, cu=None) == NULL
+    assert varlen(lib, cu=P + 4) == ALIGN
+    assert varlen(lib, v=None) == NULL
+    assert varlen(lib, N=-1) == SHAPE
+    assert varlen(lib, Tt=-1) == SHAPE
+    assert varlen(lib, Tt=1 << 31) == SHAPE     # cu_seqlens holds int32 offsets
+    assert varlen(lib, dk=96) == UNSUP
+    assert varlen(lib, dt=7) == DTYPE
+    assert varlen(lib, N=0, cu=None, q=None, o=None) == OK
+    assert varlen(lib, Tt=0, q=None, k=None, v=None, beta=None, la=None, o=None, s1=None) == OK
+
+
+def test_decode_validation(lib):
+    for name in ("q", "k", "v", "beta", "la", "st", "o"):
+        assert decode(lib, **{name: None}) == NULL, name
+        assert decode(lib, **{name: MIS}) == ALIGN, name
+    assert decode(lib, N=-3) == SHAPE
+    assert decode(lib, H=0) == SHAPE
+    assert decode(lib, dk=127) == UNSUP
+    assert decode(lib, dt=3) == DTYPE
+    assert decode(lib, N=0, q=None) == OK
+
+
+def test_binding_rejects_cpu_tensors(lib):
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 2, 1, 128)
+    with pytest.raises(ValueError, match="GPU"):
+        kda.kda_prefill(x, x, x, torch.zeros(1, 2, 1), x)
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    with pytest.raises(ImportError, match="build"):
+        kda.load_library(str(tmp_path / "libkda.so"))

@@ -1,0 +1,69 @@
+"""Decode step on the GPU vs the fp64 oracle (batched decode workload:
+B sequences x H heads, consecutive single-token steps, bf16 q/k/v/beta, fp32
+log_alpha and state, states starting from N(0, 0.02^2))."""
+import numpy as np
+import pytest
+
+import gated_delta_rule_113_amd as kda
+import kda_inputs as ki
+import oracle
+from kda_gpu import check, device, rel_err_states, rel_err_vectors, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_chain(inp, dev):
+    torch = __import__("torch")
+    t = upload(inp, dev)
+    state = t["initial_state"].clone()
+    outs = []
+    for s in range(inp.q.shape[0]):
+        outs.append(kda.kda_decode_step(t["q"][s], t["k"][s], t["v"][s], t["beta"][s],
+                                        t["log_alpha"][s], state))
+    torch.cuda.synchronize()
+    return torch.stack(outs).cpu().numpy(), state.cpu().numpy()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_small_every_step(dtype):
+    inp = ki.decode_steps(1, steps=64, N=4, H=4, dtype=dtype)
+    o, S = _run_chain(inp, device())
+    q, k, v, b, la = inp.widened()
+    o_ref, S_ref = oracle.decode_chain(q, k, v, b, la, inp.initial_state)
+    check(f"decode small {dtype}", rel_err_vectors(o, o_ref), rel_err_states(S, S_ref))
+
+
+def test_decode_full_size_sampled():
+    """The full workload (64 x 32 heads, 1024 steps) in the launch configuration
+    the benchmark times; every step's output and the final state of 64 sampled
+    heads are checked against the oracle."""
+    inp = ki.workload_decode()
+    o, S = _run_chain(inp, device())
+    r = np.random.default_rng(0)
+    pairs = [(int(n), int(h)) for n, h in zip(r.integers(0, 64, 64), r.integers(0, 32, 64))]
+    ns = np.array([p[0] for p in pairs])
+    hs = np.array([p[1] for p in pairs])
+    q, k, v, b, la = (x[:, ns, hs][:, :, None] for x in inp.widened())
+    s0 = inp.initial_state[ns, hs][:, None]
+    o_ref, S_ref = oracle.decode_chain(q, k, v, b, la, s0)
+    check("decode full (64 sampled heads)", rel_err_vectors(o[:, ns, hs], o_ref[:, :, 0]),
+          rel_err_states(S[ns, hs], S_ref[:, 0]))
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
+
+
+def test_decode_in_place_and_zero_beta():
+    """beta = 0 and log_alpha = 0 leave the state bit-for-bit unchanged; the
+    output is then S^T q."""
+    torch = __import__("torch")
+    dev = device()
+    inp = ki.decode_steps(1, steps=1, N=3, H=2)
+    t = upload(inp, dev)
+    state = t["initial_state"].clone()
+    before = state.clone()
+    o = kda.kda_decode_step(t["q"][0], t["k"][0], t["v"][0], torch.zeros_like(t["beta"][0]),
+                            torch.zeros_like(t["log_alpha"][0]), state)
+    torch.cuda.synchronize()
+    assert torch.equal(state, before)
+    q = t["q"][0].float().cpu().numpy().astype(np.float64)
+    ref = np.einsum("nhij,nhi->nhj", before.cpu().numpy().astype(np.float64), q)
+    assert rel_err_vectors(o.cpu().numpy(), ref) < 1e-5
