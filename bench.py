@@ -67,6 +67,25 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def measured_traffic(summary: str, kernel: str):
+    """HBM bytes per launch of `kernel` from a committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, scaled by a reference copy), or None
+    when there is none or the kernel's sources changed since it was taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", summary)
+    try:
+        with open(path) as f:
+            rec = json.load(f)["kernels"][kernel]
+        h = hashlib.sha256()
+        for src in rec["sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+    except (OSError, KeyError, ValueError):
+        return None
+    return rec["traffic_bytes_per_launch"] if h.hexdigest() == rec["sources_sha256"] else None
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -181,7 +200,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic("decode_B64_H32_hbm_traffic.json", "decode_step_kernel<bf16_t>"),
             "kernel": "decode_step_kernel<bf16_t>",
             "algorithmic_bytes_per_launch": bytes_per_launch,
             "avg_launch_ms_timed_region": ms_per_step,
