@@ -22,4 +22,12 @@ hipError_t launch_prefill_recurrent(const void* q, const void* k, const void* v,
                                     int64_t H, const float* initial_state, float* o,
                                     float* final_state, bool bf16, hipStream_t stream);
 
+// Chunked prefill on bf16 matrix instructions (bf16 inputs only): 64-token
+// chunks, one workgroup per (sequence, head, 16-column slice of d_v).
+hipError_t launch_prefill_chunked(const void* q, const void* k, const void* v, const void* beta,
+                                  const float* log_alpha, const int32_t* cu_seqlens,
+                                  int64_t n_seq, int64_t T, int64_t H,
+                                  const float* initial_state, float* o, float* final_state,
+                                  hipStream_t stream);
+
 }  // namespace kda
