@@ -17,8 +17,10 @@ from ._binding import (  # noqa: F401
     KDAError,
     kda_decode_step,
     kda_prefill,
+    kda_set_prefill_segment,
     kda_varlen_prefill,
     load_library,
 )
 
-__all__ = ["kda_prefill", "kda_varlen_prefill", "kda_decode_step", "KDAError", "load_library"]
+__all__ = ["kda_prefill", "kda_varlen_prefill", "kda_decode_step", "kda_set_prefill_segment",
+           "KDAError", "load_library"]

@@ -20,8 +20,8 @@ STATUS_NAMES = {
     0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
     4: "KDA_ERR_ALIGN", 5: "KDA_ERR_UNSUPPORTED", 6: "KDA_ERR_HIP",
 }
-EXPORTS = ("kda_prefill", "kda_varlen_prefill", "kda_decode_step", "kda_status_str",
-           "kda_abi_version")
+EXPORTS = ("kda_prefill", "kda_varlen_prefill", "kda_decode_step", "kda_set_prefill_segment",
+           "kda_status_str", "kda_abi_version")
 
 _lock = threading.Lock()
 _lib = None
@@ -36,8 +36,14 @@ class KDAError(RuntimeError):
 
 
 def load_library(path: str | None = None):
-    """Load libkda.so and declare the C signatures.  Raises if it is not built."""
+    """Load libkda.so and declare the C signatures.  Raises if it is not built.
+
+    torch is imported first: libkda.so then binds to the HIP runtime that
+    torch already loaded, so device memory, streams and the library's own
+    runtime calls all go through one runtime.  (Loaded first, the library
+    would pull in the system copy and the process would hold two.)"""
     global _lib
+    _torch()
     with _lock:
         if _lib is not None and path is None:
             return _lib
@@ -57,6 +63,8 @@ def load_library(path: str | None = None):
         lib.kda_decode_step.argtypes = [vp, vp, vp, vp, f32p, f32p, f32p,
                                         i64, i64, i64, i64, ctypes.c_int, vp]
         lib.kda_decode_step.restype = ctypes.c_int
+        lib.kda_set_prefill_segment.argtypes = [i64]
+        lib.kda_set_prefill_segment.restype = ctypes.c_int
         lib.kda_status_str.argtypes = [ctypes.c_int]
         lib.kda_status_str.restype = ctypes.c_char_p
         lib.kda_abi_version.argtypes = []
@@ -183,6 +191,12 @@ def kda_varlen_prefill(q, k, v, beta, log_alpha, cu_seqlens, initial_state=None,
                                   _stream(dev))
     _check(lib, "kda_varlen_prefill", code)
     return o, final_state
+
+
+def kda_set_prefill_segment(tokens: int) -> None:
+    """Force the prefill segment length (a multiple of 64), or 0 for automatic."""
+    lib = load_library()
+    _check(lib, "kda_set_prefill_segment", lib.kda_set_prefill_segment(int(tokens)))
 
 
 def kda_decode_step(q, k, v, beta, log_alpha, state, *, out=None):

@@ -55,12 +55,12 @@ kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HI
 // are not exact in bf16) take the register-resident token-by-token kernel.
 hipError_t launch_prefill(const void* q, const void* k, const void* v, const void* beta,
                           const float* log_alpha, const int32_t* cu_seqlens, int64_t n_seq,
-                          int64_t T, int64_t H, const float* initial_state, float* o,
-                          float* final_state, kda_dtype in_dtype, hipStream_t stream)
+                          int64_t T, int64_t T_total, int64_t H, const float* initial_state,
+                          float* o, float* final_state, kda_dtype in_dtype, hipStream_t stream)
 {
     if (in_dtype == KDA_BF16)
-        return kda::launch_prefill_chunked(q, k, v, beta, log_alpha, cu_seqlens, n_seq, T, H,
-                                           initial_state, o, final_state, stream);
+        return kda::launch_prefill_scan(q, k, v, beta, log_alpha, cu_seqlens, n_seq, T, T_total,
+                                        H, initial_state, o, final_state, stream);
     return kda::launch_prefill_recurrent(q, k, v, beta, log_alpha, cu_seqlens, n_seq, T, H,
                                          initial_state, o, final_state, false, stream);
 }
@@ -89,8 +89,9 @@ kda_status kda_prefill(const void* q, const void* k, const void* v, const void* 
         return st;
     }
     if (T == 0 && !final_state) return KDA_OK;
-    return from_hip(launch_prefill(q, k, v, beta, log_alpha, nullptr, B, T, H, initial_state, o,
-                                   final_state, in_dtype, static_cast<hipStream_t>(stream)));
+    return from_hip(launch_prefill(q, k, v, beta, log_alpha, nullptr, B, T, B * T, H,
+                                   initial_state, o, final_state, in_dtype,
+                                   static_cast<hipStream_t>(stream)));
 }
 
 kda_status kda_varlen_prefill(const void* q, const void* k, const void* v, const void* beta,
@@ -116,8 +117,9 @@ kda_status kda_varlen_prefill(const void* q, const void* k, const void* v, const
         return st;
     }
     if (T_total == 0 && !final_state) return KDA_OK;
-    return from_hip(launch_prefill(q, k, v, beta, log_alpha, cu_seqlens, N, 0, H, initial_state,
-                                   o, final_state, in_dtype, static_cast<hipStream_t>(stream)));
+    return from_hip(launch_prefill(q, k, v, beta, log_alpha, cu_seqlens, N, 0, T_total, H,
+                                   initial_state, o, final_state, in_dtype,
+                                   static_cast<hipStream_t>(stream)));
 }
 
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* beta,
@@ -134,6 +136,13 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
     return from_hip(kda::launch_decode_step(q, k, v, beta, log_alpha, state, o, N * H,
                                             in_dtype == KDA_BF16,
                                             static_cast<hipStream_t>(stream)));
+}
+
+kda_status kda_set_prefill_segment(int64_t tokens)
+{
+    if (tokens < 0 || tokens % 64 != 0 || tokens > (int64_t(1) << 40)) return KDA_ERR_SHAPE;
+    kda::set_prefill_segment(tokens);
+    return KDA_OK;
 }
 
 const char* kda_status_str(kda_status status)

@@ -23,11 +23,19 @@ hipError_t launch_prefill_recurrent(const void* q, const void* k, const void* v,
                                     float* final_state, bool bf16, hipStream_t stream);
 
 // Chunked prefill on bf16 matrix instructions (bf16 inputs only): 64-token
-// chunks, one workgroup per (sequence, head, 16-column slice of d_v).
-hipError_t launch_prefill_chunked(const void* q, const void* k, const void* v, const void* beta,
-                                  const float* log_alpha, const int32_t* cu_seqlens,
-                                  int64_t n_seq, int64_t T, int64_t H,
-                                  const float* initial_state, float* o, float* final_state,
-                                  hipStream_t stream);
+// chunks, one workgroup per (sequence, head, segment).  Long sequences are cut
+// into segments whose affine state maps are composed in between (three
+// launches plus a workspace from a stream-ordered pool); short ones take one
+// launch.  Dense when cu_seqlens == nullptr (T rows each), packed otherwise
+// (T_total rows in all).
+hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, const void* beta,
+                               const float* log_alpha, const int32_t* cu_seqlens, int64_t n_seq,
+                               int64_t T, int64_t T_total, int64_t H,
+                               const float* initial_state, float* o, float* final_state,
+                               hipStream_t stream);
+
+// Tokens per segment for the chunked prefill (a positive multiple of 64), or
+// 0 to choose it from the problem size and the number of CUs.
+void set_prefill_segment(int64_t tokens);
 
 }  // namespace kda

@@ -1,0 +1,1152 @@
+// Chunked KDA prefill on bf16 matrix cores with sequence segmentation.
+//
+// The recurrence (per head; S is d_k x d_v, rows = forgetting channels)
+//     S_t = (I - b_t k_t k_t^T) Diag(a_t) S_{t-1} + b_t k_t v_t^T,   o_t = S_t^T q_t
+// ("Kimi K3 -- the architecture and infrastructure, explained": section "How
+// the delta rule actually works" gives the update, section "Kimi Delta
+// Attention: the load-bearing choice" the per-channel gate and the blockwise,
+// context-parallel organisation on matrix units) is evaluated 64 tokens at a
+// time.  Within a chunk of tokens r = 0..63 entering with state S0, with G_r
+// the inclusive cumulative log2-decay of each channel:
+//     A_ri  = sum_c k_rc k_ic 2^(G_rc - G_ic)   (i < r)      key-key interactions
+//     P_ri  = sum_c q_rc k_ic 2^(G_rc - G_ic)   (i <= r)     query-key interactions
+//     T     = (I + Diag(b) A)^-1                              (UT transform)
+//     X     = Kt S0,   Kt_r = k_r 2^G_r                        decayed keys
+//     U     = T Diag(b) (V - X)                               corrected writes
+//     O     = Qt S0 + P U,   Qt_r = q_r 2^G_r
+//     S1    = Diag(2^G_63) S0 + Ke^T U,   Ke_i = k_i 2^(G_63 - G_i)
+// which is the token recurrence regrouped (exact in real arithmetic).
+//
+// Sequence segmentation ("context parallel" within one GPU).  The chunk step
+// is affine in the entering state, so a segment of the sequence maps its
+// entering state to S_end = M S_start + R with M (d_k x d_k) the product of
+// its chunk transitions.  A long sequence is cut into segments; pass 1 runs
+// each segment but the last on the augmented state [M | R] (started from
+// [I | 0], or from the true initial state for the first segment), pass 2
+// composes the segment maps in order to get every segment's true entering
+// state, pass 3 reruns every segment from its entering state and writes the
+// outputs and the final state.  Short sequences take pass 3 only.
+//
+// One workgroup (8 waves) processes one (sequence, head, segment); wave w
+// holds value columns 16w..16w+15 of the fp32 state in matrix-core
+// accumulator registers for the whole segment.  Per chunk all d_v-independent
+// work (cumulative decay, A, P, the UT solve, the decayed operands) is done
+// once and staged in LDS; the state products then run per wave with the state
+// and the corrected writes as register operands.
+//
+// Precision: every matrix-core operand that is not an exact bf16 input is
+// split into hi + lo bf16 parts and each product uses hi*hi + hi*lo + lo*hi
+// with fp32 accumulation; the state, decay factors, T and all accumulations
+// are fp32.
+//
+// Overflow-free decay factors: 2^(G_r - G_i) is never formed from 2^(-G_i).
+// Tiles of 16 x 16 tokens pair a row factor 2^(G_r - rho) with a column factor
+// 2^(rho - G_i) for a per-row-block reference rho: the block's 8th token when
+// every channel's log2-decay from there to either end of the block is <= 96
+// (both factors then stay within [2^-96, 2^96]), else the end of the previous
+// block, in which case the diagonal tile is computed pairwise on the vector
+// ALUs.  Off-diagonal column factors are always <= 1.
+//
+// Operand layouts.  A 16x16x32 matrix instruction sums over 32 k-slots; lane
+// group g (lanes 16g..16g+15) supplies slots 8g..8g+7.  Slot (g, j) of step s
+// is bound to channel (or token) 32s + 16(j >> 2) + 4g + (j & 3), so that a
+// result tile in accumulator layout (lane group g holding rows 4g..4g+3) is
+// directly the B operand of the next product over that index.  Tiles that are
+// read as A operands are stored in LDS with the same index permutation, so
+// each fragment is one 16-byte read, and XOR-swizzled by row against bank
+// conflicts.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <mutex>
+
+#include "kda_device.hpp"
+#include "kda_internal.hpp"
+
+namespace kda {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int CH = 64;            // tokens per chunk
+constexpr int NW = 8;             // waves per workgroup
+constexpr int NT = 64 * NW;       // threads per workgroup
+constexpr int G_LD = kDim + 4;    // fp32 row stride of the decay tile
+constexpr int N_LD = CH + 4;      // fp32 row stride of 64 x 64 tiles
+constexpr int SS = kDim * kDim;   // floats per state matrix
+constexpr float kSafeLog2 = 96.f;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---- LDS map (bytes).  Regions are reused within a chunk once their
+//      previous contents are dead.
+// R0: raw q | raw k | decay G (fp32), later the decayed operands Kt, Qt.
+constexpr int OFF_Q = 0;
+constexpr int OFF_K = 16384;
+constexpr int OFF_G = 32768;
+constexpr int R0_BYTES = 32768 + CH * G_LD * 4;
+constexpr int OFF_KT_HI = 0, OFF_KT_LO = 16384, OFF_QT_HI = 32768, OFF_QT_LO = 49152;
+// R1: quad sums of the decay scan; then N = Diag(b) A and T (fp32); later Ke^T.
+constexpr int OFF_R1 = R0_BYTES;
+constexpr int OFF_QSUM = OFF_R1;
+constexpr int OFF_N = OFF_R1;
+constexpr int OFF_TF = OFF_R1 + CH * N_LD * 4;
+constexpr int OFF_KE_HI = OFF_R1, OFF_KE_LO = OFF_R1 + 16384;
+constexpr int R1_BYTES = 2 * CH * N_LD * 4;
+// T and P as split operands, the raw value tile, small vectors.
+constexpr int OFF_T_HI = OFF_R1 + R1_BYTES;
+constexpr int OFF_T_LO = OFF_T_HI + 8192;
+constexpr int OFF_P_HI = OFF_T_LO + 8192;
+constexpr int OFF_P_LO = OFF_P_HI + 8192;
+constexpr int OFF_V = OFF_P_LO + 8192;
+constexpr int OFF_BETA = OFF_V + 16384;
+constexpr int OFF_EL = OFF_BETA + CH * 4;
+constexpr int OFF_UNSAFE = OFF_EL + kDim * 4;
+constexpr int LDS_BYTES = OFF_UNSAFE + 16 * 4;
+static_assert(R1_BYTES >= 32768, "Ke^T must fit in R1");
+static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CU");
+
+// Index permutation within each group of 32 (see the header comment).
+__device__ __forceinline__ int perm(int x)
+{
+    return (x & ~31) | ((x & 12) << 1) | ((x & 16) >> 2) | (x & 3);
+}
+__device__ __forceinline__ int unperm(int p)
+{
+    return (p & ~31) | ((p & 24) >> 1) | ((p & 4) << 2) | (p & 3);
+}
+// Byte offsets in bf16 tiles of 128 (256 B rows) and 64 (128 B rows) entries.
+__device__ __forceinline__ int a256(int row, int pos)
+{
+    return (row << 8) + ((((pos >> 3) ^ row) & 15) << 4) + ((pos & 7) << 1);
+}
+__device__ __forceinline__ int a128(int row, int pos)
+{
+    return (row << 7) + ((((pos >> 3) ^ (row >> 1)) & 7) << 4) + ((pos & 7) << 1);
+}
+
+template <typename T>
+__device__ __forceinline__ T& at(char* base, int off)
+{
+    return *reinterpret_cast<T*>(base + off);
+}
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float bfw(__bf16 x) { return (float)x; }
+
+template <int W, typename V>
+__device__ __forceinline__ void split_vec(const float (&x)[W], V& h, V& l)
+{
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+        const __bf16 a = (__bf16)x[j];
+        h[j] = a;
+        l[j] = (__bf16)(x[j] - (float)a);
+    }
+}
+
+// hi*hi + hi*lo + lo*hi on the 16x16x32 bf16 matrix instruction.
+__device__ __forceinline__ f32x4 mma3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, f32x4 c)
+{
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, c, 0, 0, 0);
+    return c;
+}
+
+// the same on the 16x16x16 instruction (used by the small UT-solve blocks)
+__device__ __forceinline__ f32x4 mma16x3(bf16x4 ah, bf16x4 al, bf16x4 bh, bf16x4 bl, f32x4 c)
+{
+    const i16x4 AH = __builtin_bit_cast(i16x4, ah), AL = __builtin_bit_cast(i16x4, al);
+    const i16x4 BH = __builtin_bit_cast(i16x4, bh), BL = __builtin_bit_cast(i16x4, bl);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(AL, BH, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(AH, BL, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(AH, BH, c, 0, 0, 0);
+    return c;
+}
+
+__device__ __forceinline__ float4 f4add(float4 a, float4 b)
+{
+    return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+
+}  // namespace
+
+// Arguments shared by the three passes (by value).
+struct ScanArgs {
+    const bf16_t* q;
+    const bf16_t* k;
+    const bf16_t* v;
+    const bf16_t* beta;
+    const float* log_alpha;
+    const int32_t* cu_seqlens;  // packed rows, or null for dense sequences of T rows
+    const int32_t* seg_first;   // packed + segmented: first segment of each sequence [n_seq + 1]
+    int64_t T;                  // dense sequence length
+    int64_t n_seq;
+    int64_t seg_len;            // tokens per segment (multiple of 64); 0 = one segment each
+    int64_t nseg_dense;         // dense: segments per sequence
+    int64_t n_segs;             // number of segment slots (grid bound)
+    int H;
+    const float* initial_state;
+    float* o;
+    float* final_state;
+    float* ws_maps;   // [n_segs][H][2][d_k][d_v]: M and R of each segment but the last
+    float* ws_start;  // [n_segs][H][d_k][d_v]: entering state of each segment
+};
+
+namespace {
+
+struct SegInfo {
+    int64_t n;       // sequence
+    int64_t j;       // segment within the sequence
+    int64_t nseg;    // segments of the sequence
+    int64_t z0;      // global index of its first segment
+    int64_t row0;    // first row of the sequence
+    int64_t begin;   // segment rows [begin, end) relative to row0
+    int64_t end;
+    bool valid;
+};
+
+__device__ SegInfo decode_segment(const ScanArgs& a, int64_t z)
+{
+    SegInfo s;
+    s.valid = z < a.n_segs;
+    if (!s.valid) return s;
+    int64_t len;
+    if (!a.cu_seqlens) {
+        s.nseg = a.nseg_dense;
+        s.n = z / s.nseg;
+        s.j = z - s.n * s.nseg;
+        s.z0 = z - s.j;
+        s.row0 = s.n * a.T;
+        len = a.T;
+    } else if (!a.seg_first) {
+        s.n = z;
+        s.j = 0;
+        s.nseg = 1;
+        s.z0 = z;
+        s.row0 = a.cu_seqlens[z];
+        len = static_cast<int64_t>(a.cu_seqlens[z + 1]) - s.row0;
+    } else {
+        // the sequence whose segment range holds z
+        int64_t lo = 0, hi = a.n_seq;  // seg_first[lo] <= z < seg_first[hi]
+        if (z >= a.seg_first[a.n_seq]) {
+            s.valid = false;
+            return s;
+        }
+        while (hi - lo > 1) {
+            const int64_t mid = (lo + hi) >> 1;
+            if (a.seg_first[mid] <= z) lo = mid;
+            else hi = mid;
+        }
+        s.n = lo;
+        s.z0 = a.seg_first[lo];
+        s.j = z - s.z0;
+        s.nseg = static_cast<int64_t>(a.seg_first[lo + 1]) - s.z0;
+        s.row0 = a.cu_seqlens[lo];
+        len = static_cast<int64_t>(a.cu_seqlens[lo + 1]) - s.row0;
+    }
+    const int64_t seg = s.nseg == 1 ? len : a.seg_len;
+    s.begin = s.j * seg;
+    s.end = (s.j == s.nseg - 1) ? len : s.begin + seg;
+    return s;
+}
+
+// OUT = true : pass 3 -- outputs and final state, d_v = 128 (one 16-column group per wave)
+// OUT = false: pass 1 -- segment maps [M | R], 256 columns (two groups per wave), no outputs
+template <bool OUT>
+__global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
+{
+    __shared__ __attribute__((aligned(16))) char sm[LDS_BYTES];
+    constexpr int NS = OUT ? 1 : 2;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int l16 = lane & 15;
+    const int g4 = lane >> 4;
+    const int H = a.H;
+    const int64_t z = blockIdx.x / H;
+    const int h = static_cast<int>(blockIdx.x - z * H);
+
+    const SegInfo sg = decode_segment(a, z);
+    if (!sg.valid) return;
+    if (!OUT && sg.j == sg.nseg - 1) return;  // the last segment needs no map
+    const bool blkM = !OUT && sg.j > 0;       // pass 1: is the M block carried?
+
+    const int col = 16 * wave + l16;          // this lane's value column
+    const int64_t unit = sg.n * H + h;
+
+    // ---------------- state (accumulator layout: S[g][t][i] = row 16t+4g4+i, column col)
+    f32x4 S[NS][8];
+    {
+        const float* init = nullptr;
+        if (OUT) {
+            if (sg.nseg > 1) init = a.ws_start + (z * H + h) * SS;
+            else if (a.initial_state) init = a.initial_state + unit * SS;
+        } else if (sg.j == 0 && a.initial_state) {
+            init = a.initial_state + unit * SS;
+        }
+#pragma unroll
+        for (int gi = 0; gi < NS; ++gi)
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int ch = 16 * t + 4 * g4 + i;
+                    float x;
+                    if (!OUT && gi == 0) x = (ch == col) ? 1.f : 0.f;
+                    else x = init ? init[ch * kDim + col] : 0.f;
+                    S[gi][t][i] = x;
+                }
+        if (!OUT && sg.j == 0) {
+            // pass 3 starts the first segment from this copy, so that a final
+            // state aliasing the initial one cannot race with it
+            float* dst = a.ws_start + (z * H + h) * SS;
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[(16 * t + 4 * g4 + i) * kDim + col] = S[NS - 1][t][i];
+        }
+    }
+
+    const int64_t seg_tokens = sg.end - sg.begin;
+    const int64_t nch = (seg_tokens + CH - 1) / CH;
+    const int64_t base = sg.row0 + sg.begin;  // first row of the segment
+
+    // ---------------- register prefetch of one chunk of inputs
+    uint4 pq[2], pk[2], pv[2];
+    float4 pla[4];
+    float pb = 0.f;
+    auto prefetch = [&](int64_t c0, int L, int tid) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int r = (tid >> 4) + 32 * m;
+            if (r < L) {
+                const int64_t off = ((base + c0 + r) * H + h) * kDim + 8 * (tid & 15);
+                pk[m] = *reinterpret_cast<const uint4*>(a.k + off);
+                pv[m] = *reinterpret_cast<const uint4*>(a.v + off);
+                if (OUT) pq[m] = *reinterpret_cast<const uint4*>(a.q + off);
+            } else {
+                pk[m] = pv[m] = pq[m] = make_uint4(0, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int r = 4 * (tid >> 5) + m;
+            pla[m] = r < L ? *reinterpret_cast<const float4*>(
+                                 a.log_alpha + ((base + c0 + r) * H + h) * kDim + 4 * (tid & 31))
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        if (tid < CH) pb = tid < L ? widen(a.beta[(base + c0 + tid) * H + h]) : 0.f;
+    };
+    if (nch > 0) prefetch(0, static_cast<int>(std::min<int64_t>(CH, seg_tokens)), tid);
+
+    for (int64_t ci = 0; ci < nch; ++ci) {
+        const int64_t c0 = ci * CH;
+        const int L = static_cast<int>(std::min<int64_t>(CH, seg_tokens - c0));
+        // Lane-derived offsets are recomputed every chunk from an opaque copy of
+        // the thread index: hoisted out of the loop they would each hold a
+        // register for the whole segment.
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int lane = tid & 63;
+        const int l16 = lane & 15;
+        const int g4 = lane >> 4;
+        const int col = 16 * wave + l16;
+        const int tq = tid >> 5;                 // token quad (scan, operand formation)
+        const int cq = tid & 31;                 // natural channel quad
+        const int pq4 = perm(4 * cq);            // its position in the permuted order
+
+        // ======== 0: stage the chunk; in-register scan of the log2-decay over 4 tokens
+        float4 gp[4];
+        {
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const int r = (tid >> 4) + 32 * m;
+                const int c8 = 8 * (tid & 15);
+                const int p0 = perm(c8), p1 = perm(c8 + 4);
+                at<uint2>(sm, OFF_K + a256(r, p0)) = make_uint2(pk[m].x, pk[m].y);
+                at<uint2>(sm, OFF_K + a256(r, p1)) = make_uint2(pk[m].z, pk[m].w);
+                if (OUT) {
+                    at<uint2>(sm, OFF_Q + a256(r, p0)) = make_uint2(pq[m].x, pq[m].y);
+                    at<uint2>(sm, OFF_Q + a256(r, p1)) = make_uint2(pq[m].z, pq[m].w);
+                }
+                at<uint4>(sm, OFF_V + a256(r, c8)) = pv[m];
+            }
+            if (tid < CH) at<float>(sm, OFF_BETA + 4 * tid) = pb;
+            float4 run = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const float4 x = pla[m];
+                run = make_float4(run.x + x.x * kLog2e, run.y + x.y * kLog2e, run.z + x.z * kLog2e,
+                                  run.w + x.w * kLog2e);
+                gp[m] = run;
+            }
+            at<float4>(sm, OFF_QSUM + (tq * kDim + pq4) * 4) = run;
+        }
+        __syncthreads();
+
+        // ======== 1: finish the scan across token quads; chunk-end decay
+        {
+            float4 off = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int u = 0; u < 15; ++u)
+                if (u < tq) off = f4add(off, at<float4>(sm, OFF_QSUM + (u * kDim + pq4) * 4));
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                at<float4>(sm, OFF_G + ((4 * tq + m) * G_LD + pq4) * 4) = f4add(gp[m], off);
+            if (tq == 15) {
+                const float4 g63 = f4add(gp[3], off);
+                at<float4>(sm, OFF_EL + 16 * cq) =
+                    make_float4(ex2(g63.x), ex2(g63.y), ex2(g63.z), ex2(g63.w));
+            }
+        }
+        __syncthreads();
+
+        // ======== 2: per row block, is the mid-block reference safe for every channel?
+        {
+            const int rb = tid >> 7, p = tid & 127;
+            const float* G = &at<float>(sm, OFF_G);
+            const float gs = rb ? G[(16 * rb - 1) * G_LD + p] : 0.f;
+            const float gm = G[(16 * rb + 7) * G_LD + p];
+            const float ge = G[(16 * rb + 15) * G_LD + p];
+            const bool bad = (gs - gm > kSafeLog2) || (gm - ge > kSafeLog2);
+            const uint64_t any = __ballot(bad);
+            if (lane == 0) at<int>(sm, OFF_UNSAFE + 4 * wave) = any != 0;
+        }
+        __syncthreads();
+
+        // ======== 3: A and P tiles.  Wave (rb, kh) covers row block rb over the
+        //             channel half kh; the two halves are summed in phase 4.
+        const int kh = wave >> 2;
+        const int rb = kh ? 3 - (wave & 3) : (wave & 3);
+        f32x4 accA[4], accP[4];
+        {
+            const float* G = &at<float>(sm, OFF_G);
+            const bool uns = at<int>(sm, OFF_UNSAFE + 8 * rb) | at<int>(sm, OFF_UNSAFE + 8 * rb + 4);
+            const int r = 16 * rb + l16;  // this lane's token in row-operand position
+            bf16x8 fkh[2], fkl[2], fqh[2], fql[2], cdh[2], cdl[2];
+            float rho[2][8];
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl) {
+                const int p0 = 32 * (2 * kh + sl) + 8 * g4;
+                const float4 ga = at<float4>(sm, OFF_G + (r * G_LD + p0) * 4);
+                const float4 gb = at<float4>(sm, OFF_G + (r * G_LD + p0 + 4) * 4);
+                float4 ra, rbv;
+                if (!uns) {
+                    ra = at<float4>(sm, OFF_G + ((16 * rb + 7) * G_LD + p0) * 4);
+                    rbv = at<float4>(sm, OFF_G + ((16 * rb + 7) * G_LD + p0 + 4) * 4);
+                } else if (rb > 0) {
+                    ra = at<float4>(sm, OFF_G + ((16 * rb - 1) * G_LD + p0) * 4);
+                    rbv = at<float4>(sm, OFF_G + ((16 * rb - 1) * G_LD + p0 + 4) * 4);
+                } else {
+                    ra = rbv = make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+                const float gr[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+                const float rr[8] = {ra.x, ra.y, ra.z, ra.w, rbv.x, rbv.y, rbv.z, rbv.w};
+                const bf16x8 kk = at<bf16x8>(sm, OFF_K + a256(r, p0));
+                bf16x8 qq = kk;
+                if (OUT) qq = at<bf16x8>(sm, OFF_Q + a256(r, p0));
+                float xk[8], xq[8], xd[8];
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    rho[sl][jj] = rr[jj];
+                    const float d = gr[jj] - rr[jj];
+                    const float f = ex2(d);
+                    xk[jj] = bfw(kk[jj]) * f;
+                    xq[jj] = bfw(qq[jj]) * f;
+                    xd[jj] = uns ? 0.f : bfw(kk[jj]) * ex2(-d);
+                }
+                split_vec(xk, fkh[sl], fkl[sl]);
+                if (OUT) split_vec(xq, fqh[sl], fql[sl]);
+                split_vec(xd, cdh[sl], cdl[sl]);
+            }
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib) {
+                accA[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+                accP[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (ib > rb) continue;
+                if (ib == rb) {
+                    if (!uns) {
+#pragma unroll
+                        for (int sl = 0; sl < 2; ++sl) {
+                            accA[ib] = mma3(cdh[sl], cdl[sl], fkh[sl], fkl[sl], accA[ib]);
+                            if (OUT) accP[ib] = mma3(cdh[sl], cdl[sl], fqh[sl], fql[sl], accP[ib]);
+                        }
+                    } else {
+                        // steep decay inside the block: pairwise on the vector ALUs,
+                        // result in the accumulator layout (row r, column 16rb+4g4+i)
+                        const char* K = sm + OFF_K;
+                        const char* Q = sm + (OUT ? OFF_Q : OFF_K);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int ti = 16 * rb + 4 * g4 + i;
+                            float sa = 0.f, sp = 0.f;
+                            if (ti <= r) {
+                                for (int p = 64 * kh; p < 64 * kh + 64; ++p) {
+                                    const float f = ex2(G[r * G_LD + p] - G[ti * G_LD + p]);
+                                    const float ki = bfw(*reinterpret_cast<const __bf16*>(K + a256(ti, p)));
+                                    const float kr = bfw(*reinterpret_cast<const __bf16*>(K + a256(r, p)));
+                                    const float qr = bfw(*reinterpret_cast<const __bf16*>(Q + a256(r, p)));
+                                    sa += kr * ki * f;
+                                    sp += qr * ki * f;
+                                }
+                            }
+                            accA[ib][i] = sa;
+                            accP[ib][i] = sp;
+                        }
+                    }
+                } else {
+                    const int ti = 16 * ib + l16;  // this lane's token in column position
+#pragma unroll
+                    for (int sl = 0; sl < 2; ++sl) {
+                        const int p0 = 32 * (2 * kh + sl) + 8 * g4;
+                        const float4 ga = at<float4>(sm, OFF_G + (ti * G_LD + p0) * 4);
+                        const float4 gb = at<float4>(sm, OFF_G + (ti * G_LD + p0 + 4) * 4);
+                        const float gi[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+                        const bf16x8 kk = at<bf16x8>(sm, OFF_K + a256(ti, p0));
+                        float x[8];
+#pragma unroll
+                        for (int jj = 0; jj < 8; ++jj) x[jj] = bfw(kk[jj]) * ex2(rho[sl][jj] - gi[jj]);
+                        bf16x8 ch, cl;
+                        split_vec(x, ch, cl);
+                        accA[ib] = mma3(ch, cl, fkh[sl], fkl[sl], accA[ib]);
+                        if (OUT) accP[ib] = mma3(ch, cl, fqh[sl], fql[sl], accP[ib]);
+                    }
+                }
+            }
+            // accA[ib][i] = A[r][16ib+4g4+i] over this channel half; the first
+            // half parks its partial sums where N and T will live.
+            if (kh == 0) {
+#pragma unroll
+                for (int ib = 0; ib < 4; ++ib) {
+                    if (ib > rb) continue;
+                    const int o4 = (r * N_LD + 16 * ib + 4 * g4) * 4;
+                    at<f32x4>(sm, OFF_N + o4) = accA[ib];
+                    if (OUT) at<f32x4>(sm, OFF_TF + o4) = accP[ib];
+                }
+            }
+        }
+        __syncthreads();
+
+        // ======== 4: second halves finish N = Diag(b) A (strictly lower) and P
+        //             (lower, split).
+        // Operand formation (phase 5): thread (tq, cq) covers tokens
+        // 4tq..4tq+3 x channels 4cq..4cq+3 of Kt, Qt and Ke, held in registers
+        // until their LDS regions are free.
+        bf16x4 fKh[4], fKl[4], fQh[4], fQl[4], fEh[4], fEl[4];
+        auto form = [&]() {
+            const float4 g63 = at<float4>(sm, OFF_G + (63 * G_LD + pq4) * 4);
+            float ke[4][4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int r = 4 * tq + m;
+                const float4 gv = at<float4>(sm, OFF_G + (r * G_LD + pq4) * 4);
+                const bf16x4 kv = at<bf16x4>(sm, OFF_K + a256(r, pq4));
+                bf16x4 qv = kv;
+                if (OUT) qv = at<bf16x4>(sm, OFF_Q + a256(r, pq4));
+                const float g[4] = {gv.x, gv.y, gv.z, gv.w};
+                const float e63[4] = {g63.x, g63.y, g63.z, g63.w};
+                float xk[4], xq[4];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const float e = ex2(g[x]);
+                    xk[x] = bfw(kv[x]) * e;
+                    xq[x] = bfw(qv[x]) * e;
+                    ke[x][m] = bfw(kv[x]) * ex2(e63[x] - g[x]);
+                }
+                split_vec(xk, fKh[m], fKl[m]);
+                if (OUT) split_vec(xq, fQh[m], fQl[m]);
+            }
+#pragma unroll
+            for (int x = 0; x < 4; ++x) split_vec(ke[x], fEh[x], fEl[x]);
+        };
+        if (kh == 1) {
+            const int r = 16 * rb + l16;
+            const float br = at<float>(sm, OFF_BETA + 4 * r);
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib) {
+                if (ib <= rb) {
+                    const int o4 = (r * N_LD + 16 * ib + 4 * g4) * 4;
+                    const f32x4 pa = at<f32x4>(sm, OFF_N + o4);
+                    f32x4 nn;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int ti = 16 * ib + 4 * g4 + i;
+                        nn[i] = ti < r ? br * (pa[i] + accA[ib][i]) : 0.f;
+                    }
+                    at<f32x4>(sm, OFF_N + o4) = nn;
+                    if (OUT) {
+                        const f32x4 pp = at<f32x4>(sm, OFF_TF + o4);
+                        float x[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int ti = 16 * ib + 4 * g4 + i;
+                            x[i] = ti <= r ? pp[i] + accP[ib][i] : 0.f;
+                        }
+                        bf16x4 hi, lo;
+                        split_vec(x, hi, lo);
+                        const int pp0 = perm(16 * ib + 4 * g4);
+                        at<bf16x4>(sm, OFF_P_HI + a128(r, pp0)) = hi;
+                        at<bf16x4>(sm, OFF_P_LO + a128(r, pp0)) = lo;
+                    }
+                } else if (OUT && ib == rb + 1 && (rb & 1) == 0) {
+                    // the upper tile that shares a 32-token step with the diagonal
+                    const int pp0 = perm(16 * ib + 4 * g4);
+                    const bf16x4 zz = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+                    at<bf16x4>(sm, OFF_P_HI + a128(r, pp0)) = zz;
+                    at<bf16x4>(sm, OFF_P_LO + a128(r, pp0)) = zz;
+                }
+            }
+        }
+        __syncthreads();
+
+        // ======== 5: diagonal 16x16 blocks of T = (I + N)^-1 by forward
+        //             substitution (waves 0-3); then every thread forms its
+        //             share of the decayed operands.
+        if (wave < 4) {
+            const int b = wave, jc = lane >> 2, p = lane & 3;
+            const float* N = &at<float>(sm, OFF_N);
+            float nv[16][4];
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int i = p + 4 * m;
+                    nv[rr][m] = i < rr ? N[(16 * b + rr) * N_LD + 16 * b + i] : 0.f;
+                }
+            float tv[4] = {0.f, 0.f, 0.f, 0.f};  // T[16b + p + 4m][16b + jc]
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                float s = nv[rr][0] * tv[0] + nv[rr][1] * tv[1] + nv[rr][2] * tv[2] + nv[rr][3] * tv[3];
+                s += __shfl_xor(s, 1);
+                s += __shfl_xor(s, 2);
+                const float tr = (rr == jc ? 1.f : 0.f) - s;
+                if (p == (rr & 3)) tv[rr >> 2] = tr;
+            }
+            float* Tf = &at<float>(sm, OFF_TF);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) Tf[(16 * b + p + 4 * m) * N_LD + 16 * b + jc] = tv[m];
+        }
+        form();
+        __syncthreads();
+
+        // ======== 6: off-diagonal blocks, T[b][b-d] = -T[b][b] sum_m N[b][m] T[m][b-d]
+#pragma unroll
+        for (int d = 1; d < 4; ++d) {
+            const int b = wave;
+            if (b < 4 && b >= d) {
+                const float* N = &at<float>(sm, OFF_N);
+                float* Tf = &at<float>(sm, OFF_TF);
+                f32x4 zacc = {0.f, 0.f, 0.f, 0.f};
+                for (int m = b - d; m < b; ++m) {
+                    float an[4], bt[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        an[e] = N[(16 * b + l16) * N_LD + 16 * m + 4 * g4 + e];
+                        bt[e] = Tf[(16 * m + 4 * g4 + e) * N_LD + 16 * (b - d) + l16];
+                    }
+                    bf16x4 ah, al, bh, bl;
+                    split_vec(an, ah, al);
+                    split_vec(bt, bh, bl);
+                    zacc = mma16x3(ah, al, bh, bl, zacc);
+                }
+                float tb[4], zz[4] = {zacc[0], zacc[1], zacc[2], zacc[3]};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) tb[e] = Tf[(16 * b + l16) * N_LD + 16 * b + 4 * g4 + e];
+                bf16x4 ah, al, bh, bl;
+                split_vec(tb, ah, al);
+                split_vec(zz, bh, bl);
+                f32x4 tr = {0.f, 0.f, 0.f, 0.f};
+                tr = mma16x3(ah, al, bh, bl, tr);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Tf[(16 * b + 4 * g4 + e) * N_LD + 16 * (b - d) + l16] = -tr[e];
+            }
+            __syncthreads();
+        }
+
+        // ======== 7: T as a split operand; Kt and Qt into R0 (q, k, G are dead)
+        {
+            const int r = tid >> 3, c8 = 8 * (tid & 7);
+            const float* Tf = &at<float>(sm, OFF_TF);
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int i = unperm(c8 + e);
+                x[e] = (i >> 4) <= (r >> 4) ? Tf[r * N_LD + i] : 0.f;
+            }
+            bf16x8 hi, lo;
+            split_vec(x, hi, lo);
+            at<bf16x8>(sm, OFF_T_HI + a128(r, c8)) = hi;
+            at<bf16x8>(sm, OFF_T_LO + a128(r, c8)) = lo;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int rr = 4 * tq + m;
+                at<bf16x4>(sm, OFF_KT_HI + a256(rr, pq4)) = fKh[m];
+                at<bf16x4>(sm, OFF_KT_LO + a256(rr, pq4)) = fKl[m];
+                if (OUT) {
+                    at<bf16x4>(sm, OFF_QT_HI + a256(rr, pq4)) = fQh[m];
+                    at<bf16x4>(sm, OFF_QT_LO + a256(rr, pq4)) = fQl[m];
+                }
+            }
+        }
+        __syncthreads();
+
+        // ======== 8: state products (each wave its own columns)
+        // Ke^T into R1 (N and T are dead); read only after the next barrier
+        {
+            const int tp = perm(4 * tq);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                at<bf16x4>(sm, OFF_KE_HI + a128(4 * cq + x, tp)) = fEh[x];
+                at<bf16x4>(sm, OFF_KE_LO + a128(4 * cq + x, tp)) = fEl[x];
+            }
+        }
+        bf16x8 uh[NS][2], ul[NS][2];
+        {
+            f32x4 X[NS][4], O[4];
+#pragma unroll
+            for (int gi = 0; gi < NS; ++gi)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) X[gi][q4] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) O[q4] = f32x4{0.f, 0.f, 0.f, 0.f};
+            // X = Kt S, then O = Qt S (two passes keep fewer fragments live)
+#pragma unroll
+            for (int pass = 0; pass < (OUT ? 2 : 1); ++pass) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    bf16x8 sh[NS], sl[NS];
+#pragma unroll
+                    for (int gi = 0; gi < NS; ++gi) {
+                        float x[8];
+#pragma unroll
+                        for (int jj = 0; jj < 8; ++jj) x[jj] = S[gi][2 * s + (jj >> 2)][jj & 3];
+                        split_vec(x, sh[gi], sl[gi]);
+                    }
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const int ar = 16 * q4 + l16, ap = 32 * s + 8 * g4;
+                        if (pass == 0) {
+                            const bf16x8 kh_ = at<bf16x8>(sm, OFF_KT_HI + a256(ar, ap));
+                            const bf16x8 kl_ = at<bf16x8>(sm, OFF_KT_LO + a256(ar, ap));
+#pragma unroll
+                            for (int gi = 0; gi < NS; ++gi) {
+                                if (NS == 2 && gi == 0 && !blkM) continue;
+                                X[gi][q4] = mma3(kh_, kl_, sh[gi], sl[gi], X[gi][q4]);
+                            }
+                        } else {
+                            const bf16x8 qh_ = at<bf16x8>(sm, OFF_QT_HI + a256(ar, ap));
+                            const bf16x8 ql_ = at<bf16x8>(sm, OFF_QT_LO + a256(ar, ap));
+                            O[q4] = mma3(qh_, ql_, sh[0], sl[0], O[q4]);
+                        }
+                    }
+                }
+            }
+            // inputs of the next chunk, in flight during the rest of this one
+            if (ci + 1 < nch) {
+                const int64_t c1 = c0 + CH;
+                prefetch(c1, static_cast<int>(std::min<int64_t>(CH, seg_tokens - c1)), tid);
+            }
+            // Y = Diag(b) (V - X), split as B operands over tokens
+            bf16x8 yh[NS][2], yl[NS][2];
+            {
+                float y[NS][4][4];
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int tk = 16 * q4 + 4 * g4 + i;
+                        const float bt = at<float>(sm, OFF_BETA + 4 * tk);
+                        const float vv = bfw(*reinterpret_cast<const __bf16*>(sm + OFF_V + a256(tk, col)));
+#pragma unroll
+                        for (int gi = 0; gi < NS; ++gi) {
+                            const bool zero_v = (NS == 2 && gi == 0);  // the M block has no writes
+                            y[gi][q4][i] = bt * ((zero_v ? 0.f : vv) - X[gi][q4][i]);
+                        }
+                    }
+#pragma unroll
+                for (int gi = 0; gi < NS; ++gi)
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        float x[8];
+#pragma unroll
+                        for (int jj = 0; jj < 8; ++jj) x[jj] = y[gi][2 * s + (jj >> 2)][jj & 3];
+                        split_vec(x, yh[gi][s], yl[gi][s]);
+                    }
+            }
+            // U = T Y (T is block lower triangular: row block q4 needs steps s <= q4/2)
+            f32x4 U[NS][4];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+#pragma unroll
+                for (int gi = 0; gi < NS; ++gi) U[gi][q4] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    if (s > (q4 >> 1)) continue;
+                    const int ar = 16 * q4 + l16, ap = 32 * s + 8 * g4;
+                    const bf16x8 th = at<bf16x8>(sm, OFF_T_HI + a128(ar, ap));
+                    const bf16x8 tl = at<bf16x8>(sm, OFF_T_LO + a128(ar, ap));
+#pragma unroll
+                    for (int gi = 0; gi < NS; ++gi) {
+                        if (NS == 2 && gi == 0 && !blkM) continue;
+                        U[gi][q4] = mma3(th, tl, yh[gi][s], yl[gi][s], U[gi][q4]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int gi = 0; gi < NS; ++gi)
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    float x[8];
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj) x[jj] = U[gi][2 * s + (jj >> 2)][jj & 3];
+                    split_vec(x, uh[gi][s], ul[gi][s]);
+                }
+            if (OUT) {
+                // O += P U, then store the chunk's outputs for this column
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+#pragma unroll
+                    for (int s = 0; s < 2; ++s) {
+                        if (s > (q4 >> 1)) continue;
+                        const int ar = 16 * q4 + l16, ap = 32 * s + 8 * g4;
+                        const bf16x8 ph = at<bf16x8>(sm, OFF_P_HI + a128(ar, ap));
+                        const bf16x8 pl = at<bf16x8>(sm, OFF_P_LO + a128(ar, ap));
+                        O[q4] = mma3(ph, pl, uh[0][s], ul[0][s], O[q4]);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int tk = 16 * q4 + 4 * g4 + i;
+                        if (tk < L) a.o[((base + c0 + tk) * H + h) * kDim + col] = O[q4][i];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+
+        // ======== 9: S <- Diag(2^G_63) S + Ke^T U
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const float4 e4 = at<float4>(sm, OFF_EL + (16 * t + 4 * g4) * 4);
+#pragma unroll
+            for (int gi = 0; gi < NS; ++gi) {
+                S[gi][t][0] *= e4.x;
+                S[gi][t][1] *= e4.y;
+                S[gi][t][2] *= e4.z;
+                S[gi][t][3] *= e4.w;
+            }
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int ar = 16 * t + l16, ap = 32 * s + 8 * g4;
+                const bf16x8 eh = at<bf16x8>(sm, OFF_KE_HI + a128(ar, ap));
+                const bf16x8 el = at<bf16x8>(sm, OFF_KE_LO + a128(ar, ap));
+#pragma unroll
+                for (int gi = 0; gi < NS; ++gi) {
+                    if (NS == 2 && gi == 0 && !blkM) continue;
+                    S[gi][t] = mma3(eh, el, uh[gi][s], ul[gi][s], S[gi][t]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // ---------------- results
+    if (OUT) {
+        if (sg.j == sg.nseg - 1 && a.final_state) {
+            float* dst = a.final_state + unit * SS;
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[(16 * t + 4 * g4 + i) * kDim + col] = S[0][t][i];
+        }
+    } else if (sg.j == 0) {
+        float* dst = a.ws_start + ((z + 1) * H + h) * SS;
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[(16 * t + 4 * g4 + i) * kDim + col] = S[NS - 1][t][i];
+    } else {
+        float* dm = a.ws_maps + ((z * H + h) * 2) * SS;
+#pragma unroll
+        for (int gi = 0; gi < NS; ++gi)
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    dm[gi * SS + (16 * t + 4 * g4 + i) * kDim + col] = S[gi][t][i];
+    }
+}
+
+// Pass 2: entering states of segments 2.. of every sequence,
+// S_start(j+1) = M_j S_start(j) + R_j, for one 16-column slice of one
+// (sequence, head).  The 8 slices of a unit run on one XCD (they read the
+// same M_j).  fp32 on the vector ALUs.
+__global__ __launch_bounds__(256) void combine_kernel(const ScanArgs a)
+{
+    __shared__ float sv[kDim][16];
+    const int bid = blockIdx.x;
+    const int slice = (bid >> 3) & 7;
+    const int64_t unit = static_cast<int64_t>(bid >> 6) * 8 + (bid & 7);
+    const int H = a.H;
+    if (unit >= a.n_seq * H) return;
+    const int64_t n = unit / H;
+    const int h = static_cast<int>(unit - n * H);
+    int64_t z0, nseg;
+    if (!a.cu_seqlens) {
+        nseg = a.nseg_dense;
+        z0 = n * nseg;
+    } else {
+        z0 = a.seg_first[n];
+        nseg = static_cast<int64_t>(a.seg_first[n + 1]) - z0;
+    }
+    if (nseg < 3) return;
+    const int tid = threadIdx.x;
+    const int r = tid >> 1, c8 = 8 * (tid & 1);
+    const int cbase = 16 * slice;
+    {
+        const float* src = a.ws_start + ((z0 + 1) * H + h) * SS;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int idx = tid + 256 * e;
+            sv[idx >> 4][idx & 15] = src[(idx >> 4) * kDim + cbase + (idx & 15)];
+        }
+    }
+    __syncthreads();
+    for (int64_t jj = 1; jj + 1 < nseg; ++jj) {
+        const int64_t zz = z0 + jj;
+        const float* M = a.ws_maps + ((zz * H + h) * 2) * SS;
+        const float* R = M + SS;
+        float acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = R[r * kDim + cbase + c8 + e];
+        const float* mrow = M + r * kDim;
+        for (int k4 = 0; k4 < kDim / 4; ++k4) {
+            const float4 m4 = *reinterpret_cast<const float4*>(mrow + 4 * k4);
+            const float mk[4] = {m4.x, m4.y, m4.z, m4.w};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] += mk[kk] * sv[4 * k4 + kk][c8 + e];
+        }
+        __syncthreads();  // every thread has read sv
+        float* dst = a.ws_start + ((zz + 1) * H + h) * SS;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            dst[r * kDim + cbase + c8 + e] = acc[e];
+            sv[r][c8 + e] = acc[e];
+        }
+        __syncthreads();
+    }
+}
+
+// Packed sequences: first segment index of every sequence,
+// seg_first[n] = sum_{m < n} max(1, ceil(len_m / seg_len)).  One workgroup.
+__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* cu, int64_t n_seq,
+                                                    int64_t seg_len, int32_t* seg_first)
+{
+    __shared__ int64_t part[1024];
+    const int tid = threadIdx.x;
+    const int64_t lo = n_seq * tid / 1024, hi = n_seq * (tid + 1) / 1024;
+    auto count = [&](int64_t m) {
+        const int64_t len = static_cast<int64_t>(cu[m + 1]) - cu[m];
+        const int64_t c = (len + seg_len - 1) / seg_len;
+        return c > 1 ? c : int64_t(1);
+    };
+    int64_t s = 0;
+    for (int64_t m = lo; m < hi; ++m) s += count(m);
+    part[tid] = s;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int64_t x = tid >= off ? part[tid - off] : 0;
+        __syncthreads();
+        part[tid] += x;
+        __syncthreads();
+    }
+    int64_t run = part[tid] - s;  // exclusive prefix
+    for (int64_t m = lo; m < hi; ++m) {
+        seg_first[m] = static_cast<int32_t>(run);
+        run += count(m);
+    }
+    if (tid == 1023) seg_first[n_seq] = static_cast<int32_t>(part[1023]);
+}
+
+// ---------------- host side
+
+constexpr int64_t kMinSegment = 1024;
+int64_t g_forced_segment = 0;  // tokens per segment forced by kda_set_prefill_segment (0 = automatic)
+std::mutex g_pool_mutex;
+hipMemPool_t g_pools[64] = {};
+int g_cu_count[64] = {};
+
+// With KDA_DEBUG set in the environment, failed HIP calls are printed to stderr.
+void report(const char* what, hipError_t e)
+{
+    static const bool on = std::getenv("KDA_DEBUG") != nullptr;
+    if (on && e != hipSuccess) std::fprintf(stderr, "kda: %s: %s\n", what, hipGetErrorString(e));
+}
+
+int cu_count(int dev)
+{
+    std::lock_guard<std::mutex> lk(g_pool_mutex);
+    if (dev < 0 || dev >= 64) return 256;
+    if (!g_cu_count[dev]) {
+        int c = 0;
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+            c = 256;
+        g_cu_count[dev] = c;
+    }
+    return g_cu_count[dev];
+}
+
+// A memory pool per device that keeps freed blocks cached, so per-call
+// workspace allocations on the stream are cheap after the first.
+hipMemPool_t workspace_pool(int dev)
+{
+    std::lock_guard<std::mutex> lk(g_pool_mutex);
+    if (dev < 0 || dev >= 64) return nullptr;
+    if (!g_pools[dev]) {
+        hipMemPoolProps props = {};
+        props.allocType = hipMemAllocationTypePinned;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t p = nullptr;
+        hipError_t e = hipMemPoolCreate(&p, &props);
+        if (e != hipSuccess) {
+            report("hipMemPoolCreate", e);
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        uint64_t keep = UINT64_MAX;
+        e = hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep);
+        if (e != hipSuccess) {
+            report("hipMemPoolSetAttribute", e);
+            (void)hipGetLastError();
+        }
+        g_pools[dev] = p;
+    }
+    return g_pools[dev];
+}
+
+}  // namespace
+
+void set_prefill_segment(int64_t tokens) { g_forced_segment = tokens; }
+
+hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, const void* beta,
+                               const float* log_alpha, const int32_t* cu_seqlens, int64_t n_seq,
+                               int64_t T, int64_t T_total, int64_t H,
+                               const float* initial_state, float* o, float* final_state,
+                               hipStream_t stream)
+{
+    const int64_t units = n_seq * H;
+    if (units <= 0) return hipSuccess;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    report("hipGetDevice", e);
+    if (e != hipSuccess) return e;
+    report("earlier HIP error (cleared)", hipGetLastError());
+
+    ScanArgs a = {};
+    a.q = static_cast<const bf16_t*>(q);
+    a.k = static_cast<const bf16_t*>(k);
+    a.v = static_cast<const bf16_t*>(v);
+    a.beta = static_cast<const bf16_t*>(beta);
+    a.log_alpha = log_alpha;
+    a.cu_seqlens = cu_seqlens;
+    a.T = T;
+    a.n_seq = n_seq;
+    a.H = static_cast<int>(H);
+    a.initial_state = initial_state;
+    a.o = o;
+    a.final_state = final_state;
+
+    // Segment length: enough segments to give every CU about one segment of
+    // the total work, never shorter than kMinSegment tokens.
+    const int64_t rows = cu_seqlens ? T_total : n_seq * T;
+    int64_t seg = g_forced_segment;
+    if (seg <= 0) {
+        const int64_t per_cu = (rows * H + cu_count(dev) - 1) / cu_count(dev);
+        seg = std::max<int64_t>(kMinSegment, (per_cu + CH - 1) / CH * CH);
+    }
+    const int64_t longest_bound = cu_seqlens ? T_total : T;
+    const dim3 block(NT);
+
+    int64_t n_segs = 0;
+    size_t ws_bytes = 0, plan_bytes = 0;
+    if (longest_bound > seg) {
+        n_segs = cu_seqlens ? n_seq + (T_total + seg - 1) / seg : n_seq * ((T + seg - 1) / seg);
+        plan_bytes = cu_seqlens ? ((static_cast<size_t>(n_seq) + 1) * 4 + 255) / 256 * 256 : 0;
+        ws_bytes = plan_bytes + static_cast<size_t>(n_segs) * H * 3 * SS * sizeof(float);
+    }
+    void* ws = nullptr;
+    if (ws_bytes) {
+        hipMemPool_t pool = workspace_pool(dev);
+        if (pool) {
+            e = hipMallocFromPoolAsync(&ws, ws_bytes, pool, stream);
+            if (e != hipSuccess) {
+                report("hipMallocFromPoolAsync", e);
+                (void)hipGetLastError();
+                ws = nullptr;  // fall back to one segment per sequence
+            }
+        }
+    }
+    if (!ws) {
+        // one segment per sequence: pass 3 alone from the given initial states
+        a.seg_len = 0;
+        a.nseg_dense = 1;
+        a.n_segs = n_seq;
+        a.seg_first = nullptr;
+        const dim3 grid(static_cast<unsigned>(n_seq * H));
+        hipLaunchKernelGGL(scan_kernel<true>, grid, block, 0, stream, a);
+        e = hipGetLastError();
+        report("prefill scan launch", e);
+        return e;
+    }
+
+    a.seg_len = seg;
+    a.n_segs = n_segs;
+    a.nseg_dense = cu_seqlens ? 0 : (T + seg - 1) / seg;
+    char* w = static_cast<char*>(ws);
+    if (cu_seqlens) {
+        a.seg_first = reinterpret_cast<int32_t*>(w);
+        hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens, n_seq, seg,
+                           const_cast<int32_t*>(a.seg_first));
+        e = hipGetLastError();
+        report("segment plan launch", e);
+        if (e != hipSuccess) {
+            (void)hipFreeAsync(ws, stream);
+            return e;
+        }
+    }
+    a.ws_maps = reinterpret_cast<float*>(w + plan_bytes);
+    a.ws_start = a.ws_maps + static_cast<size_t>(n_segs) * H * 2 * SS;
+
+    const dim3 grid(static_cast<unsigned>(n_segs * H));
+    hipLaunchKernelGGL(scan_kernel<false>, grid, block, 0, stream, a);
+    e = hipGetLastError();
+    report("segment map launch", e);
+    if (e == hipSuccess) {
+        const dim3 cgrid(static_cast<unsigned>((units + 7) / 8 * 64));
+        hipLaunchKernelGGL(combine_kernel, cgrid, dim3(256), 0, stream, a);
+        e = hipGetLastError();
+        report("segment combine launch", e);
+    }
+    if (e == hipSuccess) {
+        hipLaunchKernelGGL(scan_kernel<true>, grid, block, 0, stream, a);
+        e = hipGetLastError();
+        report("prefill scan launch", e);
+    }
+    const hipError_t f = hipFreeAsync(ws, stream);
+    report("hipFreeAsync", f);
+    return e != hipSuccess ? e : f;
+}
+
+}  // namespace kda

@@ -29,8 +29,12 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - All tensor pointers are DEVICE pointers (e.g. torch CUDA tensors), owned by
- *    the caller.  The library allocates nothing and keeps no mutable global
- *    state; calls are re-entrant and thread-safe.
+ *    the caller.  Decode allocates nothing.  A prefill whose sequences are
+ *    long enough to be cut into segments (see kda_set_prefill_segment) takes
+ *    a temporary workspace, allocated and freed in stream order on `stream`
+ *    from a memory pool the library keeps per device (no synchronisation);
+ *    if that allocation fails the call runs unsegmented instead.  Calls are
+ *    re-entrant and thread-safe.
  *  - Layouts are dense row-major, innermost dimension last:
  *        q, k, log_alpha : [rows, H, d_k]      v, o : [rows, H, d_v]
  *        beta            : [rows, H]
@@ -125,6 +129,20 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v, const vo
                            const float *log_alpha, float *state, float *o,
                            int64_t N, int64_t H, int64_t d_k, int64_t d_v,
                            kda_dtype in_dtype, void *stream);
+
+/*
+ * Tuning and testing knob for the bf16 prefill (process-wide; set it while no
+ * prefill call is running).  The blockwise prefill runs one workgroup per
+ * (sequence, head, segment); a sequence longer than `tokens` is cut into
+ * segments of `tokens` tokens (the last one shorter), processed in parallel
+ * and stitched together through their affine state maps ("blockwise and
+ * context-parallel" in "Kimi K3 -- the architecture and infrastructure,
+ * explained", section "Kimi Delta Attention: the load-bearing choice").
+ * 0 (the default) picks the length from the problem size and the number of
+ * compute units.  tokens must be 0 or a positive multiple of 64, else
+ * KDA_ERR_SHAPE.  Results do not depend on it beyond rounding.
+ */
+kda_status kda_set_prefill_segment(int64_t tokens);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char *kda_status_str(kda_status status);

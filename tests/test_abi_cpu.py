@@ -38,7 +38,7 @@ def _declared():
 def test_exports_match_header(lib):
     declared = _declared()
     assert declared == {"kda_prefill", "kda_varlen_prefill", "kda_decode_step",
-                        "kda_status_str", "kda_abi_version"}
+                        "kda_set_prefill_segment", "kda_status_str", "kda_abi_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", kda._binding.LIBRARY],
                          capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r" T (kda_\w+)", out))
@@ -126,3 +126,12 @@ def test_binding_rejects_cpu_tensors(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(ImportError, match="build"):
         kda.load_library(str(tmp_path / "libkda.so"))
+
+
+def test_prefill_segment_knob(lib):
+    """The segment-length knob accepts 0 and positive multiples of 64 only."""
+    assert lib.kda_set_prefill_segment(64) == OK
+    assert lib.kda_set_prefill_segment(4096) == OK
+    assert lib.kda_set_prefill_segment(0) == OK
+    assert lib.kda_set_prefill_segment(100) == SHAPE
+    assert lib.kda_set_prefill_segment(-64) == SHAPE
