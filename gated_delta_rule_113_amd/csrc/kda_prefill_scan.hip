@@ -572,6 +572,22 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
         if (kh == 1) {
             const int r = 16 * rb + l16;
             const float br = at<float>(sm, OFF_BETA + 4 * r);
+            // P_rr = q_r . k_r carries no decay; it is summed in fp32 here, since
+            // when it dominates o_r (a token right after a zero state) its
+            // cancellation would expose the ~16-bit split operands
+            float qk = 0.f;
+            if (OUT) {
+#pragma unroll
+                for (int part = 0; part < 4; ++part) {
+                    const int p0 = 32 * g4 + 8 * part;
+                    const bf16x8 kk = at<bf16x8>(sm, OFF_K + a256(r, p0));
+                    const bf16x8 qq = at<bf16x8>(sm, OFF_Q + a256(r, p0));
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj) qk += bfw(qq[jj]) * bfw(kk[jj]);
+                }
+                qk += __shfl_xor(qk, 16);
+                qk += __shfl_xor(qk, 32);
+            }
 #pragma unroll
             for (int ib = 0; ib < 4; ++ib) {
                 if (ib <= rb) {
@@ -590,7 +606,7 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             const int ti = 16 * ib + 4 * g4 + i;
-                            x[i] = ti <= r ? pp[i] + accP[ib][i] : 0.f;
+                            x[i] = ti < r ? pp[i] + accP[ib][i] : (ti == r ? qk : 0.f);
                         }
                         bf16x4 hi, lo;
                         split_vec(x, hi, lo);
