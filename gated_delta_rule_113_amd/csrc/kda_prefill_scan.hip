@@ -62,6 +62,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <mutex>
+#include <type_traits>
 
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
@@ -91,9 +92,8 @@ constexpr int OFF_K = 16384;
 constexpr int OFF_G = 32768;
 constexpr int R0_BYTES = 32768 + CH * G_LD * 4;
 constexpr int OFF_KT_HI = 0, OFF_KT_LO = 16384, OFF_QT_HI = 32768, OFF_QT_LO = 49152;
-// R1: quad sums of the decay scan; then N = Diag(b) A and T (fp32); later Ke^T.
+// R1: N = Diag(b) A and T (fp32) during the UT solve; later Ke^T.
 constexpr int OFF_R1 = R0_BYTES;
-constexpr int OFF_QSUM = OFF_R1;
 constexpr int OFF_N = OFF_R1;
 constexpr int OFF_TF = OFF_R1 + CH * N_LD * 4;
 constexpr int OFF_KE_HI = OFF_R1, OFF_KE_LO = OFF_R1 + 16384;
@@ -337,11 +337,14 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
                 pk[m] = pv[m] = pq[m] = make_uint4(0, 0, 0, 0);
             }
         }
+        // log_alpha: wave w takes channels 16w..16w+15; lane = (token group
+        // (lane >> 2): tokens 4tg..4tg+3, channel quad lane & 3)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const int r = 4 * (tid >> 5) + m;
+            const int r = 4 * ((tid & 63) >> 2) + m;
             pla[m] = r < L ? *reinterpret_cast<const float4*>(
-                                 a.log_alpha + ((base + c0 + r) * H + h) * kDim + 4 * (tid & 31))
+                                 a.log_alpha + ((base + c0 + r) * H + h) * kDim +
+                                 16 * (tid >> 6) + 4 * (tid & 3))
                            : make_float4(0.f, 0.f, 0.f, 0.f);
         }
         if (tid < CH) pb = tid < L ? widen(a.beta[(base + c0 + tid) * H + h]) : 0.f;
@@ -365,8 +368,7 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
         const int cq = tid & 31;                 // natural channel quad
         const int pq4 = perm(4 * cq);            // its position in the permuted order
 
-        // ======== 0: stage the chunk; in-register scan of the log2-decay over 4 tokens
-        float4 gp[4];
+        // ======== 0: stage the chunk; scan of the log2-decay in registers
         {
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
@@ -382,6 +384,10 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
                 at<uint4>(sm, OFF_V + a256(r, c8)) = pv[m];
             }
             if (tid < CH) at<float>(sm, OFF_BETA + 4 * tid) = pb;
+            // this lane: channels 16*wave + 4*(lane&3) .. +3, tokens 4*tg .. 4*tg+3
+            const int tg = lane >> 2;
+            const int chn = 16 * wave + 4 * (lane & 3);
+            float4 gp[4];
             float4 run = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
@@ -390,37 +396,41 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
                                   run.w + x.w * kLog2e);
                 gp[m] = run;
             }
-            at<float4>(sm, OFF_QSUM + (tq * kDim + pq4) * 4) = run;
-        }
-        __syncthreads();
-
-        // ======== 1: finish the scan across token quads; chunk-end decay
-        {
-            float4 off = make_float4(0.f, 0.f, 0.f, 0.f);
+            // inclusive scan of the 4-token sums over the 16 token groups (lanes 4 apart)
+            float4 inc = run;
 #pragma unroll
-            for (int u = 0; u < 15; ++u)
-                if (u < tq) off = f4add(off, at<float4>(sm, OFF_QSUM + (u * kDim + pq4) * 4));
+            for (int off = 4; off < 64; off <<= 1) {
+                const float4 y = make_float4(__shfl_up(inc.x, off), __shfl_up(inc.y, off),
+                                             __shfl_up(inc.z, off), __shfl_up(inc.w, off));
+                if (lane >= off) inc = f4add(inc, y);
+            }
+            const float4 exc = make_float4(inc.x - run.x, inc.y - run.y, inc.z - run.z, inc.w - run.w);
+            const int pc = perm(chn);
 #pragma unroll
             for (int m = 0; m < 4; ++m)
-                at<float4>(sm, OFF_G + ((4 * tq + m) * G_LD + pq4) * 4) = f4add(gp[m], off);
-            if (tq == 15) {
-                const float4 g63 = f4add(gp[3], off);
-                at<float4>(sm, OFF_EL + 16 * cq) =
-                    make_float4(ex2(g63.x), ex2(g63.y), ex2(g63.z), ex2(g63.w));
-            }
-        }
-        __syncthreads();
-
-        // ======== 2: per row block, is the mid-block reference safe for every channel?
-        {
-            const int rb = tid >> 7, p = tid & 127;
-            const float* G = &at<float>(sm, OFF_G);
-            const float gs = rb ? G[(16 * rb - 1) * G_LD + p] : 0.f;
-            const float gm = G[(16 * rb + 7) * G_LD + p];
-            const float ge = G[(16 * rb + 15) * G_LD + p];
-            const bool bad = (gs - gm > kSafeLog2) || (gm - ge > kSafeLog2);
-            const uint64_t any = __ballot(bad);
-            if (lane == 0) at<int>(sm, OFF_UNSAFE + 4 * wave) = any != 0;
+                at<float4>(sm, OFF_G + ((4 * tg + m) * G_LD + pc) * 4) = f4add(gp[m], exc);
+            if (tg == 15)
+                at<float4>(sm, OFF_EL + 4 * chn) =
+                    make_float4(ex2(inc.x), ex2(inc.y), ex2(inc.z), ex2(inc.w));
+            // Per row block rb, is the mid-block reference safe for every channel?
+            // inc is G at token 4tg+3; the lane with tg = 4rb+3 compares G at tokens
+            // 16rb-1, 16rb+7 and 16rb+15.
+            const float4 gm = make_float4(__shfl_up(inc.x, 8), __shfl_up(inc.y, 8),
+                                          __shfl_up(inc.z, 8), __shfl_up(inc.w, 8));
+            float4 gs = make_float4(__shfl_up(inc.x, 16), __shfl_up(inc.y, 16),
+                                    __shfl_up(inc.z, 16), __shfl_up(inc.w, 16));
+            if (tg < 4) gs = make_float4(0.f, 0.f, 0.f, 0.f);
+            const bool bad = (tg & 3) == 3 &&
+                             (gs.x - gm.x > kSafeLog2 || gm.x - inc.x > kSafeLog2 ||
+                              gs.y - gm.y > kSafeLog2 || gm.y - inc.y > kSafeLog2 ||
+                              gs.z - gm.z > kSafeLog2 || gm.z - inc.z > kSafeLog2 ||
+                              gs.w - gm.w > kSafeLog2 || gm.w - inc.w > kSafeLog2);
+            const uint64_t bm = __ballot(bad);
+            int flags = 0;
+#pragma unroll
+            for (int rbi = 0; rbi < 4; ++rbi)
+                if ((bm >> (16 * rbi + 12)) & 0xFull) flags |= 1 << rbi;
+            if (lane == 0) at<int>(sm, OFF_UNSAFE + 4 * wave) = flags;
         }
         __syncthreads();
 
@@ -429,9 +439,13 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
         const int kh = wave >> 2;
         const int rb = kh ? 3 - (wave & 3) : (wave & 3);
         f32x4 accA[4], accP[4];
+        float qk = 0.f;
         {
             const float* G = &at<float>(sm, OFF_G);
-            const bool uns = at<int>(sm, OFF_UNSAFE + 8 * rb) | at<int>(sm, OFF_UNSAFE + 8 * rb + 4);
+            int fl = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) fl |= at<int>(sm, OFF_UNSAFE + 4 * w);
+            const bool uns = (fl >> rb) & 1;
             const int r = 16 * rb + l16;  // this lane's token in row-operand position
             bf16x8 fkh[2], fkl[2], fqh[2], fql[2], cdh[2], cdl[2];
             float rho[2][8];
@@ -523,6 +537,21 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
                     }
                 }
             }
+            // P_rr = q_r . k_r carries no decay; it is summed in fp32 here, since
+            // when it dominates o_r (a token right after a zero state) its
+            // cancellation would expose the ~16-bit split operands
+            if (OUT && kh == 1) {
+#pragma unroll
+                for (int part = 0; part < 4; ++part) {
+                    const int p0 = 32 * g4 + 8 * part;
+                    const bf16x8 kk = at<bf16x8>(sm, OFF_K + a256(r, p0));
+                    const bf16x8 qq = at<bf16x8>(sm, OFF_Q + a256(r, p0));
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj) qk += bfw(qq[jj]) * bfw(kk[jj]);
+                }
+                qk += __shfl_xor(qk, 16);
+                qk += __shfl_xor(qk, 32);
+            }
             // accA[ib][i] = A[r][16ib+4g4+i] over this channel half; the first
             // half parks its partial sums where N and T will live.
             if (kh == 0) {
@@ -572,22 +601,7 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
         if (kh == 1) {
             const int r = 16 * rb + l16;
             const float br = at<float>(sm, OFF_BETA + 4 * r);
-            // P_rr = q_r . k_r carries no decay; it is summed in fp32 here, since
-            // when it dominates o_r (a token right after a zero state) its
-            // cancellation would expose the ~16-bit split operands
-            float qk = 0.f;
-            if (OUT) {
-#pragma unroll
-                for (int part = 0; part < 4; ++part) {
-                    const int p0 = 32 * g4 + 8 * part;
-                    const bf16x8 kk = at<bf16x8>(sm, OFF_K + a256(r, p0));
-                    const bf16x8 qq = at<bf16x8>(sm, OFF_Q + a256(r, p0));
-#pragma unroll
-                    for (int jj = 0; jj < 8; ++jj) qk += bfw(qq[jj]) * bfw(kk[jj]);
-                }
-                qk += __shfl_xor(qk, 16);
-                qk += __shfl_xor(qk, 32);
-            }
+
 #pragma unroll
             for (int ib = 0; ib < 4; ++ib) {
                 if (ib <= rb) {
@@ -625,84 +639,105 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
         }
         __syncthreads();
 
+        // T is consumed as a split A operand: [token][token] bf16 hi and lo,
+        // column index permuted like every other k-slot index.
+        auto put_t = [&](int row, int tok, float x) {
+            const __bf16 hb = (__bf16)x;
+            const int off = a128(row, perm(tok));
+            at<__bf16>(sm, OFF_T_HI + off) = hb;
+            at<__bf16>(sm, OFF_T_LO + off) = (__bf16)(x - (float)hb);
+        };
+
         // ======== 5: diagonal 16x16 blocks of T = (I + N)^-1 by forward
-        //             substitution (waves 0-3); then every thread forms its
-        //             share of the decayed operands.
+        //             substitution (waves 0-3; lane (jc, p) holds rows 4p..4p+3
+        //             of column jc); then every thread forms its share of the
+        //             decayed operands.
         if (wave < 4) {
             const int b = wave, jc = lane >> 2, p = lane & 3;
-            const float* N = &at<float>(sm, OFF_N);
-            float nv[16][4];
+            float4 nv[16];
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr)
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const int i = p + 4 * m;
-                    nv[rr][m] = i < rr ? N[(16 * b + rr) * N_LD + 16 * b + i] : 0.f;
-                }
-            float tv[4] = {0.f, 0.f, 0.f, 0.f};  // T[16b + p + 4m][16b + jc]
+                nv[rr] = at<float4>(sm, OFF_N + ((16 * b + rr) * N_LD + 16 * b + 4 * p) * 4);
+            float tv[4] = {0.f, 0.f, 0.f, 0.f};  // T[16b + 4p + m][16b + jc]
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) {
-                float s = nv[rr][0] * tv[0] + nv[rr][1] * tv[1] + nv[rr][2] * tv[2] + nv[rr][3] * tv[3];
+                // N is strictly lower, so entries at or right of the diagonal are zero
+                float s = nv[rr].x * tv[0] + nv[rr].y * tv[1] + nv[rr].z * tv[2] + nv[rr].w * tv[3];
                 s += __shfl_xor(s, 1);
                 s += __shfl_xor(s, 2);
                 const float tr = (rr == jc ? 1.f : 0.f) - s;
-                if (p == (rr & 3)) tv[rr >> 2] = tr;
+                if (p == (rr >> 2)) tv[rr & 3] = tr;
             }
             float* Tf = &at<float>(sm, OFF_TF);
 #pragma unroll
-            for (int m = 0; m < 4; ++m) Tf[(16 * b + p + 4 * m) * N_LD + 16 * b + jc] = tv[m];
+            for (int m = 0; m < 4; ++m) {
+                Tf[(16 * b + 4 * p + m) * N_LD + 16 * b + jc] = tv[m];
+                put_t(16 * b + 4 * p + m, 16 * b + jc, tv[m]);
+            }
         }
         form();
         __syncthreads();
 
-        // ======== 6: off-diagonal blocks, T[b][b-d] = -T[b][b] sum_m N[b][m] T[m][b-d]
+        // ======== 6: off-diagonal blocks by block column a (wave a, no barrier):
+        //             T[b][a] = -T[b][b] sum_{m=a}^{b-1} N[b][m] T[m][a].  The
+        //             blocks of one column stay in this wave's registers, in
+        //             accumulator layout, which is the B layout of the next
+        //             16x16x16 product.  Meanwhile the other waves store Kt, Qt
+        //             (q, k and G are dead) and the zero upper tiles that share
+        //             a 32-token step with a diagonal tile.
+        {
+            auto column = [&](auto ac) {
+                constexpr int A = decltype(ac)::value;
+                bf16x4 bh[4], bl[4];
+                {
+                    float da[4];
 #pragma unroll
-        for (int d = 1; d < 4; ++d) {
-            const int b = wave;
-            if (b < 4 && b >= d) {
-                const float* N = &at<float>(sm, OFF_N);
-                float* Tf = &at<float>(sm, OFF_TF);
-                f32x4 zacc = {0.f, 0.f, 0.f, 0.f};
-                for (int m = b - d; m < b; ++m) {
-                    float an[4], bt[4];
+                    for (int e = 0; e < 4; ++e)
+                        da[e] = at<float>(sm, OFF_TF + ((16 * A + 4 * g4 + e) * N_LD + 16 * A + l16) * 4);
+                    split_vec(da, bh[A], bl[A]);
+                }
+#pragma unroll
+                for (int b = A + 1; b < 4; ++b) {
+                    f32x4 zacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int m = A; m < b; ++m) {
+                        const float4 n4 = at<float4>(sm, OFF_N + ((16 * b + l16) * N_LD + 16 * m + 4 * g4) * 4);
+                        const float an[4] = {n4.x, n4.y, n4.z, n4.w};
+                        bf16x4 ah, al;
+                        split_vec(an, ah, al);
+                        zacc = mma16x3(ah, al, bh[m], bl[m], zacc);
+                    }
+                    const float4 d4 = at<float4>(sm, OFF_TF + ((16 * b + l16) * N_LD + 16 * b + 4 * g4) * 4);
+                    const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+                    const float zz[4] = {zacc[0], zacc[1], zacc[2], zacc[3]};
+                    bf16x4 ah, al, zh, zl;
+                    split_vec(dd, ah, al);
+                    split_vec(zz, zh, zl);
+                    f32x4 tr = {0.f, 0.f, 0.f, 0.f};
+                    tr = mma16x3(ah, al, zh, zl, tr);
+                    const float tb[4] = {-tr[0], -tr[1], -tr[2], -tr[3]};
+                    split_vec(tb, bh[b], bl[b]);
+                    // tb[e] = T[16b + 4g4 + e][16A + l16]
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        an[e] = N[(16 * b + l16) * N_LD + 16 * m + 4 * g4 + e];
-                        bt[e] = Tf[(16 * m + 4 * g4 + e) * N_LD + 16 * (b - d) + l16];
+                        const int off = a128(16 * b + 4 * g4 + e, perm(16 * A + l16));
+                        at<__bf16>(sm, OFF_T_HI + off) = bh[b][e];
+                        at<__bf16>(sm, OFF_T_LO + off) = bl[b][e];
                     }
-                    bf16x4 ah, al, bh, bl;
-                    split_vec(an, ah, al);
-                    split_vec(bt, bh, bl);
-                    zacc = mma16x3(ah, al, bh, bl, zacc);
                 }
-                float tb[4], zz[4] = {zacc[0], zacc[1], zacc[2], zacc[3]};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) tb[e] = Tf[(16 * b + l16) * N_LD + 16 * b + 4 * g4 + e];
-                bf16x4 ah, al, bh, bl;
-                split_vec(tb, ah, al);
-                split_vec(zz, bh, bl);
-                f32x4 tr = {0.f, 0.f, 0.f, 0.f};
-                tr = mma16x3(ah, al, bh, bl, tr);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) Tf[(16 * b + 4 * g4 + e) * N_LD + 16 * (b - d) + l16] = -tr[e];
+            };
+            if (wave == 0) column(std::integral_constant<int, 0>{});
+            else if (wave == 1) column(std::integral_constant<int, 1>{});
+            else if (wave == 2) column(std::integral_constant<int, 2>{});
+            else if (wave == 3 || wave == 4) {
+                // tile (0,1) or (2,3): rows 16rb.., tokens 16rb+16..; lane = (row, 4-token group)
+                const int rb0 = wave == 3 ? 0 : 2;
+                const int r = 16 * rb0 + (lane >> 2);
+                const int pz = perm(16 * rb0 + 16 + 4 * (lane & 3));
+                const bf16x4 zz = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+                at<bf16x4>(sm, OFF_T_HI + a128(r, pz)) = zz;
+                at<bf16x4>(sm, OFF_T_LO + a128(r, pz)) = zz;
             }
-            __syncthreads();
-        }
-
-        // ======== 7: T as a split operand; Kt and Qt into R0 (q, k, G are dead)
-        {
-            const int r = tid >> 3, c8 = 8 * (tid & 7);
-            const float* Tf = &at<float>(sm, OFF_TF);
-            float x[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int i = unperm(c8 + e);
-                x[e] = (i >> 4) <= (r >> 4) ? Tf[r * N_LD + i] : 0.f;
-            }
-            bf16x8 hi, lo;
-            split_vec(x, hi, lo);
-            at<bf16x8>(sm, OFF_T_HI + a128(r, c8)) = hi;
-            at<bf16x8>(sm, OFF_T_LO + a128(r, c8)) = lo;
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int rr = 4 * tq + m;
@@ -735,11 +770,28 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
                 for (int q4 = 0; q4 < 4; ++q4) X[gi][q4] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) O[q4] = f32x4{0.f, 0.f, 0.f, 0.f};
-            // X = Kt S, then O = Qt S (two passes keep fewer fragments live)
+            // X = Kt S, then O = Qt S (two passes keep fewer fragments live).
+            // The A fragments of step s+1 are requested before the products of
+            // step s; the scheduling barriers keep the compiler from sinking
+            // those reads back next to their use.
 #pragma unroll
             for (int pass = 0; pass < (OUT ? 2 : 1); ++pass) {
+                const int oh = pass == 0 ? OFF_KT_HI : OFF_QT_HI;
+                const int ol = pass == 0 ? OFF_KT_LO : OFF_QT_LO;
+                bf16x8 fh[2][4], fl[2][4];
+                auto fetch = [&](int s, int buf) {
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const int off = a256(16 * q4 + l16, 32 * s + 8 * g4);
+                        fh[buf][q4] = at<bf16x8>(sm, oh + off);
+                        fl[buf][q4] = at<bf16x8>(sm, ol + off);
+                    }
+                };
+                fetch(0, 0);
 #pragma unroll
                 for (int s = 0; s < 4; ++s) {
+                    if (s + 1 < 4) fetch(s + 1, (s + 1) & 1);
+                    __builtin_amdgcn_sched_barrier(0);
                     bf16x8 sh[NS], sl[NS];
 #pragma unroll
                     for (int gi = 0; gi < NS; ++gi) {
@@ -750,21 +802,17 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
                     }
 #pragma unroll
                     for (int q4 = 0; q4 < 4; ++q4) {
-                        const int ar = 16 * q4 + l16, ap = 32 * s + 8 * g4;
                         if (pass == 0) {
-                            const bf16x8 kh_ = at<bf16x8>(sm, OFF_KT_HI + a256(ar, ap));
-                            const bf16x8 kl_ = at<bf16x8>(sm, OFF_KT_LO + a256(ar, ap));
 #pragma unroll
                             for (int gi = 0; gi < NS; ++gi) {
                                 if (NS == 2 && gi == 0 && !blkM) continue;
-                                X[gi][q4] = mma3(kh_, kl_, sh[gi], sl[gi], X[gi][q4]);
+                                X[gi][q4] = mma3(fh[s & 1][q4], fl[s & 1][q4], sh[gi], sl[gi], X[gi][q4]);
                             }
                         } else {
-                            const bf16x8 qh_ = at<bf16x8>(sm, OFF_QT_HI + a256(ar, ap));
-                            const bf16x8 ql_ = at<bf16x8>(sm, OFF_QT_LO + a256(ar, ap));
-                            O[q4] = mma3(qh_, ql_, sh[0], sl[0], O[q4]);
+                            O[q4] = mma3(fh[s & 1][q4], fl[s & 1][q4], sh[0], sl[0], O[q4]);
                         }
                     }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
             // inputs of the next chunk, in flight during the rest of this one
@@ -772,6 +820,21 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
                 const int64_t c1 = c0 + CH;
                 prefetch(c1, static_cast<int>(std::min<int64_t>(CH, seg_tokens - c1)), tid);
             }
+            // T fragments for U = T Y, requested before the vector work on Y
+            bf16x8 tfh[6], tfl[6];  // (q4, s) pairs with s <= q4/2, in order
+            {
+                int n = 0;
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+                    for (int s = 0; s <= (q4 >> 1); ++s) {
+                        const int off = a128(16 * q4 + l16, 32 * s + 8 * g4);
+                        tfh[n] = at<bf16x8>(sm, OFF_T_HI + off);
+                        tfl[n] = at<bf16x8>(sm, OFF_T_LO + off);
+                        ++n;
+                    }
+            }
+            __builtin_amdgcn_sched_barrier(0);
             // Y = Diag(b) (V - X), split as B operands over tokens
             bf16x8 yh[NS][2], yl[NS][2];
             {
@@ -801,23 +864,38 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
             }
             // U = T Y (T is block lower triangular: row block q4 needs steps s <= q4/2)
             f32x4 U[NS][4];
+            {
+                int n = 0;
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
+                for (int q4 = 0; q4 < 4; ++q4) {
 #pragma unroll
-                for (int gi = 0; gi < NS; ++gi) U[gi][q4] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (int gi = 0; gi < NS; ++gi) U[gi][q4] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    if (s > (q4 >> 1)) continue;
-                    const int ar = 16 * q4 + l16, ap = 32 * s + 8 * g4;
-                    const bf16x8 th = at<bf16x8>(sm, OFF_T_HI + a128(ar, ap));
-                    const bf16x8 tl = at<bf16x8>(sm, OFF_T_LO + a128(ar, ap));
+                    for (int s = 0; s <= (q4 >> 1); ++s) {
 #pragma unroll
-                    for (int gi = 0; gi < NS; ++gi) {
-                        if (NS == 2 && gi == 0 && !blkM) continue;
-                        U[gi][q4] = mma3(th, tl, yh[gi][s], yl[gi][s], U[gi][q4]);
+                        for (int gi = 0; gi < NS; ++gi) {
+                            if (NS == 2 && gi == 0 && !blkM) continue;
+                            U[gi][q4] = mma3(tfh[n], tfl[n], yh[gi][s], yl[gi][s], U[gi][q4]);
+                        }
+                        ++n;
                     }
                 }
             }
+            // P fragments for O += P U, requested before the vector work on U
+            bf16x8 pfh[6], pfl[6];
+            if (OUT) {
+                int n = 0;
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+                    for (int s = 0; s <= (q4 >> 1); ++s) {
+                        const int off = a128(16 * q4 + l16, 32 * s + 8 * g4);
+                        pfh[n] = at<bf16x8>(sm, OFF_P_HI + off);
+                        pfl[n] = at<bf16x8>(sm, OFF_P_LO + off);
+                        ++n;
+                    }
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int gi = 0; gi < NS; ++gi)
 #pragma unroll
@@ -829,15 +907,13 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
                 }
             if (OUT) {
                 // O += P U, then store the chunk's outputs for this column
+                int n = 0;
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
 #pragma unroll
-                    for (int s = 0; s < 2; ++s) {
-                        if (s > (q4 >> 1)) continue;
-                        const int ar = 16 * q4 + l16, ap = 32 * s + 8 * g4;
-                        const bf16x8 ph = at<bf16x8>(sm, OFF_P_HI + a128(ar, ap));
-                        const bf16x8 pl = at<bf16x8>(sm, OFF_P_LO + a128(ar, ap));
-                        O[q4] = mma3(ph, pl, uh[0][s], ul[0][s], O[q4]);
+                    for (int s = 0; s <= (q4 >> 1); ++s) {
+                        O[q4] = mma3(pfh[n], pfl[n], uh[0][s], ul[0][s], O[q4]);
+                        ++n;
                     }
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -849,27 +925,40 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
         }
         __syncthreads();
 
-        // ======== 9: S <- Diag(2^G_63) S + Ke^T U
+        // ======== 9: S <- Diag(2^G_63) S + Ke^T U (fragments of tile t+1 in
+        //             flight during the products of tile t)
+        {
+            bf16x8 eh[2][2], el[2][2];
+            auto fetch = [&](int t, int buf) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const float4 e4 = at<float4>(sm, OFF_EL + (16 * t + 4 * g4) * 4);
+                for (int s = 0; s < 2; ++s) {
+                    const int off = a128(16 * t + l16, 32 * s + 8 * g4);
+                    eh[buf][s] = at<bf16x8>(sm, OFF_KE_HI + off);
+                    el[buf][s] = at<bf16x8>(sm, OFF_KE_LO + off);
+                }
+            };
+            fetch(0, 0);
 #pragma unroll
-            for (int gi = 0; gi < NS; ++gi) {
-                S[gi][t][0] *= e4.x;
-                S[gi][t][1] *= e4.y;
-                S[gi][t][2] *= e4.z;
-                S[gi][t][3] *= e4.w;
-            }
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int ar = 16 * t + l16, ap = 32 * s + 8 * g4;
-                const bf16x8 eh = at<bf16x8>(sm, OFF_KE_HI + a128(ar, ap));
-                const bf16x8 el = at<bf16x8>(sm, OFF_KE_LO + a128(ar, ap));
+            for (int t = 0; t < 8; ++t) {
+                if (t + 1 < 8) fetch(t + 1, (t + 1) & 1);
+                const float4 e4 = at<float4>(sm, OFF_EL + (16 * t + 4 * g4) * 4);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int gi = 0; gi < NS; ++gi) {
-                    if (NS == 2 && gi == 0 && !blkM) continue;
-                    S[gi][t] = mma3(eh, el, uh[gi][s], ul[gi][s], S[gi][t]);
+                    S[gi][t][0] *= e4.x;
+                    S[gi][t][1] *= e4.y;
+                    S[gi][t][2] *= e4.z;
+                    S[gi][t][3] *= e4.w;
                 }
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+#pragma unroll
+                    for (int gi = 0; gi < NS; ++gi) {
+                        if (NS == 2 && gi == 0 && !blkM) continue;
+                        S[gi][t] = mma3(eh[t & 1][s], el[t & 1][s], uh[gi][s], ul[gi][s], S[gi][t]);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         __syncthreads();
