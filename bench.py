@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--batch", type=int, default=64)
     ap.add_argument("--heads", type=int, default=32)
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
+    ap.add_argument("--eager", action="store_true",
+                    help="time direct decode calls instead of a replayed HIP graph of them")
     ap.add_argument("--prefill-T", type=int, default=32768)
     ap.add_argument("--prefill-reps", type=int, default=5)
     ap.add_argument("--cpu-steps", type=int, default=1024,
@@ -136,20 +138,49 @@ def main():
     def step(s, st):
         kda.kda_decode_step(q[s], k[s], v[s], beta[s], la[s], st, out=o)
 
+    # The timed steps are captured once into a HIP graph and replayed, so the
+    # per-call host cost of the Python binding does not leave the GPU idle
+    # between steps (the decode entry point allocates nothing and issues only
+    # its kernel, so it can be captured).  --eager times direct calls instead.
+    graph = None
+    if not args.eager:
+        try:
+            side = torch.cuda.Stream(dev)
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                step(0, state)  # warm the binding on the capture stream
+            stream.wait_stream(side)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for s in range(K):
+                    step(s % n_gen, state)
+            torch.cuda.synchronize()
+        except Exception as e:  # fall back to direct calls
+            log(f"graph capture failed ({e}); timing direct calls")
+            graph = None
+
+    def run_steps(count, first=0):
+        if graph is not None and count == K and first == 0:
+            graph.replay()
+        else:
+            for s in range(first, first + count):
+                step(s % n_gen, state)
+
     log(f"warmup {W} steps")
-    for s in range(W):
-        step(s % n_gen, state)
+    run_steps(W)
+    if graph is not None:
+        graph.replay()  # one untimed replay of the captured steps
     torch.cuda.synchronize()
     state.copy_(state0)
     torch.cuda.synchronize()
 
-    log(f"timing {K} steps")
+    log(f"timing {K} steps ({'graph replay' if graph is not None else 'direct calls'})")
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record(stream)
-    for s in range(K):
-        step(s % n_gen, state)
+    run_steps(K)
     ev1.record(stream)
     torch.cuda.synchronize()
     total_ms = ev0.elapsed_time(ev1)
@@ -161,18 +192,6 @@ def main():
         raise RuntimeError("decode produced non-finite states")
     log(f"decode: {ms_per_step * 1e3:.2f} us/step, {tokens_per_s / 1e6:.3f} M tokens/s, "
         f"{achieved:.0f} GB/s")
-
-    # per-launch kernel duration with an event pair around each launch
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(min(K, 64))]
-    state.copy_(state0)
-    torch.cuda.synchronize()
-    for s, (a, b) in enumerate(evs):
-        a.record(stream)
-        step(s % n_gen, state)
-        b.record(stream)
-    torch.cuda.synchronize()
-    launch_ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
 
     result = {
         "metric": METRIC,
@@ -204,7 +223,10 @@ def main():
             "kernel": "decode_step_kernel<bf16_t>",
             "algorithmic_bytes_per_launch": bytes_per_launch,
             "avg_launch_ms_timed_region": ms_per_step,
-            "median_launch_ms_event_pairs": launch_ms,
+            "timed_region": "graph replay of the timed steps" if graph is not None else "direct calls",
+            "state_bytes": B * H * D * D * 4,
+            "note": "the 128 MiB of state fit in the 256 MB last-level (Infinity) cache, so across "
+                    "consecutive steps part of the state stream is served from it",
         },
     }
 

@@ -14,11 +14,13 @@
 // each state byte is read once and written once per token.
 //
 // Mapping: one workgroup of 256 threads per head.  Wave w owns columns
-// [32w, 32w+32).  Lane l owns columns 32w + 4*(l & 7) .. +3 and rows
-// (l >> 3) + 8m, m = 0..15: 16 float4 = 64 state values in registers.  Each
-// load instruction of a wave covers 8 rows x 128 contiguous bytes.  The column
-// reductions finish across the 8 row groups of the wave with lane shuffles;
-// no LDS and no barrier are needed, and the four waves are independent.
+// [32w, 32w+32).  Lane l owns columns 32w + 4*(l & 7) .. +3 and the 16
+// consecutive rows 16*(l >> 3) .. +15: 16 float4 = 64 state values in
+// registers.  Each load instruction of a wave covers 8 rows x 128 contiguous
+// bytes.  The head's 128 gates, keys and queries are loaded once per
+// workgroup (exp(log_alpha) and the bf16 widening done once) into LDS, from
+// where every lane reads its 16 rows as float4.  The column
+// reductions finish across the 8 row groups of a wave with lane shuffles.
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
 
@@ -31,30 +33,52 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     const InT* __restrict__ beta, const float* __restrict__ log_alpha,
     float* __restrict__ state, float* __restrict__ o)
 {
+    __shared__ __attribute__((aligned(16))) float sa[kDim], sk[kDim], sq[kDim];
     const int64_t unit = blockIdx.x;
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
     const int rg = lane >> 3;
+    const int row0 = 16 * rg;
     const int col = wave * 32 + (lane & 7) * 4;
 
     float* S = state + unit * (kDim * kDim);
     const int64_t vec = unit * kDim;
 
+    // the per-head inputs come from memory not touched by earlier steps, so
+    // they are requested first; the state usually streams from closer caches
+    float x0, x1 = 0.f;
+    if (tid < kDim) {
+        x0 = log_alpha[vec + tid];
+    } else {
+        x0 = widen(k[vec + tid - kDim]);
+        x1 = widen(q[vec + tid - kDim]);
+    }
+    const float4 vv = load4(v + vec + col);
+    const float bt = widen(beta[unit]);
     float4 s[16];
 #pragma unroll
     for (int m = 0; m < 16; ++m)
-        s[m] = *reinterpret_cast<const float4*>(S + (rg + 8 * m) * kDim + col);
+        s[m] = *reinterpret_cast<const float4*>(S + (row0 + m) * kDim + col);
+
+    if (tid < kDim) {
+        sa[tid] = exp_gate(x0);
+    } else {
+        sk[tid - kDim] = x0;
+        sq[tid - kDim] = x1;
+    }
+    __syncthreads();
 
     float a[16], kk[16], qq[16];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        const int i = rg + 8 * m;
-        a[m] = exp_gate(log_alpha[vec + i]);
-        kk[m] = widen(k[vec + i]);
-        qq[m] = widen(q[vec + i]);
+    for (int m4 = 0; m4 < 4; ++m4) {
+        const float4 a4 = *reinterpret_cast<const float4*>(sa + row0 + 4 * m4);
+        const float4 k4 = *reinterpret_cast<const float4*>(sk + row0 + 4 * m4);
+        const float4 q4 = *reinterpret_cast<const float4*>(sq + row0 + 4 * m4);
+        a[4 * m4] = a4.x; a[4 * m4 + 1] = a4.y; a[4 * m4 + 2] = a4.z; a[4 * m4 + 3] = a4.w;
+        kk[4 * m4] = k4.x; kk[4 * m4 + 1] = k4.y; kk[4 * m4 + 2] = k4.z; kk[4 * m4 + 3] = k4.w;
+        qq[4 * m4] = q4.x; qq[4 * m4 + 1] = q4.y; qq[4 * m4 + 2] = q4.z; qq[4 * m4 + 3] = q4.w;
     }
-    const float bt = widen(beta[unit]);
-    const float4 vv = load4(v + vec + col);
 
     float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
     float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
@@ -80,7 +104,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     for (int m = 0; m < 16; ++m) {
         float4 t = s[m];
         t.x += kk[m] * u0; t.y += kk[m] * u1; t.z += kk[m] * u2; t.w += kk[m] * u3;
-        *reinterpret_cast<float4*>(S + (rg + 8 * m) * kDim + col) = t;
+        *reinterpret_cast<float4*>(S + (row0 + m) * kDim + col) = t;
     }
 }
 
