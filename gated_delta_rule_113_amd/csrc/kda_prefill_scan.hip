@@ -688,6 +688,15 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
         {
             auto column = [&](auto ac) {
                 constexpr int A = decltype(ac)::value;
+                // every N and diagonal-T block of this column's chain, read up front
+                float4 nb[4][4], db[4];
+#pragma unroll
+                for (int b = A + 1; b < 4; ++b) {
+#pragma unroll
+                    for (int m = A; m < b; ++m)
+                        nb[b][m] = at<float4>(sm, OFF_N + ((16 * b + l16) * N_LD + 16 * m + 4 * g4) * 4);
+                    db[b] = at<float4>(sm, OFF_TF + ((16 * b + l16) * N_LD + 16 * b + 4 * g4) * 4);
+                }
                 bf16x4 bh[4], bl[4];
                 {
                     float da[4];
@@ -701,13 +710,13 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
                     f32x4 zacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int m = A; m < b; ++m) {
-                        const float4 n4 = at<float4>(sm, OFF_N + ((16 * b + l16) * N_LD + 16 * m + 4 * g4) * 4);
+                        const float4 n4 = nb[b][m];
                         const float an[4] = {n4.x, n4.y, n4.z, n4.w};
                         bf16x4 ah, al;
                         split_vec(an, ah, al);
                         zacc = mma16x3(ah, al, bh[m], bl[m], zacc);
                     }
-                    const float4 d4 = at<float4>(sm, OFF_TF + ((16 * b + l16) * N_LD + 16 * b + 4 * g4) * 4);
+                    const float4 d4 = db[b];
                     const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
                     const float zz[4] = {zacc[0], zacc[1], zacc[2], zacc[3]};
                     bf16x4 ah, al, zh, zl;
@@ -774,6 +783,16 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
             // The A fragments of step s+1 are requested before the products of
             // step s; the scheduling barriers keep the compiler from sinking
             // those reads back next to their use.
+            bf16x8 shs[NS][4], sls[NS][4];
+#pragma unroll
+            for (int gi = 0; gi < NS; ++gi)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    float x[8];
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj) x[jj] = S[gi][2 * s + (jj >> 2)][jj & 3];
+                    split_vec(x, shs[gi][s], sls[gi][s]);
+                }
 #pragma unroll
             for (int pass = 0; pass < (OUT ? 2 : 1); ++pass) {
                 const int oh = pass == 0 ? OFF_KT_HI : OFF_QT_HI;
@@ -795,10 +814,8 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
                     bf16x8 sh[NS], sl[NS];
 #pragma unroll
                     for (int gi = 0; gi < NS; ++gi) {
-                        float x[8];
-#pragma unroll
-                        for (int jj = 0; jj < 8; ++jj) x[jj] = S[gi][2 * s + (jj >> 2)][jj & 3];
-                        split_vec(x, sh[gi], sl[gi]);
+                        sh[gi] = shs[gi][s];
+                        sl[gi] = sls[gi][s];
                     }
 #pragma unroll
                     for (int q4 = 0; q4 < 4; ++q4) {
@@ -809,7 +826,10 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
                                 X[gi][q4] = mma3(fh[s & 1][q4], fl[s & 1][q4], sh[gi], sl[gi], X[gi][q4]);
                             }
                         } else {
-                            O[q4] = mma3(fh[s & 1][q4], fl[s & 1][q4], sh[0], sl[0], O[q4]);
+                            // O^T = S^T Qt^T: the split state fragment is the A operand
+                            // and the Qt fragment the B operand, so each lane ends up
+                            // with four adjacent output columns of one token
+                            O[q4] = mma3(sh[0], sl[0], fh[s & 1][q4], fl[s & 1][q4], O[q4]);
                         }
                     }
                     __builtin_amdgcn_sched_barrier(0);
@@ -906,20 +926,19 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
                     split_vec(x, uh[gi][s], ul[gi][s]);
                 }
             if (OUT) {
-                // O += P U, then store the chunk's outputs for this column
+                // O^T += U^T P^T (U's split fragments as A, P's as B), then store:
+                // O[q4][i] = o[token 16 q4 + l16][column 16 wave + 4 g4 + i]
                 int n = 0;
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
 #pragma unroll
                     for (int s = 0; s <= (q4 >> 1); ++s) {
-                        O[q4] = mma3(pfh[n], pfl[n], uh[0][s], ul[0][s], O[q4]);
+                        O[q4] = mma3(uh[0][s], ul[0][s], pfh[n], pfl[n], O[q4]);
                         ++n;
                     }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int tk = 16 * q4 + 4 * g4 + i;
-                        if (tk < L) a.o[((base + c0 + tk) * H + h) * kDim + col] = O[q4][i];
-                    }
+                    const int tk = 16 * q4 + l16;
+                    if (tk < L)
+                        *reinterpret_cast<f32x4*>(a.o + ((base + c0 + tk) * H + h) * kDim + 16 * wave + 4 * g4) = O[q4];
                 }
             }
         }
