@@ -25,6 +25,8 @@ kda_status check_dtype(kda_dtype d)
 kda_status check_dims(int64_t H, int64_t d_k, int64_t d_v)
 {
     if (H < 1 || d_k < 1 || d_v < 1) return KDA_ERR_SHAPE;
+    // offsets within a 64-token chunk are 32-bit in the kernels
+    if (H > kda::kMaxHeads) return KDA_ERR_SHAPE;
     if (d_k != kda::kDim || d_v != kda::kDim) return KDA_ERR_UNSUPPORTED;
     return KDA_OK;
 }

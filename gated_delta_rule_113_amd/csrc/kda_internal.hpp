@@ -8,6 +8,7 @@
 namespace kda {
 
 constexpr int kDim = 128;  // d_k = d_v handled by the kernels
+constexpr int64_t kMaxHeads = 65536;  // keeps in-chunk element offsets within 32 bits
 
 // One fused decode step for `units` = N * H heads.
 hipError_t launch_decode_step(const void* q, const void* k, const void* v, const void* beta,

@@ -103,8 +103,11 @@ constexpr int OFF_T_HI = OFF_R1 + R1_BYTES;
 constexpr int OFF_T_LO = OFF_T_HI + 8192;
 constexpr int OFF_P_HI = OFF_T_LO + 8192;
 constexpr int OFF_P_LO = OFF_P_HI + 8192;
+// V: [token][column] bf16 rows of V_LD bytes (padded: the 16 reads of one
+// lane share a base address, and the 64 lanes of a read hit distinct banks)
+constexpr int V_LD = 2 * kDim + 8;
 constexpr int OFF_V = OFF_P_LO + 8192;
-constexpr int OFF_BETA = OFF_V + 16384;
+constexpr int OFF_BETA = OFF_V + CH * V_LD;
 constexpr int OFF_EL = OFF_BETA + CH * 4;
 constexpr int OFF_UNSAFE = OFF_EL + kDim * 4;
 constexpr int LDS_BYTES = OFF_UNSAFE + 16 * 4;
@@ -136,19 +139,42 @@ __device__ __forceinline__ T& at(char* base, int off)
     return *reinterpret_cast<T*>(base + off);
 }
 
+// base (wave-uniform) + a 32-bit byte offset, so that the access can take the
+// scalar-base + 32-bit vector-offset address form
+template <typename T, typename P>
+__device__ __forceinline__ T* gat(P* base, uint32_t byte_off)
+{
+    return reinterpret_cast<T*>(reinterpret_cast<
+        typename std::conditional<std::is_const<P>::value, const char, char>::type*>(base) + byte_off);
+}
+
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float bfw(__bf16 x) { return (float)x; }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// x = hi + lo with hi = bf16(x) (round to nearest even) and lo = bf16(x - hi).
+// Elements go in pairs: one packed conversion gives both hi parts, whose
+// fp32 values are read back from the packed bits (a shift and a mask), so
+// each element is rounded to bf16 only once for its hi part.
 template <int W, typename V>
 __device__ __forceinline__ void split_vec(const float (&x)[W], V& h, V& l)
 {
+    static_assert(W % 2 == 0 && sizeof(V) == 2 * W, "pairs of bf16");
+    typedef uint32_t uv __attribute__((ext_vector_type(W / 2)));
+    uv hu, lu;
 #pragma unroll
-    for (int j = 0; j < W; ++j) {
-        const __bf16 a = (__bf16)x[j];
-        h[j] = a;
-        l[j] = (__bf16)(x[j] - (float)a);
+    for (int j = 0; j < W; j += 2) {
+        uint32_t u = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x[j], x[j + 1]}, bf16x2));
+        asm("" : "+v"(u));  // keep the read-back on the packed bits
+        const float f0 = __uint_as_float(u << 16), f1 = __uint_as_float(u & 0xffff0000u);
+        hu[j / 2] = u;
+        lu[j / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x[j] - f0, x[j + 1] - f1}, bf16x2));
     }
+    h = __builtin_bit_cast(V, hu);
+    l = __builtin_bit_cast(V, lu);
 }
 
 // hi*hi + hi*lo + lo*hi on the 16x16x32 bf16 matrix instruction.
@@ -324,30 +350,54 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
     uint4 pq[2], pk[2], pv[2];
     float4 pla[4];
     float pb = 0.f;
+    // Addresses: a wave-uniform 64-bit pointer to the chunk's first row plus a
+    // 32-bit per-lane element offset (rows of one chunk lie within
+    // 64 * H * 128 elements, H <= 65536).
+    const uint32_t rs = static_cast<uint32_t>(H) * kDim;  // elements per row
     auto prefetch = [&](int64_t c0, int L, int tid) {
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int r = (tid >> 4) + 32 * m;
-            if (r < L) {
-                const int64_t off = ((base + c0 + r) * H + h) * kDim + 8 * (tid & 15);
-                pk[m] = *reinterpret_cast<const uint4*>(a.k + off);
-                pv[m] = *reinterpret_cast<const uint4*>(a.v + off);
-                if (OUT) pq[m] = *reinterpret_cast<const uint4*>(a.q + off);
-            } else {
-                pk[m] = pv[m] = pq[m] = make_uint4(0, 0, 0, 0);
-            }
-        }
+        const int64_t e0 = ((base + c0) * H + h) * kDim;
+        const bf16_t* kc = a.k + e0;
+        const bf16_t* vc = a.v + e0;
+        const bf16_t* qc = a.q + e0;
+        const float* lc = a.log_alpha + e0;
+        const bf16_t* bc = a.beta + ((base + c0) * H + h);
+        // q, k, v: row (tid >> 4) + 32 m, columns 8 (tid & 15) .. +7
+        const uint32_t o1 = __umul24(static_cast<uint32_t>(tid >> 4), rs) + 8 * (tid & 15);
         // log_alpha: wave w takes channels 16w..16w+15; lane = (token group
-        // (lane >> 2): tokens 4tg..4tg+3, channel quad lane & 3)
+        // (lane >> 2): rows 4tg..4tg+3, channel quad lane & 3)
+        const uint32_t o2 = __umul24(static_cast<uint32_t>(4 * ((tid & 63) >> 2)), rs) + 16 * (tid >> 6) +
+                            4 * (tid & 3);
+        if (L == CH) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int r = 4 * ((tid & 63) >> 2) + m;
-            pla[m] = r < L ? *reinterpret_cast<const float4*>(
-                                 a.log_alpha + ((base + c0 + r) * H + h) * kDim +
-                                 16 * (tid >> 6) + 4 * (tid & 3))
-                           : make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int m = 0; m < 2; ++m) {
+                const uint32_t off = o1 + m * 32 * rs;
+                pk[m] = *gat<const uint4>(kc, 2 * off);
+                pv[m] = *gat<const uint4>(vc, 2 * off);
+                if (OUT) pq[m] = *gat<const uint4>(qc, 2 * off);
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) pla[m] = *gat<const float4>(lc, 4 * (o2 + m * rs));
+            if (tid < CH) pb = widen(*gat<const bf16_t>(bc, 2 * __umul24(static_cast<uint32_t>(tid), H)));
+        } else {
+            // the last chunk of a segment: rows from L on read as zeros
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const uint32_t off = o1 + m * 32 * rs;
+                if ((tid >> 4) + 32 * m < L) {
+                    pk[m] = *gat<const uint4>(kc, 2 * off);
+                    pv[m] = *gat<const uint4>(vc, 2 * off);
+                    if (OUT) pq[m] = *gat<const uint4>(qc, 2 * off);
+                } else {
+                    pk[m] = pv[m] = pq[m] = make_uint4(0, 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                pla[m] = 4 * ((tid & 63) >> 2) + m < L ? *gat<const float4>(lc, 4 * (o2 + m * rs))
+                                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+            if (tid < CH)
+                pb = tid < L ? widen(*gat<const bf16_t>(bc, 2 * __umul24(static_cast<uint32_t>(tid), H))) : 0.f;
         }
-        if (tid < CH) pb = tid < L ? widen(a.beta[(base + c0 + tid) * H + h]) : 0.f;
     };
     if (nch > 0) prefetch(0, static_cast<int>(std::min<int64_t>(CH, seg_tokens)), tid);
 
@@ -381,7 +431,8 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
                     at<uint2>(sm, OFF_Q + a256(r, p0)) = make_uint2(pq[m].x, pq[m].y);
                     at<uint2>(sm, OFF_Q + a256(r, p1)) = make_uint2(pq[m].z, pq[m].w);
                 }
-                at<uint4>(sm, OFF_V + a256(r, c8)) = pv[m];
+                at<uint2>(sm, OFF_V + r * V_LD + 2 * c8) = make_uint2(pv[m].x, pv[m].y);
+                at<uint2>(sm, OFF_V + r * V_LD + 2 * c8 + 8) = make_uint2(pv[m].z, pv[m].w);
             }
             if (tid < CH) at<float>(sm, OFF_BETA + 4 * tid) = pb;
             // this lane: channels 16*wave + 4*(lane&3) .. +3, tokens 4*tg .. 4*tg+3
@@ -865,7 +916,7 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
                     for (int i = 0; i < 4; ++i) {
                         const int tk = 16 * q4 + 4 * g4 + i;
                         const float bt = at<float>(sm, OFF_BETA + 4 * tk);
-                        const float vv = bfw(*reinterpret_cast<const __bf16*>(sm + OFF_V + a256(tk, col)));
+                        const float vv = bfw(at<__bf16>(sm, OFF_V + tk * V_LD + 2 * col));
 #pragma unroll
                         for (int gi = 0; gi < NS; ++gi) {
                             const bool zero_v = (NS == 2 && gi == 0);  // the M block has no writes
@@ -926,6 +977,7 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
                     split_vec(x, uh[gi][s], ul[gi][s]);
                 }
             if (OUT) {
+                float* oc = a.o + ((base + c0) * H + h) * kDim;
                 // O^T += U^T P^T (U's split fragments as A, P's as B), then store:
                 // O[q4][i] = o[token 16 q4 + l16][column 16 wave + 4 g4 + i]
                 int n = 0;
@@ -938,7 +990,7 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
                     }
                     const int tk = 16 * q4 + l16;
                     if (tk < L)
-                        *reinterpret_cast<f32x4*>(a.o + ((base + c0 + tk) * H + h) * kDim + 16 * wave + 4 * g4) = O[q4];
+                        *gat<f32x4>(oc, 4 * (static_cast<uint32_t>(tk) * rs + 16 * wave + 4 * g4)) = O[q4];
                 }
             }
         }

@@ -43,7 +43,8 @@
  *  - q, k, v and beta share one storage type, `in_dtype` (KDA_F32 or
  *    KDA_BF16); log_alpha, states and o are always fp32.  Arithmetic is fp32
  *    with fp32 state; bf16 inputs are widened exactly.
- *  - Supported sizes: d_k = d_v = 128 (anything else -> KDA_ERR_UNSUPPORTED).
+ *  - Supported sizes: d_k = d_v = 128 (anything else -> KDA_ERR_UNSUPPORTED);
+ *    1 <= H <= 65536 heads (anything else -> KDA_ERR_SHAPE).
  *  - Every pointer must be 16-byte aligned (KDA_ERR_ALIGN).
  *  - Preconditions not checked (device data): log_alpha finite and <= 0;
  *    cu_seqlens[0] = 0, non-decreasing, cu_seqlens[N] = T_total.
@@ -91,7 +92,7 @@ typedef enum kda_dtype {
  *   final_state : [B, H, d_k, d_v] fp32, written, or NULL to skip; it MAY be
  *                 the same pointer as initial_state (in-place resume)
  * B = 0 is a no-op.  T = 0 writes final_state = initial_state (or zeros).
- * Requires H >= 1.
+ * Requires 1 <= H <= 65536.
  */
 kda_status kda_prefill(const void *q, const void *k, const void *v, const void *beta,
                        const float *log_alpha, const float *initial_state,

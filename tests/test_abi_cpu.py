@@ -81,6 +81,7 @@ def test_prefill_validation(lib):
     assert prefill(lib, dv=256) == UNSUP
     assert prefill(lib, dk=0) == SHAPE
     assert prefill(lib, H=0) == SHAPE
+    assert prefill(lib, H=65537, T=1) == SHAPE   # in-chunk offsets are 32-bit
     assert prefill(lib, B=-1) == SHAPE
     assert prefill(lib, T=-5) == SHAPE
     assert prefill(lib, T=1 << 40) == SHAPE
@@ -100,6 +101,7 @@ def test_varlen_validation(lib):
     assert varlen(lib, Tt=-1) == SHAPE
     assert varlen(lib, Tt=1 << 31) == SHAPE     # cu_seqlens holds int32 offsets
     assert varlen(lib, dk=96) == UNSUP
+    assert varlen(lib, H=65537) == SHAPE
     assert varlen(lib, dt=7) == DTYPE
     assert varlen(lib, N=0, cu=None, q=None, o=None) == OK
     assert varlen(lib, Tt=0, q=None, k=None, v=None, beta=None, la=None, o=None, s1=None) == OK
@@ -111,6 +113,7 @@ def test_decode_validation(lib):
         assert decode(lib, **{name: MIS}) == ALIGN, name
     assert decode(lib, N=-3) == SHAPE
     assert decode(lib, H=0) == SHAPE
+    assert decode(lib, H=65537) == SHAPE
     assert decode(lib, dk=127) == UNSUP
     assert decode(lib, dt=3) == DTYPE
     assert decode(lib, N=0, q=None) == OK
