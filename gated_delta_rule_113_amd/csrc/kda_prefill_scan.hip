@@ -197,6 +197,26 @@ __device__ __forceinline__ f32x4 mma16x3(bf16x4 ah, bf16x4 al, bf16x4 bh, bf16x4
     return c;
 }
 
+// x of the lane N places lower in the same 16-lane row, 0 for the first N
+// lanes of each row (DPP row shift; no LDS traffic)
+template <int N>
+__device__ __forceinline__ float4 row_shr(float4 x)
+{
+    auto sh = [](float v) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 + N, 0xF, 0xF, true));
+    };
+    return make_float4(sh(x.x), sh(x.y), sh(x.z), sh(x.w));
+}
+
+// x of lane (lane ^ M) for M = 1 or 2 (DPP quad permutation)
+template <int M>
+__device__ __forceinline__ float quad_xor(float x)
+{
+    static_assert(M == 1 || M == 2, "within a quad");
+    constexpr int ctrl = M == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ float4 f4add(float4 a, float4 b)
 {
     return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
@@ -364,9 +384,9 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
         // q, k, v: row (tid >> 4) + 32 m, columns 8 (tid & 15) .. +7
         const uint32_t o1 = __umul24(static_cast<uint32_t>(tid >> 4), rs) + 8 * (tid & 15);
         // log_alpha: wave w takes channels 16w..16w+15; lane = (token group
-        // (lane >> 2): rows 4tg..4tg+3, channel quad lane & 3)
-        const uint32_t o2 = __umul24(static_cast<uint32_t>(4 * ((tid & 63) >> 2)), rs) + 16 * (tid >> 6) +
-                            4 * (tid & 3);
+        // lane & 15: rows 4tg..4tg+3, channel quad lane >> 4)
+        const uint32_t o2 = __umul24(static_cast<uint32_t>(4 * (tid & 15)), rs) + 16 * (tid >> 6) +
+                            4 * ((tid & 63) >> 4);
         if (L == CH) {
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
@@ -393,7 +413,7 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
             }
 #pragma unroll
             for (int m = 0; m < 4; ++m)
-                pla[m] = 4 * ((tid & 63) >> 2) + m < L ? *gat<const float4>(lc, 4 * (o2 + m * rs))
+                pla[m] = 4 * (tid & 15) + m < L ? *gat<const float4>(lc, 4 * (o2 + m * rs))
                                                        : make_float4(0.f, 0.f, 0.f, 0.f);
             if (tid < CH)
                 pb = tid < L ? widen(*gat<const bf16_t>(bc, 2 * __umul24(static_cast<uint32_t>(tid), H))) : 0.f;
@@ -435,9 +455,11 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
                 at<uint2>(sm, OFF_V + r * V_LD + 2 * c8 + 8) = make_uint2(pv[m].z, pv[m].w);
             }
             if (tid < CH) at<float>(sm, OFF_BETA + 4 * tid) = pb;
-            // this lane: channels 16*wave + 4*(lane&3) .. +3, tokens 4*tg .. 4*tg+3
-            const int tg = lane >> 2;
-            const int chn = 16 * wave + 4 * (lane & 3);
+            // this lane: channels 16*wave + 4*(lane >> 4) .. +3, tokens 4*tg .. 4*tg+3
+            // with tg = lane & 15, so the 16 token groups of a channel quad
+            // are one 16-lane row and the scan over them stays within the row
+            const int tg = lane & 15;
+            const int chn = 16 * wave + 4 * (lane >> 4);
             float4 gp[4];
             float4 run = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -447,14 +469,12 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
                                   run.w + x.w * kLog2e);
                 gp[m] = run;
             }
-            // inclusive scan of the 4-token sums over the 16 token groups (lanes 4 apart)
+            // inclusive scan of the 4-token sums over the 16 token groups
             float4 inc = run;
-#pragma unroll
-            for (int off = 4; off < 64; off <<= 1) {
-                const float4 y = make_float4(__shfl_up(inc.x, off), __shfl_up(inc.y, off),
-                                             __shfl_up(inc.z, off), __shfl_up(inc.w, off));
-                if (lane >= off) inc = f4add(inc, y);
-            }
+            inc = f4add(inc, row_shr<1>(inc));
+            inc = f4add(inc, row_shr<2>(inc));
+            inc = f4add(inc, row_shr<4>(inc));
+            inc = f4add(inc, row_shr<8>(inc));
             const float4 exc = make_float4(inc.x - run.x, inc.y - run.y, inc.z - run.z, inc.w - run.w);
             const int pc = perm(chn);
 #pragma unroll
@@ -465,12 +485,9 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
                     make_float4(ex2(inc.x), ex2(inc.y), ex2(inc.z), ex2(inc.w));
             // Per row block rb, is the mid-block reference safe for every channel?
             // inc is G at token 4tg+3; the lane with tg = 4rb+3 compares G at tokens
-            // 16rb-1, 16rb+7 and 16rb+15.
-            const float4 gm = make_float4(__shfl_up(inc.x, 8), __shfl_up(inc.y, 8),
-                                          __shfl_up(inc.z, 8), __shfl_up(inc.w, 8));
-            float4 gs = make_float4(__shfl_up(inc.x, 16), __shfl_up(inc.y, 16),
-                                    __shfl_up(inc.z, 16), __shfl_up(inc.w, 16));
-            if (tg < 4) gs = make_float4(0.f, 0.f, 0.f, 0.f);
+            // 16rb-1 (zero for rb = 0), 16rb+7 and 16rb+15.
+            const float4 gm = row_shr<2>(inc);
+            const float4 gs = row_shr<4>(inc);
             const bool bad = (tg & 3) == 3 &&
                              (gs.x - gm.x > kSafeLog2 || gm.x - inc.x > kSafeLog2 ||
                               gs.y - gm.y > kSafeLog2 || gm.y - inc.y > kSafeLog2 ||
@@ -480,7 +497,7 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
             int flags = 0;
 #pragma unroll
             for (int rbi = 0; rbi < 4; ++rbi)
-                if ((bm >> (16 * rbi + 12)) & 0xFull) flags |= 1 << rbi;
+                if (bm & (0x0001000100010001ull << (4 * rbi + 3))) flags |= 1 << rbi;
             if (lane == 0) at<int>(sm, OFF_UNSAFE + 4 * wave) = flags;
         }
         __syncthreads();
@@ -714,8 +731,8 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
             for (int rr = 0; rr < 16; ++rr) {
                 // N is strictly lower, so entries at or right of the diagonal are zero
                 float s = nv[rr].x * tv[0] + nv[rr].y * tv[1] + nv[rr].z * tv[2] + nv[rr].w * tv[3];
-                s += __shfl_xor(s, 1);
-                s += __shfl_xor(s, 2);
+                s += quad_xor<1>(s);
+                s += quad_xor<2>(s);
                 const float tr = (rr == jc ? 1.f : 0.f) - s;
                 if (p == (rr >> 2)) tv[rr & 3] = tr;
             }
