@@ -78,7 +78,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int CH = 64;            // tokens per chunk
 constexpr int NW = 8;             // waves per workgroup
 constexpr int NT = 64 * NW;       // threads per workgroup
-constexpr int G_LD = kDim + 4;    // fp32 row stride of the decay tile
 constexpr int N_LD = CH + 4;      // fp32 row stride of 64 x 64 tiles
 constexpr int SS = kDim * kDim;   // floats per state matrix
 constexpr float kSafeLog2 = 96.f;
@@ -90,7 +89,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int OFF_Q = 0;
 constexpr int OFF_K = 16384;
 constexpr int OFF_G = 32768;
-constexpr int R0_BYTES = 32768 + CH * G_LD * 4;
+constexpr int R0_BYTES = 32768 + CH * kDim * 4;
 constexpr int OFF_KT_HI = 0, OFF_KT_LO = 16384, OFF_QT_HI = 32768, OFF_QT_LO = 49152;
 // R1: N = Diag(b) A and T (fp32) during the UT solve; later Ke^T.
 constexpr int OFF_R1 = R0_BYTES;
@@ -111,6 +110,10 @@ constexpr int OFF_BETA = OFF_V + CH * V_LD;
 constexpr int OFF_EL = OFF_BETA + CH * 4;
 constexpr int OFF_UNSAFE = OFF_EL + kDim * 4;
 constexpr int LDS_BYTES = OFF_UNSAFE + 16 * 4;
+// the output tile of a chunk (64 x 128 fp32, rows of 32 float4 slots) over T
+// and P, between a chunk's state products and the next chunk's staging
+constexpr int OFF_OT = OFF_T_HI;
+static_assert(OFF_P_LO + 8192 - OFF_T_HI == CH * kDim * 4, "output tile fits T and P exactly");
 static_assert(R1_BYTES >= 32768, "Ke^T must fit in R1");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CU");
 
@@ -131,6 +134,29 @@ __device__ __forceinline__ int a256(int row, int pos)
 __device__ __forceinline__ int a128(int row, int pos)
 {
     return (row << 7) + ((((pos >> 3) ^ (row >> 1)) & 7) << 4) + ((pos & 7) << 1);
+}
+
+// Byte offset of entry `pos` (permuted channel) of token row `row` in the fp32
+// decay tile: rows of 32 float4 chunks, the chunk index XOR-ed with
+// (row ^ row >> 4) & 15 so that both 16 consecutive rows and 16 rows four
+// apart hit distinct banks at one chunk position.
+__device__ __forceinline__ int g_off(int row, int pos)
+{
+    return OFF_G + (row << 9) + ((((pos >> 2) ^ (row ^ (row >> 4))) & 15 | ((pos >> 2) & 16)) << 4) + ((pos & 3) << 2);
+}
+// Byte offset in the transposed tile Ke^T (channel rows of 64 tokens): like
+// a128, with the chunk index XOR-ed with (row >> 1 ^ row >> 3) & 7, which
+// keeps 16 consecutive rows conflict-free and spreads rows four apart.
+__device__ __forceinline__ int ke_off(int row, int pos)
+{
+    return (row << 7) + ((((pos >> 3) ^ (row >> 1) ^ (row >> 3)) & 7) << 4) + ((pos & 7) << 1);
+}
+
+// byte offset of float4 slot `slot` (0..31) of row `row` in the output tile,
+// XOR-swizzled so that 16 rows written at one slot hit distinct banks
+__device__ __forceinline__ int o_slot(int row, int slot)
+{
+    return (row << 9) + (((slot ^ row) & 31) << 4);
 }
 
 template <typename T>
@@ -369,57 +395,60 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
     // ---------------- register prefetch of one chunk of inputs
     uint4 pq[2], pk[2], pv[2];
     float4 pla[4];
-    float pb = 0.f;
+    bf16_t pb = {0};  // raw bits: widened when staged, so no wait follows the load
     // Addresses: a wave-uniform 64-bit pointer to the chunk's first row plus a
     // 32-bit per-lane element offset (rows of one chunk lie within
     // 64 * H * 128 elements, H <= 65536).
     const uint32_t rs = static_cast<uint32_t>(H) * kDim;  // elements per row
-    auto prefetch = [&](int64_t c0, int L, int tid) {
+    // part 0 / 1: q, k, v rows (tid >> 4) + 32 part, columns 8 (tid & 15) .. +7;
+    // part 2 / 3: log_alpha of token groups 2 (part - 2) .. +1 (wave w takes
+    // channels 16w..16w+15; lane = token group tg = lane & 15: rows 4tg..4tg+3,
+    // channel quad lane >> 4), and with part 3 beta.  The four parts are
+    // issued at different points so that the vector memory requests do not
+    // queue up at once.  Rows from L on read as zeros.
+    auto prefetch = [&](int64_t c0, int L, int tid, int part) {
         const int64_t e0 = ((base + c0) * H + h) * kDim;
-        const bf16_t* kc = a.k + e0;
-        const bf16_t* vc = a.v + e0;
-        const bf16_t* qc = a.q + e0;
-        const float* lc = a.log_alpha + e0;
-        const bf16_t* bc = a.beta + ((base + c0) * H + h);
-        // q, k, v: row (tid >> 4) + 32 m, columns 8 (tid & 15) .. +7
-        const uint32_t o1 = __umul24(static_cast<uint32_t>(tid >> 4), rs) + 8 * (tid & 15);
-        // log_alpha: wave w takes channels 16w..16w+15; lane = (token group
-        // lane & 15: rows 4tg..4tg+3, channel quad lane >> 4)
-        const uint32_t o2 = __umul24(static_cast<uint32_t>(4 * (tid & 15)), rs) + 16 * (tid >> 6) +
-                            4 * ((tid & 63) >> 4);
-        if (L == CH) {
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                const uint32_t off = o1 + m * 32 * rs;
-                pk[m] = *gat<const uint4>(kc, 2 * off);
-                pv[m] = *gat<const uint4>(vc, 2 * off);
-                if (OUT) pq[m] = *gat<const uint4>(qc, 2 * off);
+        if (part < 2) {
+            const int m = part;
+            const uint32_t off = __umul24(static_cast<uint32_t>(tid >> 4), rs) + 8 * (tid & 15) + m * 32 * rs;
+            if (L == CH || (tid >> 4) + 32 * m < L) {
+                pk[m] = *gat<const uint4>(a.k + e0, 2 * off);
+                pv[m] = *gat<const uint4>(a.v + e0, 2 * off);
+                if (OUT) pq[m] = *gat<const uint4>(a.q + e0, 2 * off);
+            } else {
+                pk[m] = pv[m] = pq[m] = make_uint4(0, 0, 0, 0);
             }
-#pragma unroll
-            for (int m = 0; m < 4; ++m) pla[m] = *gat<const float4>(lc, 4 * (o2 + m * rs));
-            if (tid < CH) pb = widen(*gat<const bf16_t>(bc, 2 * __umul24(static_cast<uint32_t>(tid), H)));
         } else {
-            // the last chunk of a segment: rows from L on read as zeros
+            const uint32_t o2 = __umul24(static_cast<uint32_t>(4 * (tid & 15)), rs) + 16 * (tid >> 6) +
+                                4 * ((tid & 63) >> 4);
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                const uint32_t off = o1 + m * 32 * rs;
-                if ((tid >> 4) + 32 * m < L) {
-                    pk[m] = *gat<const uint4>(kc, 2 * off);
-                    pv[m] = *gat<const uint4>(vc, 2 * off);
-                    if (OUT) pq[m] = *gat<const uint4>(qc, 2 * off);
-                } else {
-                    pk[m] = pv[m] = pq[m] = make_uint4(0, 0, 0, 0);
-                }
+            for (int mm = 0; mm < 2; ++mm) {
+                const int m = 2 * (part - 2) + mm;
+                pla[m] = (L == CH || 4 * (tid & 15) + m < L)
+                             ? *gat<const float4>(a.log_alpha + e0, 4 * (o2 + m * rs))
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
             }
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-                pla[m] = 4 * (tid & 15) + m < L ? *gat<const float4>(lc, 4 * (o2 + m * rs))
-                                                       : make_float4(0.f, 0.f, 0.f, 0.f);
-            if (tid < CH)
-                pb = tid < L ? widen(*gat<const bf16_t>(bc, 2 * __umul24(static_cast<uint32_t>(tid), H))) : 0.f;
+            if (part == 3 && tid < CH)
+                pb = tid < L ? *gat<const bf16_t>(a.beta + ((base + c0) * H + h),
+                                                  2 * __umul24(static_cast<uint32_t>(tid), H))
+                             : bf16_t{0};
         }
     };
-    if (nch > 0) prefetch(0, static_cast<int>(std::min<int64_t>(CH, seg_tokens)), tid);
+    if (nch > 0)
+        for (int part = 0; part < 4; ++part) prefetch(0, static_cast<int>(std::min<int64_t>(CH, seg_tokens)), tid, part);
+
+    // whole rows of the output tile of the chunk at c0 (L rows) from LDS to o;
+    // thread t covers float4 slots t + 512 j: rows (t >> 5) + 16 j
+    auto store_o = [&](int64_t cp, int L, int tid) {
+        float* oc = a.o + ((base + cp) * H + h) * kDim;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = (tid >> 5) + 16 * j, slot = tid & 31;
+            if (row < L)
+                *gat<f32x4>(oc, 4 * (__umul24(static_cast<uint32_t>(row), rs) + 4 * slot)) =
+                    at<f32x4>(sm, OFF_OT + o_slot(row, slot));
+        }
+    };
 
     for (int64_t ci = 0; ci < nch; ++ci) {
         const int64_t c0 = ci * CH;
@@ -438,7 +467,10 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
         const int cq = tid & 31;                 // natural channel quad
         const int pq4 = perm(4 * cq);            // its position in the permuted order
 
-        // ======== 0: stage the chunk; scan of the log2-decay in registers
+        // ======== 0: stage the chunk; scan of the log2-decay in registers.
+        //             With outputs, the previous chunk's output tile is
+        //             written out from LDS first.
+        if (OUT && ci > 0) store_o(c0 - CH, CH, tid);
         {
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
@@ -454,7 +486,7 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
                 at<uint2>(sm, OFF_V + r * V_LD + 2 * c8) = make_uint2(pv[m].x, pv[m].y);
                 at<uint2>(sm, OFF_V + r * V_LD + 2 * c8 + 8) = make_uint2(pv[m].z, pv[m].w);
             }
-            if (tid < CH) at<float>(sm, OFF_BETA + 4 * tid) = pb;
+            if (tid < CH) at<float>(sm, OFF_BETA + 4 * tid) = widen(pb);
             // this lane: channels 16*wave + 4*(lane >> 4) .. +3, tokens 4*tg .. 4*tg+3
             // with tg = lane & 15, so the 16 token groups of a channel quad
             // are one 16-lane row and the scan over them stays within the row
@@ -479,7 +511,7 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
             const int pc = perm(chn);
 #pragma unroll
             for (int m = 0; m < 4; ++m)
-                at<float4>(sm, OFF_G + ((4 * tg + m) * G_LD + pc) * 4) = f4add(gp[m], exc);
+                at<float4>(sm, g_off(4 * tg + m, pc)) = f4add(gp[m], exc);
             if (tg == 15)
                 at<float4>(sm, OFF_EL + 4 * chn) =
                     make_float4(ex2(inc.x), ex2(inc.y), ex2(inc.z), ex2(inc.w));
@@ -509,7 +541,6 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
         f32x4 accA[4], accP[4];
         float qk = 0.f;
         {
-            const float* G = &at<float>(sm, OFF_G);
             int fl = 0;
 #pragma unroll
             for (int w = 0; w < NW; ++w) fl |= at<int>(sm, OFF_UNSAFE + 4 * w);
@@ -520,15 +551,15 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
 #pragma unroll
             for (int sl = 0; sl < 2; ++sl) {
                 const int p0 = 32 * (2 * kh + sl) + 8 * g4;
-                const float4 ga = at<float4>(sm, OFF_G + (r * G_LD + p0) * 4);
-                const float4 gb = at<float4>(sm, OFF_G + (r * G_LD + p0 + 4) * 4);
+                const float4 ga = at<float4>(sm, g_off(r, p0));
+                const float4 gb = at<float4>(sm, g_off(r, p0 + 4));
                 float4 ra, rbv;
                 if (!uns) {
-                    ra = at<float4>(sm, OFF_G + ((16 * rb + 7) * G_LD + p0) * 4);
-                    rbv = at<float4>(sm, OFF_G + ((16 * rb + 7) * G_LD + p0 + 4) * 4);
+                    ra = at<float4>(sm, g_off(16 * rb + 7, p0));
+                    rbv = at<float4>(sm, g_off(16 * rb + 7, p0 + 4));
                 } else if (rb > 0) {
-                    ra = at<float4>(sm, OFF_G + ((16 * rb - 1) * G_LD + p0) * 4);
-                    rbv = at<float4>(sm, OFF_G + ((16 * rb - 1) * G_LD + p0 + 4) * 4);
+                    ra = at<float4>(sm, g_off(16 * rb - 1, p0));
+                    rbv = at<float4>(sm, g_off(16 * rb - 1, p0 + 4));
                 } else {
                     ra = rbv = make_float4(0.f, 0.f, 0.f, 0.f);
                 }
@@ -574,7 +605,7 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
                             float sa = 0.f, sp = 0.f;
                             if (ti <= r) {
                                 for (int p = 64 * kh; p < 64 * kh + 64; ++p) {
-                                    const float f = ex2(G[r * G_LD + p] - G[ti * G_LD + p]);
+                                    const float f = ex2(at<float>(sm, g_off(r, p)) - at<float>(sm, g_off(ti, p)));
                                     const float ki = bfw(*reinterpret_cast<const __bf16*>(K + a256(ti, p)));
                                     const float kr = bfw(*reinterpret_cast<const __bf16*>(K + a256(r, p)));
                                     const float qr = bfw(*reinterpret_cast<const __bf16*>(Q + a256(r, p)));
@@ -591,8 +622,8 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
 #pragma unroll
                     for (int sl = 0; sl < 2; ++sl) {
                         const int p0 = 32 * (2 * kh + sl) + 8 * g4;
-                        const float4 ga = at<float4>(sm, OFF_G + (ti * G_LD + p0) * 4);
-                        const float4 gb = at<float4>(sm, OFF_G + (ti * G_LD + p0 + 4) * 4);
+                        const float4 ga = at<float4>(sm, g_off(ti, p0));
+                        const float4 gb = at<float4>(sm, g_off(ti, p0 + 4));
                         const float gi[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
                         const bf16x8 kk = at<bf16x8>(sm, OFF_K + a256(ti, p0));
                         float x[8];
@@ -641,12 +672,12 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
         // until their LDS regions are free.
         bf16x4 fKh[4], fKl[4], fQh[4], fQl[4], fEh[4], fEl[4];
         auto form = [&]() {
-            const float4 g63 = at<float4>(sm, OFF_G + (63 * G_LD + pq4) * 4);
+            const float4 g63 = at<float4>(sm, g_off(63, pq4));
             float ke[4][4];
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int r = 4 * tq + m;
-                const float4 gv = at<float4>(sm, OFF_G + (r * G_LD + pq4) * 4);
+                const float4 gv = at<float4>(sm, g_off(r, pq4));
                 const bf16x4 kv = at<bf16x4>(sm, OFF_K + a256(r, pq4));
                 bf16x4 qv = kv;
                 if (OUT) qv = at<bf16x4>(sm, OFF_Q + a256(r, pq4));
@@ -834,13 +865,14 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
             const int tp = perm(4 * tq);
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
-                at<bf16x4>(sm, OFF_KE_HI + a128(4 * cq + x, tp)) = fEh[x];
-                at<bf16x4>(sm, OFF_KE_LO + a128(4 * cq + x, tp)) = fEl[x];
+                at<bf16x4>(sm, OFF_KE_HI + ke_off(4 * cq + x, tp)) = fEh[x];
+                at<bf16x4>(sm, OFF_KE_LO + ke_off(4 * cq + x, tp)) = fEl[x];
             }
         }
         bf16x8 uh[NS][2], ul[NS][2];
+        f32x4 O[4];
         {
-            f32x4 X[NS][4], O[4];
+            f32x4 X[NS][4];
 #pragma unroll
             for (int gi = 0; gi < NS; ++gi)
 #pragma unroll
@@ -851,16 +883,36 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
             // The A fragments of step s+1 are requested before the products of
             // step s; the scheduling barriers keep the compiler from sinking
             // those reads back next to their use.
+            // The state is split once per chunk; the fragment of step s+1 is
+            // split while the products of step s run.
             bf16x8 shs[NS][4], sls[NS][4];
+            auto split_s = [&](int s) {
 #pragma unroll
-            for (int gi = 0; gi < NS; ++gi)
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
+                for (int gi = 0; gi < NS; ++gi) {
                     float x[8];
 #pragma unroll
                     for (int jj = 0; jj < 8; ++jj) x[jj] = S[gi][2 * s + (jj >> 2)][jj & 3];
                     split_vec(x, shs[gi][s], sls[gi][s]);
                 }
+            };
+            split_s(0);
+            // Y = Diag(b) (V - X) for the four tokens 16 q4 + 4 g4 .. +3 of this
+            // lane.  With outputs it is formed during the O pass, one row block
+            // per step, so that its vector work overlaps the matrix products.
+            float y[NS][4][4];
+            auto make_y = [&](int q4) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tk = 16 * q4 + 4 * g4 + i;
+                    const float bt = at<float>(sm, OFF_BETA + 4 * tk);
+                    const float vv = bfw(at<__bf16>(sm, OFF_V + tk * V_LD + 2 * col));
+#pragma unroll
+                    for (int gi = 0; gi < NS; ++gi) {
+                        const bool zero_v = (NS == 2 && gi == 0);  // the M block has no writes
+                        y[gi][q4][i] = bt * ((zero_v ? 0.f : vv) - X[gi][q4][i]);
+                    }
+                }
+            };
 #pragma unroll
             for (int pass = 0; pass < (OUT ? 2 : 1); ++pass) {
                 const int oh = pass == 0 ? OFF_KT_HI : OFF_QT_HI;
@@ -900,13 +952,20 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
                             O[q4] = mma3(sh[0], sl[0], fh[s & 1][q4], fl[s & 1][q4], O[q4]);
                         }
                     }
+                    if (pass == 0 && s + 1 < 4) split_s(s + 1);
+                    if (pass == 0 && ci + 1 < nch) {
+                        // a quarter of the next chunk's inputs, in flight during the
+                        // rest of this one
+                        const int64_t c1 = c0 + CH;
+                        prefetch(c1, static_cast<int>(std::min<int64_t>(CH, seg_tokens - c1)), tid, s);
+                    }
+                    if (pass == 1) make_y(s);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
-            // inputs of the next chunk, in flight during the rest of this one
-            if (ci + 1 < nch) {
-                const int64_t c1 = c0 + CH;
-                prefetch(c1, static_cast<int>(std::min<int64_t>(CH, seg_tokens - c1)), tid);
+            if (!OUT) {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) make_y(q4);
             }
             // T fragments for U = T Y, requested before the vector work on Y
             bf16x8 tfh[6], tfl[6];  // (q4, s) pairs with s <= q4/2, in order
@@ -923,23 +982,9 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
                     }
             }
             __builtin_amdgcn_sched_barrier(0);
-            // Y = Diag(b) (V - X), split as B operands over tokens
+            // Y split as B operands over tokens
             bf16x8 yh[NS][2], yl[NS][2];
             {
-                float y[NS][4][4];
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int tk = 16 * q4 + 4 * g4 + i;
-                        const float bt = at<float>(sm, OFF_BETA + 4 * tk);
-                        const float vv = bfw(at<__bf16>(sm, OFF_V + tk * V_LD + 2 * col));
-#pragma unroll
-                        for (int gi = 0; gi < NS; ++gi) {
-                            const bool zero_v = (NS == 2 && gi == 0);  // the M block has no writes
-                            y[gi][q4][i] = bt * ((zero_v ? 0.f : vv) - X[gi][q4][i]);
-                        }
-                    }
 #pragma unroll
                 for (int gi = 0; gi < NS; ++gi)
 #pragma unroll
@@ -994,8 +1039,7 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
                     split_vec(x, uh[gi][s], ul[gi][s]);
                 }
             if (OUT) {
-                float* oc = a.o + ((base + c0) * H + h) * kDim;
-                // O^T += U^T P^T (U's split fragments as A, P's as B), then store:
+                // O^T += U^T P^T (U's split fragments as A, P's as B):
                 // O[q4][i] = o[token 16 q4 + l16][column 16 wave + 4 g4 + i]
                 int n = 0;
 #pragma unroll
@@ -1005,22 +1049,30 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
                         O[q4] = mma3(uh[0][s], ul[0][s], pfh[n], pfl[n], O[q4]);
                         ++n;
                     }
-                    const int tk = 16 * q4 + l16;
-                    if (tk < L)
-                        *gat<f32x4>(oc, 4 * (static_cast<uint32_t>(tk) * rs + 16 * wave + 4 * g4)) = O[q4];
                 }
             }
         }
         __syncthreads();
 
         // ======== 9: S <- Diag(2^G_63) S + Ke^T U (fragments of tile t+1 in
-        //             flight during the products of tile t)
+        //             flight during the products of tile t).  With outputs,
+        //             the chunk's output tile first goes to LDS (over T and P,
+        //             now dead); it is written out by whole rows while the next
+        //             chunk is staged.  A wave's own 16 columns span 16 rows per
+        //             store instruction; whole rows span 2.
+        if (OUT) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int row = 16 * q4 + l16;
+                at<f32x4>(sm, OFF_OT + o_slot(row, 4 * wave + g4)) = O[q4];
+            }
+        }
         {
             bf16x8 eh[2][2], el[2][2];
             auto fetch = [&](int t, int buf) {
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
-                    const int off = a128(16 * t + l16, 32 * s + 8 * g4);
+                    const int off = ke_off(16 * t + l16, 32 * s + 8 * g4);
                     eh[buf][s] = at<bf16x8>(sm, OFF_KE_HI + off);
                     el[buf][s] = at<bf16x8>(sm, OFF_KE_LO + off);
                 }
@@ -1053,6 +1105,10 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
     }
 
     // ---------------- results
+    if (OUT && nch > 0) {
+        const int64_t cl = (nch - 1) * CH;
+        store_o(cl, static_cast<int>(seg_tokens - cl), tid);
+    }
     if (OUT) {
         if (sg.j == sg.nseg - 1 && a.final_state) {
             float* dst = a.final_state + unit * SS;
