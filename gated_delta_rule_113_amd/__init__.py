@@ -7,6 +7,10 @@ ABI of ``include/kda.h``); this package is its thin Python binding:
     kda_varlen_prefill(q, k, v, beta, log_alpha, cu_seqlens, initial_state=None)
         -> (o, final_state)
     kda_decode_step(q, k, v, beta, log_alpha, state) -> o      (state in place)
+    kda_decode_step_slots(q, k, v, beta, log_alpha, state_pool, slots) -> o
+    kda_varlen_prefill_slots(q, k, v, beta, log_alpha, cu_seqlens, state_pool,
+                             init_slots=None, final_slots=None) -> o
+        (states in a pool, addressed by int32 slots)
 
 PyTorch is used only for device memory and the current stream.
 """
@@ -16,11 +20,13 @@ from ._binding import (  # noqa: F401
     KDA_F32,
     KDAError,
     kda_decode_step,
+    kda_decode_step_slots,
     kda_prefill,
     kda_set_prefill_segment,
     kda_varlen_prefill,
+    kda_varlen_prefill_slots,
     load_library,
 )
 
-__all__ = ["kda_prefill", "kda_varlen_prefill", "kda_decode_step", "kda_set_prefill_segment",
-           "KDAError", "load_library"]
+__all__ = ["kda_prefill", "kda_varlen_prefill", "kda_decode_step", "kda_decode_step_slots",
+           "kda_varlen_prefill_slots", "kda_set_prefill_segment", "KDAError", "load_library"]

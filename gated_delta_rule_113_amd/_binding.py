@@ -20,8 +20,9 @@ STATUS_NAMES = {
     0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
     4: "KDA_ERR_ALIGN", 5: "KDA_ERR_UNSUPPORTED", 6: "KDA_ERR_HIP",
 }
-EXPORTS = ("kda_prefill", "kda_varlen_prefill", "kda_decode_step", "kda_set_prefill_segment",
-           "kda_status_str", "kda_abi_version")
+EXPORTS = ("kda_prefill", "kda_varlen_prefill", "kda_decode_step", "kda_decode_step_slots",
+           "kda_varlen_prefill_slots", "kda_set_prefill_segment", "kda_status_str",
+           "kda_abi_version")
 
 _lock = threading.Lock()
 _lib = None
@@ -63,6 +64,12 @@ def load_library(path: str | None = None):
         lib.kda_decode_step.argtypes = [vp, vp, vp, vp, f32p, f32p, f32p,
                                         i64, i64, i64, i64, ctypes.c_int, vp]
         lib.kda_decode_step.restype = ctypes.c_int
+        lib.kda_decode_step_slots.argtypes = [vp, vp, vp, vp, f32p, f32p, vp, i64, f32p,
+                                              i64, i64, i64, i64, ctypes.c_int, vp]
+        lib.kda_decode_step_slots.restype = ctypes.c_int
+        lib.kda_varlen_prefill_slots.argtypes = [vp, vp, vp, vp, f32p, vp, i64, i64, f32p, vp, vp,
+                                                 i64, f32p, i64, i64, i64, ctypes.c_int, vp]
+        lib.kda_varlen_prefill_slots.restype = ctypes.c_int
         lib.kda_set_prefill_segment.argtypes = [i64]
         lib.kda_set_prefill_segment.restype = ctypes.c_int
         lib.kda_status_str.argtypes = [ctypes.c_int]
@@ -219,4 +226,82 @@ def kda_decode_step(q, k, v, beta, log_alpha, state, *, out=None):
                                _ptr(state), _ptr(o), N, H, dk, dv, _in_dtype(q, k, v, beta),
                                _stream(dev))
     _check(lib, "kda_decode_step", code)
+    return o
+
+
+def _slots(t, name, N, dev):
+    torch = _torch()
+    _require(t, name, torch.int32, (N,), dev)
+    return t
+
+
+def kda_decode_step_slots(q, k, v, beta, log_alpha, state_pool, slots, *, out=None):
+    """One decode step with the states in a pool.  q, k, log_alpha [N, H, 128];
+    v [N, H, 128]; beta [N, H]; state_pool [P, H, 128, 128] fp32; slots int32 [N]
+    on the GPU.  Sequence n updates pool entry slots[n] in place; a slot outside
+    [0, P) skips the sequence (its rows of ``out`` are left as they are; without
+    ``out`` they are zeros).  Returns o [N, H, 128] fp32."""
+    torch = _torch()
+    lib = load_library()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _require(q, "q", device=dev)
+    _require(k, "k", q.dtype, (N, H, dk), dev)
+    _require(v, "v", q.dtype, (N, H, dv), dev)
+    _require(beta, "beta", q.dtype, (N, H), dev)
+    _require(log_alpha, "log_alpha", torch.float32, (N, H, dk), dev)
+    _require(state_pool, "state_pool", torch.float32, None, dev)
+    if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H, dk, dv):
+        raise ValueError(f"state_pool must be [P, {H}, {dk}, {dv}], got {tuple(state_pool.shape)}")
+    _slots(slots, "slots", N, dev)
+    o = out if out is not None else torch.zeros((N, H, dv), dtype=torch.float32, device=dev)
+    _require(o, "out", torch.float32, (N, H, dv), dev)
+    code = lib.kda_decode_step_slots(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
+                                     _ptr(state_pool), _ptr(slots), state_pool.shape[0], _ptr(o),
+                                     N, H, dk, dv, _in_dtype(q, k, v, beta), _stream(dev))
+    _check(lib, "kda_decode_step_slots", code)
+    return o
+
+
+def kda_varlen_prefill_slots(q, k, v, beta, log_alpha, cu_seqlens, state_pool, init_slots=None,
+                             final_slots=None, *, out=None):
+    """Packed prefill with the states in a pool.  Inputs as kda_varlen_prefill;
+    state_pool [P, H, 128, 128] fp32; init_slots / final_slots int32 [N] on the
+    GPU or None.  Sequence n starts from pool entry init_slots[n] (zeros when
+    outside [0, P) or when init_slots is None) and leaves its final state in pool
+    entry final_slots[n] (not written when outside [0, P) or when final_slots is
+    None).  Returns o shaped like v, fp32."""
+    torch = _torch()
+    lib = load_library()
+    dev = q.device
+    lead = q.shape[:-3]
+    if lead not in ((), (1,)):
+        raise ValueError("packed inputs must be [T_total, H, d] or [1, T_total, H, d]")
+    Tt, H, dk = q.shape[-3:]
+    dv = v.shape[-1]
+    _require(q, "q", device=dev)
+    _require(k, "k", q.dtype, (*lead, Tt, H, dk), dev)
+    _require(v, "v", q.dtype, (*lead, Tt, H, dv), dev)
+    _require(beta, "beta", q.dtype, (*lead, Tt, H), dev)
+    _require(log_alpha, "log_alpha", torch.float32, (*lead, Tt, H, dk), dev)
+    _require(cu_seqlens, "cu_seqlens", torch.int32, None, dev)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor of N + 1 offsets")
+    N = cu_seqlens.numel() - 1
+    _require(state_pool, "state_pool", torch.float32, None, dev)
+    if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H, dk, dv):
+        raise ValueError(f"state_pool must be [P, {H}, {dk}, {dv}], got {tuple(state_pool.shape)}")
+    if init_slots is not None:
+        _slots(init_slots, "init_slots", N, dev)
+    if final_slots is not None:
+        _slots(final_slots, "final_slots", N, dev)
+    o = out if out is not None else torch.empty((*lead, Tt, H, dv), dtype=torch.float32, device=dev)
+    _require(o, "out", torch.float32, (*lead, Tt, H, dv), dev)
+    code = lib.kda_varlen_prefill_slots(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
+                                        _ptr(cu_seqlens), N, Tt, _ptr(state_pool),
+                                        _ptr(init_slots), _ptr(final_slots), state_pool.shape[0],
+                                        _ptr(o), H, dk, dv, _in_dtype(q, k, v, beta),
+                                        _stream(dev))
+    _check(lib, "kda_varlen_prefill_slots", code)
     return o

@@ -57,14 +57,28 @@ kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HI
 // are not exact in bf16) take the register-resident token-by-token kernel.
 hipError_t launch_prefill(const void* q, const void* k, const void* v, const void* beta,
                           const float* log_alpha, const int32_t* cu_seqlens, int64_t n_seq,
-                          int64_t T, int64_t T_total, int64_t H, const float* initial_state,
-                          float* o, float* final_state, kda_dtype in_dtype, hipStream_t stream)
+                          int64_t T, int64_t T_total, int64_t H, const kda::StateRefs& st,
+                          float* o, kda_dtype in_dtype, hipStream_t stream)
 {
     if (in_dtype == KDA_BF16)
         return kda::launch_prefill_scan(q, k, v, beta, log_alpha, cu_seqlens, n_seq, T, T_total,
-                                        H, initial_state, o, final_state, stream);
-    return kda::launch_prefill_recurrent(q, k, v, beta, log_alpha, cu_seqlens, n_seq, T, H,
-                                         initial_state, o, final_state, false, stream);
+                                        H, st, o, stream);
+    return kda::launch_prefill_recurrent(q, k, v, beta, log_alpha, cu_seqlens, n_seq, T, H, st,
+                                         o, false, stream);
+}
+
+kda::StateRefs plain_states(const float* initial_state, float* final_state)
+{
+    kda::StateRefs st;
+    st.init = initial_state;
+    st.fin = final_state;
+    return st;
+}
+
+// pool entries of H * 128 * 128 floats must stay far from int64 overflow
+bool pool_too_big(int64_t n_pool, int64_t H)
+{
+    return n_pool > kMaxElems / H / (int64_t(kda::kDim) * kda::kDim);
 }
 
 }  // namespace
@@ -92,7 +106,7 @@ kda_status kda_prefill(const void* q, const void* k, const void* v, const void* 
     }
     if (T == 0 && !final_state) return KDA_OK;
     return from_hip(launch_prefill(q, k, v, beta, log_alpha, nullptr, B, T, B * T, H,
-                                   initial_state, o, final_state, in_dtype,
+                                   plain_states(initial_state, final_state), o, in_dtype,
                                    static_cast<hipStream_t>(stream)));
 }
 
@@ -120,8 +134,39 @@ kda_status kda_varlen_prefill(const void* q, const void* k, const void* v, const
     }
     if (T_total == 0 && !final_state) return KDA_OK;
     return from_hip(launch_prefill(q, k, v, beta, log_alpha, cu_seqlens, N, 0, T_total, H,
-                                   initial_state, o, final_state, in_dtype,
+                                   plain_states(initial_state, final_state), o, in_dtype,
                                    static_cast<hipStream_t>(stream)));
+}
+
+kda_status kda_varlen_prefill_slots(const void* q, const void* k, const void* v, const void* beta,
+                                    const float* log_alpha, const int32_t* cu_seqlens, int64_t N,
+                                    int64_t T_total, float* state_pool, const int32_t* init_slots,
+                                    const int32_t* final_slots, int64_t n_pool, float* o,
+                                    int64_t H, int64_t d_k, int64_t d_v, kda_dtype in_dtype,
+                                    void* stream)
+{
+    kda_status st;
+    if ((st = check_dtype(in_dtype)) != KDA_OK) return st;
+    if ((st = check_dims(H, d_k, d_v)) != KDA_OK) return st;
+    if (N < 0 || T_total < 0 || n_pool < 0) return KDA_ERR_SHAPE;
+    if (T_total > INT32_MAX || N > int64_t(1) << 24 || N * H > int64_t(1) << 30) return KDA_ERR_SHAPE;
+    if ((st = check_rows(T_total, H)) != KDA_OK) return st;
+    if (pool_too_big(n_pool, H)) return KDA_ERR_SHAPE;
+    if (N == 0) return KDA_OK;
+    if (!cu_seqlens) return KDA_ERR_NULL;
+    if (misaligned(cu_seqlens)) return KDA_ERR_ALIGN;
+    if ((init_slots || final_slots) && !state_pool) return KDA_ERR_NULL;
+    if ((st = check_ptrs({}, {state_pool, init_slots, final_slots})) != KDA_OK) return st;
+    if (T_total > 0 && (st = check_ptrs({q, k, v, beta, log_alpha, o}, {})) != KDA_OK) return st;
+    if (T_total == 0 && !final_slots) return KDA_OK;
+    kda::StateRefs refs;
+    refs.init = init_slots ? state_pool : nullptr;
+    refs.fin = final_slots ? state_pool : nullptr;
+    refs.init_slots = init_slots;
+    refs.fin_slots = final_slots;
+    refs.n_pool = n_pool;
+    return from_hip(launch_prefill(q, k, v, beta, log_alpha, cu_seqlens, N, 0, T_total, H, refs,
+                                   o, in_dtype, static_cast<hipStream_t>(stream)));
 }
 
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* beta,
@@ -135,8 +180,26 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
     if (N > int64_t(1) << 24 || N * H > INT32_MAX) return KDA_ERR_SHAPE;
     if (N == 0) return KDA_OK;
     if ((st = check_ptrs({q, k, v, beta, log_alpha, state, o}, {})) != KDA_OK) return st;
-    return from_hip(kda::launch_decode_step(q, k, v, beta, log_alpha, state, o, N * H,
-                                            in_dtype == KDA_BF16,
+    return from_hip(kda::launch_decode_step(q, k, v, beta, log_alpha, state, nullptr, 0, o, N * H,
+                                            H, in_dtype == KDA_BF16,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+kda_status kda_decode_step_slots(const void* q, const void* k, const void* v, const void* beta,
+                                 const float* log_alpha, float* state_pool, const int32_t* slots,
+                                 int64_t n_pool, float* o, int64_t N, int64_t H, int64_t d_k,
+                                 int64_t d_v, kda_dtype in_dtype, void* stream)
+{
+    kda_status st;
+    if ((st = check_dtype(in_dtype)) != KDA_OK) return st;
+    if ((st = check_dims(H, d_k, d_v)) != KDA_OK) return st;
+    if (N < 0 || n_pool < 0) return KDA_ERR_SHAPE;
+    if (N > int64_t(1) << 24 || N * H > INT32_MAX) return KDA_ERR_SHAPE;
+    if (pool_too_big(n_pool, H)) return KDA_ERR_SHAPE;
+    if (N == 0) return KDA_OK;
+    if ((st = check_ptrs({q, k, v, beta, log_alpha, state_pool, slots, o}, {})) != KDA_OK) return st;
+    return from_hip(kda::launch_decode_step(q, k, v, beta, log_alpha, state_pool, slots, n_pool, o,
+                                            N * H, H, in_dtype == KDA_BF16,
                                             static_cast<hipStream_t>(stream)));
 }
 

@@ -31,10 +31,11 @@ template <typename InT>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
     const InT* __restrict__ beta, const float* __restrict__ log_alpha,
-    float* __restrict__ state, float* __restrict__ o)
+    float* __restrict__ state, const int32_t* __restrict__ slots, int64_t n_pool, int H,
+    float* __restrict__ o)
 {
     __shared__ __attribute__((aligned(16))) float sa[kDim], sk[kDim], sq[kDim];
-    const int64_t unit = blockIdx.x;
+    const int64_t unit = blockIdx.x;  // n * H + h
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
@@ -42,7 +43,16 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     const int row0 = 16 * rg;
     const int col = wave * 32 + (lane & 7) * 4;
 
-    float* S = state + unit * (kDim * kDim);
+    // the head's state: entry unit, or with slots entry (slots[n], h) of the
+    // pool; a slot outside the pool skips the sequence (a whole-workgroup exit)
+    int64_t e = unit;
+    if (slots) {
+        const int64_t n = unit / H;
+        const int64_t sl = slots[n];
+        if (sl < 0 || sl >= n_pool) return;
+        e = sl * H + (unit - n * H);
+    }
+    float* S = state + e * (kDim * kDim);
     const int64_t vec = unit * kDim;
 
     // the per-head inputs come from memory not touched by earlier steps, so
@@ -111,8 +121,9 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 }  // namespace
 
 hipError_t launch_decode_step(const void* q, const void* k, const void* v, const void* beta,
-                              const float* log_alpha, float* state, float* o, int64_t units,
-                              bool bf16, hipStream_t stream)
+                              const float* log_alpha, float* state, const int32_t* slots,
+                              int64_t n_pool, float* o, int64_t units, int64_t H, bool bf16,
+                              hipStream_t stream)
 {
     if (units <= 0) return hipSuccess;
     const dim3 grid(static_cast<unsigned>(units)), block(256);
@@ -121,12 +132,12 @@ hipError_t launch_decode_step(const void* q, const void* k, const void* v, const
         hipLaunchKernelGGL(decode_step_kernel<T>, grid, block, 0, stream,
                            static_cast<const T*>(q), static_cast<const T*>(k),
                            static_cast<const T*>(v), static_cast<const T*>(beta), log_alpha,
-                           state, o);
+                           state, slots, n_pool, static_cast<int>(H), o);
     } else {
         hipLaunchKernelGGL(decode_step_kernel<float>, grid, block, 0, stream,
                            static_cast<const float*>(q), static_cast<const float*>(k),
                            static_cast<const float*>(v), static_cast<const float*>(beta),
-                           log_alpha, state, o);
+                           log_alpha, state, slots, n_pool, static_cast<int>(H), o);
     }
     return hipGetLastError();
 }

@@ -34,6 +34,29 @@ __device__ __forceinline__ float exp_gate(float x)
     return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
 }
 
+// The entering / leaving state of head h of sequence n (see StateRefs), or
+// NULL for "zeros" / "not written".
+__device__ __forceinline__ const float* init_state_of(const StateRefs& r, int64_t n, int h, int64_t H)
+{
+    if (!r.init) return nullptr;
+    int64_t e = n;
+    if (r.init_slots) {
+        e = r.init_slots[n];
+        if (e < 0 || e >= r.n_pool) return nullptr;
+    }
+    return r.init + (e * H + h) * (kDim * kDim);
+}
+__device__ __forceinline__ float* final_state_of(const StateRefs& r, int64_t n, int h, int64_t H)
+{
+    if (!r.fin) return nullptr;
+    int64_t e = n;
+    if (r.fin_slots) {
+        e = r.fin_slots[n];
+        if (e < 0 || e >= r.n_pool) return nullptr;
+    }
+    return r.fin + (e * H + h) * (kDim * kDim);
+}
+
 __device__ __forceinline__ float xor_sum_rows(float x)
 {
     // sum over lanes that differ in bits 3..5 (the 8 row groups of a wave)

@@ -10,18 +10,35 @@ namespace kda {
 constexpr int kDim = 128;  // d_k = d_v handled by the kernels
 constexpr int64_t kMaxHeads = 65536;  // keeps in-chunk element offsets within 32 bits
 
-// One fused decode step for `units` = N * H heads.
+// Where the entering and leaving states of the sequences live.  Without slot
+// arrays, sequence n uses entry n of `init` / `fin` ([*, H, 128, 128] fp32).
+// With a slot array, sequence n uses entry slots[n] of a pool of n_pool
+// entries, and a slot outside [0, n_pool) means "none": zeros coming in,
+// nothing written going out.  A NULL `init` means zeros for every sequence, a
+// NULL `fin` that no state is written.
+struct StateRefs {
+    const float* init = nullptr;
+    float* fin = nullptr;
+    const int32_t* init_slots = nullptr;
+    const int32_t* fin_slots = nullptr;
+    int64_t n_pool = 0;
+};
+
+// One fused decode step for `units` = N * H heads.  Sequence n's state is
+// entry n of `state`, or with `slots` entry slots[n] of a pool of n_pool
+// entries (a slot outside [0, n_pool) skips the sequence).
 hipError_t launch_decode_step(const void* q, const void* k, const void* v, const void* beta,
-                              const float* log_alpha, float* state, float* o, int64_t units,
-                              bool bf16, hipStream_t stream);
+                              const float* log_alpha, float* state, const int32_t* slots,
+                              int64_t n_pool, float* o, int64_t units, int64_t H, bool bf16,
+                              hipStream_t stream);
 
 // Token-by-token prefill with the state held in registers.  Dense when
 // cu_seqlens == nullptr (sequence n = rows n*T .. n*T+T-1), packed otherwise.
 hipError_t launch_prefill_recurrent(const void* q, const void* k, const void* v,
                                     const void* beta, const float* log_alpha,
                                     const int32_t* cu_seqlens, int64_t n_seq, int64_t T,
-                                    int64_t H, const float* initial_state, float* o,
-                                    float* final_state, bool bf16, hipStream_t stream);
+                                    int64_t H, const StateRefs& st, float* o, bool bf16,
+                                    hipStream_t stream);
 
 // Chunked prefill on bf16 matrix instructions (bf16 inputs only): 64-token
 // chunks, one workgroup per (sequence, head, segment).  Long sequences are cut
@@ -31,9 +48,8 @@ hipError_t launch_prefill_recurrent(const void* q, const void* k, const void* v,
 // (T_total rows in all).
 hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, const void* beta,
                                const float* log_alpha, const int32_t* cu_seqlens, int64_t n_seq,
-                               int64_t T, int64_t T_total, int64_t H,
-                               const float* initial_state, float* o, float* final_state,
-                               hipStream_t stream);
+                               int64_t T, int64_t T_total, int64_t H, const StateRefs& st,
+                               float* o, hipStream_t stream);
 
 // Tokens per segment for the chunked prefill (a positive multiple of 64), or
 // 0 to choose it from the problem size and the number of CUs.

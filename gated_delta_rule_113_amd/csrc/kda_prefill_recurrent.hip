@@ -20,8 +20,7 @@ __global__ __launch_bounds__(256) void prefill_recurrent_kernel(
     const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
     const InT* __restrict__ beta, const float* __restrict__ log_alpha,
     const int32_t* __restrict__ cu_seqlens, int64_t T, int H,
-    const float* initial_state, float* __restrict__ o,
-    float* final_state)  // final_state may alias initial_state (no __restrict__)
+    const StateRefs st, float* __restrict__ o)  // the final state may alias the initial one
 {
     const int64_t unit = blockIdx.x;  // n * H + h
     const int64_t n = unit / H;
@@ -41,8 +40,7 @@ __global__ __launch_bounds__(256) void prefill_recurrent_kernel(
     }
 
     float4 s[16];
-    if (initial_state) {
-        const float* S0 = initial_state + unit * (kDim * kDim);
+    if (const float* S0 = init_state_of(st, n, h, H)) {
 #pragma unroll
         for (int m = 0; m < 16; ++m)
             s[m] = *reinterpret_cast<const float4*>(S0 + (rg + 8 * m) * kDim + col);
@@ -91,8 +89,7 @@ __global__ __launch_bounds__(256) void prefill_recurrent_kernel(
         }
     }
 
-    if (final_state) {
-        float* S1 = final_state + unit * (kDim * kDim);
+    if (float* S1 = final_state_of(st, n, h, H)) {
 #pragma unroll
         for (int m = 0; m < 16; ++m)
             *reinterpret_cast<float4*>(S1 + (rg + 8 * m) * kDim + col) = s[m];
@@ -104,8 +101,8 @@ __global__ __launch_bounds__(256) void prefill_recurrent_kernel(
 hipError_t launch_prefill_recurrent(const void* q, const void* k, const void* v,
                                     const void* beta, const float* log_alpha,
                                     const int32_t* cu_seqlens, int64_t n_seq, int64_t T,
-                                    int64_t H, const float* initial_state, float* o,
-                                    float* final_state, bool bf16, hipStream_t stream)
+                                    int64_t H, const StateRefs& st, float* o, bool bf16,
+                                    hipStream_t stream)
 {
     const int64_t units = n_seq * H;
     if (units <= 0) return hipSuccess;
@@ -116,12 +113,12 @@ hipError_t launch_prefill_recurrent(const void* q, const void* k, const void* v,
         hipLaunchKernelGGL(prefill_recurrent_kernel<E>, grid, block, 0, stream,
                            static_cast<const E*>(q), static_cast<const E*>(k),
                            static_cast<const E*>(v), static_cast<const E*>(beta), log_alpha,
-                           cu_seqlens, T, h, initial_state, o, final_state);
+                           cu_seqlens, T, h, st, o);
     } else {
         hipLaunchKernelGGL(prefill_recurrent_kernel<float>, grid, block, 0, stream,
                            static_cast<const float*>(q), static_cast<const float*>(k),
                            static_cast<const float*>(v), static_cast<const float*>(beta),
-                           log_alpha, cu_seqlens, T, h, initial_state, o, final_state);
+                           log_alpha, cu_seqlens, T, h, st, o);
     }
     return hipGetLastError();
 }

@@ -265,9 +265,8 @@ struct ScanArgs {
     int64_t nseg_dense;         // dense: segments per sequence
     int64_t n_segs;             // number of segment slots (grid bound)
     int H;
-    const float* initial_state;
+    StateRefs st;  // entering and leaving states (per sequence, or pool slots)
     float* o;
-    float* final_state;
     float* ws_maps;   // [n_segs][H][2][d_k][d_v]: M and R of each segment but the last
     float* ws_start;  // [n_segs][H][d_k][d_v]: entering state of each segment
 };
@@ -353,7 +352,6 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
     const bool blkM = !OUT && sg.j > 0;       // pass 1: is the M block carried?
 
     const int col = 16 * wave + l16;          // this lane's value column
-    const int64_t unit = sg.n * H + h;
 
     // ---------------- state (accumulator layout: S[g][t][i] = row 16t+4g4+i, column col)
     f32x4 S[NS][8];
@@ -361,9 +359,9 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
         const float* init = nullptr;
         if (OUT) {
             if (sg.nseg > 1) init = a.ws_start + (z * H + h) * SS;
-            else if (a.initial_state) init = a.initial_state + unit * SS;
-        } else if (sg.j == 0 && a.initial_state) {
-            init = a.initial_state + unit * SS;
+            else init = init_state_of(a.st, sg.n, h, H);
+        } else if (sg.j == 0) {
+            init = init_state_of(a.st, sg.n, h, H);
         }
 #pragma unroll
         for (int gi = 0; gi < NS; ++gi)
@@ -1110,8 +1108,8 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
         store_o(cl, static_cast<int>(seg_tokens - cl), tid);
     }
     if (OUT) {
-        if (sg.j == sg.nseg - 1 && a.final_state) {
-            float* dst = a.final_state + unit * SS;
+        float* dst = sg.j == sg.nseg - 1 ? final_state_of(a.st, sg.n, h, H) : nullptr;
+        if (dst) {
 #pragma unroll
             for (int t = 0; t < 8; ++t)
 #pragma unroll
@@ -1292,8 +1290,7 @@ void set_prefill_segment(int64_t tokens) { g_forced_segment = tokens; }
 hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, const void* beta,
                                const float* log_alpha, const int32_t* cu_seqlens, int64_t n_seq,
                                int64_t T, int64_t T_total, int64_t H,
-                               const float* initial_state, float* o, float* final_state,
-                               hipStream_t stream)
+                               const StateRefs& st, float* o, hipStream_t stream)
 {
     const int64_t units = n_seq * H;
     if (units <= 0) return hipSuccess;
@@ -1313,9 +1310,8 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
     a.T = T;
     a.n_seq = n_seq;
     a.H = static_cast<int>(H);
-    a.initial_state = initial_state;
+    a.st = st;
     a.o = o;
-    a.final_state = final_state;
 
     // Segment length: enough segments to give every CU about one segment of
     // the total work, never shorter than kMinSegment tokens.

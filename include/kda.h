@@ -132,6 +132,53 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v, const vo
                            kda_dtype in_dtype, void *stream);
 
 /*
+ * State pool addressed by slot (serving: continuous batching and a prefill
+ * cache whose states are restored and updated without copies).  The pages
+ * describe a cached prefill state that is restored so only the new suffix is
+ * prefilled ("Kimi K3 -- the architecture and infrastructure, explained",
+ * section "Serving infrastructure: supernodes and the prefill cache"); here the
+ * states live in one caller-owned pool and each call names, per sequence, the
+ * pool entry to use.
+ *   state_pool : [n_pool, H, d_k, d_v] fp32, DEVICE memory, caller-owned.
+ *   slots      : int32 [N], DEVICE memory, read on the device.  A slot outside
+ *                [0, n_pool) means "no entry" (see each call); such a slot
+ *                never causes an access outside the pool.
+ * Arithmetic is exactly that of the plain calls: a sequence whose state sits
+ * in pool entry s gives the same bits as the plain call given that state.
+ */
+
+/*
+ * One decode step with the states in a pool: sequence n updates pool entry
+ * slots[n] IN PLACE (all H heads) and writes o[n].  A sequence whose slot is
+ * outside [0, n_pool) is skipped: its pool entries and its rows of o are left
+ * untouched (padding rows of a fixed-size batch).  Non-skipped slots must be
+ * distinct (two sequences updating one entry race).
+ *   q, k, log_alpha : [N, H, d_k];  v : [N, H, d_v];  beta : [N, H];  o : [N, H, d_v]
+ * N = 0 is a no-op.
+ */
+kda_status kda_decode_step_slots(const void *q, const void *k, const void *v, const void *beta,
+                                 const float *log_alpha, float *state_pool, const int32_t *slots,
+                                 int64_t n_pool, float *o, int64_t N, int64_t H, int64_t d_k,
+                                 int64_t d_v, kda_dtype in_dtype, void *stream);
+
+/*
+ * Packed variable-length prefill (as kda_varlen_prefill) with the states in a
+ * pool.  Sequence n starts from pool entry init_slots[n] (zeros if that slot is
+ * outside [0, n_pool), or for every sequence if init_slots is NULL) and leaves
+ * its final state in pool entry final_slots[n] (not written if that slot is
+ * outside [0, n_pool), or for every sequence if final_slots is NULL).  A
+ * sequence may resume in place (init_slots[n] == final_slots[n]); otherwise no
+ * final slot may equal another sequence's initial or final slot.
+ * state_pool may be NULL only when both slot arrays are NULL.
+ */
+kda_status kda_varlen_prefill_slots(const void *q, const void *k, const void *v, const void *beta,
+                                    const float *log_alpha, const int32_t *cu_seqlens, int64_t N,
+                                    int64_t T_total, float *state_pool, const int32_t *init_slots,
+                                    const int32_t *final_slots, int64_t n_pool, float *o,
+                                    int64_t H, int64_t d_k, int64_t d_v, kda_dtype in_dtype,
+                                    void *stream);
+
+/*
  * Tuning and testing knob for the bf16 prefill (process-wide; set it while no
  * prefill call is running).  The blockwise prefill runs one workgroup per
  * (sequence, head, segment); a sequence longer than `tokens` is cut into

@@ -38,6 +38,7 @@ def _declared():
 def test_exports_match_header(lib):
     declared = _declared()
     assert declared == {"kda_prefill", "kda_varlen_prefill", "kda_decode_step",
+                        "kda_decode_step_slots", "kda_varlen_prefill_slots",
                         "kda_set_prefill_segment", "kda_status_str", "kda_abi_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", kda._binding.LIBRARY],
                          capture_output=True, text=True, check=True).stdout
@@ -117,6 +118,45 @@ def test_decode_validation(lib):
     assert decode(lib, dk=127) == UNSUP
     assert decode(lib, dt=3) == DTYPE
     assert decode(lib, N=0, q=None) == OK
+
+
+def decode_slots(lib, q=P, k=P, v=P, beta=P, la=P, pool=P, slots=P, n_pool=4, o=P, N=2, H=2,
+                 dk=128, dv=128, dt=1):
+    return lib.kda_decode_step_slots(q, k, v, beta, la, pool, slots, n_pool, o, N, H, dk, dv, dt,
+                                     None)
+
+
+def varlen_slots(lib, q=P, k=P, v=P, beta=P, la=P, cu=P, N=2, Tt=8, pool=P, si=P, sf=P, n_pool=4,
+                 o=P, H=2, dk=128, dv=128, dt=1):
+    return lib.kda_varlen_prefill_slots(q, k, v, beta, la, cu, N, Tt, pool, si, sf, n_pool, o, H,
+                                        dk, dv, dt, None)
+
+
+def test_decode_slots_validation(lib):
+    for name in ("q", "k", "v", "beta", "la", "pool", "slots", "o"):
+        assert decode_slots(lib, **{name: None}) == NULL, name
+        assert decode_slots(lib, **{name: MIS}) == ALIGN, name
+    assert decode_slots(lib, N=-1) == SHAPE
+    assert decode_slots(lib, n_pool=-1) == SHAPE
+    assert decode_slots(lib, n_pool=1 << 40) == SHAPE   # pool index products overflow
+    assert decode_slots(lib, H=0) == SHAPE
+    assert decode_slots(lib, dv=64) == UNSUP
+    assert decode_slots(lib, dt=5) == DTYPE
+    assert decode_slots(lib, N=0, q=None, pool=None, slots=None) == OK
+
+
+def test_varlen_slots_validation(lib):
+    assert varlen_slots(lib, cu=None) == NULL
+    assert varlen_slots(lib, pool=None) == NULL             # slots need a pool
+    assert varlen_slots(lib, si=MIS) == ALIGN
+    assert varlen_slots(lib, sf=MIS) == ALIGN
+    assert varlen_slots(lib, n_pool=-2) == SHAPE
+    assert varlen_slots(lib, Tt=-1) == SHAPE
+    assert varlen_slots(lib, dk=32) == UNSUP
+    assert varlen_slots(lib, dt=9) == DTYPE
+    assert varlen_slots(lib, N=0, cu=None, pool=None) == OK
+    # nothing to read and nothing to write
+    assert varlen_slots(lib, Tt=0, pool=None, si=None, sf=None, q=None, o=None) == OK
 
 
 def test_binding_rejects_cpu_tensors(lib):
