@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--batch", type=int, default=64)
     ap.add_argument("--heads", type=int, default=32)
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
+    ap.add_argument("--no-slots", action="store_true",
+                    help="skip the decode measurement with the states in a slot-addressed pool")
     ap.add_argument("--eager", action="store_true",
                     help="time direct decode calls instead of a replayed HIP graph of them")
     ap.add_argument("--prefill-T", type=int, default=32768)
@@ -229,6 +231,71 @@ def main():
                     "consecutive steps part of the state stream is served from it",
         },
     }
+
+    # ---------------- decode with the states in a pool (secondary) ---------
+    # The same B x H decode, but the states live in a pool of 4B entries and
+    # each sequence names its entry by an int32 slot (seeded distinct slots).
+    if not args.no_slots:
+        P = 4 * B
+        pool = torch.zeros((P, H, D, D), dtype=torch.float32, device=dev)
+        slots_np = np.random.default_rng(113).permutation(P)[:B].astype(np.int32)
+        slots = torch.from_numpy(slots_np).to(dev)
+        pool.index_copy_(0, slots.long(), state0)
+        Ks = min(K, 256)
+
+        def sstep(s):
+            kda.kda_decode_step_slots(q[s], k[s], v[s], beta[s], la[s], pool, slots, out=o)
+
+        sgraph = None
+        if not args.eager:
+            try:
+                side = torch.cuda.Stream(dev)
+                side.wait_stream(stream)
+                with torch.cuda.stream(side):
+                    sstep(0)
+                stream.wait_stream(side)
+                torch.cuda.synchronize()
+                sgraph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(sgraph):
+                    for s in range(Ks):
+                        sstep(s % n_gen)
+                torch.cuda.synchronize()
+            except Exception as e:
+                log(f"graph capture of the slot steps failed ({e}); timing direct calls")
+                sgraph = None
+
+        def run_slots():
+            if sgraph is not None:
+                sgraph.replay()
+            else:
+                for s in range(Ks):
+                    sstep(s % n_gen)
+
+        run_slots()  # untimed
+        torch.cuda.synchronize()
+        pool.index_copy_(0, slots.long(), state0)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        run_slots()
+        b.record(stream)
+        torch.cuda.synchronize()
+        sms = a.elapsed_time(b) / Ks
+        sgbs = bytes_per_launch / (sms / 1e3) / 1e9
+        if not bool(torch.isfinite(pool).all()):
+            raise RuntimeError("slot decode produced non-finite states")
+        log(f"decode from a pool of {P} entries: {sms * 1e3:.2f} us/step, {sgbs:.0f} GB/s")
+        result["decode_slots"] = {
+            "workload": f"the same decode, states in a pool of {P} x H={H} entries addressed by "
+                        f"{B} distinct int32 slots",
+            "steps": Ks,
+            "ms_per_step": sms,
+            "tokens_per_s": B / (sms / 1e3),
+            "roofline": {"bound": "hbm", "achieved": sgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": sgbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": bytes_per_launch},
+        }
+        del pool, sgraph
 
     # ---------------- prefill (secondary) ---------------------------------
     if not args.no_prefill:

@@ -1,5 +1,6 @@
 """Cross-checks between the GPU entry points (each is also checked against
-the oracle elsewhere): resuming from a stored state, decode == prefill."""
+the oracle elsewhere): resuming from a stored state, decode == prefill, and
+equivariance under a permutation of the value columns."""
 import numpy as np
 import pytest
 
@@ -47,3 +48,36 @@ def test_decode_chain_equals_prefill():
     od = torch.stack(outs, dim=1).cpu().numpy()
     assert rel_err_vectors(od, o.cpu().numpy()) < 1e-4
     assert rel_err_states(st.cpu().numpy(), S.cpu().numpy()) < 1e-4
+
+
+def test_value_column_permutation_equivariance():
+    """Columns of the state are independent: permuting the value columns (v and
+    the initial state's d_v axis) permutes the columns of o and of the final
+    state and changes nothing else.  Checked for the chunked prefill (columns
+    spread over waves and lanes), with segments, and for the decode step."""
+    torch = __import__("torch")
+    dev = device()
+    perm = torch.from_numpy(np.random.default_rng(26).permutation(128)).to(dev)
+    inp = ki.dense_prefill(26, B=1, T=300, H=2, gated=True, initial_state=True)
+    t = upload(inp, dev)
+    args = lambda vv: (t["q"], t["k"], vv, t["beta"], t["log_alpha"])
+    for seg in (0, 64):
+        kda.kda_set_prefill_segment(seg)
+        try:
+            o, S = kda.kda_prefill(*args(t["v"]), t["initial_state"])
+            op, Sp = kda.kda_prefill(*args(t["v"][..., perm].contiguous()),
+                                     t["initial_state"][..., perm].contiguous())
+        finally:
+            kda.kda_set_prefill_segment(0)
+        torch.cuda.synchronize()
+        assert rel_err_vectors(op.cpu().numpy(), o[..., perm].cpu().numpy()) < 1e-5, seg
+        assert rel_err_states(Sp.cpu().numpy(), S[..., perm].cpu().numpy()) < 1e-5, seg
+    d = upload(ki.decode_steps(26, steps=1, N=3, H=2), dev)
+    st = d["initial_state"].clone()
+    stp = d["initial_state"][..., perm].contiguous()
+    o1 = kda.kda_decode_step(d["q"][0], d["k"][0], d["v"][0], d["beta"][0], d["log_alpha"][0], st)
+    o2 = kda.kda_decode_step(d["q"][0], d["k"][0], d["v"][0][..., perm].contiguous(), d["beta"][0],
+                             d["log_alpha"][0], stp)
+    torch.cuda.synchronize()
+    assert rel_err_vectors(o2.cpu().numpy(), o1[..., perm].cpu().numpy()) < 1e-5
+    assert rel_err_states(stp.cpu().numpy(), st[..., perm].cpu().numpy()) < 1e-5
