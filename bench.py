@@ -330,8 +330,11 @@ def main():
             "tokens_per_s": T / (pms / 1e3),
             "head_tokens_per_s": T * H / (pms / 1e3),
             "roofline": {"bound": "hbm", "achieved": pgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": pgbs / HBM_PEAK_GBS, "traffic": None,
-                         "algorithmic_bytes_per_launch": pbytes},
+                         "frac": pgbs / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("prefill_H32_T32768_hbm_traffic.json", "prefill_call"),
+                         "algorithmic_bytes_per_launch": pbytes,
+                         "note": "achieved = algorithmic bytes / time of one call (3 kernels); traffic = "
+                                 "measured HBM bytes of one call"},
             "mfma": {"algorithmic_tflops": ptf, "peak_tflops_bf16": BF16_MFMA_PEAK_TFLOPS,
                      "frac": ptf / BF16_MFMA_PEAK_TFLOPS,
                      "algorithmic_flops_per_launch": pflops},
