@@ -7,6 +7,8 @@ ABI of ``include/kda.h``); this package is its thin Python binding:
     kda_varlen_prefill(q, k, v, beta, log_alpha, cu_seqlens, initial_state=None)
         -> (o, final_state)
     kda_decode_step(q, k, v, beta, log_alpha, state) -> o      (state in place)
+    kda_decode_tokens(q, k, v, beta, log_alpha, state, n_commit=None) -> o
+        (K draft tokens from the state; commits an accepted prefix in place)
     kda_decode_step_slots(q, k, v, beta, log_alpha, state_pool, slots) -> o
     kda_varlen_prefill_slots(q, k, v, beta, log_alpha, cu_seqlens, state_pool,
                              init_slots=None, final_slots=None) -> o
@@ -21,6 +23,7 @@ from ._binding import (  # noqa: F401
     KDAError,
     kda_decode_step,
     kda_decode_step_slots,
+    kda_decode_tokens,
     kda_prefill,
     kda_set_prefill_segment,
     kda_varlen_prefill,
@@ -28,5 +31,6 @@ from ._binding import (  # noqa: F401
     load_library,
 )
 
-__all__ = ["kda_prefill", "kda_varlen_prefill", "kda_decode_step", "kda_decode_step_slots",
+__all__ = ["kda_prefill", "kda_varlen_prefill", "kda_decode_step", "kda_decode_tokens",
+           "kda_decode_step_slots",
            "kda_varlen_prefill_slots", "kda_set_prefill_segment", "KDAError", "load_library"]

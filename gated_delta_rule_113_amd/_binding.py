@@ -20,9 +20,9 @@ STATUS_NAMES = {
     0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
     4: "KDA_ERR_ALIGN", 5: "KDA_ERR_UNSUPPORTED", 6: "KDA_ERR_HIP",
 }
-EXPORTS = ("kda_prefill", "kda_varlen_prefill", "kda_decode_step", "kda_decode_step_slots",
-           "kda_varlen_prefill_slots", "kda_set_prefill_segment", "kda_status_str",
-           "kda_abi_version")
+EXPORTS = ("kda_prefill", "kda_varlen_prefill", "kda_decode_step", "kda_decode_tokens",
+           "kda_decode_step_slots", "kda_varlen_prefill_slots", "kda_set_prefill_segment",
+           "kda_status_str", "kda_abi_version")
 
 _lock = threading.Lock()
 _lib = None
@@ -64,6 +64,9 @@ def load_library(path: str | None = None):
         lib.kda_decode_step.argtypes = [vp, vp, vp, vp, f32p, f32p, f32p,
                                         i64, i64, i64, i64, ctypes.c_int, vp]
         lib.kda_decode_step.restype = ctypes.c_int
+        lib.kda_decode_tokens.argtypes = [vp, vp, vp, vp, f32p, f32p, vp, f32p,
+                                          i64, i64, i64, i64, i64, ctypes.c_int, vp]
+        lib.kda_decode_tokens.restype = ctypes.c_int
         lib.kda_decode_step_slots.argtypes = [vp, vp, vp, vp, f32p, f32p, vp, i64, f32p,
                                               i64, i64, i64, i64, ctypes.c_int, vp]
         lib.kda_decode_step_slots.restype = ctypes.c_int
@@ -304,4 +307,32 @@ def kda_varlen_prefill_slots(q, k, v, beta, log_alpha, cu_seqlens, state_pool, i
                                         _ptr(o), H, dk, dv, _in_dtype(q, k, v, beta),
                                         _stream(dev))
     _check(lib, "kda_varlen_prefill_slots", code)
+    return o
+
+
+def kda_decode_tokens(q, k, v, beta, log_alpha, state, n_commit=None, *, out=None):
+    """K draft tokens per sequence from its state (1 <= K <= 16).  q, k, log_alpha
+    [N, K, H, 128]; v [N, K, H, 128]; beta [N, K, H]; state [N, H, 128, 128] fp32.
+    Without ``n_commit`` the state is only read; with ``n_commit`` (int32 [N] on
+    the GPU) sequence n's state becomes, in place, the state after its first
+    n_commit[n] tokens (clamped to [0, K]).  Returns o [N, K, H, 128] fp32."""
+    torch = _torch()
+    lib = load_library()
+    N, K, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _require(q, "q", device=dev)
+    _require(k, "k", q.dtype, (N, K, H, dk), dev)
+    _require(v, "v", q.dtype, (N, K, H, dv), dev)
+    _require(beta, "beta", q.dtype, (N, K, H), dev)
+    _require(log_alpha, "log_alpha", torch.float32, (N, K, H, dk), dev)
+    _require(state, "state", torch.float32, (N, H, dk, dv), dev)
+    if n_commit is not None:
+        _slots(n_commit, "n_commit", N, dev)
+    o = out if out is not None else torch.empty((N, K, H, dv), dtype=torch.float32, device=dev)
+    _require(o, "out", torch.float32, (N, K, H, dv), dev)
+    code = lib.kda_decode_tokens(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
+                                 _ptr(state), _ptr(n_commit), _ptr(o), N, K, H, dk, dv,
+                                 _in_dtype(q, k, v, beta), _stream(dev))
+    _check(lib, "kda_decode_tokens", code)
     return o

@@ -203,6 +203,23 @@ kda_status kda_decode_step_slots(const void* q, const void* k, const void* v, co
                                             static_cast<hipStream_t>(stream)));
 }
 
+kda_status kda_decode_tokens(const void* q, const void* k, const void* v, const void* beta,
+                             const float* log_alpha, float* state, const int32_t* n_commit, float* o,
+                             int64_t N, int64_t K, int64_t H, int64_t d_k, int64_t d_v,
+                             kda_dtype in_dtype, void* stream)
+{
+    kda_status st;
+    if ((st = check_dtype(in_dtype)) != KDA_OK) return st;
+    if ((st = check_dims(H, d_k, d_v)) != KDA_OK) return st;
+    if (N < 0 || K < 1 || K > kda::kMaxDraft) return KDA_ERR_SHAPE;
+    if (N > int64_t(1) << 24 || N * H > INT32_MAX) return KDA_ERR_SHAPE;
+    if (N == 0) return KDA_OK;
+    if ((st = check_ptrs({q, k, v, beta, log_alpha, state, o}, {n_commit})) != KDA_OK) return st;
+    return from_hip(kda::launch_decode_tokens(q, k, v, beta, log_alpha, state, n_commit, o, N, K, H,
+                                              in_dtype == KDA_BF16,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 kda_status kda_set_prefill_segment(int64_t tokens)
 {
     if (tokens < 0 || tokens % 64 != 0 || tokens > (int64_t(1) << 40)) return KDA_ERR_SHAPE;

@@ -118,7 +118,140 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     }
 }
 
+// K consecutive tokens of each sequence from its current state (speculative
+// decoding: verify K draft tokens, then keep the accepted prefix).  The same
+// per-token arithmetic and lane mapping as decode_step_kernel, with the state
+// kept in registers across the tokens: it is read once, and written at most
+// once -- in place, right after token n_commit[n] (n_commit[n] <= 0, or no
+// n_commit at all, leaves it unchanged).  Every token's output is written.
+// The K tokens' gates, keys, queries and write strengths are staged in LDS
+// together before the state loads complete.
+template <typename InT>
+__global__ __launch_bounds__(256) void decode_tokens_kernel(
+    const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
+    const InT* __restrict__ beta, const float* __restrict__ log_alpha,
+    float* __restrict__ state, const int32_t* __restrict__ n_commit, int K, int H,
+    float* __restrict__ o)
+{
+    __shared__ __attribute__((aligned(16))) float sa[kMaxDraft][kDim], sk[kMaxDraft][kDim],
+        sq[kMaxDraft][kDim], sb[kMaxDraft];
+    const int64_t unit = blockIdx.x;  // n * H + h
+    const int64_t n = unit / H;
+    const int h = static_cast<int>(unit - n * H);
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int rg = lane >> 3;
+    const int row0 = 16 * rg;
+    const int col = wave * 32 + (lane & 7) * 4;
+    float* S = state + unit * (kDim * kDim);
+    const int commit = n_commit ? min(max(n_commit[n], 0), K) : 0;
+    auto rowvec = [&](int t) { return ((n * K + t) * H + h) * kDim; };  // token t's [*, 128] row
+
+    // all tokens' per-head inputs are requested first (independent loads), then
+    // the state; both are in flight together
+    float x0[kMaxDraft], x1[kMaxDraft], xb[kMaxDraft];
+#pragma unroll
+    for (int t = 0; t < kMaxDraft; ++t) {
+        if (t < K) {
+            const int64_t vec = rowvec(t);
+            if (tid < kDim) {
+                x0[t] = log_alpha[vec + tid];
+            } else {
+                x0[t] = widen(k[vec + tid - kDim]);
+                x1[t] = widen(q[vec + tid - kDim]);
+            }
+            if (tid == 0) xb[t] = widen(beta[(n * K + t) * H + h]);
+        }
+    }
+    float4 s[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m)
+        s[m] = *reinterpret_cast<const float4*>(S + (row0 + m) * kDim + col);
+    float4 vv = load4(v + rowvec(0) + col);
+#pragma unroll
+    for (int t = 0; t < kMaxDraft; ++t) {
+        if (t < K) {
+            if (tid < kDim) {
+                sa[t][tid] = exp_gate(x0[t]);
+            } else {
+                sk[t][tid - kDim] = x0[t];
+                sq[t][tid - kDim] = x1[t];
+            }
+            if (tid == 0) sb[t] = xb[t];
+        }
+    }
+    __syncthreads();
+
+    for (int t = 0; t < K; ++t) {
+        const float4 vt = vv;
+        if (t + 1 < K) vv = load4(v + rowvec(t + 1) + col);
+        float a[16], kk[16], qq[16];
+#pragma unroll
+        for (int m4 = 0; m4 < 4; ++m4) {
+            const float4 a4 = *reinterpret_cast<const float4*>(&sa[t][row0 + 4 * m4]);
+            const float4 k4 = *reinterpret_cast<const float4*>(&sk[t][row0 + 4 * m4]);
+            const float4 q4 = *reinterpret_cast<const float4*>(&sq[t][row0 + 4 * m4]);
+            a[4 * m4] = a4.x; a[4 * m4 + 1] = a4.y; a[4 * m4 + 2] = a4.z; a[4 * m4 + 3] = a4.w;
+            kk[4 * m4] = k4.x; kk[4 * m4 + 1] = k4.y; kk[4 * m4 + 2] = k4.z; kk[4 * m4 + 3] = k4.w;
+            qq[4 * m4] = q4.x; qq[4 * m4 + 1] = q4.y; qq[4 * m4 + 2] = q4.z; qq[4 * m4 + 3] = q4.w;
+        }
+        const float bt = sb[t];
+        float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+        float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
+        float kq = 0.f;
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            s[m].x *= a[m]; s[m].y *= a[m]; s[m].z *= a[m]; s[m].w *= a[m];
+            p0 += kk[m] * s[m].x; p1 += kk[m] * s[m].y; p2 += kk[m] * s[m].z; p3 += kk[m] * s[m].w;
+            r0 += qq[m] * s[m].x; r1 += qq[m] * s[m].y; r2 += qq[m] * s[m].z; r3 += qq[m] * s[m].w;
+            kq += kk[m] * qq[m];
+        }
+        p0 = xor_sum_rows(p0); p1 = xor_sum_rows(p1); p2 = xor_sum_rows(p2); p3 = xor_sum_rows(p3);
+        r0 = xor_sum_rows(r0); r1 = xor_sum_rows(r1); r2 = xor_sum_rows(r2); r3 = xor_sum_rows(r3);
+        kq = xor_sum_rows(kq);
+        const float u0 = bt * (vt.x - p0), u1 = bt * (vt.y - p1);
+        const float u2 = bt * (vt.z - p2), u3 = bt * (vt.w - p3);
+        if (rg == 0) {
+            *reinterpret_cast<float4*>(o + rowvec(t) + col) =
+                make_float4(r0 + kq * u0, r1 + kq * u1, r2 + kq * u2, r3 + kq * u3);
+        }
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            s[m].x += kk[m] * u0; s[m].y += kk[m] * u1; s[m].z += kk[m] * u2; s[m].w += kk[m] * u3;
+        }
+        if (t + 1 == commit) {
+#pragma unroll
+            for (int m = 0; m < 16; ++m) *reinterpret_cast<float4*>(S + (row0 + m) * kDim + col) = s[m];
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_decode_tokens(const void* q, const void* k, const void* v, const void* beta,
+                                const float* log_alpha, float* state, const int32_t* n_commit,
+                                float* o, int64_t N, int64_t K, int64_t H, bool bf16,
+                                hipStream_t stream)
+{
+    const int64_t units = N * H;
+    if (units <= 0 || K <= 0) return hipSuccess;
+    if (K > kMaxDraft) return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(units)), block(256);
+    if (bf16) {
+        using T = bf16_t;
+        hipLaunchKernelGGL(decode_tokens_kernel<T>, grid, block, 0, stream,
+                           static_cast<const T*>(q), static_cast<const T*>(k),
+                           static_cast<const T*>(v), static_cast<const T*>(beta), log_alpha,
+                           state, n_commit, static_cast<int>(K), static_cast<int>(H), o);
+    } else {
+        hipLaunchKernelGGL(decode_tokens_kernel<float>, grid, block, 0, stream,
+                           static_cast<const float*>(q), static_cast<const float*>(k),
+                           static_cast<const float*>(v), static_cast<const float*>(beta),
+                           log_alpha, state, n_commit, static_cast<int>(K), static_cast<int>(H), o);
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_decode_step(const void* q, const void* k, const void* v, const void* beta,
                               const float* log_alpha, float* state, const int32_t* slots,

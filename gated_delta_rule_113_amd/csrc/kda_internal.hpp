@@ -32,6 +32,15 @@ hipError_t launch_decode_step(const void* q, const void* k, const void* v, const
                               int64_t n_pool, float* o, int64_t units, int64_t H, bool bf16,
                               hipStream_t stream);
 
+// K (<= kMaxDraft) consecutive tokens of each of N sequences from its state
+// (inputs [N, K, H, *], outputs [N, K, H, 128]); with n_commit the state is
+// overwritten in place by the state after the first n_commit[n] tokens.
+constexpr int64_t kMaxDraft = 16;
+hipError_t launch_decode_tokens(const void* q, const void* k, const void* v, const void* beta,
+                                const float* log_alpha, float* state, const int32_t* n_commit,
+                                float* o, int64_t N, int64_t K, int64_t H, bool bf16,
+                                hipStream_t stream);
+
 // Token-by-token prefill with the state held in registers.  Dense when
 // cu_seqlens == nullptr (sequence n = rows n*T .. n*T+T-1), packed otherwise.
 hipError_t launch_prefill_recurrent(const void* q, const void* k, const void* v,

@@ -132,6 +132,30 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v, const vo
                            kda_dtype in_dtype, void *stream);
 
 /*
+ * K consecutive tokens (1 <= K <= 16) of each of N sequences from its current
+ * state, for speculative decoding: verify K draft tokens in one pass, then
+ * keep the accepted prefix.  The pages name speculative decoding among the
+ * serving techniques ("Kimi K3 -- the architecture and infrastructure,
+ * explained", component table); the per-token update is the decode step's.
+ *   q, k, log_alpha : [N, K, H, d_k];  v : [N, K, H, d_v];  beta : [N, K, H]
+ *   o      : [N, K, H, d_v] fp32, written for all K tokens
+ *   state  : [N, H, d_k, d_v] fp32.  Without n_commit it is only read (verify).
+ *   n_commit : int32 [N] in DEVICE memory, or NULL.  With it, sequence n's
+ *            state is replaced IN PLACE by the state after its first
+ *            n_commit[n] tokens (values are clamped to [0, K]; 0 leaves it
+ *            unchanged).  Rolling back to an accepted prefix is a second call
+ *            with the accepted counts: the tokens are recomputed from the
+ *            unchanged state, which moves fewer bytes than keeping a state
+ *            checkpoint per draft token.
+ * Each head's state is read once and written at most once.  N = 0 is a no-op;
+ * K outside [1, 16] is KDA_ERR_SHAPE.
+ */
+kda_status kda_decode_tokens(const void *q, const void *k, const void *v, const void *beta,
+                             const float *log_alpha, float *state, const int32_t *n_commit,
+                             float *o, int64_t N, int64_t K, int64_t H, int64_t d_k, int64_t d_v,
+                             kda_dtype in_dtype, void *stream);
+
+/*
  * State pool addressed by slot (serving: continuous batching and a prefill
  * cache whose states are restored and updated without copies).  The pages
  * describe a cached prefill state that is restored so only the new suffix is

@@ -38,7 +38,7 @@ def _declared():
 def test_exports_match_header(lib):
     declared = _declared()
     assert declared == {"kda_prefill", "kda_varlen_prefill", "kda_decode_step",
-                        "kda_decode_step_slots", "kda_varlen_prefill_slots",
+                        "kda_decode_tokens", "kda_decode_step_slots", "kda_varlen_prefill_slots",
                         "kda_set_prefill_segment", "kda_status_str", "kda_abi_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", kda._binding.LIBRARY],
                          capture_output=True, text=True, check=True).stdout
@@ -130,6 +130,24 @@ def varlen_slots(lib, q=P, k=P, v=P, beta=P, la=P, cu=P, N=2, Tt=8, pool=P, si=P
                  o=P, H=2, dk=128, dv=128, dt=1):
     return lib.kda_varlen_prefill_slots(q, k, v, beta, la, cu, N, Tt, pool, si, sf, n_pool, o, H,
                                         dk, dv, dt, None)
+
+
+def decode_tokens(lib, q=P, k=P, v=P, beta=P, la=P, st=P, nc=None, o=P, N=2, K=4, H=2, dk=128,
+                  dv=128, dt=1):
+    return lib.kda_decode_tokens(q, k, v, beta, la, st, nc, o, N, K, H, dk, dv, dt, None)
+
+
+def test_decode_tokens_validation(lib):
+    for name in ("q", "k", "v", "beta", "la", "st", "o"):
+        assert decode_tokens(lib, **{name: None}) == NULL, name
+        assert decode_tokens(lib, **{name: MIS}) == ALIGN, name
+    assert decode_tokens(lib, nc=MIS) == ALIGN
+    assert decode_tokens(lib, K=0) == SHAPE
+    assert decode_tokens(lib, K=17) == SHAPE       # at most 16 draft tokens
+    assert decode_tokens(lib, N=-1) == SHAPE
+    assert decode_tokens(lib, dk=16) == UNSUP
+    assert decode_tokens(lib, dt=4) == DTYPE
+    assert decode_tokens(lib, N=0, q=None, st=None) == OK
 
 
 def test_decode_slots_validation(lib):
