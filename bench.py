@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--batch", type=int, default=64)
     ap.add_argument("--heads", type=int, default=32)
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
+    ap.add_argument("--no-tokens", action="store_true",
+                    help="skip the multi-token (speculative verify / commit) decode measurement")
     ap.add_argument("--no-slots", action="store_true",
                     help="skip the decode measurement with the states in a slot-addressed pool")
     ap.add_argument("--eager", action="store_true",
@@ -296,6 +298,52 @@ def main():
                          "frac": sgbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": bytes_per_launch},
         }
         del pool, sgraph
+
+    # ---------------- K draft tokens per call (secondary) --------------------
+    # Speculative decoding: verify K = 4 draft tokens of every sequence in one
+    # call (state only read), then commit an accepted prefix (a second call
+    # that recomputes the tokens and rewrites the state).
+    if not args.no_tokens:
+        Kd = 4
+        tq, tk, tv, tb, tla = (x[:Kd].transpose(0, 1).contiguous() for x in (q, k, v, beta, la))
+        tstate = state0.clone()
+        to = torch.empty((B, Kd, H, D), dtype=torch.float32, device=dev)
+        commit = torch.full((B,), 2, dtype=torch.int32, device=dev)
+
+        def timed(fn, reps=50):
+            fn()
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / reps
+
+        vms = timed(lambda: kda.kda_decode_tokens(tq, tk, tv, tb, tla, tstate, out=to))
+        cms = timed(lambda: kda.kda_decode_tokens(tq, tk, tv, tb, tla, tstate, commit, out=to))
+        in_bytes = Kd * B * H * (3 * D * 2 + 2 + D * 4 + D * 4)   # q, k, v, beta, log_alpha in; o out
+        st_bytes = B * H * D * D * 4
+        vgbs = (st_bytes + in_bytes) / (vms / 1e3) / 1e9
+        cgbs = (2 * st_bytes + in_bytes) / (cms / 1e3) / 1e9
+        log(f"verify {Kd} tokens: {vms * 1e3:.2f} us ({vgbs:.0f} GB/s); commit: {cms * 1e3:.2f} us "
+            f"({cgbs:.0f} GB/s)")
+        result["decode_tokens"] = {
+            "workload": f"B={B} x H={H}, K={Kd} draft tokens per sequence from its state "
+                        "(speculative verify, then commit of an accepted prefix)",
+            "verify_ms": vms,
+            "verify_tokens_per_s": B * Kd / (vms / 1e3),
+            "commit_ms": cms,
+            "roofline_verify": {"bound": "hbm", "achieved": vgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": vgbs / HBM_PEAK_GBS,
+                                "algorithmic_bytes_per_launch": st_bytes + in_bytes},
+            "roofline_commit": {"bound": "hbm", "achieved": cgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": cgbs / HBM_PEAK_GBS,
+                                "algorithmic_bytes_per_launch": 2 * st_bytes + in_bytes},
+        }
+        del tq, tk, tv, tb, tla, tstate, to
 
     # ---------------- prefill (secondary) ---------------------------------
     if not args.no_prefill:
