@@ -57,13 +57,19 @@ __device__ __forceinline__ float* final_state_of(const StateRefs& r, int64_t n, 
     return r.fin + (e * H + h) * (kDim * kDim);
 }
 
+// Sum over the 8 lanes that differ in lane bits 3..5 (the 8 row groups of a
+// wave), without the LDS crossbar: lane l ^ 8 through a DPP rotate by 8 within
+// each 16-lane row; l ^ 16 and l ^ 32 through the gfx950 lane-swap
+// instructions.  permlane16_swap(x, x) returns, in every lane, the values of
+// the even and of the odd row of its row pair (their sum is x[l] + x[l ^ 16]);
+// permlane32_swap(x, x) those of the lower and upper half-wave.
 __device__ __forceinline__ float xor_sum_rows(float x)
 {
-    // sum over lanes that differ in bits 3..5 (the 8 row groups of a wave)
-    x += __shfl_xor(x, 8);
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+    const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+    const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
 }
 
 }  // namespace kda
