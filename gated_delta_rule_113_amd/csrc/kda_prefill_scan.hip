@@ -109,7 +109,11 @@ constexpr int OFF_V = OFF_P_LO + 8192;
 constexpr int OFF_BETA = OFF_V + CH * V_LD;
 constexpr int OFF_EL = OFF_BETA + CH * 4;
 constexpr int OFF_UNSAFE = OFF_EL + kDim * 4;
-constexpr int LDS_BYTES = OFF_UNSAFE + 16 * 4;
+// the diagonal 16x16 blocks of T (fp32, rows of TD_LD floats), apart from
+// the partial sums that share phase 4 with them
+constexpr int TD_LD = 20;
+constexpr int OFF_TD = OFF_UNSAFE + 16 * 4;
+constexpr int LDS_BYTES = OFF_TD + 4 * 16 * TD_LD * 4;
 // the output tile of a chunk (64 x 128 fp32, rows of 32 float4 slots) over T
 // and P, between a chunk's state products and the next chunk's staging
 constexpr int OFF_OT = OFF_T_HI;
@@ -150,6 +154,12 @@ __device__ __forceinline__ int g_off(int row, int pos)
 __device__ __forceinline__ int ke_off(int row, int pos)
 {
     return (row << 7) + ((((pos >> 3) ^ (row >> 1) ^ (row >> 3)) & 7) << 4) + ((pos & 7) << 1);
+}
+
+// byte offset of entry (row, col) of the diagonal T block b
+__device__ __forceinline__ int td_off(int b, int row, int col)
+{
+    return OFF_TD + ((16 * b + row) * TD_LD + col) * 4;
 }
 
 // byte offset of float4 slot `slot` (0..31) of row `row` in the output tile,
@@ -649,23 +659,32 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
                 qk += __shfl_xor(qk, 16);
                 qk += __shfl_xor(qk, 32);
             }
-            // accA[ib][i] = A[r][16ib+4g4+i] over this channel half; the first
-            // half parks its partial sums where N and T will live.
-            if (kh == 0) {
+            // accA[ib][i] = A[r][16ib+4g4+i] and accP likewise, over this
+            // channel half.  The halves are summed in phase 4 by the waves that
+            // finish each product: the second half parks its A, the first its P.
+            if (kh == 1) {
 #pragma unroll
                 for (int ib = 0; ib < 4; ++ib) {
                     if (ib > rb) continue;
-                    const int o4 = (r * N_LD + 16 * ib + 4 * g4) * 4;
-                    at<f32x4>(sm, OFF_N + o4) = accA[ib];
-                    if (OUT) at<f32x4>(sm, OFF_TF + o4) = accP[ib];
+                    at<f32x4>(sm, OFF_N + (r * N_LD + 16 * ib + 4 * g4) * 4) = accA[ib];
+                }
+            } else if (OUT) {
+#pragma unroll
+                for (int ib = 0; ib < 4; ++ib) {
+                    if (ib > rb) continue;
+                    at<f32x4>(sm, OFF_TF + (r * N_LD + 16 * ib + 4 * g4) * 4) = accP[ib];
                 }
             }
         }
         __syncthreads();
 
-        // ======== 4: second halves finish N = Diag(b) A (strictly lower) and P
-        //             (lower, split).
-        // Operand formation (phase 5): thread (tq, cq) covers tokens
+        // ======== 4: the first half of the waves (row block rb = wave) finishes
+        //             N = Diag(b) A (strictly lower) of its row block and, from
+        //             it, the diagonal block T[rb][rb] = (I + N[rb][rb])^-1 by
+        //             forward substitution; the second half finishes P (lower,
+        //             split) of its row block.  Then every thread forms its share
+        //             of the decayed operands.
+        // Operand formation: thread (tq, cq) covers tokens
         // 4tq..4tq+3 x channels 4cq..4cq+3 of Kt, Qt and Ke, held in registers
         // until their LDS regions are free.
         bf16x4 fKh[4], fKl[4], fQh[4], fQl[4], fEh[4], fEl[4];
@@ -695,47 +714,6 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
 #pragma unroll
             for (int x = 0; x < 4; ++x) split_vec(ke[x], fEh[x], fEl[x]);
         };
-        if (kh == 1) {
-            const int r = 16 * rb + l16;
-            const float br = at<float>(sm, OFF_BETA + 4 * r);
-
-#pragma unroll
-            for (int ib = 0; ib < 4; ++ib) {
-                if (ib <= rb) {
-                    const int o4 = (r * N_LD + 16 * ib + 4 * g4) * 4;
-                    const f32x4 pa = at<f32x4>(sm, OFF_N + o4);
-                    f32x4 nn;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int ti = 16 * ib + 4 * g4 + i;
-                        nn[i] = ti < r ? br * (pa[i] + accA[ib][i]) : 0.f;
-                    }
-                    at<f32x4>(sm, OFF_N + o4) = nn;
-                    if (OUT) {
-                        const f32x4 pp = at<f32x4>(sm, OFF_TF + o4);
-                        float x[4];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int ti = 16 * ib + 4 * g4 + i;
-                            x[i] = ti < r ? pp[i] + accP[ib][i] : (ti == r ? qk : 0.f);
-                        }
-                        bf16x4 hi, lo;
-                        split_vec(x, hi, lo);
-                        const int pp0 = perm(16 * ib + 4 * g4);
-                        at<bf16x4>(sm, OFF_P_HI + a128(r, pp0)) = hi;
-                        at<bf16x4>(sm, OFF_P_LO + a128(r, pp0)) = lo;
-                    }
-                } else if (OUT && ib == rb + 1 && (rb & 1) == 0) {
-                    // the upper tile that shares a 32-token step with the diagonal
-                    const int pp0 = perm(16 * ib + 4 * g4);
-                    const bf16x4 zz = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
-                    at<bf16x4>(sm, OFF_P_HI + a128(r, pp0)) = zz;
-                    at<bf16x4>(sm, OFF_P_LO + a128(r, pp0)) = zz;
-                }
-            }
-        }
-        __syncthreads();
-
         // T is consumed as a split A operand: [token][token] bf16 hi and lo,
         // column index permuted like every other k-slot index.
         auto put_t = [&](int row, int tok, float x) {
@@ -745,12 +723,26 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
             at<__bf16>(sm, OFF_T_LO + off) = (__bf16)(x - (float)hb);
         };
 
-        // ======== 5: diagonal 16x16 blocks of T = (I + N)^-1 by forward
-        //             substitution (waves 0-3; lane (jc, p) holds rows 4p..4p+3
-        //             of column jc); then every thread forms its share of the
-        //             decayed operands.
-        if (wave < 4) {
-            const int b = wave, jc = lane >> 2, p = lane & 3;
+        if (kh == 0) {
+            const int r = 16 * rb + l16;
+            const float br = at<float>(sm, OFF_BETA + 4 * r);
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib) {
+                if (ib > rb) continue;
+                const int o4 = (r * N_LD + 16 * ib + 4 * g4) * 4;
+                const f32x4 pa = at<f32x4>(sm, OFF_N + o4);
+                f32x4 nn;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int ti = 16 * ib + 4 * g4 + i;
+                    nn[i] = ti < r ? br * (pa[i] + accA[ib][i]) : 0.f;
+                }
+                at<f32x4>(sm, OFF_N + o4) = nn;
+            }
+            // T[b][b] for b = rb from this wave's own diagonal N block (read
+            // back in order after its writes); lane (jc, p) holds rows
+            // 4p..4p+3 of column jc
+            const int b = rb, jc = lane >> 2, p = lane & 3;
             float4 nv[16];
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr)
@@ -765,11 +757,35 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
                 const float tr = (rr == jc ? 1.f : 0.f) - s;
                 if (p == (rr >> 2)) tv[rr & 3] = tr;
             }
-            float* Tf = &at<float>(sm, OFF_TF);
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                Tf[(16 * b + 4 * p + m) * N_LD + 16 * b + jc] = tv[m];
+                at<float>(sm, td_off(b, 4 * p + m, jc)) = tv[m];
                 put_t(16 * b + 4 * p + m, 16 * b + jc, tv[m]);
+            }
+        } else if (OUT) {
+            const int r = 16 * rb + l16;
+#pragma unroll
+            for (int ib = 0; ib < 4; ++ib) {
+                if (ib <= rb) {
+                    const f32x4 pp = at<f32x4>(sm, OFF_TF + (r * N_LD + 16 * ib + 4 * g4) * 4);
+                    float x[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int ti = 16 * ib + 4 * g4 + i;
+                        x[i] = ti < r ? pp[i] + accP[ib][i] : (ti == r ? qk : 0.f);
+                    }
+                    bf16x4 hi, lo;
+                    split_vec(x, hi, lo);
+                    const int pp0 = perm(16 * ib + 4 * g4);
+                    at<bf16x4>(sm, OFF_P_HI + a128(r, pp0)) = hi;
+                    at<bf16x4>(sm, OFF_P_LO + a128(r, pp0)) = lo;
+                } else if (ib == rb + 1 && (rb & 1) == 0) {
+                    // the upper tile that shares a 32-token step with the diagonal
+                    const int pp0 = perm(16 * ib + 4 * g4);
+                    const bf16x4 zz = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+                    at<bf16x4>(sm, OFF_P_HI + a128(r, pp0)) = zz;
+                    at<bf16x4>(sm, OFF_P_LO + a128(r, pp0)) = zz;
+                }
             }
         }
         form();
@@ -792,14 +808,14 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
 #pragma unroll
                     for (int m = A; m < b; ++m)
                         nb[b][m] = at<float4>(sm, OFF_N + ((16 * b + l16) * N_LD + 16 * m + 4 * g4) * 4);
-                    db[b] = at<float4>(sm, OFF_TF + ((16 * b + l16) * N_LD + 16 * b + 4 * g4) * 4);
+                    db[b] = at<float4>(sm, td_off(b, l16, 4 * g4));
                 }
                 bf16x4 bh[4], bl[4];
                 {
                     float da[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        da[e] = at<float>(sm, OFF_TF + ((16 * A + 4 * g4 + e) * N_LD + 16 * A + l16) * 4);
+                        da[e] = at<float>(sm, td_off(A, 4 * g4 + e, l16));
                     split_vec(da, bh[A], bl[A]);
                 }
 #pragma unroll
