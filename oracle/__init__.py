@@ -67,6 +67,9 @@ def load(path: str | None = None):
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             fp, fp, fp, fp, fp, dp, dp, dp, ctypes.c_int]
         lib.kda_oracle_run.restype = ctypes.c_int
+        lib.kda_oracle_prepare.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                           fp, fp, fp, fp, ctypes.c_int, fp, fp, fp, fp]
+        lib.kda_oracle_prepare.restype = ctypes.c_int
         lib.kda_oracle_max_threads.argtypes = [ctypes.c_int]
         lib.kda_oracle_max_threads.restype = ctypes.c_int
         if path is None:
@@ -190,6 +193,29 @@ def decode_chain(q, k, v, beta, log_alpha, state, n_threads: int = 0, lib=None):
                     np.reshape(log_alpha, (steps * N, H, dk)), row0, length, N,
                     state, n_threads, lib)
     return o.reshape(steps, N, H, dv), s
+
+
+def prepare(q_raw, k_raw, b_raw, a_raw, round_bf16: bool = True, lib=None):
+    """Inputs from raw projections (see ``kda_oracle_prepare``): unit q and k
+    per (token, head), rounded to bf16 when ``round_bf16``; beta =
+    sigmoid(b_raw); log_alpha = -softplus(a_raw).  q_raw, k_raw, a_raw
+    [..., H, dk]; b_raw [..., H].  Returns float32 (q, k, beta, log_alpha)."""
+    lib = lib or load()
+    q_raw = _f32(q_raw, "q_raw"); k_raw = _f32(k_raw, "k_raw")
+    b_raw = _f32(b_raw, "b_raw"); a_raw = _f32(a_raw, "a_raw")
+    H, dk = q_raw.shape[-2:]
+    if k_raw.shape != q_raw.shape or a_raw.shape != q_raw.shape or b_raw.shape != q_raw.shape[:-1]:
+        raise ValueError("q_raw, k_raw, a_raw must share [..., H, dk] and b_raw be [..., H]")
+    rows = int(np.prod(q_raw.shape[:-2], dtype=np.int64))
+    q, k = np.empty_like(q_raw), np.empty_like(k_raw)
+    beta, la = np.empty_like(b_raw), np.empty_like(a_raw)
+    rc = lib.kda_oracle_prepare(rows, H, dk, _ptr(q_raw, ctypes.c_float), _ptr(k_raw, ctypes.c_float),
+                                _ptr(b_raw, ctypes.c_float), _ptr(a_raw, ctypes.c_float),
+                                int(bool(round_bf16)), _ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float),
+                                _ptr(beta, ctypes.c_float), _ptr(la, ctypes.c_float))
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_prepare failed with code {rc}")
+    return q, k, beta, la
 
 
 def max_threads(n_threads: int = 0) -> int:

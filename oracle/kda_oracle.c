@@ -163,3 +163,62 @@ int kda_oracle_run(int64_t n_seq, const int64_t *row0, const int64_t *len, int64
     }
     return failed ? -2 : 0;
 }
+
+/*
+ * Input preparation from raw projections (the oracle of the library's "raw"
+ * entry points).  The pages say KDA has two learned gate parameters -- beta,
+ * the writing strength, and alpha, the forgetting factor ("Inside Kimi K3:
+ * How Moonshot AI Built the Largest Open-Source Model", section "Technical
+ * Details") -- but not how they are parameterised; the readings here are the
+ * plainest ones that keep beta in (0, 1) and alpha in (0, 1):
+ *   beta      = 1 / (1 + exp(-b_raw))                  (logistic sigmoid)
+ *   log_alpha = -log(1 + exp(a_raw))                   (minus softplus)
+ * and q and k are unit vectors per (row, head):
+ *   q = q_raw / ||q_raw||_2,  k = k_raw / ||k_raw||_2  (a zero vector stays zero)
+ * With round_bf16 set, the normalised q and k are rounded to bfloat16 (8
+ * significant bits, round to nearest, ties to even), as they are when the
+ * library stages bf16 inputs.  All arithmetic is fp64; results are stored as
+ * fp32 (q and k then hold exact bf16 values).
+ *   q_raw, k_raw : rows x H x dk;  b_raw : rows x H;  a_raw : rows x H x dk
+ * Returns 0, or -1 on bad sizes.
+ */
+static double round_bf16(double x)
+{
+    if (x == 0.0 || !isfinite(x)) return x;
+    int e;
+    const double m = frexp(x, &e);          /* x = m 2^e, 0.5 <= |m| < 1 */
+    return ldexp(nearbyint(ldexp(m, 8)), e - 8);  /* 8 significant bits, ties to even */
+}
+
+static void unit_vector(const float *x, int64_t dk, int round, float *out)
+{
+    double ss = 0.0;
+    for (int64_t i = 0; i < dk; ++i) ss += (double)x[i] * (double)x[i];
+    const double inv = ss > 0.0 ? 1.0 / sqrt(ss) : 0.0;
+    for (int64_t i = 0; i < dk; ++i) {
+        const double y = (double)x[i] * inv;
+        out[i] = (float)(round ? round_bf16(y) : y);
+    }
+}
+
+int kda_oracle_prepare(int64_t rows, int64_t H, int64_t dk,
+                       const float *q_raw, const float *k_raw, const float *b_raw,
+                       const float *a_raw, int round, float *q, float *k, float *beta,
+                       float *log_alpha)
+{
+    if (rows < 0 || H <= 0 || dk <= 0) return -1;
+    for (int64_t rh = 0; rh < rows * H; ++rh) {
+        /* normalise each (row, head) vector on its own */
+        unit_vector(q_raw + rh * dk, dk, round, q + rh * dk);
+        unit_vector(k_raw + rh * dk, dk, round, k + rh * dk);
+        /* write strength */
+        beta[rh] = (float)(1.0 / (1.0 + exp(-(double)b_raw[rh])));
+        /* forgetting gate: log_alpha = -softplus(a), evaluated without overflow */
+        for (int64_t i = 0; i < dk; ++i) {
+            const double a = (double)a_raw[rh * dk + i];
+            const double sp = a > 0.0 ? a + log1p(exp(-a)) : log1p(exp(a));
+            log_alpha[rh * dk + i] = (float)(-sp);
+        }
+    }
+    return 0;
+}

@@ -370,9 +370,60 @@ def pin_varlen_and_layouts(lib=None):
     assert np.array_equal(Sc, Sp)
 
 
+# ---------------------------------------------------------------------------
+# input preparation from raw projections (oracle.prepare)
+# ---------------------------------------------------------------------------
+
+def pin_prepare_gates(lib=None):
+    """sigmoid and -softplus at points where they have closed forms:
+    sigmoid(0) = 1/2, sigmoid(ln 3) = 3/4, sigmoid(x) + sigmoid(-x) = 1;
+    softplus(0) = ln 2, softplus(x) - softplus(-x) = x, softplus(x) ~ x for
+    large x and ~ e^x for very negative x."""
+    H, dk = 2, 4
+    b = np.array([[0.0, math.log(3.0)], [2.5, -2.5]], np.float32)
+    a = np.array([0.0, 1.75, -1.75, 40.0, -40.0, 0.5, -0.5, 3.0], np.float32).reshape(1, H, dk)
+    a = np.repeat(a, 2, axis=0)
+    z = np.ones((2, H, dk), np.float32)
+    _, _, beta, la = oracle.prepare(z, z, b, a, lib=lib)
+    assert beta[0, 0] == 0.5
+    assert abs(beta[0, 1] - 0.75) < 1e-7
+    assert abs(float(beta[1, 0]) + float(beta[1, 1]) - 1.0) < 1e-6
+    assert 0.92 < beta[1, 0] < 0.93                    # sigmoid(2.5) = 0.924...
+    assert abs(la[0, 0, 0] + math.log(2.0)) < 1e-7
+    assert abs((float(la[0, 0, 1]) - float(la[0, 0, 2])) - (-1.75)) < 1e-6
+    assert abs(la[0, 0, 3] + 40.0) < 1e-5                 # -softplus(40) = -40 - e^-40
+    assert abs(la[0, 1, 0] + math.exp(-40.0)) < 1e-24     # -softplus(-40) = -e^-40
+    assert np.all(la < 0)
+
+
+def pin_prepare_unit_vectors(lib=None):
+    """Per (token, head) unit vectors: (3, 4, 0, 0) / 5 = (0.6, 0.8), which
+    round to the bf16 values 0.6015625 and 0.80078125 (8 significant bits);
+    a scaled axis vector gives the axis exactly; the zero vector stays zero;
+    heads of very different scale are normalised independently; without
+    rounding the norm is 1 to fp32 accuracy."""
+    H, dk = 3, 4
+    q = np.array([[[3, 4, 0, 0], [0, 0, -250.0, 0], [0, 0, 0, 0]]], np.float32)
+    k = np.array([[[1e-3, 0, 0, 0], [1e3, 1e3, 1e3, 1e3], [0, 5, 0, 0]]], np.float32)
+    b = np.zeros((1, H), np.float32)
+    qq, kk, _, _ = oracle.prepare(q, k, b, np.zeros((1, H, dk), np.float32), lib=lib)
+    assert np.array_equal(qq[0, 0], np.array([0.6015625, 0.80078125, 0, 0], np.float32))
+    assert np.array_equal(qq[0, 1], np.array([0, 0, -1, 0], np.float32))
+    assert np.array_equal(qq[0, 2], np.zeros(dk, np.float32))
+    assert np.array_equal(kk[0, 0], np.array([1, 0, 0, 0], np.float32))
+    assert np.array_equal(kk[0, 1], np.full(dk, 0.5, np.float32))
+    assert np.array_equal(kk[0, 2], np.array([0, 1, 0, 0], np.float32))
+    r = _rng(9).standard_normal((5, H, 16)).astype(np.float32) * np.array([1e-3, 1.0, 1e3], np.float32)[:, None]
+    qn, _, _, _ = oracle.prepare(r, r, np.zeros((5, H), np.float32), np.zeros((5, H, 16), np.float32),
+                                 round_bf16=False, lib=lib)
+    assert np.allclose(np.linalg.norm(qn.astype(np.float64), axis=-1), 1.0, atol=1e-6)
+    cos = np.sum(qn.astype(np.float64) * r, axis=-1) / np.linalg.norm(r.astype(np.float64), axis=-1)
+    assert np.allclose(cos, 1.0, atol=1e-6)
+
+
 ALL_PINS = [
     pin_bruteforce_numpy, pin_bruteforce_exact, pin_identity, pin_erase_then_write,
     pin_decay_closed_form, pin_channel_locality, pin_page_delta_rule,
     pin_causal_linear_attention, pin_scalar_gate, pin_resume, pin_linearity,
-    pin_varlen_and_layouts,
+    pin_varlen_and_layouts, pin_prepare_gates, pin_prepare_unit_vectors,
 ]

@@ -1,7 +1,9 @@
 """Plant plausible mistakes in a copy of the oracle (on the CPU) and require
 each one to be caught by at least one pin.  This shows the pins constrain
 every step of the recurrence: the decay, the recall, the compare, the
-write, the read-out, the gate indexing, the token order and the state hand-off.
+write, the read-out, the gate indexing, the token order and the state hand-off;
+and every step of the input preparation: the gate functions, the per-head
+normalisation and the bf16 rounding.
 """
 import os
 import shutil
@@ -61,6 +63,15 @@ MUTANTS = {
                                 "const int64_t row = row0[n] + (len[n] - 1 - t) * row_step;"),
     "beta_wrong_head": _replace("bt = (double)beta[row * H + h];", "bt = (double)beta[row * H];"),
     "gate_wrong_head": _replace("log_alpha + (row * H + h) * dk;", "log_alpha + (row * H) * dk;"),
+    "sigmoid_sign": _replace("beta[rh] = (float)(1.0 / (1.0 + exp(-(double)b_raw[rh])));",
+                             "beta[rh] = (float)(1.0 / (1.0 + exp((double)b_raw[rh])));"),
+    "softplus_sign": _replace("log_alpha[rh * dk + i] = (float)(-sp);", "log_alpha[rh * dk + i] = (float)(sp);"),
+    "softplus_as_plain_log": _replace("log1p(exp(a));", "log(exp(a) + 1e-3);"),
+    "norm_of_half_vector": _replace("for (int64_t i = 0; i < dk; ++i) ss += (double)x[i] * (double)x[i];",
+                                    "for (int64_t i = 0; i < dk / 2; ++i) ss += (double)x[i] * (double)x[i];"),
+    "no_bf16_rounding": _replace("out[i] = (float)(round ? round_bf16(y) : y);", "out[i] = (float)y;"),
+    "bf16_truncated": _replace("return ldexp(nearbyint(ldexp(m, 8)), e - 8);",
+                               "return ldexp(trunc(ldexp(m, 8)), e - 8);"),
     "gate_off_by_one_token": _replace("const float *lat = log_alpha + (row * H + h) * dk;",
                                       "const float *lat = log_alpha + ((t ? row - row_step : row) * H + h) * dk;"),
 }
