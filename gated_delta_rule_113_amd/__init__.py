@@ -7,6 +7,9 @@ ABI of ``include/kda.h``); this package is its thin Python binding:
     kda_varlen_prefill(q, k, v, beta, log_alpha, cu_seqlens, initial_state=None)
         -> (o, final_state)
     kda_decode_step(q, k, v, beta, log_alpha, state) -> o      (state in place)
+    kda_prefill_raw / kda_varlen_prefill_raw / kda_decode_step_raw
+        (the same on raw projections: q, k normalised, beta and log_alpha
+        logits, all inside the kernels)
     kda_decode_tokens(q, k, v, beta, log_alpha, state, n_commit=None) -> o
         (K draft tokens from the state; commits an accepted prefix in place)
     kda_decode_step_slots(q, k, v, beta, log_alpha, state_pool, slots) -> o
@@ -22,15 +25,19 @@ from ._binding import (  # noqa: F401
     KDA_F32,
     KDAError,
     kda_decode_step,
+    kda_decode_step_raw,
     kda_decode_step_slots,
     kda_decode_tokens,
     kda_prefill,
+    kda_prefill_raw,
     kda_set_prefill_segment,
     kda_varlen_prefill,
+    kda_varlen_prefill_raw,
     kda_varlen_prefill_slots,
     load_library,
 )
 
-__all__ = ["kda_prefill", "kda_varlen_prefill", "kda_decode_step", "kda_decode_tokens",
+__all__ = ["kda_prefill", "kda_varlen_prefill", "kda_decode_step", "kda_prefill_raw",
+           "kda_varlen_prefill_raw", "kda_decode_step_raw", "kda_decode_tokens",
            "kda_decode_step_slots",
            "kda_varlen_prefill_slots", "kda_set_prefill_segment", "KDAError", "load_library"]

@@ -20,7 +20,8 @@ STATUS_NAMES = {
     0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
     4: "KDA_ERR_ALIGN", 5: "KDA_ERR_UNSUPPORTED", 6: "KDA_ERR_HIP",
 }
-EXPORTS = ("kda_prefill", "kda_varlen_prefill", "kda_decode_step", "kda_decode_tokens",
+EXPORTS = ("kda_prefill", "kda_varlen_prefill", "kda_decode_step", "kda_prefill_raw",
+           "kda_varlen_prefill_raw", "kda_decode_step_raw", "kda_decode_tokens",
            "kda_decode_step_slots", "kda_varlen_prefill_slots", "kda_set_prefill_segment",
            "kda_status_str", "kda_abi_version")
 
@@ -58,12 +59,18 @@ def load_library(path: str | None = None):
         lib.kda_prefill.argtypes = [vp, vp, vp, vp, f32p, f32p, f32p, f32p,
                                     i64, i64, i64, i64, i64, ctypes.c_int, vp]
         lib.kda_prefill.restype = ctypes.c_int
+        lib.kda_prefill_raw.argtypes = lib.kda_prefill.argtypes
+        lib.kda_prefill_raw.restype = ctypes.c_int
         lib.kda_varlen_prefill.argtypes = [vp, vp, vp, vp, f32p, vp, i64, i64,
                                            f32p, f32p, f32p, i64, i64, i64, ctypes.c_int, vp]
         lib.kda_varlen_prefill.restype = ctypes.c_int
+        lib.kda_varlen_prefill_raw.argtypes = lib.kda_varlen_prefill.argtypes
+        lib.kda_varlen_prefill_raw.restype = ctypes.c_int
         lib.kda_decode_step.argtypes = [vp, vp, vp, vp, f32p, f32p, f32p,
                                         i64, i64, i64, i64, ctypes.c_int, vp]
         lib.kda_decode_step.restype = ctypes.c_int
+        lib.kda_decode_step_raw.argtypes = lib.kda_decode_step.argtypes
+        lib.kda_decode_step_raw.restype = ctypes.c_int
         lib.kda_decode_tokens.argtypes = [vp, vp, vp, vp, f32p, f32p, vp, f32p,
                                           i64, i64, i64, i64, i64, ctypes.c_int, vp]
         lib.kda_decode_tokens.restype = ctypes.c_int
@@ -133,7 +140,8 @@ def _require(t, name, dtype=None, shape=None, device=None):
     return t
 
 
-def kda_prefill(q, k, v, beta, log_alpha, initial_state=None, *, out=None, final_state=None):
+def kda_prefill(q, k, v, beta, log_alpha, initial_state=None, *, out=None, final_state=None,
+                _fn="kda_prefill"):
     """Dense prefill.  q, k, log_alpha [B, T, H, 128]; v [B, T, H, 128];
     beta [B, T, H]; initial_state [B, H, 128, 128] fp32 or None.
 
@@ -157,15 +165,15 @@ def kda_prefill(q, k, v, beta, log_alpha, initial_state=None, *, out=None, final
     if final_state is None:
         final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     _require(final_state, "final_state", torch.float32, (B, H, dk, dv), dev)
-    code = lib.kda_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
-                           _ptr(initial_state), _ptr(o), _ptr(final_state),
-                           B, T, H, dk, dv, _in_dtype(q, k, v, beta), _stream(dev))
-    _check(lib, "kda_prefill", code)
+    code = getattr(lib, _fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
+                             _ptr(initial_state), _ptr(o), _ptr(final_state),
+                             B, T, H, dk, dv, _in_dtype(q, k, v, beta), _stream(dev))
+    _check(lib, _fn, code)
     return o, final_state
 
 
 def kda_varlen_prefill(q, k, v, beta, log_alpha, cu_seqlens, initial_state=None, *,
-                       out=None, final_state=None):
+                       out=None, final_state=None, _fn="kda_varlen_prefill"):
     """Packed prefill.  q, k, log_alpha [1, T_total, H, 128] (or [T_total, H, 128]);
     cu_seqlens int32 [N + 1] on the GPU; initial_state [N, H, 128, 128] or None.
 
@@ -195,11 +203,11 @@ def kda_varlen_prefill(q, k, v, beta, log_alpha, cu_seqlens, initial_state=None,
     if final_state is None:
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     _require(final_state, "final_state", torch.float32, (N, H, dk, dv), dev)
-    code = lib.kda_varlen_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
-                                  _ptr(cu_seqlens), N, Tt, _ptr(initial_state), _ptr(o),
-                                  _ptr(final_state), H, dk, dv, _in_dtype(q, k, v, beta),
-                                  _stream(dev))
-    _check(lib, "kda_varlen_prefill", code)
+    code = getattr(lib, _fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
+                             _ptr(cu_seqlens), N, Tt, _ptr(initial_state), _ptr(o),
+                             _ptr(final_state), H, dk, dv, _in_dtype(q, k, v, beta),
+                             _stream(dev))
+    _check(lib, _fn, code)
     return o, final_state
 
 
@@ -209,7 +217,7 @@ def kda_set_prefill_segment(tokens: int) -> None:
     _check(lib, "kda_set_prefill_segment", lib.kda_set_prefill_segment(int(tokens)))
 
 
-def kda_decode_step(q, k, v, beta, log_alpha, state, *, out=None):
+def kda_decode_step(q, k, v, beta, log_alpha, state, *, out=None, _fn="kda_decode_step"):
     """One decode step.  q, k, log_alpha [N, H, 128]; v [N, H, 128]; beta [N, H];
     state [N, H, 128, 128] fp32, updated in place.  Returns o [N, H, 128] fp32."""
     torch = _torch()
@@ -225,10 +233,10 @@ def kda_decode_step(q, k, v, beta, log_alpha, state, *, out=None):
     _require(state, "state", torch.float32, (N, H, dk, dv), dev)
     o = out if out is not None else torch.empty((N, H, dv), dtype=torch.float32, device=dev)
     _require(o, "out", torch.float32, (N, H, dv), dev)
-    code = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
-                               _ptr(state), _ptr(o), N, H, dk, dv, _in_dtype(q, k, v, beta),
-                               _stream(dev))
-    _check(lib, "kda_decode_step", code)
+    code = getattr(lib, _fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
+                             _ptr(state), _ptr(o), N, H, dk, dv, _in_dtype(q, k, v, beta),
+                             _stream(dev))
+    _check(lib, _fn, code)
     return o
 
 
@@ -336,3 +344,24 @@ def kda_decode_tokens(q, k, v, beta, log_alpha, state, n_commit=None, *, out=Non
                                  _in_dtype(q, k, v, beta), _stream(dev))
     _check(lib, "kda_decode_tokens", code)
     return o
+
+
+def kda_prefill_raw(q, k, v, beta, log_alpha, initial_state=None, *, out=None, final_state=None):
+    """kda_prefill on raw projections: q and k are normalised per (token, head)
+    inside the kernels (and rounded to bf16 for bf16 inputs), ``beta`` holds
+    logits (write strength sigmoid(beta)) and ``log_alpha`` gate logits a
+    (log forgetting factor -softplus(a))."""
+    return kda_prefill(q, k, v, beta, log_alpha, initial_state, out=out, final_state=final_state,
+                       _fn="kda_prefill_raw")
+
+
+def kda_varlen_prefill_raw(q, k, v, beta, log_alpha, cu_seqlens, initial_state=None, *, out=None,
+                           final_state=None):
+    """kda_varlen_prefill on raw projections (see kda_prefill_raw)."""
+    return kda_varlen_prefill(q, k, v, beta, log_alpha, cu_seqlens, initial_state, out=out,
+                              final_state=final_state, _fn="kda_varlen_prefill_raw")
+
+
+def kda_decode_step_raw(q, k, v, beta, log_alpha, state, *, out=None):
+    """kda_decode_step on raw projections (see kda_prefill_raw)."""
+    return kda_decode_step(q, k, v, beta, log_alpha, state, out=out, _fn="kda_decode_step_raw")

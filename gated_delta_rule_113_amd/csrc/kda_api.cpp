@@ -58,13 +58,13 @@ kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HI
 hipError_t launch_prefill(const void* q, const void* k, const void* v, const void* beta,
                           const float* log_alpha, const int32_t* cu_seqlens, int64_t n_seq,
                           int64_t T, int64_t T_total, int64_t H, const kda::StateRefs& st,
-                          float* o, kda_dtype in_dtype, hipStream_t stream)
+                          float* o, kda_dtype in_dtype, bool raw, hipStream_t stream)
 {
     if (in_dtype == KDA_BF16)
         return kda::launch_prefill_scan(q, k, v, beta, log_alpha, cu_seqlens, n_seq, T, T_total,
-                                        H, st, o, stream);
+                                        H, st, o, raw, stream);
     return kda::launch_prefill_recurrent(q, k, v, beta, log_alpha, cu_seqlens, n_seq, T, H, st,
-                                         o, false, stream);
+                                         o, false, raw, stream);
 }
 
 kda::StateRefs plain_states(const float* initial_state, float* final_state)
@@ -81,14 +81,10 @@ bool pool_too_big(int64_t n_pool, int64_t H)
     return n_pool > kMaxElems / H / (int64_t(kda::kDim) * kda::kDim);
 }
 
-}  // namespace
-
-extern "C" {
-
-kda_status kda_prefill(const void* q, const void* k, const void* v, const void* beta,
+kda_status prefill_impl(const void* q, const void* k, const void* v, const void* beta,
                        const float* log_alpha, const float* initial_state, float* o,
                        float* final_state, int64_t B, int64_t T, int64_t H, int64_t d_k,
-                       int64_t d_v, kda_dtype in_dtype, void* stream)
+                       int64_t d_v, kda_dtype in_dtype, bool raw, void* stream)
 {
     kda_status st;
     if ((st = check_dtype(in_dtype)) != KDA_OK) return st;
@@ -106,15 +102,15 @@ kda_status kda_prefill(const void* q, const void* k, const void* v, const void* 
     }
     if (T == 0 && !final_state) return KDA_OK;
     return from_hip(launch_prefill(q, k, v, beta, log_alpha, nullptr, B, T, B * T, H,
-                                   plain_states(initial_state, final_state), o, in_dtype,
+                                   plain_states(initial_state, final_state), o, in_dtype, raw,
                                    static_cast<hipStream_t>(stream)));
 }
 
-kda_status kda_varlen_prefill(const void* q, const void* k, const void* v, const void* beta,
+kda_status varlen_impl(const void* q, const void* k, const void* v, const void* beta,
                               const float* log_alpha, const int32_t* cu_seqlens, int64_t N,
                               int64_t T_total, const float* initial_state, float* o,
                               float* final_state, int64_t H, int64_t d_k, int64_t d_v,
-                              kda_dtype in_dtype, void* stream)
+                              kda_dtype in_dtype, bool raw, void* stream)
 {
     kda_status st;
     if ((st = check_dtype(in_dtype)) != KDA_OK) return st;
@@ -134,8 +130,80 @@ kda_status kda_varlen_prefill(const void* q, const void* k, const void* v, const
     }
     if (T_total == 0 && !final_state) return KDA_OK;
     return from_hip(launch_prefill(q, k, v, beta, log_alpha, cu_seqlens, N, 0, T_total, H,
-                                   plain_states(initial_state, final_state), o, in_dtype,
+                                   plain_states(initial_state, final_state), o, in_dtype, raw,
                                    static_cast<hipStream_t>(stream)));
+}
+
+kda_status decode_impl(const void* q, const void* k, const void* v, const void* beta,
+                           const float* log_alpha, float* state, float* o, int64_t N, int64_t H,
+                           int64_t d_k, int64_t d_v, kda_dtype in_dtype, bool raw, void* stream)
+{
+    kda_status st;
+    if ((st = check_dtype(in_dtype)) != KDA_OK) return st;
+    if ((st = check_dims(H, d_k, d_v)) != KDA_OK) return st;
+    if (N < 0) return KDA_ERR_SHAPE;
+    if (N > int64_t(1) << 24 || N * H > INT32_MAX) return KDA_ERR_SHAPE;
+    if (N == 0) return KDA_OK;
+    if ((st = check_ptrs({q, k, v, beta, log_alpha, state, o}, {})) != KDA_OK) return st;
+    return from_hip(kda::launch_decode_step(q, k, v, beta, log_alpha, state, nullptr, 0, o, N * H,
+                                            H, in_dtype == KDA_BF16, raw,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_prefill(const void* q, const void* k, const void* v, const void* beta,
+                       const float* log_alpha, const float* initial_state, float* o,
+                       float* final_state, int64_t B, int64_t T, int64_t H, int64_t d_k,
+                       int64_t d_v, kda_dtype in_dtype, void* stream)
+{
+    return prefill_impl(q, k, v, beta, log_alpha, initial_state, o, final_state, B, T, H, d_k, d_v,
+                        in_dtype, false, stream);
+}
+
+kda_status kda_prefill_raw(const void* q, const void* k, const void* v, const void* beta,
+                           const float* log_alpha, const float* initial_state, float* o,
+                           float* final_state, int64_t B, int64_t T, int64_t H, int64_t d_k,
+                           int64_t d_v, kda_dtype in_dtype, void* stream)
+{
+    return prefill_impl(q, k, v, beta, log_alpha, initial_state, o, final_state, B, T, H, d_k, d_v,
+                        in_dtype, true, stream);
+}
+
+kda_status kda_varlen_prefill(const void* q, const void* k, const void* v, const void* beta,
+                              const float* log_alpha, const int32_t* cu_seqlens, int64_t N,
+                              int64_t T_total, const float* initial_state, float* o,
+                              float* final_state, int64_t H, int64_t d_k, int64_t d_v,
+                              kda_dtype in_dtype, void* stream)
+{
+    return varlen_impl(q, k, v, beta, log_alpha, cu_seqlens, N, T_total, initial_state, o,
+                       final_state, H, d_k, d_v, in_dtype, false, stream);
+}
+
+kda_status kda_varlen_prefill_raw(const void* q, const void* k, const void* v, const void* beta,
+                                  const float* log_alpha, const int32_t* cu_seqlens, int64_t N,
+                                  int64_t T_total, const float* initial_state, float* o,
+                                  float* final_state, int64_t H, int64_t d_k, int64_t d_v,
+                                  kda_dtype in_dtype, void* stream)
+{
+    return varlen_impl(q, k, v, beta, log_alpha, cu_seqlens, N, T_total, initial_state, o,
+                       final_state, H, d_k, d_v, in_dtype, true, stream);
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* beta,
+                           const float* log_alpha, float* state, float* o, int64_t N, int64_t H,
+                           int64_t d_k, int64_t d_v, kda_dtype in_dtype, void* stream)
+{
+    return decode_impl(q, k, v, beta, log_alpha, state, o, N, H, d_k, d_v, in_dtype, false, stream);
+}
+
+kda_status kda_decode_step_raw(const void* q, const void* k, const void* v, const void* beta,
+                               const float* log_alpha, float* state, float* o, int64_t N, int64_t H,
+                               int64_t d_k, int64_t d_v, kda_dtype in_dtype, void* stream)
+{
+    return decode_impl(q, k, v, beta, log_alpha, state, o, N, H, d_k, d_v, in_dtype, true, stream);
 }
 
 kda_status kda_varlen_prefill_slots(const void* q, const void* k, const void* v, const void* beta,
@@ -166,23 +234,7 @@ kda_status kda_varlen_prefill_slots(const void* q, const void* k, const void* v,
     refs.fin_slots = final_slots;
     refs.n_pool = n_pool;
     return from_hip(launch_prefill(q, k, v, beta, log_alpha, cu_seqlens, N, 0, T_total, H, refs,
-                                   o, in_dtype, static_cast<hipStream_t>(stream)));
-}
-
-kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* beta,
-                           const float* log_alpha, float* state, float* o, int64_t N, int64_t H,
-                           int64_t d_k, int64_t d_v, kda_dtype in_dtype, void* stream)
-{
-    kda_status st;
-    if ((st = check_dtype(in_dtype)) != KDA_OK) return st;
-    if ((st = check_dims(H, d_k, d_v)) != KDA_OK) return st;
-    if (N < 0) return KDA_ERR_SHAPE;
-    if (N > int64_t(1) << 24 || N * H > INT32_MAX) return KDA_ERR_SHAPE;
-    if (N == 0) return KDA_OK;
-    if ((st = check_ptrs({q, k, v, beta, log_alpha, state, o}, {})) != KDA_OK) return st;
-    return from_hip(kda::launch_decode_step(q, k, v, beta, log_alpha, state, nullptr, 0, o, N * H,
-                                            H, in_dtype == KDA_BF16,
-                                            static_cast<hipStream_t>(stream)));
+                                   o, in_dtype, false, static_cast<hipStream_t>(stream)));
 }
 
 kda_status kda_decode_step_slots(const void* q, const void* k, const void* v, const void* beta,
@@ -199,7 +251,7 @@ kda_status kda_decode_step_slots(const void* q, const void* k, const void* v, co
     if (N == 0) return KDA_OK;
     if ((st = check_ptrs({q, k, v, beta, log_alpha, state_pool, slots, o}, {})) != KDA_OK) return st;
     return from_hip(kda::launch_decode_step(q, k, v, beta, log_alpha, state_pool, slots, n_pool, o,
-                                            N * H, H, in_dtype == KDA_BF16,
+                                            N * H, H, in_dtype == KDA_BF16, false,
                                             static_cast<hipStream_t>(stream)));
 }
 

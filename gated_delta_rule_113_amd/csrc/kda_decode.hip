@@ -27,7 +27,7 @@
 namespace kda {
 namespace {
 
-template <typename InT>
+template <typename InT, bool RAW>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
     const InT* __restrict__ beta, const float* __restrict__ log_alpha,
@@ -65,14 +65,14 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         x1 = widen(q[vec + tid - kDim]);
     }
     const float4 vv = load4(v + vec + col);
-    const float bt = widen(beta[unit]);
+    float bt = widen(beta[unit]);
     float4 s[16];
 #pragma unroll
     for (int m = 0; m < 16; ++m)
         s[m] = *reinterpret_cast<const float4*>(S + (row0 + m) * kDim + col);
 
     if (tid < kDim) {
-        sa[tid] = exp_gate(x0);
+        sa[tid] = RAW ? alpha_from_logit(x0) : exp_gate(x0);
     } else {
         sk[tid - kDim] = x0;
         sq[tid - kDim] = x1;
@@ -90,6 +90,22 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         qq[4 * m4] = q4.x; qq[4 * m4 + 1] = q4.y; qq[4 * m4 + 2] = q4.z; qq[4 * m4 + 3] = q4.w;
     }
 
+    if (RAW) {
+        // unit q and k: the lane's 16 rows, summed over the 8 row groups
+        float ssk = 0.f, ssq = 0.f;
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            ssk += kk[m] * kk[m];
+            ssq += qq[m] * qq[m];
+        }
+        const float ik = inv_norm(xor_sum_rows(ssk)), iq = inv_norm(xor_sum_rows(ssq));
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            kk[m] = unit_round(kk[m] * ik, InT{});
+            qq[m] = unit_round(qq[m] * iq, InT{});
+        }
+        bt = sigmoid_gate(bt);
+    }
     float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
     float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
     float kq = 0.f;
@@ -256,21 +272,23 @@ hipError_t launch_decode_tokens(const void* q, const void* k, const void* v, con
 hipError_t launch_decode_step(const void* q, const void* k, const void* v, const void* beta,
                               const float* log_alpha, float* state, const int32_t* slots,
                               int64_t n_pool, float* o, int64_t units, int64_t H, bool bf16,
-                              hipStream_t stream)
+                              bool raw, hipStream_t stream)
 {
     if (units <= 0) return hipSuccess;
     const dim3 grid(static_cast<unsigned>(units)), block(256);
+    auto go = [&](auto kernel, auto tag) {
+        using T = decltype(tag);
+        hipLaunchKernelGGL(kernel, grid, block, 0, stream, static_cast<const T*>(q),
+                           static_cast<const T*>(k), static_cast<const T*>(v),
+                           static_cast<const T*>(beta), log_alpha, state, slots, n_pool,
+                           static_cast<int>(H), o);
+    };
     if (bf16) {
-        using T = bf16_t;
-        hipLaunchKernelGGL(decode_step_kernel<T>, grid, block, 0, stream,
-                           static_cast<const T*>(q), static_cast<const T*>(k),
-                           static_cast<const T*>(v), static_cast<const T*>(beta), log_alpha,
-                           state, slots, n_pool, static_cast<int>(H), o);
+        if (raw) go(decode_step_kernel<bf16_t, true>, bf16_t{});
+        else go(decode_step_kernel<bf16_t, false>, bf16_t{});
     } else {
-        hipLaunchKernelGGL(decode_step_kernel<float>, grid, block, 0, stream,
-                           static_cast<const float*>(q), static_cast<const float*>(k),
-                           static_cast<const float*>(v), static_cast<const float*>(beta),
-                           log_alpha, state, slots, n_pool, static_cast<int>(H), o);
+        if (raw) go(decode_step_kernel<float, true>, 0.f);
+        else go(decode_step_kernel<float, false>, 0.f);
     }
     return hipGetLastError();
 }

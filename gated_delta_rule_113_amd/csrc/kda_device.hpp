@@ -34,6 +34,19 @@ __device__ __forceinline__ float exp_gate(float x)
     return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
 }
 
+// Raw-input preparation (see kda.h, the *_raw entry points): q and k become
+// unit vectors per (token, head), rounded to bf16 when the inputs are bf16;
+// beta = sigmoid(b); log alpha = -softplus(a), i.e. alpha = 1 / (1 + e^a).
+__device__ __forceinline__ float unit_round(float x, bf16_t) { return (float)(__bf16)x; }
+__device__ __forceinline__ float unit_round(float x, float) { return x; }
+__device__ __forceinline__ float inv_norm(float sum_sq) { return sum_sq > 0.f ? rsqrtf(sum_sq) : 0.f; }
+__device__ __forceinline__ float sigmoid_gate(float b) { return 1.f / (1.f + __expf(-b)); }
+__device__ __forceinline__ float alpha_from_logit(float a) { return 1.f / (1.f + __expf(a)); }
+__device__ __forceinline__ float log_alpha_from_logit(float a)
+{
+    return -(fmaxf(a, 0.f) + log1pf(__expf(-fabsf(a))));  // -softplus(a) without overflow
+}
+
 // The entering / leaving state of head h of sequence n (see StateRefs), or
 // NULL for "zeros" / "not written".
 __device__ __forceinline__ const float* init_state_of(const StateRefs& r, int64_t n, int h, int64_t H)

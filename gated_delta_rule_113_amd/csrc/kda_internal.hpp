@@ -27,10 +27,12 @@ struct StateRefs {
 // One fused decode step for `units` = N * H heads.  Sequence n's state is
 // entry n of `state`, or with `slots` entry slots[n] of a pool of n_pool
 // entries (a slot outside [0, n_pool) skips the sequence).
+// With `raw`, q and k are unnormalised, beta holds logits and log_alpha gate
+// logits (the *_raw entry points of kda.h).
 hipError_t launch_decode_step(const void* q, const void* k, const void* v, const void* beta,
                               const float* log_alpha, float* state, const int32_t* slots,
                               int64_t n_pool, float* o, int64_t units, int64_t H, bool bf16,
-                              hipStream_t stream);
+                              bool raw, hipStream_t stream);
 
 // K (<= kMaxDraft) consecutive tokens of each of N sequences from its state
 // (inputs [N, K, H, *], outputs [N, K, H, 128]); with n_commit the state is
@@ -47,7 +49,7 @@ hipError_t launch_prefill_recurrent(const void* q, const void* k, const void* v,
                                     const void* beta, const float* log_alpha,
                                     const int32_t* cu_seqlens, int64_t n_seq, int64_t T,
                                     int64_t H, const StateRefs& st, float* o, bool bf16,
-                                    hipStream_t stream);
+                                    bool raw, hipStream_t stream);
 
 // Chunked prefill on bf16 matrix instructions (bf16 inputs only): 64-token
 // chunks, one workgroup per (sequence, head, segment).  Long sequences are cut
@@ -58,7 +60,7 @@ hipError_t launch_prefill_recurrent(const void* q, const void* k, const void* v,
 hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, const void* beta,
                                const float* log_alpha, const int32_t* cu_seqlens, int64_t n_seq,
                                int64_t T, int64_t T_total, int64_t H, const StateRefs& st,
-                               float* o, hipStream_t stream);
+                               float* o, bool raw, hipStream_t stream);
 
 // Tokens per segment for the chunked prefill (a positive multiple of 64), or
 // 0 to choose it from the problem size and the number of CUs.

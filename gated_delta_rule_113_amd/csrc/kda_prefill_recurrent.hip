@@ -15,7 +15,7 @@
 namespace kda {
 namespace {
 
-template <typename InT>
+template <typename InT, bool RAW>
 __global__ __launch_bounds__(256) void prefill_recurrent_kernel(
     const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
     const InT* __restrict__ beta, const float* __restrict__ log_alpha,
@@ -56,11 +56,27 @@ __global__ __launch_bounds__(256) void prefill_recurrent_kernel(
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
             const int i = rg + 8 * m;
-            a[m] = exp_gate(log_alpha[vec + i]);
+            a[m] = RAW ? alpha_from_logit(log_alpha[vec + i]) : exp_gate(log_alpha[vec + i]);
             kk[m] = widen(k[vec + i]);
             qq[m] = widen(q[vec + i]);
         }
-        const float bt = widen(beta[rh]);
+        float bt = widen(beta[rh]);
+        if (RAW) {
+            // unit q and k: the lane's 16 rows, summed over the 8 row groups
+            float ssk = 0.f, ssq = 0.f;
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                ssk += kk[m] * kk[m];
+                ssq += qq[m] * qq[m];
+            }
+            const float ik = inv_norm(xor_sum_rows(ssk)), iq = inv_norm(xor_sum_rows(ssq));
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                kk[m] = unit_round(kk[m] * ik, InT{});
+                qq[m] = unit_round(qq[m] * iq, InT{});
+            }
+            bt = sigmoid_gate(bt);
+        }
         const float4 vv = load4(v + vec + col);
 
         float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
@@ -102,23 +118,24 @@ hipError_t launch_prefill_recurrent(const void* q, const void* k, const void* v,
                                     const void* beta, const float* log_alpha,
                                     const int32_t* cu_seqlens, int64_t n_seq, int64_t T,
                                     int64_t H, const StateRefs& st, float* o, bool bf16,
-                                    hipStream_t stream)
+                                    bool raw, hipStream_t stream)
 {
     const int64_t units = n_seq * H;
     if (units <= 0) return hipSuccess;
     const dim3 grid(static_cast<unsigned>(units)), block(256);
     const int h = static_cast<int>(H);
+    auto go = [&](auto kernel, auto tag) {
+        using E = decltype(tag);
+        hipLaunchKernelGGL(kernel, grid, block, 0, stream, static_cast<const E*>(q),
+                           static_cast<const E*>(k), static_cast<const E*>(v),
+                           static_cast<const E*>(beta), log_alpha, cu_seqlens, T, h, st, o);
+    };
     if (bf16) {
-        using E = bf16_t;
-        hipLaunchKernelGGL(prefill_recurrent_kernel<E>, grid, block, 0, stream,
-                           static_cast<const E*>(q), static_cast<const E*>(k),
-                           static_cast<const E*>(v), static_cast<const E*>(beta), log_alpha,
-                           cu_seqlens, T, h, st, o);
+        if (raw) go(prefill_recurrent_kernel<bf16_t, true>, bf16_t{});
+        else go(prefill_recurrent_kernel<bf16_t, false>, bf16_t{});
     } else {
-        hipLaunchKernelGGL(prefill_recurrent_kernel<float>, grid, block, 0, stream,
-                           static_cast<const float*>(q), static_cast<const float*>(k),
-                           static_cast<const float*>(v), static_cast<const float*>(beta),
-                           log_alpha, cu_seqlens, T, h, st, o);
+        if (raw) go(prefill_recurrent_kernel<float, true>, 0.f);
+        else go(prefill_recurrent_kernel<float, false>, 0.f);
     }
     return hipGetLastError();
 }

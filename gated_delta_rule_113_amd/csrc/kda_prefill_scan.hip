@@ -253,6 +253,40 @@ __device__ __forceinline__ float quad_xor(float x)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, 0xF, 0xF, false));
 }
 
+// x of the lane N places further in the same 16-lane row, cyclically (DPP row rotate)
+template <int N>
+__device__ __forceinline__ float row_ror(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xF, 0xF, false));
+}
+
+// Eight consecutive bf16 entries of a token row, whose 128 entries are spread
+// over the 16 lanes of one DPP row: divided by the row's L2 norm (a zero row
+// stays zero) and rounded back to bf16, nearest even.
+__device__ __forceinline__ uint4 unit_row(uint4 w)
+{
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+    float f[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        f[2 * j] = __uint_as_float(u[j] << 16);
+        f[2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss += f[j] * f[j];
+    ss += row_ror<8>(ss);
+    ss += row_ror<4>(ss);
+    ss += row_ror<2>(ss);
+    ss += row_ror<1>(ss);
+    const float inv = ss > 0.f ? rsqrtf(ss) : 0.f;
+    uint32_t r[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        r[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){f[2 * j] * inv, f[2 * j + 1] * inv}, bf16x2));
+    return make_uint4(r[0], r[1], r[2], r[3]);
+}
+
 __device__ __forceinline__ float4 f4add(float4 a, float4 b)
 {
     return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
@@ -277,6 +311,7 @@ struct ScanArgs {
     int H;
     StateRefs st;  // entering and leaving states (per sequence, or pool slots)
     float* o;
+    int raw;       // q, k unnormalised, beta and log_alpha logits (kda.h *_raw)
     float* ws_maps;   // [n_segs][H][2][d_k][d_v]: M and R of each segment but the last
     float* ws_start;  // [n_segs][H][d_k][d_v]: entering state of each segment
 };
@@ -480,6 +515,13 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
         //             written out from LDS first.
         if (OUT && ci > 0) store_o(c0 - CH, CH, tid);
         {
+            if (a.raw) {
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    pk[m] = unit_row(pk[m]);
+                    if (OUT) pq[m] = unit_row(pq[m]);
+                }
+            }
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
                 const int r = (tid >> 4) + 32 * m;
@@ -494,7 +536,9 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
                 at<uint2>(sm, OFF_V + r * V_LD + 2 * c8) = make_uint2(pv[m].x, pv[m].y);
                 at<uint2>(sm, OFF_V + r * V_LD + 2 * c8 + 8) = make_uint2(pv[m].z, pv[m].w);
             }
-            if (tid < CH) at<float>(sm, OFF_BETA + 4 * tid) = widen(pb);
+            if (tid < CH)
+                at<float>(sm, OFF_BETA + 4 * tid) =
+                    !a.raw ? widen(pb) : (tid < L ? sigmoid_gate(widen(pb)) : 0.f);
             // this lane: channels 16*wave + 4*(lane >> 4) .. +3, tokens 4*tg .. 4*tg+3
             // with tg = lane & 15, so the 16 token groups of a channel quad
             // are one 16-lane row and the scan over them stays within the row
@@ -504,7 +548,13 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
             float4 run = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                const float4 x = pla[m];
+                float4 x = pla[m];
+                if (a.raw) {
+                    // gate logits; rows past the chunk's end keep a zero log-decay
+                    x = 4 * tg + m < L ? make_float4(log_alpha_from_logit(x.x), log_alpha_from_logit(x.y),
+                                                     log_alpha_from_logit(x.z), log_alpha_from_logit(x.w))
+                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
                 run = make_float4(run.x + x.x * kLog2e, run.y + x.y * kLog2e, run.z + x.z * kLog2e,
                                   run.w + x.w * kLog2e);
                 gp[m] = run;
@@ -1306,7 +1356,7 @@ void set_prefill_segment(int64_t tokens) { g_forced_segment = tokens; }
 hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, const void* beta,
                                const float* log_alpha, const int32_t* cu_seqlens, int64_t n_seq,
                                int64_t T, int64_t T_total, int64_t H,
-                               const StateRefs& st, float* o, hipStream_t stream)
+                               const StateRefs& st, float* o, bool raw, hipStream_t stream)
 {
     const int64_t units = n_seq * H;
     if (units <= 0) return hipSuccess;
@@ -1328,6 +1378,7 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
     a.H = static_cast<int>(H);
     a.st = st;
     a.o = o;
+    a.raw = raw ? 1 : 0;
 
     // Segment length: enough segments to give every CU about one segment of
     // the total work, never shorter than kMinSegment tokens.

@@ -132,6 +132,39 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v, const vo
                            kda_dtype in_dtype, void *stream);
 
 /*
+ * Raw-input variants: the same calls, arguments and layouts as kda_prefill,
+ * kda_varlen_prefill and kda_decode_step, with the inputs as a layer's
+ * projections produce them; the preparation runs inside the kernels, so the
+ * prepared inputs never make an extra pass through memory.
+ *   q, k      : need not be unit vectors; each (token, head) vector is divided
+ *               by its L2 norm (a zero vector stays zero) and, for bf16 inputs,
+ *               rounded back to bf16 (nearest, ties to even)
+ *   beta      : logits b; the write strength is sigmoid(b) = 1 / (1 + e^-b)
+ *   log_alpha : gate logits a; the log forgetting factor is
+ *               -softplus(a) = -log(1 + e^a), so alpha = 1 / (1 + e^a)
+ * The pages give beta (the writing strength) and alpha (the forgetting
+ * factor) as two learned gate parameters of KDA ("Inside Kimi K3: How
+ * Moonshot AI Built the Largest Open-Source Model", section "Technical
+ * Details") without their parameterisation; sigmoid and minus-softplus are the
+ * plainest readings that keep both in (0, 1).  Any finite a is valid.
+ */
+kda_status kda_prefill_raw(const void *q, const void *k, const void *v, const void *beta,
+                           const float *log_alpha, const float *initial_state,
+                           float *o, float *final_state,
+                           int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v,
+                           kda_dtype in_dtype, void *stream);
+kda_status kda_varlen_prefill_raw(const void *q, const void *k, const void *v, const void *beta,
+                                  const float *log_alpha, const int32_t *cu_seqlens,
+                                  int64_t N, int64_t T_total,
+                                  const float *initial_state, float *o, float *final_state,
+                                  int64_t H, int64_t d_k, int64_t d_v,
+                                  kda_dtype in_dtype, void *stream);
+kda_status kda_decode_step_raw(const void *q, const void *k, const void *v, const void *beta,
+                               const float *log_alpha, float *state, float *o,
+                               int64_t N, int64_t H, int64_t d_k, int64_t d_v,
+                               kda_dtype in_dtype, void *stream);
+
+/*
  * K consecutive tokens (1 <= K <= 16) of each of N sequences from its current
  * state, for speculative decoding: verify K draft tokens in one pass, then
  * keep the accepted prefix.  The pages name speculative decoding among the

@@ -33,7 +33,7 @@ import os
 import numpy as np
 
 ROOT_SEED = 113
-Q, K, V, BETA, LOG_ALPHA, STATE, SPECIAL, LENGTHS = range(8)
+Q, K, V, BETA, LOG_ALPHA, STATE, SPECIAL, LENGTHS, RAW = range(9)
 N_SPECIAL = 13  # round(0.10 * 128)
 
 
@@ -248,6 +248,64 @@ def decode_steps(workload: int, steps: int, N: int, H: int, dk: int = 128, dv: i
     _run_parallel(one, range(steps))
     s0 = draw_state(workload, (N, H, dk, dv))
     return KDAInputs(q, k, v, beta, la, dtype, s0)
+
+
+# ----------------------------------------------------------------------------
+# raw projections (inputs of the *_raw entry points, which prepare them)
+# ----------------------------------------------------------------------------
+
+def _raw_arrays(workload: int, lead, H: int, dk: int, dv: int):
+    """float64 raw draws of shape lead + (H, *): q_raw, k_raw = N(0,1) times a
+    per-(token, head) scale e^{N(0, 0.5^2)}; v = N(0,1); beta logits
+    N(0, 1.5^2); gate logits N(0,1), except per head 13 channels at N(-9, 1)
+    (softplus ~ 1e-4: long memory) and 13 at N(6, 1) (log alpha ~ -6: fast
+    forgetting), the raw counterpart of the gated channel mix."""
+    lead = tuple(lead)
+    r = lambda t: _rng(workload, RAW, t)
+    scale = lambda t: np.exp(0.5 * r(t).standard_normal(lead + (H, 1)))
+    q = r(Q).standard_normal(lead + (H, dk)) * scale(10 + Q)
+    k = r(K).standard_normal(lead + (H, dk)) * scale(10 + K)
+    v = r(V).standard_normal(lead + (H, dv))
+    b = 1.5 * r(BETA).standard_normal(lead + (H,))
+    a = r(LOG_ALPHA).standard_normal(lead + (H, dk))
+    for h in range(H):
+        slow, fast = special_channels(workload, h, dk)
+        a[..., h, slow] -= 9.0
+        a[..., h, fast] += 6.0
+    return q, k, v, b, a
+
+
+def raw_prefill(workload: int, B: int, T: int, H: int, dk: int = 128, dv: int = 128,
+                dtype: str = "bf16", initial_state: bool = True) -> KDAInputs:
+    """Dense [B, T, H, *] raw projections; ``beta`` holds logits and
+    ``log_alpha`` gate logits (fp32)."""
+    q, k, v, b, a = _raw_arrays(workload, (B, T), H, dk, dv)
+    s0 = draw_state(workload, (B, H, dk, dv)) if initial_state else None
+    return KDAInputs(_store(q, dtype), _store(k, dtype), _store(v, dtype), _store(b, dtype),
+                     a.astype(np.float32), dtype, s0)
+
+
+def raw_varlen(workload: int, lengths, H: int, dk: int = 128, dv: int = 128,
+               dtype: str = "bf16") -> KDAInputs:
+    """Packed [1, T_total, H, *] raw projections with cu_seqlens; even-indexed
+    sequences resume from N(0, 0.02^2) states, odd ones from zeros."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    cu = np.zeros(lengths.size + 1, np.int64)
+    cu[1:] = np.cumsum(lengths)
+    q, k, v, b, a = _raw_arrays(workload, (1, int(cu[-1])), H, dk, dv)
+    s0 = draw_state(workload, (lengths.size, H, dk, dv))
+    s0[1::2] = 0.0
+    return KDAInputs(_store(q, dtype), _store(k, dtype), _store(v, dtype), _store(b, dtype),
+                     a.astype(np.float32), dtype, s0, cu.astype(np.int32))
+
+
+def raw_decode(workload: int, steps: int, N: int, H: int, dk: int = 128, dv: int = 128,
+               dtype: str = "bf16") -> KDAInputs:
+    """[steps, N, H, *] raw projections for a chain of decode steps, plus
+    N(0, 0.02^2) initial states."""
+    q, k, v, b, a = _raw_arrays(workload, (steps, N), H, dk, dv)
+    return KDAInputs(_store(q, dtype), _store(k, dtype), _store(v, dtype), _store(b, dtype),
+                     a.astype(np.float32), dtype, draw_state(workload, (N, H, dk, dv)))
 
 
 # ----------------------------------------------------------------------------

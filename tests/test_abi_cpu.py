@@ -38,6 +38,7 @@ def _declared():
 def test_exports_match_header(lib):
     declared = _declared()
     assert declared == {"kda_prefill", "kda_varlen_prefill", "kda_decode_step",
+                        "kda_prefill_raw", "kda_varlen_prefill_raw", "kda_decode_step_raw",
                         "kda_decode_tokens", "kda_decode_step_slots", "kda_varlen_prefill_slots",
                         "kda_set_prefill_segment", "kda_status_str", "kda_abi_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", kda._binding.LIBRARY],
@@ -92,6 +93,19 @@ def test_prefill_validation(lib):
     assert prefill(lib, B=0, q=None, k=None, v=None, beta=None, la=None, o=None, s1=None) == OK
     # T = 0 without a final state has nothing to write
     assert prefill(lib, T=0, q=None, k=None, v=None, beta=None, la=None, o=None, s1=None) == OK
+
+
+def test_raw_entry_points_validate_like_the_plain_ones(lib):
+    for fn_plain, fn_raw in (("kda_prefill", "kda_prefill_raw"),
+                             ("kda_varlen_prefill", "kda_varlen_prefill_raw"),
+                             ("kda_decode_step", "kda_decode_step_raw")):
+        plain, raw = getattr(lib, fn_plain), getattr(lib, fn_raw)
+        lib_alias = type("L", (), {fn_plain: raw})
+        call = {"kda_prefill": prefill, "kda_varlen_prefill": varlen, "kda_decode_step": decode}[fn_plain]
+        for kw, expect in (({"q": None}, NULL), ({"k": MIS}, ALIGN), ({"dk": 64}, UNSUP),
+                           ({"dt": 2}, DTYPE), ({"H": 0}, SHAPE)):
+            assert call(lib_alias, **kw) == expect, (fn_raw, kw)
+            assert call(lib, **kw) == expect, (fn_plain, kw)
 
 
 def test_varlen_validation(lib):

@@ -1,0 +1,86 @@
+"""Raw-projection entry points on the GPU (q and k normalised, beta and
+log_alpha from logits, inside the kernels) against the fp64 oracle run on
+the oracle's own preparation of the same raw inputs (``oracle.prepare``)."""
+import numpy as np
+import pytest
+
+import gated_delta_rule_113_amd as kda
+import kda_inputs as ki
+import oracle
+from kda_gpu import check, device, rel_err_states, rel_err_vectors, upload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture
+def segment():
+    def set_(tokens):
+        kda.kda_set_prefill_segment(tokens)
+    yield set_
+    kda.kda_set_prefill_segment(0)
+
+
+def _prepared(inp):
+    """Oracle-prepared (q, k, v, beta, log_alpha) of raw inputs, as float32."""
+    q, k, v, b, a = inp.widened()
+    qp, kp, bp, lap = oracle.prepare(q, k, b, a, round_bf16=inp.dtype == "bf16")
+    return qp, kp, v, bp, lap
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_step_raw(dtype):
+    torch = __import__("torch")
+    inp = ki.raw_decode(51, steps=16, N=4, H=4, dtype=dtype)  # per-step slices stay 16-byte aligned
+    t = upload(inp, device())
+    state = t["initial_state"].clone()
+    outs = [kda.kda_decode_step_raw(t["q"][s], t["k"][s], t["v"][s], t["beta"][s],
+                                    t["log_alpha"][s], state) for s in range(16)]
+    torch.cuda.synchronize()
+    o, S = torch.stack(outs).cpu().numpy(), state.cpu().numpy()
+    o_ref, S_ref = oracle.decode_chain(*_prepared(inp), inp.initial_state)
+    check(f"decode raw {dtype}", rel_err_vectors(o, o_ref), rel_err_states(S, S_ref))
+
+
+@pytest.mark.parametrize("dtype,seg", [("bf16", 0), ("bf16", 64), ("f32", 0)])
+def test_prefill_raw_dense(segment, dtype, seg):
+    """Two sequences of 300 tokens (a ragged last chunk), resumed states, the
+    raw gated channel mix; also cut into 64-token segments."""
+    torch = __import__("torch")
+    segment(seg)
+    inp = ki.raw_prefill(52, B=2, T=300 if dtype == "bf16" else 70, H=3, dtype=dtype)
+    t = upload(inp, device())
+    o, S = kda.kda_prefill_raw(t["q"], t["k"], t["v"], t["beta"], t["log_alpha"], t["initial_state"])
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.prefill(*_prepared(inp), inp.initial_state)
+    check(f"prefill raw {dtype} seg {seg}", rel_err_vectors(o.cpu().numpy(), o_ref),
+          rel_err_states(S.cpu().numpy(), S_ref))
+
+
+def test_varlen_prefill_raw():
+    torch = __import__("torch")
+    inp = ki.raw_varlen(54, [0, 1, 63, 64, 65, 200], H=3)
+    t = upload(inp, device())
+    o, S = kda.kda_varlen_prefill_raw(t["q"], t["k"], t["v"], t["beta"], t["log_alpha"],
+                                      t["cu_seqlens"], t["initial_state"])
+    torch.cuda.synchronize()
+    q, k, v, b, la = _prepared(inp)
+    o_ref, S_ref = oracle.varlen_prefill(q, k, v, b, la, inp.cu_seqlens, inp.initial_state)
+    check("varlen raw", rel_err_vectors(o.cpu().numpy()[0], o_ref), rel_err_states(S.cpu().numpy(), S_ref))
+
+
+def test_raw_zero_vectors_and_extreme_logits():
+    """A zero q or k stays zero; gate logits of +-60 give alpha ~ 0 and ~ 1."""
+    torch = __import__("torch")
+    inp = ki.raw_prefill(55, B=1, T=130, H=2)
+    inp.q[0, 5] = 0          # zero query for token 5 (bf16 bits 0 = +0.0)
+    inp.k[0, 70, 1] = 0      # zero key for token 70, head 1
+    inp.log_alpha[0, 10:20] = 60.0
+    inp.log_alpha[0, 100:110, :, :64] = -60.0
+    t = upload(inp, device())
+    o, S = kda.kda_prefill_raw(t["q"], t["k"], t["v"], t["beta"], t["log_alpha"], t["initial_state"])
+    torch.cuda.synchronize()
+    o, S = o.cpu().numpy(), S.cpu().numpy()
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
+    assert np.all(o[0, 5] == 0)
+    o_ref, S_ref = oracle.prefill(*_prepared(inp), inp.initial_state)
+    check("prefill raw, zero vectors and extreme logits", rel_err_vectors(o, o_ref), rel_err_states(S, S_ref))
