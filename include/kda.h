@@ -167,9 +167,10 @@ kda_status kda_decode_step_raw(const void *q, const void *k, const void *v, cons
 /*
  * K consecutive tokens (1 <= K <= 16) of each of N sequences from its current
  * state, for speculative decoding: verify K draft tokens in one pass, then
- * keep the accepted prefix.  The pages name speculative decoding among the
- * serving techniques ("Kimi K3 -- the architecture and infrastructure,
- * explained", component table); the per-token update is the decode step's.
+ * keep the accepted prefix.  The pages describe a draft layer that guesses
+ * several tokens which the main model then checks in one pass (the
+ * marketersindex.com Kimi K3 article, section "Optimization for Inference:
+ * 4-Bit and Speculative Decoding"); the per-token update is the decode step's.
  *   q, k, log_alpha : [N, K, H, d_k];  v : [N, K, H, d_v];  beta : [N, K, H]
  *   o      : [N, K, H, d_v] fp32, written for all K tokens
  *   state  : [N, H, d_k, d_v] fp32.  Without n_commit it is only read (verify).
