@@ -42,9 +42,21 @@ __device__ __forceinline__ float unit_round(float x, float) { return x; }
 __device__ __forceinline__ float inv_norm(float sum_sq) { return sum_sq > 0.f ? rsqrtf(sum_sq) : 0.f; }
 __device__ __forceinline__ float sigmoid_gate(float b) { return 1.f / (1.f + __expf(-b)); }
 __device__ __forceinline__ float alpha_from_logit(float a) { return 1.f / (1.f + __expf(a)); }
-__device__ __forceinline__ float log_alpha_from_logit(float a)
+// log2 alpha = -softplus(a) / ln 2 = -log2(1 + 2^t) with t = a log2 e, as
+// -(max(t, 0) + log2(1 + y)) with y = 2^-|t| in (0, 1] (no overflow), on the
+// hardware exp2 / log2.  log2(1 + y) is taken as log2(u) * y / (u - 1) with
+// u = fl(1 + y): the rounding of u cancels between the two factors, so tiny y
+// keep their relative accuracy (Goldberg, "What every computer scientist
+// should know about floating-point arithmetic", the log(1 + x) theorem);
+// u == 1 means y is below half an ulp of 1 and log2(1 + y) = y log2 e.
+__device__ __forceinline__ float log2_alpha_from_logit(float a)
 {
-    return -(fmaxf(a, 0.f) + log1pf(__expf(-fabsf(a))));  // -softplus(a) without overflow
+    const float t = a * 1.4426950408889634f;
+    const float y = __builtin_amdgcn_exp2f(-fabsf(t));
+    const float u = 1.f + y;
+    const float l = u == 1.f ? y * 1.4426950408889634f
+                             : __builtin_amdgcn_logf(u) * (y * __builtin_amdgcn_rcpf(u - 1.f));
+    return -(fmaxf(t, 0.f) + l);
 }
 
 // The entering / leaving state of head h of sequence n (see StateRefs), or

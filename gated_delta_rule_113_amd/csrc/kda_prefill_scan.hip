@@ -548,15 +548,16 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
             float4 run = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                float4 x = pla[m];
+                const float4 x = pla[m];
                 if (a.raw) {
                     // gate logits; rows past the chunk's end keep a zero log-decay
-                    x = 4 * tg + m < L ? make_float4(log_alpha_from_logit(x.x), log_alpha_from_logit(x.y),
-                                                     log_alpha_from_logit(x.z), log_alpha_from_logit(x.w))
-                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+                    if (4 * tg + m < L)
+                        run = make_float4(run.x + log2_alpha_from_logit(x.x), run.y + log2_alpha_from_logit(x.y),
+                                          run.z + log2_alpha_from_logit(x.z), run.w + log2_alpha_from_logit(x.w));
+                } else {
+                    run = make_float4(run.x + x.x * kLog2e, run.y + x.y * kLog2e, run.z + x.z * kLog2e,
+                                      run.w + x.w * kLog2e);
                 }
-                run = make_float4(run.x + x.x * kLog2e, run.y + x.y * kLog2e, run.z + x.z * kLog2e,
-                                  run.w + x.w * kLog2e);
                 gp[m] = run;
             }
             // inclusive scan of the 4-token sums over the 16 token groups
