@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--batch", type=int, default=64)
     ap.add_argument("--heads", type=int, default=32)
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
+    ap.add_argument("--no-raw", action="store_true",
+                    help="skip the prefill from raw projections (same kernels: keeps kernel traces to one kind)")
     ap.add_argument("--no-tokens", action="store_true",
                     help="skip the multi-token (speculative verify / commit) decode measurement")
     ap.add_argument("--no-slots", action="store_true",
@@ -197,6 +199,25 @@ def main():
     log(f"decode: {ms_per_step * 1e3:.2f} us/step, {tokens_per_s / 1e6:.3f} M tokens/s, "
         f"{achieved:.0f} GB/s")
 
+    # Streaming ceiling for context: an in-place read-modify-write of the same
+    # state tensor (the same 128 MiB of live, random-valued state read and
+    # written once; scaling by 1 leaves it unchanged).  HBM throughput on this
+    # part depends on the data: zero-filled buffers stream markedly faster.
+    ceil_reps = 64
+    state.mul_(1.0)
+    torch.cuda.synchronize()
+    ec0 = torch.cuda.Event(enable_timing=True)
+    ec1 = torch.cuda.Event(enable_timing=True)
+    ec0.record(stream)
+    for _ in range(ceil_reps):
+        state.mul_(1.0)
+    ec1.record(stream)
+    torch.cuda.synchronize()
+    ceil_ms = ec0.elapsed_time(ec1) / ceil_reps
+    ceil_gbs = 2 * B * H * D * D * 4 / (ceil_ms / 1e3) / 1e9
+    log(f"state read-modify-write ceiling: {ceil_ms * 1e3:.2f} us ({ceil_gbs:.0f} GB/s); "
+        f"decode reaches {achieved / ceil_gbs * 100:.0f}% of it")
+
     result = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -231,6 +252,13 @@ def main():
             "state_bytes": B * H * D * D * 4,
             "note": "the 128 MiB of state fit in the 256 MB last-level (Infinity) cache, so across "
                     "consecutive steps part of the state stream is served from it",
+        },
+        "state_rmw_ceiling": {
+            "what": "torch in-place scale by 1 of the live state tensor: the state bytes read and "
+                    "written once, no other work",
+            "us": ceil_ms * 1e3,
+            "GBps": ceil_gbs,
+            "decode_frac_of_ceiling": achieved / ceil_gbs,
         },
     }
 
@@ -387,31 +415,11 @@ def main():
                      "frac": ptf / BF16_MFMA_PEAK_TFLOPS,
                      "algorithmic_flops_per_launch": pflops},
         }
-        # The same call on raw projections: the buffers above read as raw q, k,
-        # v, beta logits and gate logits (the kernels' arithmetic takes no
-        # value-dependent branch, so any values time alike); the unit-norm,
-        # sigmoid and softplus preparation runs inside the staging.
-        kda.kda_prefill_raw(pq, pk, pv, pb, pla, None, out=po, final_state=ps)
-        torch.cuda.synchronize()
-        rtimes = []
-        for _ in range(args.prefill_reps):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            kda.kda_prefill_raw(pq, pk, pv, pb, pla, None, out=po, final_state=ps)
-            b.record(stream)
-            torch.cuda.synchronize()
-            rtimes.append(a.elapsed_time(b))
-        rms = float(np.median(rtimes))
-        log(f"prefill from raw projections: {rms:.3f} ms ({(rms / pms - 1) * 100:+.1f}% over prepared)")
-        result["prefill"]["raw"] = {
-            "workload": "the same shape from raw projections (q, k normalised per head, sigmoid "
-                        "write strength, minus-softplus log gate, all inside the kernels)",
-            "ms": rms,
-            "tokens_per_s": T / (rms / 1e3),
-            "overhead_vs_prepared": rms / pms - 1,
-        }
-        del pq, pk, pv, pb, pla, po, ps
+        if args.no_raw:
+            del pq, pk, pv, pb, pla, po, ps
+        else:
+            time_raw_prefill(kda, torch, np, stream, args.prefill_reps, pq, pk, pv, pb, pla, po, ps, pms, T, result)
+            del pq, pk, pv, pb, pla, po, ps
 
     # ---------------- CPU oracle baseline ---------------------------------
     if not args.no_cpu:
@@ -436,6 +444,33 @@ def main():
 
     print(json.dumps(result), flush=True)
     return 0
+
+
+def time_raw_prefill(kda, torch, np, stream, reps, pq, pk, pv, pb, pla, po, ps, pms, T, result):
+    """The chunked prefill on raw projections: the same resident buffers read as
+    raw q, k, v, beta logits and gate logits (the kernels take no value-dependent
+    branch, so any values time alike); the unit-norm, sigmoid and softplus
+    preparation runs inside the staging."""
+    kda.kda_prefill_raw(pq, pk, pv, pb, pla, None, out=po, final_state=ps)
+    torch.cuda.synchronize()
+    rtimes = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        kda.kda_prefill_raw(pq, pk, pv, pb, pla, None, out=po, final_state=ps)
+        b.record(stream)
+        torch.cuda.synchronize()
+        rtimes.append(a.elapsed_time(b))
+    rms = float(np.median(rtimes))
+    log(f"prefill from raw projections: {rms:.3f} ms ({(rms / pms - 1) * 100:+.1f}% over prepared)")
+    result["prefill"]["raw"] = {
+        "workload": "the same shape from raw projections (q, k normalised per head, sigmoid "
+                    "write strength, minus-softplus log gate, all inside the kernels)",
+        "ms": rms,
+        "tokens_per_s": T / (rms / 1e3),
+        "overhead_vs_prepared": rms / pms - 1,
+    }
 
 
 if __name__ == "__main__":
