@@ -60,11 +60,21 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v, const voi
                           int64_t T, int64_t T_total, int64_t H, const kda::StateRefs& st,
                           float* o, kda_dtype in_dtype, bool raw, hipStream_t stream)
 {
-    if (in_dtype == KDA_BF16)
-        return kda::launch_prefill_scan(q, k, v, beta, log_alpha, cu_seqlens, n_seq, T, T_total,
-                                        H, st, o, raw, stream);
+    if (in_dtype != KDA_BF16)
+        return kda::launch_prefill_recurrent(q, k, v, beta, log_alpha, cu_seqlens, n_seq, T, H,
+                                             st, o, false, raw, 0, stream);
+    // bf16: short sequences token by token, the others chunked.  Each kernel
+    // skips the other's sequences (packed lengths are known on the device only).
+    const int64_t longest = cu_seqlens ? T_total : T;
+    if (longest <= kda::kShortPrefill)
+        return kda::launch_prefill_recurrent(q, k, v, beta, log_alpha, cu_seqlens, n_seq, T, H,
+                                             st, o, true, raw, 0, stream);
+    const hipError_t e = kda::launch_prefill_scan(q, k, v, beta, log_alpha, cu_seqlens, n_seq, T,
+                                                  T_total, H, st, o, raw,
+                                                  cu_seqlens ? kda::kShortPrefill : 0, stream);
+    if (e != hipSuccess || !cu_seqlens) return e;
     return kda::launch_prefill_recurrent(q, k, v, beta, log_alpha, cu_seqlens, n_seq, T, H, st,
-                                         o, false, raw, stream);
+                                         o, true, raw, kda::kShortPrefill, stream);
 }
 
 kda::StateRefs plain_states(const float* initial_state, float* final_state)

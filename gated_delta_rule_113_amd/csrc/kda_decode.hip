@@ -203,39 +203,11 @@ __global__ __launch_bounds__(256) void decode_tokens_kernel(
         const float4 vt = vv;
         if (t + 1 < K) vv = load4(v + rowvec(t + 1) + col);
         float a[16], kk[16], qq[16];
-#pragma unroll
-        for (int m4 = 0; m4 < 4; ++m4) {
-            const float4 a4 = *reinterpret_cast<const float4*>(&sa[t][row0 + 4 * m4]);
-            const float4 k4 = *reinterpret_cast<const float4*>(&sk[t][row0 + 4 * m4]);
-            const float4 q4 = *reinterpret_cast<const float4*>(&sq[t][row0 + 4 * m4]);
-            a[4 * m4] = a4.x; a[4 * m4 + 1] = a4.y; a[4 * m4 + 2] = a4.z; a[4 * m4 + 3] = a4.w;
-            kk[4 * m4] = k4.x; kk[4 * m4 + 1] = k4.y; kk[4 * m4 + 2] = k4.z; kk[4 * m4 + 3] = k4.w;
-            qq[4 * m4] = q4.x; qq[4 * m4 + 1] = q4.y; qq[4 * m4 + 2] = q4.z; qq[4 * m4 + 3] = q4.w;
-        }
-        const float bt = sb[t];
-        float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
-        float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
-        float kq = 0.f;
-#pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            s[m].x *= a[m]; s[m].y *= a[m]; s[m].z *= a[m]; s[m].w *= a[m];
-            p0 += kk[m] * s[m].x; p1 += kk[m] * s[m].y; p2 += kk[m] * s[m].z; p3 += kk[m] * s[m].w;
-            r0 += qq[m] * s[m].x; r1 += qq[m] * s[m].y; r2 += qq[m] * s[m].z; r3 += qq[m] * s[m].w;
-            kq += kk[m] * qq[m];
-        }
-        p0 = xor_sum_rows(p0); p1 = xor_sum_rows(p1); p2 = xor_sum_rows(p2); p3 = xor_sum_rows(p3);
-        r0 = xor_sum_rows(r0); r1 = xor_sum_rows(r1); r2 = xor_sum_rows(r2); r3 = xor_sum_rows(r3);
-        kq = xor_sum_rows(kq);
-        const float u0 = bt * (vt.x - p0), u1 = bt * (vt.y - p1);
-        const float u2 = bt * (vt.z - p2), u3 = bt * (vt.w - p3);
-        if (rg == 0) {
-            *reinterpret_cast<float4*>(o + rowvec(t) + col) =
-                make_float4(r0 + kq * u0, r1 + kq * u1, r2 + kq * u2, r3 + kq * u3);
-        }
-#pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            s[m].x += kk[m] * u0; s[m].y += kk[m] * u1; s[m].z += kk[m] * u2; s[m].w += kk[m] * u3;
-        }
+        rows16(&sa[t][row0], a);
+        rows16(&sk[t][row0], kk);
+        rows16(&sq[t][row0], qq);
+        const float4 ot = token_update(s, a, kk, qq, sb[t], vt);
+        if (rg == 0) *reinterpret_cast<float4*>(o + rowvec(t) + col) = ot;
         if (t + 1 == commit) {
 #pragma unroll
             for (int m = 0; m < 16; ++m) *reinterpret_cast<float4*>(S + (row0 + m) * kDim + col) = s[m];

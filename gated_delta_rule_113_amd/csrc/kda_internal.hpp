@@ -45,22 +45,29 @@ hipError_t launch_decode_tokens(const void* q, const void* k, const void* v, con
 
 // Token-by-token prefill with the state held in registers.  Dense when
 // cu_seqlens == nullptr (sequence n = rows n*T .. n*T+T-1), packed otherwise.
+// With max_len > 0, sequences longer than max_len are skipped (left to the
+// chunked kernel).
 hipError_t launch_prefill_recurrent(const void* q, const void* k, const void* v,
                                     const void* beta, const float* log_alpha,
                                     const int32_t* cu_seqlens, int64_t n_seq, int64_t T,
                                     int64_t H, const StateRefs& st, float* o, bool bf16,
-                                    bool raw, hipStream_t stream);
+                                    bool raw, int64_t max_len, hipStream_t stream);
+
+// bf16 sequences of at most this many tokens take the token-by-token kernel:
+// below it the chunked kernel's fixed cost per (sequence, head) dominates.
+constexpr int64_t kShortPrefill = 16;
 
 // Chunked prefill on bf16 matrix instructions (bf16 inputs only): 64-token
 // chunks, one workgroup per (sequence, head, segment).  Long sequences are cut
 // into segments whose affine state maps are composed in between (three
 // launches plus a workspace from a stream-ordered pool); short ones take one
 // launch.  Dense when cu_seqlens == nullptr (T rows each), packed otherwise
-// (T_total rows in all).
+// (T_total rows in all).  With short_max > 0, sequences of at most short_max
+// tokens are skipped (left to the token-by-token kernel); short_max <= 64.
 hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, const void* beta,
                                const float* log_alpha, const int32_t* cu_seqlens, int64_t n_seq,
                                int64_t T, int64_t T_total, int64_t H, const StateRefs& st,
-                               float* o, bool raw, hipStream_t stream);
+                               float* o, bool raw, int64_t short_max, hipStream_t stream);
 
 // Tokens per segment for the chunked prefill (a positive multiple of 64), or
 // 0 to choose it from the problem size and the number of CUs.

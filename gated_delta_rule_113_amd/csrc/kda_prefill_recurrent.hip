@@ -4,111 +4,130 @@
 // 128 x 128 fp32 state of a head never leaves the register file between
 // tokens: it is loaded once (or zeroed), carried through every token of the
 // sequence, and stored once at the end.  This is the plain sequential form of
-// the recurrence; the chunked kernel computes the same result blockwise.
+// the recurrence; the chunked kernel computes the same result blockwise.  It
+// serves fp32 inputs (not exact in bf16, so not fit for the bf16 matrix
+// path) and short sequences, where the chunked kernel's fixed cost per chunk
+// dominates.
 //
 // Mapping: one workgroup of 256 threads per (sequence, head), lanes laid out as
-// in the decode kernel (wave w: columns [32w, 32w+32); lane: 4 columns x 16
-// rows).  Packed sequences read their bounds from cu_seqlens on the device.
+// in the decode kernel.  Inputs are staged through LDS in batches of TB
+// tokens: each thread requests one gate and one value element (threads
+// 0..127) or one key and one query element (threads 128..255) of every token
+// of the next batch while the current batch is computed, so a batch costs one
+// memory round trip rather than one per token.  Packed sequences read their
+// bounds from cu_seqlens on the device.
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
 
 namespace kda {
 namespace {
 
+constexpr int TB = 8;  // tokens per staged batch
+
 template <typename InT, bool RAW>
 __global__ __launch_bounds__(256) void prefill_recurrent_kernel(
     const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
     const InT* __restrict__ beta, const float* __restrict__ log_alpha,
     const int32_t* __restrict__ cu_seqlens, int64_t T, int H,
-    const StateRefs st, float* __restrict__ o)  // the final state may alias the initial one
+    const StateRefs st, float* __restrict__ o,  // the final state may alias the initial one
+    int64_t max_len)
 {
+    // double-buffered batches: [buffer][token][element]
+    __shared__ __attribute__((aligned(16))) float sa[2][TB][kDim], sv[2][TB][kDim],
+        sk[2][TB][kDim], sq[2][TB][kDim];
+    __shared__ float sb[2][TB];
     const int64_t unit = blockIdx.x;  // n * H + h
     const int64_t n = unit / H;
     const int h = static_cast<int>(unit - n * H);
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
     const int rg = lane >> 3;
+    const int row0 = 16 * rg;
     const int col = wave * 32 + (lane & 7) * 4;
 
-    int64_t row0, len;
+    int64_t first, len;
     if (cu_seqlens) {
-        row0 = cu_seqlens[n];
-        len = static_cast<int64_t>(cu_seqlens[n + 1]) - row0;
+        first = cu_seqlens[n];
+        len = static_cast<int64_t>(cu_seqlens[n + 1]) - first;
     } else {
-        row0 = n * T;
+        first = n * T;
         len = T;
     }
+    if (max_len > 0 && len > max_len) return;  // left to the chunked kernel
 
+    // this thread's staged element
+    const int e = tid & (kDim - 1);
+    const bool gate_value = tid < kDim;
+    float x0[TB], x1[TB], xb = 0.f;
+    auto request = [&](int64_t t0) {
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+            if (t0 + t < len) {
+                const int64_t vec = ((first + t0 + t) * H + h) * kDim;
+                if (gate_value) {
+                    x0[t] = log_alpha[vec + e];
+                    x1[t] = widen(v[vec + e]);
+                } else {
+                    x0[t] = widen(k[vec + e]);
+                    x1[t] = widen(q[vec + e]);
+                }
+            }
+        }
+        if (tid < TB && t0 + tid < len) xb = widen(beta[(first + t0 + tid) * H + h]);
+    };
+    auto stage = [&](int buf, int64_t t0) {
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+            if (t0 + t < len) {
+                if (gate_value) {
+                    sa[buf][t][e] = RAW ? alpha_from_logit(x0[t]) : exp_gate(x0[t]);
+                    sv[buf][t][e] = x1[t];
+                } else {
+                    sk[buf][t][e] = x0[t];
+                    sq[buf][t][e] = x1[t];
+                }
+            }
+        }
+        if (tid < TB && t0 + tid < len) sb[buf][tid] = RAW ? sigmoid_gate(xb) : xb;
+    };
+
+    request(0);
     float4 s[16];
     if (const float* S0 = init_state_of(st, n, h, H)) {
 #pragma unroll
         for (int m = 0; m < 16; ++m)
-            s[m] = *reinterpret_cast<const float4*>(S0 + (rg + 8 * m) * kDim + col);
+            s[m] = *reinterpret_cast<const float4*>(S0 + (row0 + m) * kDim + col);
     } else {
 #pragma unroll
         for (int m = 0; m < 16; ++m) s[m] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
 
-    for (int64_t t = 0; t < len; ++t) {
-        const int64_t rh = (row0 + t) * H + h;  // (token row, head)
-        const int64_t vec = rh * kDim;
-        float a[16], kk[16], qq[16];
-#pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            const int i = rg + 8 * m;
-            a[m] = RAW ? alpha_from_logit(log_alpha[vec + i]) : exp_gate(log_alpha[vec + i]);
-            kk[m] = widen(k[vec + i]);
-            qq[m] = widen(q[vec + i]);
-        }
-        float bt = widen(beta[rh]);
-        if (RAW) {
-            // unit q and k: the lane's 16 rows, summed over the 8 row groups
-            float ssk = 0.f, ssq = 0.f;
-#pragma unroll
-            for (int m = 0; m < 16; ++m) {
-                ssk += kk[m] * kk[m];
-                ssq += qq[m] * qq[m];
-            }
-            const float ik = inv_norm(xor_sum_rows(ssk)), iq = inv_norm(xor_sum_rows(ssq));
-#pragma unroll
-            for (int m = 0; m < 16; ++m) {
-                kk[m] = unit_round(kk[m] * ik, InT{});
-                qq[m] = unit_round(qq[m] * iq, InT{});
-            }
-            bt = sigmoid_gate(bt);
-        }
-        const float4 vv = load4(v + vec + col);
-
-        float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
-        float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
-        float kq = 0.f;
-#pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            s[m].x *= a[m]; s[m].y *= a[m]; s[m].z *= a[m]; s[m].w *= a[m];
-            p0 += kk[m] * s[m].x; p1 += kk[m] * s[m].y; p2 += kk[m] * s[m].z; p3 += kk[m] * s[m].w;
-            r0 += qq[m] * s[m].x; r1 += qq[m] * s[m].y; r2 += qq[m] * s[m].z; r3 += qq[m] * s[m].w;
-            kq += kk[m] * qq[m];
-        }
-        p0 = xor_sum_rows(p0); p1 = xor_sum_rows(p1); p2 = xor_sum_rows(p2); p3 = xor_sum_rows(p3);
-        r0 = xor_sum_rows(r0); r1 = xor_sum_rows(r1); r2 = xor_sum_rows(r2); r3 = xor_sum_rows(r3);
-        kq = xor_sum_rows(kq);
-
-        const float u0 = bt * (vv.x - p0), u1 = bt * (vv.y - p1);
-        const float u2 = bt * (vv.z - p2), u3 = bt * (vv.w - p3);
-        if (rg == 0) {
-            *reinterpret_cast<float4*>(o + vec + col) =
-                make_float4(r0 + kq * u0, r1 + kq * u1, r2 + kq * u2, r3 + kq * u3);
-        }
-#pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            s[m].x += kk[m] * u0; s[m].y += kk[m] * u1; s[m].z += kk[m] * u2; s[m].w += kk[m] * u3;
+    // One barrier per batch: a wave writes a buffer again two batches later,
+    // after the barrier that every wave reaches only once done with it.
+    int buf = 0;
+    for (int64_t t0 = 0; t0 < len; t0 += TB, buf ^= 1) {
+        stage(buf, t0);
+        __syncthreads();
+        if (t0 + TB < len) request(t0 + TB);
+        const int nb = static_cast<int>(len - t0 < TB ? len - t0 : TB);
+        for (int t = 0; t < nb; ++t) {
+            float a[16], kk[16], qq[16];
+            rows16(&sa[buf][t][row0], a);
+            rows16(&sk[buf][t][row0], kk);
+            rows16(&sq[buf][t][row0], qq);
+            const float4 vt = *reinterpret_cast<const float4*>(&sv[buf][t][col]);
+            if (RAW) unit_key_query<InT>(kk, qq);
+            const float4 ot = token_update(s, a, kk, qq, sb[buf][t], vt);
+            if (rg == 0)
+                *reinterpret_cast<float4*>(o + ((first + t0 + t) * H + h) * kDim + col) = ot;
         }
     }
 
     if (float* S1 = final_state_of(st, n, h, H)) {
 #pragma unroll
         for (int m = 0; m < 16; ++m)
-            *reinterpret_cast<float4*>(S1 + (rg + 8 * m) * kDim + col) = s[m];
+            *reinterpret_cast<float4*>(S1 + (row0 + m) * kDim + col) = s[m];
     }
 }
 
@@ -118,7 +137,7 @@ hipError_t launch_prefill_recurrent(const void* q, const void* k, const void* v,
                                     const void* beta, const float* log_alpha,
                                     const int32_t* cu_seqlens, int64_t n_seq, int64_t T,
                                     int64_t H, const StateRefs& st, float* o, bool bf16,
-                                    bool raw, hipStream_t stream)
+                                    bool raw, int64_t max_len, hipStream_t stream)
 {
     const int64_t units = n_seq * H;
     if (units <= 0) return hipSuccess;
@@ -128,7 +147,8 @@ hipError_t launch_prefill_recurrent(const void* q, const void* k, const void* v,
         using E = decltype(tag);
         hipLaunchKernelGGL(kernel, grid, block, 0, stream, static_cast<const E*>(q),
                            static_cast<const E*>(k), static_cast<const E*>(v),
-                           static_cast<const E*>(beta), log_alpha, cu_seqlens, T, h, st, o);
+                           static_cast<const E*>(beta), log_alpha, cu_seqlens, T, h, st, o,
+                           max_len);
     };
     if (bf16) {
         if (raw) go(prefill_recurrent_kernel<bf16_t, true>, bf16_t{});

@@ -312,6 +312,7 @@ struct ScanArgs {
     StateRefs st;  // entering and leaving states (per sequence, or pool slots)
     float* o;
     int raw;       // q, k unnormalised, beta and log_alpha logits (kda.h *_raw)
+    int64_t short_max;  // sequences of at most this many tokens are skipped (0: none)
     float* ws_maps;   // [n_segs][H][2][d_k][d_v]: M and R of each segment but the last
     float* ws_start;  // [n_segs][H][d_k][d_v]: entering state of each segment
 };
@@ -326,6 +327,7 @@ struct SegInfo {
     int64_t row0;    // first row of the sequence
     int64_t begin;   // segment rows [begin, end) relative to row0
     int64_t end;
+    int64_t len;     // tokens of the whole sequence
     bool valid;
 };
 
@@ -368,6 +370,7 @@ __device__ SegInfo decode_segment(const ScanArgs& a, int64_t z)
         s.row0 = a.cu_seqlens[lo];
         len = static_cast<int64_t>(a.cu_seqlens[lo + 1]) - s.row0;
     }
+    s.len = len;
     const int64_t seg = s.nseg == 1 ? len : a.seg_len;
     s.begin = s.j * seg;
     s.end = (s.j == s.nseg - 1) ? len : s.begin + seg;
@@ -393,6 +396,7 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
 
     const SegInfo sg = decode_segment(a, z);
     if (!sg.valid) return;
+    if (sg.len <= a.short_max) return;        // a short sequence: the token-by-token kernel's
     if (!OUT && sg.j == sg.nseg - 1) return;  // the last segment needs no map
     const bool blkM = !OUT && sg.j > 0;       // pass 1: is the M block carried?
 
@@ -1357,7 +1361,8 @@ void set_prefill_segment(int64_t tokens) { g_forced_segment = tokens; }
 hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, const void* beta,
                                const float* log_alpha, const int32_t* cu_seqlens, int64_t n_seq,
                                int64_t T, int64_t T_total, int64_t H,
-                               const StateRefs& st, float* o, bool raw, hipStream_t stream)
+                               const StateRefs& st, float* o, bool raw, int64_t short_max,
+                               hipStream_t stream)
 {
     const int64_t units = n_seq * H;
     if (units <= 0) return hipSuccess;
@@ -1380,6 +1385,7 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
     a.st = st;
     a.o = o;
     a.raw = raw ? 1 : 0;
+    a.short_max = short_max > 0 ? short_max : -1;  // -1: no sequence is skipped (lengths are >= 0)
 
     // Segment length: enough segments to give every CU about one segment of
     // the total work, never shorter than kMinSegment tokens.

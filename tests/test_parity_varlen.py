@@ -77,3 +77,29 @@ def test_varlen_equals_separate_calls():
         torch.cuda.synchronize()
         assert rel_err_vectors(o[0, a:b], on[0].cpu().numpy()) < 1e-5
         assert rel_err_states(S[n:n + 1], Sn.cpu().numpy()) < 1e-5
+
+
+def test_short_and_chunked_sequences_in_one_call():
+    """Sequences of up to 16 tokens take the token-by-token kernel, longer ones
+    the chunked kernel; one packed call holds both kinds on each side of the
+    switch, and each sequence still equals a dense call on it alone."""
+    torch = __import__("torch")
+    dev = device()
+    lengths = [15, 16, 17, 2, 33, 0, 16, 1, 64]
+    inp = ki.varlen_prefill(12, lengths, H=3)
+    o, S = _run(inp, dev)
+    o_ref, S_ref = _oracle(inp)
+    check("short and chunked in one call", rel_err_vectors(o[0], o_ref), rel_err_states(S, S_ref))
+    assert np.array_equal(S[5], inp.initial_state[5])   # the empty sequence
+    cu = inp.cu_seqlens
+    for n in (0, 1, 2, 4):
+        a, b = int(cu[n]), int(cu[n + 1])
+        sub = ki.KDAInputs(inp.q[:, a:b], inp.k[:, a:b], inp.v[:, a:b], inp.beta[:, a:b],
+                           inp.log_alpha[:, a:b], inp.dtype, inp.initial_state[n:n + 1])
+        t = upload(sub, dev)
+        on, Sn = kda.kda_prefill(t["q"], t["k"], t["v"], t["beta"], t["log_alpha"],
+                                 t["initial_state"])
+        torch.cuda.synchronize()
+        # the same kernel serves a sequence packed or alone: the same bits
+        assert np.array_equal(o[0, a:b], on[0].cpu().numpy()), n
+        assert np.array_equal(S[n], Sn[0].cpu().numpy()), n
