@@ -84,3 +84,17 @@ def test_raw_zero_vectors_and_extreme_logits():
     assert np.all(o[0, 5] == 0)
     o_ref, S_ref = oracle.prefill(*_prepared(inp), inp.initial_state)
     check("prefill raw, zero vectors and extreme logits", rel_err_vectors(o, o_ref), rel_err_states(S, S_ref))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_raw_short_dense(dtype):
+    """Dense sequences of 9 tokens (the token-by-token path) from raw
+    projections, three sequences with resumed states."""
+    torch = __import__("torch")
+    inp = ki.raw_prefill(56, B=3, T=9, H=4, dtype=dtype)
+    t = upload(inp, device())
+    o, S = kda.kda_prefill_raw(t["q"], t["k"], t["v"], t["beta"], t["log_alpha"], t["initial_state"])
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.prefill(*_prepared(inp), inp.initial_state)
+    check(f"prefill raw short {dtype}", rel_err_vectors(o.cpu().numpy(), o_ref),
+          rel_err_states(S.cpu().numpy(), S_ref))
