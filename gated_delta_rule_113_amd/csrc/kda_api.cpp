@@ -1,7 +1,8 @@
 // C ABI of libkda.so (declared in include/kda.h): host-side validation, then
-// one asynchronous launch on the caller's stream.  Nothing here allocates,
-// synchronises or touches device memory; every check happens before a launch
-// so that on error nothing is enqueued.
+// asynchronous launches on the caller's stream.  Nothing here synchronises or
+// touches device memory (the segmented prefill's workspace is taken and
+// returned in stream order by its launcher); every check happens before a
+// launch so that on error nothing is enqueued.
 #include "kda.h"
 
 #include <hip/hip_runtime.h>
@@ -53,8 +54,9 @@ kda_status check_ptrs(std::initializer_list<const void*> required,
 
 kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
 
-// bf16 inputs take the chunked matrix-core kernel; fp32 inputs (whose q and k
-// are not exact in bf16) take the register-resident token-by-token kernel.
+// bf16 inputs take the chunked matrix-core kernel, except sequences of at most
+// kShortPrefill tokens; fp32 inputs (whose q and k are not exact in bf16) and
+// those short sequences take the register-resident token-by-token kernel.
 hipError_t launch_prefill(const void* q, const void* k, const void* v, const void* beta,
                           const float* log_alpha, const int32_t* cu_seqlens, int64_t n_seq,
                           int64_t T, int64_t T_total, int64_t H, const kda::StateRefs& st,

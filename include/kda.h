@@ -24,7 +24,8 @@
  *    strength, alpha = forgetting factor, erase then write.
  * Readings where the pages are silent: the decay is applied before the
  * erase/write; beta is one scalar per (token, head); the read-out uses the
- * updated state; there is no query scaling and no normalisation inside the op.
+ * updated state; there is no query scaling, and the plain calls normalise
+ * nothing (the *_raw calls below prepare raw projections themselves).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
