@@ -67,3 +67,11 @@ def test_decode_in_place_and_zero_beta():
     q = t["q"][0].float().cpu().numpy().astype(np.float64)
     ref = np.einsum("nhij,nhi->nhj", before.cpu().numpy().astype(np.float64), q)
     assert rel_err_vectors(o.cpu().numpy(), ref) < 1e-5
+
+
+def test_decode_many_heads():
+    """96 heads for 5 sequences, 8 consecutive steps."""
+    inp = ki.decode_steps(2, steps=8, N=5, H=96)
+    o, S = _run_chain(inp, device())
+    o_ref, S_ref = oracle.decode_chain(*inp.widened(), inp.initial_state)
+    check("decode 96 heads", rel_err_vectors(o, o_ref), rel_err_states(S, S_ref))

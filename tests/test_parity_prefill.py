@@ -116,3 +116,17 @@ def test_deterministic():
     o1, S1 = _run(inp, dev)
     o2, S2 = _run(inp, dev)
     assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
+
+
+def test_many_heads_segmented():
+    """96 heads (beyond the workloads' 32, not a power of two): two dense
+    sequences of 300 tokens cut into 128-token segments, so that every launch
+    maps its workgroups to (segment, head) pairs over 96 heads."""
+    inp = ki.dense_prefill(10, B=2, T=300, H=96, gated=True, initial_state=True)
+    kda.kda_set_prefill_segment(128)
+    try:
+        o, S = _run(inp, device())
+    finally:
+        kda.kda_set_prefill_segment(0)
+    o_ref, S_ref = _oracle(inp)
+    check("96 heads, segmented", rel_err_vectors(o, o_ref), rel_err_states(S, S_ref))
