@@ -42,8 +42,12 @@
  *        states          : [units, H, d_k, d_v]  (d_v contiguous)
  *    where a "row" is one token position (see each call).
  *  - q, k, v and beta share one storage type, `in_dtype` (KDA_F32 or
- *    KDA_BF16); log_alpha, states and o are always fp32.  Arithmetic is fp32
- *    with fp32 state; bf16 inputs are widened exactly.
+ *    KDA_BF16); log_alpha, states and o are always fp32.  The state is fp32
+ *    and bf16 inputs are widened exactly.  Arithmetic is fp32, except that
+ *    the chunked prefill (bf16 inputs, sequences over 16 tokens) forms its
+ *    matrix products on bf16 matrix cores from operands split into a high
+ *    and a low bf16 part (about 16 significant bits each), accumulating in
+ *    fp32.
  *  - Supported sizes: d_k = d_v = 128 (anything else -> KDA_ERR_UNSUPPORTED);
  *    1 <= H <= 65536 heads (anything else -> KDA_ERR_SHAPE).
  *  - Every pointer must be 16-byte aligned (KDA_ERR_ALIGN).
