@@ -21,6 +21,8 @@
 // workgroup (exp(log_alpha) and the bf16 widening done once) into LDS, from
 // where every lane reads its 16 rows as float4.  The column
 // reductions finish across the 8 row groups of a wave with lane shuffles.
+#include <type_traits>
+
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
 
@@ -142,15 +144,15 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 // n_commit at all, leaves it unchanged).  Every token's output is written.
 // The K tokens' gates, keys, queries and write strengths are staged in LDS
 // together before the state loads complete.
-template <typename InT>
+template <typename InT, int KM>
 __global__ __launch_bounds__(256) void decode_tokens_kernel(
     const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
     const InT* __restrict__ beta, const float* __restrict__ log_alpha,
     float* __restrict__ state, const int32_t* __restrict__ n_commit, int K, int H,
     float* __restrict__ o)
 {
-    __shared__ __attribute__((aligned(16))) float sa[kMaxDraft][kDim], sk[kMaxDraft][kDim],
-        sq[kMaxDraft][kDim], sb[kMaxDraft];
+    // KM >= K: token capacity of this instantiation (sizes the staging registers)
+    __shared__ __attribute__((aligned(16))) float sa[KM][kDim], sk[KM][kDim], sq[KM][kDim], sb[KM];
     const int64_t unit = blockIdx.x;  // n * H + h
     const int64_t n = unit / H;
     const int h = static_cast<int>(unit - n * H);
@@ -166,9 +168,9 @@ __global__ __launch_bounds__(256) void decode_tokens_kernel(
 
     // all tokens' per-head inputs are requested first (independent loads), then
     // the state; both are in flight together
-    float x0[kMaxDraft], x1[kMaxDraft], xb[kMaxDraft];
+    float x0[KM], x1[KM], xb[KM];
 #pragma unroll
-    for (int t = 0; t < kMaxDraft; ++t) {
+    for (int t = 0; t < KM; ++t) {
         if (t < K) {
             const int64_t vec = rowvec(t);
             if (tid < kDim) {
@@ -186,7 +188,7 @@ __global__ __launch_bounds__(256) void decode_tokens_kernel(
         s[m] = *reinterpret_cast<const float4*>(S + (row0 + m) * kDim + col);
     float4 vv = load4(v + rowvec(0) + col);
 #pragma unroll
-    for (int t = 0; t < kMaxDraft; ++t) {
+    for (int t = 0; t < KM; ++t) {
         if (t < K) {
             if (tid < kDim) {
                 sa[t][tid] = exp_gate(x0[t]);
@@ -202,11 +204,7 @@ __global__ __launch_bounds__(256) void decode_tokens_kernel(
     for (int t = 0; t < K; ++t) {
         const float4 vt = vv;
         if (t + 1 < K) vv = load4(v + rowvec(t + 1) + col);
-        float a[16], kk[16], qq[16];
-        rows16(&sa[t][row0], a);
-        rows16(&sk[t][row0], kk);
-        rows16(&sq[t][row0], qq);
-        const float4 ot = token_update(s, a, kk, qq, sb[t], vt);
+        const float4 ot = token_update<InT, false>(s, &sa[t][row0], &sk[t][row0], &sq[t][row0], sb[t], vt);
         if (rg == 0) *reinterpret_cast<float4*>(o + rowvec(t) + col) = ot;
         if (t + 1 == commit) {
 #pragma unroll
@@ -226,18 +224,21 @@ hipError_t launch_decode_tokens(const void* q, const void* k, const void* v, con
     if (units <= 0 || K <= 0) return hipSuccess;
     if (K > kMaxDraft) return hipErrorInvalidValue;
     const dim3 grid(static_cast<unsigned>(units)), block(256);
-    if (bf16) {
-        using T = bf16_t;
-        hipLaunchKernelGGL(decode_tokens_kernel<T>, grid, block, 0, stream,
+    auto go = [&](auto km, auto tag) {
+        using T = decltype(tag);
+        constexpr int KMV = decltype(km)::value;
+        hipLaunchKernelGGL((decode_tokens_kernel<T, KMV>), grid, block, 0, stream,
                            static_cast<const T*>(q), static_cast<const T*>(k),
                            static_cast<const T*>(v), static_cast<const T*>(beta), log_alpha,
                            state, n_commit, static_cast<int>(K), static_cast<int>(H), o);
-    } else {
-        hipLaunchKernelGGL(decode_tokens_kernel<float>, grid, block, 0, stream,
-                           static_cast<const float*>(q), static_cast<const float*>(k),
-                           static_cast<const float*>(v), static_cast<const float*>(beta),
-                           log_alpha, state, n_commit, static_cast<int>(K), static_cast<int>(H), o);
-    }
+    };
+    auto pick = [&](auto tag) {
+        if (K <= 4) go(std::integral_constant<int, 4>{}, tag);
+        else if (K <= 8) go(std::integral_constant<int, 8>{}, tag);
+        else go(std::integral_constant<int, 16>{}, tag);
+    };
+    if (bf16) pick(bf16_t{});
+    else pick(0.f);
     return hipGetLastError();
 }
 

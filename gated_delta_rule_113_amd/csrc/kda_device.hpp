@@ -104,22 +104,51 @@ __device__ __forceinline__ float xor_sum_rows(float x)
 //
 // One token of the recurrence on a lane's share of the state: S' = Diag(a) S;
 // p = S'^T k and r = S'^T q summed over all 128 rows (the other row groups
-// through xor_sum_rows); u = beta (v - p); S <- S' + k u^T.  a, kk and qq
-// hold the lane's 16 rows of the gate, key and query; vt its 4 columns of v.
-// Returns the lane's 4 columns of the output o = S^T q = r + (k . q) u.
-__device__ __forceinline__ float4 token_update(float4 (&s)[16], const float (&a)[16],
-                                               const float (&kk)[16], const float (&qq)[16],
-                                               float bt, float4 vt)
+// through xor_sum_rows); u = beta (v - p); S <- S' + k u^T.  a, k and q point
+// at the lane's 16 rows of the token's gate, key and query staged in LDS
+// (16-byte aligned); they are read where used rather than held in registers,
+// which keeps the kernels at four waves per SIMD.  vt holds the lane's 4
+// columns of v.  With RAW, k and q are raw projections: each is scaled to a
+// unit vector (rounded to bf16 for bf16 inputs) as it is read.  Returns the
+// lane's 4 columns of the output o = S^T q = r + (k . q) u.
+template <typename InT, bool RAW>
+__device__ __forceinline__ float4 token_update(float4 (&s)[16], const float* a, const float* k,
+                                               const float* q, float bt, float4 vt)
 {
+    float ik = 1.f, iq = 1.f;
+    if (RAW) {
+        float ssk = 0.f, ssq = 0.f;
+#pragma unroll
+        for (int m4 = 0; m4 < 4; ++m4) {
+            const float4 k4 = *reinterpret_cast<const float4*>(k + 4 * m4);
+            const float4 q4 = *reinterpret_cast<const float4*>(q + 4 * m4);
+            ssk += k4.x * k4.x + k4.y * k4.y + k4.z * k4.z + k4.w * k4.w;
+            ssq += q4.x * q4.x + q4.y * q4.y + q4.z * q4.z + q4.w * q4.w;
+        }
+        ik = inv_norm(xor_sum_rows(ssk));
+        iq = inv_norm(xor_sum_rows(ssq));
+    }
+    auto key = [&](float x) { return RAW ? unit_round(x * ik, InT{}) : x; };
+    auto query = [&](float x) { return RAW ? unit_round(x * iq, InT{}) : x; };
     float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
     float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
     float kq = 0.f;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        s[m].x *= a[m]; s[m].y *= a[m]; s[m].z *= a[m]; s[m].w *= a[m];
-        p0 += kk[m] * s[m].x; p1 += kk[m] * s[m].y; p2 += kk[m] * s[m].z; p3 += kk[m] * s[m].w;
-        r0 += qq[m] * s[m].x; r1 += qq[m] * s[m].y; r2 += qq[m] * s[m].z; r3 += qq[m] * s[m].w;
-        kq += kk[m] * qq[m];
+    for (int m4 = 0; m4 < 4; ++m4) {
+        const float4 a4 = *reinterpret_cast<const float4*>(a + 4 * m4);
+        const float4 k4 = *reinterpret_cast<const float4*>(k + 4 * m4);
+        const float4 q4 = *reinterpret_cast<const float4*>(q + 4 * m4);
+        const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+        const float kv[4] = {key(k4.x), key(k4.y), key(k4.z), key(k4.w)};
+        const float qv[4] = {query(q4.x), query(q4.y), query(q4.z), query(q4.w)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = 4 * m4 + i;
+            s[m].x *= av[i]; s[m].y *= av[i]; s[m].z *= av[i]; s[m].w *= av[i];
+            p0 += kv[i] * s[m].x; p1 += kv[i] * s[m].y; p2 += kv[i] * s[m].z; p3 += kv[i] * s[m].w;
+            r0 += qv[i] * s[m].x; r1 += qv[i] * s[m].y; r2 += qv[i] * s[m].z; r3 += qv[i] * s[m].w;
+            kq += kv[i] * qv[i];
+        }
     }
     p0 = xor_sum_rows(p0); p1 = xor_sum_rows(p1); p2 = xor_sum_rows(p2); p3 = xor_sum_rows(p3);
     r0 = xor_sum_rows(r0); r1 = xor_sum_rows(r1); r2 = xor_sum_rows(r2); r3 = xor_sum_rows(r3);
@@ -127,39 +156,16 @@ __device__ __forceinline__ float4 token_update(float4 (&s)[16], const float (&a)
     const float u0 = bt * (vt.x - p0), u1 = bt * (vt.y - p1);
     const float u2 = bt * (vt.z - p2), u3 = bt * (vt.w - p3);
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        s[m].x += kk[m] * u0; s[m].y += kk[m] * u1; s[m].z += kk[m] * u2; s[m].w += kk[m] * u3;
+    for (int m4 = 0; m4 < 4; ++m4) {
+        const float4 k4 = *reinterpret_cast<const float4*>(k + 4 * m4);
+        const float kv[4] = {key(k4.x), key(k4.y), key(k4.z), key(k4.w)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = 4 * m4 + i;
+            s[m].x += kv[i] * u0; s[m].y += kv[i] * u1; s[m].z += kv[i] * u2; s[m].w += kv[i] * u3;
+        }
     }
     return make_float4(r0 + kq * u0, r1 + kq * u1, r2 + kq * u2, r3 + kq * u3);
-}
-
-// Raw inputs: the token's key and query (the lane's 16 rows of each) become
-// unit vectors, rounded back to bf16 for bf16 inputs.
-template <typename InT>
-__device__ __forceinline__ void unit_key_query(float (&kk)[16], float (&qq)[16])
-{
-    float ssk = 0.f, ssq = 0.f;
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        ssk += kk[m] * kk[m];
-        ssq += qq[m] * qq[m];
-    }
-    const float ik = inv_norm(xor_sum_rows(ssk)), iq = inv_norm(xor_sum_rows(ssq));
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        kk[m] = unit_round(kk[m] * ik, InT{});
-        qq[m] = unit_round(qq[m] * iq, InT{});
-    }
-}
-
-// The lane's 16 rows of a 128-vector staged in LDS (16-byte aligned).
-__device__ __forceinline__ void rows16(const float* x, float (&r)[16])
-{
-#pragma unroll
-    for (int m4 = 0; m4 < 4; ++m4) {
-        const float4 v4 = *reinterpret_cast<const float4*>(x + 4 * m4);
-        r[4 * m4] = v4.x; r[4 * m4 + 1] = v4.y; r[4 * m4 + 2] = v4.z; r[4 * m4 + 3] = v4.w;
-    }
 }
 
 }  // namespace kda

@@ -112,13 +112,9 @@ __global__ __launch_bounds__(256) void prefill_recurrent_kernel(
         if (t0 + TB < len) request(t0 + TB);
         const int nb = static_cast<int>(len - t0 < TB ? len - t0 : TB);
         for (int t = 0; t < nb; ++t) {
-            float a[16], kk[16], qq[16];
-            rows16(&sa[buf][t][row0], a);
-            rows16(&sk[buf][t][row0], kk);
-            rows16(&sq[buf][t][row0], qq);
             const float4 vt = *reinterpret_cast<const float4*>(&sv[buf][t][col]);
-            if (RAW) unit_key_query<InT>(kk, qq);
-            const float4 ot = token_update(s, a, kk, qq, sb[buf][t], vt);
+            const float4 ot = token_update<InT, RAW>(s, &sa[buf][t][row0], &sk[buf][t][row0],
+                                                     &sq[buf][t][row0], sb[buf][t], vt);
             if (rg == 0)
                 *reinterpret_cast<float4*>(o + ((first + t0 + t) * H + h) * kDim + col) = ot;
         }
