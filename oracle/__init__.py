@@ -70,6 +70,11 @@ def load(path: str | None = None):
         lib.kda_oracle_prepare.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                            fp, fp, fp, fp, ctypes.c_int, fp, fp, fp, fp]
         lib.kda_oracle_prepare.restype = ctypes.c_int
+        lib.kda_oracle_backward.argtypes = [
+            ctypes.c_int64, i64p, i64p, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            fp, fp, fp, fp, fp, dp, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
+        lib.kda_oracle_backward.restype = ctypes.c_int
         lib.kda_oracle_max_threads.argtypes = [ctypes.c_int]
         lib.kda_oracle_max_threads.restype = ctypes.c_int
         if path is None:
@@ -156,6 +161,56 @@ def prefill(q, k, v, beta, log_alpha, initial_state=None, n_threads: int = 0, li
                     np.reshape(log_alpha, (B * T, H, dk)), row0, length, 1,
                     initial_state, n_threads, lib)
     return o.reshape(B, T, H, dv), s
+
+
+def backward(q, k, v, beta, log_alpha, d_o, initial_state=None, d_final_state=None,
+             n_threads: int = 0, lib=None):
+    """Gradients of L = sum <d_o, o> + <d_final_state, final_state> for a dense
+    batch (shapes as in ``prefill``; d_o like o, d_final_state like the final
+    state), by the chain rule through the token recurrence in reverse
+    (``kda_oracle_backward``).  Returns a dict of float64 arrays: dq, dk, dv,
+    dbeta, dlog_alpha (shaped like their inputs) and dinitial_state
+    [B, H, dk, dv].  Test infrastructure for a backward pass: no kernel of
+    the library computes these yet."""
+    lib = lib or load()
+    q = np.asarray(q)
+    B, T, H, dk = q.shape
+    dv = np.asarray(v).shape[-1]
+    rows = B * T
+    qf = _f32(np.reshape(q, (rows, H, dk)), "q")
+    kf = _f32(np.reshape(k, (rows, H, dk)), "k")
+    vf = _f32(np.reshape(v, (rows, H, dv)), "v")
+    bf = _f32(np.reshape(beta, (rows, H)), "beta")
+    lf = _f32(np.reshape(log_alpha, (rows, H, dk)), "log_alpha")
+    do = np.ascontiguousarray(np.reshape(d_o, (rows, H, dv)), dtype=np.float64)
+    row0 = np.arange(B, dtype=np.int64) * T
+    length = np.full(B, T, dtype=np.int64)
+    s0p = dsp = None
+    if initial_state is not None:
+        s0 = np.ascontiguousarray(initial_state, dtype=np.float64)
+        if s0.shape != (B, H, dk, dv):
+            raise ValueError(f"initial_state must be {(B, H, dk, dv)}")
+        s0p = _ptr(s0, ctypes.c_double)
+    if d_final_state is not None:
+        ds = np.ascontiguousarray(d_final_state, dtype=np.float64)
+        if ds.shape != (B, H, dk, dv):
+            raise ValueError(f"d_final_state must be {(B, H, dk, dv)}")
+        dsp = _ptr(ds, ctypes.c_double)
+    out = {"dq": np.zeros((rows, H, dk)), "dk": np.zeros((rows, H, dk)),
+           "dv": np.zeros((rows, H, dv)), "dbeta": np.zeros((rows, H)),
+           "dlog_alpha": np.zeros((rows, H, dk)), "dinitial_state": np.zeros((B, H, dk, dv))}
+    rc = lib.kda_oracle_backward(B, _ptr(row0, ctypes.c_int64), _ptr(length, ctypes.c_int64), 1,
+                                 H, dk, dv, _ptr(qf, ctypes.c_float), _ptr(kf, ctypes.c_float),
+                                 _ptr(vf, ctypes.c_float), _ptr(bf, ctypes.c_float),
+                                 _ptr(lf, ctypes.c_float), s0p, _ptr(do, ctypes.c_double), dsp,
+                                 *(_ptr(out[n], ctypes.c_double) for n in
+                                   ("dq", "dk", "dv", "dbeta", "dlog_alpha", "dinitial_state")),
+                                 int(n_threads))
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_backward failed with code {rc}")
+    shapes = {"dq": (B, T, H, dk), "dk": (B, T, H, dk), "dv": (B, T, H, dv), "dbeta": (B, T, H),
+              "dlog_alpha": (B, T, H, dk)}
+    return {n: (x.reshape(shapes[n]) if n in shapes else x) for n, x in out.items()}
 
 
 def varlen_prefill(q, k, v, beta, log_alpha, cu_seqlens, initial_state=None,

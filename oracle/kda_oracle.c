@@ -142,8 +142,9 @@ int kda_oracle_run(int64_t n_seq, const int64_t *row0, const int64_t *len, int64
     const int64_t units = n_seq * H;
     int failed = 0;
 #ifdef _OPENMP
-    if (n_threads > 0) omp_set_num_threads(n_threads);
-#pragma omp parallel reduction(| : failed)
+    /* per-call thread count; the process-wide default is left alone */
+    const int nt = n_threads > 0 ? n_threads : omp_get_max_threads();
+#pragma omp parallel reduction(| : failed) num_threads(nt)
 #endif
     {
         double *S = (double *)malloc((size_t)(dk * dv) * sizeof(double));
@@ -221,4 +222,205 @@ int kda_oracle_prepare(int64_t rows, int64_t H, int64_t dk,
         }
     }
     return 0;
+}
+
+/*
+ * Gradients (the adjoint of kda_oracle_run), for a later backward pass: the
+ * chain rule applied to the forward steps above in reverse order, token by
+ * token.  For the scalar loss
+ *     L = sum_t <dO_t, o_t> + <dS_T, S_T>
+ * (dO = d_o, dS_T = d_sT or zero) and G the gradient with respect to the
+ * current state, initialised to dS_T, each token t from the last back:
+ *     G    += q_t dO_t^T                    read-out o_t = S_t^T q_t
+ *     dq_t  = S_t dO_t
+ *     du    = G^T k_t                       correct  S_t = S' + k_t u^T
+ *     dk_t  = G u
+ *     dbeta_t = du . (v_t - p),  dv_t = beta_t du,  dp = -beta_t du
+ *     G'    = G + k_t dp^T                  recall   p = S'^T k_t
+ *     dk_t += S' dp
+ *     dlog_alpha_t[i] = sum_j G'[i][j] S'[i][j]   decay S' = Diag(a) S_{t-1}, a = exp(log_alpha)
+ *     G     = Diag(a) G'
+ * and finally dS_0 = G.  The entering state of every token is recomputed from
+ * checkpoints taken every CK tokens, so memory stays (len/CK + CK) states per
+ * (sequence, head).  Same addressing as kda_oracle_run; gradients are fp64 in
+ * the layout of their inputs.  Returns 0, -1 on bad sizes, -2 on allocation
+ * failure.
+ */
+#define CK 64
+
+static void backward_unit(int64_t n, int64_t h, const int64_t *row0, const int64_t *len,
+                          int64_t row_step, int64_t H, int64_t dk, int64_t dv,
+                          const float *q, const float *k, const float *v,
+                          const float *beta, const float *log_alpha, const double *s0,
+                          const double *d_o, const double *d_sT,
+                          double *dq, double *dkk, double *dvv, double *dbeta, double *dla,
+                          double *ds0, double *ckpt, double *blk, double *S, double *G,
+                          double *a, double *p, double *u, double *du, double *dp)
+{
+    const int64_t unit = n * H + h;
+    const int64_t L = len[n], SZ = dk * dv;
+    /* forward pass: the state entering token t for every t = 0 (mod CK) */
+    if (s0) memcpy(S, s0 + unit * SZ, (size_t)SZ * sizeof(double));
+    else memset(S, 0, (size_t)SZ * sizeof(double));
+    for (int64_t t = 0; t < L; ++t) {
+        if (t % CK == 0) memcpy(ckpt + (t / CK) * SZ, S, (size_t)SZ * sizeof(double));
+        const int64_t row = row0[n] + t * row_step;
+        const float *kt = k + (row * H + h) * dk;
+        const float *vt = v + (row * H + h) * dv;
+        const float *lat = log_alpha + (row * H + h) * dk;
+        const double bt = (double)beta[row * H + h];
+        for (int64_t i = 0; i < dk; ++i) {
+            const double ai = exp((double)lat[i]);
+            for (int64_t j = 0; j < dv; ++j) S[i * dv + j] *= ai;
+        }
+        for (int64_t j = 0; j < dv; ++j) p[j] = 0.0;
+        for (int64_t i = 0; i < dk; ++i)
+            for (int64_t j = 0; j < dv; ++j) p[j] += S[i * dv + j] * (double)kt[i];
+        for (int64_t j = 0; j < dv; ++j) u[j] = bt * ((double)vt[j] - p[j]);
+        for (int64_t i = 0; i < dk; ++i)
+            for (int64_t j = 0; j < dv; ++j) S[i * dv + j] += (double)kt[i] * u[j];
+    }
+
+    /* backward pass */
+    if (d_sT) memcpy(G, d_sT + unit * SZ, (size_t)SZ * sizeof(double));
+    else memset(G, 0, (size_t)SZ * sizeof(double));
+    for (int64_t b0 = ((L - 1) / CK) * CK; L > 0 && b0 >= 0; b0 -= CK) {
+        const int64_t b1 = b0 + CK < L ? b0 + CK : L;
+        /* entering states of tokens b0 .. b1-1, recomputed from the checkpoint */
+        memcpy(blk, ckpt + (b0 / CK) * SZ, (size_t)SZ * sizeof(double));
+        for (int64_t t = b0; t + 1 < b1; ++t) {
+            double *cur = blk + (t - b0) * SZ, *nxt = cur + SZ;
+            const int64_t row = row0[n] + t * row_step;
+            const float *kt = k + (row * H + h) * dk;
+            const float *vt = v + (row * H + h) * dv;
+            const float *lat = log_alpha + (row * H + h) * dk;
+            const double bt = (double)beta[row * H + h];
+            for (int64_t i = 0; i < dk; ++i) {
+                const double ai = exp((double)lat[i]);
+                for (int64_t j = 0; j < dv; ++j) nxt[i * dv + j] = cur[i * dv + j] * ai;
+            }
+            for (int64_t j = 0; j < dv; ++j) p[j] = 0.0;
+            for (int64_t i = 0; i < dk; ++i)
+                for (int64_t j = 0; j < dv; ++j) p[j] += nxt[i * dv + j] * (double)kt[i];
+            for (int64_t j = 0; j < dv; ++j) u[j] = bt * ((double)vt[j] - p[j]);
+            for (int64_t i = 0; i < dk; ++i)
+                for (int64_t j = 0; j < dv; ++j) nxt[i * dv + j] += (double)kt[i] * u[j];
+        }
+        for (int64_t t = b1 - 1; t >= b0; --t) {
+            const double *Sin = blk + (t - b0) * SZ;  /* S_{t-1} */
+            const int64_t row = row0[n] + t * row_step;
+            const float *qt = q + (row * H + h) * dk;
+            const float *kt = k + (row * H + h) * dk;
+            const float *vt = v + (row * H + h) * dv;
+            const float *lat = log_alpha + (row * H + h) * dk;
+            const double bt = (double)beta[row * H + h];
+            const double *dot = d_o + (row * H + h) * dv;
+            double *dqt = dq + (row * H + h) * dk;
+            double *dkt = dkk + (row * H + h) * dk;
+            double *dvt = dvv + (row * H + h) * dv;
+            double *dlat = dla + (row * H + h) * dk;
+
+            /* the token's forward quantities: S' = Diag(a) S_{t-1} (in S), p and u;
+               S_t = S' + k u^T is formed where it is used */
+            for (int64_t i = 0; i < dk; ++i) {
+                a[i] = exp((double)lat[i]);
+                for (int64_t j = 0; j < dv; ++j) S[i * dv + j] = Sin[i * dv + j] * a[i];
+            }
+            for (int64_t j = 0; j < dv; ++j) p[j] = 0.0;
+            for (int64_t i = 0; i < dk; ++i)
+                for (int64_t j = 0; j < dv; ++j) p[j] += S[i * dv + j] * (double)kt[i];
+            for (int64_t j = 0; j < dv; ++j) u[j] = bt * ((double)vt[j] - p[j]);
+
+            /* read-out: G += q dO^T;  dq = S_t dO with S_t = S' + k u^T */
+            for (int64_t i = 0; i < dk; ++i)
+                for (int64_t j = 0; j < dv; ++j) G[i * dv + j] += (double)qt[i] * dot[j];
+            for (int64_t i = 0; i < dk; ++i) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < dv; ++j)
+                    acc += (S[i * dv + j] + (double)kt[i] * u[j]) * dot[j];
+                dqt[i] = acc;
+            }
+            /* correct: du = G^T k, dk = G u */
+            for (int64_t j = 0; j < dv; ++j) du[j] = 0.0;
+            for (int64_t i = 0; i < dk; ++i)
+                for (int64_t j = 0; j < dv; ++j) du[j] += G[i * dv + j] * (double)kt[i];
+            for (int64_t i = 0; i < dk; ++i) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < dv; ++j) acc += G[i * dv + j] * u[j];
+                dkt[i] = acc;
+            }
+            /* compare: u = beta (v - p) */
+            double db = 0.0;
+            for (int64_t j = 0; j < dv; ++j) {
+                db += du[j] * ((double)vt[j] - p[j]);
+                dvt[j] = bt * du[j];
+                dp[j] = -bt * du[j];
+            }
+            dbeta[row * H + h] = db;
+            /* recall: p = S'^T k  ->  G' = G + k dp^T,  dk += S' dp */
+            for (int64_t i = 0; i < dk; ++i) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < dv; ++j) {
+                    G[i * dv + j] += (double)kt[i] * dp[j];
+                    acc += S[i * dv + j] * dp[j];
+                }
+                dkt[i] += acc;
+            }
+            /* decay: S' = Diag(a) S_{t-1} */
+            for (int64_t i = 0; i < dk; ++i) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < dv; ++j) acc += G[i * dv + j] * S[i * dv + j];
+                dlat[i] = acc;
+                for (int64_t j = 0; j < dv; ++j) G[i * dv + j] *= a[i];
+            }
+        }
+    }
+    memcpy(ds0 + unit * SZ, G, (size_t)SZ * sizeof(double));
+}
+
+int kda_oracle_backward(int64_t n_seq, const int64_t *row0, const int64_t *len, int64_t row_step,
+                        int64_t H, int64_t dk, int64_t dv,
+                        const float *q, const float *k, const float *v,
+                        const float *beta, const float *log_alpha, const double *s0,
+                        const double *d_o, const double *d_sT,
+                        double *dq, double *dkk, double *dvv, double *dbeta, double *dla,
+                        double *ds0, int n_threads)
+{
+    if (n_seq < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
+    int64_t longest = 0;
+    for (int64_t n = 0; n < n_seq; ++n) {
+        if (len[n] < 0 || row0[n] < 0) return -1;
+        if (len[n] > longest) longest = len[n];
+    }
+    const int64_t units = n_seq * H, SZ = dk * dv;
+    const int64_t nck = longest / CK + 1;
+    int failed = 0;
+#ifdef _OPENMP
+    /* per-call thread count; the process-wide default is left alone */
+    const int nt = n_threads > 0 ? n_threads : omp_get_max_threads();
+#pragma omp parallel reduction(| : failed) num_threads(nt)
+#endif
+    {
+        double *ckpt = (double *)malloc((size_t)(nck * SZ) * sizeof(double));
+        double *blk = (double *)malloc((size_t)(CK * SZ) * sizeof(double));
+        double *S = (double *)malloc((size_t)SZ * sizeof(double));
+        double *G = (double *)malloc((size_t)SZ * sizeof(double));
+        double *a = (double *)malloc((size_t)dk * sizeof(double));
+        double *p = (double *)malloc((size_t)dv * sizeof(double));
+        double *u = (double *)malloc((size_t)dv * sizeof(double));
+        double *du = (double *)malloc((size_t)dv * sizeof(double));
+        double *dp = (double *)malloc((size_t)dv * sizeof(double));
+        const int ok = ckpt && blk && S && G && a && p && u && du && dp;
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+        for (int64_t w = 0; w < units; ++w) {
+            if (!ok) { failed = 1; continue; }
+            backward_unit(w / H, w % H, row0, len, row_step, H, dk, dv, q, k, v, beta, log_alpha,
+                          s0, d_o, d_sT, dq, dkk, dvv, dbeta, dla, ds0, ckpt, blk, S, G, a, p, u,
+                          du, dp);
+        }
+        free(ckpt); free(blk); free(S); free(G); free(a); free(p); free(u); free(du); free(dp);
+    }
+    return failed ? -2 : 0;
 }

@@ -421,9 +421,83 @@ def pin_prepare_unit_vectors(lib=None):
     assert np.allclose(cos, 1.0, atol=1e-6)
 
 
+
+# ---------------------------------------------------------------------------
+# gradients (kda_oracle_backward): central differences of the forward oracle,
+# and the closed forms of the identity gate
+# ---------------------------------------------------------------------------
+
+def _loss(inputs, d_o, d_s, lib):
+    # one thread: thousands of tiny calls, and test workers share the cores
+    q, k, v, b, la, s0 = inputs
+    o, S = oracle.prefill(q, k, v, b, la, s0, n_threads=1, lib=lib)
+    return float(np.sum(o * d_o) + np.sum(S * d_s))
+
+
+def _fd_check(seed, B, T, H, dk, dv, lib):
+    q, k, v, b, la, s0 = _random_case(seed, B=B, T=T, H=H, dk=dk, dv=dv)
+    la[..., 0] = -np.float32(5.5)      # a fast-forgetting channel
+    la[..., -1] = -np.float32(1e-4)    # a long-memory channel
+    r = _rng(seed + 1000)
+    d_o = r.standard_normal((B, T, H, dv))
+    d_s = r.standard_normal((B, H, dk, dv))
+    g = oracle.backward(q, k, v, b, la, d_o, s0, d_s, n_threads=1, lib=lib)
+    inputs = [q, k, v, b, la, s0]
+    names = ["dq", "dk", "dv", "dbeta", "dlog_alpha", "dinitial_state"]
+    for slot, name in enumerate(names):
+        x = inputs[slot]
+        fd = np.zeros(x.shape)
+        for idx in np.ndindex(*x.shape):
+            h = 2.0 ** -11 if slot < 5 else 2.0 ** -20
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            step = float(xp[idx]) - float(xm[idx])   # exact: fp32 inputs take exact steps
+            lp = _loss(inputs[:slot] + [xp] + inputs[slot + 1:], d_o, d_s, lib)
+            lm = _loss(inputs[:slot] + [xm] + inputs[slot + 1:], d_o, d_s, lib)
+            fd[idx] = (lp - lm) / step
+        err = _rel(g[name], fd)
+        assert err < 2e-6, (name, err)
+
+
+def pin_backward_finite_differences(lib=None):
+    """Every gradient entry against central differences of the forward oracle's
+    loss sum <dO, o> + <dS_T, S_T>: a short case with two sequences and heads,
+    and one of 70 tokens, longer than the backward's 64-token checkpoint
+    interval.  Gated mix: one fast (log alpha = -5.5) and one slow (-1e-4)
+    channel per head."""
+    _fd_check(61, B=2, T=5, H=2, dk=4, dv=3, lib=lib)
+    _fd_check(62, B=1, T=70, H=1, dk=3, dv=2, lib=lib)
+
+
+def pin_backward_identity_gate(lib=None):
+    """alpha = 1, beta = 0: the state never changes, o_t = S0^T q_t and S_T =
+    S0, so dq_t = S0 dO_t, dS0 = dS_T + sum_t q_t dO_t^T, dv = dk = 0; with
+    G_t = dS_T + sum_{s >= t} q_s dO_s^T, the write strength gets
+    dbeta_t = (v_t - S0^T k_t) . (G_t^T k_t) and the gate
+    dlog_alpha_t[i] = sum_j G_t[i, j] S0[i, j]."""
+    B, T, H, dk, dv = 1, 6, 1, 5, 4
+    q, k, v, _, _, s0 = _random_case(63, B=B, T=T, H=H, dk=dk, dv=dv)
+    b = np.zeros((B, T, H), np.float32)
+    la = np.zeros((B, T, H, dk), np.float32)
+    r = _rng(64)
+    d_o = r.standard_normal((B, T, H, dv))
+    d_s = r.standard_normal((B, H, dk, dv))
+    g = oracle.backward(q, k, v, b, la, d_o, s0, d_s, lib=lib)
+    S0 = s0[0, 0]
+    qq, kk, vv, dd = (x[0, :, 0].astype(np.float64) for x in (q, k, v, d_o))
+    assert _rel(g["dq"][0, :, 0], dd @ S0.T) < 1e-12
+    assert _rel(g["dinitial_state"][0, 0], d_s[0, 0] + qq.T @ dd) < 1e-12
+    assert np.all(g["dv"] == 0) and np.all(g["dk"] == 0)
+    for t in range(T):
+        Gt = d_s[0, 0] + qq[t:].T @ dd[t:]
+        assert abs(g["dbeta"][0, t, 0] - (vv[t] - S0.T @ kk[t]) @ (Gt.T @ kk[t])) < 1e-12
+        assert _rel(g["dlog_alpha"][0, t, 0], np.sum(Gt * S0, axis=1)) < 1e-12
+
 ALL_PINS = [
     pin_bruteforce_numpy, pin_bruteforce_exact, pin_identity, pin_erase_then_write,
     pin_decay_closed_form, pin_channel_locality, pin_page_delta_rule,
     pin_causal_linear_attention, pin_scalar_gate, pin_resume, pin_linearity,
     pin_varlen_and_layouts, pin_prepare_gates, pin_prepare_unit_vectors,
+    pin_backward_finite_differences, pin_backward_identity_gate,
 ]

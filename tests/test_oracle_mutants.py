@@ -72,6 +72,13 @@ MUTANTS = {
     "no_bf16_rounding": _replace("out[i] = (float)(round ? round_bf16(y) : y);", "out[i] = (float)y;"),
     "bf16_truncated": _replace("return ldexp(nearbyint(ldexp(m, 8)), e - 8);",
                                "return ldexp(trunc(ldexp(m, 8)), e - 8);"),
+    "bwd_recall_term_dropped": _replace("                dkt[i] += acc;", "                (void)acc;"),
+    "bwd_gate_uses_entering_state": _replace("for (int64_t j = 0; j < dv; ++j) acc += G[i * dv + j] * S[i * dv + j];",
+                                             "for (int64_t j = 0; j < dv; ++j) acc += G[i * dv + j] * Sin[i * dv + j];"),
+    "bwd_dp_sign": _replace("dp[j] = -bt * du[j];", "dp[j] = bt * du[j];"),
+    "bwd_dq_without_write": _replace("acc += (S[i * dv + j] + (double)kt[i] * u[j]) * dot[j];",
+                                     "acc += S[i * dv + j] * dot[j];"),
+    "bwd_gradient_not_decayed": _replace("for (int64_t j = 0; j < dv; ++j) G[i * dv + j] *= a[i];", ""),
     "gate_off_by_one_token": _replace("const float *lat = log_alpha + (row * H + h) * dk;",
                                       "const float *lat = log_alpha + ((t ? row - row_step : row) * H + h) * dk;"),
 }
