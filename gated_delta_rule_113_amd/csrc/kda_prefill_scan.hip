@@ -302,7 +302,9 @@ struct ScanArgs {
     const bf16_t* beta;
     const float* log_alpha;
     const int32_t* cu_seqlens;  // packed rows, or null for dense sequences of T rows
-    const int32_t* seg_first;   // packed + segmented: first segment of each sequence [n_seq + 1]
+    const int32_t* seg_first;   // packed + segmented: first segment of each sequence [n_seq + 1],
+                                // then the segment length the plan chose
+    const int32_t* seg_order;   // packed + segmented: segments by decreasing length (launch order)
     int64_t T;                  // dense sequence length
     int64_t n_seq;
     int64_t seg_len;            // tokens per segment (multiple of 64); 0 = one segment each
@@ -371,7 +373,8 @@ __device__ SegInfo decode_segment(const ScanArgs& a, int64_t z)
         len = static_cast<int64_t>(a.cu_seqlens[lo + 1]) - s.row0;
     }
     s.len = len;
-    const int64_t seg = s.nseg == 1 ? len : a.seg_len;
+    // packed input: the segment length is the plan's choice, stored after seg_first
+    const int64_t seg = s.nseg == 1 ? len : (a.seg_first ? a.seg_first[a.n_seq + 1] : a.seg_len);
     s.begin = s.j * seg;
     s.end = (s.j == s.nseg - 1) ? len : s.begin + seg;
     return s;
@@ -391,8 +394,13 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
     const int l16 = lane & 15;
     const int g4 = lane >> 4;
     const int H = a.H;
-    const int64_t z = blockIdx.x / H;
+    int64_t z = blockIdx.x / H;
     const int h = static_cast<int>(blockIdx.x - z * H);
+    if (a.seg_order) {
+        // packed: the longest segments first, so that short ones fill in at the end
+        if (z >= a.seg_first[a.n_seq]) return;
+        z = a.seg_order[z];
+    }
 
     const SegInfo sg = decode_segment(a, z);
     if (!sg.valid) return;
@@ -1266,14 +1274,87 @@ __global__ __launch_bounds__(256) void combine_kernel(const ScanArgs a)
     }
 }
 
-// Packed sequences: first segment index of every sequence,
-// seg_first[n] = sum_{m < n} max(1, ceil(len_m / seg_len)).  One workgroup.
+// Packed sequences: the segment length and the first segment index of every
+// sequence, seg_first[n] = sum_{m < n} max(1, ceil(len_m / L)), with L stored
+// in seg_first[n_seq + 1].  One workgroup.
+//
+// L is chosen among seg_max and the powers of two below it down to seg_min
+// by the time it predicts for the two scan passes.  Pass 1 runs every segment
+// but the last of each sequence, all exactly L tokens long: it takes
+// ceil(segments * H / CUs) rounds of L tokens.  Pass 3 runs every segment and
+// takes about the larger of its work spread over the CUs and its longest
+// segment.  A pass-1 chunk costs about 0.9 of a pass-3 chunk.  Short segments
+// balance the CUs but add pass-1 work (every boundary is one more map); the
+// lengths are only known here, on the device.
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* cu, int64_t n_seq,
-                                                    int64_t seg_len, int32_t* seg_first)
+                                                    int64_t seg_max, int64_t seg_min, int64_t H,
+                                                    int64_t n_cu, int32_t* seg_first,
+                                                    int32_t* seg_order)
 {
+    constexpr int kCand = 6;
     __shared__ int64_t part[1024];
+    __shared__ double work1[kCand][32];
+    __shared__ int64_t longest_part[32];
+    __shared__ int64_t chosen;
     const int tid = threadIdx.x;
     const int64_t lo = n_seq * tid / 1024, hi = n_seq * (tid + 1) / 1024;
+    int64_t cand[kCand];
+    int nc = 0;
+    cand[nc++] = seg_max;
+    {
+        int64_t L = 64;
+        while (L * 2 < seg_max) L *= 2;  // the largest power of two below seg_max
+        for (; L >= seg_min && L >= 64 && nc < kCand; L /= 2) cand[nc++] = L;
+    }
+    // per candidate: the number of pass-1 segments (all but each sequence's last)
+    double w1[kCand];
+    int64_t longest = 0, total = 0;
+    for (int c = 0; c < kCand; ++c) w1[c] = 0.0;
+    for (int64_t m = lo; m < hi; ++m) {
+        const int64_t len = static_cast<int64_t>(cu[m + 1]) - cu[m];
+        longest = len > longest ? len : longest;
+        total += len;
+        for (int c = 0; c < nc; ++c)
+            if (len > cand[c]) w1[c] += static_cast<double>((len - 1) / cand[c]);
+    }
+    // reduce over the workgroup: wave sums through LDS
+    const int wave = tid >> 6, lane = tid & 63;
+    for (int off = 32; off > 0; off >>= 1) {
+        for (int c = 0; c < nc; ++c) w1[c] += __shfl_xor(w1[c], off);
+        const int64_t lo2 = __shfl_xor(longest, off);
+        longest = lo2 > longest ? lo2 : longest;
+        total += __shfl_xor(total, off);
+    }
+    if (lane == 0) {
+        for (int c = 0; c < nc; ++c) work1[c][wave] = w1[c];
+        longest_part[wave] = longest;
+        part[wave] = total;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int64_t lg = 0, tot = 0;
+        for (int w = 0; w < 16; ++w) {
+            lg = longest_part[w] > lg ? longest_part[w] : lg;
+            tot += part[w];
+        }
+        const double per_cu3 = static_cast<double>(tot) * H / n_cu;
+        double best = 0.0;
+        int64_t pick = cand[0];
+        for (int c = 0; c < nc; ++c) {
+            double sum1 = 0.0;
+            for (int w = 0; w < 16; ++w) sum1 += work1[c][w];
+            const double p1 = ceil(sum1 * H / n_cu) * static_cast<double>(cand[c]);
+            const double p3 = fmax(per_cu3, static_cast<double>(cand[c] < lg ? cand[c] : lg));
+            const double est = 0.9 * p1 + p3;
+            if (c == 0 || est < best) {
+                best = est;
+                pick = cand[c];
+            }
+        }
+        chosen = pick;
+    }
+    __syncthreads();
+    const int64_t seg_len = chosen;
     auto count = [&](int64_t m) {
         const int64_t len = static_cast<int64_t>(cu[m + 1]) - cu[m];
         const int64_t c = (len + seg_len - 1) / seg_len;
@@ -1294,7 +1375,47 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* cu, int64_t n
         seg_first[m] = static_cast<int32_t>(run);
         run += count(m);
     }
-    if (tid == 1023) seg_first[n_seq] = static_cast<int32_t>(part[1023]);
+    if (tid == 1023) {
+        seg_first[n_seq] = static_cast<int32_t>(part[1023]);
+        seg_first[n_seq + 1] = static_cast<int32_t>(seg_len);
+    }
+
+    // Launch order: segments by decreasing chunk count (a counting sort; the
+    // order within one count is whatever the atomics give, which changes no
+    // result: every segment is computed the same way wherever it runs).
+    constexpr int NB = 2048;  // chunk-count buckets; longer segments share the top one
+    __shared__ int hist[NB], start[NB];
+    for (int b = tid; b < NB; b += 1024) hist[b] = 0;
+    __syncthreads();
+    const int64_t n_act = part[1023];
+    auto bucket_of = [&](int64_t z) {
+        int64_t lo2 = 0, hi2 = n_seq;  // seg_first[lo2] <= z < seg_first[hi2]
+        while (hi2 - lo2 > 1) {
+            const int64_t mid = (lo2 + hi2) >> 1;
+            if (seg_first[mid] <= z) lo2 = mid;
+            else hi2 = mid;
+        }
+        const int64_t len = static_cast<int64_t>(cu[lo2 + 1]) - cu[lo2];
+        const int64_t j = z - seg_first[lo2];
+        const int64_t nseg = static_cast<int64_t>(seg_first[lo2 + 1]) - seg_first[lo2];
+        const int64_t tokens = nseg == 1 ? len : (j == nseg - 1 ? len - j * seg_len : seg_len);
+        const int64_t chunks = (tokens + 63) / 64;
+        return static_cast<int>(chunks < NB ? chunks : NB - 1);
+    };
+    for (int64_t z = tid; z < n_act; z += 1024) atomicAdd(&hist[bucket_of(z)], 1);
+    __syncthreads();
+    if (tid == 0) {
+        int run2 = 0;
+        for (int b = NB - 1; b >= 0; --b) {
+            start[b] = run2;
+            run2 += hist[b];
+        }
+    }
+    __syncthreads();
+    for (int64_t z = tid; z < n_act; z += 1024) {
+        const int r = atomicAdd(&start[bucket_of(z)], 1);
+        seg_order[r] = static_cast<int32_t>(z);
+    }
 }
 
 // ---------------- host side
@@ -1398,11 +1519,21 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
     const int64_t longest_bound = cu_seqlens ? T_total : T;
     const dim3 block(NT);
 
+    // Packed input with the automatic length: the plan kernel picks the
+    // segment length on the device, between seg and seg_min; grid and
+    // workspace are sized for the shortest candidate.
+    const bool plan_on_device = cu_seqlens && g_forced_segment <= 0;
+    const int64_t seg_min =
+        plan_on_device ? std::max<int64_t>(kMinSegment, (seg / 8 + CH - 1) / CH * CH) : seg;
     int64_t n_segs = 0;
     size_t ws_bytes = 0, plan_bytes = 0;
-    if (longest_bound > seg) {
-        n_segs = cu_seqlens ? n_seq + (T_total + seg - 1) / seg : n_seq * ((T + seg - 1) / seg);
-        plan_bytes = cu_seqlens ? ((static_cast<size_t>(n_seq) + 1) * 4 + 255) / 256 * 256 : 0;
+    if (longest_bound > seg_min) {
+        n_segs = cu_seqlens ? n_seq + (T_total + seg_min - 1) / seg_min
+                            : n_seq * ((T + seg - 1) / seg);
+        plan_bytes = cu_seqlens
+                         ? ((static_cast<size_t>(n_seq) + 2 + static_cast<size_t>(n_segs)) * 4 + 255) /
+                               256 * 256
+                         : 0;
         ws_bytes = plan_bytes + static_cast<size_t>(n_segs) * H * 3 * SS * sizeof(float);
     }
     void* ws = nullptr;
@@ -1436,8 +1567,10 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
     char* w = static_cast<char*>(ws);
     if (cu_seqlens) {
         a.seg_first = reinterpret_cast<int32_t*>(w);
+        a.seg_order = a.seg_first + n_seq + 2;
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens, n_seq, seg,
-                           const_cast<int32_t*>(a.seg_first));
+                           seg_min, H, static_cast<int64_t>(cu_count(dev)),
+                           const_cast<int32_t*>(a.seg_first), const_cast<int32_t*>(a.seg_order));
         e = hipGetLastError();
         report("segment plan launch", e);
         if (e != hipSuccess) {
