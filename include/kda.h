@@ -250,8 +250,11 @@ kda_status kda_varlen_prefill_slots(const void *q, const void *k, const void *v,
  * context-parallel" in "Kimi K3 -- the architecture and infrastructure,
  * explained", section "Kimi Delta Attention: the load-bearing choice").
  * 0 (the default) picks the length from the problem size and the number of
- * compute units.  tokens must be 0 or a positive multiple of 64, else
- * KDA_ERR_SHAPE.  Results do not depend on it beyond rounding.
+ * compute units; for packed input a small planning kernel then chooses, on
+ * the device where the sequence lengths are, between that length and the
+ * powers of two below it (down to an eighth of it).  tokens must be 0 or a
+ * positive multiple of 64, else KDA_ERR_SHAPE.  Results do not depend on it
+ * beyond rounding.
  */
 kda_status kda_set_prefill_segment(int64_t tokens);
 
