@@ -49,3 +49,40 @@ def test_decode_graph_replay_matches_direct_calls():
         assert torch.equal(state, ref_state), f"replay {rep}: state differs"
         assert torch.equal(out, ref_out), f"replay {rep}: outputs differ"
     assert np.isfinite(out.cpu().numpy()).all()
+
+
+def test_segmented_packed_prefill_graph_replay():
+    """A packed prefill cut into segments (the plan kernel, both scan passes,
+    the combine kernel, the token kernel for short sequences and the
+    stream-ordered workspace) captured in a HIP graph: every replay gives the
+    bits of the direct call."""
+    torch = __import__("torch")
+    dev = device()
+    inp = ki.varlen_prefill(71, [300, 5, 700, 64, 12], H=2)
+    t = upload(inp, dev)
+    args = (t["q"], t["k"], t["v"], t["beta"], t["log_alpha"], t["cu_seqlens"], t["initial_state"])
+    kda.kda_set_prefill_segment(128)
+    try:
+        o_ref, S_ref = kda.kda_varlen_prefill(*args)
+        torch.cuda.synchronize()
+        o, S = torch.empty_like(o_ref), torch.empty_like(S_ref)
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            kda.kda_varlen_prefill(*args, out=o, final_state=S)
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            kda.kda_varlen_prefill(*args, out=o, final_state=S)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            o.zero_()  # eager work between replays
+            S.zero_()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(o, o_ref), f"replay {rep}: outputs differ"
+            assert torch.equal(S, S_ref), f"replay {rep}: final states differ"
+    finally:
+        kda.kda_set_prefill_segment(0)
