@@ -305,6 +305,8 @@ struct ScanArgs {
     const int32_t* seg_first;   // packed + segmented: first segment of each sequence [n_seq + 1],
                                 // then the segment length the plan chose
     const int32_t* seg_order;   // packed + segmented: segments by decreasing length (launch order)
+    const int32_t* ws_first;    // packed + segmented: first workspace slot of each sequence
+                                // (only sequences of two or more segments have slots)
     int64_t T;                  // dense sequence length
     int64_t n_seq;
     int64_t seg_len;            // tokens per segment (multiple of 64); 0 = one segment each
@@ -315,8 +317,8 @@ struct ScanArgs {
     float* o;
     int raw;       // q, k unnormalised, beta and log_alpha logits (kda.h *_raw)
     int64_t short_max;  // sequences of at most this many tokens are skipped (0: none)
-    float* ws_maps;   // [n_segs][H][2][d_k][d_v]: M and R of each segment but the last
-    float* ws_start;  // [n_segs][H][d_k][d_v]: entering state of each segment
+    float* ws_maps;   // [slots][H][2][d_k][d_v]: M and R of each segment but the last
+    float* ws_start;  // [slots][H][d_k][d_v]: entering state of each segment
 };
 
 namespace {
@@ -406,6 +408,9 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
     if (!sg.valid) return;
     if (sg.len <= a.short_max) return;        // a short sequence: the token-by-token kernel's
     if (!OUT && sg.j == sg.nseg - 1) return;  // the last segment needs no map
+    // this segment's workspace slot (dense: the segment index; packed: the
+    // sequence's first slot + j, multi-segment sequences only)
+    const int64_t wz = a.ws_first ? a.ws_first[sg.n] + sg.j : z;
     const bool blkM = !OUT && sg.j > 0;       // pass 1: is the M block carried?
 
     const int col = 16 * wave + l16;          // this lane's value column
@@ -415,7 +420,7 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
     {
         const float* init = nullptr;
         if (OUT) {
-            if (sg.nseg > 1) init = a.ws_start + (z * H + h) * SS;
+            if (sg.nseg > 1) init = a.ws_start + (wz * H + h) * SS;
             else init = init_state_of(a.st, sg.n, h, H);
         } else if (sg.j == 0) {
             init = init_state_of(a.st, sg.n, h, H);
@@ -435,7 +440,7 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
         if (!OUT && sg.j == 0) {
             // pass 3 starts the first segment from this copy, so that a final
             // state aliasing the initial one cannot race with it
-            float* dst = a.ws_start + (z * H + h) * SS;
+            float* dst = a.ws_start + (wz * H + h) * SS;
 #pragma unroll
             for (int t = 0; t < 8; ++t)
 #pragma unroll
@@ -1195,13 +1200,13 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
                 for (int i = 0; i < 4; ++i) dst[(16 * t + 4 * g4 + i) * kDim + col] = S[0][t][i];
         }
     } else if (sg.j == 0) {
-        float* dst = a.ws_start + ((z + 1) * H + h) * SS;
+        float* dst = a.ws_start + ((wz + 1) * H + h) * SS;
 #pragma unroll
         for (int t = 0; t < 8; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i) dst[(16 * t + 4 * g4 + i) * kDim + col] = S[NS - 1][t][i];
     } else {
-        float* dm = a.ws_maps + ((z * H + h) * 2) * SS;
+        float* dm = a.ws_maps + ((wz * H + h) * 2) * SS;
 #pragma unroll
         for (int gi = 0; gi < NS; ++gi)
 #pragma unroll
@@ -1226,13 +1231,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const ScanArgs a)
     if (unit >= a.n_seq * H) return;
     const int64_t n = unit / H;
     const int h = static_cast<int>(unit - n * H);
-    int64_t z0, nseg;
+    int64_t z0, nseg;  // z0: the sequence's first workspace slot
     if (!a.cu_seqlens) {
         nseg = a.nseg_dense;
         z0 = n * nseg;
     } else {
-        z0 = a.seg_first[n];
-        nseg = static_cast<int64_t>(a.seg_first[n + 1]) - z0;
+        nseg = static_cast<int64_t>(a.seg_first[n + 1]) - a.seg_first[n];
+        z0 = a.ws_first[n];
     }
     if (nseg < 3) return;
     const int tid = threadIdx.x;
@@ -1289,7 +1294,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const ScanArgs a)
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* cu, int64_t n_seq,
                                                     int64_t seg_max, int64_t seg_min, int64_t H,
                                                     int64_t n_cu, int32_t* seg_first,
-                                                    int32_t* seg_order)
+                                                    int32_t* ws_first, int32_t* seg_order)
 {
     constexpr int kCand = 6;
     __shared__ int64_t part[1024];
@@ -1379,6 +1384,30 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* cu, int64_t n
         seg_first[n_seq] = static_cast<int32_t>(part[1023]);
         seg_first[n_seq + 1] = static_cast<int32_t>(seg_len);
     }
+    __syncthreads();
+    const int64_t n_act = part[1023];
+    __syncthreads();
+    // workspace slots: only sequences of two or more segments use any
+    int64_t s2 = 0;
+    for (int64_t m = lo; m < hi; ++m) {
+        const int64_t c = count(m);
+        s2 += c > 1 ? c : 0;
+    }
+    part[tid] = s2;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int64_t x = tid >= off ? part[tid - off] : 0;
+        __syncthreads();
+        part[tid] += x;
+        __syncthreads();
+    }
+    int64_t run2 = part[tid] - s2;
+    for (int64_t m = lo; m < hi; ++m) {
+        const int64_t c = count(m);
+        ws_first[m] = static_cast<int32_t>(run2);
+        run2 += c > 1 ? c : 0;
+    }
+    if (tid == 1023) ws_first[n_seq] = static_cast<int32_t>(part[1023]);
 
     // Launch order: segments by decreasing chunk count (a counting sort; the
     // order within one count is whatever the atomics give, which changes no
@@ -1387,7 +1416,6 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* cu, int64_t n
     __shared__ int hist[NB], start[NB];
     for (int b = tid; b < NB; b += 1024) hist[b] = 0;
     __syncthreads();
-    const int64_t n_act = part[1023];
     auto bucket_of = [&](int64_t z) {
         int64_t lo2 = 0, hi2 = n_seq;  // seg_first[lo2] <= z < seg_first[hi2]
         while (hi2 - lo2 > 1) {
@@ -1405,10 +1433,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* cu, int64_t n
     for (int64_t z = tid; z < n_act; z += 1024) atomicAdd(&hist[bucket_of(z)], 1);
     __syncthreads();
     if (tid == 0) {
-        int run2 = 0;
+        int run3 = 0;
         for (int b = NB - 1; b >= 0; --b) {
-            start[b] = run2;
-            run2 += hist[b];
+            start[b] = run3;
+            run3 += hist[b];
         }
     }
     __syncthreads();
@@ -1525,16 +1553,21 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
     const bool plan_on_device = cu_seqlens && g_forced_segment <= 0;
     const int64_t seg_min =
         plan_on_device ? std::max<int64_t>(kMinSegment, (seg / 8 + CH - 1) / CH * CH) : seg;
-    int64_t n_segs = 0;
+    // Workspace slots: dense, one per segment; packed, only the segments of
+    // sequences cut in two or more, fewer than 2 * T_total / seg_min of them
+    // (such a sequence is longer than a segment, so its count is below
+    // twice its length over the segment length).
+    int64_t n_segs = 0, slots = 0;
     size_t ws_bytes = 0, plan_bytes = 0;
     if (longest_bound > seg_min) {
         n_segs = cu_seqlens ? n_seq + (T_total + seg_min - 1) / seg_min
                             : n_seq * ((T + seg - 1) / seg);
-        plan_bytes = cu_seqlens
-                         ? ((static_cast<size_t>(n_seq) + 2 + static_cast<size_t>(n_segs)) * 4 + 255) /
-                               256 * 256
-                         : 0;
-        ws_bytes = plan_bytes + static_cast<size_t>(n_segs) * H * 3 * SS * sizeof(float);
+        slots = cu_seqlens ? std::min<int64_t>(n_segs, 2 * ((T_total + seg_min - 1) / seg_min))
+                           : n_segs;
+        plan_bytes = cu_seqlens ? ((2 * static_cast<size_t>(n_seq) + 3 + static_cast<size_t>(n_segs)) *
+                                       4 + 255) / 256 * 256
+                                : 0;
+        ws_bytes = plan_bytes + static_cast<size_t>(slots) * H * 3 * SS * sizeof(float);
     }
     void* ws = nullptr;
     if (ws_bytes) {
@@ -1566,11 +1599,13 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
     a.nseg_dense = cu_seqlens ? 0 : (T + seg - 1) / seg;
     char* w = static_cast<char*>(ws);
     if (cu_seqlens) {
-        a.seg_first = reinterpret_cast<int32_t*>(w);
-        a.seg_order = a.seg_first + n_seq + 2;
+        a.seg_first = reinterpret_cast<int32_t*>(w);             // [n_seq + 2]
+        a.ws_first = a.seg_first + n_seq + 2;                     // [n_seq + 1]
+        a.seg_order = a.ws_first + n_seq + 1;                     // [n_segs]
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens, n_seq, seg,
                            seg_min, H, static_cast<int64_t>(cu_count(dev)),
-                           const_cast<int32_t*>(a.seg_first), const_cast<int32_t*>(a.seg_order));
+                           const_cast<int32_t*>(a.seg_first), const_cast<int32_t*>(a.ws_first),
+                           const_cast<int32_t*>(a.seg_order));
         e = hipGetLastError();
         report("segment plan launch", e);
         if (e != hipSuccess) {
@@ -1579,7 +1614,7 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
         }
     }
     a.ws_maps = reinterpret_cast<float*>(w + plan_bytes);
-    a.ws_start = a.ws_maps + static_cast<size_t>(n_segs) * H * 2 * SS;
+    a.ws_start = a.ws_maps + static_cast<size_t>(slots) * H * 2 * SS;
 
     const dim3 grid(static_cast<unsigned>(n_segs * H));
     hipLaunchKernelGGL(scan_kernel<false>, grid, block, 0, stream, a);
