@@ -25,7 +25,11 @@
 // [I | 0], or from the true initial state for the first segment), pass 2
 // composes the segment maps in order to get every segment's true entering
 // state, pass 3 reruns every segment from its entering state and writes the
-// outputs and the final state.  Short sequences take pass 3 only.
+// outputs and the final state.  Sequences no longer than a segment take pass
+// 3 only; those of at most 16 tokens are left to the token-by-token kernel.
+// For packed input a one-workgroup plan kernel, on the device where the
+// lengths are, picks the segment length, numbers the segments (and workspace
+// slots, for sequences cut in two or more) and orders them longest first.
 //
 // One workgroup (8 waves) processes one (sequence, head, segment); wave w
 // holds value columns 16w..16w+15 of the fp32 state in matrix-core
