@@ -103,14 +103,14 @@ __device__ __forceinline__ float xor_sum_rows(float x)
 // 16*(l >> 3) .. +15 of columns 32w + 4*(l & 7) .. +3, 64 values in registers.
 //
 // One token of the recurrence on a lane's share of the state: S' = Diag(a) S;
-// p = S'^T k and r = S'^T q summed over all 128 rows (the other row groups
-// through xor_sum_rows); u = beta (v - p); S <- S' + k u^T.  a, k and q point
-// at the lane's 16 rows of the token's gate, key and query staged in LDS
-// (16-byte aligned); they are read where used rather than held in registers,
-// which keeps the kernels at four waves per SIMD.  vt holds the lane's 4
-// columns of v.  With RAW, k and q are raw projections: each is scaled to a
-// unit vector (rounded to bf16 for bf16 inputs) as it is read.  Returns the
-// lane's 4 columns of the output o = S^T q = r + (k . q) u.
+// p = S'^T k summed over all 128 rows (the other row groups through
+// xor_sum_rows); u = beta (v - p); S <- S' + k u^T; then o = S^T q from the
+// updated state.  a, k and q point at the lane's 16 rows of the token's gate,
+// key and query staged in LDS (16-byte aligned); they are read where used
+// rather than held in registers, which keeps the kernels at four waves per
+// SIMD.  vt holds the lane's 4 columns of v.  With RAW, k and q are raw
+// projections: each is scaled to a unit vector (rounded to bf16 for bf16
+// inputs) as it is read.  Returns the lane's 4 columns of o.
 template <typename InT, bool RAW>
 __device__ __forceinline__ float4 token_update(float4 (&s)[16], const float* a, const float* k,
                                                const float* q, float bt, float4 vt)
@@ -131,41 +131,37 @@ __device__ __forceinline__ float4 token_update(float4 (&s)[16], const float* a, 
     auto key = [&](float x) { return RAW ? unit_round(x * ik, InT{}) : x; };
     auto query = [&](float x) { return RAW ? unit_round(x * iq, InT{}) : x; };
     float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
-    float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
-    float kq = 0.f;
 #pragma unroll
     for (int m4 = 0; m4 < 4; ++m4) {
         const float4 a4 = *reinterpret_cast<const float4*>(a + 4 * m4);
         const float4 k4 = *reinterpret_cast<const float4*>(k + 4 * m4);
-        const float4 q4 = *reinterpret_cast<const float4*>(q + 4 * m4);
         const float av[4] = {a4.x, a4.y, a4.z, a4.w};
         const float kv[4] = {key(k4.x), key(k4.y), key(k4.z), key(k4.w)};
-        const float qv[4] = {query(q4.x), query(q4.y), query(q4.z), query(q4.w)};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int m = 4 * m4 + i;
             s[m].x *= av[i]; s[m].y *= av[i]; s[m].z *= av[i]; s[m].w *= av[i];
             p0 += kv[i] * s[m].x; p1 += kv[i] * s[m].y; p2 += kv[i] * s[m].z; p3 += kv[i] * s[m].w;
-            r0 += qv[i] * s[m].x; r1 += qv[i] * s[m].y; r2 += qv[i] * s[m].z; r3 += qv[i] * s[m].w;
-            kq += kv[i] * qv[i];
         }
     }
     p0 = xor_sum_rows(p0); p1 = xor_sum_rows(p1); p2 = xor_sum_rows(p2); p3 = xor_sum_rows(p3);
-    r0 = xor_sum_rows(r0); r1 = xor_sum_rows(r1); r2 = xor_sum_rows(r2); r3 = xor_sum_rows(r3);
-    kq = xor_sum_rows(kq);
     const float u0 = bt * (vt.x - p0), u1 = bt * (vt.y - p1);
     const float u2 = bt * (vt.z - p2), u3 = bt * (vt.w - p3);
+    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
 #pragma unroll
     for (int m4 = 0; m4 < 4; ++m4) {
         const float4 k4 = *reinterpret_cast<const float4*>(k + 4 * m4);
+        const float4 q4 = *reinterpret_cast<const float4*>(q + 4 * m4);
         const float kv[4] = {key(k4.x), key(k4.y), key(k4.z), key(k4.w)};
+        const float qv[4] = {query(q4.x), query(q4.y), query(q4.z), query(q4.w)};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int m = 4 * m4 + i;
             s[m].x += kv[i] * u0; s[m].y += kv[i] * u1; s[m].z += kv[i] * u2; s[m].w += kv[i] * u3;
+            o0 += qv[i] * s[m].x; o1 += qv[i] * s[m].y; o2 += qv[i] * s[m].z; o3 += qv[i] * s[m].w;
         }
     }
-    return make_float4(r0 + kq * u0, r1 + kq * u1, r2 + kq * u2, r3 + kq * u3);
+    return make_float4(xor_sum_rows(o0), xor_sum_rows(o1), xor_sum_rows(o2), xor_sum_rows(o3));
 }
 
 }  // namespace kda

@@ -72,8 +72,10 @@ def test_verify_then_commit(dtype, K):
 
 def test_tokens_match_single_steps_full_size():
     """The batched decode shape (64 x 32 heads) with K = 4 and every token
-    committed, against four single-token decode steps (same per-token
-    arithmetic) and, for two heads, the oracle."""
+    committed, against four single-token decode steps and, for two heads, the
+    oracle.  The two kernels run the same fp32 recurrence but form the output
+    differently (read from the updated state here, as r + (k.q) u in the
+    decode step), so they agree to fp32 rounding, not bit for bit."""
     torch = _torch()
     dev = device()
     N, H, K = 64, 32, 4
@@ -90,7 +92,7 @@ def test_tokens_match_single_steps_full_size():
     o = o.cpu().numpy()
     o_steps = torch.stack(steps, dim=1).cpu().numpy()
     S, S_chain = state.cpu().numpy(), chain.cpu().numpy()
-    assert rel_err_vectors(o, o_steps) < 1e-6 and rel_err_states(S, S_chain) < 1e-6
+    assert rel_err_vectors(o, o_steps) < 1e-5 and rel_err_states(S, S_chain) < 1e-6
     sub = _inputs(32, N, K, H, "bf16")[0]
     heads = [0, 31]
     sub = ki.KDAInputs(*(getattr(sub, n)[:, :, heads] for n in ("q", "k", "v", "beta", "log_alpha")),
