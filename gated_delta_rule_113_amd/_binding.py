@@ -105,6 +105,12 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _on(device):
+    """The library allocates its workspace on, and counts the compute units
+    of, the calling thread's current device: make it the tensors' device."""
+    return _torch().cuda.device(device)
+
+
 def _stream(device):
     torch = _torch()
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
@@ -165,9 +171,10 @@ def kda_prefill(q, k, v, beta, log_alpha, initial_state=None, *, out=None, final
     if final_state is None:
         final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     _require(final_state, "final_state", torch.float32, (B, H, dk, dv), dev)
-    code = getattr(lib, _fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
-                             _ptr(initial_state), _ptr(o), _ptr(final_state),
-                             B, T, H, dk, dv, _in_dtype(q, k, v, beta), _stream(dev))
+    with _on(dev):
+        code = getattr(lib, _fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
+                                 _ptr(initial_state), _ptr(o), _ptr(final_state),
+                                 B, T, H, dk, dv, _in_dtype(q, k, v, beta), _stream(dev))
     _check(lib, _fn, code)
     return o, final_state
 
@@ -203,10 +210,11 @@ def kda_varlen_prefill(q, k, v, beta, log_alpha, cu_seqlens, initial_state=None,
     if final_state is None:
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     _require(final_state, "final_state", torch.float32, (N, H, dk, dv), dev)
-    code = getattr(lib, _fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
-                             _ptr(cu_seqlens), N, Tt, _ptr(initial_state), _ptr(o),
-                             _ptr(final_state), H, dk, dv, _in_dtype(q, k, v, beta),
-                             _stream(dev))
+    with _on(dev):
+        code = getattr(lib, _fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
+                                 _ptr(cu_seqlens), N, Tt, _ptr(initial_state), _ptr(o),
+                                 _ptr(final_state), H, dk, dv, _in_dtype(q, k, v, beta),
+                                 _stream(dev))
     _check(lib, _fn, code)
     return o, final_state
 
@@ -233,9 +241,10 @@ def kda_decode_step(q, k, v, beta, log_alpha, state, *, out=None, _fn="kda_decod
     _require(state, "state", torch.float32, (N, H, dk, dv), dev)
     o = out if out is not None else torch.empty((N, H, dv), dtype=torch.float32, device=dev)
     _require(o, "out", torch.float32, (N, H, dv), dev)
-    code = getattr(lib, _fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
-                             _ptr(state), _ptr(o), N, H, dk, dv, _in_dtype(q, k, v, beta),
-                             _stream(dev))
+    with _on(dev):
+        code = getattr(lib, _fn)(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
+                                 _ptr(state), _ptr(o), N, H, dk, dv, _in_dtype(q, k, v, beta),
+                                 _stream(dev))
     _check(lib, _fn, code)
     return o
 
@@ -268,9 +277,10 @@ def kda_decode_step_slots(q, k, v, beta, log_alpha, state_pool, slots, *, out=No
     _slots(slots, "slots", N, dev)
     o = out if out is not None else torch.zeros((N, H, dv), dtype=torch.float32, device=dev)
     _require(o, "out", torch.float32, (N, H, dv), dev)
-    code = lib.kda_decode_step_slots(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
-                                     _ptr(state_pool), _ptr(slots), state_pool.shape[0], _ptr(o),
-                                     N, H, dk, dv, _in_dtype(q, k, v, beta), _stream(dev))
+    with _on(dev):
+        code = lib.kda_decode_step_slots(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
+                                         _ptr(state_pool), _ptr(slots), state_pool.shape[0], _ptr(o),
+                                         N, H, dk, dv, _in_dtype(q, k, v, beta), _stream(dev))
     _check(lib, "kda_decode_step_slots", code)
     return o
 
@@ -309,11 +319,12 @@ def kda_varlen_prefill_slots(q, k, v, beta, log_alpha, cu_seqlens, state_pool, i
         _slots(final_slots, "final_slots", N, dev)
     o = out if out is not None else torch.empty((*lead, Tt, H, dv), dtype=torch.float32, device=dev)
     _require(o, "out", torch.float32, (*lead, Tt, H, dv), dev)
-    code = lib.kda_varlen_prefill_slots(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
-                                        _ptr(cu_seqlens), N, Tt, _ptr(state_pool),
-                                        _ptr(init_slots), _ptr(final_slots), state_pool.shape[0],
-                                        _ptr(o), H, dk, dv, _in_dtype(q, k, v, beta),
-                                        _stream(dev))
+    with _on(dev):
+        code = lib.kda_varlen_prefill_slots(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
+                                            _ptr(cu_seqlens), N, Tt, _ptr(state_pool),
+                                            _ptr(init_slots), _ptr(final_slots), state_pool.shape[0],
+                                            _ptr(o), H, dk, dv, _in_dtype(q, k, v, beta),
+                                            _stream(dev))
     _check(lib, "kda_varlen_prefill_slots", code)
     return o
 
@@ -339,9 +350,10 @@ def kda_decode_tokens(q, k, v, beta, log_alpha, state, n_commit=None, *, out=Non
         _slots(n_commit, "n_commit", N, dev)
     o = out if out is not None else torch.empty((N, K, H, dv), dtype=torch.float32, device=dev)
     _require(o, "out", torch.float32, (N, K, H, dv), dev)
-    code = lib.kda_decode_tokens(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
-                                 _ptr(state), _ptr(n_commit), _ptr(o), N, K, H, dk, dv,
-                                 _in_dtype(q, k, v, beta), _stream(dev))
+    with _on(dev):
+        code = lib.kda_decode_tokens(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
+                                     _ptr(state), _ptr(n_commit), _ptr(o), N, K, H, dk, dv,
+                                     _in_dtype(q, k, v, beta), _stream(dev))
     _check(lib, "kda_decode_tokens", code)
     return o
 

@@ -53,6 +53,9 @@
  *  - Every pointer must be 16-byte aligned (KDA_ERR_ALIGN).
  *  - Preconditions not checked (device data): log_alpha finite and <= 0;
  *    cu_seqlens[0] = 0, non-decreasing, cu_seqlens[N] = T_total.
+ *  - The calling thread's current device (hipSetDevice) must be the device
+ *    that holds the pointers and `stream`: the segmented prefill takes its
+ *    workspace from that device's pool and sizes its work by its CU count.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call is
  *    asynchronous on it: arguments are validated on the host first, and on any
  *    error nothing is enqueued.  No call synchronises.  A fault inside a
