@@ -16,6 +16,10 @@ ABI of ``include/kda.h``); this package is its thin Python binding:
     kda_varlen_prefill_slots(q, k, v, beta, log_alpha, cu_seqlens, state_pool,
                              init_slots=None, final_slots=None) -> o
         (states in a pool, addressed by int32 slots)
+    kda_backward(q, k, v, beta, log_alpha, d_o, initial_state=None,
+                 d_final_state=None) -> dict of gradients
+    kda_varlen_backward(q, k, v, beta, log_alpha, d_o, cu_seqlens, ...)
+        (gradients of a prefill in all its inputs, for training)
 
 PyTorch is used only for device memory and the current stream.
 """
@@ -24,6 +28,7 @@ from ._binding import (  # noqa: F401
     KDA_BF16,
     KDA_F32,
     KDAError,
+    kda_backward,
     kda_decode_step,
     kda_decode_step_raw,
     kda_decode_step_slots,
@@ -31,6 +36,7 @@ from ._binding import (  # noqa: F401
     kda_prefill,
     kda_prefill_raw,
     kda_set_prefill_segment,
+    kda_varlen_backward,
     kda_varlen_prefill,
     kda_varlen_prefill_raw,
     kda_varlen_prefill_slots,
@@ -40,4 +46,5 @@ from ._binding import (  # noqa: F401
 __all__ = ["kda_prefill", "kda_varlen_prefill", "kda_decode_step", "kda_prefill_raw",
            "kda_varlen_prefill_raw", "kda_decode_step_raw", "kda_decode_tokens",
            "kda_decode_step_slots",
-           "kda_varlen_prefill_slots", "kda_set_prefill_segment", "KDAError", "load_library"]
+           "kda_varlen_prefill_slots", "kda_backward", "kda_varlen_backward",
+           "kda_set_prefill_segment", "KDAError", "load_library"]

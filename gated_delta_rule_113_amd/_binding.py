@@ -22,8 +22,9 @@ STATUS_NAMES = {
 }
 EXPORTS = ("kda_prefill", "kda_varlen_prefill", "kda_decode_step", "kda_prefill_raw",
            "kda_varlen_prefill_raw", "kda_decode_step_raw", "kda_decode_tokens",
-           "kda_decode_step_slots", "kda_varlen_prefill_slots", "kda_set_prefill_segment",
-           "kda_status_str", "kda_abi_version")
+           "kda_decode_step_slots", "kda_varlen_prefill_slots", "kda_backward",
+           "kda_varlen_backward", "kda_set_prefill_segment", "kda_status_str",
+           "kda_abi_version")
 
 _lock = threading.Lock()
 _lib = None
@@ -80,6 +81,14 @@ def load_library(path: str | None = None):
         lib.kda_varlen_prefill_slots.argtypes = [vp, vp, vp, vp, f32p, vp, i64, i64, f32p, vp, vp,
                                                  i64, f32p, i64, i64, i64, ctypes.c_int, vp]
         lib.kda_varlen_prefill_slots.restype = ctypes.c_int
+        lib.kda_backward.argtypes = [vp, vp, vp, vp, f32p, f32p, f32p, f32p,
+                                     f32p, f32p, f32p, f32p, f32p, f32p,
+                                     i64, i64, i64, i64, i64, ctypes.c_int, vp]
+        lib.kda_backward.restype = ctypes.c_int
+        lib.kda_varlen_backward.argtypes = [vp, vp, vp, vp, f32p, vp, i64, i64, f32p, f32p, f32p,
+                                            f32p, f32p, f32p, f32p, f32p, f32p,
+                                            i64, i64, i64, ctypes.c_int, vp]
+        lib.kda_varlen_backward.restype = ctypes.c_int
         lib.kda_set_prefill_segment.argtypes = [i64]
         lib.kda_set_prefill_segment.restype = ctypes.c_int
         lib.kda_status_str.argtypes = [ctypes.c_int]
@@ -217,6 +226,80 @@ def kda_varlen_prefill(q, k, v, beta, log_alpha, cu_seqlens, initial_state=None,
                                  _stream(dev))
     _check(lib, _fn, code)
     return o, final_state
+
+
+def _backward(q, k, v, beta, log_alpha, d_o, cu_seqlens, initial_state, d_final_state):
+    """Shared marshalling of kda_backward / kda_varlen_backward."""
+    torch = _torch()
+    lib = load_library()
+    dev = q.device
+    rows = tuple(q.shape[:-2])
+    H, dk = q.shape[-2:]
+    dv = v.shape[-1]
+    _require(q, "q", device=dev)
+    _require(k, "k", q.dtype, (*rows, H, dk), dev)
+    _require(v, "v", q.dtype, (*rows, H, dv), dev)
+    _require(beta, "beta", q.dtype, (*rows, H), dev)
+    _require(log_alpha, "log_alpha", torch.float32, (*rows, H, dk), dev)
+    _require(d_o, "d_o", torch.float32, (*rows, H, dv), dev)
+    if cu_seqlens is None:
+        B, T = rows
+        units = B
+    else:
+        if rows[:-1] not in ((), (1,)):
+            raise ValueError("packed inputs must be [T_total, H, d] or [1, T_total, H, d]")
+        _require(cu_seqlens, "cu_seqlens", torch.int32, None, dev)
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+            raise ValueError("cu_seqlens must be a 1-D int32 tensor of N + 1 offsets")
+        units = cu_seqlens.numel() - 1
+        Tt = rows[-1]
+    sshape = (units, H, dk, dv)
+    if initial_state is not None:
+        _require(initial_state, "initial_state", torch.float32, sshape, dev)
+    if d_final_state is not None:
+        _require(d_final_state, "d_final_state", torch.float32, sshape, dev)
+    g = {name: torch.empty(like.shape, dtype=torch.float32, device=dev)
+         for name, like in (("dq", q), ("dk", k), ("dv", v), ("dbeta", beta),
+                            ("dlog_alpha", log_alpha))}
+    g["dinitial_state"] = torch.empty(sshape, dtype=torch.float32, device=dev)
+    with _on(dev):
+        if cu_seqlens is None:
+            fn = "kda_backward"
+            code = lib.kda_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
+                                    _ptr(initial_state), _ptr(d_o), _ptr(d_final_state),
+                                    _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dbeta"]),
+                                    _ptr(g["dlog_alpha"]), _ptr(g["dinitial_state"]),
+                                    B, T, H, dk, dv, _in_dtype(q, k, v, beta), _stream(dev))
+        else:
+            fn = "kda_varlen_backward"
+            code = lib.kda_varlen_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
+                                           _ptr(cu_seqlens), units, Tt, _ptr(initial_state),
+                                           _ptr(d_o), _ptr(d_final_state), _ptr(g["dq"]),
+                                           _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dbeta"]),
+                                           _ptr(g["dlog_alpha"]), _ptr(g["dinitial_state"]),
+                                           H, dk, dv, _in_dtype(q, k, v, beta), _stream(dev))
+    _check(lib, fn, code)
+    return g
+
+
+def kda_backward(q, k, v, beta, log_alpha, d_o, initial_state=None, d_final_state=None):
+    """Gradients of a dense prefill.  Inputs as kda_prefill, plus d_o (fp32,
+    shaped like o) and d_final_state ([B, H, 128, 128] fp32 or None = zeros).
+
+    Returns a dict of fp32 tensors: dq, dk, dv, dbeta, dlog_alpha (each shaped
+    like its input) and dinitial_state [B, H, 128, 128].
+    """
+    if q.dim() != 4:
+        raise ValueError("dense inputs must be [B, T, H, d]")
+    return _backward(q, k, v, beta, log_alpha, d_o, None, initial_state, d_final_state)
+
+
+def kda_varlen_backward(q, k, v, beta, log_alpha, d_o, cu_seqlens, initial_state=None,
+                        d_final_state=None):
+    """Gradients of a packed prefill (inputs as kda_varlen_prefill, plus d_o
+    and d_final_state [N, H, 128, 128] or None).  Returns the dict of
+    kda_backward, dinitial_state [N, H, 128, 128]."""
+    return _backward(q, k, v, beta, log_alpha, d_o, cu_seqlens, initial_state, d_final_state)
 
 
 def kda_set_prefill_segment(tokens: int) -> None:

@@ -162,6 +162,38 @@ kda_status decode_impl(const void* q, const void* k, const void* v, const void* 
                                             static_cast<hipStream_t>(stream)));
 }
 
+kda_status backward_impl(const void* q, const void* k, const void* v, const void* beta,
+                         const float* log_alpha, const int32_t* cu_seqlens, int64_t n_seq,
+                         int64_t T, int64_t T_total, const float* initial_state, const float* d_o,
+                         const float* d_final_state, float* dq, float* dk, float* dv, float* dbeta,
+                         float* dlog_alpha, float* d_initial_state, int64_t H, int64_t d_k,
+                         int64_t d_v, kda_dtype in_dtype, void* stream)
+{
+    kda_status st;
+    if ((st = check_dtype(in_dtype)) != KDA_OK) return st;
+    if ((st = check_dims(H, d_k, d_v)) != KDA_OK) return st;
+    if (n_seq < 0 || T < 0 || T_total < 0) return KDA_ERR_SHAPE;
+    if (cu_seqlens && T_total > INT32_MAX) return KDA_ERR_SHAPE;
+    if (!cu_seqlens && n_seq > 0 && T > kMaxElems / n_seq) return KDA_ERR_SHAPE;
+    const int64_t rows = cu_seqlens ? T_total : n_seq * T;
+    if ((st = check_rows(rows, H)) != KDA_OK) return st;
+    if (n_seq > int64_t(1) << 24 || n_seq * H > int64_t(1) << 30) return KDA_ERR_SHAPE;
+    if (n_seq == 0) return KDA_OK;
+    if (cu_seqlens && misaligned(cu_seqlens)) return KDA_ERR_ALIGN;
+    if (rows > 0) {
+        if ((st = check_ptrs({q, k, v, beta, log_alpha, d_o, dq, dk, dv, dbeta, dlog_alpha},
+                             {initial_state, d_final_state, d_initial_state})) != KDA_OK)
+            return st;
+    } else if ((st = check_ptrs({}, {initial_state, d_final_state, d_initial_state})) != KDA_OK) {
+        return st;
+    }
+    if (rows == 0 && !d_initial_state) return KDA_OK;
+    return from_hip(kda::launch_backward(q, k, v, beta, log_alpha, d_o, cu_seqlens, n_seq, T,
+                                         T_total, H, initial_state, d_final_state, dq, dk, dv,
+                                         dbeta, dlog_alpha, d_initial_state, in_dtype == KDA_BF16,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -282,6 +314,30 @@ kda_status kda_decode_tokens(const void* q, const void* k, const void* v, const 
     return from_hip(kda::launch_decode_tokens(q, k, v, beta, log_alpha, state, n_commit, o, N, K, H,
                                               in_dtype == KDA_BF16,
                                               static_cast<hipStream_t>(stream)));
+}
+
+kda_status kda_backward(const void* q, const void* k, const void* v, const void* beta,
+                        const float* log_alpha, const float* initial_state, const float* d_o,
+                        const float* d_final_state, float* dq, float* dk, float* dv, float* dbeta,
+                        float* dlog_alpha, float* d_initial_state, int64_t B, int64_t T, int64_t H,
+                        int64_t d_k, int64_t d_v, kda_dtype in_dtype, void* stream)
+{
+    return backward_impl(q, k, v, beta, log_alpha, nullptr, B, T, 0, initial_state, d_o,
+                         d_final_state, dq, dk, dv, dbeta, dlog_alpha, d_initial_state, H, d_k,
+                         d_v, in_dtype, stream);
+}
+
+kda_status kda_varlen_backward(const void* q, const void* k, const void* v, const void* beta,
+                               const float* log_alpha, const int32_t* cu_seqlens, int64_t N,
+                               int64_t T_total, const float* initial_state, const float* d_o,
+                               const float* d_final_state, float* dq, float* dk, float* dv,
+                               float* dbeta, float* dlog_alpha, float* d_initial_state, int64_t H,
+                               int64_t d_k, int64_t d_v, kda_dtype in_dtype, void* stream)
+{
+    if (N > 0 && !cu_seqlens) return KDA_ERR_NULL;
+    return backward_impl(q, k, v, beta, log_alpha, cu_seqlens, N, 0, T_total, initial_state, d_o,
+                         d_final_state, dq, dk, dv, dbeta, dlog_alpha, d_initial_state, H, d_k,
+                         d_v, in_dtype, stream);
 }
 
 kda_status kda_set_prefill_segment(int64_t tokens)

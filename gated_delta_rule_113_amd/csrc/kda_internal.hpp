@@ -69,6 +69,31 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
                                int64_t T, int64_t T_total, int64_t H, const StateRefs& st,
                                float* o, bool raw, int64_t short_max, hipStream_t stream);
 
+// Backward pass (gradients in q, k, v, beta, log_alpha and the initial state
+// from those in o and the final state), token by token; dense or packed as the
+// prefill.  Gradients are fp32 in the layouts of their inputs.  The forward
+// sweep stores a checkpoint state every kBackwardBlock tokens (more if the
+// workspace would exceed kBackwardWorkspaceCap, up to kMaxBackwardBlock) in a
+// workspace taken in stream order from the device's pool; the reverse sweep
+// recomputes each block from its checkpoint.
+constexpr int kBackwardBlock = 8;
+constexpr int kMaxBackwardBlock = 16;
+constexpr int64_t kBackwardWorkspaceCap = int64_t(16) << 30;
+hipError_t launch_backward(const void* q, const void* k, const void* v, const void* beta,
+                           const float* log_alpha, const float* d_o, const int32_t* cu_seqlens,
+                           int64_t n_seq, int64_t T, int64_t T_total, int64_t H,
+                           const float* initial_state, const float* d_final_state, float* dq,
+                           float* dk, float* dv, float* dbeta, float* dlog_alpha,
+                           float* d_initial_state, bool bf16, hipStream_t stream);
+
+// A memory pool per device that keeps freed blocks cached, so per-call
+// workspace allocations on the stream are cheap after the first (NULL if the
+// pool cannot be created).
+hipMemPool_t workspace_pool(int dev);
+
+// With KDA_DEBUG set in the environment, failed HIP calls are printed to stderr.
+void report(const char* what, hipError_t e);
+
 // Tokens per segment for the chunked prefill (a positive multiple of 64), or
 // 0 to choose it from the problem size and the number of CUs.
 void set_prefill_segment(int64_t tokens);

@@ -1458,7 +1458,8 @@ std::mutex g_pool_mutex;
 hipMemPool_t g_pools[64] = {};
 int g_cu_count[64] = {};
 
-// With KDA_DEBUG set in the environment, failed HIP calls are printed to stderr.
+}  // namespace
+
 void report(const char* what, hipError_t e)
 {
     static const bool on = std::getenv("KDA_DEBUG") != nullptr;
@@ -1478,8 +1479,6 @@ int cu_count(int dev)
     return g_cu_count[dev];
 }
 
-// A memory pool per device that keeps freed blocks cached, so per-call
-// workspace allocations on the stream are cheap after the first.
 hipMemPool_t workspace_pool(int dev)
 {
     std::lock_guard<std::mutex> lk(g_pool_mutex);
@@ -1506,8 +1505,6 @@ hipMemPool_t workspace_pool(int dev)
     }
     return g_pools[dev];
 }
-
-}  // namespace
 
 void set_prefill_segment(int64_t tokens) { g_forced_segment = tokens; }
 

@@ -245,6 +245,49 @@ kda_status kda_varlen_prefill_slots(const void *q, const void *k, const void *v,
                                     void *stream);
 
 /*
+ * Backward pass: the gradients of a loss in the inputs of a prefill, given its
+ * gradients in the outputs, for training a KDA layer.  The pages describe the
+ * model's training (quantization-aware from fine-tuning onward: "Kimi K3 --
+ * the architecture and infrastructure, explained", section "Training
+ * infrastructure: quantization-aware from SFT onward"); the gradients are the
+ * chain rule taken through the recurrence above, token by token in reverse.
+ * Inputs are those of the prefill call they differentiate:
+ *   q, k, v, beta, log_alpha, initial_state : as kda_prefill (dense, [B, T, H, *])
+ *                 or kda_varlen_prefill (packed, [T_total, H, *] with
+ *                 cu_seqlens in DEVICE memory); initial_state NULL = zeros
+ *   d_o           : fp32, the layout of o: the loss gradient in every output
+ *   d_final_state : [B or N, H, d_k, d_v] fp32, the loss gradient in the final
+ *                 state, or NULL for zeros
+ * Outputs, fp32, all written:
+ *   dq, dk, dlog_alpha : the layout of q;  dv : the layout of v;  dbeta : the
+ *                 layout of beta
+ *   d_initial_state : [B or N, H, d_k, d_v], or NULL to skip; it MAY be the same
+ *                 pointer as d_final_state
+ * q, k, v, beta are in_dtype (bf16 inputs widened exactly); arithmetic is fp32.
+ * The call recomputes the forward states: it runs the recurrence once storing
+ * a state every 8 tokens (16 if that would take over 16 GiB) in a workspace
+ * taken in stream order from the device's pool, then sweeps back recomputing
+ * each block from its stored state.  If that allocation fails the call
+ * returns KDA_ERR_HIP and enqueues nothing.  B or N = 0 is a no-op; with no
+ * tokens, d_initial_state = d_final_state (or zeros).
+ */
+kda_status kda_backward(const void *q, const void *k, const void *v, const void *beta,
+                        const float *log_alpha, const float *initial_state,
+                        const float *d_o, const float *d_final_state,
+                        float *dq, float *dk, float *dv, float *dbeta, float *dlog_alpha,
+                        float *d_initial_state,
+                        int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v,
+                        kda_dtype in_dtype, void *stream);
+kda_status kda_varlen_backward(const void *q, const void *k, const void *v, const void *beta,
+                               const float *log_alpha, const int32_t *cu_seqlens,
+                               int64_t N, int64_t T_total, const float *initial_state,
+                               const float *d_o, const float *d_final_state,
+                               float *dq, float *dk, float *dv, float *dbeta,
+                               float *dlog_alpha, float *d_initial_state,
+                               int64_t H, int64_t d_k, int64_t d_v,
+                               kda_dtype in_dtype, void *stream);
+
+/*
  * Tuning and testing knob for the bf16 prefill (process-wide; set it while no
  * prefill call is running).  The blockwise prefill runs one workgroup per
  * (sequence, head, segment); a sequence longer than `tokens` is cut into

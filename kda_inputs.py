@@ -6,7 +6,8 @@ contains none of the attention arithmetic itself.
 
 Recipe (all draws from numpy PCG64 streams seeded by
 ``SeedSequence([113, workload_id, tensor_id, ...])``; tensor ids: q=0, k=1,
-v=2, beta=3, log_alpha=4, initial state=5, special channels=6, lengths=7):
+v=2, beta=3, log_alpha=4, initial state=5, special channels=6, lengths=7,
+raw projections=8, loss gradients=9):
 
 * q, k ~ N(0, 1), then L2-normalised per (token, head) in float64;
 * v ~ N(0, 1);
@@ -16,7 +17,9 @@ v=2, beta=3, log_alpha=4, initial state=5, special channels=6, lengths=7):
   the 128 channels as long-memory channels with log_alpha = -1e-4 * U[0, 1)
   and a disjoint set of 13 fast-forgetting channels with
   log_alpha = -5 - softplus(N(0, 1));
-* initial states ~ N(0, 0.02^2) in float32.
+* initial states ~ N(0, 0.02^2) in float32;
+* for the backward pass, the loss gradients in the outputs and in the final
+  states ~ N(0, 1) in float32 (``loss_gradients``).
 
 Storage: ``dtype="f32"`` keeps every tensor float32; ``dtype="bf16"`` rounds
 q, k, v and beta to bfloat16 (round-to-nearest-even from float32) and keeps
@@ -33,7 +36,7 @@ import os
 import numpy as np
 
 ROOT_SEED = 113
-Q, K, V, BETA, LOG_ALPHA, STATE, SPECIAL, LENGTHS, RAW = range(9)
+Q, K, V, BETA, LOG_ALPHA, STATE, SPECIAL, LENGTHS, RAW, GRAD = range(10)
 N_SPECIAL = 13  # round(0.10 * 128)
 
 
@@ -113,6 +116,14 @@ def draw_head(workload: int, head: int, n_tokens: int, dk: int = 128, dv: int = 
 
 def draw_state(workload: int, shape, key=()) -> np.ndarray:
     return (0.02 * _rng(workload, STATE, *tuple(key)).standard_normal(shape)).astype(np.float32)
+
+
+def loss_gradients(workload: int, o_shape, n_states: int, H: int, dk: int = 128, dv: int = 128):
+    """Seeded gradients of a loss in the outputs (``o_shape``, e.g. [B, T, H,
+    dv]) and in the final states ([n_states, H, dk, dv]), N(0, 1) float32."""
+    d_o = _rng(workload, GRAD, 0).standard_normal(tuple(o_shape)).astype(np.float32)
+    d_s = _rng(workload, GRAD, 1).standard_normal((n_states, H, dk, dv)).astype(np.float32)
+    return d_o, d_s
 
 
 # ----------------------------------------------------------------------------
@@ -335,3 +346,14 @@ def workload_million(T: int = 1 << 20, H: int = 32, heads=None) -> KDAInputs:
 def workload_varlen(n_seqs: int = 16, H: int = 32, lo: int = 1024, hi: int = 65536) -> KDAInputs:
     """16 packed sequences, lengths log-uniform in [1024, 65536], half resumed."""
     return varlen_prefill(4, varlen_lengths(4, n_seqs, lo, hi), H)
+
+
+BACKWARD_WORKLOAD = 5
+BACKWARD_SHAPE = (8, 4096, 32)  # B, T, H
+
+
+def workload_backward(B: int = 8, T: int = 4096, H: int = 32, heads=None) -> KDAInputs:
+    """Training shape for the backward pass: B=8 sequences of T=4096 tokens,
+    H=32, bf16 q/k/v/beta, gated channel mix, zero initial state; its loss
+    gradients come from ``loss_gradients(BACKWARD_WORKLOAD, ...)``."""
+    return dense_prefill(BACKWARD_WORKLOAD, B, T, H, gated=True, heads=heads)

@@ -163,44 +163,35 @@ def prefill(q, k, v, beta, log_alpha, initial_state=None, n_threads: int = 0, li
     return o.reshape(B, T, H, dv), s
 
 
-def backward(q, k, v, beta, log_alpha, d_o, initial_state=None, d_final_state=None,
-             n_threads: int = 0, lib=None):
-    """Gradients of L = sum <d_o, o> + <d_final_state, final_state> for a dense
-    batch (shapes as in ``prefill``; d_o like o, d_final_state like the final
-    state), by the chain rule through the token recurrence in reverse
-    (``kda_oracle_backward``).  Returns a dict of float64 arrays: dq, dk, dv,
-    dbeta, dlog_alpha (shaped like their inputs) and dinitial_state
-    [B, H, dk, dv].  Test infrastructure for a backward pass: no kernel of
-    the library computes these yet."""
+def _backward_rows(q, k, v, beta, log_alpha, d_o, row0, length, initial_state, d_final_state,
+                   n_threads, lib):
+    """kda_oracle_backward on rows [rows, H, *]; sequence n owns rows
+    row0[n] .. row0[n]+length[n]-1.  Rows outside every sequence get zeros."""
     lib = lib or load()
-    q = np.asarray(q)
-    B, T, H, dk = q.shape
+    rows, H, dk = np.asarray(q).shape
     dv = np.asarray(v).shape[-1]
-    rows = B * T
-    qf = _f32(np.reshape(q, (rows, H, dk)), "q")
-    kf = _f32(np.reshape(k, (rows, H, dk)), "k")
-    vf = _f32(np.reshape(v, (rows, H, dv)), "v")
-    bf = _f32(np.reshape(beta, (rows, H)), "beta")
-    lf = _f32(np.reshape(log_alpha, (rows, H, dk)), "log_alpha")
-    do = np.ascontiguousarray(np.reshape(d_o, (rows, H, dv)), dtype=np.float64)
-    row0 = np.arange(B, dtype=np.int64) * T
-    length = np.full(B, T, dtype=np.int64)
+    n_seq = len(row0)
+    qf = _f32(q, "q"); kf = _f32(k, "k"); vf = _f32(v, "v")
+    bf = _f32(beta, "beta"); lf = _f32(log_alpha, "log_alpha")
+    do = np.ascontiguousarray(d_o, dtype=np.float64)
+    row0 = np.ascontiguousarray(row0, dtype=np.int64)
+    length = np.ascontiguousarray(length, dtype=np.int64)
     s0p = dsp = None
     if initial_state is not None:
         s0 = np.ascontiguousarray(initial_state, dtype=np.float64)
-        if s0.shape != (B, H, dk, dv):
-            raise ValueError(f"initial_state must be {(B, H, dk, dv)}")
+        if s0.shape != (n_seq, H, dk, dv):
+            raise ValueError(f"initial_state must be {(n_seq, H, dk, dv)}")
         s0p = _ptr(s0, ctypes.c_double)
     if d_final_state is not None:
         ds = np.ascontiguousarray(d_final_state, dtype=np.float64)
-        if ds.shape != (B, H, dk, dv):
-            raise ValueError(f"d_final_state must be {(B, H, dk, dv)}")
+        if ds.shape != (n_seq, H, dk, dv):
+            raise ValueError(f"d_final_state must be {(n_seq, H, dk, dv)}")
         dsp = _ptr(ds, ctypes.c_double)
     out = {"dq": np.zeros((rows, H, dk)), "dk": np.zeros((rows, H, dk)),
            "dv": np.zeros((rows, H, dv)), "dbeta": np.zeros((rows, H)),
-           "dlog_alpha": np.zeros((rows, H, dk)), "dinitial_state": np.zeros((B, H, dk, dv))}
-    rc = lib.kda_oracle_backward(B, _ptr(row0, ctypes.c_int64), _ptr(length, ctypes.c_int64), 1,
-                                 H, dk, dv, _ptr(qf, ctypes.c_float), _ptr(kf, ctypes.c_float),
+           "dlog_alpha": np.zeros((rows, H, dk)), "dinitial_state": np.zeros((n_seq, H, dk, dv))}
+    rc = lib.kda_oracle_backward(n_seq, _ptr(row0, ctypes.c_int64), _ptr(length, ctypes.c_int64),
+                                 1, H, dk, dv, _ptr(qf, ctypes.c_float), _ptr(kf, ctypes.c_float),
                                  _ptr(vf, ctypes.c_float), _ptr(bf, ctypes.c_float),
                                  _ptr(lf, ctypes.c_float), s0p, _ptr(do, ctypes.c_double), dsp,
                                  *(_ptr(out[n], ctypes.c_double) for n in
@@ -208,9 +199,45 @@ def backward(q, k, v, beta, log_alpha, d_o, initial_state=None, d_final_state=No
                                  int(n_threads))
     if rc != 0:
         raise RuntimeError(f"kda_oracle_backward failed with code {rc}")
+    return out
+
+
+def backward(q, k, v, beta, log_alpha, d_o, initial_state=None, d_final_state=None,
+             n_threads: int = 0, lib=None):
+    """Gradients of L = sum <d_o, o> + <d_final_state, final_state> for a dense
+    batch (shapes as in ``prefill``; d_o like o, d_final_state like the final
+    state), by the chain rule through the token recurrence in reverse
+    (``kda_oracle_backward``).  Returns a dict of float64 arrays: dq, dk, dv,
+    dbeta, dlog_alpha (shaped like their inputs) and dinitial_state
+    [B, H, dk, dv].  The reference for the library's backward pass."""
+    q = np.asarray(q)
+    B, T, H, dk = q.shape
+    dv = np.asarray(v).shape[-1]
+    rows = B * T
+    out = _backward_rows(np.reshape(q, (rows, H, dk)), np.reshape(k, (rows, H, dk)),
+                         np.reshape(v, (rows, H, dv)), np.reshape(beta, (rows, H)),
+                         np.reshape(log_alpha, (rows, H, dk)), np.reshape(d_o, (rows, H, dv)),
+                         np.arange(B, dtype=np.int64) * T, np.full(B, T, dtype=np.int64),
+                         initial_state, d_final_state, n_threads, lib)
     shapes = {"dq": (B, T, H, dk), "dk": (B, T, H, dk), "dv": (B, T, H, dv), "dbeta": (B, T, H),
               "dlog_alpha": (B, T, H, dk)}
     return {n: (x.reshape(shapes[n]) if n in shapes else x) for n, x in out.items()}
+
+
+def varlen_backward(q, k, v, beta, log_alpha, d_o, cu_seqlens, initial_state=None,
+                    d_final_state=None, n_threads: int = 0, lib=None):
+    """``backward`` for a packed batch (layouts as ``varlen_prefill``; d_o
+    [T_total, H, dv]; initial_state and d_final_state [N, H, dk, dv]).
+    Returns the dict of ``backward``, token gradients [T_total, H, *]."""
+    q = np.asarray(q)
+    if q.ndim == 4:
+        q, k, v, beta, log_alpha, d_o = (np.asarray(x)[0] for x in (q, k, v, beta, log_alpha, d_o))
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    if cu.ndim != 1 or cu.shape[0] < 1 or cu[0] != 0 or np.any(np.diff(cu) < 0) \
+            or cu[-1] != q.shape[0]:
+        raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at T_total")
+    return _backward_rows(q, k, v, beta, log_alpha, d_o, cu[:-1], np.diff(cu), initial_state,
+                          d_final_state, n_threads, lib)
 
 
 def varlen_prefill(q, k, v, beta, log_alpha, cu_seqlens, initial_state=None,

@@ -494,10 +494,34 @@ def pin_backward_identity_gate(lib=None):
         assert abs(g["dbeta"][0, t, 0] - (vv[t] - S0.T @ kk[t]) @ (Gt.T @ kk[t])) < 1e-12
         assert _rel(g["dlog_alpha"][0, t, 0], np.sum(Gt * S0, axis=1)) < 1e-12
 
+def pin_backward_packing(lib=None):
+    """Sequences are independent: the packed backward equals the dense
+    backward of each sequence alone (rows of other sequences untouched), and
+    an empty sequence passes its final-state gradient through unchanged."""
+    lengths = [3, 0, 5, 1]
+    H, dk, dv = 2, 4, 3
+    r = _rng(65)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    Tt = int(cu[-1])
+    q, k, v, b, la, _ = _random_case(66, B=1, T=Tt, H=H, dk=dk, dv=dv)
+    s0 = r.standard_normal((len(lengths), H, dk, dv)).astype(np.float32)
+    d_o = r.standard_normal((Tt, H, dv))
+    d_s = r.standard_normal((len(lengths), H, dk, dv))
+    g = oracle.varlen_backward(q[0], k[0], v[0], b[0], la[0], d_o, cu, s0, d_s, lib=lib)
+    for n, L in enumerate(lengths):
+        a, z = cu[n], cu[n + 1]
+        one = oracle.backward(q[:, a:z], k[:, a:z], v[:, a:z], b[:, a:z], la[:, a:z],
+                              d_o[None, a:z], s0[n:n + 1], d_s[n:n + 1], lib=lib)
+        for name in ("dq", "dk", "dv", "dbeta", "dlog_alpha"):
+            assert np.array_equal(g[name][a:z], one[name][0]), (n, name)
+        assert np.array_equal(g["dinitial_state"][n], one["dinitial_state"][0]), n
+    assert np.array_equal(g["dinitial_state"][1], d_s[1])
+
+
 ALL_PINS = [
     pin_bruteforce_numpy, pin_bruteforce_exact, pin_identity, pin_erase_then_write,
     pin_decay_closed_form, pin_channel_locality, pin_page_delta_rule,
     pin_causal_linear_attention, pin_scalar_gate, pin_resume, pin_linearity,
     pin_varlen_and_layouts, pin_prepare_gates, pin_prepare_unit_vectors,
-    pin_backward_finite_differences, pin_backward_identity_gate,
+    pin_backward_finite_differences, pin_backward_identity_gate, pin_backward_packing,
 ]

@@ -40,6 +40,7 @@ def test_exports_match_header(lib):
     assert declared == {"kda_prefill", "kda_varlen_prefill", "kda_decode_step",
                         "kda_prefill_raw", "kda_varlen_prefill_raw", "kda_decode_step_raw",
                         "kda_decode_tokens", "kda_decode_step_slots", "kda_varlen_prefill_slots",
+                        "kda_backward", "kda_varlen_backward",
                         "kda_set_prefill_segment", "kda_status_str", "kda_abi_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", kda._binding.LIBRARY],
                          capture_output=True, text=True, check=True).stdout
@@ -189,6 +190,48 @@ def test_varlen_slots_validation(lib):
     assert varlen_slots(lib, N=0, cu=None, pool=None) == OK
     # nothing to read and nothing to write
     assert varlen_slots(lib, Tt=0, pool=None, si=None, sf=None, q=None, o=None) == OK
+
+
+def backward(lib, q=P, k=P, v=P, beta=P, la=P, s0=None, do=P, dsT=None, dq=P, dk_=P, dv_=P, db=P,
+             dla=P, ds0=P, B=1, T=4, H=2, dk=128, dv=128, dt=1):
+    return lib.kda_backward(q, k, v, beta, la, s0, do, dsT, dq, dk_, dv_, db, dla, ds0,
+                            B, T, H, dk, dv, dt, None)
+
+
+def varlen_backward(lib, q=P, k=P, v=P, beta=P, la=P, cu=P, N=2, Tt=8, s0=None, do=P, dsT=None,
+                    dq=P, dk_=P, dv_=P, db=P, dla=P, ds0=P, H=2, dk=128, dv=128, dt=1):
+    return lib.kda_varlen_backward(q, k, v, beta, la, cu, N, Tt, s0, do, dsT, dq, dk_, dv_, db,
+                                   dla, ds0, H, dk, dv, dt, None)
+
+
+def test_backward_validation(lib):
+    for name in ("q", "k", "v", "beta", "la", "do", "dq", "dk_", "dv_", "db", "dla"):
+        assert backward(lib, **{name: None}) == NULL, name
+        assert backward(lib, **{name: MIS}) == ALIGN, name
+        assert varlen_backward(lib, **{name: None}) == NULL, name
+    for name in ("s0", "dsT", "ds0"):
+        assert backward(lib, **{name: MIS}) == ALIGN, name
+        assert varlen_backward(lib, **{name: MIS}) == ALIGN, name
+    assert backward(lib, B=-1) == SHAPE
+    assert backward(lib, T=-1) == SHAPE
+    assert backward(lib, T=1 << 40) == SHAPE
+    assert backward(lib, H=0) == SHAPE
+    assert backward(lib, H=65537) == SHAPE
+    assert backward(lib, dk=64) == UNSUP
+    assert backward(lib, dt=2) == DTYPE
+    assert varlen_backward(lib, cu=None) == NULL
+    assert varlen_backward(lib, cu=P + 4) == ALIGN
+    assert varlen_backward(lib, Tt=1 << 31) == SHAPE
+    assert varlen_backward(lib, N=-1) == SHAPE
+    assert varlen_backward(lib, dv=32) == UNSUP
+    # no sequences: nothing to do and no pointers needed
+    assert backward(lib, B=0, q=None, do=None, dq=None, ds0=None) == OK
+    assert varlen_backward(lib, N=0, cu=None, q=None, do=None, dq=None, ds0=None) == OK
+    # no tokens and no initial-state gradient requested: nothing to write
+    none = dict(q=None, k=None, v=None, beta=None, la=None, do=None, dq=None, dk_=None,
+                dv_=None, db=None, dla=None, ds0=None)
+    assert backward(lib, T=0, **none) == OK
+    assert varlen_backward(lib, Tt=0, **none) == OK
 
 
 def test_binding_rejects_cpu_tensors(lib):

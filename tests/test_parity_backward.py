@@ -1,0 +1,149 @@
+"""Backward pass on the GPU (kda_backward, kda_varlen_backward) vs the fp64
+oracle's backward, which is pinned against finite differences of the forward
+oracle.
+
+Every gradient is compared with the error measure of the forward outputs: per
+vector (one token and head: dq, dk, dv, d log alpha; one sequence and head
+over its tokens: d beta) and per matrix (d initial state), max over all, at
+most 2e-3.  The kernel computes in fp32 throughout; the measured errors are
+far below that.
+"""
+import numpy as np
+import pytest
+
+import gated_delta_rule_113_amd as kda
+import kda_inputs as ki
+import oracle
+from kda_gpu import TOL, device, rel_err_states, rel_err_vectors, to_dev, upload
+
+pytestmark = pytest.mark.gpu
+
+TOKEN_GRADS = ("dq", "dk", "dv", "dlog_alpha")
+
+
+def _compare(name, got, ref, tol=TOL):
+    errs = {n: rel_err_vectors(got[n], ref[n]) for n in TOKEN_GRADS}
+    # d beta: one value per (token, head); compared per head over the tokens
+    errs["dbeta"] = rel_err_vectors(np.swapaxes(got["dbeta"], -1, -2),
+                                    np.swapaxes(ref["dbeta"], -1, -2))
+    errs["dinitial_state"] = rel_err_states(got["dinitial_state"], ref["dinitial_state"])
+    print(f"{name}: " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()) + f" (tol {tol:g})",
+          flush=True)
+    for n, e in errs.items():
+        assert e <= tol, f"{name}: {n} error {e:.3e} > {tol}"
+
+
+def _host(g):
+    return {n: x.cpu().numpy() for n, x in g.items()}
+
+
+def _dense(inp, d_o, d_s, dev):
+    torch = __import__("torch")
+    t = upload(inp, dev)
+    g = kda.kda_backward(t["q"], t["k"], t["v"], t["beta"], t["log_alpha"], to_dev(d_o, "f32", dev),
+                         t["initial_state"], None if d_s is None else to_dev(d_s, "f32", dev))
+    torch.cuda.synchronize()
+    return _host(g)
+
+
+def test_backward_dense_bf16():
+    """Two sequences of 150 tokens (18 blocks of 8 and a ragged 6), three
+    heads, the gated channel mix, resumed states, both loss gradients."""
+    B, T, H = 2, 150, 3
+    inp = ki.dense_prefill(40, B=B, T=T, H=H, gated=True, initial_state=True)
+    d_o, d_s = ki.loss_gradients(40, (B, T, H, 128), B, H)
+    got = _dense(inp, d_o, d_s, device())
+    ref = oracle.backward(*inp.widened(), d_o, inp.initial_state, d_s)
+    _compare("backward dense bf16", got, ref)
+
+
+def test_backward_fp32_inputs_no_states():
+    """fp32 inputs, no initial state and no final-state gradient (zeros)."""
+    inp = ki.workload_single(T=256)
+    d_o, _ = ki.loss_gradients(41, (1, 256, 1, 128), 1, 1)
+    got = _dense(inp, d_o, None, device())
+    ref = oracle.backward(*inp.widened(), d_o)
+    _compare("backward fp32", got, ref)
+
+
+@pytest.mark.parametrize("T", [1, 7, 8, 9])
+def test_backward_short_sequences(T):
+    """Fewer tokens than one checkpoint block, exactly one, one more."""
+    inp = ki.dense_prefill(42 + T, B=3, T=T, H=2, gated=True, initial_state=True)
+    d_o, d_s = ki.loss_gradients(42 + T, (3, T, 2, 128), 3, 2)
+    got = _dense(inp, d_o, d_s, device())
+    ref = oracle.backward(*inp.widened(), d_o, inp.initial_state, d_s)
+    _compare(f"backward T={T}", got, ref)
+
+
+def test_backward_no_tokens():
+    """T = 0: the initial-state gradient is the final-state gradient, bit for
+    bit (zeros when none is given)."""
+    torch = __import__("torch")
+    dev = device()
+    H = 2
+    z = torch.zeros((1, 0, H, 128), dtype=torch.bfloat16, device=dev)
+    b = torch.zeros((1, 0, H), dtype=torch.bfloat16, device=dev)
+    la = torch.zeros((1, 0, H, 128), dtype=torch.float32, device=dev)
+    d_o = torch.zeros((1, 0, H, 128), dtype=torch.float32, device=dev)
+    _, d_s = ki.loss_gradients(50, (1, 0, H, 128), 1, H)
+    ds_dev = to_dev(d_s, "f32", dev)
+    g = kda.kda_backward(z, z, z, b, la, d_o, None, ds_dev)
+    g0 = kda.kda_backward(z, z, z, b, la, d_o)
+    torch.cuda.synchronize()
+    assert np.array_equal(g["dinitial_state"].cpu().numpy(), d_s)
+    assert not g0["dinitial_state"].cpu().numpy().any()
+
+
+def test_backward_varlen():
+    """Packed sequences of 0, 1, 7, 8, 9, 70, 0 and 33 tokens (even ones
+    resumed): per-sequence recurrences, empty ones pass the final-state
+    gradient through unchanged."""
+    torch = __import__("torch")
+    dev = device()
+    lengths = [0, 1, 7, 8, 9, 70, 0, 33]
+    H = 2
+    inp = ki.varlen_prefill(51, lengths, H=H)
+    Tt = int(sum(lengths))
+    d_o, d_s = ki.loss_gradients(51, (1, Tt, H, 128), len(lengths), H)
+    t = upload(inp, dev)
+    g = kda.kda_varlen_backward(t["q"], t["k"], t["v"], t["beta"], t["log_alpha"],
+                                to_dev(d_o, "f32", dev), t["cu_seqlens"], t["initial_state"],
+                                to_dev(d_s, "f32", dev))
+    torch.cuda.synchronize()
+    got = _host(g)
+    ref = oracle.varlen_backward(*inp.widened(), d_o, inp.cu_seqlens, inp.initial_state, d_s)
+    got = {n: (x[0] if n != "dinitial_state" else x) for n, x in got.items()}
+    _compare("backward varlen", got, ref)
+    assert np.array_equal(got["dinitial_state"][0], d_s[0])
+    assert np.array_equal(got["dinitial_state"][6], d_s[6])
+
+
+def test_backward_long_gated():
+    """2048 tokens, four heads, gated mix: long-memory channels carry the
+    gradient over the whole sequence."""
+    B, T, H = 1, 2048, 4
+    inp = ki.dense_prefill(52, B=B, T=T, H=H, gated=True, initial_state=True)
+    d_o, d_s = ki.loss_gradients(52, (B, T, H, 128), B, H)
+    got = _dense(inp, d_o, d_s, device())
+    ref = oracle.backward(*inp.widened(), d_o, inp.initial_state, d_s)
+    _compare("backward T=2048", got, ref)
+
+
+def test_backward_training_shape_sampled_heads():
+    """The training shape the benchmark times (8 sequences of 4096 tokens, 32
+    heads, gated mix, no initial state): every gradient of heads 0 and 31
+    against the oracle; all of it finite."""
+    torch = __import__("torch")
+    dev = device()
+    B, T, H = ki.BACKWARD_SHAPE
+    inp = ki.workload_backward()
+    d_o, d_s = ki.loss_gradients(ki.BACKWARD_WORKLOAD, (B, T, H, 128), B, H)
+    got = _dense(inp, d_o, d_s, dev)
+    for n, x in got.items():
+        assert np.all(np.isfinite(x)), n
+    heads = [0, H - 1]
+    q, k, v, b, la = (x[:, :, heads] for x in inp.widened())
+    ref = oracle.backward(q, k, v, b, la, d_o[:, :, heads], None, d_s[:, heads])
+    sub = {n: (x[:, heads] if n == "dinitial_state" else x[:, :, heads]) for n, x in got.items()}
+    _compare("backward 8x4096x32, heads 0 and 31", sub, ref)
