@@ -13,7 +13,8 @@ T = 32768, bf16 inputs, gated channel mix) timed with HIP events, its
 tokens/s and roofline; the roofline of the decode kernel (algorithmic bytes
 per launch over the measured average launch duration, against 8 TB/s); and
 the CPU oracle timed on a bounded sample of the decode workload on the host
-cores.
+cores; and the backward pass (gradients of a prefill) at a training shape,
+B = 8 x T = 4096, H = 32.
 
     python bench.py [--gpus 1] [--steps 1024] [--warmup 32] [--no-prefill]
 """
@@ -42,6 +43,13 @@ DECODE_BYTES_PER_HEAD = 2 * D * D * 4 + 2 * D * 2 + D * 2 + 2 + D * 4 + D * 4
 PREFILL_BYTES_PER_HEAD_TOKEN = 3 * D * 2 + 2 + D * 4 + D * 4
 # Chunked-algorithm flops per head-token at chunk 64 (d_k = d_v = 128).
 PREFILL_FLOPS_PER_HEAD_TOKEN = 9_024_853 / 64
+# Backward, per head-token (d = 128, a multiply-add counted as 2): the token's
+# forward to S' and the next state (S' = Diag(a) S: d^2; p = S'^T k: 2 d^2;
+# S' + k u^T: 2 d^2) and its chain rule (G += q dO^T, du = G^T k, S' dO,
+# G u, S' dp, G + k dp^T, rowsum(G' .* S'): 2 d^2 each; Diag(a) G': d^2),
+# vectors of length d left out.  Recomputation from checkpoints is not counted.
+BACKWARD_FLOPS_PER_HEAD_TOKEN = (1 + 2 + 2 + 7 * 2 + 1) * D * D
+FP32_VALU_PEAK_TFLOPS = 157.3
 
 
 def parse():
@@ -52,6 +60,8 @@ def parse():
     ap.add_argument("--batch", type=int, default=64)
     ap.add_argument("--heads", type=int, default=32)
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
+    ap.add_argument("--backward-reps", type=int, default=3)
     ap.add_argument("--no-raw", action="store_true",
                     help="skip the prefill from raw projections (same kernels: keeps kernel traces to one kind)")
     ap.add_argument("--no-tokens", action="store_true",
@@ -421,6 +431,10 @@ def main():
             time_raw_prefill(kda, torch, np, stream, args.prefill_reps, pq, pk, pv, pb, pla, po, ps, pms, T, result)
             del pq, pk, pv, pb, pla, po, ps
 
+    # ---------------- backward pass (secondary) ---------------------------
+    if not args.no_backward:
+        time_backward(kda, ki, torch, np, dev, up, stream, args.backward_reps, result)
+
     # ---------------- CPU oracle baseline ---------------------------------
     if not args.no_cpu:
         import oracle
@@ -471,6 +485,52 @@ def time_raw_prefill(kda, torch, np, stream, reps, pq, pk, pv, pb, pla, po, ps, 
         "tokens_per_s": T / (rms / 1e3),
         "overhead_vs_prepared": rms / pms - 1,
     }
+
+
+def time_backward(kda, ki, torch, np, dev, up, stream, reps, result):
+    """Gradients of a prefill at a training shape (B = 8 sequences of 4096
+    tokens, H = 32, bf16 inputs, gated channel mix), timed with HIP events
+    (median of the repeats) beside the chunked forward on the same inputs."""
+    B, T, H = ki.BACKWARD_SHAPE
+    log(f"generating backward inputs B={B} T={T} H={H}")
+    inp = ki.workload_backward()
+    d_o, d_s = ki.loss_gradients(ki.BACKWARD_WORKLOAD, (B, T, H, D), B, H)
+    q, k, v, b = (up(x, True) for x in (inp.q, inp.k, inp.v, inp.beta))
+    la, do, ds = up(inp.log_alpha, False), up(d_o, False), up(d_s, False)
+    del inp, d_o, d_s
+
+    def med(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            e.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(e))
+        return float(np.median(ts))
+
+    bms = med(lambda: kda.kda_backward(q, k, v, b, la, do, None, ds))
+    fms = med(lambda: kda.kda_prefill(q, k, v, b, la, None))
+    flops = BACKWARD_FLOPS_PER_HEAD_TOKEN * B * T * H
+    tf = flops / (bms / 1e3) / 1e12
+    log(f"backward: {bms:.2f} ms ({B * T * H / bms / 1e3:.1f} M head-tokens/s, {tf:.1f} TFLOP/s); "
+        f"forward on the same inputs {fms:.2f} ms")
+    result["backward"] = {
+        "workload": f"gradients of a prefill: B={B} x T={T} tokens, H={H}, bf16 q/k/v/beta, fp32 "
+                    "log_alpha/d_o/d_final_state, gated channel mix, zero initial state",
+        "ms": bms,
+        "tokens_per_s": B * T / (bms / 1e3),
+        "head_tokens_per_s": B * T * H / (bms / 1e3),
+        "forward_ms_same_inputs": fms,
+        "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / FP32_VALU_PEAK_TFLOPS, "algorithmic_flops_per_launch": flops,
+                     "note": "fp32 vector arithmetic; recomputation from checkpoints not counted"},
+    }
+    del q, k, v, b, la, do, ds
 
 
 if __name__ == "__main__":

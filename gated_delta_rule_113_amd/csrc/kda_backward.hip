@@ -24,16 +24,20 @@
 // the block's checkpoint into registers and, for each token of the block from
 // the last, recomputes the state up to that token from the checkpoint.  This
 // costs (cb - 1) / 2 extra token updates per token and moves 128 KiB / cb per
-// head-token through the workspace.
+// head-token through the workspace (cb = 8: 16 KiB).
 //
-// Mapping: one workgroup of 256 threads per (sequence, head), with the lane
-// mapping of the other token-by-token kernels (wave w: state columns
-// 32w .. 32w+31; lane l: rows 16*(l >> 3) .. +15 of columns 32w + 4*(l & 7)
-// .. +3), for the state, its checkpoint and its gradient (192 registers).
-// Column sums (p, du) stay inside a wave; row sums (dq, dk, d log a) are
-// summed over the wave's 8 column groups with DPP and over the 4 waves
-// through LDS, double-buffered by token parity so that one barrier per token
-// suffices.
+// Mapping: one workgroup of 512 threads per (sequence, head) (see Layout
+// and BackwardLayout below): each lane holds 8 rows x 4 columns of the state,
+// its block checkpoint and its gradient in registers.  Column sums (p, du)
+// stay inside a wave (DPP row rotations and the gfx950 lane swaps); row sums
+// (dq, dk, d log a) are summed over the wave's column groups with DPP and over
+// the 8 waves through LDS, double-buffered by token parity so that one
+// barrier per token suffices.  The next block's inputs and checkpoint are
+// requested while the current block is computed.  The work is fp32 vector
+// arithmetic, about 1000 instructions per wave and token; no matrix
+// instruction is involved.
+#include <type_traits>
+
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
 
@@ -65,14 +69,69 @@ struct BwdArgs {
     int64_t n_slots;
 };
 
-// Sum over the 8 lanes that differ in lane bits 0..2 (the 8 column groups of
-// a row group): quad swaps by 1 and 2, then the mirror within each 8 lanes.
-__device__ __forceinline__ float sum_cols8(float x)
+// Lane layout of the state, its checkpoint and its gradient: wave w owns the
+// 4*CG columns 4*CG*w ..; lane l holds R consecutive rows R*(l / CG) .. of
+// the 4 columns 4*CG*w + 4*(l % CG) ..  (CG column groups times 128 / R row
+// groups = 64 lanes).
+template <int R_, int CG_>
+struct Layout {
+    static constexpr int R = R_;              // rows per lane
+    static constexpr int CG = CG_;            // column groups per wave
+    static constexpr int RG = kDim / R_;      // row groups per wave
+    static constexpr int NW = kDim / (4 * CG_);  // waves
+    static constexpr int NT = 64 * NW;        // threads
+    static_assert(RG * CG == 64, "a wave is 64 lanes");
+};
+
+// 8 rows x 4 columns per lane, 16 columns per wave, 8 waves (512 threads):
+// two waves per SIMD for one (sequence, head), and a share of 32 registers
+// per matrix, small enough for the checkpoint, the state and its gradient to
+// stay in registers together.  (16 x 4 per lane with 4 waves runs one wave per SIMD and is
+// about 8% slower; 4 x 4 with 16 waves spends more on the column sums.)
+using BackwardLayout = Layout<8, 4>;
+
+// x plus x from another lane (DPP control C).  Every source lane of the
+// patterns used here is valid, so bound_ctrl does not change the result; it
+// lets the compiler fold the lane move into the add.
+template <int C>
+__device__ __forceinline__ float dpp_add_c(float x)
 {
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), C, 0xF, 0xF, true));
+}
+
+// Sum over the CG column groups of a row group (lane bits below log2 CG).
+template <int CG>
+__device__ __forceinline__ float row_sum(float x)
+{
+    x = dpp_add_c<0xB1>(x);                    // lane ^ 1 (quad permutation)
+    if (CG >= 4) x = dpp_add_c<0x4E>(x);       // lane ^ 2
+    if (CG >= 8) x = dpp_add_c<0x141>(x);      // the other quad of 8 (half-row mirror)
     return x;
+}
+
+// Sum over the row groups of a column group (lane bits from log2 CG up):
+// rotations within each 16-lane row, then the gfx950 lane swaps across rows
+// 16 and 32 apart.
+template <int CG>
+__device__ __forceinline__ float col_sum(float x)
+{
+    if (CG <= 1) x = dpp_add_c<0x121>(x);      // row_ror 1
+    if (CG <= 2) x = dpp_add_c<0x122>(x);      // row_ror 2
+    if (CG <= 4) x = dpp_add_c<0x124>(x);      // row_ror 4
+    if (CG <= 8) x = dpp_add_c<0x128>(x);      // row_ror 8
+    const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+    const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+}
+
+// Raw storage bits of one input element, and their value.
+__device__ __forceinline__ uint32_t raw_bits(const bf16_t* p) { return p->bits; }
+__device__ __forceinline__ uint32_t raw_bits(const float* p) { return __float_as_uint(*p); }
+template <typename InT>
+__device__ __forceinline__ float from_bits(uint32_t x)
+{
+    return std::is_same<InT, bf16_t>::value ? __uint_as_float(x << 16) : __uint_as_float(x);
 }
 
 __device__ __forceinline__ float dot4(float4 a, float4 b)
@@ -81,12 +140,13 @@ __device__ __forceinline__ float dot4(float4 a, float4 b)
 }
 
 // S' = Diag(a) S on the lane's share; returns p = S'^T k for its 4 columns
-// (summed over all 128 rows).
-__device__ __forceinline__ float4 decay_and_read(float4 (&s)[16], const float* a, const float* k)
+// (summed over all 128 rows).  a, k: the lane's R rows in LDS.
+template <class Ly>
+__device__ __forceinline__ float4 decay_and_read(float4 (&s)[Ly::R], const float* a, const float* k)
 {
     float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
 #pragma unroll
-    for (int m4 = 0; m4 < 4; ++m4) {
+    for (int m4 = 0; m4 < Ly::R / 4; ++m4) {
         const float4 a4 = *reinterpret_cast<const float4*>(a + 4 * m4);
         const float4 k4 = *reinterpret_cast<const float4*>(k + 4 * m4);
         const float av[4] = {a4.x, a4.y, a4.z, a4.w};
@@ -98,18 +158,20 @@ __device__ __forceinline__ float4 decay_and_read(float4 (&s)[16], const float* a
             p0 += kv[i] * s[m].x; p1 += kv[i] * s[m].y; p2 += kv[i] * s[m].z; p3 += kv[i] * s[m].w;
         }
     }
-    return make_float4(xor_sum_rows(p0), xor_sum_rows(p1), xor_sum_rows(p2), xor_sum_rows(p3));
+    return make_float4(col_sum<Ly::CG>(p0), col_sum<Ly::CG>(p1), col_sum<Ly::CG>(p2),
+                       col_sum<Ly::CG>(p3));
 }
 
 // One token forward on the lane's share: S <- Diag(a) S + k u^T, u = b (v - p).
-__device__ __forceinline__ void forward_token(float4 (&s)[16], const float* a, const float* k,
+template <class Ly>
+__device__ __forceinline__ void forward_token(float4 (&s)[Ly::R], const float* a, const float* k,
                                               float bt, float4 vt)
 {
-    const float4 p = decay_and_read(s, a, k);
+    const float4 p = decay_and_read<Ly>(s, a, k);
     const float4 u = make_float4(bt * (vt.x - p.x), bt * (vt.y - p.y), bt * (vt.z - p.z),
                                  bt * (vt.w - p.w));
 #pragma unroll
-    for (int m4 = 0; m4 < 4; ++m4) {
+    for (int m4 = 0; m4 < Ly::R / 4; ++m4) {
         const float4 k4 = *reinterpret_cast<const float4*>(k + 4 * m4);
         const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
 #pragma unroll
@@ -120,19 +182,31 @@ __device__ __forceinline__ void forward_token(float4 (&s)[16], const float* a, c
     }
 }
 
-template <typename InT>
-__global__ __launch_bounds__(256, 1) void backward_kernel(const BwdArgs a)
+// Barrier for LDS traffic only: each wave's LDS reads and writes complete
+// before it; its global stores stay in flight (a __syncthreads() would also
+// wait for those).  The memory clobber keeps the compiler from moving memory
+// accesses across it.  Global memory is never shared between the waves of a
+// workgroup here (each lane reads back only the checkpoints it wrote).
+__device__ __forceinline__ void lds_barrier()
 {
-    // one block of cb tokens staged: gates (as factors), keys, queries,
-    // values, output gradients; beta
-    __shared__ __attribute__((aligned(16))) float sa[kMaxBackwardBlock][kDim],
-        sk[kMaxBackwardBlock][kDim], sq[kMaxBackwardBlock][kDim], sv[kMaxBackwardBlock][kDim],
-        sdo[kMaxBackwardBlock][kDim];
-    __shared__ float sb[kMaxBackwardBlock];
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <typename InT, class Ly>
+__global__ __launch_bounds__(Ly::NT, 1) void backward_kernel(const BwdArgs a)
+{
+    constexpr int R = Ly::R, NW = Ly::NW;
+    static_assert(Ly::NT >= 3 * kDim, "staging takes three groups of 128 threads");
+    constexpr int TB = kMaxBackwardBlock;
+    // blocks of cb tokens staged, double-buffered: gates (as factors), keys,
+    // queries, values, output gradients; beta
+    __shared__ __attribute__((aligned(16))) float sa[2][TB][kDim], sk[2][TB][kDim],
+        sq[2][TB][kDim], sv[2][TB][kDim], sdo[2][TB][kDim];
+    __shared__ float sb[2][TB];
     // per-wave row sums [token parity][dq, dk, d log a][wave][row] and
     // scalars [token parity][u . dO, d beta][wave]
-    __shared__ __attribute__((aligned(16))) float red[2][3][4][kDim];
-    __shared__ float sred[2][2][4];
+    __shared__ __attribute__((aligned(16))) float red[2][3][NW][kDim];
+    __shared__ float sred[2][2][NW];
 
     const InT* Q = static_cast<const InT*>(a.q);
     const InT* K = static_cast<const InT*>(a.k);
@@ -145,9 +219,10 @@ __global__ __launch_bounds__(256, 1) void backward_kernel(const BwdArgs a)
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
-    const int rg = lane >> 3;
-    const int row0 = 16 * rg;
-    const int col = 32 * wave + 4 * (lane & 7);
+    const int cg = lane % Ly::CG;
+    const int rg = lane / Ly::CG;
+    const int row0 = R * rg;
+    const int col = 4 * Ly::CG * wave + 4 * cg;
     const int cb = a.cb;
 
     int64_t first, len, slot0;
@@ -165,86 +240,146 @@ __global__ __launch_bounds__(256, 1) void backward_kernel(const BwdArgs a)
     const int64_t nb = (len + cb - 1) / cb;
     if (slot0 + nb > a.n_slots) return;  // malformed cu_seqlens: stay inside the workspace
     auto ckpt_of = [&](int64_t b) { return a.ckpt + ((slot0 + b) * H + h) * SS; };
+    auto block_len = [&](int64_t b) { return static_cast<int>(len - b * cb < cb ? len - b * cb : cb); };
 
-    // Stage tokens t0 .. t0+nt-1 of the sequence: threads 0..127 take one
-    // gate and one value element (and with `all` one output-gradient
-    // element) of each token, threads 128..255 one key (and query) element.
+    // Inputs of a block, one element of a token's vector per thread: threads
+    // 0..127 the gate and the value, 128..255 the key and the query,
+    // 256..383 (with `all`) the output gradient; threads below cb beta.  They
+    // are requested one block ahead as raw bits (so no instruction waits for
+    // the loads) and widened when written to the LDS buffer of their block,
+    // just before it is used.  `role` is uniform within a wave.
     const int e = tid & (kDim - 1);
-    auto stage = [&](int64_t t0, int nt, bool all) {
+    const int role = __builtin_amdgcn_readfirstlane(tid >> 7);
+    uint32_t x0[TB], x1[TB], xb = 0;
+    auto request = [&](int64_t b, bool all) {
+        const int nt = block_len(b);
+        const int64_t v0 = ((first + b * cb) * H + h) * kDim + e;
+        const int64_t step = static_cast<int64_t>(H) * kDim;
+        if (role == 0) {
 #pragma unroll
-        for (int t = 0; t < kMaxBackwardBlock; ++t) {
-            if (t < nt) {
-                const int64_t vec = ((first + t0 + t) * H + h) * kDim + e;
-                if (tid < kDim) {
-                    sa[t][e] = exp_gate(a.log_alpha[vec]);
-                    sv[t][e] = widen(V[vec]);
-                    if (all) sdo[t][e] = a.d_o[vec];
-                } else {
-                    sk[t][e] = widen(K[vec]);
-                    if (all) sq[t][e] = widen(Q[vec]);
+            for (int t = 0; t < TB; ++t)
+                if (t < nt) {
+                    x0[t] = __float_as_uint(a.log_alpha[v0 + t * step]);
+                    x1[t] = raw_bits(V + v0 + t * step);
                 }
-            }
-        }
-        if (tid < nt) sb[tid] = widen(B[(first + t0 + tid) * H + h]);
-    };
-    auto load_state = [&](float4 (&x)[16], const float* src) {
+        } else if (role == 1) {
 #pragma unroll
-        for (int m = 0; m < 16; ++m)
+            for (int t = 0; t < TB; ++t)
+                if (t < nt) {
+                    x0[t] = raw_bits(K + v0 + t * step);
+                    x1[t] = raw_bits(Q + v0 + t * step);
+                }
+        } else if (role == 2 && all) {
+#pragma unroll
+            for (int t = 0; t < TB; ++t)
+                if (t < nt) x0[t] = __float_as_uint(a.d_o[v0 + t * step]);
+        }
+        if (tid < nt) xb = raw_bits(B + (first + b * cb + tid) * H + h);
+    };
+    auto stage = [&](int buf, int nt, bool all) {
+        if (role == 0) {
+#pragma unroll
+            for (int t = 0; t < TB; ++t)
+                if (t < nt) {
+                    sa[buf][t][e] = exp_gate(__uint_as_float(x0[t]));
+                    sv[buf][t][e] = from_bits<InT>(x1[t]);
+                }
+        } else if (role == 1) {
+#pragma unroll
+            for (int t = 0; t < TB; ++t)
+                if (t < nt) {
+                    sk[buf][t][e] = from_bits<InT>(x0[t]);
+                    sq[buf][t][e] = from_bits<InT>(x1[t]);
+                }
+        } else if (role == 2 && all) {
+#pragma unroll
+            for (int t = 0; t < TB; ++t)
+                if (t < nt) sdo[buf][t][e] = __uint_as_float(x0[t]);
+        }
+        if (tid < nt) sb[buf][tid] = from_bits<InT>(xb);
+    };
+    auto load_state = [&](float4 (&x)[R], const float* src) {
+#pragma unroll
+        for (int m = 0; m < R; ++m)
             x[m] = src ? *reinterpret_cast<const float4*>(src + (row0 + m) * kDim + col)
                        : make_float4(0.f, 0.f, 0.f, 0.f);
     };
-    auto store_state = [&](const float4 (&x)[16], float* dst) {
+    auto store_state = [&](const float4 (&x)[R], float* dst) {
 #pragma unroll
-        for (int m = 0; m < 16; ++m) *reinterpret_cast<float4*>(dst + (row0 + m) * kDim + col) = x[m];
+        for (int m = 0; m < R; ++m) *reinterpret_cast<float4*>(dst + (row0 + m) * kDim + col) = x[m];
     };
+    // row sums of the R values of every lane over the whole wave, written to
+    // this wave's slot of the LDS partial sums
+    auto put_rows = [&](float (&r)[R], float* dst) {
+#pragma unroll
+        for (int m = 0; m < R; ++m) r[m] = row_sum<Ly::CG>(r[m]);
+        if (cg == 0) {
+#pragma unroll
+            for (int m4 = 0; m4 < R / 4; ++m4)
+                *reinterpret_cast<float4*>(dst + 4 * m4) =
+                    make_float4(r[4 * m4], r[4 * m4 + 1], r[4 * m4 + 2], r[4 * m4 + 3]);
+        }
+    };
+    // A buffer is written again two blocks after it was read; every wave has
+    // passed the barrier of the block in between by then.
 
     // ---- forward sweep: a checkpoint at the start of every block
-    float4 s[16];
+    float4 s[R];
     load_state(s, a.s0 ? a.s0 + unit * SS : nullptr);
+    if (nb > 0) request(0, false);
     for (int64_t b = 0; b < nb; ++b) {
-        const int64_t t0 = b * cb;
-        const int nt = static_cast<int>(len - t0 < cb ? len - t0 : cb);
+        const int buf = static_cast<int>(b & 1);
+        const int nt = block_len(b);
         store_state(s, ckpt_of(b));
-        stage(t0, nt, false);
-        __syncthreads();
+        stage(buf, nt, false);
+        lds_barrier();
+        if (b + 1 < nb) request(b + 1, false);
         for (int t = 0; t < nt; ++t)
-            forward_token(s, &sa[t][row0], &sk[t][row0], sb[t],
-                          *reinterpret_cast<const float4*>(&sv[t][col]));
-        __syncthreads();  // the next block's staging overwrites this one
+            forward_token<Ly>(s, &sa[buf][t][row0], &sk[buf][t][row0], sb[buf][t],
+                              *reinterpret_cast<const float4*>(&sv[buf][t][col]));
     }
 
-    // ---- reverse sweep
-    float4 G[16];
+    // ---- reverse sweep, blocks last to first
+    float4 G[R], ck[R];
     load_state(G, a.d_sT ? a.d_sT + unit * SS : nullptr);
+    if (nb > 0) {
+        request(nb - 1, true);
+        load_state(ck, ckpt_of(nb - 1));
+    }
+    lds_barrier();  // the forward sweep's last block is no longer read
     int par = 0;
     for (int64_t b = nb - 1; b >= 0; --b) {
+        const int buf = static_cast<int>(b & 1);
+        const int nt = block_len(b);
         const int64_t t0 = b * cb;
-        const int nt = static_cast<int>(len - t0 < cb ? len - t0 : cb);
-        float4 ck[16];
-        load_state(ck, ckpt_of(b));
-        stage(t0, nt, true);
-        __syncthreads();
+        stage(buf, nt, true);
+        lds_barrier();
+        float4 ckn[R];
+        if (b > 0) {
+            request(b - 1, true);
+            load_state(ckn, ckpt_of(b - 1));
+        }
         for (int tt = nt - 1; tt >= 0; --tt) {
 #pragma unroll
-            for (int m = 0; m < 16; ++m) s[m] = ck[m];
+            for (int m = 0; m < R; ++m) s[m] = ck[m];
             for (int t = 0; t < tt; ++t)
-                forward_token(s, &sa[t][row0], &sk[t][row0], sb[t],
-                              *reinterpret_cast<const float4*>(&sv[t][col]));
+                forward_token<Ly>(s, &sa[buf][t][row0], &sk[buf][t][row0], sb[buf][t],
+                                  *reinterpret_cast<const float4*>(&sv[buf][t][col]));
             // s = S_{t-1} -> S', and u
-            const float* ar = &sa[tt][row0];
-            const float* kr = &sk[tt][row0];
-            const float* qr = &sq[tt][row0];
-            const float bt = sb[tt];
-            const float4 vt = *reinterpret_cast<const float4*>(&sv[tt][col]);
-            const float4 dot = *reinterpret_cast<const float4*>(&sdo[tt][col]);
-            const float4 p = decay_and_read(s, ar, kr);
+            const float* ar = &sa[buf][tt][row0];
+            const float* kr = &sk[buf][tt][row0];
+            const float* qr = &sq[buf][tt][row0];
+            const float bt = sb[buf][tt];
+            const float4 vt = *reinterpret_cast<const float4*>(&sv[buf][tt][col]);
+            const float4 dot = *reinterpret_cast<const float4*>(&sdo[buf][tt][col]);
+            const float4 p = decay_and_read<Ly>(s, ar, kr);
             const float4 vp = make_float4(vt.x - p.x, vt.y - p.y, vt.z - p.z, vt.w - p.w);
             const float4 u = make_float4(bt * vp.x, bt * vp.y, bt * vp.z, bt * vp.w);
 
             // G += q dO^T;  du = G^T k
             float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
 #pragma unroll
-            for (int m4 = 0; m4 < 4; ++m4) {
+            for (int m4 = 0; m4 < R / 4; ++m4) {
                 const float4 q4 = *reinterpret_cast<const float4*>(qr + 4 * m4);
                 const float4 k4 = *reinterpret_cast<const float4*>(kr + 4 * m4);
                 const float qv[4] = {q4.x, q4.y, q4.z, q4.w};
@@ -257,35 +392,22 @@ __global__ __launch_bounds__(256, 1) void backward_kernel(const BwdArgs a)
                     d0 += kv[i] * G[m].x; d1 += kv[i] * G[m].y; d2 += kv[i] * G[m].z; d3 += kv[i] * G[m].w;
                 }
             }
-            const float4 du = make_float4(xor_sum_rows(d0), xor_sum_rows(d1), xor_sum_rows(d2),
-                                          xor_sum_rows(d3));
+            const float4 du = make_float4(col_sum<Ly::CG>(d0), col_sum<Ly::CG>(d1),
+                                          col_sum<Ly::CG>(d2), col_sum<Ly::CG>(d3));
             const float4 dp = make_float4(-bt * du.x, -bt * du.y, -bt * du.z, -bt * du.w);
 
-            // row sums over the lane's 4 columns, then over the wave's 32:
-            // dq part S' dO, dk = G u + S' dp; then G' = G + k dp^T and
+            // row sums over the lane's 4 columns, then over the wave's: the dq
+            // part S' dO; dk = G u + S' dp; then G' = G + k dp^T and
             // d log a = rowsum(G' .* S'); G <- Diag(a) G'
-            float* rq = &red[par][0][wave][row0];
-            float* rk = &red[par][1][wave][row0];
-            float* rl = &red[par][2][wave][row0];
-            float r[16];
+            float r[R];
 #pragma unroll
-            for (int m = 0; m < 16; ++m) r[m] = sum_cols8(dot4(s[m], dot));
-            if ((lane & 7) == 0) {
+            for (int m = 0; m < R; ++m) r[m] = dot4(s[m], dot);
+            put_rows(r, &red[par][0][wave][row0]);
 #pragma unroll
-                for (int m4 = 0; m4 < 4; ++m4)
-                    *reinterpret_cast<float4*>(rq + 4 * m4) =
-                        make_float4(r[4 * m4], r[4 * m4 + 1], r[4 * m4 + 2], r[4 * m4 + 3]);
-            }
+            for (int m = 0; m < R; ++m) r[m] = dot4(G[m], u) + dot4(s[m], dp);
+            put_rows(r, &red[par][1][wave][row0]);
 #pragma unroll
-            for (int m = 0; m < 16; ++m) r[m] = sum_cols8(dot4(G[m], u) + dot4(s[m], dp));
-            if ((lane & 7) == 0) {
-#pragma unroll
-                for (int m4 = 0; m4 < 4; ++m4)
-                    *reinterpret_cast<float4*>(rk + 4 * m4) =
-                        make_float4(r[4 * m4], r[4 * m4 + 1], r[4 * m4 + 2], r[4 * m4 + 3]);
-            }
-#pragma unroll
-            for (int m4 = 0; m4 < 4; ++m4) {
+            for (int m4 = 0; m4 < R / 4; ++m4) {
                 const float4 a4 = *reinterpret_cast<const float4*>(ar + 4 * m4);
                 const float4 k4 = *reinterpret_cast<const float4*>(kr + 4 * m4);
                 const float av[4] = {a4.x, a4.y, a4.z, a4.w};
@@ -295,49 +417,54 @@ __global__ __launch_bounds__(256, 1) void backward_kernel(const BwdArgs a)
                     const int m = 4 * m4 + i;
                     G[m].x += kv[i] * dp.x; G[m].y += kv[i] * dp.y;
                     G[m].z += kv[i] * dp.z; G[m].w += kv[i] * dp.w;
-                    r[m] = sum_cols8(dot4(G[m], s[m]));
+                    r[m] = dot4(G[m], s[m]);
                     G[m].x *= av[i]; G[m].y *= av[i]; G[m].z *= av[i]; G[m].w *= av[i];
                 }
             }
-            if ((lane & 7) == 0) {
-#pragma unroll
-                for (int m4 = 0; m4 < 4; ++m4)
-                    *reinterpret_cast<float4*>(rl + 4 * m4) =
-                        make_float4(r[4 * m4], r[4 * m4 + 1], r[4 * m4 + 2], r[4 * m4 + 3]);
-            }
-            // scalars over the wave's 32 columns (identical in every row group)
-            const float x1 = sum_cols8(dot4(u, dot));
-            const float x2 = sum_cols8(dot4(du, vp));
+            put_rows(r, &red[par][2][wave][row0]);
+            // scalars over the wave's columns (identical in every row group)
+            const float x1s = row_sum<Ly::CG>(dot4(u, dot));
+            const float x2s = row_sum<Ly::CG>(dot4(du, vp));
             if (lane == 0) {
-                sred[par][0][wave] = x1;
-                sred[par][1][wave] = x2;
+                sred[par][0][wave] = x1s;
+                sred[par][1][wave] = x2s;
             }
             const int64_t row = first + t0 + tt;
             const int64_t vec = (row * H + h) * kDim;
             if (rg == 0)
                 *reinterpret_cast<float4*>(a.dv + vec + col) =
                     make_float4(bt * du.x, bt * du.y, bt * du.z, bt * du.w);
-            __syncthreads();
-            if (tid < kDim) {
-                const int i = tid;
-                float gq = 0.f, gk = 0.f, gl = 0.f, ud = 0.f;
+            lds_barrier();
+            // threads 0..127: dq and d log a of channel tid; 128..255: dk
+            if (tid < 2 * kDim) {
+                const int i = e;
+                if (tid < kDim) {
+                    float gq = 0.f, gl = 0.f, ud = 0.f;
 #pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    gq += red[par][0][w][i];
-                    gk += red[par][1][w][i];
-                    gl += red[par][2][w][i];
-                    ud += sred[par][0][w];
+                    for (int w = 0; w < NW; ++w) {
+                        gq += red[par][0][w][i];
+                        gl += red[par][2][w][i];
+                        ud += sred[par][0][w];
+                    }
+                    a.dq[vec + i] = gq + sk[buf][tt][i] * ud;
+                    a.dla[vec + i] = gl;
+                } else {
+                    float gk = 0.f, db = 0.f;
+#pragma unroll
+                    for (int w = 0; w < NW; ++w) {
+                        gk += red[par][1][w][i];
+                        db += sred[par][1][w];
+                    }
+                    a.dk[vec + i] = gk;
+                    if (tid == kDim) a.dbeta[row * H + h] = db;
                 }
-                a.dq[vec + i] = gq + sk[tt][i] * ud;
-                a.dk[vec + i] = gk;
-                a.dla[vec + i] = gl;
-            } else if (tid == kDim) {
-                a.dbeta[row * H + h] =
-                    sred[par][1][0] + sred[par][1][1] + sred[par][1][2] + sred[par][1][3];
             }
             par ^= 1;
         }
-        __syncthreads();  // the next block's staging overwrites this one
+        if (b > 0) {
+#pragma unroll
+            for (int m = 0; m < R; ++m) ck[m] = ckn[m];
+        }
     }
     if (a.ds0) store_state(G, a.ds0 + unit * SS);
 }
@@ -401,9 +528,10 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const vo
         if (e != hipSuccess) return e;
         a.ckpt = static_cast<float*>(ws);
     }
-    const dim3 grid(static_cast<unsigned>(units)), block(256);
-    if (bf16) hipLaunchKernelGGL(backward_kernel<bf16_t>, grid, block, 0, stream, a);
-    else hipLaunchKernelGGL(backward_kernel<float>, grid, block, 0, stream, a);
+    using Ly = BackwardLayout;
+    const dim3 grid(static_cast<unsigned>(units)), block(Ly::NT);
+    if (bf16) hipLaunchKernelGGL((backward_kernel<bf16_t, Ly>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((backward_kernel<float, Ly>), grid, block, 0, stream, a);
     e = hipGetLastError();
     report("backward launch", e);
     if (ws) {
