@@ -34,8 +34,9 @@
  *    long enough to be cut into segments (see kda_set_prefill_segment) takes
  *    a temporary workspace, allocated and freed in stream order on `stream`
  *    from a memory pool the library keeps per device (no synchronisation);
- *    if that allocation fails the call runs unsegmented instead.  Calls are
- *    re-entrant and thread-safe.
+ *    if that allocation fails the call runs unsegmented instead.  The
+ *    backward calls take their state checkpoints from the same pool.  Calls
+ *    are re-entrant and thread-safe.
  *  - Layouts are dense row-major, innermost dimension last:
  *        q, k, log_alpha : [rows, H, d_k]      v, o : [rows, H, d_v]
  *        beta            : [rows, H]
