@@ -86,3 +86,37 @@ def test_segmented_packed_prefill_graph_replay():
             assert torch.equal(S, S_ref), f"replay {rep}: final states differ"
     finally:
         kda.kda_set_prefill_segment(0)
+
+
+def test_backward_graph_replay():
+    """The backward pass (forward sweep, checkpoints in a stream-ordered
+    workspace, reverse sweep) captured in a HIP graph: every replay gives the
+    bits of the direct call."""
+    torch = __import__("torch")
+    dev = device()
+    inp = ki.dense_prefill(72, B=2, T=45, H=2, gated=True, initial_state=True)
+    d_o, d_s = ki.loss_gradients(72, (2, 45, 2, 128), 2, 2)
+    t = upload(inp, dev)
+    from kda_gpu import to_dev
+    args = (t["q"], t["k"], t["v"], t["beta"], t["log_alpha"], to_dev(d_o, "f32", dev),
+            t["initial_state"], to_dev(d_s, "f32", dev))
+    ref = kda.kda_backward(*args)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        kda.kda_backward(*args)  # warm the binding on a side stream
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = kda.kda_backward(*args)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for x in out.values():
+            x.zero_()  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for n in ref:
+            assert torch.equal(out[n], ref[n]), f"replay {rep}: {n} differs"

@@ -147,3 +147,40 @@ def test_backward_training_shape_sampled_heads():
     ref = oracle.backward(q, k, v, b, la, d_o[:, :, heads], None, d_s[:, heads])
     sub = {n: (x[:, heads] if n == "dinitial_state" else x[:, :, heads]) for n, x in got.items()}
     _compare("backward 8x4096x32, heads 0 and 31", sub, ref)
+
+
+def test_backward_deterministic():
+    """Two calls on the same inputs give the same bits (no atomics, fixed
+    reduction order)."""
+    torch = __import__("torch")
+    dev = device()
+    inp = ki.dense_prefill(53, B=2, T=77, H=3, gated=True, initial_state=True)
+    d_o, d_s = ki.loss_gradients(53, (2, 77, 3, 128), 2, 3)
+    t = upload(inp, dev)
+    args = (t["q"], t["k"], t["v"], t["beta"], t["log_alpha"], to_dev(d_o, "f32", dev),
+            t["initial_state"], to_dev(d_s, "f32", dev))
+    g1 = kda.kda_backward(*args)
+    g2 = kda.kda_backward(*args)
+    torch.cuda.synchronize()
+    for n in g1:
+        assert torch.equal(g1[n], g2[n]), n
+
+
+def test_backward_many_short_packed():
+    """200 packed sequences of 0 to 40 tokens (seeded lengths; about a fifth
+    of them shorter than one checkpoint block, a few empty), two heads."""
+    torch = __import__("torch")
+    dev = device()
+    lengths = [int(x) for x in np.random.default_rng(54).integers(0, 41, 200)]
+    H = 2
+    inp = ki.varlen_prefill(54, lengths, H=H)
+    Tt = int(sum(lengths))
+    d_o, d_s = ki.loss_gradients(54, (1, Tt, H, 128), len(lengths), H)
+    t = upload(inp, dev)
+    g = kda.kda_varlen_backward(t["q"], t["k"], t["v"], t["beta"], t["log_alpha"],
+                                to_dev(d_o, "f32", dev), t["cu_seqlens"], t["initial_state"],
+                                to_dev(d_s, "f32", dev))
+    torch.cuda.synchronize()
+    got = {n: (x.cpu().numpy()[0] if n != "dinitial_state" else x.cpu().numpy()) for n, x in g.items()}
+    ref = oracle.varlen_backward(*inp.widened(), d_o, inp.cu_seqlens, inp.initial_state, d_s)
+    _compare("backward 200 short packed sequences", got, ref)
