@@ -19,12 +19,13 @@
 // The reverse sweep needs S_{t-1} at every token, which cannot be recovered
 // from S_t (Diag(a) is not stably invertible when a channel forgets fast).
 // Each workgroup therefore first runs the recurrence forward and stores the
-// state every `cb` tokens (a checkpoint, 64 KiB per head) in a workspace;
-// the reverse sweep then takes the blocks of cb tokens last to first, loads
-// the block's checkpoint into registers and, for each token of the block from
-// the last, recomputes the state up to that token from the checkpoint.  This
-// costs (cb - 1) / 2 extra token updates per token and moves 128 KiB / cb per
-// head-token through the workspace (cb = 8: 16 KiB).
+// state every cb = 8 tokens (a checkpoint, 64 KiB per head) in a workspace;
+// the reverse sweep then takes the blocks of 8 tokens last to first, loads the
+// block's checkpoint into registers, computes the state after the block's 4th
+// token into LDS and, for each token of the block from the last, recomputes
+// its entering state from the nearer of the two.  This costs 2 extra token
+// updates per token on average and moves 16 KiB per head-token through the
+// workspace (8 KiB written, 8 KiB read).
 //
 // Mapping: one workgroup of 512 threads per (sequence, head) (see Layout
 // and BackwardLayout below): each lane holds 8 rows x 4 columns of the state,
@@ -65,7 +66,7 @@ struct BwdArgs {
     float* dla;
     float* ds0;         // [n_seq, H, 128, 128] or NULL (not written)
     float* ckpt;        // workspace: n_slots * H states
-    int cb;             // checkpoint interval, 1 <= cb <= kMaxBackwardBlock
+    int cb;             // checkpoint interval, 1 <= cb <= kBackwardBlock
     int64_t n_slots;
 };
 
@@ -86,8 +87,9 @@ struct Layout {
 // 8 rows x 4 columns per lane, 16 columns per wave, 8 waves (512 threads):
 // two waves per SIMD for one (sequence, head), and a share of 32 registers
 // per matrix, small enough for the checkpoint, the state and its gradient to
-// stay in registers together.  (16 x 4 per lane with 4 waves runs one wave per SIMD and is
-// about 8% slower; 4 x 4 with 16 waves spends more on the column sums.)
+// stay in registers together.  (16 x 4 per lane with 4 waves runs one wave
+// per SIMD and is about 8% slower; 4 x 4 with 16 waves spends more on the
+// column sums and is slower still.)
 using BackwardLayout = Layout<8, 4>;
 
 // x plus x from another lane (DPP control C).  Every source lane of the
@@ -197,7 +199,8 @@ __global__ __launch_bounds__(Ly::NT, 1) void backward_kernel(const BwdArgs a)
 {
     constexpr int R = Ly::R, NW = Ly::NW;
     static_assert(Ly::NT >= 3 * kDim, "staging takes three groups of 128 threads");
-    constexpr int TB = kMaxBackwardBlock;
+    constexpr int TB = kBackwardBlock;
+    constexpr int MID = TB / 2;  // the state after this many tokens of a block is kept in LDS
     // blocks of cb tokens staged, double-buffered: gates (as factors), keys,
     // queries, values, output gradients; beta
     __shared__ __attribute__((aligned(16))) float sa[2][TB][kDim], sk[2][TB][kDim],
@@ -207,6 +210,9 @@ __global__ __launch_bounds__(Ly::NT, 1) void backward_kernel(const BwdArgs a)
     // scalars [token parity][u . dO, d beta][wave]
     __shared__ __attribute__((aligned(16))) float red[2][3][NW][kDim];
     __shared__ float sred[2][2][NW];
+    // the state after the first MID tokens of the current block, each thread's
+    // share in its own slots (written and read by the same thread only)
+    __shared__ float4 smid[Ly::R][Ly::NT];
 
     const InT* Q = static_cast<const InT*>(a.q);
     const InT* K = static_cast<const InT*>(a.k);
@@ -359,10 +365,29 @@ __global__ __launch_bounds__(Ly::NT, 1) void backward_kernel(const BwdArgs a)
             request(b - 1, true);
             load_state(ckn, ckpt_of(b - 1));
         }
-        for (int tt = nt - 1; tt >= 0; --tt) {
+        // the state after MID tokens: the later tokens of the block are
+        // recomputed from it rather than from the checkpoint
+        const bool use_mid = nt > MID;
+        if (use_mid) {
 #pragma unroll
             for (int m = 0; m < R; ++m) s[m] = ck[m];
-            for (int t = 0; t < tt; ++t)
+            for (int t = 0; t < MID; ++t)
+                forward_token<Ly>(s, &sa[buf][t][row0], &sk[buf][t][row0], sb[buf][t],
+                                  *reinterpret_cast<const float4*>(&sv[buf][t][col]));
+#pragma unroll
+            for (int m = 0; m < R; ++m) smid[m][tid] = s[m];
+        }
+        for (int tt = nt - 1; tt >= 0; --tt) {
+            int t = 0;
+            if (use_mid && tt >= MID) {
+                t = MID;
+#pragma unroll
+                for (int m = 0; m < R; ++m) s[m] = smid[m][tid];
+            } else {
+#pragma unroll
+                for (int m = 0; m < R; ++m) s[m] = ck[m];
+            }
+            for (; t < tt; ++t)
                 forward_token<Ly>(s, &sa[buf][t][row0], &sk[buf][t][row0], sb[buf][t],
                                   *reinterpret_cast<const float4*>(&sv[buf][t][col]));
             // s = S_{t-1} -> S', and u
@@ -505,18 +530,12 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const vo
     a.dla = dlog_alpha;
     a.ds0 = d_initial_state;
 
-    // Checkpoint interval: the shortest (least recomputation) whose
-    // workspace stays within kBackwardWorkspaceCap, else the longest.
+    // One checkpoint slot per block of kBackwardBlock tokens: dense, every
+    // sequence ceil(T / cb); packed, fewer than T_total / cb + n_seq in all.
     const int64_t rows = cu_seqlens ? T_total : n_seq * T;
-    auto slots_for = [&](int64_t cb) {
-        return cu_seqlens ? T_total / cb + n_seq : n_seq * ((T + cb - 1) / cb);
-    };
-    int64_t cb = kBackwardBlock;
-    while (cb < kMaxBackwardBlock &&
-           slots_for(cb) * H * SS * static_cast<int64_t>(sizeof(float)) > kBackwardWorkspaceCap)
-        cb *= 2;
+    const int64_t cb = kBackwardBlock;
     a.cb = static_cast<int>(cb);
-    a.n_slots = rows > 0 ? slots_for(cb) : 0;
+    a.n_slots = rows <= 0 ? 0 : cu_seqlens ? T_total / cb + n_seq : n_seq * ((T + cb - 1) / cb);
 
     void* ws = nullptr;
     if (a.n_slots > 0) {

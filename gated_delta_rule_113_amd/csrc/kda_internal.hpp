@@ -72,13 +72,10 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
 // Backward pass (gradients in q, k, v, beta, log_alpha and the initial state
 // from those in o and the final state), token by token; dense or packed as the
 // prefill.  Gradients are fp32 in the layouts of their inputs.  The forward
-// sweep stores a checkpoint state every kBackwardBlock tokens (more if the
-// workspace would exceed kBackwardWorkspaceCap, up to kMaxBackwardBlock) in a
-// workspace taken in stream order from the device's pool; the reverse sweep
-// recomputes each block from its checkpoint.
+// sweep stores a checkpoint state every kBackwardBlock tokens (8 KiB per
+// head-token) in a workspace taken in stream order from the device's pool;
+// the reverse sweep recomputes each block from its checkpoint.
 constexpr int kBackwardBlock = 8;
-constexpr int kMaxBackwardBlock = 16;
-constexpr int64_t kBackwardWorkspaceCap = int64_t(16) << 30;
 hipError_t launch_backward(const void* q, const void* k, const void* v, const void* beta,
                            const float* log_alpha, const float* d_o, const int32_t* cu_seqlens,
                            int64_t n_seq, int64_t T, int64_t T_total, int64_t H,

@@ -266,10 +266,10 @@ kda_status kda_varlen_prefill_slots(const void *q, const void *k, const void *v,
  *                 pointer as d_final_state
  * q, k, v, beta are in_dtype (bf16 inputs widened exactly); arithmetic is fp32.
  * The call recomputes the forward states: it runs the recurrence once storing
- * a state every 8 tokens (16 if that would take over 16 GiB) in a workspace
- * taken in stream order from the device's pool, then sweeps back recomputing
- * each block from its stored state.  If that allocation fails the call
- * returns KDA_ERR_HIP and enqueues nothing.  B or N = 0 is a no-op; with no
+ * a state every 8 tokens in a workspace taken in stream order from the
+ * device's pool (8 KiB per head-token, e.g. 8 GiB for 8 x 4096 tokens x 32
+ * heads), then sweeps back recomputing each block from its stored state.  If
+ * that allocation fails the call returns KDA_ERR_HIP and enqueues nothing.  B or N = 0 is a no-op; with no
  * tokens, d_initial_state = d_final_state (or zeros).
  */
 kda_status kda_backward(const void *q, const void *k, const void *v, const void *beta,
