@@ -494,6 +494,45 @@ def pin_backward_identity_gate(lib=None):
         assert abs(g["dbeta"][0, t, 0] - (vv[t] - S0.T @ kk[t]) @ (Gt.T @ kk[t])) < 1e-12
         assert _rel(g["dlog_alpha"][0, t, 0], np.sum(Gt * S0, axis=1)) < 1e-12
 
+def pin_backward_gate_identity(lib=None):
+    """d log alpha by a second route.  With the cumulative log-decay G_t and the
+    rescaled state S^_t = exp(-G_t) S_t, the loss depends on G_t only through
+    exp(-G_t) k_t (the written key), exp(G_t) k_t (the read key), exp(G_t) q_t
+    and the final state exp(G_T) S^_T.  So dL/dG_t = q_t dq_t + k_t (S'_t dp_t)
+    - k_t (G_t u_t) elementwise, plus rowsum(dS_T .* S_T) at t = T, and
+    d log alpha_t is the sum of dL/dG_s over s >= t.  Here S'_t and u_t come
+    from a numpy forward pass, dp_t = -dv_t (dv = beta du, dp = -beta du), and
+    G_t u_t = dk_t - S'_t dp_t; the result must equal the oracle's per-token
+    sum of G'_t .* S'_t.  The fast (-5.5) and slow (-1e-4) channels are in."""
+    B, T, H, dk, dv = 1, 9, 1, 5, 4
+    q, k, v, b, la, s0 = _random_case(67, B=B, T=T, H=H, dk=dk, dv=dv)
+    la[..., 0] = -5.5
+    la[..., 1] = -1e-4
+    r = _rng(68)
+    d_o = r.standard_normal((B, T, H, dv))
+    d_s = r.standard_normal((B, H, dk, dv))
+    g = oracle.backward(q, k, v, b, la, d_o, s0, d_s, lib=lib)
+    qq, kk, vv, dd = (x[0, :, 0].astype(np.float64) for x in (q, k, v, d_o))
+    bb = b[0, :, 0].astype(np.float64)
+    aa = np.exp(la[0, :, 0].astype(np.float64))
+    S = s0[0, 0].astype(np.float64)
+    Sp = []
+    for t in range(T):
+        S = aa[t][:, None] * S
+        Sp.append(S.copy())
+        u = bb[t] * (vv[t] - S.T @ kk[t])
+        S = S + np.outer(kk[t], u)
+    acc = np.sum(d_s[0, 0] * S, axis=1)
+    want = np.zeros((T, dk))
+    for t in range(T - 1, -1, -1):
+        dp = -g["dv"][0, t, 0]
+        read = Sp[t] @ dp
+        write = g["dk"][0, t, 0] - read
+        acc = acc + qq[t] * g["dq"][0, t, 0] + kk[t] * (read - write)
+        want[t] = acc
+    assert _rel(g["dlog_alpha"][0, :, 0], want) < 1e-11
+
+
 def pin_backward_packing(lib=None):
     """Sequences are independent: the packed backward equals the dense
     backward of each sequence alone (rows of other sequences untouched), and
@@ -523,5 +562,6 @@ ALL_PINS = [
     pin_decay_closed_form, pin_channel_locality, pin_page_delta_rule,
     pin_causal_linear_attention, pin_scalar_gate, pin_resume, pin_linearity,
     pin_varlen_and_layouts, pin_prepare_gates, pin_prepare_unit_vectors,
-    pin_backward_finite_differences, pin_backward_identity_gate, pin_backward_packing,
+    pin_backward_finite_differences, pin_backward_identity_gate, pin_backward_gate_identity,
+    pin_backward_packing,
 ]

@@ -184,3 +184,34 @@ def test_backward_many_short_packed():
     got = {n: (x.cpu().numpy()[0] if n != "dinitial_state" else x.cpu().numpy()) for n, x in g.items()}
     ref = oracle.varlen_backward(*inp.widened(), d_o, inp.cu_seqlens, inp.initial_state, d_s)
     _compare("backward 200 short packed sequences", got, ref)
+
+
+def test_backward_initial_gradient_in_place():
+    """d_initial_state may be the d_final_state buffer itself (include/kda.h
+    allows it: each workgroup reads its head's final-state gradient before it
+    writes the initial one).  Called through the C ABI with one buffer for
+    both: the same bits as separate buffers."""
+    import ctypes
+    torch = __import__("torch")
+    dev = device()
+    B, T, H = 2, 30, 2
+    inp = ki.dense_prefill(55, B=B, T=T, H=H, gated=True, initial_state=True)
+    d_o, d_s = ki.loss_gradients(55, (B, T, H, 128), B, H)
+    t = upload(inp, dev)
+    do = to_dev(d_o, "f32", dev)
+    ref = kda.kda_backward(t["q"], t["k"], t["v"], t["beta"], t["log_alpha"], do,
+                           t["initial_state"], to_dev(d_s, "f32", dev))
+    buf = to_dev(d_s, "f32", dev)
+    outs = {n: torch.empty_like(ref[n]) for n in ("dq", "dk", "dv", "dbeta", "dlog_alpha")}
+    p = lambda x: ctypes.c_void_p(x.data_ptr())
+    lib = kda.load_library()
+    code = lib.kda_backward(p(t["q"]), p(t["k"]), p(t["v"]), p(t["beta"]), p(t["log_alpha"]),
+                            p(t["initial_state"]), p(do), p(buf), p(outs["dq"]), p(outs["dk"]),
+                            p(outs["dv"]), p(outs["dbeta"]), p(outs["dlog_alpha"]), p(buf),
+                            B, T, H, 128, 128, kda.KDA_BF16,
+                            ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+    torch.cuda.synchronize()
+    assert code == 0, code
+    for n, x in outs.items():
+        assert torch.equal(x, ref[n]), n
+    assert torch.equal(buf, ref["dinitial_state"])
