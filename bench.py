@@ -107,8 +107,8 @@ def measured_traffic(summary: str, kernel: str):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(heads and sequences would shard with no exchange; see the design notes). "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(heads and sequences would shard across GPUs with no exchange). "
               "Run with --gpus 1.", file=sys.stderr)
         return 2
 
