@@ -76,12 +76,20 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
 // head-token) in a workspace taken in stream order from the device's pool;
 // the reverse sweep recomputes each block from its checkpoint.
 constexpr int kBackwardBlock = 8;
+// Long dense bf16 sequences with fewer (sequence, head) pairs than CUs are cut
+// into segments of at least this many tokens (a multiple of 64), run in
+// parallel from their entering states (the chunked prefill's segment pass) and
+// leaving gradients (per-segment gradient maps, composed in order).
+constexpr int64_t kBackwardMinSegment = 1024;
 hipError_t launch_backward(const void* q, const void* k, const void* v, const void* beta,
                            const float* log_alpha, const float* d_o, const int32_t* cu_seqlens,
                            int64_t n_seq, int64_t T, int64_t T_total, int64_t H,
                            const float* initial_state, const float* d_final_state, float* dq,
                            float* dk, float* dv, float* dbeta, float* dlog_alpha,
                            float* d_initial_state, bool bf16, hipStream_t stream);
+
+// Compute units of a device (cached; 256 if the query fails).
+int cu_count(int dev);
 
 // A memory pool per device that keeps freed blocks cached, so per-call
 // workspace allocations on the stream are cheap after the first (NULL if the
@@ -90,6 +98,18 @@ hipMemPool_t workspace_pool(int dev);
 
 // With KDA_DEBUG set in the environment, failed HIP calls are printed to stderr.
 void report(const char* what, hipError_t e);
+
+// The entering state of every segment of `seg` tokens (a positive multiple
+// of 64) of n_seq dense bf16 sequences of T tokens: pass 1 and the combine of
+// the segmented chunked prefill, without its outputs.  `ws` holds
+// n_seq * nseg slots (nseg = ceil(T / seg), slot n * nseg + j) of H states
+// each, three times over: the segment maps [0, 2 * slots * H) states, then
+// the entering states [2 * slots * H, 3 * slots * H).  Nothing is launched
+// when nseg < 2.
+hipError_t launch_segment_states(const void* k, const void* v, const void* beta,
+                                 const float* log_alpha, int64_t n_seq, int64_t T, int64_t H,
+                                 const float* initial_state, int64_t seg, float* ws,
+                                 hipStream_t stream);
 
 // Tokens per segment for the chunked prefill (a positive multiple of 64), or
 // 0 to choose it from the problem size and the number of CUs.

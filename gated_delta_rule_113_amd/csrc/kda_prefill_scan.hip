@@ -1637,4 +1637,43 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
     return e != hipSuccess ? e : f;
 }
 
+hipError_t launch_segment_states(const void* k, const void* v, const void* beta,
+                                 const float* log_alpha, int64_t n_seq, int64_t T, int64_t H,
+                                 const float* initial_state, int64_t seg, float* ws,
+                                 hipStream_t stream)
+{
+    const int64_t nseg = (T + seg - 1) / seg;
+    if (n_seq <= 0 || nseg < 2) return hipSuccess;
+    ScanArgs a = {};
+    a.q = static_cast<const bf16_t*>(k);  // pass 1 reads no queries
+    a.k = static_cast<const bf16_t*>(k);
+    a.v = static_cast<const bf16_t*>(v);
+    a.beta = static_cast<const bf16_t*>(beta);
+    a.log_alpha = log_alpha;
+    a.cu_seqlens = nullptr;
+    a.T = T;
+    a.n_seq = n_seq;
+    a.H = static_cast<int>(H);
+    a.st.init = initial_state;
+    a.o = nullptr;
+    a.raw = 0;
+    a.short_max = -1;
+    a.seg_len = seg;
+    a.nseg_dense = nseg;
+    a.n_segs = n_seq * nseg;
+    a.ws_maps = ws;
+    a.ws_start = ws + static_cast<size_t>(a.n_segs) * H * 2 * SS;
+    hipLaunchKernelGGL(scan_kernel<false>, dim3(static_cast<unsigned>(a.n_segs * H)), dim3(NT), 0,
+                       stream, a);
+    hipError_t e = hipGetLastError();
+    report("segment map launch", e);
+    if (e != hipSuccess) return e;
+    const int64_t units = n_seq * H;
+    hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>((units + 7) / 8 * 64)), dim3(256),
+                       0, stream, a);
+    e = hipGetLastError();
+    report("segment combine launch", e);
+    return e;
+}
+
 }  // namespace kda

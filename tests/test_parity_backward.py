@@ -121,13 +121,27 @@ def test_backward_varlen():
 
 def test_backward_long_gated():
     """2048 tokens, four heads, gated mix: long-memory channels carry the
-    gradient over the whole sequence."""
+    gradient over the whole sequence.  Four (sequence, head) pairs give the
+    CUs too little work, so this runs in two segments of 1024 tokens."""
     B, T, H = 1, 2048, 4
     inp = ki.dense_prefill(52, B=B, T=T, H=H, gated=True, initial_state=True)
     d_o, d_s = ki.loss_gradients(52, (B, T, H, 128), B, H)
     got = _dense(inp, d_o, d_s, device())
     ref = oracle.backward(*inp.widened(), d_o, inp.initial_state, d_s)
     _compare("backward T=2048", got, ref)
+
+
+def test_backward_segmented_ragged():
+    """Two sequences of 3500 tokens, two heads, resumed states: three
+    segments of 1216 tokens and a ragged last one of 1068.  The entering
+    states come from the chunked prefill's segment pass, the leaving
+    gradients from the composed gradient maps."""
+    B, T, H = 2, 3500, 2
+    inp = ki.dense_prefill(56, B=B, T=T, H=H, gated=True, initial_state=True)
+    d_o, d_s = ki.loss_gradients(56, (B, T, H, 128), B, H)
+    got = _dense(inp, d_o, d_s, device())
+    ref = oracle.backward(*inp.widened(), d_o, inp.initial_state, d_s)
+    _compare("backward 2x3500x2, 3 segments", got, ref)
 
 
 def test_backward_training_shape_sampled_heads():
@@ -186,15 +200,17 @@ def test_backward_many_short_packed():
     _compare("backward 200 short packed sequences", got, ref)
 
 
-def test_backward_initial_gradient_in_place():
+@pytest.mark.parametrize("T", [30, 2100])
+def test_backward_initial_gradient_in_place(T):
     """d_initial_state may be the d_final_state buffer itself (include/kda.h
-    allows it: each workgroup reads its head's final-state gradient before it
-    writes the initial one).  Called through the C ABI with one buffer for
-    both: the same bits as separate buffers."""
+    allows it: the final-state gradient is read before the initial one is
+    written).  Called through the C ABI with one buffer for both: the same
+    bits as separate buffers, unsegmented (30 tokens) and in two segments
+    (2100 tokens, two heads of one sequence)."""
     import ctypes
     torch = __import__("torch")
     dev = device()
-    B, T, H = 2, 30, 2
+    B, H = (2, 2) if T < 1000 else (1, 2)
     inp = ki.dense_prefill(55, B=B, T=T, H=H, gated=True, initial_state=True)
     d_o, d_s = ki.loss_gradients(55, (B, T, H, 128), B, H)
     t = upload(inp, dev)
