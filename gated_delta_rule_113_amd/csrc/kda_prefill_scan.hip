@@ -314,6 +314,8 @@ struct ScanArgs {
     int64_t T;                  // dense sequence length
     int64_t n_seq;
     int64_t seg_len;            // tokens per segment (multiple of 64); 0 = one segment each
+    int64_t seg0_len;           // dense: tokens of each sequence's first segment (multiple of 64)
+    int seg0_out;               // dense: pass 1 runs the first segment with outputs (pass 3 skips it)
     int64_t nseg_dense;         // dense: segments per sequence
     int64_t n_segs;             // number of segment slots (grid bound)
     int H;
@@ -381,17 +383,22 @@ __device__ SegInfo decode_segment(const ScanArgs& a, int64_t z)
     s.len = len;
     // packed input: the segment length is the plan's choice, stored after seg_first
     const int64_t seg = s.nseg == 1 ? len : (a.seg_first ? a.seg_first[a.n_seq + 1] : a.seg_len);
-    s.begin = s.j * seg;
-    s.end = (s.j == s.nseg - 1) ? len : s.begin + seg;
+    // dense: the first segment may be shorter than the others
+    const int64_t seg0 = (s.nseg == 1 || a.cu_seqlens || a.seg0_len <= 0) ? seg : a.seg0_len;
+    s.begin = s.j == 0 ? 0 : seg0 + (s.j - 1) * seg;
+    s.end = (s.j == s.nseg - 1) ? len : (s.j == 0 ? seg0 : s.begin + seg);
     return s;
 }
 
-// OUT = true : pass 3 -- outputs and final state, d_v = 128 (one 16-column group per wave)
-// OUT = false: pass 1 -- segment maps [M | R], 256 columns (two groups per wave), no outputs
+// One (sequence, head, segment) of a pass; sm is the workgroup's LDS.
+// OUT = true : outputs and leaving state, d_v = 128 (one 16-column group per wave)
+// OUT = false: segment maps [M | R], 256 columns (two groups per wave), no outputs
+// With seg0_out (dense input), the first segment of a sequence cut in two or
+// more runs with outputs in pass 1, from the true initial state, and leaves its
+// state where pass 2 expects it; pass 3 then skips it.
 template <bool OUT>
-__global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
+__device__ __forceinline__ void scan_segment(const ScanArgs& a, char* sm, bool pass1)
 {
-    __shared__ __attribute__((aligned(16))) char sm[LDS_BYTES];
     constexpr int NS = OUT ? 1 : 2;
 
     const int tid = threadIdx.x;
@@ -412,6 +419,8 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
     if (!sg.valid) return;
     if (sg.len <= a.short_max) return;        // a short sequence: the token-by-token kernel's
     if (!OUT && sg.j == sg.nseg - 1) return;  // the last segment needs no map
+    const bool first_out = a.seg0_out && sg.nseg > 1 && sg.j == 0;
+    if (OUT ? first_out != pass1 : first_out) return;
     // this segment's workspace slot (dense: the segment index; packed: the
     // sequence's first slot + j, multi-segment sequences only)
     const int64_t wz = a.ws_first ? a.ws_first[sg.n] + sg.j : z;
@@ -424,7 +433,7 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
     {
         const float* init = nullptr;
         if (OUT) {
-            if (sg.nseg > 1) init = a.ws_start + (wz * H + h) * SS;
+            if (sg.nseg > 1 && !first_out) init = a.ws_start + (wz * H + h) * SS;
             else init = init_state_of(a.st, sg.n, h, H);
         } else if (sg.j == 0) {
             init = init_state_of(a.st, sg.n, h, H);
@@ -1196,7 +1205,8 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
         store_o(cl, static_cast<int>(seg_tokens - cl), tid);
     }
     if (OUT) {
-        float* dst = sg.j == sg.nseg - 1 ? final_state_of(a.st, sg.n, h, H) : nullptr;
+        float* dst = first_out ? a.ws_start + ((wz + 1) * H + h) * SS
+                               : (sg.j == sg.nseg - 1 ? final_state_of(a.st, sg.n, h, H) : nullptr);
         if (dst) {
 #pragma unroll
             for (int t = 0; t < 8; ++t)
@@ -1218,6 +1228,20 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     dm[gi * SS + (16 * t + 4 * g4 + i) * kDim + col] = S[gi][t][i];
+    }
+}
+
+// PASS3 = false: pass 1 (segment maps; with seg0_out also the first segments'
+// outputs); PASS3 = true: pass 3 (outputs and final states).
+template <bool PASS3>
+__global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
+{
+    __shared__ __attribute__((aligned(16))) char sm[LDS_BYTES];
+    if (PASS3) {
+        scan_segment<true>(a, sm, false);
+    } else {
+        if (a.seg0_out) scan_segment<true>(a, sm, true);
+        scan_segment<false>(a, sm, true);
     }
 }
 
@@ -1545,6 +1569,18 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
         const int64_t per_cu = (rows * H + cu_count(dev) - 1) / cu_count(dev);
         seg = std::max<int64_t>(kMinSegment, (per_cu + CH - 1) / CH * CH);
     }
+    // Dense input: the first segment of each sequence runs with outputs in
+    // pass 1, beside the maps of the others, so a sequence takes one segment
+    // more for the same number of workgroups per pass.  A chunk with outputs
+    // costs about 8/7 of a map chunk, so the first segment is 7/8 as long.
+    int64_t seg0 = seg;
+    if (!cu_seqlens && g_forced_segment <= 0 && T > seg) {
+        const int64_t k = (T + seg - 1) / seg;  // segments at the plain length
+        const int64_t even = (8 * T + 8 * k + 6) / (8 * k + 7);
+        seg = std::max<int64_t>(kMinSegment, (even + CH - 1) / CH * CH);
+        seg0 = std::min<int64_t>(seg, (seg * 7 / 8 + CH - 1) / CH * CH);
+    }
+    const int64_t nseg_dense = T > seg0 ? 1 + (T - seg0 + seg - 1) / seg : 1;
     const int64_t longest_bound = cu_seqlens ? T_total : T;
     const dim3 block(NT);
 
@@ -1560,9 +1596,8 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
     // twice its length over the segment length).
     int64_t n_segs = 0, slots = 0;
     size_t ws_bytes = 0, plan_bytes = 0;
-    if (longest_bound > seg_min) {
-        n_segs = cu_seqlens ? n_seq + (T_total + seg_min - 1) / seg_min
-                            : n_seq * ((T + seg - 1) / seg);
+    if (cu_seqlens ? longest_bound > seg_min : nseg_dense > 1) {
+        n_segs = cu_seqlens ? n_seq + (T_total + seg_min - 1) / seg_min : n_seq * nseg_dense;
         slots = cu_seqlens ? std::min<int64_t>(n_segs, 2 * ((T_total + seg_min - 1) / seg_min))
                            : n_segs;
         plan_bytes = cu_seqlens ? ((2 * static_cast<size_t>(n_seq) + 3 + static_cast<size_t>(n_segs)) *
@@ -1596,8 +1631,10 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
     }
 
     a.seg_len = seg;
+    a.seg0_len = seg0;
+    a.seg0_out = cu_seqlens ? 0 : 1;
     a.n_segs = n_segs;
-    a.nseg_dense = cu_seqlens ? 0 : (T + seg - 1) / seg;
+    a.nseg_dense = cu_seqlens ? 0 : nseg_dense;
     char* w = static_cast<char*>(ws);
     if (cu_seqlens) {
         a.seg_first = reinterpret_cast<int32_t*>(w);             // [n_seq + 2]
@@ -1659,6 +1696,8 @@ hipError_t launch_segment_states(const void* k, const void* v, const void* beta,
     a.raw = 0;
     a.short_max = -1;
     a.seg_len = seg;
+    a.seg0_len = seg;
+    a.seg0_out = 0;  // every segment's map, and each entering state, in the workspace
     a.nseg_dense = nseg;
     a.n_segs = n_seq * nseg;
     a.ws_maps = ws;

@@ -297,7 +297,9 @@ kda_status kda_varlen_backward(const void *q, const void *k, const void *v, cons
  * context-parallel" in "Kimi K3 -- the architecture and infrastructure,
  * explained", section "Kimi Delta Attention: the load-bearing choice").
  * 0 (the default) picks the length from the problem size and the number of
- * compute units; for packed input a small planning kernel then chooses, on
+ * compute units; for dense input the first segment of each sequence is then
+ * about 7/8 as long as the others, since it runs with its outputs while the
+ * other segments build their maps; for packed input a small planning kernel then chooses, on
  * the device where the sequence lengths are, between that length and the
  * powers of two below it (down to an eighth of it).  tokens must be 0 or a
  * positive multiple of 64, else KDA_ERR_SHAPE.  Results do not depend on it

@@ -52,6 +52,17 @@ def test_dense_segmented(segment, seg, T):
     check(f"dense segmented seg={seg} T={T}", rel_err_vectors(o, o_ref), rel_err_states(S, S_ref))
 
 
+def test_dense_automatic_shorter_first_segment():
+    """Automatic segment lengths for dense input: at B=2, H=8, T=4096 on 256
+    compute units the first segment of each sequence has 896 tokens and runs
+    with outputs in pass 1, then come three of 1024 and a last one of 128;
+    resumed (non-zero) initial states."""
+    inp = ki.dense_prefill(42, B=2, T=4096, H=8, gated=True, initial_state=True)
+    o, S = _dense(inp, device())
+    o_ref, S_ref = oracle.prefill(*inp.widened(), inp.initial_state)
+    check("dense automatic segments", rel_err_vectors(o, o_ref), rel_err_states(S, S_ref))
+
+
 def test_dense_segmented_zero_initial_state(segment):
     inp = ki.dense_prefill(41, B=1, T=700, H=2, gated=True)
     segment(64)
