@@ -122,6 +122,8 @@ constexpr int LDS_BYTES = OFF_TD + 4 * 16 * TD_LD * 4;
 // and P, between a chunk's state products and the next chunk's staging
 constexpr int OFF_OT = OFF_T_HI;
 static_assert(OFF_P_LO + 8192 - OFF_T_HI == CH * kDim * 4, "output tile fits T and P exactly");
+constexpr int TP_BYTES = 4 * 8192;  // the split T and P of one chunk (T hi, T lo, P hi, P lo)
+static_assert(TP_BYTES == 16 * NT * 4, "four 16-byte pieces per thread");
 static_assert(R1_BYTES >= 32768, "Ke^T must fit in R1");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CU");
 
@@ -325,6 +327,9 @@ struct ScanArgs {
     int64_t short_max;  // sequences of at most this many tokens are skipped (0: none)
     float* ws_maps;   // [slots][H][2][d_k][d_v]: M and R of each segment but the last
     float* ws_start;  // [slots][H][d_k][d_v]: entering state of each segment
+    char* ws_tp;      // dense, or null: [segments][H][tp_chunks] LDS images (32 KiB) of the split
+                      // T and P of every chunk of the segments that pass 1 maps; pass 3 reuses them
+    int64_t tp_chunks;
 };
 
 namespace {
@@ -396,10 +401,17 @@ __device__ SegInfo decode_segment(const ScanArgs& a, int64_t z)
 // With seg0_out (dense input), the first segment of a sequence cut in two or
 // more runs with outputs in pass 1, from the true initial state, and leaves its
 // state where pass 2 expects it; pass 3 then skips it.
-template <bool OUT>
+// TP (with a T/P workspace): pass 1 also forms P and stores each chunk's split
+// T and P; pass 3 loads them instead of forming the A and P tiles and solving
+// for T (the segment's inputs are the same, so are T and P).
+template <bool OUT, bool TP>
 __device__ __forceinline__ void scan_segment(const ScanArgs& a, char* sm, bool pass1)
 {
     constexpr int NS = OUT ? 1 : 2;
+    constexpr bool LOADTP = OUT && TP;        // T and P from the workspace
+    constexpr bool STORETP = !OUT && TP;      // T and P to the workspace
+    constexpr bool WITHP = (OUT && !TP) || STORETP;  // the P tile is formed here
+    constexpr bool QIN = OUT || STORETP;      // queries are staged
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -420,7 +432,9 @@ __device__ __forceinline__ void scan_segment(const ScanArgs& a, char* sm, bool p
     if (sg.len <= a.short_max) return;        // a short sequence: the token-by-token kernel's
     if (!OUT && sg.j == sg.nseg - 1) return;  // the last segment needs no map
     const bool first_out = a.seg0_out && sg.nseg > 1 && sg.j == 0;
-    if (OUT ? first_out != pass1 : first_out) return;
+    // segments that pass 1 maps, when there is a T/P workspace
+    const bool tp_seg = a.ws_tp && sg.nseg > 1 && sg.j < sg.nseg - 1 && !first_out;
+    if (OUT ? (first_out != pass1 || (!first_out && TP != tp_seg)) : first_out) return;
     // this segment's workspace slot (dense: the segment index; packed: the
     // sequence's first slot + j, multi-segment sequences only)
     const int64_t wz = a.ws_first ? a.ws_first[sg.n] + sg.j : z;
@@ -487,7 +501,7 @@ __device__ __forceinline__ void scan_segment(const ScanArgs& a, char* sm, bool p
             if (L == CH || (tid >> 4) + 32 * m < L) {
                 pk[m] = *gat<const uint4>(a.k + e0, 2 * off);
                 pv[m] = *gat<const uint4>(a.v + e0, 2 * off);
-                if (OUT) pq[m] = *gat<const uint4>(a.q + e0, 2 * off);
+                if (QIN) pq[m] = *gat<const uint4>(a.q + e0, 2 * off);
             } else {
                 pk[m] = pv[m] = pq[m] = make_uint4(0, 0, 0, 0);
             }
@@ -539,6 +553,15 @@ __device__ __forceinline__ void scan_segment(const ScanArgs& a, char* sm, bool p
         const int tq = tid >> 5;                 // token quad (scan, operand formation)
         const int cq = tid & 31;                 // natural channel quad
         const int pq4 = perm(4 * cq);            // its position in the permuted order
+        // this chunk's T/P image in the workspace: 512 threads x 4 x 16 bytes
+        char* tpg = TP ? a.ws_tp + ((wz * H + h) * a.tp_chunks + ci) * static_cast<int64_t>(TP_BYTES) : nullptr;
+        uint4 tp0, tp1, tp2, tp3;  // (named registers: an array here ended up in scratch memory)
+        if (LOADTP) {
+            tp0 = *gat<const uint4>(tpg, 16 * tid);
+            tp1 = *gat<const uint4>(tpg, 16 * (tid + NT));
+            tp2 = *gat<const uint4>(tpg, 16 * (tid + 2 * NT));
+            tp3 = *gat<const uint4>(tpg, 16 * (tid + 3 * NT));
+        }
 
         // ======== 0: stage the chunk; scan of the log2-decay in registers.
         //             With outputs, the previous chunk's output tile is
@@ -549,7 +572,7 @@ __device__ __forceinline__ void scan_segment(const ScanArgs& a, char* sm, bool p
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
                     pk[m] = unit_row(pk[m]);
-                    if (OUT) pq[m] = unit_row(pq[m]);
+                    if (QIN) pq[m] = unit_row(pq[m]);
                 }
             }
 #pragma unroll
@@ -559,7 +582,7 @@ __device__ __forceinline__ void scan_segment(const ScanArgs& a, char* sm, bool p
                 const int p0 = perm(c8), p1 = perm(c8 + 4);
                 at<uint2>(sm, OFF_K + a256(r, p0)) = make_uint2(pk[m].x, pk[m].y);
                 at<uint2>(sm, OFF_K + a256(r, p1)) = make_uint2(pk[m].z, pk[m].w);
-                if (OUT) {
+                if (QIN) {
                     at<uint2>(sm, OFF_Q + a256(r, p0)) = make_uint2(pq[m].x, pq[m].y);
                     at<uint2>(sm, OFF_Q + a256(r, p1)) = make_uint2(pq[m].z, pq[m].w);
                 }
@@ -629,7 +652,7 @@ __device__ __forceinline__ void scan_segment(const ScanArgs& a, char* sm, bool p
         const int rb = kh ? 3 - (wave & 3) : (wave & 3);
         f32x4 accA[4], accP[4];
         float qk = 0.f;
-        {
+        if constexpr (!LOADTP) {
             int fl = 0;
 #pragma unroll
             for (int w = 0; w < NW; ++w) fl |= at<int>(sm, OFF_UNSAFE + 4 * w);
@@ -656,7 +679,7 @@ __device__ __forceinline__ void scan_segment(const ScanArgs& a, char* sm, bool p
                 const float rr[8] = {ra.x, ra.y, ra.z, ra.w, rbv.x, rbv.y, rbv.z, rbv.w};
                 const bf16x8 kk = at<bf16x8>(sm, OFF_K + a256(r, p0));
                 bf16x8 qq = kk;
-                if (OUT) qq = at<bf16x8>(sm, OFF_Q + a256(r, p0));
+                if (WITHP) qq = at<bf16x8>(sm, OFF_Q + a256(r, p0));
                 float xk[8], xq[8], xd[8];
 #pragma unroll
                 for (int jj = 0; jj < 8; ++jj) {
@@ -668,7 +691,7 @@ __device__ __forceinline__ void scan_segment(const ScanArgs& a, char* sm, bool p
                     xd[jj] = uns ? 0.f : bfw(kk[jj]) * ex2(-d);
                 }
                 split_vec(xk, fkh[sl], fkl[sl]);
-                if (OUT) split_vec(xq, fqh[sl], fql[sl]);
+                if (WITHP) split_vec(xq, fqh[sl], fql[sl]);
                 split_vec(xd, cdh[sl], cdl[sl]);
             }
 #pragma unroll
@@ -681,13 +704,13 @@ __device__ __forceinline__ void scan_segment(const ScanArgs& a, char* sm, bool p
 #pragma unroll
                         for (int sl = 0; sl < 2; ++sl) {
                             accA[ib] = mma3(cdh[sl], cdl[sl], fkh[sl], fkl[sl], accA[ib]);
-                            if (OUT) accP[ib] = mma3(cdh[sl], cdl[sl], fqh[sl], fql[sl], accP[ib]);
+                            if (WITHP) accP[ib] = mma3(cdh[sl], cdl[sl], fqh[sl], fql[sl], accP[ib]);
                         }
                     } else {
                         // steep decay inside the block: pairwise on the vector ALUs,
                         // result in the accumulator layout (row r, column 16rb+4g4+i)
                         const char* K = sm + OFF_K;
-                        const char* Q = sm + (OUT ? OFF_Q : OFF_K);
+                        const char* Q = sm + (WITHP ? OFF_Q : OFF_K);
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             const int ti = 16 * rb + 4 * g4 + i;
@@ -721,14 +744,14 @@ __device__ __forceinline__ void scan_segment(const ScanArgs& a, char* sm, bool p
                         bf16x8 ch, cl;
                         split_vec(x, ch, cl);
                         accA[ib] = mma3(ch, cl, fkh[sl], fkl[sl], accA[ib]);
-                        if (OUT) accP[ib] = mma3(ch, cl, fqh[sl], fql[sl], accP[ib]);
+                        if (WITHP) accP[ib] = mma3(ch, cl, fqh[sl], fql[sl], accP[ib]);
                     }
                 }
             }
             // P_rr = q_r . k_r carries no decay; it is summed in fp32 here, since
             // when it dominates o_r (a token right after a zero state) its
             // cancellation would expose the ~16-bit split operands
-            if (OUT && kh == 1) {
+            if (WITHP && kh == 1) {
 #pragma unroll
                 for (int part = 0; part < 4; ++part) {
                     const int p0 = 32 * g4 + 8 * part;
@@ -749,15 +772,15 @@ __device__ __forceinline__ void scan_segment(const ScanArgs& a, char* sm, bool p
                     if (ib > rb) continue;
                     at<f32x4>(sm, OFF_N + (r * N_LD + 16 * ib + 4 * g4) * 4) = accA[ib];
                 }
-            } else if (OUT) {
+            } else if (WITHP) {
 #pragma unroll
                 for (int ib = 0; ib < 4; ++ib) {
                     if (ib > rb) continue;
                     at<f32x4>(sm, OFF_TF + (r * N_LD + 16 * ib + 4 * g4) * 4) = accP[ib];
                 }
             }
+            __syncthreads();
         }
-        __syncthreads();
 
         // ======== 4: the first half of the waves (row block rb = wave) finishes
         //             N = Diag(b) A (strictly lower) of its row block and, from
@@ -804,7 +827,13 @@ __device__ __forceinline__ void scan_segment(const ScanArgs& a, char* sm, bool p
             at<__bf16>(sm, OFF_T_LO + off) = (__bf16)(x - (float)hb);
         };
 
-        if (kh == 0) {
+        if constexpr (LOADTP) {
+            // the output tile over T and P was written out in phase 0
+            at<uint4>(sm, OFF_T_HI + 16 * tid) = tp0;
+            at<uint4>(sm, OFF_T_HI + 16 * (tid + NT)) = tp1;
+            at<uint4>(sm, OFF_T_HI + 16 * (tid + 2 * NT)) = tp2;
+            at<uint4>(sm, OFF_T_HI + 16 * (tid + 3 * NT)) = tp3;
+        } else if (kh == 0) {
             const int r = 16 * rb + l16;
             const float br = at<float>(sm, OFF_BETA + 4 * r);
 #pragma unroll
@@ -843,7 +872,7 @@ __device__ __forceinline__ void scan_segment(const ScanArgs& a, char* sm, bool p
                 at<float>(sm, td_off(b, 4 * p + m, jc)) = tv[m];
                 put_t(16 * b + 4 * p + m, 16 * b + jc, tv[m]);
             }
-        } else if (OUT) {
+        } else if (WITHP) {
             const int r = 16 * rb + l16;
 #pragma unroll
             for (int ib = 0; ib < 4; ++ib) {
@@ -929,7 +958,8 @@ __device__ __forceinline__ void scan_segment(const ScanArgs& a, char* sm, bool p
                     }
                 }
             };
-            if (wave == 0) column(std::integral_constant<int, 0>{});
+            if (LOADTP) {
+            } else if (wave == 0) column(std::integral_constant<int, 0>{});
             else if (wave == 1) column(std::integral_constant<int, 1>{});
             else if (wave == 2) column(std::integral_constant<int, 2>{});
             else if (wave == 3 || wave == 4) {
@@ -955,6 +985,13 @@ __device__ __forceinline__ void scan_segment(const ScanArgs& a, char* sm, bool p
         __syncthreads();
 
         // ======== 8: state products (each wave its own columns)
+        if (STORETP) {
+            // T and P are complete (and only read from here on): their image
+            // goes to the workspace for pass 3
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *gat<uint4>(tpg, 16 * (tid + NT * j)) = at<uint4>(sm, OFF_T_HI + 16 * (tid + NT * j));
+        }
         // Ke^T into R1 (N and T are dead); read only after the next barrier
         {
             const int tp = perm(4 * tq);
@@ -1233,15 +1270,17 @@ __device__ __forceinline__ void scan_segment(const ScanArgs& a, char* sm, bool p
 
 // PASS3 = false: pass 1 (segment maps; with seg0_out also the first segments'
 // outputs); PASS3 = true: pass 3 (outputs and final states).
-template <bool PASS3>
+// TP: with the T/P workspace (a.ws_tp set).
+template <bool PASS3, bool TP>
 __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
 {
     __shared__ __attribute__((aligned(16))) char sm[LDS_BYTES];
     if (PASS3) {
-        scan_segment<true>(a, sm, false);
+        if (TP) scan_segment<true, true>(a, sm, false);
+        scan_segment<true, false>(a, sm, false);
     } else {
-        if (a.seg0_out) scan_segment<true>(a, sm, true);
-        scan_segment<false>(a, sm, true);
+        if (a.seg0_out) scan_segment<true, false>(a, sm, true);
+        scan_segment<false, TP>(a, sm, true);
     }
 }
 
@@ -1477,6 +1516,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* cu, int64_t n
 // ---------------- host side
 
 constexpr int64_t kMinSegment = 1024;
+constexpr int64_t kMaxTPBytes = int64_t(8) << 30;  // largest T/P workspace of one dense call
 int64_t g_forced_segment = 0;  // tokens per segment forced by kda_set_prefill_segment (0 = automatic)
 std::mutex g_pool_mutex;
 hipMemPool_t g_pools[64] = {};
@@ -1571,16 +1611,37 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
     }
     // Dense input: the first segment of each sequence runs with outputs in
     // pass 1, beside the maps of the others, so a sequence takes one segment
-    // more for the same number of workgroups per pass.  A chunk with outputs
-    // costs about 8/7 of a map chunk, so the first segment is 7/8 as long.
+    // more for the same number of workgroups per pass.  Pass 1 also keeps the
+    // split T and P of every chunk it maps (32 KiB each) when that workspace
+    // stays within kMaxTPBytes; pass 3 then reruns those chunks without
+    // forming T and P, at about 5/8 of the cost, and the last segment, which
+    // pass 1 does not map, is about 5/8 as long as the others.  Without it a
+    // chunk with outputs costs about 8/7 of a map chunk, and the first segment
+    // is 7/8 as long instead.
+    auto dense_segments = [&](int64_t s0, int64_t s) { return T > s0 ? 1 + (T - s0 + s - 1) / s : 1; };
     int64_t seg0 = seg;
-    if (!cu_seqlens && g_forced_segment <= 0 && T > seg) {
-        const int64_t k = (T + seg - 1) / seg;  // segments at the plain length
-        const int64_t even = (8 * T + 8 * k + 6) / (8 * k + 7);
-        seg = std::max<int64_t>(kMinSegment, (even + CH - 1) / CH * CH);
-        seg0 = std::min<int64_t>(seg, (seg * 7 / 8 + CH - 1) / CH * CH);
+    bool tp = false;
+    if (!cu_seqlens) {
+        int64_t seg_tp = seg;
+        if (g_forced_segment <= 0 && T > seg) {
+            const int64_t k = (T + seg - 1) / seg;  // segments at the plain length
+            const int64_t even = (8 * T + 8 * k + 4) / (8 * k + 5);
+            seg_tp = std::max<int64_t>(kMinSegment, (even + CH - 1) / CH * CH);
+        }
+        const int64_t nseg_tp = dense_segments(seg_tp, seg_tp);
+        tp = nseg_tp > 1 && static_cast<double>(n_seq) * nseg_tp * H * ((seg_tp + CH - 1) / CH) * TP_BYTES <=
+                                static_cast<double>(kMaxTPBytes);
+        if (tp) {
+            seg = seg0 = seg_tp;
+        } else if (g_forced_segment <= 0 && T > seg) {
+            const int64_t k = (T + seg - 1) / seg;
+            const int64_t even = (8 * T + 8 * k + 6) / (8 * k + 7);
+            seg = std::max<int64_t>(kMinSegment, (even + CH - 1) / CH * CH);
+            seg0 = std::min<int64_t>(seg, (seg * 7 / 8 + CH - 1) / CH * CH);
+        }
     }
-    const int64_t nseg_dense = T > seg0 ? 1 + (T - seg0 + seg - 1) / seg : 1;
+    const int64_t nseg_dense = dense_segments(seg0, seg);
+    const int64_t tp_chunks = tp ? (std::max(seg0, seg) + CH - 1) / CH : 0;
     const int64_t longest_bound = cu_seqlens ? T_total : T;
     const dim3 block(NT);
 
@@ -1603,7 +1664,8 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
         plan_bytes = cu_seqlens ? ((2 * static_cast<size_t>(n_seq) + 3 + static_cast<size_t>(n_segs)) *
                                        4 + 255) / 256 * 256
                                 : 0;
-        ws_bytes = plan_bytes + static_cast<size_t>(slots) * H * 3 * SS * sizeof(float);
+        ws_bytes = plan_bytes + static_cast<size_t>(slots) * H * 3 * SS * sizeof(float) +
+                   static_cast<size_t>(n_segs) * H * tp_chunks * TP_BYTES;
     }
     void* ws = nullptr;
     if (ws_bytes) {
@@ -1624,7 +1686,7 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
         a.n_segs = n_seq;
         a.seg_first = nullptr;
         const dim3 grid(static_cast<unsigned>(n_seq * H));
-        hipLaunchKernelGGL(scan_kernel<true>, grid, block, 0, stream, a);
+        hipLaunchKernelGGL((scan_kernel<true, false>), grid, block, 0, stream, a);
         e = hipGetLastError();
         report("prefill scan launch", e);
         return e;
@@ -1653,9 +1715,14 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
     }
     a.ws_maps = reinterpret_cast<float*>(w + plan_bytes);
     a.ws_start = a.ws_maps + static_cast<size_t>(slots) * H * 2 * SS;
+    if (tp) {
+        a.ws_tp = reinterpret_cast<char*>(a.ws_start + static_cast<size_t>(slots) * H * SS);
+        a.tp_chunks = tp_chunks;
+    }
 
     const dim3 grid(static_cast<unsigned>(n_segs * H));
-    hipLaunchKernelGGL(scan_kernel<false>, grid, block, 0, stream, a);
+    if (tp) hipLaunchKernelGGL((scan_kernel<false, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((scan_kernel<false, false>), grid, block, 0, stream, a);
     e = hipGetLastError();
     report("segment map launch", e);
     if (e == hipSuccess) {
@@ -1665,7 +1732,8 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
         report("segment combine launch", e);
     }
     if (e == hipSuccess) {
-        hipLaunchKernelGGL(scan_kernel<true>, grid, block, 0, stream, a);
+        if (tp) hipLaunchKernelGGL((scan_kernel<true, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((scan_kernel<true, false>), grid, block, 0, stream, a);
         e = hipGetLastError();
         report("prefill scan launch", e);
     }
@@ -1702,7 +1770,7 @@ hipError_t launch_segment_states(const void* k, const void* v, const void* beta,
     a.n_segs = n_seq * nseg;
     a.ws_maps = ws;
     a.ws_start = ws + static_cast<size_t>(a.n_segs) * H * 2 * SS;
-    hipLaunchKernelGGL(scan_kernel<false>, dim3(static_cast<unsigned>(a.n_segs * H)), dim3(NT), 0,
+    hipLaunchKernelGGL((scan_kernel<false, false>), dim3(static_cast<unsigned>(a.n_segs * H)), dim3(NT), 0,
                        stream, a);
     hipError_t e = hipGetLastError();
     report("segment map launch", e);
