@@ -1613,26 +1613,32 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
     // pass 1, beside the maps of the others, so a sequence takes one segment
     // more for the same number of workgroups per pass.  Pass 1 also keeps the
     // split T and P of every chunk it maps (32 KiB each) when that workspace
-    // stays within kMaxTPBytes; pass 3 then reruns those chunks without
-    // forming T and P, at about 5/8 of the cost, and the last segment, which
-    // pass 1 does not map, is about 5/8 as long as the others.  Without it a
-    // chunk with outputs costs about 8/7 of a map chunk, and the first segment
-    // is 7/8 as long instead.
+    // stays within kMaxTPBytes.  Measured per chunk, relative to a chunk with
+    // outputs: a mapped chunk that keeps T and P costs about 17/16, a chunk of
+    // pass 3 that reuses them about 11/16.  So the first segment is 17/16 as
+    // long as the middle ones and the last one (which pass 1 does not map,
+    // so pass 3 forms its T and P) gets the rest, about 11/16.  Without the
+    // workspace a chunk with outputs costs about 8/7 of a map chunk, and the
+    // first segment is 7/8 as long instead.
     auto dense_segments = [&](int64_t s0, int64_t s) { return T > s0 ? 1 + (T - s0 + s - 1) / s : 1; };
     int64_t seg0 = seg;
     bool tp = false;
     if (!cu_seqlens) {
-        int64_t seg_tp = seg;
+        int64_t seg_tp = seg, seg0_tp = seg;
         if (g_forced_segment <= 0 && T > seg) {
             const int64_t k = (T + seg - 1) / seg;  // segments at the plain length
-            const int64_t even = (8 * T + 8 * k + 4) / (8 * k + 5);
+            // T = (17/16) L + (k - 1) L + (11/16) L
+            const int64_t even = (4 * T + 4 * k + 2) / (4 * k + 3);
             seg_tp = std::max<int64_t>(kMinSegment, (even + CH - 1) / CH * CH);
+            seg0_tp = std::min<int64_t>(T, (seg_tp * 17 / 16 + CH - 1) / CH * CH);
         }
-        const int64_t nseg_tp = dense_segments(seg_tp, seg_tp);
-        tp = nseg_tp > 1 && static_cast<double>(n_seq) * nseg_tp * H * ((seg_tp + CH - 1) / CH) * TP_BYTES <=
+        const int64_t nseg_tp = dense_segments(seg0_tp, seg_tp);
+        tp = nseg_tp > 1 && static_cast<double>(n_seq) * nseg_tp * H *
+                                    ((std::max(seg0_tp, seg_tp) + CH - 1) / CH) * TP_BYTES <=
                                 static_cast<double>(kMaxTPBytes);
         if (tp) {
-            seg = seg0 = seg_tp;
+            seg = seg_tp;
+            seg0 = seg0_tp;
         } else if (g_forced_segment <= 0 && T > seg) {
             const int64_t k = (T + seg - 1) / seg;
             const int64_t even = (8 * T + 8 * k + 6) / (8 * k + 7);
