@@ -1287,10 +1287,15 @@ __global__ __launch_bounds__(NT, 1) void scan_kernel(const ScanArgs a)
 // Pass 2: entering states of segments 2.. of every sequence,
 // S_start(j+1) = M_j S_start(j) + R_j, for one 16-column slice of one
 // (sequence, head).  The 8 slices of a unit run on one XCD (they read the
-// same M_j).  fp32 on the vector ALUs.
-__global__ __launch_bounds__(256) void combine_kernel(const ScanArgs a)
+// same M_j).  fp32 matrix instructions (16x16x4, exact fp32 products, fp32
+// sums): wave w owns rows 16w..16w+15 of the slice.  The slice of S is kept in
+// LDS in accumulator layout (lane group g: rows 4g..4g+3 of a row tile); with
+// the sum index ordered so that step (t, i) of a product takes rows 16t + 4g + i,
+// a tile in accumulator layout is directly the B operand of the next product,
+// and the A operand of lane (row, g) is the float4 M[row][16t + 4g .. +3].
+__global__ __launch_bounds__(512) void combine_kernel(const ScanArgs a)
 {
-    __shared__ float sv[kDim][16];
+    __shared__ f32x4 xs[8][64];  // S slice: row tile, lane
     const int bid = blockIdx.x;
     const int slice = (bid >> 3) & 7;
     const int64_t unit = static_cast<int64_t>(bid >> 6) * 8 + (bid & 7);
@@ -1308,41 +1313,53 @@ __global__ __launch_bounds__(256) void combine_kernel(const ScanArgs a)
     }
     if (nseg < 3) return;
     const int tid = threadIdx.x;
-    const int r = tid >> 1, c8 = 8 * (tid & 1);
-    const int cbase = 16 * slice;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int col = 16 * slice + (lane & 15), g = lane >> 4;
+    const int crow = 16 * wave + 4 * g;          // accumulator rows crow..crow+3
+    const int arow = 16 * wave + (lane & 15);    // A-operand row
     {
         const float* src = a.ws_start + ((z0 + 1) * H + h) * SS;
+        f32x4 x;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int idx = tid + 256 * e;
-            sv[idx >> 4][idx & 15] = src[(idx >> 4) * kDim + cbase + (idx & 15)];
-        }
+        for (int i = 0; i < 4; ++i) x[i] = src[(crow + i) * kDim + col];
+        xs[wave][lane] = x;
     }
+    // M_j rows and R_j of the first step; each step requests the next one's
+    float4 mc[8];
+    f32x4 rc;
+    auto load = [&](int64_t jj, float4 (&m)[8], f32x4& r) {
+        const float* M = a.ws_maps + (((z0 + jj) * H + h) * 2) * SS;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) m[t] = *reinterpret_cast<const float4*>(M + arow * kDim + 16 * t + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = M[SS + (crow + i) * kDim + col];
+    };
+    load(1, mc, rc);
     __syncthreads();
     for (int64_t jj = 1; jj + 1 < nseg; ++jj) {
-        const int64_t zz = z0 + jj;
-        const float* M = a.ws_maps + ((zz * H + h) * 2) * SS;
-        const float* R = M + SS;
-        float acc[8];
+        float4 mn[8];
+        f32x4 rn;
+        if (jj + 2 < nseg) load(jj + 1, mn, rn);
+        f32x4 c = rc;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = R[r * kDim + cbase + c8 + e];
-        const float* mrow = M + r * kDim;
-        for (int k4 = 0; k4 < kDim / 4; ++k4) {
-            const float4 m4 = *reinterpret_cast<const float4*>(mrow + 4 * k4);
-            const float mk[4] = {m4.x, m4.y, m4.z, m4.w};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] += mk[kk] * sv[4 * k4 + kk][c8 + e];
+        for (int t = 0; t < 8; ++t) {
+            const f32x4 b = xs[t][lane];
+            c = __builtin_amdgcn_mfma_f32_16x16x4f32(mc[t].x, b[0], c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x4f32(mc[t].y, b[1], c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x4f32(mc[t].z, b[2], c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x4f32(mc[t].w, b[3], c, 0, 0, 0);
         }
-        __syncthreads();  // every thread has read sv
-        float* dst = a.ws_start + ((zz + 1) * H + h) * SS;
+        __syncthreads();  // every wave has read the slice
+        float* dst = a.ws_start + ((z0 + jj + 1) * H + h) * SS;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            dst[r * kDim + cbase + c8 + e] = acc[e];
-            sv[r][c8 + e] = acc[e];
-        }
+        for (int i = 0; i < 4; ++i) dst[(crow + i) * kDim + col] = c[i];
+        xs[wave][lane] = c;
         __syncthreads();
+        if (jj + 2 < nseg) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) mc[t] = mn[t];
+            rc = rn;
+        }
     }
 }
 
@@ -1733,7 +1750,7 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
     report("segment map launch", e);
     if (e == hipSuccess) {
         const dim3 cgrid(static_cast<unsigned>((units + 7) / 8 * 64));
-        hipLaunchKernelGGL(combine_kernel, cgrid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(combine_kernel, cgrid, dim3(512), 0, stream, a);
         e = hipGetLastError();
         report("segment combine launch", e);
     }
@@ -1782,7 +1799,7 @@ hipError_t launch_segment_states(const void* k, const void* v, const void* beta,
     report("segment map launch", e);
     if (e != hipSuccess) return e;
     const int64_t units = n_seq * H;
-    hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>((units + 7) / 8 * 64)), dim3(256),
+    hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>((units + 7) / 8 * 64)), dim3(512),
                        0, stream, a);
     e = hipGetLastError();
     report("segment combine launch", e);
