@@ -36,6 +36,7 @@ from ._binding import (  # noqa: F401
     kda_prefill,
     kda_prefill_raw,
     kda_set_prefill_segment,
+    kda_set_prefill_tp_limit,
     kda_varlen_backward,
     kda_varlen_prefill,
     kda_varlen_prefill_raw,
@@ -47,4 +48,4 @@ __all__ = ["kda_prefill", "kda_varlen_prefill", "kda_decode_step", "kda_prefill_
            "kda_varlen_prefill_raw", "kda_decode_step_raw", "kda_decode_tokens",
            "kda_decode_step_slots",
            "kda_varlen_prefill_slots", "kda_backward", "kda_varlen_backward",
-           "kda_set_prefill_segment", "KDAError", "load_library"]
+           "kda_set_prefill_segment", "kda_set_prefill_tp_limit", "KDAError", "load_library"]

@@ -23,7 +23,7 @@ STATUS_NAMES = {
 EXPORTS = ("kda_prefill", "kda_varlen_prefill", "kda_decode_step", "kda_prefill_raw",
            "kda_varlen_prefill_raw", "kda_decode_step_raw", "kda_decode_tokens",
            "kda_decode_step_slots", "kda_varlen_prefill_slots", "kda_backward",
-           "kda_varlen_backward", "kda_set_prefill_segment", "kda_status_str",
+           "kda_varlen_backward", "kda_set_prefill_segment", "kda_set_prefill_tp_limit", "kda_status_str",
            "kda_abi_version")
 
 _lock = threading.Lock()
@@ -91,6 +91,8 @@ def load_library(path: str | None = None):
         lib.kda_varlen_backward.restype = ctypes.c_int
         lib.kda_set_prefill_segment.argtypes = [i64]
         lib.kda_set_prefill_segment.restype = ctypes.c_int
+        lib.kda_set_prefill_tp_limit.argtypes = [i64]
+        lib.kda_set_prefill_tp_limit.restype = ctypes.c_int
         lib.kda_status_str.argtypes = [ctypes.c_int]
         lib.kda_status_str.restype = ctypes.c_char_p
         lib.kda_abi_version.argtypes = []
@@ -306,6 +308,12 @@ def kda_set_prefill_segment(tokens: int) -> None:
     """Force the prefill segment length (a multiple of 64), or 0 for automatic."""
     lib = load_library()
     _check(lib, "kda_set_prefill_segment", lib.kda_set_prefill_segment(int(tokens)))
+
+
+def kda_set_prefill_tp_limit(nbytes: int) -> None:
+    """Largest T/P workspace (bytes) one dense prefill call may use; 0 turns the reuse off."""
+    lib = load_library()
+    _check(lib, "kda_set_prefill_tp_limit", lib.kda_set_prefill_tp_limit(int(nbytes)))
 
 
 def kda_decode_step(q, k, v, beta, log_alpha, state, *, out=None, _fn="kda_decode_step"):

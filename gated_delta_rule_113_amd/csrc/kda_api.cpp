@@ -347,6 +347,13 @@ kda_status kda_set_prefill_segment(int64_t tokens)
     return KDA_OK;
 }
 
+kda_status kda_set_prefill_tp_limit(int64_t bytes)
+{
+    if (bytes < 0) return KDA_ERR_SHAPE;
+    kda::set_prefill_tp_limit(bytes);
+    return KDA_OK;
+}
+
 const char* kda_status_str(kda_status status)
 {
     switch (status) {

@@ -114,5 +114,6 @@ hipError_t launch_segment_states(const void* k, const void* v, const void* beta,
 // Tokens per segment for the chunked prefill (a positive multiple of 64), or
 // 0 to choose it from the problem size and the number of CUs.
 void set_prefill_segment(int64_t tokens);
+void set_prefill_tp_limit(int64_t bytes);
 
 }  // namespace kda

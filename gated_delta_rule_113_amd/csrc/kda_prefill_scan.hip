@@ -1533,7 +1533,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* cu, int64_t n
 // ---------------- host side
 
 constexpr int64_t kMinSegment = 1024;
-constexpr int64_t kMaxTPBytes = int64_t(8) << 30;  // largest T/P workspace of one dense call
+int64_t g_tp_limit = int64_t(8) << 30;  // largest T/P workspace of one dense call (kda_set_prefill_tp_limit)
 int64_t g_forced_segment = 0;  // tokens per segment forced by kda_set_prefill_segment (0 = automatic)
 std::mutex g_pool_mutex;
 hipMemPool_t g_pools[64] = {};
@@ -1589,6 +1589,8 @@ hipMemPool_t workspace_pool(int dev)
 
 void set_prefill_segment(int64_t tokens) { g_forced_segment = tokens; }
 
+void set_prefill_tp_limit(int64_t bytes) { g_tp_limit = bytes; }
+
 hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, const void* beta,
                                const float* log_alpha, const int32_t* cu_seqlens, int64_t n_seq,
                                int64_t T, int64_t T_total, int64_t H,
@@ -1630,7 +1632,7 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
     // pass 1, beside the maps of the others, so a sequence takes one segment
     // more for the same number of workgroups per pass.  Pass 1 also keeps the
     // split T and P of every chunk it maps (32 KiB each) when that workspace
-    // stays within kMaxTPBytes.  Measured per chunk, relative to a chunk with
+    // stays within g_tp_limit.  Measured per chunk, relative to a chunk with
     // outputs: a mapped chunk that keeps T and P costs about 17/16, a chunk of
     // pass 3 that reuses them about 11/16.  So the first segment is 17/16 as
     // long as the middle ones and the last one (which pass 1 does not map,
@@ -1652,7 +1654,7 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
         const int64_t nseg_tp = dense_segments(seg0_tp, seg_tp);
         tp = nseg_tp > 1 && static_cast<double>(n_seq) * nseg_tp * H *
                                     ((std::max(seg0_tp, seg_tp) + CH - 1) / CH) * TP_BYTES <=
-                                static_cast<double>(kMaxTPBytes);
+                                static_cast<double>(g_tp_limit);
         if (tp) {
             seg = seg_tp;
             seg0 = seg0_tp;

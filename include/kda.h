@@ -307,6 +307,19 @@ kda_status kda_varlen_backward(const void *q, const void *k, const void *v, cons
  */
 kda_status kda_set_prefill_segment(int64_t tokens);
 
+/*
+ * Second knob of the bf16 dense prefill (process-wide, like the one above).
+ * When a dense sequence is cut into segments, pass 1 (which builds the
+ * segment maps) also keeps the split UT transform T = (I + Diag(beta) A)^-1
+ * and query-key matrix P of every chunk it maps, 32 KiB per chunk and head,
+ * and pass 3 reuses them instead of forming them again.  That workspace comes
+ * from the same stream-ordered pool as the rest and is used only while one
+ * call needs at most `bytes` of it (default 8 GiB; 0 turns it off, and the
+ * first segment is then made shorter instead).  Results do not depend on it
+ * beyond rounding.  bytes < 0 is KDA_ERR_SHAPE.
+ */
+kda_status kda_set_prefill_tp_limit(int64_t bytes);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char *kda_status_str(kda_status status);
 

@@ -41,7 +41,8 @@ def test_exports_match_header(lib):
                         "kda_prefill_raw", "kda_varlen_prefill_raw", "kda_decode_step_raw",
                         "kda_decode_tokens", "kda_decode_step_slots", "kda_varlen_prefill_slots",
                         "kda_backward", "kda_varlen_backward",
-                        "kda_set_prefill_segment", "kda_status_str", "kda_abi_version"}
+                        "kda_set_prefill_segment", "kda_set_prefill_tp_limit", "kda_status_str",
+                        "kda_abi_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", kda._binding.LIBRARY],
                          capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r" T (kda_\w+)", out))
@@ -253,3 +254,6 @@ def test_prefill_segment_knob(lib):
     assert lib.kda_set_prefill_segment(0) == OK
     assert lib.kda_set_prefill_segment(100) == SHAPE
     assert lib.kda_set_prefill_segment(-64) == SHAPE
+    assert lib.kda_set_prefill_tp_limit(0) == OK
+    assert lib.kda_set_prefill_tp_limit(-1) == SHAPE
+    assert lib.kda_set_prefill_tp_limit(8 << 30) == OK

@@ -63,6 +63,32 @@ def test_dense_automatic_shorter_first_segment():
     check("dense automatic segments", rel_err_vectors(o, o_ref), rel_err_states(S, S_ref))
 
 
+@pytest.fixture
+def no_tp():
+    """Turn the T/P reuse of the dense prefill off for one test."""
+    kda.kda_set_prefill_tp_limit(0)
+    yield
+    kda.kda_set_prefill_tp_limit(8 << 30)
+
+
+def test_dense_automatic_without_tp_workspace(no_tp):
+    """Without the T/P workspace the automatic lengths at B=2, H=8, T=4096 are
+    896 (first segment, with outputs in pass 1), three of 1024 and 128, and
+    every pass-3 segment forms its own T and P."""
+    inp = ki.dense_prefill(43, B=2, T=4096, H=8, gated=True, initial_state=True)
+    o, S = _dense(inp, device())
+    o_ref, S_ref = oracle.prefill(*inp.widened(), inp.initial_state)
+    check("dense automatic segments, no T/P reuse", rel_err_vectors(o, o_ref), rel_err_states(S, S_ref))
+
+
+def test_dense_forced_segments_without_tp_workspace(segment, no_tp):
+    inp = ki.dense_prefill(44, B=2, T=500, H=3, gated=True, initial_state=True)
+    segment(64)
+    o, S = _dense(inp, device())
+    o_ref, S_ref = oracle.prefill(*inp.widened(), inp.initial_state)
+    check("dense segmented seg=64, no T/P reuse", rel_err_vectors(o, o_ref), rel_err_states(S, S_ref))
+
+
 def test_dense_segmented_zero_initial_state(segment):
     inp = ki.dense_prefill(41, B=1, T=700, H=2, gated=True)
     segment(64)
