@@ -1640,9 +1640,12 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
     // workspace a chunk with outputs costs about 8/7 of a map chunk, and the
     // first segment is 7/8 as long instead.
     auto dense_segments = [&](int64_t s0, int64_t s) { return T > s0 ? 1 + (T - s0 + s - 1) / s : 1; };
-    int64_t seg0 = seg;
+    const int64_t seg_base = seg;
+    int64_t seg0 = seg, nseg_dense = 1, tp_chunks = 0;
     bool tp = false;
-    if (!cu_seqlens) {
+    auto plan_dense = [&](bool allow_tp) {
+        seg = seg0 = seg_base;
+        tp = false;
         int64_t seg_tp = seg, seg0_tp = seg;
         if (g_forced_segment <= 0 && T > seg) {
             const int64_t k = (T + seg - 1) / seg;  // segments at the plain length
@@ -1652,9 +1655,9 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
             seg0_tp = std::min<int64_t>(T, (seg_tp * 17 / 16 + CH - 1) / CH * CH);
         }
         const int64_t nseg_tp = dense_segments(seg0_tp, seg_tp);
-        tp = nseg_tp > 1 && static_cast<double>(n_seq) * nseg_tp * H *
-                                    ((std::max(seg0_tp, seg_tp) + CH - 1) / CH) * TP_BYTES <=
-                                static_cast<double>(g_tp_limit);
+        tp = allow_tp && nseg_tp > 1 &&
+             static_cast<double>(n_seq) * nseg_tp * H * ((std::max(seg0_tp, seg_tp) + CH - 1) / CH) * TP_BYTES <=
+                 static_cast<double>(g_tp_limit);
         if (tp) {
             seg = seg_tp;
             seg0 = seg0_tp;
@@ -1664,9 +1667,10 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
             seg = std::max<int64_t>(kMinSegment, (even + CH - 1) / CH * CH);
             seg0 = std::min<int64_t>(seg, (seg * 7 / 8 + CH - 1) / CH * CH);
         }
-    }
-    const int64_t nseg_dense = dense_segments(seg0, seg);
-    const int64_t tp_chunks = tp ? (std::max(seg0, seg) + CH - 1) / CH : 0;
+        nseg_dense = dense_segments(seg0, seg);
+        tp_chunks = tp ? (std::max(seg0, seg) + CH - 1) / CH : 0;
+    };
+    if (!cu_seqlens) plan_dense(true);
     const int64_t longest_bound = cu_seqlens ? T_total : T;
     const dim3 block(NT);
 
@@ -1682,26 +1686,37 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
     // twice its length over the segment length).
     int64_t n_segs = 0, slots = 0;
     size_t ws_bytes = 0, plan_bytes = 0;
-    if (cu_seqlens ? longest_bound > seg_min : nseg_dense > 1) {
-        n_segs = cu_seqlens ? n_seq + (T_total + seg_min - 1) / seg_min : n_seq * nseg_dense;
-        slots = cu_seqlens ? std::min<int64_t>(n_segs, 2 * ((T_total + seg_min - 1) / seg_min))
-                           : n_segs;
-        plan_bytes = cu_seqlens ? ((2 * static_cast<size_t>(n_seq) + 3 + static_cast<size_t>(n_segs)) *
-                                       4 + 255) / 256 * 256
-                                : 0;
-        ws_bytes = plan_bytes + static_cast<size_t>(slots) * H * 3 * SS * sizeof(float) +
-                   static_cast<size_t>(n_segs) * H * tp_chunks * TP_BYTES;
-    }
+    auto size_workspace = [&]() {
+        n_segs = slots = 0;
+        ws_bytes = plan_bytes = 0;
+        if (cu_seqlens ? longest_bound > seg_min : nseg_dense > 1) {
+            n_segs = cu_seqlens ? n_seq + (T_total + seg_min - 1) / seg_min : n_seq * nseg_dense;
+            slots = cu_seqlens ? std::min<int64_t>(n_segs, 2 * ((T_total + seg_min - 1) / seg_min))
+                               : n_segs;
+            plan_bytes = cu_seqlens ? ((2 * static_cast<size_t>(n_seq) + 3 + static_cast<size_t>(n_segs)) *
+                                           4 + 255) / 256 * 256
+                                    : 0;
+            ws_bytes = plan_bytes + static_cast<size_t>(slots) * H * 3 * SS * sizeof(float) +
+                       static_cast<size_t>(n_segs) * H * tp_chunks * TP_BYTES;
+        }
+    };
+    size_workspace();
     void* ws = nullptr;
-    if (ws_bytes) {
-        hipMemPool_t pool = workspace_pool(dev);
-        if (pool) {
+    hipMemPool_t pool = ws_bytes ? workspace_pool(dev) : nullptr;
+    if (pool) {
+        e = hipMallocFromPoolAsync(&ws, ws_bytes, pool, stream);
+        if (e != hipSuccess && tp) {
+            // without the T/P images the workspace is a few MB per head
+            report("hipMallocFromPoolAsync (with T/P)", e);
+            (void)hipGetLastError();
+            plan_dense(false);
+            size_workspace();
             e = hipMallocFromPoolAsync(&ws, ws_bytes, pool, stream);
-            if (e != hipSuccess) {
-                report("hipMallocFromPoolAsync", e);
-                (void)hipGetLastError();
-                ws = nullptr;  // fall back to one segment per sequence
-            }
+        }
+        if (e != hipSuccess) {
+            report("hipMallocFromPoolAsync", e);
+            (void)hipGetLastError();
+            ws = nullptr;  // fall back to one segment per sequence
         }
     }
     if (!ws) {
