@@ -564,9 +564,10 @@ __device__ __forceinline__ void scan_segment(const ScanArgs& a, char* sm, bool p
         }
 
         // ======== 0: stage the chunk; scan of the log2-decay in registers.
-        //             With outputs, the previous chunk's output tile is
-        //             written out from LDS first.
-        if (OUT && ci > 0) store_o(c0 - CH, CH, tid);
+        //             With outputs, the previous chunk's output tile is then
+        //             written out from LDS (after the staging, whose waits for
+        //             the prefetched inputs then need not count the stores or
+        //             wait for the T/P loads issued after the prefetch).
         {
             if (a.raw) {
 #pragma unroll
@@ -644,6 +645,7 @@ __device__ __forceinline__ void scan_segment(const ScanArgs& a, char* sm, bool p
                 if (bm & (0x0001000100010001ull << (4 * rbi + 3))) flags |= 1 << rbi;
             if (lane == 0) at<int>(sm, OFF_UNSAFE + 4 * wave) = flags;
         }
+        if (OUT && ci > 0) store_o(c0 - CH, CH, tid);
         __syncthreads();
 
         // ======== 3: A and P tiles.  Wave (rb, kh) covers row block rb over the
