@@ -327,9 +327,11 @@ struct ScanArgs {
     int64_t short_max;  // sequences of at most this many tokens are skipped (0: none)
     float* ws_maps;   // [slots][H][2][d_k][d_v]: M and R of each segment but the last
     float* ws_start;  // [slots][H][d_k][d_v]: entering state of each segment
-    char* ws_tp;      // dense, or null: [segments][H][tp_chunks] LDS images (32 KiB) of the split
-                      // T and P of every chunk of the segments that pass 1 maps; pass 3 reuses them
-    int64_t tp_chunks;
+    char* ws_tp;      // or null: LDS images (32 KiB) of the split T and P of every chunk of the
+                      // segments that pass 1 maps, for pass 3 to reuse; block (chunk id, head), with
+                      // chunk id = (first row of the segment) / 64 + sequence + chunk within the segment
+                      // (segments start at multiples of 64 within their sequence, so ids are unique
+                      // and below rows / 64 + sequences + 1)
 };
 
 namespace {
@@ -554,7 +556,8 @@ __device__ __forceinline__ void scan_segment(const ScanArgs& a, char* sm, bool p
         const int cq = tid & 31;                 // natural channel quad
         const int pq4 = perm(4 * cq);            // its position in the permuted order
         // this chunk's T/P image in the workspace: 512 threads x 4 x 16 bytes
-        char* tpg = TP ? a.ws_tp + ((wz * H + h) * a.tp_chunks + ci) * static_cast<int64_t>(TP_BYTES) : nullptr;
+        char* tpg = TP ? a.ws_tp + (((sg.row0 + sg.begin) / CH + sg.n + ci) * H + h) * static_cast<int64_t>(TP_BYTES)
+                       : nullptr;
         uint4 tp0, tp1, tp2, tp3;  // (named registers: an array here ended up in scratch memory)
         if (LOADTP) {
             tp0 = *gat<const uint4>(tpg, 16 * tid);
@@ -1643,8 +1646,11 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
     // first segment is 7/8 as long instead.
     auto dense_segments = [&](int64_t s0, int64_t s) { return T > s0 ? 1 + (T - s0 + s - 1) / s : 1; };
     const int64_t seg_base = seg;
-    int64_t seg0 = seg, nseg_dense = 1, tp_chunks = 0;
+    int64_t seg0 = seg, nseg_dense = 1, tp_blocks = 0;
     bool tp = false;
+    // T/P blocks: one per (chunk id, head), ids below rows / 64 + sequences + 1
+    const int64_t tp_ids = rows / CH + n_seq + 1;
+    const bool tp_fits = static_cast<double>(tp_ids) * H * TP_BYTES <= static_cast<double>(g_tp_limit);
     auto plan_dense = [&](bool allow_tp) {
         seg = seg0 = seg_base;
         tp = false;
@@ -1656,10 +1662,7 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
             seg_tp = std::max<int64_t>(kMinSegment, (even + CH - 1) / CH * CH);
             seg0_tp = std::min<int64_t>(T, (seg_tp * 17 / 16 + CH - 1) / CH * CH);
         }
-        const int64_t nseg_tp = dense_segments(seg0_tp, seg_tp);
-        tp = allow_tp && nseg_tp > 1 &&
-             static_cast<double>(n_seq) * nseg_tp * H * ((std::max(seg0_tp, seg_tp) + CH - 1) / CH) * TP_BYTES <=
-                 static_cast<double>(g_tp_limit);
+        tp = allow_tp && tp_fits && dense_segments(seg0_tp, seg_tp) > 1;
         if (tp) {
             seg = seg_tp;
             seg0 = seg0_tp;
@@ -1670,7 +1673,7 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
             seg0 = std::min<int64_t>(seg, (seg * 7 / 8 + CH - 1) / CH * CH);
         }
         nseg_dense = dense_segments(seg0, seg);
-        tp_chunks = tp ? (std::max(seg0, seg) + CH - 1) / CH : 0;
+        tp_blocks = tp ? tp_ids : 0;
     };
     if (!cu_seqlens) plan_dense(true);
     const int64_t longest_bound = cu_seqlens ? T_total : T;
@@ -1699,10 +1702,15 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
                                            4 + 255) / 256 * 256
                                     : 0;
             ws_bytes = plan_bytes + static_cast<size_t>(slots) * H * 3 * SS * sizeof(float) +
-                       static_cast<size_t>(n_segs) * H * tp_chunks * TP_BYTES;
+                       static_cast<size_t>(tp_blocks) * H * TP_BYTES;
         }
     };
     size_workspace();
+    if (cu_seqlens && n_segs > 0 && tp_fits) {
+        tp = true;  // packed input: pass 1 maps the first segments too, and keeps their T/P as well
+        tp_blocks = tp_ids;
+        size_workspace();
+    }
     void* ws = nullptr;
     hipMemPool_t pool = ws_bytes ? workspace_pool(dev) : nullptr;
     if (pool) {
@@ -1711,7 +1719,12 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
             // without the T/P images the workspace is a few MB per head
             report("hipMallocFromPoolAsync (with T/P)", e);
             (void)hipGetLastError();
-            plan_dense(false);
+            if (cu_seqlens) {
+                tp = false;
+                tp_blocks = 0;
+            } else {
+                plan_dense(false);
+            }
             size_workspace();
             e = hipMallocFromPoolAsync(&ws, ws_bytes, pool, stream);
         }
@@ -1759,7 +1772,6 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
     a.ws_start = a.ws_maps + static_cast<size_t>(slots) * H * 2 * SS;
     if (tp) {
         a.ws_tp = reinterpret_cast<char*>(a.ws_start + static_cast<size_t>(slots) * H * SS);
-        a.tp_chunks = tp_chunks;
     }
 
     const dim3 grid(static_cast<unsigned>(n_segs * H));
