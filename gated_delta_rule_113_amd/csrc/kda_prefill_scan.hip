@@ -22,11 +22,15 @@
 // entering state to S_end = M S_start + R with M (d_k x d_k) the product of
 // its chunk transitions.  A long sequence is cut into segments; pass 1 runs
 // each segment but the last on the augmented state [M | R] (started from
-// [I | 0], or from the true initial state for the first segment), pass 2
-// composes the segment maps in order to get every segment's true entering
-// state, pass 3 reruns every segment from its entering state and writes the
-// outputs and the final state.  Sequences no longer than a segment take pass
-// 3 only; those of at most 16 tokens are left to the token-by-token kernel.
+// [I | 0]; packed input: the first segment builds R only, from the true
+// initial state; dense input: the first segment instead runs with outputs,
+// since its entering state is known), pass 2 composes the segment maps in
+// order to get every segment's true entering state, pass 3 reruns every
+// segment not yet done from its entering state and writes the outputs and the
+// final state.  While pass 1 maps a chunk it also keeps the chunk's split T and
+// P in a workspace, so that pass 3 loads them instead of forming them again.
+// Sequences no longer than a segment take pass 3 only; those of at most 16
+// tokens are left to the token-by-token kernel.
 // For packed input a one-workgroup plan kernel, on the device where the
 // lengths are, picks the segment length, numbers the segments (and workspace
 // slots, for sequences cut in two or more) and orders them longest first.
