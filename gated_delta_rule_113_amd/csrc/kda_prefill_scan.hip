@@ -1641,11 +1641,13 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
     // pass 1, beside the maps of the others, so a sequence takes one segment
     // more for the same number of workgroups per pass.  Pass 1 also keeps the
     // split T and P of every chunk it maps (32 KiB each) when that workspace
-    // stays within g_tp_limit.  Measured per chunk, relative to a chunk with
-    // outputs: a mapped chunk that keeps T and P costs about 17/16, a chunk of
-    // pass 3 that reuses them about 11/16.  So the first segment is 17/16 as
-    // long as the middle ones and the last one (which pass 1 does not map,
-    // so pass 3 forms its T and P) gets the rest, about 11/16.  Without the
+    // stays within g_tp_limit.  A pass-3 chunk that reuses them costs about
+    // 3/5 of one that forms them, so the last segment (which pass 1 does not
+    // map) gets about 3/5 of the others' length; the first segment, with
+    // outputs in pass 1, costs about as much per chunk as a mapped one and is
+    // as long.  (Timed: 32 heads x 32,768 tokens, equal segments of 3,840 and
+    // a last one of 2,048 beat a first segment 17/16 as long by 1%, and
+    // lengths 64 tokens shorter or longer by 5% and 3%.)  Without the
     // workspace a chunk with outputs costs about 8/7 of a map chunk, and the
     // first segment is 7/8 as long instead.
     auto dense_segments = [&](int64_t s0, int64_t s) { return T > s0 ? 1 + (T - s0 + s - 1) / s : 1; };
@@ -1661,10 +1663,10 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
         int64_t seg_tp = seg, seg0_tp = seg;
         if (g_forced_segment <= 0 && T > seg) {
             const int64_t k = (T + seg - 1) / seg;  // segments at the plain length
-            // T = (17/16) L + (k - 1) L + (11/16) L
-            const int64_t even = (4 * T + 4 * k + 2) / (4 * k + 3);
+            // T = k L + (3/5) L
+            const int64_t even = (5 * T + 5 * k + 2) / (5 * k + 3);
             seg_tp = std::max<int64_t>(kMinSegment, (even + CH - 1) / CH * CH);
-            seg0_tp = std::min<int64_t>(T, (seg_tp * 17 / 16 + CH - 1) / CH * CH);
+            seg0_tp = seg_tp;
         }
         tp = allow_tp && tp_fits && dense_segments(seg0_tp, seg_tp) > 1;
         if (tp) {

@@ -54,9 +54,9 @@ def test_dense_segmented(segment, seg, T):
 
 def test_dense_automatic_shorter_first_segment():
     """Automatic segment lengths for dense input: at B=2, H=8, T=4096 on 256
-    compute units the first segment of each sequence has 1088 tokens and runs
-    with outputs in pass 1, then come two of 1024 whose T and P pass 3 reuses
-    and a last one of 960; resumed (non-zero) initial states."""
+    compute units each sequence is cut into four segments of 1024 tokens; the
+    first runs with outputs in pass 1, pass 3 reuses the T and P of the next
+    two and forms those of the last; resumed (non-zero) initial states."""
     inp = ki.dense_prefill(42, B=2, T=4096, H=8, gated=True, initial_state=True)
     o, S = _dense(inp, device())
     o_ref, S_ref = oracle.prefill(*inp.widened(), inp.initial_state)
