@@ -662,6 +662,10 @@ __device__ __forceinline__ void scan_segment(const ScanArgs& a, char* sm, bool p
         f32x4 accA[4], accP[4];
         float qk = 0.f;
         if constexpr (!LOADTP) {
+            // Row blocks 2 and 3 have the most tiles; each shares its SIMD with
+            // the wave of row block 1 or 0, which then issues in their gaps
+            // (2% faster per call than equal priority, timed alternately).
+            if (rb >= 2) __builtin_amdgcn_s_setprio(1);
             int fl = 0;
 #pragma unroll
             for (int w = 0; w < NW; ++w) fl |= at<int>(sm, OFF_UNSAFE + 4 * w);
@@ -788,6 +792,7 @@ __device__ __forceinline__ void scan_segment(const ScanArgs& a, char* sm, bool p
                     at<f32x4>(sm, OFF_TF + (r * N_LD + 16 * ib + 4 * g4) * 4) = accP[ib];
                 }
             }
+            __builtin_amdgcn_s_setprio(0);
             __syncthreads();
         }
 
