@@ -1386,12 +1386,14 @@ __global__ __launch_bounds__(512) void combine_kernel(const ScanArgs a)
 // but the last of each sequence, all exactly L tokens long: it takes
 // ceil(segments * H / CUs) rounds of L tokens.  Pass 3 runs every segment and
 // takes about the larger of its work spread over the CUs and its longest
-// segment.  A pass-1 chunk costs about 0.9 of a pass-3 chunk.  Short segments
-// balance the CUs but add pass-1 work (every boundary is one more map); the
-// lengths are only known here, on the device.
+// segment.  Relative to a pass-3 chunk that forms T and P, a pass-1 chunk
+// costs about 0.9, or 1.07 when it also keeps T and P (tp), and a pass-3
+// chunk that reuses them 0.6.  Short segments balance the CUs but add pass-1
+// work (every boundary is one more map); the lengths are only known here, on
+// the device.
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* cu, int64_t n_seq,
                                                     int64_t seg_max, int64_t seg_min, int64_t H,
-                                                    int64_t n_cu, int32_t* seg_first,
+                                                    int64_t n_cu, int tp, int32_t* seg_first,
                                                     int32_t* ws_first, int32_t* seg_order)
 {
     constexpr int kCand = 6;
@@ -1447,8 +1449,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* cu, int64_t n
             double sum1 = 0.0;
             for (int w = 0; w < 16; ++w) sum1 += work1[c][w];
             const double p1 = ceil(sum1 * H / n_cu) * static_cast<double>(cand[c]);
-            const double p3 = fmax(per_cu3, static_cast<double>(cand[c] < lg ? cand[c] : lg));
-            const double est = 0.9 * p1 + p3;
+            // with T/P reuse the mapped tokens (sum1 segments of L) cost 0.6 in pass 3
+            const double saved3 = tp ? 0.4 * sum1 * static_cast<double>(cand[c]) * H / n_cu : 0.0;
+            const double p3 = fmax(per_cu3 - saved3, static_cast<double>(cand[c] < lg ? cand[c] : lg));
+            const double est = (tp ? 1.07 : 0.9) * p1 + p3;
             if (c == 0 || est < best) {
                 best = est;
                 pick = cand[c];
@@ -1769,7 +1773,7 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
         a.ws_first = a.seg_first + n_seq + 2;                     // [n_seq + 1]
         a.seg_order = a.ws_first + n_seq + 1;                     // [n_segs]
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens, n_seq, seg,
-                           seg_min, H, static_cast<int64_t>(cu_count(dev)),
+                           seg_min, H, static_cast<int64_t>(cu_count(dev)), tp ? 1 : 0,
                            const_cast<int32_t*>(a.seg_first), const_cast<int32_t*>(a.ws_first),
                            const_cast<int32_t*>(a.seg_order));
         e = hipGetLastError();
