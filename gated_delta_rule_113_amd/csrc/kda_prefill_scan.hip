@@ -999,13 +999,6 @@ __device__ __forceinline__ void scan_segment(const ScanArgs& a, char* sm, bool p
         __syncthreads();
 
         // ======== 8: state products (each wave its own columns)
-        if (STORETP) {
-            // T and P are complete (and only read from here on): their image
-            // goes to the workspace for pass 3
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                *gat<uint4>(tpg, 16 * (tid + NT * j)) = at<uint4>(sm, OFF_T_HI + 16 * (tid + NT * j));
-        }
         // Ke^T into R1 (N and T are dead); read only after the next barrier
         {
             const int tp = perm(4 * tq);
@@ -1108,6 +1101,14 @@ __device__ __forceinline__ void scan_segment(const ScanArgs& a, char* sm, bool p
                     if (pass == 1) make_y(s);
                     __builtin_amdgcn_sched_barrier(0);
                 }
+            }
+            if (STORETP) {
+                // T and P are complete and only read from here on: their image
+                // goes to the workspace for pass 3 (here, after the X pass,
+                // rather than before it: 2% per call)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    *gat<uint4>(tpg, 16 * (tid + NT * j)) = at<uint4>(sm, OFF_T_HI + 16 * (tid + NT * j));
             }
             if (!OUT) {
 #pragma unroll
