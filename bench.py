@@ -71,7 +71,10 @@ def parse():
     ap.add_argument("--eager", action="store_true",
                     help="time direct decode calls instead of a replayed HIP graph of them")
     ap.add_argument("--prefill-T", type=int, default=32768)
-    ap.add_argument("--prefill-reps", type=int, default=5)
+    ap.add_argument("--prefill-reps", type=int, default=10)
+    ap.add_argument("--prefill-warmup", type=int, default=30,
+                    help="untimed prefill calls first: right after the decode section the first "
+                         "~30 calls run up to 25%% slower while the GPU settles")
     ap.add_argument("--cpu-steps", type=int, default=1024,
                     help="decode steps of the workload the CPU oracle runs (all heads)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -392,7 +395,8 @@ def main():
         pla = up(pin.log_alpha, False)
         po = torch.empty((1, T, H, D), dtype=torch.float32, device=dev)
         ps = torch.empty((1, H, D, D), dtype=torch.float32, device=dev)
-        kda.kda_prefill(pq, pk, pv, pb, pla, None, out=po, final_state=ps)
+        for _ in range(max(1, args.prefill_warmup)):
+            kda.kda_prefill(pq, pk, pv, pb, pla, None, out=po, final_state=ps)
         torch.cuda.synchronize()
         times = []
         for _ in range(args.prefill_reps):
@@ -413,6 +417,8 @@ def main():
             "workload": f"chunked KDA prefill: B=1, H={H}, T={T}, d_k=d_v=128, bf16 q/k/v/beta, "
                         "fp32 log_alpha/state/o, gated channel mix, zero initial state",
             "ms": pms,
+            "timing": f"median of {args.prefill_reps} calls, each between two HIP events, after "
+                      f"{max(1, args.prefill_warmup)} untimed calls",
             "tokens_per_s": T / (pms / 1e3),
             "head_tokens_per_s": T * H / (pms / 1e3),
             "roofline": {"bound": "hbm", "achieved": pgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -428,7 +434,8 @@ def main():
         if args.no_raw:
             del pq, pk, pv, pb, pla, po, ps
         else:
-            time_raw_prefill(kda, torch, np, stream, args.prefill_reps, pq, pk, pv, pb, pla, po, ps, pms, T, result)
+            time_raw_prefill(kda, torch, np, stream, args.prefill_reps, args.prefill_warmup, pq, pk, pv, pb, pla,
+                             po, ps, pms, T, result)
             del pq, pk, pv, pb, pla, po, ps
 
     # ---------------- backward pass (secondary) ---------------------------
@@ -460,12 +467,13 @@ def main():
     return 0
 
 
-def time_raw_prefill(kda, torch, np, stream, reps, pq, pk, pv, pb, pla, po, ps, pms, T, result):
+def time_raw_prefill(kda, torch, np, stream, reps, warmup, pq, pk, pv, pb, pla, po, ps, pms, T, result):
     """The chunked prefill on raw projections: the same resident buffers read as
     raw q, k, v, beta logits and gate logits (the kernels take no value-dependent
     branch, so any values time alike); the unit-norm, sigmoid and softplus
     preparation runs inside the staging."""
-    kda.kda_prefill_raw(pq, pk, pv, pb, pla, None, out=po, final_state=ps)
+    for _ in range(max(1, warmup // 3)):
+        kda.kda_prefill_raw(pq, pk, pv, pb, pla, None, out=po, final_state=ps)
     torch.cuda.synchronize()
     rtimes = []
     for _ in range(reps):
