@@ -112,12 +112,18 @@ def test_dense_segmented_aliased_state(segment):
           rel_err_states(S.cpu().numpy(), S_ref))
 
 
-def test_varlen_segmented(segment):
+@pytest.mark.parametrize("tp", [True, False])
+def test_varlen_segmented(segment, tp):
     """Packed sequences of lengths 0, 1, 63, 64, 65, 300, 0, 129, 520 with
-    segments of 128 tokens: some sequences have one segment, some five."""
+    segments of 128 tokens: some sequences have one segment, some five; with
+    and without the T/P reuse."""
     inp = ki.varlen_prefill(43, [0, 1, 63, 64, 65, 300, 0, 129, 520], H=3)
     segment(128)
-    o, S = _varlen(inp, device())
+    kda.kda_set_prefill_tp_limit(8 << 30 if tp else 0)
+    try:
+        o, S = _varlen(inp, device())
+    finally:
+        kda.kda_set_prefill_tp_limit(8 << 30)
     q, k, v, b, la = inp.widened()
     o_ref, S_ref = oracle.varlen_prefill(q, k, v, b, la, inp.cu_seqlens, inp.initial_state)
     check("varlen segmented", rel_err_vectors(o[0], o_ref), rel_err_states(S, S_ref))
