@@ -297,9 +297,11 @@ kda_status kda_varlen_backward(const void *q, const void *k, const void *v, cons
  * context-parallel" in "Kimi K3 -- the architecture and infrastructure,
  * explained", section "Kimi Delta Attention: the load-bearing choice").
  * 0 (the default) picks the length from the problem size and the number of
- * compute units; for dense input the first segment of each sequence is then
- * about 7/8 as long as the others, since it runs with its outputs while the
- * other segments build their maps; for packed input a small planning kernel then chooses, on
+ * compute units; for dense input the first segment of each sequence runs
+ * with its outputs while the other segments build their maps, so a sequence
+ * takes one segment more, and the last segment is made shorter (about 3/5 of
+ * the others with the T/P reuse below, else the first is 7/8 as long); for
+ * packed input a small planning kernel then chooses, on
  * the device where the sequence lengths are, between that length and the
  * powers of two below it (down to an eighth of it).  tokens must be 0 or a
  * positive multiple of 64, else KDA_ERR_SHAPE.  Results do not depend on it
@@ -308,15 +310,17 @@ kda_status kda_varlen_backward(const void *q, const void *k, const void *v, cons
 kda_status kda_set_prefill_segment(int64_t tokens);
 
 /*
- * Second knob of the bf16 dense prefill (process-wide, like the one above).
- * When a dense sequence is cut into segments, pass 1 (which builds the
+ * Second knob of the bf16 prefill (process-wide, like the one above).  When
+ * a sequence (dense or packed) is cut into segments, pass 1 (which builds the
  * segment maps) also keeps the split UT transform T = (I + Diag(beta) A)^-1
  * and query-key matrix P of every chunk it maps, 32 KiB per chunk and head,
- * and pass 3 reuses them instead of forming them again.  That workspace comes
- * from the same stream-ordered pool as the rest and is used only while one
- * call needs at most `bytes` of it (default 8 GiB; 0 turns it off, and the
- * first segment is then made shorter instead).  Results do not depend on it
- * beyond rounding.  bytes < 0 is KDA_ERR_SHAPE.
+ * and pass 3 reuses them instead of forming them again.  That workspace (one
+ * block per 64 rows of the input plus one per sequence, per head) comes from
+ * the same stream-ordered pool as the rest and is used only while one call
+ * needs at most `bytes` of it (default 8 GiB; 0 turns it off, and for dense
+ * input the first segment is then made shorter instead).  If the pool cannot
+ * provide it, the call goes without it.  Results do not depend on it beyond
+ * rounding.  bytes < 0 is KDA_ERR_SHAPE.
  */
 kda_status kda_set_prefill_tp_limit(int64_t bytes);
 
