@@ -52,7 +52,7 @@ def test_dense_segmented(segment, seg, T):
     check(f"dense segmented seg={seg} T={T}", rel_err_vectors(o, o_ref), rel_err_states(S, S_ref))
 
 
-def test_dense_automatic_shorter_first_segment():
+def test_dense_automatic_segments():
     """Automatic segment lengths for dense input: at B=2, H=8, T=4096 on 256
     compute units each sequence is cut into four segments of 1024 tokens; the
     first runs with outputs in pass 1, pass 3 reuses the T and P of the next
