@@ -65,7 +65,7 @@ def load(path: str | None = None):
         lib.kda_oracle_run.argtypes = [
             ctypes.c_int64, i64p, i64p, ctypes.c_int64,
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
-            fp, fp, fp, fp, fp, dp, dp, dp, ctypes.c_int]
+            fp, fp, fp, fp, fp, dp, dp, dp, dp, ctypes.c_int]
         lib.kda_oracle_run.restype = ctypes.c_int
         lib.kda_oracle_prepare.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                            fp, fp, fp, fp, ctypes.c_int, fp, fp, fp, fp]
@@ -99,13 +99,14 @@ def _ptr(a, ctype):
 
 
 def run_rows(q, k, v, beta, log_alpha, row0, length, row_step, initial_state=None,
-             n_threads: int = 0, lib=None):
+             n_threads: int = 0, lib=None, with_magnitude: bool = False):
     """Core call on token-row addressing.
 
     q, k, log_alpha: [rows, H, dk]; v: [rows, H, dv]; beta: [rows, H].
     Token t of sequence n is row ``row0[n] + t * row_step``.
     Returns (o [rows, H, dv] float64 -- NaN where no token was visited,
-    final_state [n_seq, H, dk, dv] float64).
+    final_state [n_seq, H, dk, dv] float64), and with ``with_magnitude`` also
+    m [rows, H, dv] = |S_t|^T |q_t|, the magnitude of each read-out's terms.
     """
     lib = lib or load()
     q = _f32(q, "q"); k = _f32(k, "k"); v = _f32(v, "v")
@@ -133,34 +134,40 @@ def run_rows(q, k, v, beta, log_alpha, row0, length, row_step, initial_state=Non
             raise ValueError(f"initial_state must be {(n_seq, H, dk, dv)}")
         s0p = _ptr(s0, ctypes.c_double)
     o = np.full((rows, H, dv), np.nan, dtype=np.float64)
+    mag = np.full((rows, H, dv), np.nan, dtype=np.float64) if with_magnitude else None
     s_final = np.empty((n_seq, H, dk, dv), dtype=np.float64)
     rc = lib.kda_oracle_run(n_seq, _ptr(row0, ctypes.c_int64), _ptr(length, ctypes.c_int64),
                             int(row_step), H, dk, dv,
                             _ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float),
                             _ptr(v, ctypes.c_float), _ptr(beta, ctypes.c_float),
                             _ptr(log_alpha, ctypes.c_float), s0p,
-                            _ptr(o, ctypes.c_double), _ptr(s_final, ctypes.c_double),
-                            int(n_threads))
+                            _ptr(o, ctypes.c_double),
+                            None if mag is None else _ptr(mag, ctypes.c_double),
+                            _ptr(s_final, ctypes.c_double), int(n_threads))
     if rc != 0:
         raise RuntimeError(f"kda_oracle_run failed with code {rc}")
-    return o, s_final
+    return (o, s_final, mag) if with_magnitude else (o, s_final)
 
 
-def prefill(q, k, v, beta, log_alpha, initial_state=None, n_threads: int = 0, lib=None):
+def prefill(q, k, v, beta, log_alpha, initial_state=None, n_threads: int = 0, lib=None,
+            with_magnitude: bool = False):
     """Dense batch: q, k, log_alpha [B, T, H, dk]; v [B, T, H, dv]; beta [B, T, H].
 
-    Returns (o [B, T, H, dv], final_state [B, H, dk, dv]), float64.
+    Returns (o [B, T, H, dv], final_state [B, H, dk, dv]), float64 (with
+    ``with_magnitude`` also the read-out magnitudes, shaped like o).
     """
     q = np.asarray(q)
     B, T, H, dk = q.shape
     dv = np.asarray(v).shape[-1]
     row0 = np.arange(B, dtype=np.int64) * T
     length = np.full(B, T, dtype=np.int64)
-    o, s = run_rows(np.reshape(q, (B * T, H, dk)), np.reshape(k, (B * T, H, dk)),
-                    np.reshape(v, (B * T, H, dv)), np.reshape(beta, (B * T, H)),
-                    np.reshape(log_alpha, (B * T, H, dk)), row0, length, 1,
-                    initial_state, n_threads, lib)
-    return o.reshape(B, T, H, dv), s
+    r = run_rows(np.reshape(q, (B * T, H, dk)), np.reshape(k, (B * T, H, dk)),
+                 np.reshape(v, (B * T, H, dv)), np.reshape(beta, (B * T, H)),
+                 np.reshape(log_alpha, (B * T, H, dk)), row0, length, 1,
+                 initial_state, n_threads, lib, with_magnitude)
+    if with_magnitude:
+        return r[0].reshape(B, T, H, dv), r[1], r[2].reshape(B, T, H, dv)
+    return r[0].reshape(B, T, H, dv), r[1]
 
 
 def _backward_rows(q, k, v, beta, log_alpha, d_o, row0, length, initial_state, d_final_state,
@@ -241,7 +248,7 @@ def varlen_backward(q, k, v, beta, log_alpha, d_o, cu_seqlens, initial_state=Non
 
 
 def varlen_prefill(q, k, v, beta, log_alpha, cu_seqlens, initial_state=None,
-                   n_threads: int = 0, lib=None):
+                   n_threads: int = 0, lib=None, with_magnitude: bool = False):
     """Packed batch: q, k, log_alpha [T_total, H, dk] (a leading 1 is allowed);
     sequence n owns rows cu_seqlens[n] .. cu_seqlens[n+1]-1.
 
@@ -255,7 +262,7 @@ def varlen_prefill(q, k, v, beta, log_alpha, cu_seqlens, initial_state=None,
             or cu[-1] != q.shape[0]:
         raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at T_total")
     return run_rows(q, k, v, beta, log_alpha, cu[:-1], np.diff(cu), 1,
-                    initial_state, n_threads, lib)
+                    initial_state, n_threads, lib, with_magnitude)
 
 
 def decode_chain(q, k, v, beta, log_alpha, state, n_threads: int = 0, lib=None):

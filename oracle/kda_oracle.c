@@ -30,6 +30,10 @@
  *       S   = S + k_t u^T                  correct [A][D]
  *       o_t = S^T q_t                      read-out from the updated state
  *     final state <- S
+ * Optionally also, per token, the magnitude of the read-out's terms,
+ * m_t = |S_t|^T |q_t| (elementwise absolute values): the scale against which
+ * rounding in a finite-precision evaluation of o_t = S_t^T q_t is measured
+ * (o_t can be far smaller than m_t when its terms cancel).
  * i.e. S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T.
  * Readings where the pages are silent: decay comes before the erase/write;
  * beta is one scalar per (token, head) and alpha the per-channel gate; no
@@ -74,7 +78,7 @@ static void run_unit(int64_t n, int64_t h, const int64_t *row0, const int64_t *l
                      int64_t row_step, int64_t H, int64_t dk, int64_t dv,
                      const float *q, const float *k, const float *v,
                      const float *beta, const float *log_alpha,
-                     const double *s0, double *o, double *s_final,
+                     const double *s0, double *o, double *o_mag, double *s_final,
                      double *S, double *a, double *p, double *u)
 {
     const int64_t unit = n * H + h;
@@ -113,6 +117,14 @@ static void run_unit(int64_t n, int64_t h, const int64_t *row0, const int64_t *l
         for (int64_t j = 0; j < dv; ++j) ot[j] = 0.0;
         for (int64_t i = 0; i < dk; ++i)
             for (int64_t j = 0; j < dv; ++j) ot[j] += S[i * dv + j] * (double)qt[i];
+
+        /* magnitude of the read-out's terms: m = |S|^T |q| */
+        if (o_mag) {
+            double *mt = o_mag + (row * H + h) * dv;
+            for (int64_t j = 0; j < dv; ++j) mt[j] = 0.0;
+            for (int64_t i = 0; i < dk; ++i)
+                for (int64_t j = 0; j < dv; ++j) mt[j] += fabs(S[i * dv + j]) * fabs((double)qt[i]);
+        }
     }
     memcpy(s_final + unit * dk * dv, S, (size_t)(dk * dv) * sizeof(double));
 }
@@ -125,6 +137,7 @@ static void run_unit(int64_t n, int64_t h, const int64_t *row0, const int64_t *l
  *   beta            : rows x H       (fp32)
  *   s0              : [n_seq, H, dk, dv] fp64, or NULL for zeros
  *   o               : rows x H x dv  fp64, written for every token visited
+ *   o_mag           : rows x H x dv  fp64 (|S_t|^T |q_t| per token), or NULL
  *   s_final         : [n_seq, H, dk, dv] fp64
  *   n_threads       : <= 0 means the OpenMP default
  * Returns 0 on success, -1 on bad sizes, -2 on allocation failure.
@@ -133,7 +146,7 @@ int kda_oracle_run(int64_t n_seq, const int64_t *row0, const int64_t *len, int64
                    int64_t H, int64_t dk, int64_t dv,
                    const float *q, const float *k, const float *v,
                    const float *beta, const float *log_alpha,
-                   const double *s0, double *o, double *s_final, int n_threads)
+                   const double *s0, double *o, double *o_mag, double *s_final, int n_threads)
 {
     if (n_seq < 0 || H <= 0 || dk <= 0 || dv <= 0) return -1;
     for (int64_t n = 0; n < n_seq; ++n)
@@ -158,7 +171,7 @@ int kda_oracle_run(int64_t n_seq, const int64_t *row0, const int64_t *len, int64
         for (int64_t w = 0; w < units; ++w) {
             if (!ok) { failed = 1; continue; }
             run_unit(w / H, w % H, row0, len, row_step, H, dk, dv, q, k, v, beta,
-                     log_alpha, s0, o, s_final, S, a, p, u);
+                     log_alpha, s0, o, o_mag, s_final, S, a, p, u);
         }
         free(S); free(a); free(p); free(u);
     }

@@ -10,6 +10,16 @@ error is the maximum over all of them.
 A reference vector whose largest entry is below FLOOR = 1e-30 (for instance
 the read-out right after a log-decay of -200 with nothing written) lies below
 what an fp32 state can resolve; it is compared absolutely, |o - o_ref| <= FLOOR.
+
+Cancellation.  The read-out o_t = S_t^T q_t is a sum of d_k = 128 terms; an
+fp32 evaluation can be off by up to about d_k * 2^-24 times the magnitude of
+those terms, m_t = |S_t|^T |q_t|, whatever the order of summation.  When the
+terms cancel (e.g. the first token from a zero state gives o = beta (k.q) v,
+and k.q can be 1e-6 of sum |k_i q_i|), o_t is far below m_t and no fp32
+evaluation resolves it relative to its own norm.  Where the oracle supplies
+m_t, the per-vector measure divides by max(||o_ref||_inf, ||m_t||_inf *
+d_k 2^-24 / TOL): the tolerance then never asks for more than fp32 rounding of
+the terms allows, and is unchanged for every vector whose terms do not cancel.
 """
 from __future__ import annotations
 
@@ -17,6 +27,7 @@ import numpy as np
 
 TOL = 2e-3
 FLOOR = 1e-30
+FP32_SUM_ERR = 128 * 2.0 ** -24   # relative rounding bound of a 128-term fp32 sum
 
 
 def torch_mod():
@@ -49,8 +60,10 @@ def upload(inp, dev):
     return out
 
 
-def rel_err_vectors(got, ref):
-    """Max over vectors (last axis) of ||got - ref||_inf / ||ref||_inf."""
+def rel_err_vectors(got, ref, mag=None):
+    """Max over vectors (last axis) of ||got - ref||_inf / ||ref||_inf; with the
+    oracle's read-out magnitudes ``mag`` the denominator is at least
+    ||mag||_inf * FP32_SUM_ERR / TOL (see the module docstring)."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
@@ -59,6 +72,8 @@ def rel_err_vectors(got, ref):
     assert np.all(np.isfinite(got)), "non-finite output"
     num = np.max(np.abs(got - ref), axis=-1)
     den = np.max(np.abs(ref), axis=-1)
+    if mag is not None:
+        den = np.maximum(den, np.max(np.abs(np.asarray(mag, np.float64)), axis=-1) * (FP32_SUM_ERR / TOL))
     tiny = den < FLOOR
     if np.any(tiny):
         assert np.all(num[tiny] <= FLOOR), "output far from a reference below the fp32 floor"
@@ -89,3 +104,34 @@ def check(name, o_err, s_err, tol=TOL):
     print(f"{name}: max rel err o={o_err:.3e} state={s_err:.3e} (tol {tol:g})", flush=True)
     assert o_err <= tol, f"{name}: output error {o_err:.3e} > {tol}"
     assert s_err <= tol, f"{name}: state error {s_err:.3e} > {tol}"
+
+
+class GroupCheck:
+    """Accumulates the error metric over groups of heads or sequences that the
+    oracle recomputes one after another (to keep host memory bounded), and
+    the oracle's wall time, then checks the maxima against the tolerance."""
+
+    def __init__(self, name):
+        self.name = name
+        self.o_err = 0.0
+        self.s_err = 0.0
+        self.oracle_s = 0.0
+        self.units = 0
+
+    def timed(self, fn, *args, **kw):
+        import time
+        t0 = time.time()
+        out = fn(*args, **kw)
+        self.oracle_s += time.time() - t0
+        return out
+
+    def add(self, o_err, s_err, units):
+        self.o_err = max(self.o_err, o_err)
+        self.s_err = max(self.s_err, s_err)
+        self.units += units
+
+    def finish(self, tol=TOL):
+        import oracle
+        print(f"{self.name}: oracle recomputed {self.units} (sequence, head) units in "
+              f"{self.oracle_s:.1f}s wall on {oracle.max_threads()} threads", flush=True)
+        check(self.name, self.o_err, self.s_err, tol)

@@ -85,6 +85,33 @@ def pin_bruteforce_numpy(lib=None):
             assert _rel(S[b, h], Sb) < 1e-12, ("S", b, h, _rel(S[b, h], Sb))
 
 
+def pin_readout_magnitude(lib=None):
+    """The read-out magnitudes m_t = |S_t|^T |q_t| against the states of the
+    brute-force transition-matrix products (T <= 8); and in the identity case
+    (alpha = 1, beta = 0) the closed form |S_0|^T |q_t|."""
+    q, k, v, beta, la, S0 = _random_case(3, B=2, T=6, H=2, dk=5, dv=3)
+    o, S, m = oracle.prefill(q, k, v, beta, la, S0, lib=lib, with_magnitude=True)
+    o2, S2 = oracle.prefill(q, k, v, beta, la, S0, lib=lib)
+    assert np.array_equal(o, o2) and np.array_equal(S, S2)
+    B, T, H, dk = q.shape
+    for b in range(B):
+        for h in range(H):
+            alpha = np.exp(la[b, :, h].astype(np.float64))
+            qq, kk, vv, bb = (x[b, :, h].astype(np.float64) for x in (q, k, v, beta))
+            for t in range(T):
+                _, St = _bruteforce_unit(qq[:t + 1], kk[:t + 1], vv[:t + 1], bb[:t + 1], alpha[:t + 1],
+                                         S0[b, h], 1.0, 0.0, np.matmul, np.eye(dk))
+                ref = np.abs(St).T @ np.abs(qq[t])
+                assert _rel(m[b, t, h], ref) < 1e-12, (b, h, t)
+                assert np.all(m[b, t, h] + 1e-12 >= np.abs(o[b, t, h]))
+    z = np.zeros_like(beta)
+    _, _, m0 = oracle.prefill(q, k, v, z, np.zeros_like(la), S0, lib=lib, with_magnitude=True)
+    for b in range(B):
+        for h in range(H):
+            ref = np.abs(q[b, :, h].astype(np.float64)) @ np.abs(S0[b, h])
+            assert _rel(m0[b, :, h], ref) < 1e-13
+
+
 def _fmat(a):
     return np.array([[Fraction(float(x)) for x in row] for row in a], dtype=object)
 
@@ -563,5 +590,5 @@ ALL_PINS = [
     pin_causal_linear_attention, pin_scalar_gate, pin_resume, pin_linearity,
     pin_varlen_and_layouts, pin_prepare_gates, pin_prepare_unit_vectors,
     pin_backward_finite_differences, pin_backward_identity_gate, pin_backward_gate_identity,
-    pin_backward_packing,
+    pin_backward_packing, pin_readout_magnitude,
 ]

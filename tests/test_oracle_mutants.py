@@ -55,6 +55,10 @@ MUTANTS = {
     "write_dropped": _replace("S[i * dv + j] += (double)kt[i] * u[j];", "(void)u;"),
     "write_with_query": _replace("S[i * dv + j] += (double)kt[i] * u[j];", "S[i * dv + j] += (double)qt[i] * u[j];"),
     "readout_with_key": _replace("ot[j] += S[i * dv + j] * (double)qt[i];", "ot[j] += S[i * dv + j] * (double)kt[i];"),
+    "magnitude_signed_state": _replace("mt[j] += fabs(S[i * dv + j]) * fabs((double)qt[i]);",
+                                       "mt[j] += S[i * dv + j] * fabs((double)qt[i]);"),
+    "magnitude_with_key": _replace("mt[j] += fabs(S[i * dv + j]) * fabs((double)qt[i]);",
+                                   "mt[j] += fabs(S[i * dv + j]) * fabs((double)kt[i]);"),
     "readout_before_write": lambda s: _move_before(s, "read-out", "correct"),
     "decay_after_write": lambda s: _move_after(s, "decay", "correct"),
     "decay_after_recall": lambda s: _move_after(s, "decay", "recall"),
