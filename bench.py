@@ -395,15 +395,17 @@ def main():
         pla = up(pin.log_alpha, False)
         po = torch.empty((1, T, H, D), dtype=torch.float32, device=dev)
         ps = torch.empty((1, H, D, D), dtype=torch.float32, device=dev)
+        pws = torch.empty(max(1, kda.prefill_workspace_size(1, T, H, torch.bfloat16)), dtype=torch.uint8,
+                          device=dev)
         for _ in range(max(1, args.prefill_warmup)):
-            kda.kda_prefill(pq, pk, pv, pb, pla, None, out=po, final_state=ps)
+            kda.kda_prefill(pq, pk, pv, pb, pla, None, out=po, final_state=ps, workspace=pws)
         torch.cuda.synchronize()
         times = []
         for _ in range(args.prefill_reps):
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            kda.kda_prefill(pq, pk, pv, pb, pla, None, out=po, final_state=ps)
+            kda.kda_prefill(pq, pk, pv, pb, pla, None, out=po, final_state=ps, workspace=pws)
             b.record(stream)
             torch.cuda.synchronize()
             times.append(a.elapsed_time(b))
@@ -432,11 +434,11 @@ def main():
                      "algorithmic_flops_per_launch": pflops},
         }
         if args.no_raw:
-            del pq, pk, pv, pb, pla, po, ps
+            del pq, pk, pv, pb, pla, po, ps, pws
         else:
             time_raw_prefill(kda, torch, np, stream, args.prefill_reps, args.prefill_warmup, pq, pk, pv, pb, pla,
-                             po, ps, pms, T, result)
-            del pq, pk, pv, pb, pla, po, ps
+                             po, ps, pms, T, result, pws)
+            del pq, pk, pv, pb, pla, po, ps, pws
 
     # ---------------- backward pass (secondary) ---------------------------
     if not args.no_backward:
@@ -467,20 +469,20 @@ def main():
     return 0
 
 
-def time_raw_prefill(kda, torch, np, stream, reps, warmup, pq, pk, pv, pb, pla, po, ps, pms, T, result):
+def time_raw_prefill(kda, torch, np, stream, reps, warmup, pq, pk, pv, pb, pla, po, ps, pms, T, result, pws):
     """The chunked prefill on raw projections: the same resident buffers read as
     raw q, k, v, beta logits and gate logits (the kernels take no value-dependent
     branch, so any values time alike); the unit-norm, sigmoid and softplus
     preparation runs inside the staging."""
     for _ in range(max(1, warmup // 3)):
-        kda.kda_prefill_raw(pq, pk, pv, pb, pla, None, out=po, final_state=ps)
+        kda.kda_prefill_raw(pq, pk, pv, pb, pla, None, out=po, final_state=ps, workspace=pws)
     torch.cuda.synchronize()
     rtimes = []
     for _ in range(reps):
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        kda.kda_prefill_raw(pq, pk, pv, pb, pla, None, out=po, final_state=ps)
+        kda.kda_prefill_raw(pq, pk, pv, pb, pla, None, out=po, final_state=ps, workspace=pws)
         b.record(stream)
         torch.cuda.synchronize()
         rtimes.append(a.elapsed_time(b))

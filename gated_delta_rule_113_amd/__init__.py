@@ -20,6 +20,9 @@ ABI of ``include/kda.h``); this package is its thin Python binding:
                  d_final_state=None) -> dict of gradients
     kda_varlen_backward(q, k, v, beta, log_alpha, d_o, cu_seqlens, ...)
         (gradients of a prefill in all its inputs, for training)
+    prefill_workspace_size / varlen_prefill_workspace_size /
+    backward_workspace_size -> bytes of device workspace a call needs
+        (the calls take ``workspace=``: None, "auto" or a caller-owned tensor)
 
 PyTorch is used only for device memory and the current stream.
 """
@@ -27,6 +30,10 @@ from ._binding import (  # noqa: F401
     EXPORTS,
     KDA_BF16,
     KDA_F32,
+    KDA_PLAN_FULL,
+    KDA_PLAN_SEGMENTS,
+    KDA_PLAN_UNSEGMENTED,
+    KDA_WORKSPACE_AUTO,
     KDAError,
     kda_backward,
     kda_decode_step,
@@ -36,16 +43,20 @@ from ._binding import (  # noqa: F401
     kda_prefill,
     kda_prefill_raw,
     kda_set_prefill_segment,
-    kda_set_prefill_tp_limit,
     kda_varlen_backward,
     kda_varlen_prefill,
     kda_varlen_prefill_raw,
     kda_varlen_prefill_slots,
+    backward_workspace_size,
     load_library,
+    prefill_workspace_size,
+    varlen_prefill_workspace_size,
 )
 
 __all__ = ["kda_prefill", "kda_varlen_prefill", "kda_decode_step", "kda_prefill_raw",
            "kda_varlen_prefill_raw", "kda_decode_step_raw", "kda_decode_tokens",
            "kda_decode_step_slots",
            "kda_varlen_prefill_slots", "kda_backward", "kda_varlen_backward",
-           "kda_set_prefill_segment", "kda_set_prefill_tp_limit", "KDAError", "load_library"]
+           "kda_set_prefill_segment", "prefill_workspace_size", "varlen_prefill_workspace_size",
+           "backward_workspace_size", "KDA_WORKSPACE_AUTO", "KDA_PLAN_FULL", "KDA_PLAN_SEGMENTS",
+           "KDA_PLAN_UNSEGMENTED", "KDAError", "load_library"]

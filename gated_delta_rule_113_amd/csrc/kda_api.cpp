@@ -1,8 +1,8 @@
-// C ABI of libkda.so (declared in include/kda.h): host-side validation, then
-// asynchronous launches on the caller's stream.  Nothing here synchronises or
-// touches device memory (the segmented prefill's workspace is taken and
-// returned in stream order by its launcher); every check happens before a
-// launch so that on error nothing is enqueued.
+// C ABI of libkda.so (declared in include/kda.h): host-side validation, the
+// choice of plan and workspace, then asynchronous launches on the caller's
+// stream.  Every check happens before a launch, so that on error nothing is
+// enqueued; nothing here synchronises, except the KDA_DEBUG precondition
+// checks.
 #include "kda.h"
 
 #include <hip/hip_runtime.h>
@@ -16,7 +16,7 @@ namespace {
 
 constexpr int64_t kMaxElems = int64_t(1) << 46;  // keeps every index product in int64
 
-bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+bool misaligned(const void* p, uintptr_t a = 16) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; }
 
 kda_status check_dtype(kda_dtype d)
 {
@@ -52,31 +52,113 @@ kda_status check_ptrs(std::initializer_list<const void*> required,
     return KDA_OK;
 }
 
+// A caller-owned workspace is `bytes` bytes at a 256-byte aligned `ws` (NULL
+// when bytes is 0); KDA_WORKSPACE_AUTO asks the library for one (ws NULL).
+kda_status check_workspace(const void* ws, int64_t bytes)
+{
+    if (bytes == KDA_WORKSPACE_AUTO) return ws ? KDA_ERR_WORKSPACE : KDA_OK;
+    if (bytes < 0) return KDA_ERR_WORKSPACE;
+    if (bytes > 0 && !ws) return KDA_ERR_NULL;
+    if (ws && misaligned(ws, 256)) return KDA_ERR_ALIGN;
+    return KDA_OK;
+}
+
 kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
+
+// An unread HIP error of the calling thread (left by an earlier call of the
+// caller's) stays for the caller to read: the call enqueues nothing.  After
+// this check, hipGetLastError() after a launch reports that launch only.
+kda_status no_pending_error()
+{
+    const hipError_t e = hipPeekAtLastError();
+    kda::report("an earlier HIP error is pending; nothing enqueued", e);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+// The current device and its compute units (the plans are sized by them).
+kda_status current_cus(int* n_cu)
+{
+    int dev = 0;
+    const hipError_t e = hipGetDevice(&dev);
+    kda::report("hipGetDevice", e);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();  // this call's own failure, reported as a status
+        return KDA_ERR_HIP;
+    }
+    *n_cu = kda::cu_count(dev);
+    return KDA_OK;
+}
+
+// KDA_DEBUG: the device-side preconditions, checked before anything else is
+// enqueued (this synchronises the stream).
+kda_status debug_check(const float* log_alpha, int64_t n_gates, bool raw, const int32_t* cu,
+                       int64_t n_seq, int64_t T_total, hipStream_t stream)
+{
+    if (!kda::debug_enabled()) return KDA_OK;
+    unsigned int bad = 0;
+    const hipError_t e =
+        kda::check_preconditions(log_alpha, n_gates, raw, cu, n_seq, T_total, stream, &bad);
+    if (e != hipSuccess) return KDA_ERR_HIP;
+    return bad ? KDA_ERR_PRECONDITION : KDA_OK;
+}
 
 // bf16 inputs take the chunked matrix-core kernel, except sequences of at most
 // kShortPrefill tokens; fp32 inputs (whose q and k are not exact in bf16) and
 // those short sequences take the register-resident token-by-token kernel.
-hipError_t launch_prefill(const void* q, const void* k, const void* v, const void* beta,
-                          const float* log_alpha, const int32_t* cu_seqlens, int64_t n_seq,
-                          int64_t T, int64_t T_total, int64_t H, const kda::StateRefs& st,
-                          float* o, kda_dtype in_dtype, bool raw, hipStream_t stream)
+bool prefill_uses_scan(kda_dtype in_dtype, bool packed, int64_t T, int64_t T_total)
 {
-    if (in_dtype != KDA_BF16)
-        return kda::launch_prefill_recurrent(q, k, v, beta, log_alpha, cu_seqlens, n_seq, T, H,
-                                             st, o, false, raw, 0, stream);
-    // bf16: short sequences token by token, the others chunked.  Each kernel
-    // skips the other's sequences (packed lengths are known on the device only).
-    const int64_t longest = cu_seqlens ? T_total : T;
-    if (longest <= kda::kShortPrefill)
-        return kda::launch_prefill_recurrent(q, k, v, beta, log_alpha, cu_seqlens, n_seq, T, H,
-                                             st, o, true, raw, 0, stream);
-    const hipError_t e = kda::launch_prefill_scan(q, k, v, beta, log_alpha, cu_seqlens, n_seq, T,
-                                                  T_total, H, st, o, raw,
-                                                  cu_seqlens ? kda::kShortPrefill : 0, stream);
-    if (e != hipSuccess || !cu_seqlens) return e;
-    return kda::launch_prefill_recurrent(q, k, v, beta, log_alpha, cu_seqlens, n_seq, T, H, st,
-                                         o, true, raw, kda::kShortPrefill, stream);
+    const int64_t longest = packed ? T_total : T;
+    return in_dtype == KDA_BF16 && longest > kda::kShortPrefill;
+}
+
+// The fastest plan whose workspace fits `bytes` (the fastest of all for
+// KDA_WORKSPACE_AUTO); the tier-2 plan needs none, so one always fits.
+kda::PrefillPlan fitting_plan(bool packed, int64_t n_seq, int64_t T, int64_t T_total, int64_t H,
+                              int n_cu, int64_t bytes)
+{
+    const int64_t forced = kda::forced_segment();
+    for (int tier = 0; tier < 2; ++tier) {
+        const kda::PrefillPlan p = kda::plan_prefill_scan(packed, n_seq, T, T_total, H, n_cu, forced, tier);
+        if (bytes == KDA_WORKSPACE_AUTO || static_cast<int64_t>(p.ws_bytes) <= bytes) return p;
+    }
+    return kda::plan_prefill_scan(packed, n_seq, T, T_total, H, n_cu, forced, 2);
+}
+
+kda_status run_prefill(const void* q, const void* k, const void* v, const void* beta,
+                       const float* log_alpha, const int32_t* cu_seqlens, int64_t n_seq, int64_t T,
+                       int64_t T_total, int64_t H, const kda::StateRefs& st, float* o,
+                       kda_dtype in_dtype, bool raw, void* workspace, int64_t workspace_bytes,
+                       hipStream_t stream)
+{
+    const bool packed = cu_seqlens != nullptr;
+    const int64_t rows = packed ? T_total : n_seq * T;
+    kda_status s;
+    if ((s = no_pending_error()) != KDA_OK) return s;
+    if ((s = debug_check(rows > 0 ? log_alpha : nullptr, rows * H * kda::kDim, raw, cu_seqlens,
+                         n_seq, T_total, stream)) != KDA_OK)
+        return s;
+    if (!prefill_uses_scan(in_dtype, packed, T, T_total))
+        return from_hip(kda::launch_prefill_recurrent(q, k, v, beta, log_alpha, cu_seqlens, n_seq, T,
+                                                      H, st, o, in_dtype == KDA_BF16, raw, 0, stream));
+    int n_cu = 0;
+    if ((s = current_cus(&n_cu)) != KDA_OK) return s;
+    const kda::PrefillPlan plan = fitting_plan(packed, n_seq, T, T_total, H, n_cu, workspace_bytes);
+    kda::StreamWorkspace lease;
+    void* ws = workspace;
+    if (workspace_bytes == KDA_WORKSPACE_AUTO && plan.ws_bytes > 0) {
+        if (lease.acquire(plan.ws_bytes, stream) != hipSuccess) return KDA_ERR_WORKSPACE;
+        ws = lease.ptr;
+    }
+    // bf16 packed: short sequences token by token, the others chunked.  Each
+    // kernel skips the other's sequences (packed lengths are on the device).
+    hipError_t e = kda::launch_prefill_scan(q, k, v, beta, log_alpha, cu_seqlens, n_seq, T, H, st, o,
+                                            raw, packed ? kda::kShortPrefill : 0, plan, ws, n_cu,
+                                            stream);
+    if (e == hipSuccess && packed)
+        e = kda::launch_prefill_recurrent(q, k, v, beta, log_alpha, cu_seqlens, n_seq, T, H, st, o,
+                                          true, raw, kda::kShortPrefill, stream);
+    const hipError_t f = lease.release();
+    return from_hip(e != hipSuccess ? e : f);
 }
 
 kda::StateRefs plain_states(const float* initial_state, float* final_state)
@@ -93,10 +175,7 @@ bool pool_too_big(int64_t n_pool, int64_t H)
     return n_pool > kMaxElems / H / (int64_t(kda::kDim) * kda::kDim);
 }
 
-kda_status prefill_impl(const void* q, const void* k, const void* v, const void* beta,
-                       const float* log_alpha, const float* initial_state, float* o,
-                       float* final_state, int64_t B, int64_t T, int64_t H, int64_t d_k,
-                       int64_t d_v, kda_dtype in_dtype, bool raw, void* stream)
+kda_status check_dense(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v, kda_dtype in_dtype)
 {
     kda_status st;
     if ((st = check_dtype(in_dtype)) != KDA_OK) return st;
@@ -105,6 +184,30 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const void*
     if (B > 0 && T > kMaxElems / B) return KDA_ERR_SHAPE;
     if ((st = check_rows(B * T, H)) != KDA_OK) return st;
     if (B > int64_t(1) << 24 || B * H > int64_t(1) << 30) return KDA_ERR_SHAPE;
+    return KDA_OK;
+}
+
+kda_status check_packed(int64_t N, int64_t T_total, int64_t H, int64_t d_k, int64_t d_v,
+                        kda_dtype in_dtype)
+{
+    kda_status st;
+    if ((st = check_dtype(in_dtype)) != KDA_OK) return st;
+    if ((st = check_dims(H, d_k, d_v)) != KDA_OK) return st;
+    if (N < 0 || T_total < 0) return KDA_ERR_SHAPE;
+    // cu_seqlens holds int32 row indices
+    if (T_total > INT32_MAX || N > int64_t(1) << 24 || N * H > int64_t(1) << 30) return KDA_ERR_SHAPE;
+    return check_rows(T_total, H);
+}
+
+kda_status prefill_impl(const void* q, const void* k, const void* v, const void* beta,
+                        const float* log_alpha, const float* initial_state, float* o,
+                        float* final_state, int64_t B, int64_t T, int64_t H, int64_t d_k,
+                        int64_t d_v, kda_dtype in_dtype, bool raw, void* workspace,
+                        int64_t workspace_bytes, void* stream)
+{
+    kda_status st;
+    if ((st = check_dense(B, T, H, d_k, d_v, in_dtype)) != KDA_OK) return st;
+    if ((st = check_workspace(workspace, workspace_bytes)) != KDA_OK) return st;
     if (B == 0) return KDA_OK;
     if (T > 0) {
         if ((st = check_ptrs({q, k, v, beta, log_alpha, o}, {initial_state, final_state})) != KDA_OK)
@@ -113,24 +216,20 @@ kda_status prefill_impl(const void* q, const void* k, const void* v, const void*
         return st;
     }
     if (T == 0 && !final_state) return KDA_OK;
-    return from_hip(launch_prefill(q, k, v, beta, log_alpha, nullptr, B, T, B * T, H,
-                                   plain_states(initial_state, final_state), o, in_dtype, raw,
-                                   static_cast<hipStream_t>(stream)));
+    return run_prefill(q, k, v, beta, log_alpha, nullptr, B, T, B * T, H,
+                       plain_states(initial_state, final_state), o, in_dtype, raw, workspace,
+                       workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 kda_status varlen_impl(const void* q, const void* k, const void* v, const void* beta,
-                              const float* log_alpha, const int32_t* cu_seqlens, int64_t N,
-                              int64_t T_total, const float* initial_state, float* o,
-                              float* final_state, int64_t H, int64_t d_k, int64_t d_v,
-                              kda_dtype in_dtype, bool raw, void* stream)
+                       const float* log_alpha, const int32_t* cu_seqlens, int64_t N,
+                       int64_t T_total, const float* initial_state, float* o, float* final_state,
+                       int64_t H, int64_t d_k, int64_t d_v, kda_dtype in_dtype, bool raw,
+                       void* workspace, int64_t workspace_bytes, void* stream)
 {
     kda_status st;
-    if ((st = check_dtype(in_dtype)) != KDA_OK) return st;
-    if ((st = check_dims(H, d_k, d_v)) != KDA_OK) return st;
-    if (N < 0 || T_total < 0) return KDA_ERR_SHAPE;
-    // cu_seqlens holds int32 row indices
-    if (T_total > INT32_MAX || N > int64_t(1) << 24 || N * H > int64_t(1) << 30) return KDA_ERR_SHAPE;
-    if ((st = check_rows(T_total, H)) != KDA_OK) return st;
+    if ((st = check_packed(N, T_total, H, d_k, d_v, in_dtype)) != KDA_OK) return st;
+    if ((st = check_workspace(workspace, workspace_bytes)) != KDA_OK) return st;
     if (N == 0) return KDA_OK;
     if (!cu_seqlens) return KDA_ERR_NULL;
     if (misaligned(cu_seqlens)) return KDA_ERR_ALIGN;
@@ -141,14 +240,14 @@ kda_status varlen_impl(const void* q, const void* k, const void* v, const void* 
         return st;
     }
     if (T_total == 0 && !final_state) return KDA_OK;
-    return from_hip(launch_prefill(q, k, v, beta, log_alpha, cu_seqlens, N, 0, T_total, H,
-                                   plain_states(initial_state, final_state), o, in_dtype, raw,
-                                   static_cast<hipStream_t>(stream)));
+    return run_prefill(q, k, v, beta, log_alpha, cu_seqlens, N, 0, T_total, H,
+                       plain_states(initial_state, final_state), o, in_dtype, raw, workspace,
+                       workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 kda_status decode_impl(const void* q, const void* k, const void* v, const void* beta,
-                           const float* log_alpha, float* state, float* o, int64_t N, int64_t H,
-                           int64_t d_k, int64_t d_v, kda_dtype in_dtype, bool raw, void* stream)
+                       const float* log_alpha, float* state, float* o, int64_t N, int64_t H,
+                       int64_t d_k, int64_t d_v, kda_dtype in_dtype, bool raw, void* stream)
 {
     kda_status st;
     if ((st = check_dtype(in_dtype)) != KDA_OK) return st;
@@ -157,9 +256,18 @@ kda_status decode_impl(const void* q, const void* k, const void* v, const void* 
     if (N > int64_t(1) << 24 || N * H > INT32_MAX) return KDA_ERR_SHAPE;
     if (N == 0) return KDA_OK;
     if ((st = check_ptrs({q, k, v, beta, log_alpha, state, o}, {})) != KDA_OK) return st;
+    if ((st = no_pending_error()) != KDA_OK) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = debug_check(log_alpha, N * H * kda::kDim, raw, nullptr, 0, 0, s)) != KDA_OK) return st;
     return from_hip(kda::launch_decode_step(q, k, v, beta, log_alpha, state, nullptr, 0, o, N * H,
-                                            H, in_dtype == KDA_BF16, raw,
-                                            static_cast<hipStream_t>(stream)));
+                                            H, in_dtype == KDA_BF16, raw, s));
+}
+
+kda_status backward_sizes(bool packed, int64_t n_seq, int64_t T, int64_t T_total, int64_t H,
+                          int64_t d_k, int64_t d_v, kda_dtype in_dtype)
+{
+    return packed ? check_packed(n_seq, T_total, H, d_k, d_v, in_dtype)
+                  : check_dense(n_seq, T, H, d_k, d_v, in_dtype);
 }
 
 kda_status backward_impl(const void* q, const void* k, const void* v, const void* beta,
@@ -167,19 +275,16 @@ kda_status backward_impl(const void* q, const void* k, const void* v, const void
                          int64_t T, int64_t T_total, const float* initial_state, const float* d_o,
                          const float* d_final_state, float* dq, float* dk, float* dv, float* dbeta,
                          float* dlog_alpha, float* d_initial_state, int64_t H, int64_t d_k,
-                         int64_t d_v, kda_dtype in_dtype, void* stream)
+                         int64_t d_v, kda_dtype in_dtype, void* workspace, int64_t workspace_bytes,
+                         void* stream)
 {
+    const bool packed = cu_seqlens != nullptr;
     kda_status st;
-    if ((st = check_dtype(in_dtype)) != KDA_OK) return st;
-    if ((st = check_dims(H, d_k, d_v)) != KDA_OK) return st;
-    if (n_seq < 0 || T < 0 || T_total < 0) return KDA_ERR_SHAPE;
-    if (cu_seqlens && T_total > INT32_MAX) return KDA_ERR_SHAPE;
-    if (!cu_seqlens && n_seq > 0 && T > kMaxElems / n_seq) return KDA_ERR_SHAPE;
-    const int64_t rows = cu_seqlens ? T_total : n_seq * T;
-    if ((st = check_rows(rows, H)) != KDA_OK) return st;
-    if (n_seq > int64_t(1) << 24 || n_seq * H > int64_t(1) << 30) return KDA_ERR_SHAPE;
+    if ((st = backward_sizes(packed, n_seq, T, T_total, H, d_k, d_v, in_dtype)) != KDA_OK) return st;
+    if ((st = check_workspace(workspace, workspace_bytes)) != KDA_OK) return st;
     if (n_seq == 0) return KDA_OK;
-    if (cu_seqlens && misaligned(cu_seqlens)) return KDA_ERR_ALIGN;
+    if (packed && misaligned(cu_seqlens)) return KDA_ERR_ALIGN;
+    const int64_t rows = packed ? T_total : n_seq * T;
     if (rows > 0) {
         if ((st = check_ptrs({q, k, v, beta, log_alpha, d_o, dq, dk, dv, dbeta, dlog_alpha},
                              {initial_state, d_final_state, d_initial_state})) != KDA_OK)
@@ -188,10 +293,63 @@ kda_status backward_impl(const void* q, const void* k, const void* v, const void
         return st;
     }
     if (rows == 0 && !d_initial_state) return KDA_OK;
-    return from_hip(kda::launch_backward(q, k, v, beta, log_alpha, d_o, cu_seqlens, n_seq, T,
-                                         T_total, H, initial_state, d_final_state, dq, dk, dv,
-                                         dbeta, dlog_alpha, d_initial_state, in_dtype == KDA_BF16,
-                                         static_cast<hipStream_t>(stream)));
+    if ((st = no_pending_error()) != KDA_OK) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = debug_check(rows > 0 ? log_alpha : nullptr, rows * H * kda::kDim, false, cu_seqlens,
+                          n_seq, T_total, s)) != KDA_OK)
+        return st;
+    int n_cu = 0;
+    if ((st = current_cus(&n_cu)) != KDA_OK) return st;
+    const kda::BackwardPlan plan =
+        kda::plan_backward(packed, n_seq, T, T_total, H, in_dtype == KDA_BF16, n_cu);
+    kda::StreamWorkspace lease;
+    void* ws = workspace;
+    if (workspace_bytes == KDA_WORKSPACE_AUTO) {
+        if (plan.ws_bytes > 0 && lease.acquire(plan.ws_bytes, s) != hipSuccess) return KDA_ERR_WORKSPACE;
+        ws = lease.ptr;
+    } else if (static_cast<int64_t>(plan.ws_bytes) > workspace_bytes) {
+        return KDA_ERR_WORKSPACE;
+    }
+    const hipError_t e = kda::launch_backward(q, k, v, beta, log_alpha, d_o, cu_seqlens, n_seq, T, H,
+                                              initial_state, d_final_state, dq, dk, dv, dbeta,
+                                              dlog_alpha, d_initial_state, in_dtype == KDA_BF16, plan,
+                                              ws, s);
+    const hipError_t f = lease.release();
+    return from_hip(e != hipSuccess ? e : f);
+}
+
+kda_status prefill_size(bool packed, int64_t n_seq, int64_t T, int64_t T_total, int64_t H,
+                        int64_t d_k, int64_t d_v, kda_dtype in_dtype, kda_plan plan, int64_t* bytes)
+{
+    if (!bytes) return KDA_ERR_NULL;
+    *bytes = 0;
+    kda_status st = packed ? check_packed(n_seq, T_total, H, d_k, d_v, in_dtype)
+                           : check_dense(n_seq, T, H, d_k, d_v, in_dtype);
+    if (st != KDA_OK) return st;
+    if (plan != KDA_PLAN_FULL && plan != KDA_PLAN_SEGMENTS && plan != KDA_PLAN_UNSEGMENTED)
+        return KDA_ERR_SHAPE;
+    if (n_seq == 0 || !prefill_uses_scan(in_dtype, packed, T, T_total)) return KDA_OK;
+    int n_cu = 0;
+    if ((st = current_cus(&n_cu)) != KDA_OK) return st;
+    *bytes = static_cast<int64_t>(kda::plan_prefill_scan(packed, n_seq, T, packed ? T_total : n_seq * T,
+                                                         H, n_cu, kda::forced_segment(),
+                                                         static_cast<int>(plan)).ws_bytes);
+    return KDA_OK;
+}
+
+kda_status backward_size(bool packed, int64_t n_seq, int64_t T, int64_t T_total, int64_t H,
+                         int64_t d_k, int64_t d_v, kda_dtype in_dtype, int64_t* bytes)
+{
+    if (!bytes) return KDA_ERR_NULL;
+    *bytes = 0;
+    kda_status st = backward_sizes(packed, n_seq, T, T_total, H, d_k, d_v, in_dtype);
+    if (st != KDA_OK) return st;
+    if (n_seq == 0) return KDA_OK;
+    int n_cu = 0;
+    if ((st = current_cus(&n_cu)) != KDA_OK) return st;
+    *bytes = static_cast<int64_t>(
+        kda::plan_backward(packed, n_seq, T, T_total, H, in_dtype == KDA_BF16, n_cu).ws_bytes);
+    return KDA_OK;
 }
 
 }  // namespace
@@ -201,39 +359,43 @@ extern "C" {
 kda_status kda_prefill(const void* q, const void* k, const void* v, const void* beta,
                        const float* log_alpha, const float* initial_state, float* o,
                        float* final_state, int64_t B, int64_t T, int64_t H, int64_t d_k,
-                       int64_t d_v, kda_dtype in_dtype, void* stream)
+                       int64_t d_v, kda_dtype in_dtype, void* workspace, int64_t workspace_bytes,
+                       void* stream)
 {
     return prefill_impl(q, k, v, beta, log_alpha, initial_state, o, final_state, B, T, H, d_k, d_v,
-                        in_dtype, false, stream);
+                        in_dtype, false, workspace, workspace_bytes, stream);
 }
 
 kda_status kda_prefill_raw(const void* q, const void* k, const void* v, const void* beta,
                            const float* log_alpha, const float* initial_state, float* o,
                            float* final_state, int64_t B, int64_t T, int64_t H, int64_t d_k,
-                           int64_t d_v, kda_dtype in_dtype, void* stream)
+                           int64_t d_v, kda_dtype in_dtype, void* workspace,
+                           int64_t workspace_bytes, void* stream)
 {
     return prefill_impl(q, k, v, beta, log_alpha, initial_state, o, final_state, B, T, H, d_k, d_v,
-                        in_dtype, true, stream);
+                        in_dtype, true, workspace, workspace_bytes, stream);
 }
 
 kda_status kda_varlen_prefill(const void* q, const void* k, const void* v, const void* beta,
                               const float* log_alpha, const int32_t* cu_seqlens, int64_t N,
                               int64_t T_total, const float* initial_state, float* o,
                               float* final_state, int64_t H, int64_t d_k, int64_t d_v,
-                              kda_dtype in_dtype, void* stream)
+                              kda_dtype in_dtype, void* workspace, int64_t workspace_bytes,
+                              void* stream)
 {
     return varlen_impl(q, k, v, beta, log_alpha, cu_seqlens, N, T_total, initial_state, o,
-                       final_state, H, d_k, d_v, in_dtype, false, stream);
+                       final_state, H, d_k, d_v, in_dtype, false, workspace, workspace_bytes, stream);
 }
 
 kda_status kda_varlen_prefill_raw(const void* q, const void* k, const void* v, const void* beta,
                                   const float* log_alpha, const int32_t* cu_seqlens, int64_t N,
                                   int64_t T_total, const float* initial_state, float* o,
                                   float* final_state, int64_t H, int64_t d_k, int64_t d_v,
-                                  kda_dtype in_dtype, void* stream)
+                                  kda_dtype in_dtype, void* workspace, int64_t workspace_bytes,
+                                  void* stream)
 {
     return varlen_impl(q, k, v, beta, log_alpha, cu_seqlens, N, T_total, initial_state, o,
-                       final_state, H, d_k, d_v, in_dtype, true, stream);
+                       final_state, H, d_k, d_v, in_dtype, true, workspace, workspace_bytes, stream);
 }
 
 kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* beta,
@@ -255,15 +417,12 @@ kda_status kda_varlen_prefill_slots(const void* q, const void* k, const void* v,
                                     int64_t T_total, float* state_pool, const int32_t* init_slots,
                                     const int32_t* final_slots, int64_t n_pool, float* o,
                                     int64_t H, int64_t d_k, int64_t d_v, kda_dtype in_dtype,
-                                    void* stream)
+                                    void* workspace, int64_t workspace_bytes, void* stream)
 {
     kda_status st;
-    if ((st = check_dtype(in_dtype)) != KDA_OK) return st;
-    if ((st = check_dims(H, d_k, d_v)) != KDA_OK) return st;
-    if (N < 0 || T_total < 0 || n_pool < 0) return KDA_ERR_SHAPE;
-    if (T_total > INT32_MAX || N > int64_t(1) << 24 || N * H > int64_t(1) << 30) return KDA_ERR_SHAPE;
-    if ((st = check_rows(T_total, H)) != KDA_OK) return st;
-    if (pool_too_big(n_pool, H)) return KDA_ERR_SHAPE;
+    if ((st = check_packed(N, T_total, H, d_k, d_v, in_dtype)) != KDA_OK) return st;
+    if (n_pool < 0 || pool_too_big(n_pool, H)) return KDA_ERR_SHAPE;
+    if ((st = check_workspace(workspace, workspace_bytes)) != KDA_OK) return st;
     if (N == 0) return KDA_OK;
     if (!cu_seqlens) return KDA_ERR_NULL;
     if (misaligned(cu_seqlens)) return KDA_ERR_ALIGN;
@@ -277,8 +436,8 @@ kda_status kda_varlen_prefill_slots(const void* q, const void* k, const void* v,
     refs.init_slots = init_slots;
     refs.fin_slots = final_slots;
     refs.n_pool = n_pool;
-    return from_hip(launch_prefill(q, k, v, beta, log_alpha, cu_seqlens, N, 0, T_total, H, refs,
-                                   o, in_dtype, false, static_cast<hipStream_t>(stream)));
+    return run_prefill(q, k, v, beta, log_alpha, cu_seqlens, N, 0, T_total, H, refs, o, in_dtype,
+                       false, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 kda_status kda_decode_step_slots(const void* q, const void* k, const void* v, const void* beta,
@@ -294,9 +453,11 @@ kda_status kda_decode_step_slots(const void* q, const void* k, const void* v, co
     if (pool_too_big(n_pool, H)) return KDA_ERR_SHAPE;
     if (N == 0) return KDA_OK;
     if ((st = check_ptrs({q, k, v, beta, log_alpha, state_pool, slots, o}, {})) != KDA_OK) return st;
+    if ((st = no_pending_error()) != KDA_OK) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = debug_check(log_alpha, N * H * kda::kDim, false, nullptr, 0, 0, s)) != KDA_OK) return st;
     return from_hip(kda::launch_decode_step(q, k, v, beta, log_alpha, state_pool, slots, n_pool, o,
-                                            N * H, H, in_dtype == KDA_BF16, false,
-                                            static_cast<hipStream_t>(stream)));
+                                            N * H, H, in_dtype == KDA_BF16, false, s));
 }
 
 kda_status kda_decode_tokens(const void* q, const void* k, const void* v, const void* beta,
@@ -311,20 +472,24 @@ kda_status kda_decode_tokens(const void* q, const void* k, const void* v, const 
     if (N > int64_t(1) << 24 || N * H > INT32_MAX) return KDA_ERR_SHAPE;
     if (N == 0) return KDA_OK;
     if ((st = check_ptrs({q, k, v, beta, log_alpha, state, o}, {n_commit})) != KDA_OK) return st;
+    if ((st = no_pending_error()) != KDA_OK) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((st = debug_check(log_alpha, N * K * H * kda::kDim, false, nullptr, 0, 0, s)) != KDA_OK)
+        return st;
     return from_hip(kda::launch_decode_tokens(q, k, v, beta, log_alpha, state, n_commit, o, N, K, H,
-                                              in_dtype == KDA_BF16,
-                                              static_cast<hipStream_t>(stream)));
+                                              in_dtype == KDA_BF16, s));
 }
 
 kda_status kda_backward(const void* q, const void* k, const void* v, const void* beta,
                         const float* log_alpha, const float* initial_state, const float* d_o,
                         const float* d_final_state, float* dq, float* dk, float* dv, float* dbeta,
                         float* dlog_alpha, float* d_initial_state, int64_t B, int64_t T, int64_t H,
-                        int64_t d_k, int64_t d_v, kda_dtype in_dtype, void* stream)
+                        int64_t d_k, int64_t d_v, kda_dtype in_dtype, void* workspace,
+                        int64_t workspace_bytes, void* stream)
 {
     return backward_impl(q, k, v, beta, log_alpha, nullptr, B, T, 0, initial_state, d_o,
                          d_final_state, dq, dk, dv, dbeta, dlog_alpha, d_initial_state, H, d_k,
-                         d_v, in_dtype, stream);
+                         d_v, in_dtype, workspace, workspace_bytes, stream);
 }
 
 kda_status kda_varlen_backward(const void* q, const void* k, const void* v, const void* beta,
@@ -332,25 +497,44 @@ kda_status kda_varlen_backward(const void* q, const void* k, const void* v, cons
                                int64_t T_total, const float* initial_state, const float* d_o,
                                const float* d_final_state, float* dq, float* dk, float* dv,
                                float* dbeta, float* dlog_alpha, float* d_initial_state, int64_t H,
-                               int64_t d_k, int64_t d_v, kda_dtype in_dtype, void* stream)
+                               int64_t d_k, int64_t d_v, kda_dtype in_dtype, void* workspace,
+                               int64_t workspace_bytes, void* stream)
 {
     if (N > 0 && !cu_seqlens) return KDA_ERR_NULL;
     return backward_impl(q, k, v, beta, log_alpha, cu_seqlens, N, 0, T_total, initial_state, d_o,
                          d_final_state, dq, dk, dv, dbeta, dlog_alpha, d_initial_state, H, d_k,
-                         d_v, in_dtype, stream);
+                         d_v, in_dtype, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_prefill_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v,
+                                      kda_dtype in_dtype, kda_plan plan, int64_t* bytes)
+{
+    return prefill_size(false, B, T, 0, H, d_k, d_v, in_dtype, plan, bytes);
+}
+
+kda_status kda_varlen_prefill_workspace_size(int64_t N, int64_t T_total, int64_t H, int64_t d_k,
+                                             int64_t d_v, kda_dtype in_dtype, kda_plan plan,
+                                             int64_t* bytes)
+{
+    return prefill_size(true, N, 0, T_total, H, d_k, d_v, in_dtype, plan, bytes);
+}
+
+kda_status kda_backward_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v,
+                                       kda_dtype in_dtype, int64_t* bytes)
+{
+    return backward_size(false, B, T, 0, H, d_k, d_v, in_dtype, bytes);
+}
+
+kda_status kda_varlen_backward_workspace_size(int64_t N, int64_t T_total, int64_t H, int64_t d_k,
+                                              int64_t d_v, kda_dtype in_dtype, int64_t* bytes)
+{
+    return backward_size(true, N, 0, T_total, H, d_k, d_v, in_dtype, bytes);
 }
 
 kda_status kda_set_prefill_segment(int64_t tokens)
 {
     if (tokens < 0 || tokens % 64 != 0 || tokens > (int64_t(1) << 40)) return KDA_ERR_SHAPE;
-    kda::set_prefill_segment(tokens);
-    return KDA_OK;
-}
-
-kda_status kda_set_prefill_tp_limit(int64_t bytes)
-{
-    if (bytes < 0) return KDA_ERR_SHAPE;
-    kda::set_prefill_tp_limit(bytes);
+    kda::set_forced_segment(tokens);
     return KDA_OK;
 }
 
@@ -361,9 +545,11 @@ const char* kda_status_str(kda_status status)
         case KDA_ERR_NULL: return "KDA_ERR_NULL: a required pointer is NULL";
         case KDA_ERR_SHAPE: return "KDA_ERR_SHAPE: a size is negative, zero where it may not be, or too large";
         case KDA_ERR_DTYPE: return "KDA_ERR_DTYPE: unknown input dtype";
-        case KDA_ERR_ALIGN: return "KDA_ERR_ALIGN: a pointer is not 16-byte aligned";
+        case KDA_ERR_ALIGN: return "KDA_ERR_ALIGN: a pointer is not 16-byte aligned (a workspace: 256-byte)";
         case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: only d_k = d_v = 128 is supported";
-        case KDA_ERR_HIP: return "KDA_ERR_HIP: the HIP runtime rejected a launch";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP: the HIP runtime rejected a launch, or an earlier HIP error is pending";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: the workspace is too small, or the library could not allocate one";
+        case KDA_ERR_PRECONDITION: return "KDA_ERR_PRECONDITION: (KDA_DEBUG) log_alpha not finite or > 0, or cu_seqlens not 0..T_total non-decreasing";
     }
     return "KDA_ERR_UNKNOWN: not a kda_status value";
 }

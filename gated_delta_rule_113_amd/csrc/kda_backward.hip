@@ -722,20 +722,50 @@ __global__ __launch_bounds__(256) void grad_combine_kernel(const BwdArgs a, cons
 
 }  // namespace
 
+BackwardPlan plan_backward(bool packed, int64_t n_seq, int64_t T, int64_t T_total, int64_t H,
+                          bool bf16, int n_cu)
+{
+    BackwardPlan p;
+    const int64_t units = n_seq * H;
+    if (units <= 0) return p;
+    // One checkpoint slot per block of kBackwardBlock tokens: dense, every
+    // sequence ceil(T / cb); packed, fewer than T_total / cb + n_seq in all.
+    const int64_t rows = packed ? T_total : n_seq * T;
+    const int64_t cb = kBackwardBlock;
+    p.n_slots = rows <= 0 ? 0 : packed ? T_total / cb + n_seq : n_seq * ((T + cb - 1) / cb);
+    // Long dense bf16 sequences that give the CUs too few (sequence, head)
+    // pairs are cut into segments of at least kBackwardMinSegment tokens: the
+    // chunked prefill's segment pass gives each segment's entering state,
+    // the gradient maps give each segment's leaving gradient, and the
+    // segments then run in parallel.
+    if (!packed && bf16 && T >= 2 * kBackwardMinSegment && units < n_cu) {
+        int64_t nseg = std::min((n_cu + units - 1) / units, T / kBackwardMinSegment);
+        const int64_t seg = ((T + nseg - 1) / nseg + 63) / 64 * 64;
+        nseg = (T + seg - 1) / seg;
+        if (nseg >= 2) {
+            p.seg = seg;
+            p.nseg = nseg;
+        }
+    }
+    const int64_t n_segs = p.seg ? n_seq * p.nseg : 0;
+    p.ck_floats = static_cast<size_t>(p.n_slots) * H * SS;
+    p.seg_floats = static_cast<size_t>(n_segs) * H * SS;
+    // checkpoints; then with segments: maps and entering states of the
+    // segment pass (3 states per slot), gradient maps (2), leaving gradients (1)
+    p.ws_bytes = (p.ck_floats + 6 * p.seg_floats) * sizeof(float);
+    return p;
+}
+
 hipError_t launch_backward(const void* q, const void* k, const void* v, const void* beta,
                            const float* log_alpha, const float* d_o, const int32_t* cu_seqlens,
-                           int64_t n_seq, int64_t T, int64_t T_total, int64_t H,
-                           const float* initial_state, const float* d_final_state, float* dq,
-                           float* dk, float* dv, float* dbeta, float* dlog_alpha,
-                           float* d_initial_state, bool bf16, hipStream_t stream)
+                           int64_t n_seq, int64_t T, int64_t H, const float* initial_state,
+                           const float* d_final_state, float* dq, float* dk, float* dv,
+                           float* dbeta, float* dlog_alpha, float* d_initial_state, bool bf16,
+                           const BackwardPlan& plan, void* ws, hipStream_t stream)
 {
     const int64_t units = n_seq * H;
     if (units <= 0) return hipSuccess;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    report("hipGetDevice", e);
-    if (e != hipSuccess) return e;
-    report("earlier HIP error (cleared)", hipGetLastError());
+    hipError_t e = hipSuccess;
 
     BwdArgs a = {};
     a.q = q;
@@ -755,56 +785,22 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const vo
     a.dbeta = dbeta;
     a.dla = dlog_alpha;
     a.ds0 = d_initial_state;
+    a.cb = kBackwardBlock;
+    a.n_slots = plan.n_slots;
+    a.ckpt = static_cast<float*>(ws);
 
-    // One checkpoint slot per block of kBackwardBlock tokens: dense, every
-    // sequence ceil(T / cb); packed, fewer than T_total / cb + n_seq in all.
-    const int64_t rows = cu_seqlens ? T_total : n_seq * T;
-    const int64_t cb = kBackwardBlock;
-    a.cb = static_cast<int>(cb);
-    a.n_slots = rows <= 0 ? 0 : cu_seqlens ? T_total / cb + n_seq : n_seq * ((T + cb - 1) / cb);
-
-    // Long dense bf16 sequences that give the CUs too few (sequence, head)
-    // pairs are cut into segments of at least kBackwardMinSegment tokens: the
-    // chunked prefill's segment pass gives each segment's entering state,
-    // the gradient maps give each segment's leaving gradient, and the
-    // segments then run in parallel.
-    int64_t seg = 0, nseg = 1;
-    if (!cu_seqlens && bf16 && T >= 2 * kBackwardMinSegment) {
-        const int64_t ncu = cu_count(dev);
-        if (units < ncu) {
-            nseg = std::min((ncu + units - 1) / units, T / kBackwardMinSegment);
-            seg = ((T + nseg - 1) / nseg + 63) / 64 * 64;
-            nseg = (T + seg - 1) / seg;
-            if (nseg < 2) seg = 0, nseg = 1;
-        }
-    }
-    const int64_t n_segs = seg ? n_seq * nseg : 0;
-    const size_t ck_floats = static_cast<size_t>(a.n_slots) * H * SS;
-    const size_t seg_floats = static_cast<size_t>(n_segs) * H * SS;
-    // checkpoints; then with segments: maps and entering states of the
-    // segment pass (3 states per slot), gradient maps (2), leaving gradients (1)
-    const size_t floats = ck_floats + 6 * seg_floats;
-
-    void* ws = nullptr;
-    if (floats > 0) {
-        hipMemPool_t pool = workspace_pool(dev);
-        if (!pool) return hipErrorOutOfMemory;
-        e = hipMallocFromPoolAsync(&ws, floats * sizeof(float), pool, stream);
-        report("hipMallocFromPoolAsync", e);
-        if (e != hipSuccess) return e;
-        a.ckpt = static_cast<float*>(ws);
-    }
     using Ly = BackwardLayout;
-    if (seg) {
-        float* scan_ws = static_cast<float*>(ws) + ck_floats;
-        float* gmaps = scan_ws + 3 * seg_floats;
-        float* ggrad = gmaps + 2 * seg_floats;
-        a.seg_len = seg;
-        a.nseg = nseg;
-        a.seg_start = scan_ws + 2 * seg_floats;
+    if (plan.seg) {
+        const int64_t n_segs = n_seq * plan.nseg;
+        float* scan_ws = static_cast<float*>(ws) + plan.ck_floats;
+        float* gmaps = scan_ws + 3 * plan.seg_floats;
+        float* ggrad = gmaps + 2 * plan.seg_floats;
+        a.seg_len = plan.seg;
+        a.nseg = plan.nseg;
+        a.seg_start = scan_ws + 2 * plan.seg_floats;
         a.seg_grad = ggrad;
-        e = launch_segment_states(k, v, beta, log_alpha, n_seq, T, H, initial_state, seg, scan_ws,
-                                  stream);
+        e = launch_segment_states(k, v, beta, log_alpha, n_seq, T, H, initial_state, plan.seg,
+                                  scan_ws, stream);
         if (e == hipSuccess) {
             hipLaunchKernelGGL((gradmap_kernel<bf16_t, Ly>), dim3(static_cast<unsigned>(2 * n_segs * H)),
                                dim3(Ly::NT), 0, stream, a, gmaps);
@@ -829,11 +825,6 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const vo
         else hipLaunchKernelGGL((backward_kernel<float, Ly>), grid, block, 0, stream, a);
         e = hipGetLastError();
         report("backward launch", e);
-    }
-    if (ws) {
-        const hipError_t f = hipFreeAsync(ws, stream);
-        report("hipFreeAsync", f);
-        if (e == hipSuccess) e = f;
     }
     return e;
 }

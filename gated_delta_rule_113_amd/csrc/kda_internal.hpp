@@ -60,14 +60,39 @@ constexpr int64_t kShortPrefill = 16;
 // Chunked prefill on bf16 matrix instructions (bf16 inputs only): 64-token
 // chunks, one workgroup per (sequence, head, segment).  Long sequences are cut
 // into segments whose affine state maps are composed in between (three
-// launches plus a workspace from a stream-ordered pool); short ones take one
-// launch.  Dense when cu_seqlens == nullptr (T rows each), packed otherwise
-// (T_total rows in all).  With short_max > 0, sequences of at most short_max
-// tokens are skipped (left to the token-by-token kernel); short_max <= 64.
+// launches plus a workspace); short ones take one launch.  Dense when
+// cu_seqlens == nullptr (T rows each), packed otherwise (T_total rows in all).
+// With short_max > 0, sequences of at most short_max tokens are skipped (left
+// to the token-by-token kernel); short_max <= 64.
+//
+// A plan fixes the segmentation and the workspace it needs.  Tier 0 is the
+// fastest plan: segments, with the split T and P of every mapped chunk kept
+// for pass 3 while those images stay under a cap; tier 1 the same segments
+// without the images; tier 2 one workgroup per (sequence, head) and no
+// workspace.  A tier that would not cut any sequence comes back as tier 2.
+struct PrefillPlan {
+    int tier = 2;
+    bool segmented = false;
+    bool tp = false;            // pass 1 keeps T and P for pass 3
+    int64_t seg = 0;            // tokens per segment (packed: the longest candidate)
+    int64_t seg0 = 0;           // dense: tokens of the first segment
+    int64_t seg_min = 0;        // packed: the shortest candidate length
+    int64_t nseg_dense = 0;     // dense: segments per sequence
+    int64_t n_segs = 0;         // segment slots of the grid
+    int64_t slots = 0;          // workspace slots (maps and entering states)
+    int64_t tp_blocks = 0;      // T/P images per head
+    size_t plan_bytes = 0;      // packed: the plan kernel's tables
+    size_t ws_bytes = 0;        // workspace bytes in all
+};
+PrefillPlan plan_prefill_scan(bool packed, int64_t n_seq, int64_t T, int64_t T_total, int64_t H,
+                              int n_cu, int64_t forced_segment, int tier);
+// ws: at least plan.ws_bytes bytes of device memory, 256-byte aligned (unused
+// when the plan is not segmented).  n_cu: compute units the plan was made for.
 hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, const void* beta,
                                const float* log_alpha, const int32_t* cu_seqlens, int64_t n_seq,
-                               int64_t T, int64_t T_total, int64_t H, const StateRefs& st,
-                               float* o, bool raw, int64_t short_max, hipStream_t stream);
+                               int64_t T, int64_t H, const StateRefs& st, float* o, bool raw,
+                               int64_t short_max, const PrefillPlan& plan, void* ws, int n_cu,
+                               hipStream_t stream);
 
 // Backward pass (gradients in q, k, v, beta, log_alpha and the initial state
 // from those in o and the final state), token by token; dense or packed as the
@@ -81,23 +106,57 @@ constexpr int kBackwardBlock = 8;
 // parallel from their entering states (the chunked prefill's segment pass) and
 // leaving gradients (per-segment gradient maps, composed in order).
 constexpr int64_t kBackwardMinSegment = 1024;
+struct BackwardPlan {
+    int64_t n_slots = 0;        // checkpoint slots per head
+    int64_t seg = 0, nseg = 1;  // dense bf16 segments in time (seg = 0: none)
+    size_t ck_floats = 0;       // checkpoint floats
+    size_t seg_floats = 0;      // floats of one per-segment state array
+    size_t ws_bytes = 0;        // workspace bytes in all
+};
+BackwardPlan plan_backward(bool packed, int64_t n_seq, int64_t T, int64_t T_total, int64_t H,
+                          bool bf16, int n_cu);
+// ws: at least plan.ws_bytes bytes of device memory, 256-byte aligned.
 hipError_t launch_backward(const void* q, const void* k, const void* v, const void* beta,
                            const float* log_alpha, const float* d_o, const int32_t* cu_seqlens,
-                           int64_t n_seq, int64_t T, int64_t T_total, int64_t H,
-                           const float* initial_state, const float* d_final_state, float* dq,
-                           float* dk, float* dv, float* dbeta, float* dlog_alpha,
-                           float* d_initial_state, bool bf16, hipStream_t stream);
+                           int64_t n_seq, int64_t T, int64_t H, const float* initial_state,
+                           const float* d_final_state, float* dq, float* dk, float* dv,
+                           float* dbeta, float* dlog_alpha, float* d_initial_state, bool bf16,
+                           const BackwardPlan& plan, void* ws, hipStream_t stream);
+
+// ---- runtime helpers (kda_runtime.cpp)
 
 // Compute units of a device (cached; 256 if the query fails).
 int cu_count(int dev);
 
-// A memory pool per device that keeps freed blocks cached, so per-call
-// workspace allocations on the stream are cheap after the first (NULL if the
-// pool cannot be created).
-hipMemPool_t workspace_pool(int dev);
+// The opt-in workspace of a call made with KDA_WORKSPACE_AUTO: taken in
+// stream order from a per-device pool whose release threshold is 0 (freed
+// blocks go back to the device at the next synchronisation) and returned in
+// stream order by release().
+struct StreamWorkspace {
+    void* ptr = nullptr;
+    hipStream_t stream = nullptr;
+    hipError_t acquire(size_t bytes, hipStream_t s);
+    hipError_t release();
+    ~StreamWorkspace() { release(); }
+};
 
 // With KDA_DEBUG set in the environment, failed HIP calls are printed to stderr.
 void report(const char* what, hipError_t e);
+bool debug_enabled();
+
+// KDA_DEBUG precondition checks (kda_checks.hip): the bits of *violations
+// name what failed.  The gates are n_gates floats (log alpha <= 0 and finite,
+// or with raw only finite); cu_seqlens, if given, n_seq + 1 offsets.  Enqueues
+// on `stream` and synchronises it.
+constexpr unsigned int kViolationGate = 1u, kViolationStart = 2u, kViolationOrder = 4u,
+                       kViolationEnd = 8u;
+hipError_t check_preconditions(const float* log_alpha, int64_t n_gates, bool raw,
+                               const int32_t* cu_seqlens, int64_t n_seq, int64_t T_total,
+                               hipStream_t stream, unsigned int* violations);
+
+// Tokens per segment forced by kda_set_prefill_segment (0 = automatic).
+int64_t forced_segment();
+void set_forced_segment(int64_t tokens);
 
 // The entering state of every segment of `seg` tokens (a positive multiple
 // of 64) of n_seq dense bf16 sequences of T tokens: pass 1 and the combine of
@@ -111,9 +170,5 @@ hipError_t launch_segment_states(const void* k, const void* v, const void* beta,
                                  const float* initial_state, int64_t seg, float* ws,
                                  hipStream_t stream);
 
-// Tokens per segment for the chunked prefill (a positive multiple of 64), or
-// 0 to choose it from the problem size and the number of CUs.
-void set_prefill_segment(int64_t tokens);
-void set_prefill_tp_limit(int64_t bytes);
 
 }  // namespace kda

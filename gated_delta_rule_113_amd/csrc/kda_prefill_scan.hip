@@ -1552,78 +1552,114 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* cu, int64_t n
 // ---------------- host side
 
 constexpr int64_t kMinSegment = 1024;
-int64_t g_tp_limit = int64_t(8) << 30;  // largest T/P workspace of one dense call (kda_set_prefill_tp_limit)
-int64_t g_forced_segment = 0;  // tokens per segment forced by kda_set_prefill_segment (0 = automatic)
-std::mutex g_pool_mutex;
-hipMemPool_t g_pools[64] = {};
-int g_cu_count[64] = {};
+// The fastest plan keeps the T/P images only while one call needs at most
+// this many bytes of them: the million-token workload (32 heads) would need
+// 17 GB of them for about 1% less time.
+constexpr double kTpCap = static_cast<double>(int64_t(8) << 30);
 
 }  // namespace
 
-void report(const char* what, hipError_t e)
+// Segment length: enough segments to give every CU about one segment of the
+// total work, never shorter than kMinSegment tokens (or the forced length).
+//
+// Dense input: the first segment of each sequence runs with outputs in pass
+// 1, beside the maps of the others, so a sequence takes one segment more for
+// the same number of workgroups per pass.  Pass 1 also keeps the split T and
+// P of every chunk it maps (32 KiB each) in the fastest plan.  A pass-3 chunk
+// that reuses them costs about 3/5 of one that forms them, so the last
+// segment (which pass 1 does not map) gets about 3/5 of the others' length;
+// the first segment, with outputs in pass 1, costs about as much per chunk as
+// a mapped one and is as long.  (Timed: 32 heads x 32,768 tokens, equal
+// segments of 3,840 and a last one of 2,048 beat a first segment 17/16 as
+// long by 1%, and lengths 64 tokens shorter or longer by 5% and 3%.)  Without
+// the images a chunk with outputs costs about 8/7 of a map chunk, and the
+// first segment is 7/8 as long instead.
+//
+// Packed input: the plan kernel picks the length on the device, between seg
+// and seg_min; grid and workspace are sized for the shortest candidate.
+// Workspace slots: dense, one per segment; packed, only the segments of
+// sequences cut in two or more, fewer than 2 * T_total / seg_min of them
+// (such a sequence is longer than a segment, so its count is below twice its
+// length over the segment length).
+PrefillPlan plan_prefill_scan(bool packed, int64_t n_seq, int64_t T, int64_t T_total, int64_t H,
+                              int n_cu, int64_t forced, int tier)
 {
-    static const bool on = std::getenv("KDA_DEBUG") != nullptr;
-    if (on && e != hipSuccess) std::fprintf(stderr, "kda: %s: %s\n", what, hipGetErrorString(e));
-}
-
-int cu_count(int dev)
-{
-    std::lock_guard<std::mutex> lk(g_pool_mutex);
-    if (dev < 0 || dev >= 64) return 256;
-    if (!g_cu_count[dev]) {
-        int c = 0;
-        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
-            c = 256;
-        g_cu_count[dev] = c;
+    PrefillPlan p;
+    p.tier = 2;
+    if (n_seq <= 0 || H <= 0 || tier >= 2) return p;
+    const int64_t rows = packed ? T_total : n_seq * T;
+    int64_t seg = forced;
+    if (seg <= 0) {
+        const int64_t per_cu = (rows * H + n_cu - 1) / n_cu;
+        seg = std::max<int64_t>(kMinSegment, (per_cu + CH - 1) / CH * CH);
     }
-    return g_cu_count[dev];
-}
-
-hipMemPool_t workspace_pool(int dev)
-{
-    std::lock_guard<std::mutex> lk(g_pool_mutex);
-    if (dev < 0 || dev >= 64) return nullptr;
-    if (!g_pools[dev]) {
-        hipMemPoolProps props = {};
-        props.allocType = hipMemAllocationTypePinned;
-        props.location.type = hipMemLocationTypeDevice;
-        props.location.id = dev;
-        hipMemPool_t p = nullptr;
-        hipError_t e = hipMemPoolCreate(&p, &props);
-        if (e != hipSuccess) {
-            report("hipMemPoolCreate", e);
-            (void)hipGetLastError();
-            return nullptr;
+    // T/P blocks: one per (chunk id, head), ids below rows / 64 + sequences + 1
+    const int64_t tp_ids = rows / CH + n_seq + 1;
+    const bool tp_ok = tier == 0 && static_cast<double>(tp_ids) * H * TP_BYTES <= kTpCap;
+    int64_t seg0 = seg, seg_min = seg, nseg_dense = 1, n_segs = 0, slots = 0;
+    bool tp = false;
+    size_t plan_bytes = 0;
+    if (!packed) {
+        auto dense_segments = [&](int64_t s0, int64_t s) {
+            return T > s0 ? 1 + (T - s0 + s - 1) / s : int64_t(1);
+        };
+        int64_t seg_tp = seg, seg0_tp = seg;
+        if (forced <= 0 && T > seg) {
+            const int64_t k = (T + seg - 1) / seg;  // segments at the plain length
+            // T = k L + (3/5) L
+            const int64_t even = (5 * T + 5 * k + 2) / (5 * k + 3);
+            seg_tp = std::max<int64_t>(kMinSegment, (even + CH - 1) / CH * CH);
+            seg0_tp = seg_tp;
         }
-        uint64_t keep = UINT64_MAX;
-        e = hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep);
-        if (e != hipSuccess) {
-            report("hipMemPoolSetAttribute", e);
-            (void)hipGetLastError();
+        tp = tp_ok && dense_segments(seg0_tp, seg_tp) > 1;
+        if (tp) {
+            seg = seg_tp;
+            seg0 = seg0_tp;
+        } else if (forced <= 0 && T > seg) {
+            const int64_t k = (T + seg - 1) / seg;
+            const int64_t even = (8 * T + 8 * k + 6) / (8 * k + 7);
+            seg = std::max<int64_t>(kMinSegment, (even + CH - 1) / CH * CH);
+            seg0 = std::min<int64_t>(seg, (seg * 7 / 8 + CH - 1) / CH * CH);
         }
-        g_pools[dev] = p;
+        nseg_dense = dense_segments(seg0, seg);
+        if (nseg_dense < 2) return p;
+        n_segs = slots = n_seq * nseg_dense;
+        seg_min = seg;
+    } else {
+        if (forced <= 0) seg_min = std::max<int64_t>(kMinSegment, (seg / 8 + CH - 1) / CH * CH);
+        if (T_total <= seg_min) return p;  // no sequence is longer than a segment
+        const int64_t per_min = (T_total + seg_min - 1) / seg_min;
+        n_segs = n_seq + per_min;
+        slots = std::min<int64_t>(n_segs, 2 * per_min);
+        // seg_first [n_seq + 2], ws_first [n_seq + 1], seg_order [n_segs]
+        plan_bytes = ((2 * static_cast<size_t>(n_seq) + 3 + static_cast<size_t>(n_segs)) * 4 + 255) /
+                     256 * 256;
+        tp = tp_ok;
     }
-    return g_pools[dev];
+    p.tier = tp ? 0 : 1;
+    p.segmented = true;
+    p.tp = tp;
+    p.seg = seg;
+    p.seg0 = seg0;
+    p.seg_min = seg_min;
+    p.nseg_dense = packed ? 0 : nseg_dense;
+    p.n_segs = n_segs;
+    p.slots = slots;
+    p.plan_bytes = plan_bytes;
+    p.tp_blocks = tp ? tp_ids : 0;
+    p.ws_bytes = plan_bytes + static_cast<size_t>(slots) * H * 3 * SS * sizeof(float) +
+                 static_cast<size_t>(p.tp_blocks) * H * TP_BYTES;
+    return p;
 }
-
-void set_prefill_segment(int64_t tokens) { g_forced_segment = tokens; }
-
-void set_prefill_tp_limit(int64_t bytes) { g_tp_limit = bytes; }
 
 hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, const void* beta,
                                const float* log_alpha, const int32_t* cu_seqlens, int64_t n_seq,
-                               int64_t T, int64_t T_total, int64_t H,
-                               const StateRefs& st, float* o, bool raw, int64_t short_max,
+                               int64_t T, int64_t H, const StateRefs& st, float* o, bool raw,
+                               int64_t short_max, const PrefillPlan& plan, void* ws, int n_cu,
                                hipStream_t stream)
 {
     const int64_t units = n_seq * H;
     if (units <= 0) return hipSuccess;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    report("hipGetDevice", e);
-    if (e != hipSuccess) return e;
-    report("earlier HIP error (cleared)", hipGetLastError());
-
     ScanArgs a = {};
     a.q = static_cast<const bf16_t*>(q);
     a.k = static_cast<const bf16_t*>(k);
@@ -1638,178 +1674,60 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
     a.o = o;
     a.raw = raw ? 1 : 0;
     a.short_max = short_max > 0 ? short_max : -1;  // -1: no sequence is skipped (lengths are >= 0)
-
-    // Segment length: enough segments to give every CU about one segment of
-    // the total work, never shorter than kMinSegment tokens.
-    const int64_t rows = cu_seqlens ? T_total : n_seq * T;
-    int64_t seg = g_forced_segment;
-    if (seg <= 0) {
-        const int64_t per_cu = (rows * H + cu_count(dev) - 1) / cu_count(dev);
-        seg = std::max<int64_t>(kMinSegment, (per_cu + CH - 1) / CH * CH);
-    }
-    // Dense input: the first segment of each sequence runs with outputs in
-    // pass 1, beside the maps of the others, so a sequence takes one segment
-    // more for the same number of workgroups per pass.  Pass 1 also keeps the
-    // split T and P of every chunk it maps (32 KiB each) when that workspace
-    // stays within g_tp_limit.  A pass-3 chunk that reuses them costs about
-    // 3/5 of one that forms them, so the last segment (which pass 1 does not
-    // map) gets about 3/5 of the others' length; the first segment, with
-    // outputs in pass 1, costs about as much per chunk as a mapped one and is
-    // as long.  (Timed: 32 heads x 32,768 tokens, equal segments of 3,840 and
-    // a last one of 2,048 beat a first segment 17/16 as long by 1%, and
-    // lengths 64 tokens shorter or longer by 5% and 3%.)  Without the
-    // workspace a chunk with outputs costs about 8/7 of a map chunk, and the
-    // first segment is 7/8 as long instead.
-    auto dense_segments = [&](int64_t s0, int64_t s) { return T > s0 ? 1 + (T - s0 + s - 1) / s : 1; };
-    const int64_t seg_base = seg;
-    int64_t seg0 = seg, nseg_dense = 1, tp_blocks = 0;
-    bool tp = false;
-    // T/P blocks: one per (chunk id, head), ids below rows / 64 + sequences + 1
-    const int64_t tp_ids = rows / CH + n_seq + 1;
-    const bool tp_fits = static_cast<double>(tp_ids) * H * TP_BYTES <= static_cast<double>(g_tp_limit);
-    auto plan_dense = [&](bool allow_tp) {
-        seg = seg0 = seg_base;
-        tp = false;
-        int64_t seg_tp = seg, seg0_tp = seg;
-        if (g_forced_segment <= 0 && T > seg) {
-            const int64_t k = (T + seg - 1) / seg;  // segments at the plain length
-            // T = k L + (3/5) L
-            const int64_t even = (5 * T + 5 * k + 2) / (5 * k + 3);
-            seg_tp = std::max<int64_t>(kMinSegment, (even + CH - 1) / CH * CH);
-            seg0_tp = seg_tp;
-        }
-        tp = allow_tp && tp_fits && dense_segments(seg0_tp, seg_tp) > 1;
-        if (tp) {
-            seg = seg_tp;
-            seg0 = seg0_tp;
-        } else if (g_forced_segment <= 0 && T > seg) {
-            const int64_t k = (T + seg - 1) / seg;
-            const int64_t even = (8 * T + 8 * k + 6) / (8 * k + 7);
-            seg = std::max<int64_t>(kMinSegment, (even + CH - 1) / CH * CH);
-            seg0 = std::min<int64_t>(seg, (seg * 7 / 8 + CH - 1) / CH * CH);
-        }
-        nseg_dense = dense_segments(seg0, seg);
-        tp_blocks = tp ? tp_ids : 0;
-    };
-    if (!cu_seqlens) plan_dense(true);
-    const int64_t longest_bound = cu_seqlens ? T_total : T;
     const dim3 block(NT);
+    hipError_t e;
 
-    // Packed input with the automatic length: the plan kernel picks the
-    // segment length on the device, between seg and seg_min; grid and
-    // workspace are sized for the shortest candidate.
-    const bool plan_on_device = cu_seqlens && g_forced_segment <= 0;
-    const int64_t seg_min =
-        plan_on_device ? std::max<int64_t>(kMinSegment, (seg / 8 + CH - 1) / CH * CH) : seg;
-    // Workspace slots: dense, one per segment; packed, only the segments of
-    // sequences cut in two or more, fewer than 2 * T_total / seg_min of them
-    // (such a sequence is longer than a segment, so its count is below
-    // twice its length over the segment length).
-    int64_t n_segs = 0, slots = 0;
-    size_t ws_bytes = 0, plan_bytes = 0;
-    auto size_workspace = [&]() {
-        n_segs = slots = 0;
-        ws_bytes = plan_bytes = 0;
-        if (cu_seqlens ? longest_bound > seg_min : nseg_dense > 1) {
-            n_segs = cu_seqlens ? n_seq + (T_total + seg_min - 1) / seg_min : n_seq * nseg_dense;
-            slots = cu_seqlens ? std::min<int64_t>(n_segs, 2 * ((T_total + seg_min - 1) / seg_min))
-                               : n_segs;
-            plan_bytes = cu_seqlens ? ((2 * static_cast<size_t>(n_seq) + 3 + static_cast<size_t>(n_segs)) *
-                                           4 + 255) / 256 * 256
-                                    : 0;
-            ws_bytes = plan_bytes + static_cast<size_t>(slots) * H * 3 * SS * sizeof(float) +
-                       static_cast<size_t>(tp_blocks) * H * TP_BYTES;
-        }
-    };
-    size_workspace();
-    if (cu_seqlens && n_segs > 0 && tp_fits) {
-        tp = true;  // packed input: pass 1 maps the first segments too, and keeps their T/P as well
-        tp_blocks = tp_ids;
-        size_workspace();
-    }
-    void* ws = nullptr;
-    hipMemPool_t pool = ws_bytes ? workspace_pool(dev) : nullptr;
-    if (pool) {
-        e = hipMallocFromPoolAsync(&ws, ws_bytes, pool, stream);
-        if (e != hipSuccess && tp) {
-            // without the T/P images the workspace is a few MB per head
-            report("hipMallocFromPoolAsync (with T/P)", e);
-            (void)hipGetLastError();
-            if (cu_seqlens) {
-                tp = false;
-                tp_blocks = 0;
-            } else {
-                plan_dense(false);
-            }
-            size_workspace();
-            e = hipMallocFromPoolAsync(&ws, ws_bytes, pool, stream);
-        }
-        if (e != hipSuccess) {
-            report("hipMallocFromPoolAsync", e);
-            (void)hipGetLastError();
-            ws = nullptr;  // fall back to one segment per sequence
-        }
-    }
-    if (!ws) {
+    if (!plan.segmented) {
         // one segment per sequence: pass 3 alone from the given initial states
         a.seg_len = 0;
         a.nseg_dense = 1;
         a.n_segs = n_seq;
         a.seg_first = nullptr;
-        const dim3 grid(static_cast<unsigned>(n_seq * H));
-        hipLaunchKernelGGL((scan_kernel<true, false>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((scan_kernel<true, false>), dim3(static_cast<unsigned>(units)), block, 0,
+                           stream, a);
         e = hipGetLastError();
         report("prefill scan launch", e);
         return e;
     }
 
-    a.seg_len = seg;
-    a.seg0_len = seg0;
+    a.seg_len = plan.seg;
+    a.seg0_len = plan.seg0;
     a.seg0_out = cu_seqlens ? 0 : 1;
-    a.n_segs = n_segs;
-    a.nseg_dense = cu_seqlens ? 0 : nseg_dense;
+    a.n_segs = plan.n_segs;
+    a.nseg_dense = plan.nseg_dense;
     char* w = static_cast<char*>(ws);
     if (cu_seqlens) {
         a.seg_first = reinterpret_cast<int32_t*>(w);             // [n_seq + 2]
         a.ws_first = a.seg_first + n_seq + 2;                     // [n_seq + 1]
         a.seg_order = a.ws_first + n_seq + 1;                     // [n_segs]
-        hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens, n_seq, seg,
-                           seg_min, H, static_cast<int64_t>(cu_count(dev)), tp ? 1 : 0,
+        hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens, n_seq, plan.seg,
+                           plan.seg_min, H, static_cast<int64_t>(n_cu), plan.tp ? 1 : 0,
                            const_cast<int32_t*>(a.seg_first), const_cast<int32_t*>(a.ws_first),
                            const_cast<int32_t*>(a.seg_order));
         e = hipGetLastError();
         report("segment plan launch", e);
-        if (e != hipSuccess) {
-            (void)hipFreeAsync(ws, stream);
-            return e;
-        }
+        if (e != hipSuccess) return e;
     }
-    a.ws_maps = reinterpret_cast<float*>(w + plan_bytes);
-    a.ws_start = a.ws_maps + static_cast<size_t>(slots) * H * 2 * SS;
-    if (tp) {
-        a.ws_tp = reinterpret_cast<char*>(a.ws_start + static_cast<size_t>(slots) * H * SS);
-    }
+    a.ws_maps = reinterpret_cast<float*>(w + plan.plan_bytes);
+    a.ws_start = a.ws_maps + static_cast<size_t>(plan.slots) * H * 2 * SS;
+    if (plan.tp) a.ws_tp = reinterpret_cast<char*>(a.ws_start + static_cast<size_t>(plan.slots) * H * SS);
 
-    const dim3 grid(static_cast<unsigned>(n_segs * H));
-    if (tp) hipLaunchKernelGGL((scan_kernel<false, true>), grid, block, 0, stream, a);
+    const dim3 grid(static_cast<unsigned>(plan.n_segs * H));
+    if (plan.tp) hipLaunchKernelGGL((scan_kernel<false, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((scan_kernel<false, false>), grid, block, 0, stream, a);
     e = hipGetLastError();
     report("segment map launch", e);
-    if (e == hipSuccess) {
-        const dim3 cgrid(static_cast<unsigned>((units + 7) / 8 * 64));
-        hipLaunchKernelGGL(combine_kernel, cgrid, dim3(512), 0, stream, a);
-        e = hipGetLastError();
-        report("segment combine launch", e);
-    }
-    if (e == hipSuccess) {
-        if (tp) hipLaunchKernelGGL((scan_kernel<true, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((scan_kernel<true, false>), grid, block, 0, stream, a);
-        e = hipGetLastError();
-        report("prefill scan launch", e);
-    }
-    const hipError_t f = hipFreeAsync(ws, stream);
-    report("hipFreeAsync", f);
-    return e != hipSuccess ? e : f;
+    if (e != hipSuccess) return e;
+    const dim3 cgrid(static_cast<unsigned>((units + 7) / 8 * 64));
+    hipLaunchKernelGGL(combine_kernel, cgrid, dim3(512), 0, stream, a);
+    e = hipGetLastError();
+    report("segment combine launch", e);
+    if (e != hipSuccess) return e;
+    if (plan.tp) hipLaunchKernelGGL((scan_kernel<true, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((scan_kernel<true, false>), grid, block, 0, stream, a);
+    e = hipGetLastError();
+    report("prefill scan launch", e);
+    return e;
 }
 
 hipError_t launch_segment_states(const void* k, const void* v, const void* beta,

@@ -30,13 +30,31 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - All tensor pointers are DEVICE pointers (e.g. torch CUDA tensors), owned by
- *    the caller.  Decode allocates nothing.  A prefill whose sequences are
- *    long enough to be cut into segments (see kda_set_prefill_segment) takes
- *    a temporary workspace, allocated and freed in stream order on `stream`
- *    from a memory pool the library keeps per device (no synchronisation);
- *    if that allocation fails the call runs unsegmented instead.  The
- *    backward calls take their state checkpoints from the same pool.  Calls
- *    are re-entrant and thread-safe.
+ *    the caller.  The library keeps no device memory between calls.
+ *  - Workspace.  The prefill calls on bf16 inputs cut long sequences into
+ *    segments (see kda_set_prefill_segment) and need device scratch memory
+ *    for the segment maps; the backward calls need it for their state
+ *    checkpoints.  Those calls take two arguments for it:
+ *      workspace, workspace_bytes : caller-owned device memory, 256-byte
+ *          aligned (KDA_ERR_ALIGN), of workspace_bytes bytes (NULL when 0).
+ *          It is used in stream order: it must stay allocated and must not be
+ *          used for anything else until the call's work on `stream` is done.
+ *          Its contents on entry do not matter and are undefined afterwards.
+ *      workspace_bytes = KDA_WORKSPACE_AUTO (workspace NULL) : the library
+ *          takes the workspace itself, in stream order on `stream`, from a
+ *          per-device pool whose release threshold is 0 (freed memory goes
+ *          back to the device at the next synchronisation, nothing stays
+ *          reserved), and returns it in stream order at the end of the call.
+ *          If that allocation fails the call returns KDA_ERR_WORKSPACE and
+ *          enqueues nothing.
+ *    The *_workspace_size calls below give the bytes of each plan.  A prefill
+ *    takes the fastest plan whose workspace fits workspace_bytes: FULL, else
+ *    SEGMENTS, else UNSEGMENTED (which needs none, so a prefill always runs;
+ *    with little work per compute unit it is much slower).  A backward call
+ *    with less than its workspace size returns KDA_ERR_WORKSPACE.
+ *  - Calls are re-entrant and thread-safe (the one knob,
+ *    kda_set_prefill_segment, is an atomic process-wide setting for tests and
+ *    tuning).
  *  - Layouts are dense row-major, innermost dimension last:
  *        q, k, log_alpha : [rows, H, d_k]      v, o : [rows, H, d_v]
  *        beta            : [rows, H]
@@ -51,16 +69,24 @@
  *    fp32.
  *  - Supported sizes: d_k = d_v = 128 (anything else -> KDA_ERR_UNSUPPORTED);
  *    1 <= H <= 65536 heads (anything else -> KDA_ERR_SHAPE).
- *  - Every pointer must be 16-byte aligned (KDA_ERR_ALIGN).
- *  - Preconditions not checked (device data): log_alpha finite and <= 0;
- *    cu_seqlens[0] = 0, non-decreasing, cu_seqlens[N] = T_total.
+ *  - Every tensor pointer must be 16-byte aligned (KDA_ERR_ALIGN).
+ *  - Preconditions on device data: log_alpha finite and <= 0 (the *_raw
+ *    calls: gate logits finite); cu_seqlens[0] = 0, non-decreasing,
+ *    cu_seqlens[N] = T_total.  They are not checked unless KDA_DEBUG is set in
+ *    the environment: then every call first runs a check kernel and
+ *    synchronises `stream` (so it cannot be captured into a graph), and
+ *    returns KDA_ERR_PRECONDITION, enqueueing nothing more, on a violation.
+ *    KDA_DEBUG also prints failed HIP calls to stderr.
  *  - The calling thread's current device (hipSetDevice) must be the device
- *    that holds the pointers and `stream`: the segmented prefill takes its
- *    workspace from that device's pool and sizes its work by its CU count.
+ *    that holds the pointers and `stream`: plans and workspace sizes follow
+ *    its compute-unit count.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call is
  *    asynchronous on it: arguments are validated on the host first, and on any
- *    error nothing is enqueued.  No call synchronises.  A fault inside a
- *    kernel surfaces at the caller's next synchronisation.
+ *    error nothing is enqueued.  No call synchronises (KDA_DEBUG aside).  A
+ *    fault inside a kernel surfaces at the caller's next synchronisation.
+ *  - A HIP error left unread by an earlier call of the calling thread is not
+ *    cleared: the call enqueues nothing and returns KDA_ERR_HIP, and the error
+ *    stays for the caller to read (hipGetLastError).
  *  - Inputs must not overlap outputs, except where stated.
  */
 #ifndef KDA_H
@@ -72,7 +98,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum kda_status {
     KDA_OK = 0,
@@ -81,8 +107,23 @@ typedef enum kda_status {
     KDA_ERR_DTYPE = 3,        /* in_dtype is not a kda_dtype value             */
     KDA_ERR_ALIGN = 4,        /* a pointer is not 16-byte aligned              */
     KDA_ERR_UNSUPPORTED = 5,  /* d_k or d_v other than 128                      */
-    KDA_ERR_HIP = 6           /* the HIP runtime rejected a launch             */
+    KDA_ERR_HIP = 6,          /* the HIP runtime rejected a launch, or a HIP error is pending */
+    KDA_ERR_WORKSPACE = 7,    /* workspace too small or misused, or none could be allocated */
+    KDA_ERR_PRECONDITION = 8  /* KDA_DEBUG: a device-data precondition does not hold */
 } kda_status;
+
+/* workspace_bytes value asking the library to allocate the workspace itself */
+#define KDA_WORKSPACE_AUTO (-1)
+
+/* Prefill plans, fastest first (see the workspace convention above). */
+typedef enum kda_plan {
+    KDA_PLAN_FULL = 0,        /* segments; pass 1 also keeps the split UT transform
+                                 T and query-key matrix P of every chunk it maps
+                                 (32 KiB per chunk and head) for pass 3, while
+                                 those stay under 8 GiB per call */
+    KDA_PLAN_SEGMENTS = 1,    /* segments, without the T/P images */
+    KDA_PLAN_UNSEGMENTED = 2  /* one workgroup per (sequence, head); no workspace */
+} kda_plan;
 
 typedef enum kda_dtype {
     KDA_F32 = 0,
@@ -100,6 +141,8 @@ typedef enum kda_dtype {
  *   o           : [B, T, H, d_v]  fp32, written
  *   final_state : [B, H, d_k, d_v] fp32, written, or NULL to skip; it MAY be
  *                 the same pointer as initial_state (in-place resume)
+ *   workspace, workspace_bytes : see the workspace convention above
+ *                 (kda_prefill_workspace_size gives each plan's bytes)
  * B = 0 is a no-op.  T = 0 writes final_state = initial_state (or zeros).
  * Requires 1 <= H <= 65536.
  */
@@ -107,7 +150,8 @@ kda_status kda_prefill(const void *q, const void *k, const void *v, const void *
                        const float *log_alpha, const float *initial_state,
                        float *o, float *final_state,
                        int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v,
-                       kda_dtype in_dtype, void *stream);
+                       kda_dtype in_dtype, void *workspace, int64_t workspace_bytes,
+                       void *stream);
 
 /*
  * Packed variable-length prefill of N sequences stored back to back.
@@ -119,6 +163,8 @@ kda_status kda_prefill(const void *q, const void *k, const void *v, const void *
  *                 (NULL initial state = zeros for every sequence; the two may
  *                 alias).  No state crosses a sequence boundary; an empty
  *                 sequence returns its initial state.
+ *   workspace, workspace_bytes : see the workspace convention above
+ *                 (kda_varlen_prefill_workspace_size gives each plan's bytes)
  * N = 0 is a no-op.  T_total may be 0 (then every sequence is empty).
  */
 kda_status kda_varlen_prefill(const void *q, const void *k, const void *v, const void *beta,
@@ -126,7 +172,8 @@ kda_status kda_varlen_prefill(const void *q, const void *k, const void *v, const
                               int64_t N, int64_t T_total,
                               const float *initial_state, float *o, float *final_state,
                               int64_t H, int64_t d_k, int64_t d_v,
-                              kda_dtype in_dtype, void *stream);
+                              kda_dtype in_dtype, void *workspace, int64_t workspace_bytes,
+                              void *stream);
 
 /*
  * One decode step: one new token for each of N sequences, all H heads.
@@ -161,13 +208,15 @@ kda_status kda_prefill_raw(const void *q, const void *k, const void *v, const vo
                            const float *log_alpha, const float *initial_state,
                            float *o, float *final_state,
                            int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v,
-                           kda_dtype in_dtype, void *stream);
+                           kda_dtype in_dtype, void *workspace, int64_t workspace_bytes,
+                           void *stream);
 kda_status kda_varlen_prefill_raw(const void *q, const void *k, const void *v, const void *beta,
                                   const float *log_alpha, const int32_t *cu_seqlens,
                                   int64_t N, int64_t T_total,
                                   const float *initial_state, float *o, float *final_state,
                                   int64_t H, int64_t d_k, int64_t d_v,
-                                  kda_dtype in_dtype, void *stream);
+                                  kda_dtype in_dtype, void *workspace, int64_t workspace_bytes,
+                                  void *stream);
 kda_status kda_decode_step_raw(const void *q, const void *k, const void *v, const void *beta,
                                const float *log_alpha, float *state, float *o,
                                int64_t N, int64_t H, int64_t d_k, int64_t d_v,
@@ -236,14 +285,15 @@ kda_status kda_decode_step_slots(const void *q, const void *k, const void *v, co
  * outside [0, n_pool), or for every sequence if final_slots is NULL).  A
  * sequence may resume in place (init_slots[n] == final_slots[n]); otherwise no
  * final slot may equal another sequence's initial or final slot.
- * state_pool may be NULL only when both slot arrays are NULL.
+ * state_pool may be NULL only when both slot arrays are NULL.  The workspace
+ * is that of kda_varlen_prefill (same sizes, same plans).
  */
 kda_status kda_varlen_prefill_slots(const void *q, const void *k, const void *v, const void *beta,
                                     const float *log_alpha, const int32_t *cu_seqlens, int64_t N,
                                     int64_t T_total, float *state_pool, const int32_t *init_slots,
                                     const int32_t *final_slots, int64_t n_pool, float *o,
                                     int64_t H, int64_t d_k, int64_t d_v, kda_dtype in_dtype,
-                                    void *stream);
+                                    void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
  * Backward pass: the gradients of a loss in the inputs of a prefill, given its
@@ -265,12 +315,10 @@ kda_status kda_varlen_prefill_slots(const void *q, const void *k, const void *v,
  *   d_initial_state : [B or N, H, d_k, d_v], or NULL to skip; it MAY be the same
  *                 pointer as d_final_state
  * q, k, v, beta are in_dtype (bf16 inputs widened exactly); arithmetic is fp32.
- * The call recomputes the forward states: it runs the recurrence once storing
- * a state every 8 tokens in a workspace taken in stream order from the
- * device's pool (8 KiB per head-token, e.g. 8 GiB for 8 x 4096 tokens x 32
- * heads), then sweeps back recomputing each block from its stored state.  If
- * that allocation fails the call returns KDA_ERR_HIP and enqueues nothing.  B or N = 0 is a no-op; with no
- * tokens, d_initial_state = d_final_state (or zeros).
+ * The call recomputes the forward states, which it keeps in the workspace
+ * (kda_backward_workspace_size gives its bytes; a smaller one is
+ * KDA_ERR_WORKSPACE).  B or N = 0 is a no-op; with no tokens,
+ * d_initial_state = d_final_state (or zeros).
  */
 kda_status kda_backward(const void *q, const void *k, const void *v, const void *beta,
                         const float *log_alpha, const float *initial_state,
@@ -278,7 +326,8 @@ kda_status kda_backward(const void *q, const void *k, const void *v, const void 
                         float *dq, float *dk, float *dv, float *dbeta, float *dlog_alpha,
                         float *d_initial_state,
                         int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v,
-                        kda_dtype in_dtype, void *stream);
+                        kda_dtype in_dtype, void *workspace, int64_t workspace_bytes,
+                        void *stream);
 kda_status kda_varlen_backward(const void *q, const void *k, const void *v, const void *beta,
                                const float *log_alpha, const int32_t *cu_seqlens,
                                int64_t N, int64_t T_total, const float *initial_state,
@@ -286,43 +335,49 @@ kda_status kda_varlen_backward(const void *q, const void *k, const void *v, cons
                                float *dq, float *dk, float *dv, float *dbeta,
                                float *dlog_alpha, float *d_initial_state,
                                int64_t H, int64_t d_k, int64_t d_v,
-                               kda_dtype in_dtype, void *stream);
+                               kda_dtype in_dtype, void *workspace, int64_t workspace_bytes,
+                               void *stream);
 
 /*
- * Tuning and testing knob for the bf16 prefill (process-wide; set it while no
- * prefill call is running).  The blockwise prefill runs one workgroup per
- * (sequence, head, segment); a sequence longer than `tokens` is cut into
- * segments of `tokens` tokens (the last one shorter), processed in parallel
- * and stitched together through their affine state maps ("blockwise and
- * context-parallel" in "Kimi K3 -- the architecture and infrastructure,
- * explained", section "Kimi Delta Attention: the load-bearing choice").
- * 0 (the default) picks the length from the problem size and the number of
- * compute units; for dense input the first segment of each sequence runs
- * with its outputs while the other segments build their maps, so a sequence
- * takes one segment more, and the last segment is made shorter (about 3/5 of
- * the others with the T/P reuse below, else the first is 7/8 as long); for
- * packed input a small planning kernel then chooses, on
- * the device where the sequence lengths are, between that length and the
- * powers of two below it (down to an eighth of it).  tokens must be 0 or a
- * positive multiple of 64, else KDA_ERR_SHAPE.  Results do not depend on it
- * beyond rounding.
+ * Workspace sizes.  *bytes receives the device workspace, in bytes, that the
+ * call of the same name with these sizes needs on the calling thread's current
+ * device (0 when it needs none): for the prefills under the given plan (a plan
+ * that would cut no sequence needs none), for the backward calls in all.  The
+ * arguments are validated as the calls validate them (a non-OK status leaves
+ * *bytes = 0); nothing is enqueued.  The sizes depend on the device's compute
+ * units and on kda_set_prefill_segment.  The *_raw and *_slots prefills take
+ * the sizes of their plain forms.
+ */
+kda_status kda_prefill_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v,
+                                      kda_dtype in_dtype, kda_plan plan, int64_t *bytes);
+kda_status kda_varlen_prefill_workspace_size(int64_t N, int64_t T_total, int64_t H, int64_t d_k,
+                                             int64_t d_v, kda_dtype in_dtype, kda_plan plan,
+                                             int64_t *bytes);
+kda_status kda_backward_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v,
+                                       kda_dtype in_dtype, int64_t *bytes);
+kda_status kda_varlen_backward_workspace_size(int64_t N, int64_t T_total, int64_t H, int64_t d_k,
+                                              int64_t d_v, kda_dtype in_dtype, int64_t *bytes);
+
+/*
+ * Tuning and testing knob for the bf16 prefill (process-wide and atomic; a
+ * call reads it once, and the workspace sizes above follow it, so change it
+ * only between a size query and the call it sizes).  The blockwise prefill
+ * runs one workgroup per (sequence, head, segment); a sequence longer than
+ * `tokens` is cut into segments of `tokens` tokens (the last one shorter),
+ * processed in parallel and stitched together through their affine state maps
+ * ("blockwise and context-parallel" in "Kimi K3 -- the architecture and
+ * infrastructure, explained", section "Kimi Delta Attention: the load-bearing
+ * choice").  0 (the default) picks the length from the problem size and the
+ * number of compute units; for dense input the first segment of each sequence
+ * runs with its outputs while the other segments build their maps, so a
+ * sequence takes one segment more, and the last segment is made shorter
+ * (about 3/5 of the others under KDA_PLAN_FULL, else the first is 7/8 as
+ * long); for packed input a small planning kernel then chooses, on the device
+ * where the sequence lengths are, between that length and the powers of two
+ * below it (down to an eighth of it).  tokens must be 0 or a positive multiple
+ * of 64, else KDA_ERR_SHAPE.  Results do not depend on it beyond rounding.
  */
 kda_status kda_set_prefill_segment(int64_t tokens);
-
-/*
- * Second knob of the bf16 prefill (process-wide, like the one above).  When
- * a sequence (dense or packed) is cut into segments, pass 1 (which builds the
- * segment maps) also keeps the split UT transform T = (I + Diag(beta) A)^-1
- * and query-key matrix P of every chunk it maps, 32 KiB per chunk and head,
- * and pass 3 reuses them instead of forming them again.  That workspace (one
- * block per 64 rows of the input plus one per sequence, per head) comes from
- * the same stream-ordered pool as the rest and is used only while one call
- * needs at most `bytes` of it (default 8 GiB; 0 turns it off, and for dense
- * input the first segment is then made shorter instead).  If the pool cannot
- * provide it, the call goes without it.  Results do not depend on it beyond
- * rounding.  bytes < 0 is KDA_ERR_SHAPE.
- */
-kda_status kda_set_prefill_tp_limit(int64_t bytes);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char *kda_status_str(kda_status status);

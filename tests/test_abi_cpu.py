@@ -15,7 +15,8 @@ import gated_delta_rule_113_amd as kda
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
 
-OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, HIP = range(7)
+OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, HIP, WORKSPACE, PRECONDITION = range(9)
+AUTO = -1            # KDA_WORKSPACE_AUTO
 P = 0x10000          # a 16-byte aligned fake device address
 MIS = 0x10008        # 8-byte aligned only
 
@@ -40,9 +41,10 @@ def test_exports_match_header(lib):
     assert declared == {"kda_prefill", "kda_varlen_prefill", "kda_decode_step",
                         "kda_prefill_raw", "kda_varlen_prefill_raw", "kda_decode_step_raw",
                         "kda_decode_tokens", "kda_decode_step_slots", "kda_varlen_prefill_slots",
-                        "kda_backward", "kda_varlen_backward",
-                        "kda_set_prefill_segment", "kda_set_prefill_tp_limit", "kda_status_str",
-                        "kda_abi_version"}
+                        "kda_backward", "kda_varlen_backward", "kda_prefill_workspace_size",
+                        "kda_varlen_prefill_workspace_size", "kda_backward_workspace_size",
+                        "kda_varlen_backward_workspace_size", "kda_set_prefill_segment",
+                        "kda_status_str", "kda_abi_version"}
     out = subprocess.run(["nm", "-D", "--defined-only", kda._binding.LIBRARY],
                          capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r" T (kda_\w+)", out))
@@ -53,21 +55,22 @@ def test_exports_match_header(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 1
-    for code in range(7):
+    assert lib.kda_abi_version() == 2
+    for code in range(9):
         s = lib.kda_status_str(code).decode()
         assert s.startswith(kda._binding.STATUS_NAMES[code])
     assert lib.kda_status_str(99).decode().startswith("KDA_ERR_UNKNOWN")
 
 
 def prefill(lib, q=P, k=P, v=P, beta=P, la=P, s0=None, o=P, s1=P, B=1, T=4, H=2,
-            dk=128, dv=128, dt=1):
-    return lib.kda_prefill(q, k, v, beta, la, s0, o, s1, B, T, H, dk, dv, dt, None)
+            dk=128, dv=128, dt=1, ws=None, wb=0):
+    return lib.kda_prefill(q, k, v, beta, la, s0, o, s1, B, T, H, dk, dv, dt, ws, wb, None)
 
 
 def varlen(lib, q=P, k=P, v=P, beta=P, la=P, cu=P, N=2, Tt=8, s0=None, o=P, s1=P, H=2,
-           dk=128, dv=128, dt=1):
-    return lib.kda_varlen_prefill(q, k, v, beta, la, cu, N, Tt, s0, o, s1, H, dk, dv, dt, None)
+           dk=128, dv=128, dt=1, ws=None, wb=0):
+    return lib.kda_varlen_prefill(q, k, v, beta, la, cu, N, Tt, s0, o, s1, H, dk, dv, dt, ws, wb,
+                                  None)
 
 
 def decode(lib, q=P, k=P, v=P, beta=P, la=P, st=P, o=P, N=2, H=2, dk=128, dv=128, dt=1):
@@ -145,7 +148,7 @@ def decode_slots(lib, q=P, k=P, v=P, beta=P, la=P, pool=P, slots=P, n_pool=4, o=
 def varlen_slots(lib, q=P, k=P, v=P, beta=P, la=P, cu=P, N=2, Tt=8, pool=P, si=P, sf=P, n_pool=4,
                  o=P, H=2, dk=128, dv=128, dt=1):
     return lib.kda_varlen_prefill_slots(q, k, v, beta, la, cu, N, Tt, pool, si, sf, n_pool, o, H,
-                                        dk, dv, dt, None)
+                                        dk, dv, dt, None, 0, None)
 
 
 def decode_tokens(lib, q=P, k=P, v=P, beta=P, la=P, st=P, nc=None, o=P, N=2, K=4, H=2, dk=128,
@@ -194,15 +197,16 @@ def test_varlen_slots_validation(lib):
 
 
 def backward(lib, q=P, k=P, v=P, beta=P, la=P, s0=None, do=P, dsT=None, dq=P, dk_=P, dv_=P, db=P,
-             dla=P, ds0=P, B=1, T=4, H=2, dk=128, dv=128, dt=1):
+             dla=P, ds0=P, B=1, T=4, H=2, dk=128, dv=128, dt=1, ws=None, wb=0):
     return lib.kda_backward(q, k, v, beta, la, s0, do, dsT, dq, dk_, dv_, db, dla, ds0,
-                            B, T, H, dk, dv, dt, None)
+                            B, T, H, dk, dv, dt, ws, wb, None)
 
 
 def varlen_backward(lib, q=P, k=P, v=P, beta=P, la=P, cu=P, N=2, Tt=8, s0=None, do=P, dsT=None,
-                    dq=P, dk_=P, dv_=P, db=P, dla=P, ds0=P, H=2, dk=128, dv=128, dt=1):
+                    dq=P, dk_=P, dv_=P, db=P, dla=P, ds0=P, H=2, dk=128, dv=128, dt=1, ws=None,
+                    wb=0):
     return lib.kda_varlen_backward(q, k, v, beta, la, cu, N, Tt, s0, do, dsT, dq, dk_, dv_, db,
-                                   dla, ds0, H, dk, dv, dt, None)
+                                   dla, ds0, H, dk, dv, dt, ws, wb, None)
 
 
 def test_backward_validation(lib):
@@ -254,6 +258,49 @@ def test_prefill_segment_knob(lib):
     assert lib.kda_set_prefill_segment(0) == OK
     assert lib.kda_set_prefill_segment(100) == SHAPE
     assert lib.kda_set_prefill_segment(-64) == SHAPE
-    assert lib.kda_set_prefill_tp_limit(0) == OK
-    assert lib.kda_set_prefill_tp_limit(-1) == SHAPE
-    assert lib.kda_set_prefill_tp_limit(8 << 30) == OK
+
+
+W = 0x20000          # a 256-byte aligned fake workspace address
+
+
+def test_workspace_arguments(lib):
+    """Workspace rules, checked before anything reaches the device: a caller
+    workspace is 256-byte aligned and non-NULL when it has bytes;
+    KDA_WORKSPACE_AUTO takes no pointer; other negative sizes are refused."""
+    for call in (prefill, varlen, backward, varlen_backward):
+        assert call(lib, q=None, ws=W, wb=1 << 20) == NULL, call.__name__   # still validated first
+        assert call(lib, ws=None, wb=4096) == NULL, call.__name__
+        assert call(lib, ws=P + 16, wb=4096) == ALIGN, call.__name__        # 16- but not 256-aligned
+        assert call(lib, ws=W, wb=AUTO) == WORKSPACE, call.__name__
+        assert call(lib, ws=None, wb=-2) == WORKSPACE, call.__name__
+        assert call(lib, ws=W, wb=-5) == WORKSPACE, call.__name__
+    # no work: a workspace argument of any valid form is accepted
+    assert prefill(lib, B=0, q=None, o=None, s1=None, ws=None, wb=AUTO) == OK
+    assert varlen(lib, N=0, cu=None, q=None, o=None, ws=W, wb=256) == OK
+
+
+def size_query(lib, fn, *args):
+    out = ctypes.c_int64(-7)
+    code = getattr(lib, fn)(*args, ctypes.byref(out))
+    return code, out.value
+
+
+def test_workspace_size_validation(lib):
+    """The size queries validate like the calls and report 0 bytes then;
+    fp32 inputs and bf16 sequences of at most 16 tokens (token-by-token
+    kernel) need no workspace, known without a device."""
+    bad_shapes = ((1, 4, 0, 128, 128, 1), (-1, 4, 2, 128, 128, 1), (1, 4, 2, 64, 128, 1),
+                  (1, 4, 2, 128, 128, 3), (1, 1 << 40, 2, 128, 128, 1), (1, 4, 65537, 128, 128, 1))
+    expect = (SHAPE, SHAPE, UNSUP, DTYPE, SHAPE, SHAPE)
+    for args, code in zip(bad_shapes, expect):
+        assert size_query(lib, "kda_prefill_workspace_size", *args, 0) == (code, 0), args
+        assert size_query(lib, "kda_backward_workspace_size", *args) == (code, 0), args
+    assert size_query(lib, "kda_varlen_prefill_workspace_size", 2, 1 << 31, 2, 128, 128, 1, 0)[0] == SHAPE
+    assert size_query(lib, "kda_prefill_workspace_size", 1, 4, 2, 128, 128, 1, 3)[0] == SHAPE  # plan
+    assert lib.kda_prefill_workspace_size(1, 4, 2, 128, 128, 1, 0, None) == NULL
+    # no workspace without the chunked kernel: fp32 inputs, or at most 16 tokens
+    for plan in (0, 1, 2):
+        assert size_query(lib, "kda_prefill_workspace_size", 4, 50000, 32, 128, 128, 0, plan) == (OK, 0)
+        assert size_query(lib, "kda_prefill_workspace_size", 4, 16, 32, 128, 128, 1, plan) == (OK, 0)
+        assert size_query(lib, "kda_varlen_prefill_workspace_size", 3, 16, 8, 128, 128, 1, plan) == (OK, 0)
+        assert size_query(lib, "kda_prefill_workspace_size", 0, 5000, 2, 128, 128, 1, plan) == (OK, 0)

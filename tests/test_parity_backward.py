@@ -224,7 +224,7 @@ def test_backward_initial_gradient_in_place(T):
     code = lib.kda_backward(p(t["q"]), p(t["k"]), p(t["v"]), p(t["beta"]), p(t["log_alpha"]),
                             p(t["initial_state"]), p(do), p(buf), p(outs["dq"]), p(outs["dk"]),
                             p(outs["dv"]), p(outs["dbeta"]), p(outs["dlog_alpha"]), p(buf),
-                            B, T, H, 128, 128, kda.KDA_BF16,
+                            B, T, H, 128, 128, kda.KDA_BF16, None, kda.KDA_WORKSPACE_AUTO,
                             ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
     torch.cuda.synchronize()
     assert code == 0, code

@@ -32,11 +32,11 @@ def _dense(inp, dev, **kw):
     return o.cpu().numpy(), S.cpu().numpy()
 
 
-def _varlen(inp, dev):
+def _varlen(inp, dev, **kw):
     torch = __import__("torch")
     t = upload(inp, dev)
     o, S = kda.kda_varlen_prefill(t["q"], t["k"], t["v"], t["beta"], t["log_alpha"],
-                                  t["cu_seqlens"], t["initial_state"])
+                                  t["cu_seqlens"], t["initial_state"], **kw)
     torch.cuda.synchronize()
     return o.cpu().numpy(), S.cpu().numpy()
 
@@ -63,28 +63,35 @@ def test_dense_automatic_segments():
     check("dense automatic segments", rel_err_vectors(o, o_ref), rel_err_states(S, S_ref))
 
 
-@pytest.fixture
-def no_tp():
-    """Turn the T/P reuse of the dense prefill off for one test."""
-    kda.kda_set_prefill_tp_limit(0)
-    yield
-    kda.kda_set_prefill_tp_limit(8 << 30)
+def _segments_workspace(B, T, H, packed_n=None):
+    """A caller workspace of exactly the KDA_PLAN_SEGMENTS size (segments
+    without the T/P images), which the call then takes."""
+    torch = __import__("torch")
+    if packed_n is None:
+        n = kda.prefill_workspace_size(B, T, H, torch.bfloat16, kda.KDA_PLAN_SEGMENTS)
+        full = kda.prefill_workspace_size(B, T, H, torch.bfloat16, kda.KDA_PLAN_FULL)
+    else:
+        n = kda.varlen_prefill_workspace_size(packed_n, T, H, torch.bfloat16, kda.KDA_PLAN_SEGMENTS)
+        full = kda.varlen_prefill_workspace_size(packed_n, T, H, torch.bfloat16, kda.KDA_PLAN_FULL)
+    assert 0 < n < full
+    return torch.empty(n, dtype=torch.uint8, device=device())
 
 
-def test_dense_automatic_without_tp_workspace(no_tp):
-    """Without the T/P workspace the automatic lengths at B=2, H=8, T=4096 are
-    896 (first segment, with outputs in pass 1), three of 1024 and 128, and
-    every pass-3 segment forms its own T and P."""
+def test_dense_automatic_without_tp_workspace():
+    """Without the T/P images (a workspace of the KDA_PLAN_SEGMENTS size) the
+    automatic lengths at B=2, H=8, T=4096 are 896 (first segment, with outputs
+    in pass 1), three of 1024 and 128, and every pass-3 segment forms its own
+    T and P."""
     inp = ki.dense_prefill(43, B=2, T=4096, H=8, gated=True, initial_state=True)
-    o, S = _dense(inp, device())
+    o, S = _dense(inp, device(), workspace=_segments_workspace(2, 4096, 8))
     o_ref, S_ref = oracle.prefill(*inp.widened(), inp.initial_state)
     check("dense automatic segments, no T/P reuse", rel_err_vectors(o, o_ref), rel_err_states(S, S_ref))
 
 
-def test_dense_forced_segments_without_tp_workspace(segment, no_tp):
+def test_dense_forced_segments_without_tp_workspace(segment):
     inp = ki.dense_prefill(44, B=2, T=500, H=3, gated=True, initial_state=True)
     segment(64)
-    o, S = _dense(inp, device())
+    o, S = _dense(inp, device(), workspace=_segments_workspace(2, 500, 3))
     o_ref, S_ref = oracle.prefill(*inp.widened(), inp.initial_state)
     check("dense segmented seg=64, no T/P reuse", rel_err_vectors(o, o_ref), rel_err_states(S, S_ref))
 
@@ -119,11 +126,8 @@ def test_varlen_segmented(segment, tp):
     and without the T/P reuse."""
     inp = ki.varlen_prefill(43, [0, 1, 63, 64, 65, 300, 0, 129, 520], H=3)
     segment(128)
-    kda.kda_set_prefill_tp_limit(8 << 30 if tp else 0)
-    try:
-        o, S = _varlen(inp, device())
-    finally:
-        kda.kda_set_prefill_tp_limit(8 << 30)
+    ws = None if tp else _segments_workspace(None, int(inp.cu_seqlens[-1]), 3, packed_n=9)
+    o, S = _varlen(inp, device(), workspace=ws)
     q, k, v, b, la = inp.widened()
     o_ref, S_ref = oracle.varlen_prefill(q, k, v, b, la, inp.cu_seqlens, inp.initial_state)
     check("varlen segmented", rel_err_vectors(o[0], o_ref), rel_err_states(S, S_ref))
