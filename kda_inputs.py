@@ -237,6 +237,29 @@ def varlen_prefill(workload: int, lengths, H: int, dk: int = 128, dv: int = 128,
     return KDAInputs(q, k, v, beta, la, dtype, s0, cu.astype(np.int32))
 
 
+def varlen_prefill_bulk(workload: int, lengths, H: int, dtype: str = "bf16", gated: bool = True,
+                        resumed: str = "even") -> KDAInputs:
+    """Packed prefill inputs like ``varlen_prefill`` (same distributions and
+    state rule) for batches of thousands of sequences: each head's rows are
+    drawn for the whole packed batch from one stream keyed (workload, tensor,
+    0, head) and then cut at the sequence boundaries, instead of one stream
+    per (sequence, head)."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    n = lengths.size
+    cu = np.zeros(n + 1, np.int64)
+    cu[1:] = np.cumsum(lengths)
+    dense = dense_prefill(workload, 1, int(cu[-1]), H, dtype=dtype, gated=gated)
+    s0 = draw_state(workload, (n, H, 128, 128))
+    if resumed == "even":
+        s0[1::2] = 0.0
+    elif resumed == "none":
+        s0[:] = 0.0
+    elif resumed != "all":
+        raise ValueError(resumed)
+    return KDAInputs(dense.q, dense.k, dense.v, dense.beta, dense.log_alpha, dtype, s0,
+                     cu.astype(np.int32))
+
+
 def decode_steps(workload: int, steps: int, N: int, H: int, dk: int = 128, dv: int = 128,
                  dtype: str = "bf16", first_step: int = 0) -> KDAInputs:
     """Inputs for a chain of single-token decode steps, [steps, N, H, *], plus

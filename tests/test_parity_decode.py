@@ -7,7 +7,7 @@ import pytest
 import gated_delta_rule_113_amd as kda
 import kda_inputs as ki
 import oracle
-from kda_gpu import check, device, rel_err_states, rel_err_vectors, upload
+from kda_gpu import GroupCheck, check, device, rel_err_states, rel_err_vectors, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -33,22 +33,24 @@ def test_decode_small_every_step(dtype):
     check(f"decode small {dtype}", rel_err_vectors(o, o_ref), rel_err_states(S, S_ref))
 
 
-def test_decode_full_size_sampled():
-    """The full workload (64 x 32 heads, 1024 steps) in the launch configuration
-    the benchmark times; every step's output and the final state of 64 sampled
-    heads are checked against the oracle."""
+def test_decode_full_size_every_head():
+    """The full workload (64 sequences x 32 heads, 1024 steps) in the launch
+    configuration the benchmark times: every head's output at every step and
+    every final state are checked against the oracle, which recomputes the
+    chain 8 sequences (256 heads) at a time."""
     inp = ki.workload_decode()
+    steps, N, H = inp.q.shape[:3]
     o, S = _run_chain(inp, device())
-    r = np.random.default_rng(0)
-    pairs = [(int(n), int(h)) for n, h in zip(r.integers(0, 64, 64), r.integers(0, 32, 64))]
-    ns = np.array([p[0] for p in pairs])
-    hs = np.array([p[1] for p in pairs])
-    q, k, v, b, la = (x[:, ns, hs][:, :, None] for x in inp.widened())
-    s0 = inp.initial_state[ns, hs][:, None]
-    o_ref, S_ref = oracle.decode_chain(q, k, v, b, la, s0)
-    check("decode full (64 sampled heads)", rel_err_vectors(o[:, ns, hs], o_ref[:, :, 0]),
-          rel_err_states(S[ns, hs], S_ref[:, 0]))
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
+    gc = GroupCheck(f"decode full, all {N * H} heads x {steps} steps")
+    for n0 in range(0, N, 8):
+        ns = slice(n0, n0 + 8)
+        w = [ki.bf16_to_f32(np.ascontiguousarray(x[:, ns])) for x in (inp.q, inp.k, inp.v, inp.beta)]
+        la = np.ascontiguousarray(inp.log_alpha[:, ns])
+        o_ref, S_ref = gc.timed(oracle.decode_chain, *w, la, inp.initial_state[ns])
+        gc.add(rel_err_vectors(o[:, ns], o_ref), rel_err_states(S[ns], S_ref), 8 * H)
+    assert gc.units == N * H
+    gc.finish()
 
 
 def test_decode_in_place_and_zero_beta():

@@ -5,7 +5,7 @@ import pytest
 import gated_delta_rule_113_amd as kda
 import kda_inputs as ki
 import oracle
-from kda_gpu import check, device, rel_err_states, rel_err_vectors, upload
+from kda_gpu import GroupCheck, check, device, rel_err_states, rel_err_vectors, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -50,17 +50,23 @@ def test_chunked_reduced():
     check("chunked H=4 T=4096", rel_err_vectors(o, o_ref), rel_err_states(S, S_ref))
 
 
-def test_chunked_full_size_sampled_heads():
-    """The full chunked-prefill workload (H=32, T=32768); the oracle
-    recomputes two sampled heads in full (outputs and final states)."""
+def test_chunked_full_size_every_head():
+    """The full chunked-prefill workload (H=32, T=32768) in the launch
+    configuration the benchmark times; the oracle recomputes every head in
+    full (all outputs and final states), 8 heads at a time."""
     inp = ki.workload_chunked()
     o, S = _run(inp, device())
-    heads = [0, 21]
-    sub = ki.workload_chunked(heads=heads)
-    o_ref, S_ref = _oracle(sub)
-    check("chunked full, heads 0 and 21", rel_err_vectors(o[:, :, heads], o_ref),
-          rel_err_states(S[:, heads], S_ref))
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
+    H = inp.q.shape[2]
+    gc = GroupCheck(f"chunked full, all {H} heads")
+    for h0 in range(0, H, 8):
+        hs = slice(h0, h0 + 8)
+        w = [ki.bf16_to_f32(np.ascontiguousarray(x[:, :, hs])) for x in (inp.q, inp.k, inp.v, inp.beta)]
+        la = np.ascontiguousarray(inp.log_alpha[:, :, hs])
+        o_ref, S_ref = gc.timed(oracle.prefill, *w, la, None)
+        gc.add(rel_err_vectors(o[:, :, hs], o_ref), rel_err_states(S[:, hs], S_ref), 8)
+    assert gc.units == H
+    gc.finish()
 
 
 def test_empty_sequence_returns_initial_state():

@@ -80,21 +80,20 @@ def test_decode_slots_small(dtype):
 
 def test_decode_slots_full_size():
     """The batched decode shape (64 sequences x 32 heads) from a pool of 256
-    entries at seeded distinct slots, 4 steps: bit for bit the plain step."""
+    entries at seeded distinct slots, 16 steps: bit for bit the plain step,
+    and every head's outputs and final state against the oracle."""
     rng = np.random.default_rng(23)
     slots = rng.permutation(256)[:64].astype(np.int32)
     inp, pool0, slots, valid, o, pool, o_plain, s_plain = _decode_case(
-        "bf16", N=64, H=32, P=256, slots=slots, steps=4, workload=23)
+        "bf16", N=64, H=32, P=256, slots=slots, steps=16, workload=23)
     assert valid.all()
     assert np.array_equal(o, o_plain)
     assert np.array_equal(pool[slots], s_plain)
     untouched = sorted(set(range(256)) - set(slots.tolist()))
     assert np.array_equal(pool[untouched], pool0[untouched])
-    # one head of one sequence against the oracle over the 4 steps
-    q, k, v, b, la = (x[:, 5:6, 7:8] for x in inp.widened())
-    o_ref, S_ref = oracle.decode_chain(q, k, v, b, la, pool0[slots[5:6], 7:8])
-    check("decode slots full size, one head", rel_err_vectors(o[:, 5:6, 7:8], o_ref),
-          rel_err_states(pool[slots[5:6], 7:8], S_ref))
+    o_ref, S_ref = oracle.decode_chain(*inp.widened(), pool0[slots])
+    check("decode slots full size, all 2048 heads", rel_err_vectors(o, o_ref),
+          rel_err_states(pool[slots], S_ref))
 
 
 # sequence lengths, their initial and final slots in a pool of 8:

@@ -5,7 +5,7 @@ import pytest
 import gated_delta_rule_113_amd as kda
 import kda_inputs as ki
 import oracle
-from kda_gpu import check, device, rel_err_states, rel_err_vectors, upload
+from kda_gpu import GroupCheck, check, device, rel_err_states, rel_err_vectors, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -20,12 +20,13 @@ def _run(inp, dev):
 
 
 def _oracle(inp, heads=None):
-    q, k, v, b, la = inp.widened()
-    s0 = inp.initial_state
-    if heads is not None:
-        q, k, v, b, la = (x[:, :, heads] for x in (q, k, v, b, la))
-        s0 = s0[:, heads]
-    return oracle.varlen_prefill(q, k, v, b, la, inp.cu_seqlens, s0)
+    if heads is None:
+        return oracle.varlen_prefill(*inp.widened(), inp.cu_seqlens, inp.initial_state)
+    # slice before widening: the full packed workload is large
+    w = [ki.bf16_to_f32(np.ascontiguousarray(x[:, :, heads])) if inp.dtype == "bf16"
+         else np.ascontiguousarray(x[:, :, heads]) for x in (inp.q, inp.k, inp.v, inp.beta)]
+    la = np.ascontiguousarray(inp.log_alpha[:, :, heads])
+    return oracle.varlen_prefill(*w, la, inp.cu_seqlens, inp.initial_state[:, heads])
 
 
 def test_varlen_edge_lengths():
@@ -47,16 +48,22 @@ def test_varlen_reduced():
     check("varlen reduced", rel_err_vectors(o[0], o_ref), rel_err_states(S, S_ref))
 
 
-def test_varlen_full_size_sampled_heads():
-    """The full packed workload (16 sequences, lengths in [1024, 65536], H=32);
-    the oracle recomputes heads 3 and 30 of every sequence."""
+def test_varlen_full_size_every_head():
+    """The full packed workload (16 sequences, lengths in [1024, 65536], H=32,
+    even sequences resumed) in the launch configuration the benchmark times;
+    the oracle recomputes every head of every sequence (all outputs and final
+    states), 8 heads at a time."""
     inp = ki.workload_varlen()
     o, S = _run(inp, device())
-    heads = [3, 30]
-    o_ref, S_ref = _oracle(inp, heads)
-    check("varlen full, heads 3 and 30", rel_err_vectors(o[0][:, heads], o_ref),
-          rel_err_states(S[:, heads], S_ref))
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
+    N, H = inp.initial_state.shape[:2]
+    gc = GroupCheck(f"varlen full, {N} sequences x all {H} heads ({int(inp.cu_seqlens[-1])} tokens)")
+    for h0 in range(0, H, 8):
+        heads = list(range(h0, h0 + 8))
+        o_ref, S_ref = gc.timed(_oracle, inp, heads)
+        gc.add(rel_err_vectors(o[0][:, heads], o_ref), rel_err_states(S[:, heads], S_ref), N * 8)
+    assert gc.units == N * H
+    gc.finish()
 
 
 def test_varlen_equals_separate_calls():
