@@ -26,7 +26,7 @@ STATUS_NAMES = {
 KDA_WORKSPACE_AUTO = -1
 # prefill plans, fastest first
 KDA_PLAN_FULL, KDA_PLAN_SEGMENTS, KDA_PLAN_UNSEGMENTED = 0, 1, 2
-EXPORTS = ("kda_prefill", "kda_varlen_prefill", "kda_decode_step", "kda_prefill_raw",
+EXPORTS = ("kda_prefill", "kda_prefill_noalloc", "kda_varlen_prefill", "kda_decode_step", "kda_prefill_raw",
            "kda_varlen_prefill_raw", "kda_decode_step_raw", "kda_decode_tokens",
            "kda_decode_step_slots", "kda_varlen_prefill_slots", "kda_backward",
            "kda_varlen_backward", "kda_prefill_workspace_size",
@@ -69,6 +69,9 @@ def load_library(path: str | None = None):
         lib.kda_prefill.argtypes = [vp, vp, vp, vp, f32p, f32p, f32p, f32p,
                                     i64, i64, i64, i64, i64, ctypes.c_int, vp, i64, vp]
         lib.kda_prefill.restype = ctypes.c_int
+        lib.kda_prefill_noalloc.argtypes = [vp, vp, vp, vp, f32p, f32p, f32p, f32p,
+                                            i64, i64, i64, i64, i64, ctypes.c_int, vp]
+        lib.kda_prefill_noalloc.restype = ctypes.c_int
         lib.kda_prefill_raw.argtypes = lib.kda_prefill.argtypes
         lib.kda_prefill_raw.restype = ctypes.c_int
         lib.kda_varlen_prefill.argtypes = [vp, vp, vp, vp, f32p, vp, i64, i64,

@@ -376,6 +376,40 @@ kda_status kda_prefill_raw(const void* q, const void* k, const void* v, const vo
                         in_dtype, true, workspace, workspace_bytes, stream);
 }
 
+kda_status kda_prefill_noalloc(const void* q, const void* k, const void* v, const void* beta,
+                               const float* log_alpha, const float* initial_state, float* o,
+                               float* final_state, int64_t B, int64_t T, int64_t H, int64_t d_k,
+                               int64_t d_v, kda_dtype in_dtype, void* stream)
+{
+    kda_status st;
+    if ((st = check_dense(B, T, H, d_k, d_v, in_dtype)) != KDA_OK) return st;
+    if (B == 0 || T == 0) {
+        // nothing segmented: the plain call, which needs no workspace here
+        return prefill_impl(q, k, v, beta, log_alpha, initial_state, o, final_state, B, T, H, d_k,
+                            d_v, in_dtype, false, nullptr, 0, stream);
+    }
+    // the pointers are validated before anything touches the device
+    if ((st = check_ptrs({q, k, v, beta, log_alpha, o}, {initial_state, final_state})) != KDA_OK)
+        return st;
+    const int64_t limit = static_cast<int64_t>(kda::kNoallocScratchBytes);
+    if (prefill_uses_scan(in_dtype, false, T, B * T)) {
+        // refuse what the scratch cannot hold without falling back to the
+        // unsegmented plan: the segments plan must fit
+        int n_cu = 0;
+        if ((st = current_cus(&n_cu)) != KDA_OK) return st;
+        const kda::PrefillPlan seg =
+            kda::plan_prefill_scan(false, B, T, B * T, H, n_cu, kda::forced_segment(), 1);
+        if (static_cast<int64_t>(seg.ws_bytes) > limit) return KDA_ERR_WORKSPACE;
+    }
+    void* scratch = nullptr;
+    if (kda::noalloc_scratch(&scratch) != hipSuccess) {
+        (void)hipGetLastError();  // the lookup's own failure, reported as a status
+        return KDA_ERR_HIP;
+    }
+    return prefill_impl(q, k, v, beta, log_alpha, initial_state, o, final_state, B, T, H, d_k, d_v,
+                        in_dtype, false, scratch, limit, stream);
+}
+
 kda_status kda_varlen_prefill(const void* q, const void* k, const void* v, const void* beta,
                               const float* log_alpha, const int32_t* cu_seqlens, int64_t N,
                               int64_t T_total, const float* initial_state, float* o,

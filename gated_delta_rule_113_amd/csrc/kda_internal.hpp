@@ -144,6 +144,15 @@ struct StreamWorkspace {
 void report(const char* what, hipError_t e);
 bool debug_enabled();
 
+// The scratch of kda_prefill_noalloc (kda_noalloc.hip): a file-scope device
+// array of this many bytes per device; *ptr receives its address on the
+// current device (looked up once per device).
+// 160 MiB holds the segments plan of every dense prefill at the automatic
+// segment length on 256 compute units (at most about 144 MiB: fewer than
+// 3 x 256 segment slots of 192 KiB).
+constexpr size_t kNoallocScratchBytes = size_t(160) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // KDA_DEBUG precondition checks (kda_checks.hip): the bits of *violations
 // name what failed.  The gates are n_gates floats (log alpha <= 0 and finite,
 // or with raw only finite); cu_seqlens, if given, n_seq + 1 offsets.  Enqueues

@@ -154,6 +154,31 @@ kda_status kda_prefill(const void *q, const void *k, const void *v, const void *
                        void *stream);
 
 /*
+ * kda_prefill for callers that cannot allocate device memory at all (code
+ * under HIP graph capture, serving loops or harnesses that forbid
+ * allocation): the same arguments and results as kda_prefill without a
+ * workspace argument.  Its workspace is a fixed scratch array of 160 MiB per
+ * device inside the library, held from the library's first use of that
+ * device until the process ends; the call allocates nothing.
+ *   - It takes the fastest plan that fits 160 MiB (see kda_plan).  At the
+ *     automatic segment length the KDA_PLAN_SEGMENTS workspace of a dense
+ *     prefill on an MI355X (256 compute units) is at most about 144 MiB, so
+ *     every such call runs segmented.  A problem whose KDA_PLAN_SEGMENTS
+ *     workspace exceeds 160 MiB (only possible with a short length forced by
+ *     kda_set_prefill_segment) is refused with KDA_ERR_WORKSPACE and nothing
+ *     enqueued, rather than run unsegmented.
+ *   - Every call on one device shares that device's scratch, which keeps the
+ *     last call's contents (nothing in it needs clearing): calls that overlap
+ *     on one device (concurrent streams, or threads) race and give wrong
+ *     results.  Serialise them, e.g. on one stream.
+ */
+kda_status kda_prefill_noalloc(const void *q, const void *k, const void *v, const void *beta,
+                               const float *log_alpha, const float *initial_state,
+                               float *o, float *final_state,
+                               int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v,
+                               kda_dtype in_dtype, void *stream);
+
+/*
  * Packed variable-length prefill of N sequences stored back to back.
  *   q, k, log_alpha : [T_total, H, d_k];  v, o : [T_total, H, d_v];  beta : [T_total, H]
  *   cu_seqlens  : [N + 1] int32, DEVICE memory: sequence n owns token rows

@@ -38,7 +38,7 @@ def _declared():
 
 def test_exports_match_header(lib):
     declared = _declared()
-    assert declared == {"kda_prefill", "kda_varlen_prefill", "kda_decode_step",
+    assert declared == {"kda_prefill", "kda_prefill_noalloc", "kda_varlen_prefill", "kda_decode_step",
                         "kda_prefill_raw", "kda_varlen_prefill_raw", "kda_decode_step_raw",
                         "kda_decode_tokens", "kda_decode_step_slots", "kda_varlen_prefill_slots",
                         "kda_backward", "kda_varlen_backward", "kda_prefill_workspace_size",
@@ -98,6 +98,19 @@ def test_prefill_validation(lib):
     assert prefill(lib, B=0, q=None, k=None, v=None, beta=None, la=None, o=None, s1=None) == OK
     # T = 0 without a final state has nothing to write
     assert prefill(lib, T=0, q=None, k=None, v=None, beta=None, la=None, o=None, s1=None) == OK
+
+
+def test_noalloc_validates_like_the_plain_call(lib):
+    """kda_prefill_noalloc refuses what kda_prefill refuses, before it looks up
+    its scratch on the device."""
+    def noalloc(q=P, k=P, v=P, beta=P, la=P, s0=None, o=P, s1=P, B=1, T=4, H=2, dk=128, dv=128, dt=1):
+        return lib.kda_prefill_noalloc(q, k, v, beta, la, s0, o, s1, B, T, H, dk, dv, dt, None)
+    for kw, expect in (({"q": None}, NULL), ({"o": None}, NULL), ({"k": MIS}, ALIGN),
+                       ({"s1": MIS}, ALIGN), ({"dk": 64}, UNSUP), ({"dt": 2}, DTYPE), ({"H": 0}, SHAPE),
+                       ({"B": -1}, SHAPE), ({"T": 1 << 40}, SHAPE)):
+        assert noalloc(**kw) == expect, kw
+        assert prefill(lib, **kw) == expect, kw
+    assert noalloc(B=0, q=None, o=None, s1=None) == OK
 
 
 def test_raw_entry_points_validate_like_the_plain_ones(lib):
