@@ -728,9 +728,16 @@ BackwardPlan plan_backward(bool packed, int64_t n_seq, int64_t T, int64_t T_tota
     BackwardPlan p;
     const int64_t units = n_seq * H;
     if (units <= 0) return p;
+    const int64_t rows = packed ? T_total : n_seq * T;
+    if (bf16) {
+        // chunked: one workspace slot per (chunk id, head); ids below rows / 64 + sequences + 1
+        p.chunked = true;
+        p.n_ids = rows / 64 + n_seq + 1;
+        p.ws_bytes = static_cast<size_t>(p.n_ids) * H * chunk_backward_bytes_per_chunk();
+        return p;
+    }
     // One checkpoint slot per block of kBackwardBlock tokens: dense, every
     // sequence ceil(T / cb); packed, fewer than T_total / cb + n_seq in all.
-    const int64_t rows = packed ? T_total : n_seq * T;
     const int64_t cb = kBackwardBlock;
     p.n_slots = rows <= 0 ? 0 : packed ? T_total / cb + n_seq : n_seq * ((T + cb - 1) / cb);
     // Long dense bf16 sequences that give the CUs too few (sequence, head)
@@ -765,6 +772,10 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const vo
 {
     const int64_t units = n_seq * H;
     if (units <= 0) return hipSuccess;
+    if (plan.chunked)
+        return launch_backward_chunked(q, k, v, beta, log_alpha, d_o, cu_seqlens, n_seq, T, H,
+                                       initial_state, d_final_state, dq, dk, dv, dbeta, dlog_alpha,
+                                       d_initial_state, plan.n_ids, ws, stream);
     hipError_t e = hipSuccess;
 
     BwdArgs a = {};

@@ -1,0 +1,1442 @@
+// Chunked backward pass of the KDA prefill on bf16 matrix cores.
+//
+// The forward (per head; S is d_k x d_v, rows = forgetting channels)
+//     S_t = (I - b_t k_t k_t^T) Diag(a_t) S_{t-1} + b_t k_t v_t^T,   o_t = S_t^T q_t
+// ("Kimi K3 -- the architecture and infrastructure, explained": section "How
+// the delta rule actually works" gives the update, section "Kimi Delta
+// Attention: the load-bearing choice" the per-channel gate and the blockwise
+// organisation on matrix units; section "Training infrastructure:
+// quantization-aware from SFT onward" that the layer is trained) is regrouped
+// per 64-token chunk.  With G_r the inclusive cumulative log2-decay of each
+// channel within the chunk (gam_r = 2^G_r, gam_L its value at the last token),
+// entering state S0 and B = Diag(b):
+//     Kt = K (.) gam,  Qt = Q (.) gam,  Ke = K (.) gam_L / gam   (row-wise, per channel)
+//     A_ri = sum_c k_rc k_ic 2^(G_rc - G_ic)  (i < r),   P_ri = sum_c q_rc k_ic 2^(G_rc - G_ic)  (i <= r)
+//     T = (I + B A)^-1,  X = Kt S0,  W = V - X,  U = T B W
+//     O = Qt S0 + P U,   S1 = Diag(gam_L) S0 + Ke^T U.
+// Given dO and the gradient dS1 in the leaving state, the chain rule gives
+//     dU = P^T dO + Ke dS1,   dW' = T^T dU  (the gradient in B W),  dV = B dW'
+//     dS0 = Diag(gam_L) dS1 + Qt^T dO - Kt^T B dW'
+//     dQt = dO S0^T,  dKt = -B dW' S0^T,  dKe = U dS1^T,  dgam_L = rowsum(dS1 (.) S0)
+//     dP = dO U^T (i <= r),  dT = dU (B W)^T,  dM = -T^T dT T^T,  dA = B dM (i < r)
+//     db_r = sum_j dW'_rj W_rj + sum_i dM_ri A_ri
+// and, through the decay factors, for every channel c (natural-log units:
+// 2^(G_r - G_i) = e^(L_r - L_i) with L the cumulative log-decay)
+//     dq_r += sum_{i<=r} dP_ri k_i e^(L_r - L_i),   dk_r += sum_{i<r} dA_ri k_i e^(L_r - L_i)
+//     dk_i += sum_{r>=i} (dP_ri q_r + dA_ri k_r) e^(L_r - L_i)
+//     dL_r = q_r dq_r(P) + k_r dk_r(A rows) - k_r dk_r(columns)
+//           + Qt dQt + Kt dKt - Ke dKe   (+ at the last token: sum_r Ke dKe + gam_L dgam_L)
+// and d log a_j = sum_{r >= j} dL_r within the chunk (L_r = sum_{j <= r} log a_j).
+// For the chunk's first token that sum is taken in closed form: a uniform
+// shift of L over the chunk leaves A, P and Ke unchanged, so
+//     d log a_0 = sum_r (Qt dQt + Kt dKt)_r + gam_L dgam_L,
+// every term of which is proportional to S0 (so it is exactly zero for a
+// sequence that starts from a zero state, where the terms of the plain sum
+// would cancel only up to rounding).
+//
+// Kernels (one head of one sequence is a "unit"; chunks are numbered per head
+// by the id floor(row0 / 64) + sequence + chunk, unique and below rows / 64 +
+// sequences + 1, so dense and packed input share one workspace layout):
+//   prep   (one workgroup per chunk)  A, P and T of every chunk;
+//   states (one per unit, in order)   the entering state S0 of every chunk;
+//   dstate (one per unit, reversed)   the gradient dS1 in every chunk's leaving
+//                                     state, and the initial-state gradient;
+//   grads  (one per chunk)            dV, the S0/dS1 parts of dq, dk and dL,
+//                                     db's first term, dP and dT;
+//   intra  (one per chunk)            dM, dA, db's second term, the decay
+//                                     products and the chunk's reverse
+//                                     cumulative sum of dL into d log a.
+//
+// Matrix products run on v_mfma_f32_16x16x32_bf16 with every operand split
+// into hi + lo bf16 (hi*hi + hi*lo + lo*hi, fp32 accumulation), as in the
+// prefill.  Operands in LDS are stored as "images": 16 x 32 tiles in lane
+// order, so a fragment is one conflict-free 16-byte read per lane.  State-sized
+// matrices stay in accumulator layout in registers; with the contraction index
+// of a 32-step bound to (lane group g, slot j) as 16 (j >> 2) + 4 g + (j & 3),
+// two accumulator tiles are directly the B operand of the next product (PERM
+// images use the same binding for their A operand).
+//
+// Decay factors never overflow: in the off-diagonal 16 x 16 blocks (rows r in
+// block R, columns i in an earlier block) 2^(G_r - G_i) is split at the last
+// token of block R - 1 into two factors <= 1; inside the diagonal blocks it is
+// formed pairwise, 2^(G_r - G_i) <= 1.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kda_device.hpp"
+#include "kda_internal.hpp"
+
+namespace kda {
+namespace {
+
+constexpr int CH = 64;                      // tokens per chunk
+constexpr int SS = kDim * kDim;             // floats per state
+constexpr int TSZ = CH * CH;                // floats per 64 x 64 tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct ChunkBwdArgs {
+    const bf16_t* q;
+    const bf16_t* k;
+    const bf16_t* v;
+    const bf16_t* beta;
+    const float* la;
+    const float* d_o;
+    const int32_t* cu;   // packed row offsets [n_seq + 1], or null (dense: T rows each)
+    int64_t T;
+    int64_t n_seq;
+    int H;
+    const float* s0;     // [n_seq, H, 128, 128] or null (zeros)
+    const float* d_sT;   // [n_seq, H, 128, 128] or null (zeros)
+    float* dq;
+    float* dk;
+    float* dv;
+    float* dbeta;
+    float* dla;
+    float* ds0;          // [n_seq, H, 128, 128] or null (not written)
+    float* ws_s0;        // [ids][H][128][128]  entering state of every chunk
+    float* ws_ds;        // [ids][H][128][128]  gradient in every chunk's leaving state
+    float* ws_apt;       // [ids][H][3][64][64] A, P, T
+    float* ws_dpt;       // [ids][H][kDptFloats] dP, dT, last-token dL terms
+};
+
+// dP and dT (64 x 64 each), the last-token terms of dL (128) and the
+// first-token d log alpha (128)
+constexpr int kDptFloats = 2 * TSZ + 2 * kDim;
+
+__device__ __forceinline__ int64_t seq_row0(const ChunkBwdArgs& a, int64_t n)
+{
+    return a.cu ? static_cast<int64_t>(a.cu[n]) : n * a.T;
+}
+__device__ __forceinline__ int64_t seq_len(const ChunkBwdArgs& a, int64_t n)
+{
+    return a.cu ? static_cast<int64_t>(a.cu[n + 1]) - a.cu[n] : a.T;
+}
+__device__ __forceinline__ int64_t chunk_id(int64_t row0, int64_t n, int64_t c)
+{
+    return (row0 >> 6) + n + c;
+}
+
+// Chunk id -> (sequence, chunk); false for ids that name no chunk.
+__device__ bool locate(const ChunkBwdArgs& a, int64_t id, int64_t& n, int64_t& c)
+{
+    int64_t lo = 0, hi = a.n_seq;  // the last n with chunk_id(row0(n), n, 0) <= id
+    while (hi - lo > 1) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (chunk_id(seq_row0(a, mid), mid, 0) <= id) lo = mid;
+        else hi = mid;
+    }
+    n = lo;
+    c = id - chunk_id(seq_row0(a, lo), lo, 0);
+    return c >= 0 && c * CH < seq_len(a, lo);
+}
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// ---------------------------------------------------------------- splits
+
+// x0, x1 -> (hi pair, lo pair) of bf16, each packed in 32 bits:
+// hi = bf16(x) (nearest even), lo = bf16(x - hi).
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& h, uint32_t& l)
+{
+    h = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x0, x1}, bf16x2));
+    uint32_t u = h;
+    asm("" : "+v"(u));  // read the hi values back from the packed bits
+    l = __builtin_bit_cast(uint32_t,
+                           __builtin_convertvector((f32x2){x0 - bf_lo(u), x1 - bf_hi(u)}, bf16x2));
+}
+
+// Eight values -> hi and lo bf16x8.
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8& h, bf16x8& l)
+{
+    uint32_t hu[4], lu[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) split2(x[2 * j], x[2 * j + 1], hu[j], lu[j]);
+    h = __builtin_bit_cast(bf16x8, (uint4){hu[0], hu[1], hu[2], hu[3]});
+    l = __builtin_bit_cast(bf16x8, (uint4){lu[0], lu[1], lu[2], lu[3]});
+}
+
+// Two accumulator tiles (rows 4g..4g+3 of tiles t0 and t1 in lane group g) as
+// the B operand of a product summing over their rows (PERM binding).
+__device__ __forceinline__ void bfrag(f32x4 t0, f32x4 t1, bf16x8& h, bf16x8& l)
+{
+    const float x[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+    split8(x, h, l);
+}
+
+// hi*hi + hi*lo + lo*hi
+__device__ __forceinline__ f32x4 mma3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, f32x4 c)
+{
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, c, 0, 0, 0);
+    return c;
+}
+
+// ---------------------------------------------------------------- images
+//
+// An image of an R x K matrix Z (R a multiple of 16, K of 32) holds its 16 x 32
+// tiles (row block rb, k-step s: tile rb * (K / 32) + s) in lane order: lane
+// l = (row & 15) + 16 g keeps the 8 slots j of its row for slot group g, slot
+// (g, j) holding k index 32 s + 8 g + j (natural) or 32 s + 16 (j >> 2) + 4 g +
+// (j & 3) (PERM).  The hi plane comes first, the lo plane `plane` bytes later
+// (plane = R * K * 2).
+
+template <bool PERM>
+__device__ __forceinline__ int img_off(int row, int kidx, int ks)
+{
+    const int kk = kidx & 31;
+    int g, j;
+    if (PERM) {
+        g = (kk >> 2) & 3;
+        j = ((kk >> 4) << 2) | (kk & 3);
+    } else {
+        g = kk >> 3;
+        j = kk & 7;
+    }
+    return (((row >> 4) * ks + (kidx >> 5)) << 10) + (((row & 15) + 16 * g) << 4) + (j << 1);
+}
+
+// Store the split pair (x0 at kidx, x1 at kidx + 1; kidx even).
+template <bool PERM>
+__device__ __forceinline__ void img_put2(char* img, int plane, int row, int kidx, int ks, float x0,
+                                         float x1)
+{
+    uint32_t h, l;
+    split2(x0, x1, h, l);
+    const int off = img_off<PERM>(row, kidx, ks);
+    *reinterpret_cast<uint32_t*>(img + off) = h;
+    *reinterpret_cast<uint32_t*>(img + plane + off) = l;
+}
+
+__device__ __forceinline__ void img_frag(const char* img, int plane, int tile, int lane, bf16x8& h,
+                                         bf16x8& l)
+{
+    h = *reinterpret_cast<const bf16x8*>(img + (tile << 10) + (lane << 4));
+    l = *reinterpret_cast<const bf16x8*>(img + plane + (tile << 10) + (lane << 4));
+}
+
+// ---------------------------------------------------------------- staging
+//
+// Thread t stages channels 2 (t & 63), +1 for tokens TOK * (t >> 6) .. +TOK-1
+// of one chunk (NT / 64 token groups): log alpha becomes the inclusive
+// cumulative log2-decay G (the group prefix through `tot`, an LDS array of
+// NT / 64 x 128 floats), k and (WITHQ) q are widened.  Rows from L on are
+// zeros (so they decay nothing and write nothing).
+template <int NT>
+struct Staged {
+    static constexpr int TG = NT / 64;
+    static constexpr int TOK = CH / TG;
+    int c0;                 // first of the thread's two channels
+    int r0;                 // first of its tokens
+    float g[TOK][2];        // G
+    float kk[TOK][2];
+    float qq[TOK][2];
+    float gl[2];            // G at the chunk's last token
+};
+
+template <int NT, bool WITHQ>
+__device__ __forceinline__ void stage(const ChunkBwdArgs& a, int64_t row0c, int L, int h, float* tot,
+                                      Staged<NT>& s)
+{
+    constexpr int TG = Staged<NT>::TG, TOK = Staged<NT>::TOK;
+    const int t = threadIdx.x;
+    s.c0 = 2 * (t & 63);
+    s.r0 = TOK * (t >> 6);
+    const int64_t rstride = static_cast<int64_t>(a.H) * kDim;
+    const int64_t e0 = (row0c * a.H + h) * kDim + s.c0;
+    float run0 = 0.f, run1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < TOK; ++j) {
+        const int r = s.r0 + j;
+        float2 l2 = make_float2(0.f, 0.f);
+        uint32_t kb = 0, qb = 0;
+        if (r < L) {
+            const int64_t e = e0 + r * rstride;
+            l2 = *reinterpret_cast<const float2*>(a.la + e);
+            kb = *reinterpret_cast<const uint32_t*>(a.k + e);
+            if (WITHQ) qb = *reinterpret_cast<const uint32_t*>(a.q + e);
+        }
+        run0 += l2.x * kLog2e;
+        run1 += l2.y * kLog2e;
+        s.g[j][0] = run0;
+        s.g[j][1] = run1;
+        s.kk[j][0] = bf_lo(kb);
+        s.kk[j][1] = bf_hi(kb);
+        s.qq[j][0] = bf_lo(qb);
+        s.qq[j][1] = bf_hi(qb);
+    }
+    tot[(t >> 6) * kDim + s.c0] = run0;
+    tot[(t >> 6) * kDim + s.c0 + 1] = run1;
+    __syncthreads();
+    float p0 = 0.f, p1 = 0.f, a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int u = 0; u < TG; ++u) {
+        const float x0 = tot[u * kDim + s.c0], x1 = tot[u * kDim + s.c0 + 1];
+        if (u < (t >> 6)) {
+            p0 += x0;
+            p1 += x1;
+        }
+        a0 += x0;
+        a1 += x1;
+    }
+#pragma unroll
+    for (int j = 0; j < TOK; ++j) {
+        s.g[j][0] += p0;
+        s.g[j][1] += p1;
+    }
+    s.gl[0] = a0;
+    s.gl[1] = a1;
+}
+
+// beta of the chunk's rows (zeros from L on) into LDS, by the first 64 threads
+__device__ __forceinline__ void stage_beta(const ChunkBwdArgs& a, int64_t row0c, int L, int h, float* bs)
+{
+    const int t = threadIdx.x;
+    if (t < CH) bs[t] = t < L ? widen(a.beta[(row0c + t) * a.H + h]) : 0.f;
+}
+
+// A 64 x 64 fp32 tile from global memory into an image: TRANS = false stores
+// Z[r][i] at (row r, k i), TRANS = true at (row i, k r); PERM binding.
+template <bool TRANS, int NT>
+__device__ __forceinline__ void tile_image(const float* src, char* img)
+{
+    constexpr int plane = CH * CH * 2;
+    for (int p = threadIdx.x; p < TSZ / 2; p += NT) {
+        if (!TRANS) {
+            const int r = p >> 5, i = 2 * (p & 31);
+            const float2 x = *reinterpret_cast<const float2*>(src + r * CH + i);
+            img_put2<true>(img, plane, r, i, 2, x.x, x.y);
+        } else {
+            // consecutive threads take consecutive columns i of one pair of rows
+            const int i = p & 63, r = 2 * (p >> 6);
+            img_put2<true>(img, plane, i, r, 2, src[r * CH + i], src[(r + 1) * CH + i]);
+        }
+    }
+}
+
+// ================================================================ prep
+//
+// A, P and T of one chunk of one head (grid: chunk ids x heads; 256 threads).
+
+constexpr int PREP_NT = 256;
+constexpr int GLD = 132;     // fp32 row stride of the G tile
+constexpr int BLD = 136;     // bf16 row stride of the k and q tiles
+constexpr int TLD = 65;      // fp32 row stride of 64 x 64 tiles
+
+// The six off-diagonal 16 x 16 blocks (row block, column block).
+__device__ __forceinline__ void offdiag_block(int p, int& R, int& I)
+{
+    R = p < 1 ? 1 : p < 3 ? 2 : 3;
+    I = p - (R * (R - 1)) / 2;
+}
+
+__global__ __launch_bounds__(PREP_NT) void chunk_prep_kernel(const ChunkBwdArgs a)
+{
+    __shared__ __attribute__((aligned(16))) float Gs[CH * GLD];
+    __shared__ __attribute__((aligned(16))) __bf16 Ks[CH * BLD];
+    __shared__ __attribute__((aligned(16))) __bf16 Qs[CH * BLD];
+    __shared__ float As[CH * TLD], Ps[CH * TLD], Ts[CH * TLD];
+    __shared__ float Ys[3 * 256];
+    __shared__ float bs[CH];
+    __shared__ float tot[(PREP_NT / 64) * kDim];
+
+    const int H = a.H;
+    const int64_t id = blockIdx.x / H;
+    const int h = static_cast<int>(blockIdx.x - id * H);
+    int64_t n, c;
+    if (!locate(a, id, n, c)) return;
+    const int64_t row0c = seq_row0(a, n) + c * CH;
+    const int L = static_cast<int>(min<int64_t>(CH, seq_len(a, n) - c * CH));
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+
+    Staged<PREP_NT> st;
+    stage<PREP_NT, true>(a, row0c, L, h, tot, st);
+    stage_beta(a, row0c, L, h, bs);
+#pragma unroll
+    for (int j = 0; j < Staged<PREP_NT>::TOK; ++j) {
+        const int r = st.r0 + j;
+        *reinterpret_cast<float2*>(&Gs[r * GLD + st.c0]) = make_float2(st.g[j][0], st.g[j][1]);
+        *reinterpret_cast<bf16x2*>(&Ks[r * BLD + st.c0]) = (bf16x2){(__bf16)st.kk[j][0], (__bf16)st.kk[j][1]};
+        *reinterpret_cast<bf16x2*>(&Qs[r * BLD + st.c0]) = (bf16x2){(__bf16)st.qq[j][0], (__bf16)st.qq[j][1]};
+    }
+    __syncthreads();
+
+    // ---- off-diagonal blocks on the matrix cores: rows r of block R carry
+    // 2^(G_r - rho), columns i of block I < R carry 2^(rho - G_i), with rho =
+    // G at the last token of block R - 1 (both factors <= 1).
+    for (int p = wave; p < 6; p += PREP_NT / 64) {
+        int R, I;
+        offdiag_block(p, R, I);
+        const int rr = 16 * R + (lane & 15), ii = 16 * I + (lane & 15), g = lane >> 4;
+        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = accA;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int cc = 32 * s + 8 * g;
+            float fk[8], fq[8], fh[8];
+            const bf16x8 kr = *reinterpret_cast<const bf16x8*>(&Ks[rr * BLD + cc]);
+            const bf16x8 qr = *reinterpret_cast<const bf16x8*>(&Qs[rr * BLD + cc]);
+            const bf16x8 ki = *reinterpret_cast<const bf16x8*>(&Ks[ii * BLD + cc]);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float rho = Gs[(16 * R - 1) * GLD + cc + j];
+                const float fr = ex2(Gs[rr * GLD + cc + j] - rho);
+                fk[j] = (float)kr[j] * fr;
+                fq[j] = (float)qr[j] * fr;
+                fh[j] = (float)ki[j] * ex2(rho - Gs[ii * GLD + cc + j]);
+            }
+            bf16x8 kh, kl, qh, ql, hh, hl;
+            split8(fk, kh, kl);
+            split8(fq, qh, ql);
+            split8(fh, hh, hl);
+            accA = mma3(kh, kl, hh, hl, accA);
+            accP = mma3(qh, ql, hh, hl, accP);
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int r = 16 * R + 4 * g + x;
+            As[r * TLD + ii] = accA[x];
+            Ps[r * TLD + ii] = accP[x];
+        }
+    }
+
+    // ---- diagonal blocks, pairwise: lane (i, channel quarter) of wave R
+    // sums over its 32 channels for every row r of the block, then over the
+    // four quarters.
+    for (int R = wave; R < 4; R += PREP_NT / 64) {
+        const int iloc = lane & 15, cq = lane >> 4;
+        const int i = 16 * R + iloc;
+        float gi[32], ki[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            gi[j] = Gs[i * GLD + 32 * cq + j];
+            ki[j] = (float)Ks[i * BLD + 32 * cq + j];
+        }
+        for (int rl = 0; rl < 16; ++rl) {
+            const int r = 16 * R + rl;
+            float sa = 0.f, sp = 0.f;
+#pragma unroll
+            for (int j = 0; j < 32; ++j) {
+                const int cc = 32 * cq + j;
+                const float e = ex2(fminf(Gs[r * GLD + cc] - gi[j], 0.f));
+                const float ke = ki[j] * e;
+                sa += (float)Ks[r * BLD + cc] * ke;
+                sp += (float)Qs[r * BLD + cc] * ke;
+            }
+            sa += __shfl_xor(sa, 16);
+            sa += __shfl_xor(sa, 32);
+            sp += __shfl_xor(sp, 16);
+            sp += __shfl_xor(sp, 32);
+            if (cq == 0) {
+                As[r * TLD + i] = rl > iloc ? sa : 0.f;
+                Ps[r * TLD + i] = rl >= iloc ? sp : 0.f;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- T = (I + Diag(beta) A)^-1, unit lower triangular, by 16 x 16 blocks:
+    // the diagonal blocks by forward substitution (lane = column), then
+    // T_RI = -T_RR sum_{I <= J < R} N_RJ T_JI in order of R - I (N = Diag(beta) A).
+    if (lane < 16) {
+        const int R = wave, j = lane;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float acc = r == j ? 1.f : 0.f;
+            if (r > j) {
+                const int gr = 16 * R + r;
+#pragma unroll
+                for (int m = 0; m < 16; ++m)
+                    if (m < r) acc -= bs[gr] * As[gr * TLD + 16 * R + m] * x[m];
+            }
+            x[r] = acc;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Ts[(16 * R + r) * TLD + 16 * R + j] = x[r];
+    }
+    __syncthreads();
+    for (int d = 1; d < 4; ++d) {
+        // Y = sum_J N_RJ T_JI for the 4 - d blocks of this distance
+        const int rl = t >> 4, il = t & 15;
+        for (int R = d; R < 4; ++R) {
+            const int I = R - d, r = 16 * R + rl;
+            float y = 0.f;
+            for (int J = I; J < R; ++J)
+#pragma unroll
+                for (int m = 0; m < 16; ++m)
+                    y += bs[r] * As[r * TLD + 16 * J + m] * Ts[(16 * J + m) * TLD + 16 * I + il];
+            Ys[(R - d) * 256 + rl * 16 + il] = y;
+        }
+        __syncthreads();
+        for (int R = d; R < 4; ++R) {
+            const int I = R - d, r = 16 * R + rl;
+            float x = 0.f;
+#pragma unroll
+            for (int m = 0; m < 16; ++m) x -= Ts[r * TLD + 16 * R + m] * Ys[(R - d) * 256 + m * 16 + il];
+            Ts[r * TLD + 16 * I + il] = x;
+        }
+        __syncthreads();
+    }
+
+    // ---- out: A (i < r), P (i <= r), T (i < r, unit diagonal), zeros elsewhere
+    float* dst = a.ws_apt + (id * H + h) * (3 * TSZ);
+    for (int e = t; e < TSZ; e += PREP_NT) {
+        const int r = e >> 6, i = e & 63;
+        dst[e] = i < r ? As[r * TLD + i] : 0.f;
+        dst[TSZ + e] = i <= r ? Ps[r * TLD + i] : 0.f;
+        dst[2 * TSZ + e] = i < r ? Ts[r * TLD + i] : (i == r ? 1.f : 0.f);
+    }
+}
+
+// ================================================================ states
+//
+// The entering state S0 of every chunk of one unit (grid: units; 512 threads).
+// Wave w holds state columns 16w..16w+15 in accumulator layout: S[t][x] is
+// row 16t + 4g + x of column 16w + (lane & 15), g = lane >> 4.
+//   X = Kt S0,  W = V - X,  U = T B W,  S1 = Diag(gam_L) S0 + Ke^T U.
+
+constexpr int SEQ_NT = 512;
+
+__global__ __launch_bounds__(SEQ_NT, 1) void chunk_states_kernel(const ChunkBwdArgs a)
+{
+    constexpr int KT_PL = CH * kDim * 2, KE_PL = kDim * CH * 2, T_PL = CH * CH * 2;
+    __shared__ __attribute__((aligned(16))) char KT[2 * KT_PL];   // Kt: rows r, k = channels
+    __shared__ __attribute__((aligned(16))) char KE[2 * KE_PL];   // Ke^T: rows c, k = tokens
+    __shared__ __attribute__((aligned(16))) char TI[2 * T_PL];    // T: rows r, k = i
+    __shared__ float tot[(SEQ_NT / 64) * kDim];
+    __shared__ float bs[CH], gls[kDim];
+
+    const int H = a.H;
+    const int64_t n = blockIdx.x / H;
+    const int h = static_cast<int>(blockIdx.x - n * H);
+    const int64_t row0 = seq_row0(a, n), len = seq_len(a, n);
+    const int64_t nch = (len + CH - 1) / CH;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 4;
+    const int col = 16 * wave + (lane & 15);
+
+    f32x4 S[8];
+    {
+        const float* s0 = a.s0 ? a.s0 + (n * H + h) * SS : nullptr;
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) S[tt][x] = s0 ? s0[(16 * tt + 4 * g + x) * kDim + col] : 0.f;
+    }
+
+    for (int64_t c = 0; c < nch; ++c) {
+        const int64_t row0c = row0 + c * CH;
+        const int L = static_cast<int>(min<int64_t>(CH, len - c * CH));
+        const int64_t id = chunk_id(row0, n, c);
+        __syncthreads();  // the previous chunk's products are done with the images
+        tile_image<false, SEQ_NT>(a.ws_apt + (id * H + h) * (3 * TSZ) + 2 * TSZ, TI);
+        Staged<SEQ_NT> st;
+        stage<SEQ_NT, false>(a, row0c, L, h, tot, st);
+        stage_beta(a, row0c, L, h, bs);
+#pragma unroll
+        for (int j = 0; j < Staged<SEQ_NT>::TOK; ++j) {
+            const int r = st.r0 + j;
+            img_put2<true>(KT, KT_PL, r, st.c0, 4, st.kk[j][0] * ex2(st.g[j][0]),
+                           st.kk[j][1] * ex2(st.g[j][1]));
+        }
+#pragma unroll
+        for (int j = 0; j < Staged<SEQ_NT>::TOK; j += 2) {
+            const int r = st.r0 + j;
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                img_put2<true>(KE, KE_PL, st.c0 + u, r, 2, st.kk[j][u] * ex2(st.gl[u] - st.g[j][u]),
+                               st.kk[j + 1][u] * ex2(st.gl[u] - st.g[j + 1][u]));
+        }
+        if (st.r0 == 0) {
+            gls[st.c0] = ex2(st.gl[0]);
+            gls[st.c0 + 1] = ex2(st.gl[1]);
+        }
+        __syncthreads();
+
+        // X = Kt S0 (sum over channels: B from S, 4 steps)
+        bf16x8 bh[4], bl[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) bfrag(S[2 * s], S[2 * s + 1], bh[s], bl[s]);
+        f32x4 X[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            X[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                bf16x8 ah, al;
+                img_frag(KT, KT_PL, m * 4 + s, lane, ah, al);
+                X[m] = mma3(ah, al, bh[s], bl[s], X[m]);
+            }
+        }
+        // B W = B (V - X)
+        const int64_t vrow = (row0c * H + h) * kDim + col;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int r = 16 * m + 4 * g + x;
+                const float v = r < L ? widen(a.v[vrow + static_cast<int64_t>(r) * H * kDim]) : 0.f;
+                X[m][x] = bs[r] * (v - X[m][x]);
+            }
+        // U = T (B W) (sum over tokens: 2 steps)
+        bf16x8 wh[2], wl[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) bfrag(X[2 * s], X[2 * s + 1], wh[s], wl[s]);
+        f32x4 U[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            U[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                bf16x8 ah, al;
+                img_frag(TI, T_PL, m * 2 + s, lane, ah, al);
+                U[m] = mma3(ah, al, wh[s], wl[s], U[m]);
+            }
+        }
+        // checkpoint S0, then S1 = Diag(gam_L) S0 + Ke^T U
+        float* dst = a.ws_s0 + (id * H + h) * SS;
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) dst[(16 * tt + 4 * g + x) * kDim + col] = S[tt][x];
+        bf16x8 uh[2], ul[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) bfrag(U[2 * s], U[2 * s + 1], uh[s], ul[s]);
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) S[tt][x] *= gls[16 * tt + 4 * g + x];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                bf16x8 ah, al;
+                img_frag(KE, KE_PL, tt * 2 + s, lane, ah, al);
+                S[tt] = mma3(ah, al, uh[s], ul[s], S[tt]);
+            }
+        }
+    }
+}
+
+// ================================================================ dstate
+//
+// The gradient dS1 in the leaving state of every chunk of one unit, last
+// chunk first (grid: units; 512 threads; the layout of the states kernel),
+// and the initial-state gradient:
+//   dU = P^T dO + Ke dS1,  dW' = T^T dU,  dS0 = Diag(gam_L) dS1 + Qt^T dO - Kt^T B dW'.
+
+__global__ __launch_bounds__(SEQ_NT, 1) void chunk_dstate_kernel(const ChunkBwdArgs a)
+{
+    constexpr int KE_PL = CH * kDim * 2, TT_PL = kDim * CH * 2, T_PL = CH * CH * 2;
+    __shared__ __attribute__((aligned(16))) char KE[2 * KE_PL];    // Ke: rows i, k = channels
+    __shared__ __attribute__((aligned(16))) char QTT[2 * TT_PL];   // Qt^T: rows c, k = tokens
+    __shared__ __attribute__((aligned(16))) char KTT[2 * TT_PL];   // Kt^T: rows c, k = tokens
+    __shared__ __attribute__((aligned(16))) char PT[2 * T_PL];     // P^T: rows i, k = r
+    __shared__ __attribute__((aligned(16))) char TT[2 * T_PL];     // T^T: rows i, k = r
+    __shared__ float tot[(SEQ_NT / 64) * kDim];
+    __shared__ float bs[CH], gls[kDim];
+
+    const int H = a.H;
+    const int64_t n = blockIdx.x / H;
+    const int h = static_cast<int>(blockIdx.x - n * H);
+    const int64_t row0 = seq_row0(a, n), len = seq_len(a, n);
+    const int64_t nch = (len + CH - 1) / CH;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 4;
+    const int col = 16 * wave + (lane & 15);
+
+    f32x4 dS[8];
+    {
+        const float* src = a.d_sT ? a.d_sT + (n * H + h) * SS : nullptr;
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) dS[tt][x] = src ? src[(16 * tt + 4 * g + x) * kDim + col] : 0.f;
+    }
+
+    for (int64_t c = nch - 1; c >= 0; --c) {
+        const int64_t row0c = row0 + c * CH;
+        const int L = static_cast<int>(min<int64_t>(CH, len - c * CH));
+        const int64_t id = chunk_id(row0, n, c);
+        __syncthreads();
+        const float* apt = a.ws_apt + (id * H + h) * (3 * TSZ);
+        tile_image<true, SEQ_NT>(apt + TSZ, PT);
+        tile_image<true, SEQ_NT>(apt + 2 * TSZ, TT);
+        Staged<SEQ_NT> st;
+        stage<SEQ_NT, true>(a, row0c, L, h, tot, st);
+        stage_beta(a, row0c, L, h, bs);
+#pragma unroll
+        for (int j = 0; j < Staged<SEQ_NT>::TOK; ++j) {
+            const int r = st.r0 + j;
+            img_put2<true>(KE, KE_PL, r, st.c0, 4, st.kk[j][0] * ex2(st.gl[0] - st.g[j][0]),
+                           st.kk[j][1] * ex2(st.gl[1] - st.g[j][1]));
+        }
+#pragma unroll
+        for (int j = 0; j < Staged<SEQ_NT>::TOK; j += 2) {
+            const int r = st.r0 + j;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const float e0 = ex2(st.g[j][u]), e1 = ex2(st.g[j + 1][u]);
+                img_put2<true>(QTT, TT_PL, st.c0 + u, r, 2, st.qq[j][u] * e0, st.qq[j + 1][u] * e1);
+                img_put2<true>(KTT, TT_PL, st.c0 + u, r, 2, st.kk[j][u] * e0, st.kk[j + 1][u] * e1);
+            }
+        }
+        if (st.r0 == 0) {
+            gls[st.c0] = ex2(st.gl[0]);
+            gls[st.c0 + 1] = ex2(st.gl[1]);
+        }
+        // dO in accumulator layout (rows r = 16m + 4g + x of column col)
+        f32x4 dO[4];
+        const int64_t orow = (row0c * H + h) * kDim + col;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int r = 16 * m + 4 * g + x;
+                dO[m][x] = r < L ? a.d_o[orow + static_cast<int64_t>(r) * H * kDim] : 0.f;
+            }
+        __syncthreads();
+
+        bf16x8 oh[2], ol[2], sh[4], sl[4];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) bfrag(dO[2 * s], dO[2 * s + 1], oh[s], ol[s]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) bfrag(dS[2 * s], dS[2 * s + 1], sh[s], sl[s]);
+        // dU = P^T dO + Ke dS1
+        f32x4 dU[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            dU[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                bf16x8 ah, al;
+                img_frag(PT, T_PL, m * 2 + s, lane, ah, al);
+                dU[m] = mma3(ah, al, oh[s], ol[s], dU[m]);
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                bf16x8 ah, al;
+                img_frag(KE, KE_PL, m * 4 + s, lane, ah, al);
+                dU[m] = mma3(ah, al, sh[s], sl[s], dU[m]);
+            }
+        }
+        // dW' = T^T dU, then -B dW'
+        bf16x8 uh[2], ul[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) bfrag(dU[2 * s], dU[2 * s + 1], uh[s], ul[s]);
+        f32x4 nW[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            nW[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                bf16x8 ah, al;
+                img_frag(TT, T_PL, m * 2 + s, lane, ah, al);
+                nW[m] = mma3(ah, al, uh[s], ul[s], nW[m]);
+            }
+#pragma unroll
+            for (int x = 0; x < 4; ++x) nW[m][x] *= -bs[16 * m + 4 * g + x];
+        }
+        // the gradient in this chunk's leaving state
+        float* dst = a.ws_ds + (id * H + h) * SS;
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) dst[(16 * tt + 4 * g + x) * kDim + col] = dS[tt][x];
+        // dS0 = Diag(gam_L) dS1 + Qt^T dO - Kt^T B dW'
+        bf16x8 wh[2], wl[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) bfrag(nW[2 * s], nW[2 * s + 1], wh[s], wl[s]);
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) dS[tt][x] *= gls[16 * tt + 4 * g + x];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                bf16x8 ah, al;
+                img_frag(QTT, TT_PL, tt * 2 + s, lane, ah, al);
+                dS[tt] = mma3(ah, al, oh[s], ol[s], dS[tt]);
+                img_frag(KTT, TT_PL, tt * 2 + s, lane, ah, al);
+                dS[tt] = mma3(ah, al, wh[s], wl[s], dS[tt]);
+            }
+        }
+    }
+    if (a.ds0) {
+        float* dst = a.ds0 + (n * H + h) * SS;
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) dst[(16 * tt + 4 * g + x) * kDim + col] = dS[tt][x];
+    }
+}
+
+// ================================================================ grads
+//
+// Per chunk of one head (grid: chunk ids x heads; 512 threads).
+// Phase A, wave w on value columns 16w..16w+15 (accumulator layout):
+//   X = Kt S0, W = V - X, U = T B W, dU = P^T dO + Ke dS1, dW' = T^T dU;
+//   writes dv = B dW' and the row sums of dW' (.) W (db, first term).
+// Phase B, wave w on channels 16w..16w+15 (sums over the value columns j,
+// from LDS images of dO, -B dW' and U and the rows of S0 and dS1 read from
+// the workspaces as B operands):
+//   dQt = dO S0^T, dKt = -B dW' S0^T, dKe = U dS1^T, dgam_L = rowsum(dS1 (.) S0);
+//   writes dq = dQt gam, dk = dKt gam + dKe gam_L / gam and
+//   dL = Qt dQt + Kt dKt - Ke dKe (the intra kernel adds the rest), and the
+//   last-token terms sum_r Ke dKe + gam_L dgam_L; dP = dO U^T (lower blocks).
+// Phase C: dT = dU (B W)^T (lower blocks) from images of dU and B W.
+
+__global__ __launch_bounds__(SEQ_NT, 1) void chunk_grads_kernel(const ChunkBwdArgs a)
+{
+    constexpr int KT_PL = CH * kDim * 2, T_PL = CH * CH * 2;
+    // phase A: Kt | Ke | T | P^T | T^T;  phase B: dO | -B dW' | U;  phase C: dU | B W
+    constexpr int OFF_KT = 0, OFF_KE = 2 * KT_PL, OFF_TI = 4 * KT_PL, OFF_PT = OFF_TI + 2 * T_PL,
+                  OFF_TT = OFF_PT + 2 * T_PL, REGION = OFF_TT + 2 * T_PL;
+    constexpr int OFF_I0 = 0, OFF_I1 = 2 * KT_PL, OFF_I2 = 4 * KT_PL;
+    static_assert(6 * KT_PL <= REGION, "phase B images fit the phase A region");
+    __shared__ __attribute__((aligned(16))) char img[REGION];
+    __shared__ __attribute__((aligned(16))) float Gs[CH * GLD];
+    __shared__ float tot[(SEQ_NT / 64) * kDim];
+    __shared__ float bs[CH], gLs[kDim], dbr[SEQ_NT / 64][CH], dpd[SEQ_NT / 64][CH];
+
+    const int H = a.H;
+    const int64_t id = blockIdx.x / H;
+    const int h = static_cast<int>(blockIdx.x - id * H);
+    int64_t n, c;
+    if (!locate(a, id, n, c)) return;
+    const int64_t row0c = seq_row0(a, n) + c * CH;
+    const int L = static_cast<int>(min<int64_t>(CH, seq_len(a, n) - c * CH));
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 4, l16 = lane & 15;
+    const int col = 16 * wave + l16;
+    const int64_t rs = static_cast<int64_t>(H) * kDim;      // elements per token row
+    const int64_t wslot = id * H + h;
+
+    // ---- staging: G tile, Kt and Ke images, T, P^T and T^T images
+    {
+        const float* apt = a.ws_apt + wslot * (3 * TSZ);
+        tile_image<false, SEQ_NT>(apt + 2 * TSZ, img + OFF_TI);
+        tile_image<true, SEQ_NT>(apt + TSZ, img + OFF_PT);
+        tile_image<true, SEQ_NT>(apt + 2 * TSZ, img + OFF_TT);
+        Staged<SEQ_NT> st;
+        stage<SEQ_NT, false>(a, row0c, L, h, tot, st);
+        stage_beta(a, row0c, L, h, bs);
+#pragma unroll
+        for (int j = 0; j < Staged<SEQ_NT>::TOK; ++j) {
+            const int r = st.r0 + j;
+            *reinterpret_cast<float2*>(&Gs[r * GLD + st.c0]) = make_float2(st.g[j][0], st.g[j][1]);
+            img_put2<true>(img + OFF_KT, KT_PL, r, st.c0, 4, st.kk[j][0] * ex2(st.g[j][0]),
+                           st.kk[j][1] * ex2(st.g[j][1]));
+            img_put2<true>(img + OFF_KE, KT_PL, r, st.c0, 4, st.kk[j][0] * ex2(st.gl[0] - st.g[j][0]),
+                           st.kk[j][1] * ex2(st.gl[1] - st.g[j][1]));
+        }
+        if (st.r0 == 0) {
+            gLs[st.c0] = st.gl[0];
+            gLs[st.c0 + 1] = st.gl[1];
+        }
+    }
+    // ---- this wave's columns of S0, dS1, dO and V
+    f32x4 S[8], dS[8], dO[4], W[4];
+    {
+        const float* s0 = a.ws_s0 + wslot * SS;
+        const float* ds = a.ws_ds + wslot * SS;
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int e = (16 * tt + 4 * g + x) * kDim + col;
+                S[tt][x] = s0[e];
+                dS[tt][x] = ds[e];
+            }
+        const int64_t e0 = (row0c * H + h) * kDim + col;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int r = 16 * m + 4 * g + x;
+                dO[m][x] = r < L ? a.d_o[e0 + r * rs] : 0.f;
+                W[m][x] = r < L ? widen(a.v[e0 + r * rs]) : 0.f;
+            }
+    }
+    __syncthreads();
+
+    // ---- phase A
+    f32x4 U[4], dU[4], dW[4];
+    {
+        bf16x8 bh[4], bl[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) bfrag(S[2 * s], S[2 * s + 1], bh[s], bl[s]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            f32x4 X = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                bf16x8 ah, al;
+                img_frag(img + OFF_KT, KT_PL, m * 4 + s, lane, ah, al);
+                X = mma3(ah, al, bh[s], bl[s], X);
+            }
+            W[m] -= X;  // W = V - X
+        }
+        f32x4 BW[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) BW[m][x] = bs[16 * m + 4 * g + x] * W[m][x];
+        bf16x8 wh[2], wl[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) bfrag(BW[2 * s], BW[2 * s + 1], wh[s], wl[s]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            U[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                bf16x8 ah, al;
+                img_frag(img + OFF_TI, T_PL, m * 2 + s, lane, ah, al);
+                U[m] = mma3(ah, al, wh[s], wl[s], U[m]);
+            }
+        }
+        bf16x8 oh[2], ol[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) bfrag(dO[2 * s], dO[2 * s + 1], oh[s], ol[s]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) bfrag(dS[2 * s], dS[2 * s + 1], bh[s], bl[s]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            dU[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                bf16x8 ah, al;
+                img_frag(img + OFF_PT, T_PL, m * 2 + s, lane, ah, al);
+                dU[m] = mma3(ah, al, oh[s], ol[s], dU[m]);
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                bf16x8 ah, al;
+                img_frag(img + OFF_KE, KT_PL, m * 4 + s, lane, ah, al);
+                dU[m] = mma3(ah, al, bh[s], bl[s], dU[m]);
+            }
+        }
+        bf16x8 uh[2], ul[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) bfrag(dU[2 * s], dU[2 * s + 1], uh[s], ul[s]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            dW[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                bf16x8 ah, al;
+                img_frag(img + OFF_TT, T_PL, m * 2 + s, lane, ah, al);
+                dW[m] = mma3(ah, al, uh[s], ul[s], dW[m]);
+            }
+        }
+        // dv = B dW'; db (first term): row sums of dW' (.) W over this wave's columns
+        const int64_t e0 = (row0c * H + h) * kDim + col;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int r = 16 * m + 4 * g + x;
+                if (r < L) a.dv[e0 + r * rs] = bs[r] * dW[m][x];
+                float p = dW[m][x] * W[m][x];
+                float d = dO[m][x] * U[m][x];  // the diagonal of dP in fp32
+#pragma unroll
+                for (int o = 8; o > 0; o >>= 1) {
+                    p += __shfl_xor(p, o);
+                    d += __shfl_xor(d, o);
+                }
+                if (l16 == 0) {
+                    dbr[wave][r] = p;
+                    dpd[wave][r] = d;
+                }
+            }
+    }
+    __syncthreads();  // every wave is done with the phase A images
+
+    // ---- phase B images (natural binding, rows = tokens, k = value columns):
+    // dO, -B dW', U.  Even lanes store their value and the odd neighbour's.
+    auto put_pair = [&](int off, int r, float x) {
+        const float y = __shfl_xor(x, 1);
+        if ((l16 & 1) == 0) img_put2<false>(img + off, KT_PL, r, col, 4, x, y);
+    };
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int r = 16 * m + 4 * g + x;
+            put_pair(OFF_I0, r, dO[m][x]);
+            put_pair(OFF_I1, r, -bs[r] * dW[m][x]);
+            put_pair(OFF_I2, r, U[m][x]);
+        }
+    __syncthreads();
+
+    // ---- phase B: wave w on channels cw = 16w + l16; rows of S0 and dS1 as B operands
+    float* dpt = a.ws_dpt + wslot * kDptFloats;
+    {
+        const int cw = col;
+        bf16x8 sh[4], sl[4], dh[4], dl[4];
+        float dg = 0.f;
+        {
+            const float* s0 = a.ws_s0 + wslot * SS + cw * kDim;
+            const float* ds = a.ws_ds + wslot * SS + cw * kDim;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int j0 = 32 * s + 8 * g;
+                const float4 a0 = *reinterpret_cast<const float4*>(s0 + j0);
+                const float4 a1 = *reinterpret_cast<const float4*>(s0 + j0 + 4);
+                const float4 b0 = *reinterpret_cast<const float4*>(ds + j0);
+                const float4 b1 = *reinterpret_cast<const float4*>(ds + j0 + 4);
+                const float xs[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+                const float xd[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+                for (int j = 0; j < 8; ++j) dg += xs[j] * xd[j];
+                split8(xs, sh[s], sl[s]);
+                split8(xd, dh[s], dl[s]);
+            }
+            dg += __shfl_xor(dg, 16);
+            dg += __shfl_xor(dg, 32);
+        }
+        const float gLc = gLs[cw];
+        float keke = 0.f;  // sum over the rows of Ke dKe for channel cw
+        float first = 0.f;  // sum over the rows of Qt dQt + Kt dKt
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            f32x4 dQt = {0.f, 0.f, 0.f, 0.f}, dKt = dQt, dKe = dQt;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                bf16x8 ah, al;
+                img_frag(img + OFF_I0, KT_PL, m * 4 + s, lane, ah, al);
+                dQt = mma3(ah, al, sh[s], sl[s], dQt);
+                img_frag(img + OFF_I1, KT_PL, m * 4 + s, lane, ah, al);
+                dKt = mma3(ah, al, sh[s], sl[s], dKt);
+                img_frag(img + OFF_I2, KT_PL, m * 4 + s, lane, ah, al);
+                dKe = mma3(ah, al, dh[s], dl[s], dKe);
+            }
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int r = 16 * m + 4 * g + x;
+                if (r < L) {
+                    const int64_t e = ((row0c + r) * H + h) * kDim + cw;
+                    const float G = Gs[r * GLD + cw];
+                    const float gam = ex2(G), ge = ex2(gLc - G);
+                    const float qv = widen(a.q[e]), kv = widen(a.k[e]);
+                    const float dq = dQt[x] * gam;
+                    const float dkt = dKt[x] * gam, dke = dKe[x] * ge;
+                    a.dq[e] = dq;
+                    a.dk[e] = dkt + dke;
+                    a.dla[e] = qv * dq + kv * dkt - kv * dke;
+                    keke += kv * dke;
+                    first += qv * dq + kv * dkt;
+                }
+            }
+        }
+        keke += __shfl_xor(keke, 16);
+        keke += __shfl_xor(keke, 32);
+        first += __shfl_xor(first, 16);
+        first += __shfl_xor(first, 32);
+        if (g == 0) {
+            dpt[2 * TSZ + cw] = keke + ex2(gLc) * dg;
+            dpt[2 * TSZ + kDim + cw] = first + ex2(gLc) * dg;
+        }
+    }
+    // dP = dO U^T on the 10 lower 16 x 16 blocks (2 per wave for waves 0, 1)
+    for (int b = wave; b < 10; b += SEQ_NT / 64) {
+        int mr = 0;
+        while ((mr + 1) * (mr + 2) / 2 <= b) ++mr;
+        const int mi = b - mr * (mr + 1) / 2;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            bf16x8 ah, al, bh2, bl2;
+            img_frag(img + OFF_I0, KT_PL, mr * 4 + s, lane, ah, al);
+            img_frag(img + OFF_I2, KT_PL, mi * 4 + s, lane, bh2, bl2);
+            acc = mma3(ah, al, bh2, bl2, acc);
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int r = 16 * mr + 4 * g + x, i = 16 * mi + l16;
+            float val = acc[x];
+            if (r == i) {
+                // dP_rr = dO_r . U_r carries the first token of a sequence from a
+                // zero state (dq = dP_rr k_r there); its sum can cancel far below
+                // its terms, so it is summed in fp32 rather than on split bf16
+                val = 0.f;
+#pragma unroll
+                for (int w = 0; w < SEQ_NT / 64; ++w) val += dpd[w][r];
+            }
+            dpt[r * CH + i] = val;
+        }
+    }
+    __syncthreads();  // phase B images are dead
+
+    // ---- phase C: images of dU and B W, then dT = dU (B W)^T on the lower blocks
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int r = 16 * m + 4 * g + x;
+            put_pair(OFF_I0, r, dU[m][x]);
+            put_pair(OFF_I1, r, bs[r] * W[m][x]);
+        }
+    __syncthreads();
+    for (int b = wave; b < 10; b += SEQ_NT / 64) {
+        int mr = 0;
+        while ((mr + 1) * (mr + 2) / 2 <= b) ++mr;
+        const int mi = b - mr * (mr + 1) / 2;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            bf16x8 ah, al, bh2, bl2;
+            img_frag(img + OFF_I0, KT_PL, mr * 4 + s, lane, ah, al);
+            img_frag(img + OFF_I1, KT_PL, mi * 4 + s, lane, bh2, bl2);
+            acc = mma3(ah, al, bh2, bl2, acc);
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x) dpt[TSZ + (16 * mr + 4 * g + x) * CH + 16 * mi + l16] = acc[x];
+    }
+    // db, first term
+    if (t < L) {
+        float sdb = 0.f;
+#pragma unroll
+        for (int w = 0; w < SEQ_NT / 64; ++w) sdb += dbr[w][t];
+        a.dbeta[(row0c + t) * H + h] = sdb;
+    }
+}
+
+// ================================================================ intra
+//
+// Per chunk of one head (grid: chunk ids x heads; 512 threads).
+// Phase 1:  dM = -T^T dT T^T,  dA = B dM (i < r),  db_r += sum_{i<r} dM_ri A_ri.
+// Phase 2, wave w on channels 16w..16w+15: the decay products of dP and dA,
+//   dq_r  = sum_{i<=r} dP_ri k_i 2^(G_r - G_i),   dk_r += sum_{i<r} dA_ri k_i 2^(G_r - G_i),
+//   dk_i += sum_{r>=i} (dP_ri q_r + dA_ri k_r) 2^(G_r - G_i),
+// on 16x16x16 matrix instructions per pair of 16-token blocks (R, I <= R),
+// with 2^(G_r - G_i) = 2^(G_r - rho) 2^(rho - G_i).  For I < R, rho = G at the
+// last token of block R - 1 and both factors are <= 1.  For I = R, rho = G at
+// the block's 8th token, and a channel is taken this way only if both factors
+// stay within 2^96; the others ("unsafe" channels, whose decay over half a
+// block exceeds 2^-96) get that block pairwise on the vector ALUs.  Then dL,
+// its reverse cumulative sum over the chunk, and the totals of dq and dk.
+
+constexpr int INTRA_NT = 512;
+constexpr int PLD = 68;   // fp32 row stride of the 64 x 64 tiles
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// hi*hi + hi*lo + lo*hi on the 16x16x16 bf16 instruction
+__device__ __forceinline__ f32x4 mma16(i16x4 ah, i16x4 al, i16x4 bh, i16x4 bl, f32x4 c)
+{
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, c, 0, 0, 0);
+    return c;
+}
+
+__device__ __forceinline__ void split4(float x0, float x1, float x2, float x3, i16x4& h, i16x4& l)
+{
+    uint32_t h0, l0, h1, l1;
+    split2(x0, x1, h0, l0);
+    split2(x2, x3, h1, l1);
+    h = __builtin_bit_cast(i16x4, (uint2){h0, h1});
+    l = __builtin_bit_cast(i16x4, (uint2){l0, l1});
+}
+
+__global__ __launch_bounds__(INTRA_NT, 1) void chunk_intra_kernel(const ChunkBwdArgs a)
+{
+    __shared__ __attribute__((aligned(16))) float Pd[CH * PLD];       // dP (i <= r)
+    __shared__ __attribute__((aligned(16))) float Ad[CH * PLD];       // dT, Y, dM, then dA
+    __shared__ __attribute__((aligned(16))) float U1[2 * CH * PLD];   // T and A, then G
+    __shared__ __attribute__((aligned(16))) __bf16 Ks[CH * kDim];
+    __shared__ __attribute__((aligned(16))) __bf16 Qs[CH * kDim];
+    __shared__ float bs[CH], db2[CH], tot[(INTRA_NT / 64) * kDim];
+    static_assert(CH * kDim <= 2 * CH * PLD, "G fits where T and A were");
+    float* Ts = U1;
+    float* As = U1 + CH * PLD;
+    float* Gs = U1;
+
+    const int H = a.H;
+    const int64_t id = blockIdx.x / H;
+    const int h = static_cast<int>(blockIdx.x - id * H);
+    int64_t n, c;
+    if (!locate(a, id, n, c)) return;
+    const int64_t row0c = seq_row0(a, n) + c * CH;
+    const int L = static_cast<int>(min<int64_t>(CH, seq_len(a, n) - c * CH));
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 4, l16 = lane & 15;
+    const int64_t wslot = id * H + h;
+
+    // ---- phase 1: T, A, dT (i < r), dP (i <= r)
+    {
+        const float* apt = a.ws_apt + wslot * (3 * TSZ);
+        const float* dpt = a.ws_dpt + wslot * kDptFloats;
+        for (int e = t; e < TSZ; e += INTRA_NT) {
+            const int r = e >> 6, i = e & 63;
+            As[r * PLD + i] = apt[e];
+            Ts[r * PLD + i] = apt[2 * TSZ + e];
+            Pd[r * PLD + i] = i <= r ? dpt[e] : 0.f;
+            Ad[r * PLD + i] = i < r ? dpt[TSZ + e] : 0.f;
+        }
+        stage_beta(a, row0c, L, h, bs);
+    }
+    __syncthreads();
+    const int yi = t >> 3, y0 = 8 * (t & 7);   // this thread's row and first 8 columns
+    {
+        // Y = T^T dT: Y_im = sum_{r >= i} T_ri dT_rm
+        float y[8] = {};
+        for (int r = yi; r < CH; ++r) {
+            const float tr = Ts[r * PLD + yi];
+            const float4 d0 = *reinterpret_cast<const float4*>(&Ad[r * PLD + y0]);
+            const float4 d1 = *reinterpret_cast<const float4*>(&Ad[r * PLD + y0 + 4]);
+            y[0] += tr * d0.x; y[1] += tr * d0.y; y[2] += tr * d0.z; y[3] += tr * d0.w;
+            y[4] += tr * d1.x; y[5] += tr * d1.y; y[6] += tr * d1.z; y[7] += tr * d1.w;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < 8; ++u) Ad[yi * PLD + y0 + u] = y[u];
+    }
+    __syncthreads();
+    {
+        // dM = -Y T^T: dM_ik = -sum_m Y_im T_km (only k < i is used)
+        float dm[8] = {};
+        if (y0 < yi) {
+            for (int m = 0; m < CH; m += 4) {
+                const float4 yv = *reinterpret_cast<const float4*>(&Ad[yi * PLD + m]);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float4 tv = *reinterpret_cast<const float4*>(&Ts[(y0 + u) * PLD + m]);
+                    dm[u] -= yv.x * tv.x + yv.y * tv.y + yv.z * tv.z + yv.w * tv.w;
+                }
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < 8; ++u) Ad[yi * PLD + y0 + u] = dm[u];
+    }
+    __syncthreads();
+    if (t < CH) {
+        float s2 = 0.f;
+        for (int k = 0; k < t; ++k) s2 += Ad[t * PLD + k] * As[t * PLD + k];
+        db2[t] = s2;
+    }
+    __syncthreads();
+    for (int e = t; e < TSZ; e += INTRA_NT) {
+        const int r = e >> 6, i = e & 63;
+        Ad[r * PLD + i] = i < r ? bs[r] * Ad[r * PLD + i] : 0.f;   // dA
+    }
+    // ---- phase 2 staging: G (over T and A), k, q
+    {
+        Staged<INTRA_NT> st;
+        stage<INTRA_NT, true>(a, row0c, L, h, tot, st);   // its barrier also ends phase 1
+#pragma unroll
+        for (int j = 0; j < Staged<INTRA_NT>::TOK; ++j) {
+            const int r = st.r0 + j;
+            *reinterpret_cast<float2*>(&Gs[r * kDim + st.c0]) = make_float2(st.g[j][0], st.g[j][1]);
+            *reinterpret_cast<bf16x2*>(&Ks[r * kDim + st.c0]) = (bf16x2){(__bf16)st.kk[j][0], (__bf16)st.kk[j][1]};
+            *reinterpret_cast<bf16x2*>(&Qs[r * kDim + st.c0]) = (bf16x2){(__bf16)st.qq[j][0], (__bf16)st.qq[j][1]};
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 2: wave w on channels cc = 16w + l16; rows 16R + 4g + x of each block R
+    const int cc = 16 * wave + l16;
+    auto Gv = [&](int r) { return Gs[r * kDim + cc]; };
+    auto Kv = [&](int r) { return (float)Ks[r * kDim + cc]; };
+    auto Qv = [&](int r) { return (float)Qs[r * kDim + cc]; };
+    f32x4 dq[4], dkr[4], dkc[4];
+#pragma unroll
+    for (int R = 0; R < 4; ++R) dq[R] = dkr[R] = dkc[R] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+        float gR[4], kR[4], qR[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int r = 16 * R + 4 * g + x;
+            gR[x] = Gv(r);
+            kR[x] = Kv(r);
+            qR[x] = Qv(r);
+        }
+#pragma unroll
+        for (int I = 0; I <= R; ++I) {
+            const float rho = I < R ? Gv(16 * R - 1) : Gv(16 * R + 7);
+            const bool safe = I < R || (Gv(16 * R) - rho <= 96.f && rho - Gv(16 * R + 15) <= 96.f);
+            float f[4], hh[4], kh[4], qf[4], kf[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int i = 16 * I + 4 * g + x;
+                f[x] = safe ? ex2(gR[x] - rho) : 0.f;
+                hh[x] = safe ? ex2(rho - Gv(i)) : 0.f;
+                kh[x] = Kv(i) * hh[x];
+                qf[x] = qR[x] * f[x];
+                kf[x] = kR[x] * f[x];
+            }
+            i16x4 bkh, bkl, bqh, bql, bfh, bfl;
+            split4(kh[0], kh[1], kh[2], kh[3], bkh, bkl);
+            split4(qf[0], qf[1], qf[2], qf[3], bqh, bql);
+            split4(kf[0], kf[1], kf[2], kf[3], bfh, bfl);
+            // row side: A = dP_RI, dA_RI (row l16 of block R, columns 4g.. of block I)
+            const float4 p4 = *reinterpret_cast<const float4*>(&Pd[(16 * R + l16) * PLD + 16 * I + 4 * g]);
+            const float4 a4 = *reinterpret_cast<const float4*>(&Ad[(16 * R + l16) * PLD + 16 * I + 4 * g]);
+            i16x4 aph, apl, aah, aal;
+            split4(p4.x, p4.y, p4.z, p4.w, aph, apl);
+            split4(a4.x, a4.y, a4.z, a4.w, aah, aal);
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            const f32x4 sq = mma16(aph, apl, bkh, bkl, z);
+            const f32x4 sk = mma16(aah, aal, bkh, bkl, z);
+            // column side: A = dP_RI^T, dA_RI^T (row l16 of block I, columns 4g.. of block R)
+            float pc[4], ac[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                pc[x] = Pd[(16 * R + 4 * g + x) * PLD + 16 * I + l16];
+                ac[x] = Ad[(16 * R + 4 * g + x) * PLD + 16 * I + l16];
+            }
+            i16x4 cph, cpl, cah, cal;
+            split4(pc[0], pc[1], pc[2], pc[3], cph, cpl);
+            split4(ac[0], ac[1], ac[2], ac[3], cah, cal);
+            f32x4 sc = mma16(cph, cpl, bqh, bql, z);
+            sc = mma16(cah, cal, bfh, bfl, sc);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                dq[R][x] += f[x] * sq[x];
+                dkr[R][x] += f[x] * sk[x];
+                dkc[I][x] += hh[x] * sc[x];
+            }
+            if (I == R && __any(!safe)) {
+                // pairwise on the vector ALUs for the unsafe channels
+                if (!safe) {
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        const int r = 16 * R + 4 * g + x;
+                        float aq = 0.f, ak = 0.f, acc = 0.f;
+                        for (int i = 16 * R; i <= r; ++i) {
+                            const float kie = Kv(i) * ex2(gR[x] - Gv(i));
+                            aq += Pd[r * PLD + i] * kie;
+                            ak += Ad[r * PLD + i] * kie;
+                        }
+                        const float gi = gR[x];  // row r as the column index i
+                        for (int rr = r; rr < 16 * R + 16; ++rr)
+                            acc += (Pd[rr * PLD + r] * Qv(rr) + Ad[rr * PLD + r] * Kv(rr)) * ex2(Gv(rr) - gi);
+                        dq[R][x] += aq;
+                        dkr[R][x] += ak;
+                        dkc[R][x] += acc;
+                    }
+                }
+            }
+        }
+    }
+
+    // ---- totals and the reverse cumulative sum of dL over the chunk's rows
+    const float last = a.ws_dpt[wslot * kDptFloats + 2 * TSZ + cc];
+    const float first = a.ws_dpt[wslot * kDptFloats + 2 * TSZ + kDim + cc];
+    const int64_t rs = static_cast<int64_t>(H) * kDim;
+    const int64_t e0 = (row0c * H + h) * kDim + cc;
+    float dl[4][4], part[4];
+#pragma unroll
+    for (int R = 0; R < 4; ++R) {
+        part[R] = 0.f;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int r = 16 * R + 4 * g + x;
+            dl[R][x] = 0.f;
+            if (r < L) {
+                const float kv = Kv(r), qv = Qv(r);
+                const int64_t e = e0 + r * rs;
+                a.dq[e] += dq[R][x];
+                a.dk[e] += dkr[R][x] + dkc[R][x];
+                dl[R][x] = a.dla[e] + qv * dq[R][x] + kv * dkr[R][x] - kv * dkc[R][x] +
+                           (r == L - 1 ? last : 0.f);
+            }
+            part[R] += dl[R][x];
+        }
+    }
+    float carry = 0.f;   // sum of dL over the blocks after R
+#pragma unroll
+    for (int R = 3; R >= 0; --R) {
+        float above = 0.f, block = 0.f;   // later lane groups of this block; the whole block
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+            const float pg = __shfl(part[R], l16 + 16 * gg);
+            block += pg;
+            if (gg > g) above += pg;
+        }
+        float run = carry + above;
+#pragma unroll
+        for (int x = 3; x >= 0; --x) {
+            const int r = 16 * R + 4 * g + x;
+            run += dl[R][x];
+            if (r < L) a.dla[e0 + r * rs] = r == 0 ? first : run;
+        }
+        carry += block;
+    }
+    if (t < L) a.dbeta[(row0c + t) * H + h] += db2[t];
+}
+
+}  // namespace
+
+size_t chunk_backward_bytes_per_chunk()
+{
+    // entering state, leaving-state gradient, A/P/T, dP/dT and the last-token terms
+    return (2 * static_cast<size_t>(SS) + 3 * TSZ + kDptFloats) * sizeof(float);
+}
+
+hipError_t launch_backward_chunked(const void* q, const void* k, const void* v, const void* beta,
+                                   const float* log_alpha, const float* d_o, const int32_t* cu_seqlens,
+                                   int64_t n_seq, int64_t T, int64_t H, const float* initial_state,
+                                   const float* d_final_state, float* dq, float* dk, float* dv,
+                                   float* dbeta, float* dlog_alpha, float* d_initial_state,
+                                   int64_t n_ids, void* ws, hipStream_t stream)
+{
+    const int64_t units = n_seq * H;
+    if (units <= 0) return hipSuccess;
+    ChunkBwdArgs a = {};
+    a.q = static_cast<const bf16_t*>(q);
+    a.k = static_cast<const bf16_t*>(k);
+    a.v = static_cast<const bf16_t*>(v);
+    a.beta = static_cast<const bf16_t*>(beta);
+    a.la = log_alpha;
+    a.d_o = d_o;
+    a.cu = cu_seqlens;
+    a.T = T;
+    a.n_seq = n_seq;
+    a.H = static_cast<int>(H);
+    a.s0 = initial_state;
+    a.d_sT = d_final_state;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.dbeta = dbeta;
+    a.dla = dlog_alpha;
+    a.ds0 = d_initial_state;
+    const size_t slots = static_cast<size_t>(n_ids) * H;
+    float* w = static_cast<float*>(ws);
+    a.ws_s0 = w;
+    a.ws_ds = a.ws_s0 + slots * SS;
+    a.ws_apt = a.ws_ds + slots * SS;
+    a.ws_dpt = a.ws_apt + slots * 3 * TSZ;
+
+    const dim3 chunks(static_cast<unsigned>(n_ids * H)), seqs(static_cast<unsigned>(units));
+    hipError_t e;
+    if (n_ids > 0) {
+        hipLaunchKernelGGL(chunk_prep_kernel, chunks, dim3(PREP_NT), 0, stream, a);
+        e = hipGetLastError();
+        report("backward prep launch", e);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(chunk_states_kernel, seqs, dim3(SEQ_NT), 0, stream, a);
+    e = hipGetLastError();
+    report("backward states launch", e);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(chunk_dstate_kernel, seqs, dim3(SEQ_NT), 0, stream, a);
+    e = hipGetLastError();
+    report("backward state-gradient launch", e);
+    if (e != hipSuccess || n_ids == 0) return e;
+    hipLaunchKernelGGL(chunk_grads_kernel, chunks, dim3(SEQ_NT), 0, stream, a);
+    e = hipGetLastError();
+    report("backward gradient launch", e);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(chunk_intra_kernel, chunks, dim3(INTRA_NT), 0, stream, a);
+    e = hipGetLastError();
+    report("backward intra-chunk launch", e);
+    return e;
+}
+
+}  // namespace kda

@@ -107,7 +107,9 @@ constexpr int kBackwardBlock = 8;
 // leaving gradients (per-segment gradient maps, composed in order).
 constexpr int64_t kBackwardMinSegment = 1024;
 struct BackwardPlan {
-    int64_t n_slots = 0;        // checkpoint slots per head
+    bool chunked = false;       // bf16 inputs: the chunked matrix-core backward
+    int64_t n_ids = 0;          // chunked: chunk ids per head
+    int64_t n_slots = 0;        // token-by-token: checkpoint slots per head
     int64_t seg = 0, nseg = 1;  // dense bf16 segments in time (seg = 0: none)
     size_t ck_floats = 0;       // checkpoint floats
     size_t seg_floats = 0;      // floats of one per-segment state array
@@ -115,6 +117,15 @@ struct BackwardPlan {
 };
 BackwardPlan plan_backward(bool packed, int64_t n_seq, int64_t T, int64_t T_total, int64_t H,
                           bool bf16, int n_cu);
+// Chunked backward (bf16 inputs; kda_backward_chunk.hip): per (chunk, head)
+// the entering state, the gradient in the leaving state, A, P, T, dP and dT.
+size_t chunk_backward_bytes_per_chunk();
+hipError_t launch_backward_chunked(const void* q, const void* k, const void* v, const void* beta,
+                                   const float* log_alpha, const float* d_o, const int32_t* cu_seqlens,
+                                   int64_t n_seq, int64_t T, int64_t H, const float* initial_state,
+                                   const float* d_final_state, float* dq, float* dk, float* dv,
+                                   float* dbeta, float* dlog_alpha, float* d_initial_state,
+                                   int64_t n_ids, void* ws, hipStream_t stream);
 // ws: at least plan.ws_bytes bytes of device memory, 256-byte aligned.
 hipError_t launch_backward(const void* q, const void* k, const void* v, const void* beta,
                            const float* log_alpha, const float* d_o, const int32_t* cu_seqlens,
@@ -137,7 +148,7 @@ struct StreamWorkspace {
     hipStream_t stream = nullptr;
     hipError_t acquire(size_t bytes, hipStream_t s);
     hipError_t release();
-    ~StreamWorkspace() { release(); }
+    ~StreamWorkspace() { (void)release(); }
 };
 
 // With KDA_DEBUG set in the environment, failed HIP calls are printed to stderr.

@@ -326,7 +326,7 @@ kda_status kda_varlen_prefill_slots(const void *q, const void *k, const void *v,
  * model's training (quantization-aware from fine-tuning onward: "Kimi K3 --
  * the architecture and infrastructure, explained", section "Training
  * infrastructure: quantization-aware from SFT onward"); the gradients are the
- * chain rule taken through the recurrence above, token by token in reverse.
+ * chain rule taken through the recurrence above.
  * Inputs are those of the prefill call they differentiate:
  *   q, k, v, beta, log_alpha, initial_state : as kda_prefill (dense, [B, T, H, *])
  *                 or kda_varlen_prefill (packed, [T_total, H, *] with
@@ -339,11 +339,16 @@ kda_status kda_varlen_prefill_slots(const void *q, const void *k, const void *v,
  *                 layout of beta
  *   d_initial_state : [B or N, H, d_k, d_v], or NULL to skip; it MAY be the same
  *                 pointer as d_final_state
- * q, k, v, beta are in_dtype (bf16 inputs widened exactly); arithmetic is fp32.
- * The call recomputes the forward states, which it keeps in the workspace
- * (kda_backward_workspace_size gives its bytes; a smaller one is
- * KDA_ERR_WORKSPACE).  B or N = 0 is a no-op; with no tokens,
- * d_initial_state = d_final_state (or zeros).
+ * bf16 inputs take the chunked form on the matrix cores (64-token chunks;
+ * operands split into hi + lo bf16 as in the prefill, fp32 accumulation): the
+ * workspace keeps, per (64-token chunk, head), the chunk's entering state and
+ * the gradient in its leaving state, its UT transform, A and P matrices and
+ * their gradients, about 208 KiB, i.e. 3.3 KiB per head-token (3.3 GiB for
+ * 8 x 4096 tokens x 32 heads, 104 GiB for 1,048,576 tokens x 32 heads).  fp32
+ * inputs take the token-by-token chain rule with a state checkpoint every 8
+ * tokens (8 KiB per head-token).  kda_backward_workspace_size gives the bytes;
+ * a smaller workspace is KDA_ERR_WORKSPACE.  B or N = 0 is a no-op; with no
+ * tokens, d_initial_state = d_final_state (or zeros).
  */
 kda_status kda_backward(const void *q, const void *k, const void *v, const void *beta,
                         const float *log_alpha, const float *initial_state,
