@@ -63,6 +63,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "kda_device.hpp"
 #include "kda_internal.hpp"
@@ -135,6 +136,46 @@ __device__ bool locate(const ChunkBwdArgs& a, int64_t id, int64_t& n, int64_t& c
     c = id - chunk_id(seq_row0(a, lo), lo, 0);
     return c >= 0 && c * CH < seq_len(a, lo);
 }
+
+// Workgroup barrier for LDS only: each wave's LDS reads and writes complete
+// before it, while its global loads and stores stay in flight (a
+// __syncthreads() would wait for those too).  The memory clobber keeps the
+// compiler from moving memory accesses across it.  No kernel of this file
+// reads, within one launch, global memory that another wave wrote.
+__device__ __forceinline__ void lds_sync()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Element i of an array at a wave-uniform base, addressed by a 32-bit byte
+// offset (the base stays in scalar registers; i * sizeof(T) < 2^32).
+template <typename T>
+__device__ __forceinline__ T& at(T* base, uint32_t i)
+{
+    using C = typename std::conditional<std::is_const<T>::value, const char, char>::type;
+    return *reinterpret_cast<T*>(reinterpret_cast<C*>(base) + i * static_cast<uint32_t>(sizeof(T)));
+}
+
+// A 128 x 128 fp32 state in accumulator layout: element (16 tt + 4 g + x,
+// col) in X[tt][x], lane offset 4 g * 128 + col; the row's part of the
+// address stays in the (scalar) base.
+__device__ __forceinline__ void state_load(const float* src, uint32_t lo, f32x4 (&X)[8])
+{
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) X[tt][x] = src ? at(src + (16 * tt + x) * kDim, lo) : 0.f;
+}
+__device__ __forceinline__ void state_store(float* dst, uint32_t lo, const f32x4 (&X)[8])
+{
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) at(dst + (16 * tt + x) * kDim, lo) = X[tt][x];
+}
+
+// The wave's index in the workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
@@ -242,45 +283,68 @@ struct Staged {
     float gl[2];            // G at the chunk's last token
 };
 
+// The raw inputs a thread stages for one chunk, requested ahead of their use.
 template <int NT, bool WITHQ>
-__device__ __forceinline__ void stage(const ChunkBwdArgs& a, int64_t row0c, int L, int h, float* tot,
-                                      Staged<NT>& s)
+struct ChunkRaw {
+    static constexpr int TOK = Staged<NT>::TOK;
+    float2 la[TOK];
+    uint32_t k[TOK];
+    uint32_t q[WITHQ ? TOK : 1];
+};
+
+template <int NT, bool WITHQ>
+__device__ __forceinline__ void request(const ChunkBwdArgs& a, int64_t row0c, int L, int h,
+                                        ChunkRaw<NT, WITHQ>& p)
+{
+    constexpr int TOK = Staged<NT>::TOK;
+    const int t = threadIdx.x;
+    const int c0 = 2 * (t & 63), r0 = TOK * wave_id();
+    // wave-uniform bases and 32-bit lane offsets
+    const int64_t base = (row0c * a.H + h) * kDim;
+    const float* la = a.la + base;
+    const bf16_t* k = a.k + base;
+    const bf16_t* q = a.q + base;
+    const uint32_t rstride = static_cast<uint32_t>(a.H) * kDim;
+#pragma unroll
+    for (int j = 0; j < TOK; ++j) {
+        const int r = r0 + j;
+        const bool in = r < L;
+        const uint32_t e = static_cast<uint32_t>(c0) + static_cast<uint32_t>(in ? r : 0) * rstride;
+        p.la[j] = in ? at(reinterpret_cast<const float2*>(la), e >> 1) : make_float2(0.f, 0.f);
+        p.k[j] = in ? at(reinterpret_cast<const uint32_t*>(k), e >> 1) : 0u;
+        if (WITHQ) p.q[j] = in ? at(reinterpret_cast<const uint32_t*>(q), e >> 1) : 0u;
+    }
+}
+
+// The cumulative log2-decay of the requested inputs (one barrier, for the
+// group prefix through `tot`).
+template <int NT, bool WITHQ>
+__device__ __forceinline__ void stage_raw(const ChunkRaw<NT, WITHQ>& p, float* tot, Staged<NT>& s)
 {
     constexpr int TG = Staged<NT>::TG, TOK = Staged<NT>::TOK;
     const int t = threadIdx.x;
     s.c0 = 2 * (t & 63);
-    s.r0 = TOK * (t >> 6);
-    const int64_t rstride = static_cast<int64_t>(a.H) * kDim;
-    const int64_t e0 = (row0c * a.H + h) * kDim + s.c0;
+    s.r0 = TOK * wave_id();
     float run0 = 0.f, run1 = 0.f;
 #pragma unroll
     for (int j = 0; j < TOK; ++j) {
-        const int r = s.r0 + j;
-        float2 l2 = make_float2(0.f, 0.f);
-        uint32_t kb = 0, qb = 0;
-        if (r < L) {
-            const int64_t e = e0 + r * rstride;
-            l2 = *reinterpret_cast<const float2*>(a.la + e);
-            kb = *reinterpret_cast<const uint32_t*>(a.k + e);
-            if (WITHQ) qb = *reinterpret_cast<const uint32_t*>(a.q + e);
-        }
-        run0 += l2.x * kLog2e;
-        run1 += l2.y * kLog2e;
+        run0 += p.la[j].x * kLog2e;
+        run1 += p.la[j].y * kLog2e;
         s.g[j][0] = run0;
         s.g[j][1] = run1;
-        s.kk[j][0] = bf_lo(kb);
-        s.kk[j][1] = bf_hi(kb);
-        s.qq[j][0] = bf_lo(qb);
-        s.qq[j][1] = bf_hi(qb);
+        s.kk[j][0] = bf_lo(p.k[j]);
+        s.kk[j][1] = bf_hi(p.k[j]);
+        s.qq[j][0] = WITHQ ? bf_lo(p.q[j]) : 0.f;
+        s.qq[j][1] = WITHQ ? bf_hi(p.q[j]) : 0.f;
     }
-    tot[(t >> 6) * kDim + s.c0] = run0;
-    tot[(t >> 6) * kDim + s.c0 + 1] = run1;
-    __syncthreads();
+    tot[wave_id() * kDim + s.c0] = run0;
+    tot[wave_id() * kDim + s.c0 + 1] = run1;
+    lds_sync();
     float p0 = 0.f, p1 = 0.f, a0 = 0.f, a1 = 0.f;
 #pragma unroll
     for (int u = 0; u < TG; ++u) {
         const float x0 = tot[u * kDim + s.c0], x1 = tot[u * kDim + s.c0 + 1];
-        if (u < (t >> 6)) {
+        if (u < wave_id()) {
             p0 += x0;
             p1 += x1;
         }
@@ -296,6 +360,15 @@ __device__ __forceinline__ void stage(const ChunkBwdArgs& a, int64_t row0c, int 
     s.gl[1] = a1;
 }
 
+template <int NT, bool WITHQ>
+__device__ __forceinline__ void stage(const ChunkBwdArgs& a, int64_t row0c, int L, int h, float* tot,
+                                      Staged<NT>& s)
+{
+    ChunkRaw<NT, WITHQ> p;
+    request<NT, WITHQ>(a, row0c, L, h, p);
+    stage_raw<NT, WITHQ>(p, tot, s);
+}
+
 // beta of the chunk's rows (zeros from L on) into LDS, by the first 64 threads
 __device__ __forceinline__ void stage_beta(const ChunkBwdArgs& a, int64_t row0c, int L, int h, float* bs)
 {
@@ -304,22 +377,50 @@ __device__ __forceinline__ void stage_beta(const ChunkBwdArgs& a, int64_t row0c,
 }
 
 // A 64 x 64 fp32 tile from global memory into an image: TRANS = false stores
-// Z[r][i] at (row r, k i), TRANS = true at (row i, k r); PERM binding.
+// Z[r][i] at (row r, k i), TRANS = true at (row i, k r); PERM binding.  The
+// loads (request_tile) come apart from the stores (tile_put) so that they can
+// be issued a chunk ahead.
+template <int NT>
+struct TileRaw {
+    static constexpr int N = TSZ / 2 / NT;
+    float2 x[N];
+};
+
+template <bool TRANS, int NT>
+__device__ __forceinline__ void request_tile(const float* src, TileRaw<NT>& p)
+{
+#pragma unroll
+    for (int j = 0; j < TileRaw<NT>::N; ++j) {
+        const uint32_t q = threadIdx.x + j * NT;
+        if (!TRANS) {
+            const uint32_t r = q >> 5, i = 2 * (q & 31);
+            p.x[j] = at(reinterpret_cast<const float2*>(src), (r * CH + i) >> 1);
+        } else {
+            // consecutive threads take consecutive columns i of one pair of rows
+            const uint32_t i = q & 63, r = 2 * (q >> 6);
+            p.x[j] = make_float2(at(src, r * CH + i), at(src, (r + 1) * CH + i));
+        }
+    }
+}
+
+template <bool TRANS, int NT>
+__device__ __forceinline__ void tile_put(const TileRaw<NT>& p, char* img)
+{
+    constexpr int plane = CH * CH * 2;
+#pragma unroll
+    for (int j = 0; j < TileRaw<NT>::N; ++j) {
+        const int q = threadIdx.x + j * NT;
+        if (!TRANS) img_put2<true>(img, plane, q >> 5, 2 * (q & 31), 2, p.x[j].x, p.x[j].y);
+        else img_put2<true>(img, plane, q & 63, 2 * (q >> 6), 2, p.x[j].x, p.x[j].y);
+    }
+}
+
 template <bool TRANS, int NT>
 __device__ __forceinline__ void tile_image(const float* src, char* img)
 {
-    constexpr int plane = CH * CH * 2;
-    for (int p = threadIdx.x; p < TSZ / 2; p += NT) {
-        if (!TRANS) {
-            const int r = p >> 5, i = 2 * (p & 31);
-            const float2 x = *reinterpret_cast<const float2*>(src + r * CH + i);
-            img_put2<true>(img, plane, r, i, 2, x.x, x.y);
-        } else {
-            // consecutive threads take consecutive columns i of one pair of rows
-            const int i = p & 63, r = 2 * (p >> 6);
-            img_put2<true>(img, plane, i, r, 2, src[r * CH + i], src[(r + 1) * CH + i]);
-        }
-    }
+    TileRaw<NT> p;
+    request_tile<TRANS, NT>(src, p);
+    tile_put<TRANS, NT>(p, img);
 }
 
 // ================================================================ prep
@@ -355,7 +456,7 @@ __global__ __launch_bounds__(PREP_NT) void chunk_prep_kernel(const ChunkBwdArgs 
     if (!locate(a, id, n, c)) return;
     const int64_t row0c = seq_row0(a, n) + c * CH;
     const int L = static_cast<int>(min<int64_t>(CH, seq_len(a, n) - c * CH));
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int t = threadIdx.x, lane = t & 63, wave = wave_id();
 
     Staged<PREP_NT> st;
     stage<PREP_NT, true>(a, row0c, L, h, tot, st);
@@ -367,7 +468,7 @@ __global__ __launch_bounds__(PREP_NT) void chunk_prep_kernel(const ChunkBwdArgs 
         *reinterpret_cast<bf16x2*>(&Ks[r * BLD + st.c0]) = (bf16x2){(__bf16)st.kk[j][0], (__bf16)st.kk[j][1]};
         *reinterpret_cast<bf16x2*>(&Qs[r * BLD + st.c0]) = (bf16x2){(__bf16)st.qq[j][0], (__bf16)st.qq[j][1]};
     }
-    __syncthreads();
+    lds_sync();
 
     // ---- off-diagonal blocks on the matrix cores: rows r of block R carry
     // 2^(G_r - rho), columns i of block I < R carry 2^(rho - G_i), with rho =
@@ -440,7 +541,7 @@ __global__ __launch_bounds__(PREP_NT) void chunk_prep_kernel(const ChunkBwdArgs 
             }
         }
     }
-    __syncthreads();
+    lds_sync();
 
     // ---- T = (I + Diag(beta) A)^-1, unit lower triangular, by 16 x 16 blocks:
     // the diagonal blocks by forward substitution (lane = column), then
@@ -462,7 +563,7 @@ __global__ __launch_bounds__(PREP_NT) void chunk_prep_kernel(const ChunkBwdArgs 
 #pragma unroll
         for (int r = 0; r < 16; ++r) Ts[(16 * R + r) * TLD + 16 * R + j] = x[r];
     }
-    __syncthreads();
+    lds_sync();
     for (int d = 1; d < 4; ++d) {
         // Y = sum_J N_RJ T_JI for the 4 - d blocks of this distance
         const int rl = t >> 4, il = t & 15;
@@ -475,7 +576,7 @@ __global__ __launch_bounds__(PREP_NT) void chunk_prep_kernel(const ChunkBwdArgs 
                     y += bs[r] * As[r * TLD + 16 * J + m] * Ts[(16 * J + m) * TLD + 16 * I + il];
             Ys[(R - d) * 256 + rl * 16 + il] = y;
         }
-        __syncthreads();
+        lds_sync();
         for (int R = d; R < 4; ++R) {
             const int I = R - d, r = 16 * R + rl;
             float x = 0.f;
@@ -483,7 +584,7 @@ __global__ __launch_bounds__(PREP_NT) void chunk_prep_kernel(const ChunkBwdArgs 
             for (int m = 0; m < 16; ++m) x -= Ts[r * TLD + 16 * R + m] * Ys[(R - d) * 256 + m * 16 + il];
             Ts[r * TLD + 16 * I + il] = x;
         }
-        __syncthreads();
+        lds_sync();
     }
 
     // ---- out: A (i < r), P (i <= r), T (i < r, unit diagonal), zeros elsewhere
@@ -511,6 +612,7 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_states_kernel(const ChunkBwdA
     __shared__ __attribute__((aligned(16))) char KT[2 * KT_PL];   // Kt: rows r, k = channels
     __shared__ __attribute__((aligned(16))) char KE[2 * KE_PL];   // Ke^T: rows c, k = tokens
     __shared__ __attribute__((aligned(16))) char TI[2 * T_PL];    // T: rows r, k = i
+    __shared__ __attribute__((aligned(16))) uint4 VS[2 * SEQ_NT]; // each thread's own V rows
     __shared__ float tot[(SEQ_NT / 64) * kDim];
     __shared__ float bs[CH], gls[kDim];
 
@@ -519,27 +621,52 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_states_kernel(const ChunkBwdA
     const int h = static_cast<int>(blockIdx.x - n * H);
     const int64_t row0 = seq_row0(a, n), len = seq_len(a, n);
     const int64_t nch = (len + CH - 1) / CH;
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 4;
+    const int t = threadIdx.x, lane = t & 63, wave = wave_id(), g = lane >> 4;
     const int col = 16 * wave + (lane & 15);
 
+    const uint32_t slo = 4 * g * kDim + col;
     f32x4 S[8];
-    {
-        const float* s0 = a.s0 ? a.s0 + (n * H + h) * SS : nullptr;
-#pragma unroll
-        for (int tt = 0; tt < 8; ++tt)
-#pragma unroll
-            for (int x = 0; x < 4; ++x) S[tt][x] = s0 ? s0[(16 * tt + 4 * g + x) * kDim + col] : 0.f;
-    }
+    state_load(a.s0 ? a.s0 + (n * H + h) * SS : nullptr, slo, S);
 
-    for (int64_t c = 0; c < nch; ++c) {
+    // The inputs of chunk c + 1 are requested while chunk c's products run:
+    // log alpha and k, the T tile, this thread's V rows and beta.
+    ChunkRaw<SEQ_NT, false> raw;
+    TileRaw<SEQ_NT> traw;
+    uint32_t vraw[16];
+    float braw = 0.f;
+    auto request_chunk = [&](int64_t c) {
         const int64_t row0c = row0 + c * CH;
         const int L = static_cast<int>(min<int64_t>(CH, len - c * CH));
         const int64_t id = chunk_id(row0, n, c);
-        __syncthreads();  // the previous chunk's products are done with the images
-        tile_image<false, SEQ_NT>(a.ws_apt + (id * H + h) * (3 * TSZ) + 2 * TSZ, TI);
+        request_tile<false, SEQ_NT>(a.ws_apt + (id * H + h) * (3 * TSZ) + 2 * TSZ, traw);
+        request<SEQ_NT, false>(a, row0c, L, h, raw);
+        // rows from L on read row L - 1 and are replaced by zeros (no branches)
+        const bf16_t* vb = a.v + (row0c * H + h) * kDim;
+        const uint32_t rs = H * kDim;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int r = 16 * m + 4 * g + x;
+                const uint32_t u = at(vb, col + static_cast<uint32_t>(min(r, L - 1)) * rs).bits;
+                vraw[4 * m + x] = r < L ? u : 0u;
+            }
+        const float b = widen(at(a.beta + row0c * H + h, static_cast<uint32_t>(min(t, L - 1)) * H));
+        braw = t < L ? b : 0.f;
+    };
+    if (nch > 0) request_chunk(0);
+
+    for (int64_t c = 0; c < nch; ++c) {
+        const int64_t id = chunk_id(row0, n, c);
+        lds_sync();  // the previous chunk's products are done with the images
+        tile_put<false, SEQ_NT>(traw, TI);
+        VS[2 * t] = make_uint4(vraw[0] | (vraw[1] << 16), vraw[2] | (vraw[3] << 16),
+                               vraw[4] | (vraw[5] << 16), vraw[6] | (vraw[7] << 16));
+        VS[2 * t + 1] = make_uint4(vraw[8] | (vraw[9] << 16), vraw[10] | (vraw[11] << 16),
+                                   vraw[12] | (vraw[13] << 16), vraw[14] | (vraw[15] << 16));
+        if (t < CH) bs[t] = braw;
         Staged<SEQ_NT> st;
-        stage<SEQ_NT, false>(a, row0c, L, h, tot, st);
-        stage_beta(a, row0c, L, h, bs);
+        stage_raw<SEQ_NT, false>(raw, tot, st);
 #pragma unroll
         for (int j = 0; j < Staged<SEQ_NT>::TOK; ++j) {
             const int r = st.r0 + j;
@@ -558,54 +685,56 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_states_kernel(const ChunkBwdA
             gls[st.c0] = ex2(st.gl[0]);
             gls[st.c0 + 1] = ex2(st.gl[1]);
         }
-        __syncthreads();
+        // checkpoint S0 (before the next chunk's requests, so that waiting for
+        // those does not wait for these stores)
+        state_store(a.ws_s0 + (id * H + h) * SS, slo, S);
+        lds_sync();
+        if (c + 1 < nch) request_chunk(c + 1);
 
         // X = Kt S0 (sum over channels: B from S, 4 steps)
-        bf16x8 bh[4], bl[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) bfrag(S[2 * s], S[2 * s + 1], bh[s], bl[s]);
         f32x4 X[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            X[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int m = 0; m < 4; ++m) X[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < 4; ++s) {
+            bf16x8 bh, bl;
+            bfrag(S[2 * s], S[2 * s + 1], bh, bl);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
                 bf16x8 ah, al;
                 img_frag(KT, KT_PL, m * 4 + s, lane, ah, al);
-                X[m] = mma3(ah, al, bh[s], bl[s], X[m]);
+                X[m] = mma3(ah, al, bh, bl, X[m]);
             }
         }
         // B W = B (V - X)
-        const int64_t vrow = (row0c * H + h) * kDim + col;
+        {
+            const uint4 v0 = VS[2 * t], v1 = VS[2 * t + 1];
+            const uint32_t vw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
+            for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int r = 16 * m + 4 * g + x;
-                const float v = r < L ? widen(a.v[vrow + static_cast<int64_t>(r) * H * kDim]) : 0.f;
-                X[m][x] = bs[r] * (v - X[m][x]);
-            }
+                for (int x = 0; x < 4; ++x) {
+                    const int e = 4 * m + x;
+                    const float v = (e & 1) ? bf_hi(vw[e >> 1]) : bf_lo(vw[e >> 1]);
+                    X[m][x] = bs[16 * m + 4 * g + x] * (v - X[m][x]);
+                }
+        }
         // U = T (B W) (sum over tokens: 2 steps)
-        bf16x8 wh[2], wl[2];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) bfrag(X[2 * s], X[2 * s + 1], wh[s], wl[s]);
         f32x4 U[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            U[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int m = 0; m < 4; ++m) U[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
+        for (int s = 0; s < 2; ++s) {
+            bf16x8 wh, wl;
+            bfrag(X[2 * s], X[2 * s + 1], wh, wl);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
                 bf16x8 ah, al;
                 img_frag(TI, T_PL, m * 2 + s, lane, ah, al);
-                U[m] = mma3(ah, al, wh[s], wl[s], U[m]);
+                U[m] = mma3(ah, al, wh, wl, U[m]);
             }
         }
-        // checkpoint S0, then S1 = Diag(gam_L) S0 + Ke^T U
-        float* dst = a.ws_s0 + (id * H + h) * SS;
-#pragma unroll
-        for (int tt = 0; tt < 8; ++tt)
-#pragma unroll
-            for (int x = 0; x < 4; ++x) dst[(16 * tt + 4 * g + x) * kDim + col] = S[tt][x];
+        // S1 = Diag(gam_L) S0 + Ke^T U
         bf16x8 uh[2], ul[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s) bfrag(U[2 * s], U[2 * s + 1], uh[s], ul[s]);
@@ -646,29 +775,54 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_dstate_kernel(const ChunkBwdA
     const int h = static_cast<int>(blockIdx.x - n * H);
     const int64_t row0 = seq_row0(a, n), len = seq_len(a, n);
     const int64_t nch = (len + CH - 1) / CH;
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 4;
+    const int t = threadIdx.x, lane = t & 63, wave = wave_id(), g = lane >> 4;
     const int col = 16 * wave + (lane & 15);
 
+    const uint32_t slo = 4 * g * kDim + col;
     f32x4 dS[8];
-    {
-        const float* src = a.d_sT ? a.d_sT + (n * H + h) * SS : nullptr;
-#pragma unroll
-        for (int tt = 0; tt < 8; ++tt)
-#pragma unroll
-            for (int x = 0; x < 4; ++x) dS[tt][x] = src ? src[(16 * tt + 4 * g + x) * kDim + col] : 0.f;
-    }
+    state_load(a.d_sT ? a.d_sT + (n * H + h) * SS : nullptr, slo, dS);
 
-    for (int64_t c = nch - 1; c >= 0; --c) {
+    // The inputs of chunk c - 1 are requested while chunk c's products run:
+    // log alpha, k and q, the P and T tiles, this thread's dO rows and beta.
+    ChunkRaw<SEQ_NT, true> raw;
+    TileRaw<SEQ_NT> praw, traw;
+    f32x4 oraw[4];
+    float braw = 0.f;
+    auto request_chunk = [&](int64_t c) {
         const int64_t row0c = row0 + c * CH;
         const int L = static_cast<int>(min<int64_t>(CH, len - c * CH));
+        const float* apt = a.ws_apt + (chunk_id(row0, n, c) * H + h) * (3 * TSZ);
+        request_tile<true, SEQ_NT>(apt + TSZ, praw);
+        request_tile<true, SEQ_NT>(apt + 2 * TSZ, traw);
+        request<SEQ_NT, true>(a, row0c, L, h, raw);
+        // rows from L on read row L - 1 and are replaced by zeros (no branches)
+        const float* ob = a.d_o + (row0c * H + h) * kDim;
+        const uint32_t rs = H * kDim;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int r = 16 * m + 4 * g + x;
+                const float o = at(ob, col + static_cast<uint32_t>(min(r, L - 1)) * rs);
+                oraw[m][x] = r < L ? o : 0.f;
+            }
+        const float b = widen(at(a.beta + row0c * H + h, static_cast<uint32_t>(min(t, L - 1)) * H));
+        braw = t < L ? b : 0.f;
+    };
+    if (nch > 0) request_chunk(nch - 1);
+
+    for (int64_t c = nch - 1; c >= 0; --c) {
         const int64_t id = chunk_id(row0, n, c);
-        __syncthreads();
-        const float* apt = a.ws_apt + (id * H + h) * (3 * TSZ);
-        tile_image<true, SEQ_NT>(apt + TSZ, PT);
-        tile_image<true, SEQ_NT>(apt + 2 * TSZ, TT);
+        lds_sync();
+        tile_put<true, SEQ_NT>(praw, PT);
+        tile_put<true, SEQ_NT>(traw, TT);
+        if (t < CH) bs[t] = braw;
+        // dO in accumulator layout (rows r = 16m + 4g + x of column col), split
+        bf16x8 oh[2], ol[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) bfrag(oraw[2 * s], oraw[2 * s + 1], oh[s], ol[s]);
         Staged<SEQ_NT> st;
-        stage<SEQ_NT, true>(a, row0c, L, h, tot, st);
-        stage_beta(a, row0c, L, h, bs);
+        stage_raw<SEQ_NT, true>(raw, tot, st);
 #pragma unroll
         for (int j = 0; j < Staged<SEQ_NT>::TOK; ++j) {
             const int r = st.r0 + j;
@@ -689,23 +843,13 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_dstate_kernel(const ChunkBwdA
             gls[st.c0] = ex2(st.gl[0]);
             gls[st.c0 + 1] = ex2(st.gl[1]);
         }
-        // dO in accumulator layout (rows r = 16m + 4g + x of column col)
-        f32x4 dO[4];
-        const int64_t orow = (row0c * H + h) * kDim + col;
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int r = 16 * m + 4 * g + x;
-                dO[m][x] = r < L ? a.d_o[orow + static_cast<int64_t>(r) * H * kDim] : 0.f;
-            }
-        __syncthreads();
+        // the gradient in this chunk's leaving state (before the next requests,
+        // so that waiting for those does not wait for these stores)
+        state_store(a.ws_ds + (id * H + h) * SS, slo, dS);
+        lds_sync();
+        if (c > 0) request_chunk(c - 1);
+        __builtin_amdgcn_sched_barrier(0);  // the requests go out before the products
 
-        bf16x8 oh[2], ol[2], sh[4], sl[4];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) bfrag(dO[2 * s], dO[2 * s + 1], oh[s], ol[s]);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) bfrag(dS[2 * s], dS[2 * s + 1], sh[s], sl[s]);
         // dU = P^T dO + Ke dS1
         f32x4 dU[4];
 #pragma unroll
@@ -717,36 +861,39 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_dstate_kernel(const ChunkBwdA
                 img_frag(PT, T_PL, m * 2 + s, lane, ah, al);
                 dU[m] = mma3(ah, al, oh[s], ol[s], dU[m]);
             }
+        }
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < 4; ++s) {
+            bf16x8 sh, sl;
+            bfrag(dS[2 * s], dS[2 * s + 1], sh, sl);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
                 bf16x8 ah, al;
                 img_frag(KE, KE_PL, m * 4 + s, lane, ah, al);
-                dU[m] = mma3(ah, al, sh[s], sl[s], dU[m]);
+                dU[m] = mma3(ah, al, sh, sl, dU[m]);
             }
+            __builtin_amdgcn_sched_barrier(0);  // bounds the fragments in flight
         }
         // dW' = T^T dU, then -B dW'
-        bf16x8 uh[2], ul[2];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) bfrag(dU[2 * s], dU[2 * s + 1], uh[s], ul[s]);
         f32x4 nW[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            nW[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int m = 0; m < 4; ++m) nW[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
+        for (int s = 0; s < 2; ++s) {
+            bf16x8 uh, ul;
+            bfrag(dU[2 * s], dU[2 * s + 1], uh, ul);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
                 bf16x8 ah, al;
                 img_frag(TT, T_PL, m * 2 + s, lane, ah, al);
-                nW[m] = mma3(ah, al, uh[s], ul[s], nW[m]);
+                nW[m] = mma3(ah, al, uh, ul, nW[m]);
             }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
 #pragma unroll
             for (int x = 0; x < 4; ++x) nW[m][x] *= -bs[16 * m + 4 * g + x];
-        }
-        // the gradient in this chunk's leaving state
-        float* dst = a.ws_ds + (id * H + h) * SS;
-#pragma unroll
-        for (int tt = 0; tt < 8; ++tt)
-#pragma unroll
-            for (int x = 0; x < 4; ++x) dst[(16 * tt + 4 * g + x) * kDim + col] = dS[tt][x];
         // dS0 = Diag(gam_L) dS1 + Qt^T dO - Kt^T B dW'
         bf16x8 wh[2], wl[2];
 #pragma unroll
@@ -763,15 +910,10 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_dstate_kernel(const ChunkBwdA
                 img_frag(KTT, TT_PL, tt * 2 + s, lane, ah, al);
                 dS[tt] = mma3(ah, al, wh[s], wl[s], dS[tt]);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
-    if (a.ds0) {
-        float* dst = a.ds0 + (n * H + h) * SS;
-#pragma unroll
-        for (int tt = 0; tt < 8; ++tt)
-#pragma unroll
-            for (int x = 0; x < 4; ++x) dst[(16 * tt + 4 * g + x) * kDim + col] = dS[tt][x];
-    }
+    if (a.ds0) state_store(a.ds0 + (n * H + h) * SS, slo, dS);
 }
 
 // ================================================================ grads
@@ -809,7 +951,7 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_grads_kernel(const ChunkBwdAr
     if (!locate(a, id, n, c)) return;
     const int64_t row0c = seq_row0(a, n) + c * CH;
     const int L = static_cast<int>(min<int64_t>(CH, seq_len(a, n) - c * CH));
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 4, l16 = lane & 15;
+    const int t = threadIdx.x, lane = t & 63, wave = wave_id(), g = lane >> 4, l16 = lane & 15;
     const int col = 16 * wave + l16;
     const int64_t rs = static_cast<int64_t>(H) * kDim;      // elements per token row
     const int64_t wslot = id * H + h;
@@ -860,7 +1002,7 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_grads_kernel(const ChunkBwdAr
                 W[m][x] = r < L ? widen(a.v[e0 + r * rs]) : 0.f;
             }
     }
-    __syncthreads();
+    lds_sync();
 
     // ---- phase A
     f32x4 U[4], dU[4], dW[4];
@@ -952,7 +1094,7 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_grads_kernel(const ChunkBwdAr
                 }
             }
     }
-    __syncthreads();  // every wave is done with the phase A images
+    lds_sync();  // every wave is done with the phase A images
 
     // ---- phase B images (natural binding, rows = tokens, k = value columns):
     // dO, -B dW', U.  Even lanes store their value and the odd neighbour's.
@@ -969,12 +1111,23 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_grads_kernel(const ChunkBwdAr
             put_pair(OFF_I1, r, -bs[r] * dW[m][x]);
             put_pair(OFF_I2, r, U[m][x]);
         }
-    __syncthreads();
+    lds_sync();
 
     // ---- phase B: wave w on channels cw = 16w + l16; rows of S0 and dS1 as B operands
     float* dpt = a.ws_dpt + wslot * kDptFloats;
     {
         const int cw = col;
+        // queries and keys of this lane's rows and channel (all loads before the stores below)
+        float qv[4][4], kv[4][4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int r = 16 * m + 4 * g + x;
+                const int64_t e = ((row0c + (r < L ? r : 0)) * H + h) * kDim + cw;
+                qv[m][x] = r < L ? widen(a.q[e]) : 0.f;
+                kv[m][x] = r < L ? widen(a.k[e]) : 0.f;
+            }
         bf16x8 sh[4], sl[4], dh[4], dl[4];
         float dg = 0.f;
         {
@@ -1020,14 +1173,14 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_grads_kernel(const ChunkBwdAr
                     const int64_t e = ((row0c + r) * H + h) * kDim + cw;
                     const float G = Gs[r * GLD + cw];
                     const float gam = ex2(G), ge = ex2(gLc - G);
-                    const float qv = widen(a.q[e]), kv = widen(a.k[e]);
+                    const float q1 = qv[m][x], k1 = kv[m][x];
                     const float dq = dQt[x] * gam;
                     const float dkt = dKt[x] * gam, dke = dKe[x] * ge;
                     a.dq[e] = dq;
                     a.dk[e] = dkt + dke;
-                    a.dla[e] = qv * dq + kv * dkt - kv * dke;
-                    keke += kv * dke;
-                    first += qv * dq + kv * dkt;
+                    a.dla[e] = q1 * dq + k1 * dkt - k1 * dke;
+                    keke += k1 * dke;
+                    first += q1 * dq + k1 * dkt;
                 }
             }
         }
@@ -1068,7 +1221,7 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_grads_kernel(const ChunkBwdAr
             dpt[r * CH + i] = val;
         }
     }
-    __syncthreads();  // phase B images are dead
+    lds_sync();  // phase B images are dead
 
     // ---- phase C: images of dU and B W, then dT = dU (B W)^T on the lower blocks
 #pragma unroll
@@ -1079,7 +1232,7 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_grads_kernel(const ChunkBwdAr
             put_pair(OFF_I0, r, dU[m][x]);
             put_pair(OFF_I1, r, bs[r] * W[m][x]);
         }
-    __syncthreads();
+    lds_sync();
     for (int b = wave; b < 10; b += SEQ_NT / 64) {
         int mr = 0;
         while ((mr + 1) * (mr + 2) / 2 <= b) ++mr;
@@ -1162,7 +1315,7 @@ __global__ __launch_bounds__(INTRA_NT, 1) void chunk_intra_kernel(const ChunkBwd
     if (!locate(a, id, n, c)) return;
     const int64_t row0c = seq_row0(a, n) + c * CH;
     const int L = static_cast<int>(min<int64_t>(CH, seq_len(a, n) - c * CH));
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 4, l16 = lane & 15;
+    const int t = threadIdx.x, lane = t & 63, wave = wave_id(), g = lane >> 4, l16 = lane & 15;
     const int64_t wslot = id * H + h;
 
     // ---- phase 1: T, A, dT (i < r), dP (i <= r)
@@ -1178,7 +1331,7 @@ __global__ __launch_bounds__(INTRA_NT, 1) void chunk_intra_kernel(const ChunkBwd
         }
         stage_beta(a, row0c, L, h, bs);
     }
-    __syncthreads();
+    lds_sync();
     const int yi = t >> 3, y0 = 8 * (t & 7);   // this thread's row and first 8 columns
     {
         // Y = T^T dT: Y_im = sum_{r >= i} T_ri dT_rm
@@ -1190,11 +1343,11 @@ __global__ __launch_bounds__(INTRA_NT, 1) void chunk_intra_kernel(const ChunkBwd
             y[0] += tr * d0.x; y[1] += tr * d0.y; y[2] += tr * d0.z; y[3] += tr * d0.w;
             y[4] += tr * d1.x; y[5] += tr * d1.y; y[6] += tr * d1.z; y[7] += tr * d1.w;
         }
-        __syncthreads();
+        lds_sync();
 #pragma unroll
         for (int u = 0; u < 8; ++u) Ad[yi * PLD + y0 + u] = y[u];
     }
-    __syncthreads();
+    lds_sync();
     {
         // dM = -Y T^T: dM_ik = -sum_m Y_im T_km (only k < i is used)
         float dm[8] = {};
@@ -1208,17 +1361,23 @@ __global__ __launch_bounds__(INTRA_NT, 1) void chunk_intra_kernel(const ChunkBwd
                 }
             }
         }
-        __syncthreads();
+        lds_sync();
 #pragma unroll
         for (int u = 0; u < 8; ++u) Ad[yi * PLD + y0 + u] = dm[u];
     }
-    __syncthreads();
-    if (t < CH) {
+    lds_sync();
+    {
+        // db_r (second term): 8 threads per row, 8 columns each, then their sum
+        const int r = t >> 3, k0 = 8 * (t & 7);
         float s2 = 0.f;
-        for (int k = 0; k < t; ++k) s2 += Ad[t * PLD + k] * As[t * PLD + k];
-        db2[t] = s2;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) s2 += k0 + k < r ? Ad[r * PLD + k0 + k] * As[r * PLD + k0 + k] : 0.f;
+        s2 += __shfl_xor(s2, 4);
+        s2 += __shfl_xor(s2, 2);
+        s2 += __shfl_xor(s2, 1);
+        if ((t & 7) == 0) db2[r] = s2;
     }
-    __syncthreads();
+    lds_sync();
     for (int e = t; e < TSZ; e += INTRA_NT) {
         const int r = e >> 6, i = e & 63;
         Ad[r * PLD + i] = i < r ? bs[r] * Ad[r * PLD + i] : 0.f;   // dA
@@ -1235,7 +1394,7 @@ __global__ __launch_bounds__(INTRA_NT, 1) void chunk_intra_kernel(const ChunkBwd
             *reinterpret_cast<bf16x2*>(&Qs[r * kDim + st.c0]) = (bf16x2){(__bf16)st.qq[j][0], (__bf16)st.qq[j][1]};
         }
     }
-    __syncthreads();
+    lds_sync();
 
     // ---- phase 2: wave w on channels cc = 16w + l16; rows 16R + 4g + x of each block R
     const int cc = 16 * wave + l16;
@@ -1250,10 +1409,9 @@ __global__ __launch_bounds__(INTRA_NT, 1) void chunk_intra_kernel(const ChunkBwd
         float gR[4], kR[4], qR[4];
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-            const int r = 16 * R + 4 * g + x;
-            gR[x] = Gv(r);
-            kR[x] = Kv(r);
-            qR[x] = Qv(r);
+            gR[x] = Gv(16 * R + 4 * g + x);
+            kR[x] = Kv(16 * R + 4 * g + x);
+            qR[x] = Qv(16 * R + 4 * g + x);
         }
 #pragma unroll
         for (int I = 0; I <= R; ++I) {
@@ -1325,10 +1483,24 @@ __global__ __launch_bounds__(INTRA_NT, 1) void chunk_intra_kernel(const ChunkBwd
     }
 
     // ---- totals and the reverse cumulative sum of dL over the chunk's rows
-    const float last = a.ws_dpt[wslot * kDptFloats + 2 * TSZ + cc];
-    const float first = a.ws_dpt[wslot * kDptFloats + 2 * TSZ + kDim + cc];
+    // the grads kernel's terms of dq, dk and dL for this lane's rows: every
+    // load is issued before any store, so they share one memory round trip
     const int64_t rs = static_cast<int64_t>(H) * kDim;
     const int64_t e0 = (row0c * H + h) * kDim + cc;
+    float pq[4][4], pk[4][4], pl[4][4];
+#pragma unroll
+    for (int R = 0; R < 4; ++R)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int r = 16 * R + 4 * g + x;
+            const bool in = r < L;
+            const int64_t e = e0 + (in ? r : 0) * rs;
+            pq[R][x] = in ? a.dq[e] : 0.f;
+            pk[R][x] = in ? a.dk[e] : 0.f;
+            pl[R][x] = in ? a.dla[e] : 0.f;
+        }
+    const float last = a.ws_dpt[wslot * kDptFloats + 2 * TSZ + cc];
+    const float first = a.ws_dpt[wslot * kDptFloats + 2 * TSZ + kDim + cc];
     float dl[4][4], part[4];
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
@@ -1340,9 +1512,9 @@ __global__ __launch_bounds__(INTRA_NT, 1) void chunk_intra_kernel(const ChunkBwd
             if (r < L) {
                 const float kv = Kv(r), qv = Qv(r);
                 const int64_t e = e0 + r * rs;
-                a.dq[e] += dq[R][x];
-                a.dk[e] += dkr[R][x] + dkc[R][x];
-                dl[R][x] = a.dla[e] + qv * dq[R][x] + kv * dkr[R][x] - kv * dkc[R][x] +
+                a.dq[e] = pq[R][x] + dq[R][x];
+                a.dk[e] = pk[R][x] + dkr[R][x] + dkc[R][x];
+                dl[R][x] = pl[R][x] + qv * dq[R][x] + kv * dkr[R][x] - kv * dkc[R][x] +
                            (r == L - 1 ? last : 0.f);
             }
             part[R] += dl[R][x];
