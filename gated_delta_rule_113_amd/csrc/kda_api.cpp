@@ -298,10 +298,8 @@ kda_status backward_impl(const void* q, const void* k, const void* v, const void
     if ((st = debug_check(rows > 0 ? log_alpha : nullptr, rows * H * kda::kDim, false, cu_seqlens,
                           n_seq, T_total, s)) != KDA_OK)
         return st;
-    int n_cu = 0;
-    if ((st = current_cus(&n_cu)) != KDA_OK) return st;
     const kda::BackwardPlan plan =
-        kda::plan_backward(packed, n_seq, T, T_total, H, in_dtype == KDA_BF16, n_cu);
+        kda::plan_backward(packed, n_seq, T, T_total, H, in_dtype == KDA_BF16);
     kda::StreamWorkspace lease;
     void* ws = workspace;
     if (workspace_bytes == KDA_WORKSPACE_AUTO) {
@@ -345,10 +343,8 @@ kda_status backward_size(bool packed, int64_t n_seq, int64_t T, int64_t T_total,
     kda_status st = backward_sizes(packed, n_seq, T, T_total, H, d_k, d_v, in_dtype);
     if (st != KDA_OK) return st;
     if (n_seq == 0) return KDA_OK;
-    int n_cu = 0;
-    if ((st = current_cus(&n_cu)) != KDA_OK) return st;
     *bytes = static_cast<int64_t>(
-        kda::plan_backward(packed, n_seq, T, T_total, H, in_dtype == KDA_BF16, n_cu).ws_bytes);
+        kda::plan_backward(packed, n_seq, T, T_total, H, in_dtype == KDA_BF16).ws_bytes);
     return KDA_OK;
 }
 

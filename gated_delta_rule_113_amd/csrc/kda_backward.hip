@@ -69,14 +69,6 @@ struct BwdArgs {
     float* ckpt;        // workspace: n_slots * H states
     int cb;             // checkpoint interval, 1 <= cb <= kBackwardBlock
     int64_t n_slots;
-    // Segmented (dense input only; seg_len = 0: one workgroup per sequence and
-    // head): a workgroup per (sequence, segment, head), segment slot
-    // z = n * nseg + j, with the segment's entering state seg_start[z][h] and
-    // the gradient in its leaving state seg_grad[z][h].
-    int64_t seg_len;    // a multiple of cb
-    int64_t nseg;
-    const float* seg_start;
-    const float* seg_grad;
 };
 
 // Lane layout of the state, its checkpoint and its gradient: wave w owns the
@@ -229,8 +221,8 @@ __global__ __launch_bounds__(Ly::NT, 1) void backward_kernel(const BwdArgs a)
     const InT* B = static_cast<const InT*>(a.beta);
     const int H = a.H;
     const int64_t blk = blockIdx.x;
-    const int64_t zz = blk / H;  // n, or with segments n * nseg + j
-    const int h = static_cast<int>(blk - zz * H);
+    const int64_t n = blk / H;
+    const int h = static_cast<int>(blk - n * H);
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
@@ -240,34 +232,20 @@ __global__ __launch_bounds__(Ly::NT, 1) void backward_kernel(const BwdArgs a)
     const int col = 4 * Ly::CG * wave + 4 * cg;
     const int cb = a.cb;
 
-    int64_t first, len, slot0, n = zz;
-    const float* s0p;   // entering state (NULL: zeros)
-    const float* dsTp;  // gradient in the leaving state (NULL: zeros)
-    float* ds0p;        // where the gradient in the entering state goes (NULL: nowhere)
-    if (a.seg_len > 0) {
-        n = zz / a.nseg;
-        const int64_t j = zz - n * a.nseg;
-        first = n * a.T + j * a.seg_len;
-        len = a.T - j * a.seg_len < a.seg_len ? a.T - j * a.seg_len : a.seg_len;
-        slot0 = n * ((a.T + cb - 1) / cb) + j * (a.seg_len / cb);
-        s0p = a.seg_start + (zz * H + h) * SS;
-        dsTp = a.seg_grad + (zz * H + h) * SS;
-        ds0p = (j == 0 && a.ds0) ? a.ds0 + (n * H + h) * SS : nullptr;
+    int64_t first, len, slot0;
+    const int64_t unit = n * H + h;
+    const float* s0p = a.s0 ? a.s0 + unit * SS : nullptr;     // entering state (NULL: zeros)
+    const float* dsTp = a.d_sT ? a.d_sT + unit * SS : nullptr; // gradient in the leaving state
+    float* ds0p = a.ds0 ? a.ds0 + unit * SS : nullptr;        // gradient in the entering state
+    if (a.cu_seqlens) {
+        first = a.cu_seqlens[n];
+        len = static_cast<int64_t>(a.cu_seqlens[n + 1]) - first;
+        // floor(first / cb) + n: sequences get disjoint runs of slots
+        slot0 = first / cb + n;
     } else {
-        const int64_t unit = n * H + h;
-        s0p = a.s0 ? a.s0 + unit * SS : nullptr;
-        dsTp = a.d_sT ? a.d_sT + unit * SS : nullptr;
-        ds0p = a.ds0 ? a.ds0 + unit * SS : nullptr;
-        if (a.cu_seqlens) {
-            first = a.cu_seqlens[n];
-            len = static_cast<int64_t>(a.cu_seqlens[n + 1]) - first;
-            // floor(first / cb) + n: sequences get disjoint runs of slots
-            slot0 = first / cb + n;
-        } else {
-            first = n * a.T;
-            len = a.T;
-            slot0 = n * ((a.T + cb - 1) / cb);
-        }
+        first = n * a.T;
+        len = a.T;
+        slot0 = n * ((a.T + cb - 1) / cb);
     }
     if (len < 0 || first < 0) return;  // malformed cu_seqlens
     const int64_t nb = (len + cb - 1) / cb;
@@ -521,247 +499,7 @@ __global__ __launch_bounds__(Ly::NT, 1) void backward_kernel(const BwdArgs a)
     if (ds0p) store_state(G, ds0p);
 }
 
-// Gradient map of one segment [s0, s1) of a sequence: the gradient in the
-// state entering it is G_out = A G_in + C, with G_in the gradient in its
-// leaving state, A = Phi_{s0} ... Phi_{s1-1} and Phi_t = Diag(a_t)(I - b_t k_t k_t^T).
-// Run backwards from [A | C] = [I | 0]: per token, C += q dO^T, then both
-// A <- Phi_t A and C <- Phi_t C.  It needs no forward state.  A and C are
-// independent: one workgroup each per (sequence, segment j >= 1, head), with
-// the lane layout of the backward.
-template <typename InT, class Ly>
-__global__ __launch_bounds__(Ly::NT, 1) void gradmap_kernel(const BwdArgs a, float* gmaps)
-{
-    constexpr int R = Ly::R, TB = kBackwardBlock;
-    // blocks of TB tokens staged, double-buffered
-    __shared__ __attribute__((aligned(16))) float sa[2][TB][kDim], sk[2][TB][kDim],
-        sq[2][TB][kDim], sdo[2][TB][kDim];
-    __shared__ float sb[2][TB];
-    const InT* Q = static_cast<const InT*>(a.q);
-    const InT* K = static_cast<const InT*>(a.k);
-    const InT* B = static_cast<const InT*>(a.beta);
-    const int H = a.H;
-    const int part = blockIdx.x & 1;  // 0: A, 1: C
-    const int64_t blk = blockIdx.x >> 1;
-    const int64_t zz = blk / H;  // n * nseg + j
-    const int h = static_cast<int>(blk - zz * H);
-    const int64_t n = zz / a.nseg;
-    const int64_t j = zz - n * a.nseg;
-    if (j == 0) return;  // the first segment's map is never used
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6;
-    const int lane = tid & 63;
-    const int cg = lane % Ly::CG;
-    const int rg = lane / Ly::CG;
-    const int row0 = R * rg;
-    const int col = 4 * Ly::CG * wave + 4 * cg;
-    const int64_t first = n * a.T + j * a.seg_len;
-    const int64_t len = a.T - j * a.seg_len < a.seg_len ? a.T - j * a.seg_len : a.seg_len;
-    const int e = tid & (kDim - 1);
-    const int role = __builtin_amdgcn_readfirstlane(tid >> 7);
-
-    float4 X[R];  // A (from I) or C (from 0)
-#pragma unroll
-    for (int m = 0; m < R; ++m) {
-        const int r = row0 + m;
-        X[m] = part ? make_float4(0.f, 0.f, 0.f, 0.f)
-                    : make_float4(r == col ? 1.f : 0.f, r == col + 1 ? 1.f : 0.f,
-                                  r == col + 2 ? 1.f : 0.f, r == col + 3 ? 1.f : 0.f);
-    }
-    // X <- Diag(a)(I - b k k^T) X on the lane's share
-    auto apply = [&](const float* ar, const float* kr, float bt) {
-        float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
-#pragma unroll
-        for (int m4 = 0; m4 < R / 4; ++m4) {
-            const float4 k4 = *reinterpret_cast<const float4*>(kr + 4 * m4);
-            const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = 4 * m4 + i;
-                p0 += kv[i] * X[m].x; p1 += kv[i] * X[m].y; p2 += kv[i] * X[m].z; p3 += kv[i] * X[m].w;
-            }
-        }
-        p0 = bt * col_sum<Ly::CG>(p0); p1 = bt * col_sum<Ly::CG>(p1);
-        p2 = bt * col_sum<Ly::CG>(p2); p3 = bt * col_sum<Ly::CG>(p3);
-#pragma unroll
-        for (int m4 = 0; m4 < R / 4; ++m4) {
-            const float4 a4 = *reinterpret_cast<const float4*>(ar + 4 * m4);
-            const float4 k4 = *reinterpret_cast<const float4*>(kr + 4 * m4);
-            const float av[4] = {a4.x, a4.y, a4.z, a4.w};
-            const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = 4 * m4 + i;
-                X[m].x = av[i] * (X[m].x - kv[i] * p0); X[m].y = av[i] * (X[m].y - kv[i] * p1);
-                X[m].z = av[i] * (X[m].z - kv[i] * p2); X[m].w = av[i] * (X[m].w - kv[i] * p3);
-            }
-        }
-    };
-    // Blocks of up to TB tokens, last to first.  One element of a token's
-    // vector per thread (threads 0..127 gates, 128..255 keys, 256..383
-    // queries, 384..511 output gradients; the last two only for C), requested
-    // as raw bits one block ahead and written to the LDS buffer of its block
-    // just before it is used.  A buffer is written again two blocks after it
-    // was read, with a barrier in between.
-    uint32_t x[TB], xb = 0;
-    auto request = [&](int64_t b0) {
-        const int nt = static_cast<int>(len - b0 < TB ? len - b0 : TB);
-        const int64_t v0 = ((first + b0) * H + h) * kDim + e;
-        const int64_t step = static_cast<int64_t>(H) * kDim;
-#pragma unroll
-        for (int t = 0; t < TB; ++t) {
-            if (t < nt) {
-                if (role == 0) x[t] = __float_as_uint(a.log_alpha[v0 + t * step]);
-                else if (role == 1) x[t] = raw_bits(K + v0 + t * step);
-                else if (role == 2 && part) x[t] = raw_bits(Q + v0 + t * step);
-                else if (role == 3 && part) x[t] = __float_as_uint(a.d_o[v0 + t * step]);
-            }
-        }
-        if (tid < nt) xb = raw_bits(B + (first + b0 + tid) * H + h);
-    };
-    auto stage = [&](int buf, int nt) {
-#pragma unroll
-        for (int t = 0; t < TB; ++t) {
-            if (t < nt) {
-                if (role == 0) sa[buf][t][e] = exp_gate(__uint_as_float(x[t]));
-                else if (role == 1) sk[buf][t][e] = from_bits<InT>(x[t]);
-                else if (role == 2 && part) sq[buf][t][e] = from_bits<InT>(x[t]);
-                else if (role == 3 && part) sdo[buf][t][e] = __uint_as_float(x[t]);
-            }
-        }
-        if (tid < nt) sb[buf][tid] = from_bits<InT>(xb);
-    };
-    int buf = 0;
-    int64_t b0 = (len - 1) / TB * TB;
-    request(b0);
-    for (; b0 >= 0; b0 -= TB, buf ^= 1) {
-        const int nt = static_cast<int>(len - b0 < TB ? len - b0 : TB);
-        stage(buf, nt);
-        __syncthreads();
-        if (b0 >= TB) request(b0 - TB);
-        for (int tt = nt - 1; tt >= 0; --tt) {
-            if (part) {
-                const float* qr = &sq[buf][tt][row0];
-                const float4 dot = *reinterpret_cast<const float4*>(&sdo[buf][tt][col]);
-#pragma unroll
-                for (int m4 = 0; m4 < R / 4; ++m4) {
-                    const float4 q4 = *reinterpret_cast<const float4*>(qr + 4 * m4);
-                    const float qv[4] = {q4.x, q4.y, q4.z, q4.w};
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int m = 4 * m4 + i;
-                        X[m].x += qv[i] * dot.x; X[m].y += qv[i] * dot.y;
-                        X[m].z += qv[i] * dot.z; X[m].w += qv[i] * dot.w;
-                    }
-                }
-            }
-            apply(&sa[buf][tt][row0], &sk[buf][tt][row0], sb[buf][tt]);
-        }
-    }
-    float* dst = gmaps + ((zz * H + h) * 2 + part) * SS;
-#pragma unroll
-    for (int m = 0; m < R; ++m) *reinterpret_cast<float4*>(dst + (row0 + m) * kDim + col) = X[m];
-}
-
-// The gradient in the leaving state of every segment, last to first:
-// G_in(nseg-1) = dS_T (or zeros), G_in(j) = A_{j+1} G_in(j+1) + C_{j+1}.  One
-// 16-column slice of one (sequence, head) per workgroup (8 workgroups per
-// head); fp32 on the vector ALUs.
-__global__ __launch_bounds__(256) void grad_combine_kernel(const BwdArgs a, const float* gmaps,
-                                                           float* ggrad, int64_t n_units)
-{
-    __shared__ float sv[kDim][16];
-    const int bid = blockIdx.x;
-    const int slice = bid & 7;
-    const int64_t unit = bid >> 3;
-    if (unit >= n_units) return;
-    const int H = a.H;
-    const int64_t n = unit / H;
-    const int h = static_cast<int>(unit - n * H);
-    const int64_t z0 = n * a.nseg;
-    const int tid = threadIdx.x;
-    const int r = tid >> 1, c8 = 8 * (tid & 1);
-    const int cbase = 16 * slice;
-    {
-        const float* src = a.d_sT ? a.d_sT + unit * SS : nullptr;
-        float* dst = ggrad + ((z0 + a.nseg - 1) * H + h) * SS;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int idx = tid + 256 * e;
-            const int off = (idx >> 4) * kDim + cbase + (idx & 15);
-            const float x = src ? src[off] : 0.f;
-            sv[idx >> 4][idx & 15] = x;
-            dst[off] = x;
-        }
-    }
-    __syncthreads();
-    for (int64_t j = a.nseg - 2; j >= 0; --j) {
-        const float* Am = gmaps + (((z0 + j + 1) * H + h) * 2) * SS;
-        const float* Cm = Am + SS;
-        float acc[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = Cm[r * kDim + cbase + c8 + e];
-        const float* arow = Am + r * kDim;
-        for (int k4 = 0; k4 < kDim / 4; ++k4) {
-            const float4 m4 = *reinterpret_cast<const float4*>(arow + 4 * k4);
-            const float mk[4] = {m4.x, m4.y, m4.z, m4.w};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] += mk[kk] * sv[4 * k4 + kk][c8 + e];
-        }
-        __syncthreads();  // every thread has read sv
-        float* dst = ggrad + ((z0 + j) * H + h) * SS;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            dst[r * kDim + cbase + c8 + e] = acc[e];
-            sv[r][c8 + e] = acc[e];
-        }
-        __syncthreads();
-    }
-}
-
 }  // namespace
-
-BackwardPlan plan_backward(bool packed, int64_t n_seq, int64_t T, int64_t T_total, int64_t H,
-                          bool bf16, int n_cu)
-{
-    BackwardPlan p;
-    const int64_t units = n_seq * H;
-    if (units <= 0) return p;
-    const int64_t rows = packed ? T_total : n_seq * T;
-    if (bf16) {
-        // chunked: one workspace slot per (chunk id, head); ids below rows / 64 + sequences + 1
-        p.chunked = true;
-        p.n_ids = rows / 64 + n_seq + 1;
-        p.ws_bytes = static_cast<size_t>(p.n_ids) * H * chunk_backward_bytes_per_chunk();
-        return p;
-    }
-    // One checkpoint slot per block of kBackwardBlock tokens: dense, every
-    // sequence ceil(T / cb); packed, fewer than T_total / cb + n_seq in all.
-    const int64_t cb = kBackwardBlock;
-    p.n_slots = rows <= 0 ? 0 : packed ? T_total / cb + n_seq : n_seq * ((T + cb - 1) / cb);
-    // Long dense bf16 sequences that give the CUs too few (sequence, head)
-    // pairs are cut into segments of at least kBackwardMinSegment tokens: the
-    // chunked prefill's segment pass gives each segment's entering state,
-    // the gradient maps give each segment's leaving gradient, and the
-    // segments then run in parallel.
-    if (!packed && bf16 && T >= 2 * kBackwardMinSegment && units < n_cu) {
-        int64_t nseg = std::min((n_cu + units - 1) / units, T / kBackwardMinSegment);
-        const int64_t seg = ((T + nseg - 1) / nseg + 63) / 64 * 64;
-        nseg = (T + seg - 1) / seg;
-        if (nseg >= 2) {
-            p.seg = seg;
-            p.nseg = nseg;
-        }
-    }
-    const int64_t n_segs = p.seg ? n_seq * p.nseg : 0;
-    p.ck_floats = static_cast<size_t>(p.n_slots) * H * SS;
-    p.seg_floats = static_cast<size_t>(n_segs) * H * SS;
-    // checkpoints; then with segments: maps and entering states of the
-    // segment pass (3 states per slot), gradient maps (2), leaving gradients (1)
-    p.ws_bytes = (p.ck_floats + 6 * p.seg_floats) * sizeof(float);
-    return p;
-}
 
 hipError_t launch_backward(const void* q, const void* k, const void* v, const void* beta,
                            const float* log_alpha, const float* d_o, const int32_t* cu_seqlens,
@@ -800,43 +538,13 @@ hipError_t launch_backward(const void* q, const void* k, const void* v, const vo
     a.n_slots = plan.n_slots;
     a.ckpt = static_cast<float*>(ws);
 
+    // the token-by-token path serves fp32 inputs (bf16 ones take the chunked path)
+    if (bf16) return hipErrorInvalidValue;
     using Ly = BackwardLayout;
-    if (plan.seg) {
-        const int64_t n_segs = n_seq * plan.nseg;
-        float* scan_ws = static_cast<float*>(ws) + plan.ck_floats;
-        float* gmaps = scan_ws + 3 * plan.seg_floats;
-        float* ggrad = gmaps + 2 * plan.seg_floats;
-        a.seg_len = plan.seg;
-        a.nseg = plan.nseg;
-        a.seg_start = scan_ws + 2 * plan.seg_floats;
-        a.seg_grad = ggrad;
-        e = launch_segment_states(k, v, beta, log_alpha, n_seq, T, H, initial_state, plan.seg,
-                                  scan_ws, stream);
-        if (e == hipSuccess) {
-            hipLaunchKernelGGL((gradmap_kernel<bf16_t, Ly>), dim3(static_cast<unsigned>(2 * n_segs * H)),
-                               dim3(Ly::NT), 0, stream, a, gmaps);
-            e = hipGetLastError();
-            report("gradient map launch", e);
-        }
-        if (e == hipSuccess) {
-            hipLaunchKernelGGL(grad_combine_kernel, dim3(static_cast<unsigned>(units * 8)), dim3(256),
-                               0, stream, a, static_cast<const float*>(gmaps), ggrad, units);
-            e = hipGetLastError();
-            report("gradient combine launch", e);
-        }
-        if (e == hipSuccess) {
-            hipLaunchKernelGGL((backward_kernel<bf16_t, Ly>), dim3(static_cast<unsigned>(n_segs * H)),
-                               dim3(Ly::NT), 0, stream, a);
-            e = hipGetLastError();
-            report("backward launch", e);
-        }
-    } else {
-        const dim3 grid(static_cast<unsigned>(units)), block(Ly::NT);
-        if (bf16) hipLaunchKernelGGL((backward_kernel<bf16_t, Ly>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((backward_kernel<float, Ly>), grid, block, 0, stream, a);
-        e = hipGetLastError();
-        report("backward launch", e);
-    }
+    hipLaunchKernelGGL((backward_kernel<float, Ly>), dim3(static_cast<unsigned>(units)),
+                       dim3(Ly::NT), 0, stream, a);
+    e = hipGetLastError();
+    report("backward launch", e);
     return e;
 }
 

@@ -1544,11 +1544,11 @@ __global__ __launch_bounds__(INTRA_NT, 1) void chunk_intra_kernel(const ChunkBwd
 
 }  // namespace
 
-size_t chunk_backward_bytes_per_chunk()
-{
-    // entering state, leaving-state gradient, A/P/T, dP/dT and the last-token terms
-    return (2 * static_cast<size_t>(SS) + 3 * TSZ + kDptFloats) * sizeof(float);
-}
+// the workspace the plan sizes: entering state, leaving-state gradient, A/P/T,
+// dP/dT and the first- and last-token terms, per (chunk id, head)
+static_assert(kChunkBackwardFloats == 2 * static_cast<size_t>(SS) + 3 * TSZ + kDptFloats,
+              "the workspace layout of the chunked backward");
+static_assert(CH == kChunk, "the plan's chunk length");
 
 hipError_t launch_backward_chunked(const void* q, const void* k, const void* v, const void* beta,
                                    const float* log_alpha, const float* d_o, const int32_t* cu_seqlens,

@@ -9,6 +9,8 @@ namespace kda {
 
 constexpr int kDim = 128;  // d_k = d_v handled by the kernels
 constexpr int64_t kMaxHeads = 65536;  // keeps in-chunk element offsets within 32 bits
+constexpr int64_t kChunk = 64;        // tokens per chunk of the chunked kernels
+constexpr int64_t kStateFloats = int64_t(kDim) * kDim;
 
 // Where the entering and leaving states of the sequences live.  Without slot
 // arrays, sequence n uses entry n of `init` / `fin` ([*, H, 128, 128] fp32).
@@ -70,6 +72,13 @@ constexpr int64_t kShortPrefill = 16;
 // for pass 3 while those images stay under a cap; tier 1 the same segments
 // without the images; tier 2 one workgroup per (sequence, head) and no
 // workspace.  A tier that would not cut any sequence comes back as tier 2.
+// The plans are host arithmetic only (kda_plan.cpp).
+constexpr int64_t kMinSegment = 1024;   // shortest automatic segment
+constexpr size_t kTpBytes = 4 * 8192;   // the split T and P of one chunk (T hi, T lo, P hi, P lo)
+// The fastest plan keeps the T/P images only while one call needs at most
+// this many bytes of them: the million-token workload (32 heads) would need
+// 17 GB of them for about 1% less time.
+constexpr double kTpCap = static_cast<double>(int64_t(8) << 30);
 struct PrefillPlan {
     int tier = 2;
     bool segmented = false;
@@ -95,31 +104,26 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
                                hipStream_t stream);
 
 // Backward pass (gradients in q, k, v, beta, log_alpha and the initial state
-// from those in o and the final state), token by token; dense or packed as the
-// prefill.  Gradients are fp32 in the layouts of their inputs.  The forward
-// sweep stores a checkpoint state every kBackwardBlock tokens (8 KiB per
-// head-token) in a workspace taken in stream order from the device's pool;
-// the reverse sweep recomputes each block from its checkpoint.
+// from those in o and the final state); dense or packed as the prefill.
+// Gradients are fp32 in the layouts of their inputs.  bf16 inputs take the
+// chunked form (kda_backward_chunk.hip), whose workspace holds
+// kChunkBackwardFloats per (chunk id, head).  fp32 inputs take the
+// token-by-token chain rule (kda_backward.hip): its forward sweep stores a
+// checkpoint state every kBackwardBlock tokens (8 KiB per head-token) in the
+// workspace, and the reverse sweep recomputes each block from its checkpoint.
 constexpr int kBackwardBlock = 8;
-// Long dense bf16 sequences with fewer (sequence, head) pairs than CUs are cut
-// into segments of at least this many tokens (a multiple of 64), run in
-// parallel from their entering states (the chunked prefill's segment pass) and
-// leaving gradients (per-segment gradient maps, composed in order).
-constexpr int64_t kBackwardMinSegment = 1024;
+// per (chunk, head): entering state, leaving-state gradient, A / P / T, and
+// dP, dT with the first- and last-token terms of d log alpha
+constexpr size_t kChunkBackwardFloats =
+    2 * kStateFloats + 3 * kChunk * kChunk + (2 * kChunk * kChunk + 2 * kDim);
 struct BackwardPlan {
     bool chunked = false;       // bf16 inputs: the chunked matrix-core backward
     int64_t n_ids = 0;          // chunked: chunk ids per head
     int64_t n_slots = 0;        // token-by-token: checkpoint slots per head
-    int64_t seg = 0, nseg = 1;  // dense bf16 segments in time (seg = 0: none)
-    size_t ck_floats = 0;       // checkpoint floats
-    size_t seg_floats = 0;      // floats of one per-segment state array
     size_t ws_bytes = 0;        // workspace bytes in all
 };
 BackwardPlan plan_backward(bool packed, int64_t n_seq, int64_t T, int64_t T_total, int64_t H,
-                          bool bf16, int n_cu);
-// Chunked backward (bf16 inputs; kda_backward_chunk.hip): per (chunk, head)
-// the entering state, the gradient in the leaving state, A, P, T, dP and dT.
-size_t chunk_backward_bytes_per_chunk();
+                          bool bf16);
 hipError_t launch_backward_chunked(const void* q, const void* k, const void* v, const void* beta,
                                    const float* log_alpha, const float* d_o, const int32_t* cu_seqlens,
                                    int64_t n_seq, int64_t T, int64_t H, const float* initial_state,
@@ -127,6 +131,7 @@ hipError_t launch_backward_chunked(const void* q, const void* k, const void* v, 
                                    float* dbeta, float* dlog_alpha, float* d_initial_state,
                                    int64_t n_ids, void* ws, hipStream_t stream);
 // ws: at least plan.ws_bytes bytes of device memory, 256-byte aligned.
+// bf16 must match the plan (chunked); fp32 inputs take the token-by-token path.
 hipError_t launch_backward(const void* q, const void* k, const void* v, const void* beta,
                            const float* log_alpha, const float* d_o, const int32_t* cu_seqlens,
                            int64_t n_seq, int64_t T, int64_t H, const float* initial_state,
@@ -177,18 +182,6 @@ hipError_t check_preconditions(const float* log_alpha, int64_t n_gates, bool raw
 // Tokens per segment forced by kda_set_prefill_segment (0 = automatic).
 int64_t forced_segment();
 void set_forced_segment(int64_t tokens);
-
-// The entering state of every segment of `seg` tokens (a positive multiple
-// of 64) of n_seq dense bf16 sequences of T tokens: pass 1 and the combine of
-// the segmented chunked prefill, without its outputs.  `ws` holds
-// n_seq * nseg slots (nseg = ceil(T / seg), slot n * nseg + j) of H states
-// each, three times over: the segment maps [0, 2 * slots * H) states, then
-// the entering states [2 * slots * H, 3 * slots * H).  Nothing is launched
-// when nseg < 2.
-hipError_t launch_segment_states(const void* k, const void* v, const void* beta,
-                                 const float* log_alpha, int64_t n_seq, int64_t T, int64_t H,
-                                 const float* initial_state, int64_t seg, float* ws,
-                                 hipStream_t stream);
 
 
 }  // namespace kda

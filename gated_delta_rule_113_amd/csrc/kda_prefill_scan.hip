@@ -1551,11 +1551,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* cu, int64_t n
 
 // ---------------- host side
 
-constexpr int64_t kMinSegment = 1024;
-// The fastest plan keeps the T/P images only while one call needs at most
-// this many bytes of them: the million-token workload (32 heads) would need
-// 17 GB of them for about 1% less time.
-constexpr double kTpCap = static_cast<double>(int64_t(8) << 30);
+static_assert(TP_BYTES == kTpBytes, "the plan sizes the T/P images of this kernel");
+static_assert(CH == kChunk && SS == kStateFloats, "the plan's chunk and state sizes");
 
 }  // namespace
 
@@ -1581,77 +1578,6 @@ constexpr double kTpCap = static_cast<double>(int64_t(8) << 30);
 // sequences cut in two or more, fewer than 2 * T_total / seg_min of them
 // (such a sequence is longer than a segment, so its count is below twice its
 // length over the segment length).
-PrefillPlan plan_prefill_scan(bool packed, int64_t n_seq, int64_t T, int64_t T_total, int64_t H,
-                              int n_cu, int64_t forced, int tier)
-{
-    PrefillPlan p;
-    p.tier = 2;
-    if (n_seq <= 0 || H <= 0 || tier >= 2) return p;
-    const int64_t rows = packed ? T_total : n_seq * T;
-    int64_t seg = forced;
-    if (seg <= 0) {
-        const int64_t per_cu = (rows * H + n_cu - 1) / n_cu;
-        seg = std::max<int64_t>(kMinSegment, (per_cu + CH - 1) / CH * CH);
-    }
-    // T/P blocks: one per (chunk id, head), ids below rows / 64 + sequences + 1
-    const int64_t tp_ids = rows / CH + n_seq + 1;
-    const bool tp_ok = tier == 0 && static_cast<double>(tp_ids) * H * TP_BYTES <= kTpCap;
-    int64_t seg0 = seg, seg_min = seg, nseg_dense = 1, n_segs = 0, slots = 0;
-    bool tp = false;
-    size_t plan_bytes = 0;
-    if (!packed) {
-        auto dense_segments = [&](int64_t s0, int64_t s) {
-            return T > s0 ? 1 + (T - s0 + s - 1) / s : int64_t(1);
-        };
-        int64_t seg_tp = seg, seg0_tp = seg;
-        if (forced <= 0 && T > seg) {
-            const int64_t k = (T + seg - 1) / seg;  // segments at the plain length
-            // T = k L + (3/5) L
-            const int64_t even = (5 * T + 5 * k + 2) / (5 * k + 3);
-            seg_tp = std::max<int64_t>(kMinSegment, (even + CH - 1) / CH * CH);
-            seg0_tp = seg_tp;
-        }
-        tp = tp_ok && dense_segments(seg0_tp, seg_tp) > 1;
-        if (tp) {
-            seg = seg_tp;
-            seg0 = seg0_tp;
-        } else if (forced <= 0 && T > seg) {
-            const int64_t k = (T + seg - 1) / seg;
-            const int64_t even = (8 * T + 8 * k + 6) / (8 * k + 7);
-            seg = std::max<int64_t>(kMinSegment, (even + CH - 1) / CH * CH);
-            seg0 = std::min<int64_t>(seg, (seg * 7 / 8 + CH - 1) / CH * CH);
-        }
-        nseg_dense = dense_segments(seg0, seg);
-        if (nseg_dense < 2) return p;
-        n_segs = slots = n_seq * nseg_dense;
-        seg_min = seg;
-    } else {
-        if (forced <= 0) seg_min = std::max<int64_t>(kMinSegment, (seg / 8 + CH - 1) / CH * CH);
-        if (T_total <= seg_min) return p;  // no sequence is longer than a segment
-        const int64_t per_min = (T_total + seg_min - 1) / seg_min;
-        n_segs = n_seq + per_min;
-        slots = std::min<int64_t>(n_segs, 2 * per_min);
-        // seg_first [n_seq + 2], ws_first [n_seq + 1], seg_order [n_segs]
-        plan_bytes = ((2 * static_cast<size_t>(n_seq) + 3 + static_cast<size_t>(n_segs)) * 4 + 255) /
-                     256 * 256;
-        tp = tp_ok;
-    }
-    p.tier = tp ? 0 : 1;
-    p.segmented = true;
-    p.tp = tp;
-    p.seg = seg;
-    p.seg0 = seg0;
-    p.seg_min = seg_min;
-    p.nseg_dense = packed ? 0 : nseg_dense;
-    p.n_segs = n_segs;
-    p.slots = slots;
-    p.plan_bytes = plan_bytes;
-    p.tp_blocks = tp ? tp_ids : 0;
-    p.ws_bytes = plan_bytes + static_cast<size_t>(slots) * H * 3 * SS * sizeof(float) +
-                 static_cast<size_t>(p.tp_blocks) * H * TP_BYTES;
-    return p;
-}
-
 hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, const void* beta,
                                const float* log_alpha, const int32_t* cu_seqlens, int64_t n_seq,
                                int64_t T, int64_t H, const StateRefs& st, float* o, bool raw,
@@ -1727,47 +1653,6 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
     else hipLaunchKernelGGL((scan_kernel<true, false>), grid, block, 0, stream, a);
     e = hipGetLastError();
     report("prefill scan launch", e);
-    return e;
-}
-
-hipError_t launch_segment_states(const void* k, const void* v, const void* beta,
-                                 const float* log_alpha, int64_t n_seq, int64_t T, int64_t H,
-                                 const float* initial_state, int64_t seg, float* ws,
-                                 hipStream_t stream)
-{
-    const int64_t nseg = (T + seg - 1) / seg;
-    if (n_seq <= 0 || nseg < 2) return hipSuccess;
-    ScanArgs a = {};
-    a.q = static_cast<const bf16_t*>(k);  // pass 1 reads no queries
-    a.k = static_cast<const bf16_t*>(k);
-    a.v = static_cast<const bf16_t*>(v);
-    a.beta = static_cast<const bf16_t*>(beta);
-    a.log_alpha = log_alpha;
-    a.cu_seqlens = nullptr;
-    a.T = T;
-    a.n_seq = n_seq;
-    a.H = static_cast<int>(H);
-    a.st.init = initial_state;
-    a.o = nullptr;
-    a.raw = 0;
-    a.short_max = -1;
-    a.seg_len = seg;
-    a.seg0_len = seg;
-    a.seg0_out = 0;  // every segment's map, and each entering state, in the workspace
-    a.nseg_dense = nseg;
-    a.n_segs = n_seq * nseg;
-    a.ws_maps = ws;
-    a.ws_start = ws + static_cast<size_t>(a.n_segs) * H * 2 * SS;
-    hipLaunchKernelGGL((scan_kernel<false, false>), dim3(static_cast<unsigned>(a.n_segs * H)), dim3(NT), 0,
-                       stream, a);
-    hipError_t e = hipGetLastError();
-    report("segment map launch", e);
-    if (e != hipSuccess) return e;
-    const int64_t units = n_seq * H;
-    hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>((units + 7) / 8 * 64)), dim3(512),
-                       0, stream, a);
-    e = hipGetLastError();
-    report("segment combine launch", e);
     return e;
 }
 

@@ -79,7 +79,7 @@ int cu_count(int dev)
 
 hipError_t StreamWorkspace::acquire(size_t bytes, hipStream_t s)
 {
-    release();
+    (void)release();
     if (bytes == 0) return hipSuccess;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);

@@ -374,9 +374,11 @@ kda_status kda_varlen_backward(const void *q, const void *k, const void *v, cons
  * device (0 when it needs none): for the prefills under the given plan (a plan
  * that would cut no sequence needs none), for the backward calls in all.  The
  * arguments are validated as the calls validate them (a non-OK status leaves
- * *bytes = 0); nothing is enqueued.  The sizes depend on the device's compute
- * units and on kda_set_prefill_segment.  The *_raw and *_slots prefills take
- * the sizes of their plain forms.
+ * *bytes = 0); nothing is enqueued.  The prefill sizes depend on the current
+ * device's compute units (a query that needs them and finds no device returns
+ * KDA_ERR_HIP) and on kda_set_prefill_segment; the backward sizes depend on
+ * the arguments alone.  The *_raw and *_slots prefills take the sizes of their
+ * plain forms.
  */
 kda_status kda_prefill_workspace_size(int64_t B, int64_t T, int64_t H, int64_t d_k, int64_t d_v,
                                       kda_dtype in_dtype, kda_plan plan, int64_t *bytes);

@@ -126,6 +126,21 @@ def loss_gradients(workload: int, o_shape, n_states: int, H: int, dk: int = 128,
     return d_o, d_s
 
 
+def output_gradients(workload: int, B: int, T: int, H: int, dv: int = 128, heads=None) -> np.ndarray:
+    """Seeded N(0, 1) float32 gradients of a loss in the outputs, [B, T, H, dv]
+    (or the given heads only), one stream per (sequence, head), drawn in
+    parallel: for large workloads, where one stream would be slow."""
+    heads = list(range(H)) if heads is None else list(heads)
+    d_o = np.empty((B, T, len(heads), dv), np.float32)
+
+    def one(job):
+        b, j, h = job
+        d_o[b, :, j] = _rng(workload, GRAD, 2, b, h).standard_normal((T, dv), dtype=np.float32)
+
+    _run_parallel(one, [(b, j, h) for b in range(B) for j, h in enumerate(heads)])
+    return d_o
+
+
 # ----------------------------------------------------------------------------
 # workloads in the library layout
 # ----------------------------------------------------------------------------

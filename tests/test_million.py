@@ -1,14 +1,29 @@
-"""Million-token prefill on the GPU vs the fp64 oracle.
+"""The million-token workload on the GPU vs the fp64 oracle.
 
 The workload: B = 1, H = 32, T = 1,048,576, bf16 q/k/v/beta, fp32 log_alpha
-and state, the gated channel mix, zero initial state.  The check follows the
-workload's own plan: (i) the GPU runs all 1,048,576 tokens and the oracle
-recomputes heads 0 and 31 over all of them (outputs and final states); (ii) a
-separate GPU prefill of the first 65,536 tokens is compared with the oracle on
-the final states of all 32 heads.
+and state, the gated channel mix, zero initial state.
 
-The inputs take about 56 GiB of host and device memory; generating them and
-running the oracle dominate the test's time."""
+Prefill, following the workload's own plan: (i) the GPU runs all 1,048,576
+tokens and the oracle recomputes heads 0 and 31 over all of them (outputs and
+final states), in two pieces: the first 983,040 tokens, then the last 65,536
+from the state the first piece leaves (the same arithmetic as one call);
+(ii) a separate GPU prefill of the first 65,536 tokens is compared with the
+oracle on the final states of all 32 heads.
+
+Backward (seeded N(0, 1) gradients in every output and in the final states):
+the chunked backward of all 1,048,576 tokens and 32 heads with its workspace
+(about 105 GiB) next to the inputs and gradients on one device; then
+(iii) every gradient of the last 65,536 tokens of heads 0 and 31 against the
+oracle's backward of that suffix, entered with the oracle's state after the
+first 983,040 tokens (the suffix's gradients depend on nothing else);
+(iv) over all heads and tokens, two identities that hold at any size: the
+loss is linear in q at fixed everything else, so sum dq . q = sum dO . o, and
+jointly linear in v and the initial state (zero here), so
+sum dv . v = sum dO . o + sum dS_T . S_T, with o and S_T from the GPU
+prefill; (v) every gradient finite.
+
+The host copies of the inputs take about 72 GiB; generating them and running
+the oracle dominate the time."""
 import time
 
 import numpy as np
@@ -17,20 +32,23 @@ import pytest
 import gated_delta_rule_113_amd as kda
 import kda_inputs as ki
 import oracle
-from kda_gpu import check, device, rel_err_states, rel_err_vectors, to_dev
+from kda_gpu import TOL, check, device, rel_err_states, rel_err_vectors, to_dev
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 T_FULL = 1 << 20
 PREFIX = 65536
+SUFFIX = 65536
 HEADS = (0, 31)
+GRAD_WORKLOAD = 7
 
 
 def _log(msg):
     print(f"[million] {msg}", flush=True)
 
 
-def test_million_token_prefill():
+@pytest.fixture(scope="module")
+def million():
     torch = __import__("torch")
     dev = device()
     t0 = time.time()
@@ -38,13 +56,35 @@ def test_million_token_prefill():
     _log(f"inputs generated in {time.time() - t0:.0f}s")
     t = {n: to_dev(getattr(inp, n), "bf16", dev) for n in ("q", "k", "v", "beta")}
     t["log_alpha"] = to_dev(inp.log_alpha, "f32", dev)
+    yield inp, t
+    t.clear()
+    torch.cuda.empty_cache()
 
-    def widened(index):
-        """Oracle inputs (exact fp32 widening) of a slice of the workload."""
-        w = [ki.bf16_to_f32(np.ascontiguousarray(getattr(inp, n)[index]))
-             for n in ("q", "k", "v", "beta")]
-        return (*w, np.ascontiguousarray(inp.log_alpha[index]))
 
+def _widened(inp, index):
+    """Oracle inputs (exact fp32 widening) of a slice of the workload."""
+    w = [ki.bf16_to_f32(np.ascontiguousarray(getattr(inp, n)[index])) for n in ("q", "k", "v", "beta")]
+    return (*w, np.ascontiguousarray(inp.log_alpha[index]))
+
+
+@pytest.fixture(scope="module")
+def oracle_heads(million):
+    """The oracle over heads 0 and 31 in two pieces: (outputs of all tokens,
+    state after the first T - SUFFIX tokens, final state)."""
+    inp, _ = million
+    hs = list(HEADS)
+    cut = T_FULL - SUFFIX
+    t1 = time.time()
+    o1, s_mid = oracle.prefill(*_widened(inp, (slice(None), slice(0, cut), hs)), None)
+    o2, s_fin = oracle.prefill(*_widened(inp, (slice(None), slice(cut, None), hs)), s_mid)
+    _log(f"oracle, 2 heads x {T_FULL} tokens, in {time.time() - t1:.0f}s")
+    return np.concatenate([o1, o2], axis=1), s_mid, s_fin
+
+
+def test_million_token_prefill(million, oracle_heads):
+    torch = __import__("torch")
+    inp, t = million
+    o_ref, _, S_ref = oracle_heads
     # (i) all tokens; heads 0 and 31 checked over every token
     o, S = kda.kda_prefill(t["q"], t["k"], t["v"], t["beta"], t["log_alpha"], None)
     torch.cuda.synchronize()
@@ -53,18 +93,89 @@ def test_million_token_prefill():
     o_h = o[:, :, hs].cpu().numpy()
     S_h = S[:, hs].cpu().numpy()
     assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(S).all())
-    del o
-    t1 = time.time()
-    o_ref, S_ref = oracle.prefill(*widened((slice(None), slice(None), hs)), None)
-    _log(f"oracle, 2 heads x {T_FULL} tokens, in {time.time() - t1:.0f}s")
+    del o, S
     check("million, heads 0 and 31", rel_err_vectors(o_h, o_ref), rel_err_states(S_h, S_ref))
 
     # (ii) the 65,536-token prefix; final states of all heads
     pre = {n: x[:, :PREFIX].contiguous() for n, x in t.items()}
-    del t
     o_p, S_p = kda.kda_prefill(pre["q"], pre["k"], pre["v"], pre["beta"], pre["log_alpha"], None)
     torch.cuda.synchronize()
+    del pre, o_p
     t2 = time.time()
-    _, S_pref = oracle.prefill(*widened((slice(None), slice(0, PREFIX))), None)
+    _, S_pref = oracle.prefill(*_widened(inp, (slice(None), slice(0, PREFIX))), None)
     _log(f"oracle, 32 heads x {PREFIX} tokens, in {time.time() - t2:.0f}s")
     check("million prefix, all heads (final states)", 0.0, rel_err_states(S_p.cpu().numpy(), S_pref))
+
+
+def _dot(a, b, h):
+    """sum a[..., h, :] * b[..., h, :] in fp64 over one head (bounded temporaries)."""
+    return float((a[:, :, h].double() * b[:, :, h].double()).sum())
+
+
+def _absdot(a, b, h):
+    return float((a[:, :, h].double() * b[:, :, h].double()).abs().sum())
+
+
+def test_million_token_backward(million, oracle_heads):
+    torch = __import__("torch")
+    dev = device()
+    inp, t = million
+    _, s_mid, _ = oracle_heads
+    H = 32
+    t0 = time.time()
+    d_o = ki.output_gradients(GRAD_WORKLOAD, 1, T_FULL, H)
+    _, d_s = ki.loss_gradients(GRAD_WORKLOAD, (1, 0, H, 128), 1, H)
+    _log(f"loss gradients generated in {time.time() - t0:.0f}s")
+    do_dev = to_dev(d_o, "f32", dev)
+    ds_dev = to_dev(d_s, "f32", dev)
+
+    # the prefill's outputs and final state for the identities
+    o, S = kda.kda_prefill(t["q"], t["k"], t["v"], t["beta"], t["log_alpha"], None)
+    torch.cuda.synchronize()
+    lin = sum(_dot(do_dev, o, h) for h in range(H))
+    lin_abs = sum(_absdot(do_dev, o, h) for h in range(H))
+    st = float((ds_dev.double() * S.double()).sum())
+    st_abs = float((ds_dev.double() * S.double()).abs().sum())
+    del o, S
+    torch.cuda.empty_cache()
+
+    wbytes = kda.backward_workspace_size(1, T_FULL, H, torch.bfloat16)
+    free, total = torch.cuda.mem_get_info(dev)
+    _log(f"backward workspace {wbytes / 2**30:.1f} GiB; device memory free {free / 2**30:.1f} "
+         f"of {total / 2**30:.1f} GiB before it and the gradients")
+    ws = torch.empty(wbytes, dtype=torch.uint8, device=dev)
+    t1 = time.time()
+    g = kda.kda_backward(t["q"], t["k"], t["v"], t["beta"], t["log_alpha"], do_dev, None, ds_dev,
+                         workspace=ws)
+    torch.cuda.synchronize()
+    _log(f"GPU backward of {T_FULL} tokens x {H} heads in {time.time() - t1:.2f}s (first call)")
+    del ws
+    for n, x in g.items():
+        assert bool(torch.isfinite(x).all()), n
+
+    # (iv) the identities over every head and token
+    q_id = sum(_dot(g["dq"], t["q"], h) for h in range(H))
+    q_abs = sum(_absdot(g["dq"], t["q"], h) for h in range(H))
+    v_id = sum(_dot(g["dv"], t["v"], h) for h in range(H))
+    v_abs = sum(_absdot(g["dv"], t["v"], h) for h in range(H))
+    e_q = abs(q_id - lin) / max(q_abs, lin_abs)
+    e_v = abs(v_id - lin - st) / max(v_abs, lin_abs + st_abs)
+    _log(f"sum dq.q = {q_id:.6e}, sum dO.o = {lin:.6e} (rel {e_q:.2e}); "
+         f"sum dv.v = {v_id:.6e}, + sum dS.S = {lin + st:.6e} (rel {e_v:.2e})")
+    assert e_q <= TOL and e_v <= TOL
+
+    # (iii) the last SUFFIX tokens of heads 0 and 31
+    hs = list(HEADS)
+    cut = T_FULL - SUFFIX
+    got = {n: (x[:, hs] if n == "dinitial_state" else x[:, cut:, hs]).cpu().numpy()
+           for n, x in g.items()}
+    del g
+    t2 = time.time()
+    ref = oracle.backward(*_widened(inp, (slice(None), slice(cut, None), hs)),
+                          d_o[:, cut:, hs], s_mid, d_s[:, hs])
+    _log(f"oracle backward, 2 heads x {SUFFIX} tokens, in {time.time() - t2:.0f}s")
+    errs = {n: rel_err_vectors(got[n], ref[n]) for n in ("dq", "dk", "dv", "dlog_alpha")}
+    errs["dbeta"] = rel_err_vectors(np.swapaxes(got["dbeta"], -1, -2), np.swapaxes(ref["dbeta"], -1, -2))
+    _log("suffix: " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()) + f" (tol {TOL:g})")
+    for n, e in errs.items():
+        assert e <= TOL, (n, e)
