@@ -8,13 +8,21 @@ by one token (kda_decode_step over all 2048 head states).  The default run
 times 1024 consecutive steps, the length of the workload.  ``value`` is decode
 tokens/s (64 tokens per step) with all inputs already resident in HBM.
 
-Also reported (same JSON line): the chunked-prefill workload (B = 1, H = 32,
-T = 32768, bf16 inputs, gated channel mix) timed with HIP events, its
-tokens/s and roofline; the roofline of the decode kernel (algorithmic bytes
-per launch over the measured average launch duration, against 8 TB/s); and
-the CPU oracle timed on a bounded sample of the decode workload on the host
-cores; and the backward pass (gradients of a prefill) at a training shape,
-B = 8 x T = 4096, H = 32.
+Also reported (same JSON line), each timed with HIP events:
+  * the roofline of the decode kernel (algorithmic bytes per launch over the
+    measured average launch duration, against 8 TB/s), and the same decode at
+    B = 256 (512 MiB of state, twice the last-level cache);
+  * the chunked-prefill workload (B = 1, H = 32, T = 32768, bf16 inputs,
+    gated channel mix): tokens/s and roofline;
+  * the million-token prefill (B = 1, H = 32, T = 1,048,576, the same
+    distributions), the packed prefill of 16 sequences with log-uniform
+    lengths in [1024, 65536], half resumed from states, and the small fp32
+    prefill (B = 1, H = 1, T = 256);
+  * the backward pass (gradients of a prefill) at a training shape,
+    B = 8 x T = 4096, H = 32;
+  * the fp64 CPU oracle on the host cores: a bounded sample of the decode
+    workload on every core, and a 4096-token slice of the chunked-prefill
+    workload on one thread.
 
     python bench.py [--gpus 1] [--steps 1024] [--warmup 32] [--no-prefill]
 """
@@ -43,13 +51,16 @@ DECODE_BYTES_PER_HEAD = 2 * D * D * 4 + 2 * D * 2 + D * 2 + 2 + D * 4 + D * 4
 PREFILL_BYTES_PER_HEAD_TOKEN = 3 * D * 2 + 2 + D * 4 + D * 4
 # Chunked-algorithm flops per head-token at chunk 64 (d_k = d_v = 128).
 PREFILL_FLOPS_PER_HEAD_TOKEN = 9_024_853 / 64
-# Backward, per head-token (d = 128, a multiply-add counted as 2): the token's
-# forward to S' and the next state (S' = Diag(a) S: d^2; p = S'^T k: 2 d^2;
-# S' + k u^T: 2 d^2) and its chain rule (G += q dO^T, du = G^T k, S' dO,
-# G u, S' dp, G + k dp^T, rowsum(G' .* S'): 2 d^2 each; Diag(a) G': d^2),
-# vectors of length d left out.  Recomputation from checkpoints is not counted.
-BACKWARD_FLOPS_PER_HEAD_TOKEN = (1 + 2 + 2 + 7 * 2 + 1) * D * D
-FP32_VALU_PEAK_TFLOPS = 157.3
+# Backward (bf16 inputs, the chunked form), per head-token: reads q, k, v
+# (bf16), beta (bf16), log_alpha and d_o (fp32); writes dq, dk, dv, d log_alpha
+# (fp32) and d beta (fp32).
+BACKWARD_BYTES_PER_HEAD_TOKEN = 3 * D * 2 + 2 + 2 * D * 4 + 4 * D * 4 + 4
+# Its matrix products per 64-token chunk and head (C = 64, d = 128, a
+# multiply-add counted as 2): eight C x d x d products (the recomputed
+# X = Kt S0 and leaving state, Ke dS1, Qt^T dO, Kt^T B dW', dQt, dKt, dKe) and
+# twelve C x C x d ones (the recomputed A, P and U; P^T dO, T^T dU, dP, dT,
+# dM = -T^T dT T^T, and the dA / dP terms of dq and dk).
+BACKWARD_FLOPS_PER_HEAD_TOKEN = (8 * 2 * 64 * D * D + 12 * 2 * 64 * 64 * D) / 64
 
 
 def parse():
@@ -75,8 +86,12 @@ def parse():
     ap.add_argument("--prefill-warmup", type=int, default=30,
                     help="untimed prefill calls first: right after the decode section the first "
                          "~30 calls run up to 25%% slower while the GPU settles")
-    ap.add_argument("--cpu-steps", type=int, default=1024,
-                    help="decode steps of the workload the CPU oracle runs (all heads)")
+    ap.add_argument("--cpu-steps", type=int, default=512,
+                    help="decode steps of the workload the CPU oracle runs (all heads, every core)")
+    ap.add_argument("--no-million", action="store_true", help="skip the million-token prefill")
+    ap.add_argument("--no-varlen", action="store_true", help="skip the packed prefill")
+    ap.add_argument("--no-small", action="store_true", help="skip the small fp32 prefill")
+    ap.add_argument("--no-large-decode", action="store_true", help="skip the B = 256 decode")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB "
@@ -440,33 +455,252 @@ def main():
                              po, ps, pms, T, result, pws)
             del pq, pk, pv, pb, pla, po, ps, pws
 
+    if not args.no_large_decode:
+        time_decode_large(kda, ki, torch, np, dev, up, stream, H, result)
+    if not args.no_million:
+        time_prefill_million(kda, ki, torch, np, dev, up, stream, H, result)
+    if not args.no_varlen:
+        time_prefill_varlen(kda, ki, torch, np, dev, up, stream, H, result)
+    if not args.no_small:
+        time_prefill_small(kda, ki, torch, np, dev, up, stream, result)
+
     # ---------------- backward pass (secondary) ---------------------------
     if not args.no_backward:
         time_backward(kda, ki, torch, np, dev, up, stream, args.backward_reps, result)
 
     # ---------------- CPU oracle baseline ---------------------------------
     if not args.no_cpu:
-        import oracle
-
-        S = min(args.cpu_steps, n_gen)
-        qf, kf, vf, bf, laf = (x[:S] for x in inp.widened())
-        threads = len(os.sched_getaffinity(0))
-        log(f"cpu oracle: {S} decode steps x {B * H} heads on {threads} threads")
-        t0 = time.time()
-        oracle.decode_chain(qf, kf, vf, bf, laf, inp.initial_state, n_threads=threads)
-        dt = time.time() - t0
-        result["cpu_baseline"] = {
-            "value": B * S / dt,
-            "unit": "tokens/s",
-            "cores": oracle.max_threads(threads),
-            "kind": "oracle",
-            "sample": f"the first {S} of the workload's decode steps, all {B}x{H} heads, "
-                      f"fp64 token-by-token recurrence, {dt:.1f} s wall",
-        }
-        log(f"cpu oracle: {B * S / dt:.1f} tokens/s in {dt:.1f}s")
+        result["cpu_baseline"] = cpu_baseline(ki, np, B, H, args.cpu_steps, inp if n_gen >= args.cpu_steps else None)
 
     print(json.dumps(result), flush=True)
     return 0
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(ki, np, B, H, steps, inp=None):
+    """The fp64 oracle on the host: `steps` steps of the decode workload (all
+    B x H heads, every core the process may use), and one thread on the first
+    4096 tokens of 16 heads of the chunked-prefill workload."""
+    import oracle
+
+    if inp is None:
+        inp = ki.decode_steps(1, steps=steps, N=B, H=H)
+    qf, kf, vf, bf, laf = (x[:steps] for x in inp.widened())
+    threads = len(os.sched_getaffinity(0))
+    log(f"cpu oracle: {steps} decode steps x {B * H} heads on {threads} threads")
+    t0 = time.time()
+    oracle.decode_chain(qf, kf, vf, bf, laf, inp.initial_state, n_threads=threads)
+    dt = time.time() - t0
+    Ts, Hs = 4096, 16
+    pin = ki.workload_chunked(T=Ts, H=32, heads=range(Hs))
+    t1 = time.time()
+    oracle.prefill(*pin.widened(), None, n_threads=1)
+    dt1 = time.time() - t1
+    log(f"cpu oracle: decode {B * steps / dt:.1f} tokens/s in {dt:.1f}s; one thread, prefill "
+        f"{Ts * Hs / dt1:.0f} head-tokens/s in {dt1:.1f}s")
+    return {
+        "value": B * steps / dt,
+        "unit": "tokens/s",
+        "cores": oracle.max_threads(threads),
+        "kind": "oracle",
+        "cpu_model": cpu_model(),
+        "sample": f"the first {steps} of the decode workload's 1024 steps, all {B}x{H} heads, fp64 "
+                  f"token-by-token recurrence, {dt:.1f} s wall on {oracle.max_threads(threads)} threads",
+        "one_thread_prefill": {
+            "sample": f"the first {Ts} tokens of heads 0..{Hs - 1} of the chunked-prefill workload "
+                      "(T = 32768, gated mix), fp64 token-by-token, one thread",
+            "seconds": dt1,
+            "head_tokens_per_s": Ts * Hs / dt1,
+            "tokens_per_s_at_32_heads": Ts * Hs / dt1 / 32,
+        },
+    }
+
+
+def _median_ms(torch, np, stream, fn, reps, warmup=1):
+    for _ in range(max(1, warmup)):
+        fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    return float(np.median(ts))
+
+
+def _prefill_roofline(head_tokens, n_states, ms, traffic=None):
+    pbytes = PREFILL_BYTES_PER_HEAD_TOKEN * head_tokens + 2 * n_states * D * D * 4
+    pflops = PREFILL_FLOPS_PER_HEAD_TOKEN * head_tokens
+    gbs = pbytes / (ms / 1e3) / 1e9
+    tf = pflops / (ms / 1e3) / 1e12
+    return {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": gbs / HBM_PEAK_GBS, "traffic": traffic, "algorithmic_bytes_per_launch": pbytes,
+            "mfma_algorithmic_tflops": tf, "mfma_frac": tf / BF16_MFMA_PEAK_TFLOPS}
+
+
+def time_decode_large(kda, ki, torch, np, dev, up, stream, H, result, B=256, steps=1024, distinct=64):
+    """The decode at B = 256 (512 MiB of fp32 state, twice the 256 MB
+    last-level cache, so the state stream comes from DRAM): `steps` steps
+    cycling over `distinct` seeded steps of inputs (a few KiB per head and
+    step; the state stream does not depend on their values)."""
+    log(f"generating {distinct} decode steps for B={B} H={H}")
+    inp = ki.decode_steps(11, steps=distinct, N=B, H=H)
+    q, k, v, b = (up(x, True) for x in (inp.q, inp.k, inp.v, inp.beta))
+    la = up(inp.log_alpha, False)
+    state = up(inp.initial_state, False)
+    o = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    del inp
+
+    def run():
+        for s in range(steps):
+            j = s % distinct
+            kda.kda_decode_step(q[j], k[j], v[j], b[j], la[j], state, out=o)
+
+    graph = None
+    try:
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            kda.kda_decode_step(q[0], k[0], v[0], b[0], la[0], state, out=o)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run()
+        torch.cuda.synchronize()
+    except Exception as e:
+        log(f"graph capture failed ({e}); timing direct calls")
+        graph = None
+    fn = graph.replay if graph is not None else run
+    ms = _median_ms(torch, np, stream, fn, reps=3) / steps
+    if not bool(torch.isfinite(state).all()):
+        raise RuntimeError("decode produced non-finite states")
+    nbytes = DECODE_BYTES_PER_HEAD * B * H
+    gbs = nbytes / (ms / 1e3) / 1e9
+    # the streaming ceiling of the same state tensor (read and written once)
+    cms = _median_ms(torch, np, stream, lambda: state.mul_(1.0), reps=16, warmup=4)
+    cgbs = 2 * B * H * D * D * 4 / (cms / 1e3) / 1e9
+    log(f"decode B={B}: {ms * 1e3:.2f} us/step, {B / ms * 1e3 / 1e6:.3f} M tokens/s, {gbs:.0f} GB/s "
+        f"(state read-modify-write ceiling {cgbs:.0f} GB/s)")
+    result["decode_large"] = {
+        "workload": f"the decode workload at B={B} sequences x H={H} heads (fp32 state {B * H * D * D * 4 >> 20} "
+                    f"MiB), {steps} consecutive steps cycling over {distinct} seeded input steps",
+        "ms_per_step": ms,
+        "tokens_per_s": B / (ms / 1e3),
+        "timing": f"median of 3 {'graph replays' if graph is not None else 'runs'} of {steps} steps",
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes},
+        "state_rmw_ceiling": {"what": "torch in-place scale by 1 of the same state tensor", "us": cms * 1e3,
+                              "GBps": cgbs, "decode_frac_of_ceiling": gbs / cgbs},
+    }
+    del q, k, v, b, la, state, o, graph
+
+
+def time_prefill_million(kda, ki, torch, np, dev, up, stream, H, result, T=1 << 20, reps=5):
+    """The million-token prefill: B = 1, H = 32, T = 1,048,576, bf16 inputs,
+    the gated channel mix, zero initial state (the parity-tested inputs)."""
+    log(f"generating million-token prefill inputs B=1 H={H} T={T}")
+    t0 = time.time()
+    inp = ki.workload_million(T=T, H=H)
+    q, k, v, b = (up(x, True) for x in (inp.q, inp.k, inp.v, inp.beta))
+    la = up(inp.log_alpha, False)
+    del inp
+    log(f"generated and uploaded in {time.time() - t0:.0f}s")
+    o = torch.empty((1, T, H, D), dtype=torch.float32, device=dev)
+    st = torch.empty((1, H, D, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, kda.prefill_workspace_size(1, T, H, torch.bfloat16)), dtype=torch.uint8, device=dev)
+    ms = _median_ms(torch, np, stream,
+                    lambda: kda.kda_prefill(q, k, v, b, la, None, out=o, final_state=st, workspace=ws),
+                    reps=reps, warmup=2)
+    if not bool(torch.isfinite(st).all()):
+        raise RuntimeError("million-token prefill produced non-finite states")
+    roof = _prefill_roofline(T * H, H, ms)
+    log(f"prefill T={T}: {ms:.2f} ms, {T / ms * 1e3 / 1e6:.2f} M tokens/s, {roof['achieved']:.0f} GB/s")
+    result["prefill_million"] = {
+        "workload": f"million-token KDA prefill: B=1, H={H}, T={T}, d_k=d_v=128, bf16 q/k/v/beta, fp32 "
+                    "log_alpha/state/o, gated channel mix (10% long-memory, 10% fast-forgetting "
+                    "channels per head), zero initial state",
+        "ms": ms,
+        "timing": f"median of {reps} calls, each between two HIP events, after 2 untimed calls",
+        "workspace_bytes": ws.numel(),
+        "tokens_per_s": T / (ms / 1e3),
+        "head_tokens_per_s": T * H / (ms / 1e3),
+        "roofline": roof,
+    }
+    del q, k, v, b, la, o, st, ws
+
+
+def time_prefill_varlen(kda, ki, torch, np, dev, up, stream, H, result, reps=10):
+    """The packed prefill: 16 sequences, lengths log-uniform in [1024, 65536]
+    (seeded), even-indexed ones resumed from N(0, 0.02^2) states."""
+    inp = ki.workload_varlen(H=H)
+    cu = inp.cu_seqlens
+    N, Tt = cu.size - 1, int(cu[-1])
+    log(f"packed prefill: {N} sequences, {Tt} tokens")
+    q, k, v, b = (up(x, True) for x in (inp.q, inp.k, inp.v, inp.beta))
+    la = up(inp.log_alpha, False)
+    s0 = up(inp.initial_state, False)
+    cud = torch.from_numpy(cu).to(dev)
+    del inp
+    o = torch.empty((1, Tt, H, D), dtype=torch.float32, device=dev)
+    st = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, kda.varlen_prefill_workspace_size(N, Tt, H, torch.bfloat16)), dtype=torch.uint8,
+                     device=dev)
+    ms = _median_ms(torch, np, stream,
+                    lambda: kda.kda_varlen_prefill(q, k, v, b, la, cud, s0, out=o, final_state=st,
+                                                   workspace=ws),
+                    reps=reps, warmup=5)
+    roof = _prefill_roofline(Tt * H, N * H, ms)
+    log(f"packed prefill: {ms:.2f} ms, {Tt / ms * 1e3 / 1e6:.2f} M tokens/s, {roof['achieved']:.0f} GB/s")
+    result["prefill_varlen"] = {
+        "workload": f"packed KDA prefill: {N} sequences of log-uniform lengths in [1024, 65536] "
+                    f"(seeded; {Tt} tokens in all, longest {int(np.max(np.diff(cu)))}), H={H}, bf16 inputs, "
+                    "gated channel mix, even-indexed sequences resumed from N(0, 0.02^2) fp32 states",
+        "ms": ms,
+        "timing": f"median of {reps} calls, each between two HIP events, after 5 untimed calls",
+        "tokens_per_s": Tt / (ms / 1e3),
+        "head_tokens_per_s": Tt * H / (ms / 1e3),
+        "roofline": roof,
+    }
+    del q, k, v, b, la, s0, cud, o, st, ws
+
+
+def time_prefill_small(kda, ki, torch, np, dev, up, stream, result, calls=200):
+    """The small fp32 prefill: B = 1, H = 1, T = 256 (one unit: the token
+    kernel, bound by its 256 dependent steps and the launch)."""
+    inp = ki.workload_single(T=256)
+    q, k, v, b, la = (up(x, False) for x in (inp.q, inp.k, inp.v, inp.beta, inp.log_alpha))
+    o = torch.empty((1, 256, 1, D), dtype=torch.float32, device=dev)
+    st = torch.empty((1, 1, D, D), dtype=torch.float32, device=dev)
+
+    def run():
+        for _ in range(calls):
+            kda.kda_prefill(q, k, v, b, la, None, out=o, final_state=st)
+
+    ms = _median_ms(torch, np, stream, run, reps=3) / calls
+    log(f"small fp32 prefill: {ms * 1e3:.1f} us per call, {256 / ms * 1e3 / 1e6:.2f} M tokens/s")
+    result["prefill_small"] = {
+        "workload": "single-sequence fp32 KDA prefill: B=1, H=1, T=256, d_k=d_v=128, zero initial state",
+        "ms": ms,
+        "timing": f"median of 3 runs of {calls} consecutive calls (direct calls from Python), per call",
+        "tokens_per_s": 256 / (ms / 1e3),
+        "note": "one (sequence, head) unit on one CU: latency of 256 dependent token steps plus the "
+                "launch, not a bandwidth or matrix-core figure",
+    }
 
 
 def time_raw_prefill(kda, torch, np, stream, reps, warmup, pq, pk, pv, pb, pla, po, ps, pms, T, result, pws):
@@ -523,22 +757,31 @@ def time_backward(kda, ki, torch, np, dev, up, stream, reps, result):
             ts.append(a.elapsed_time(e))
         return float(np.median(ts))
 
-    bms = med(lambda: kda.kda_backward(q, k, v, b, la, do, None, ds))
+    ws = torch.empty(kda.backward_workspace_size(B, T, H, torch.bfloat16), dtype=torch.uint8, device=dev)
+    bms = med(lambda: kda.kda_backward(q, k, v, b, la, do, None, ds, workspace=ws))
     fms = med(lambda: kda.kda_prefill(q, k, v, b, la, None))
+    nbytes = BACKWARD_BYTES_PER_HEAD_TOKEN * B * T * H
     flops = BACKWARD_FLOPS_PER_HEAD_TOKEN * B * T * H
+    gbs = nbytes / (bms / 1e3) / 1e9
     tf = flops / (bms / 1e3) / 1e12
-    log(f"backward: {bms:.2f} ms ({B * T * H / bms / 1e3:.1f} M head-tokens/s, {tf:.1f} TFLOP/s); "
-        f"forward on the same inputs {fms:.2f} ms")
+    log(f"backward: {bms:.2f} ms ({B * T * H / bms / 1e3:.1f} M head-tokens/s, {gbs:.0f} GB/s, "
+        f"{tf:.1f} TFLOP/s); forward on the same inputs {fms:.2f} ms")
     result["backward"] = {
         "workload": f"gradients of a prefill: B={B} x T={T} tokens, H={H}, bf16 q/k/v/beta, fp32 "
                     "log_alpha/d_o/d_final_state, gated channel mix, zero initial state",
         "ms": bms,
+        "timing": f"median of {reps} calls, each between two HIP events, after one untimed call; "
+                  "caller-provided workspace",
+        "workspace_bytes": ws.numel(),
         "tokens_per_s": B * T / (bms / 1e3),
         "head_tokens_per_s": B * T * H / (bms / 1e3),
         "forward_ms_same_inputs": fms,
-        "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tf / FP32_VALU_PEAK_TFLOPS, "algorithmic_flops_per_launch": flops,
-                     "note": "fp32 vector arithmetic; recomputation from checkpoints not counted"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes,
+                     "mfma_algorithmic_tflops": tf, "mfma_frac": tf / BF16_MFMA_PEAK_TFLOPS,
+                     "algorithmic_flops_per_launch": flops,
+                     "note": "the chunked backward (five kernels); algorithmic bytes = inputs read "
+                             "and gradients written once; the workspace round trips are not counted"},
     }
     del q, k, v, b, la, do, ds
 
