@@ -58,8 +58,10 @@
 //
 // Decay factors never overflow: in the off-diagonal 16 x 16 blocks (rows r in
 // block R, columns i in an earlier block) 2^(G_r - G_i) is split at the last
-// token of block R - 1 into two factors <= 1; inside the diagonal blocks it is
-// formed pairwise, 2^(G_r - G_i) <= 1.
+// token of block R - 1 into two factors <= 1.  Inside the diagonal blocks the
+// prep kernel forms it pairwise, 2^(G_r - G_i) <= 1; the intra kernel splits it
+// at the block's 8th token where both factors stay within 2^96 and forms it
+// pairwise for the other channels.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
