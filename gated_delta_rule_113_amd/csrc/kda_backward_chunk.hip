@@ -24,15 +24,17 @@
 // 2^(G_r - G_i) = e^(L_r - L_i) with L the cumulative log-decay)
 //     dq_r += sum_{i<=r} dP_ri k_i e^(L_r - L_i),   dk_r += sum_{i<r} dA_ri k_i e^(L_r - L_i)
 //     dk_i += sum_{r>=i} (dP_ri q_r + dA_ri k_r) e^(L_r - L_i)
-//     dL_r = q_r dq_r(P) + k_r dk_r(A rows) - k_r dk_r(columns)
-//           + Qt dQt + Kt dKt - Ke dKe   (+ at the last token: sum_r Ke dKe + gam_L dgam_L)
-// and d log a_j = sum_{r >= j} dL_r within the chunk (L_r = sum_{j <= r} log a_j).
-// For the chunk's first token that sum is taken in closed form: a uniform
-// shift of L over the chunk leaves A, P and Ke unchanged, so
-//     d log a_0 = sum_r (Qt dQt + Kt dKt)_r + gam_L dgam_L,
-// every term of which is proportional to S0 (so it is exactly zero for a
-// sequence that starts from a zero state, where the terms of the plain sum
-// would cancel only up to rounding).
+// The gate's gradient comes from shifting L_r = sum_{j' <= r} log a_j' by the
+// same amount for every r >= j (that is, changing log a_j): Qt_r and Kt_r
+// (r >= j), Ke_r (r < j) and gam_L scale with it, and so do A_ri and P_ri
+// for r >= j > i, so
+//     d log a_j = sum_{r >= j} (Qt dQt + Kt dKt)_r + sum_{r < j} (Ke dKe)_r
+//               + gam_L dgam_L + sum_{r >= j > i} X_ri,
+//     X_ri = (dA_ri k_r + dP_ri q_r) k_i e^(L_r - L_i).
+// Every term carries the decay over token j, so where that decay (or the
+// state entering token j) vanishes, the gradient comes out as small as it
+// is; the equivalent reverse sum over r >= j of the per-row derivatives would
+// leave the rounding residue of terms that cancel.
 //
 // Kernels (one head of one sequence is a "unit"; chunks are numbered per head
 // by the id floor(row0 / 64) + sequence + chunk, unique and below rows / 64 +
@@ -44,8 +46,8 @@
 //   grads  (one per chunk)            dV, the S0/dS1 parts of dq, dk and dL,
 //                                     db's first term, dP and dT;
 //   intra  (one per chunk)            dM, dA, db's second term, the decay
-//                                     products and the chunk's reverse
-//                                     cumulative sum of dL into d log a.
+//                                     products and their cross sums, the
+//                                     A/P part of d log a.
 //
 // Matrix products run on v_mfma_f32_16x16x32_bf16 with every operand split
 // into hi + lo bf16 (hi*hi + hi*lo + lo*hi, fp32 accumulation), as in the
@@ -105,12 +107,11 @@ struct ChunkBwdArgs {
     float* ws_s0;        // [ids][H][128][128]  entering state of every chunk
     float* ws_ds;        // [ids][H][128][128]  gradient in every chunk's leaving state
     float* ws_apt;       // [ids][H][3][64][64] A, P, T
-    float* ws_dpt;       // [ids][H][kDptFloats] dP, dT, last-token dL terms
+    float* ws_dpt;       // [ids][H][kDptFloats] dP, dT
 };
 
-// dP and dT (64 x 64 each), the last-token terms of dL (128) and the
-// first-token d log alpha (128)
-constexpr int kDptFloats = 2 * TSZ + 2 * kDim;
+// dP and dT (64 x 64 each)
+constexpr int kDptFloats = 2 * TSZ;
 
 __device__ __forceinline__ int64_t seq_row0(const ChunkBwdArgs& a, int64_t n)
 {
@@ -427,7 +428,18 @@ __device__ __forceinline__ void tile_image(const float* src, char* img)
 
 // ================================================================ prep
 //
-// A, P and T of one chunk of one head (grid: chunk ids x heads; 256 threads).
+// A, P and T of one chunk of one head (grid: chunk ids x heads; 256 threads,
+// two workgroups per CU).  The ten lower 16 x 16 blocks of A and P run on the
+// matrix cores (2.5 per wave), with 2^(G_r - G_i) split at a reference rho:
+// the last token of block R - 1 for the six off-diagonal blocks (both factors
+// <= 1), the block's 8th token for the four diagonal ones, where a channel is
+// taken this way only if both factors stay within 2^96; the other ("unsafe")
+// channels of a diagonal block are added pairwise on the vector ALUs.  Then
+// T = (I + B A)^-1: its diagonal blocks by forward substitution (one wave per
+// block, lane = (column, row quarter), quad sums over the lanes of a column),
+// its off-diagonal blocks as T_RI = -T_RR sum_{I <= J < R} N_RJ T_JI in order
+// of R - I (N = B A).  G, k and q live in LDS only until the A/P products are
+// done; A, P and T then take their place.
 
 constexpr int PREP_NT = 256;
 constexpr int GLD = 132;     // fp32 row stride of the G tile
@@ -441,15 +453,31 @@ __device__ __forceinline__ void offdiag_block(int p, int& R, int& I)
     I = p - (R * (R - 1)) / 2;
 }
 
-__global__ __launch_bounds__(PREP_NT) void chunk_prep_kernel(const ChunkBwdArgs a)
+// x plus x from the lane that differs in lane bit 0 (XOR1) or bit 1 (XOR2).
+template <int CTRL>
+__device__ __forceinline__ float quad_add(float x)
 {
-    __shared__ __attribute__((aligned(16))) float Gs[CH * GLD];
-    __shared__ __attribute__((aligned(16))) __bf16 Ks[CH * BLD];
-    __shared__ __attribute__((aligned(16))) __bf16 Qs[CH * BLD];
-    __shared__ float As[CH * TLD], Ps[CH * TLD], Ts[CH * TLD];
-    __shared__ float Ys[3 * 256];
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E;
+
+__global__ __launch_bounds__(PREP_NT, 2) void chunk_prep_kernel(const ChunkBwdArgs a)
+{
+    // phase 1: G | k | q;  phase 2 (the same bytes): A | P | T | Y
+    constexpr int OFF_G = 0, OFF_K = CH * GLD * 4, OFF_Q = OFF_K + CH * BLD * 2, P1 = OFF_Q + CH * BLD * 2;
+    constexpr int OFF_A = 0, OFF_P = CH * TLD * 4, OFF_T = 2 * CH * TLD * 4, OFF_Y = 3 * CH * TLD * 4,
+                  P2 = OFF_Y + 3 * 256 * 4;
+    __shared__ __attribute__((aligned(16))) char sm[P1 > P2 ? P1 : P2];
     __shared__ float bs[CH];
     __shared__ float tot[(PREP_NT / 64) * kDim];
+    __shared__ unsigned char unsafe_ch[4][kDim];   // per diagonal block and channel
+    float* Gs = reinterpret_cast<float*>(sm + OFF_G);
+    __bf16* Ks = reinterpret_cast<__bf16*>(sm + OFF_K);
+    __bf16* Qs = reinterpret_cast<__bf16*>(sm + OFF_Q);
+    float* As = reinterpret_cast<float*>(sm + OFF_A);
+    float* Ps = reinterpret_cast<float*>(sm + OFF_P);
+    float* Ts = reinterpret_cast<float*>(sm + OFF_T);
+    float* Ys = reinterpret_cast<float*>(sm + OFF_Y);
 
     const int H = a.H;
     const int64_t id = blockIdx.x / H;
@@ -458,28 +486,45 @@ __global__ __launch_bounds__(PREP_NT) void chunk_prep_kernel(const ChunkBwdArgs 
     if (!locate(a, id, n, c)) return;
     const int64_t row0c = seq_row0(a, n) + c * CH;
     const int L = static_cast<int>(min<int64_t>(CH, seq_len(a, n) - c * CH));
-    const int t = threadIdx.x, lane = t & 63, wave = wave_id();
+    const int t = threadIdx.x, lane = t & 63, wave = wave_id(), g = lane >> 4, l16 = lane & 15;
 
-    Staged<PREP_NT> st;
-    stage<PREP_NT, true>(a, row0c, L, h, tot, st);
-    stage_beta(a, row0c, L, h, bs);
+    {
+        Staged<PREP_NT> st;
+        stage<PREP_NT, true>(a, row0c, L, h, tot, st);
+        stage_beta(a, row0c, L, h, bs);
 #pragma unroll
-    for (int j = 0; j < Staged<PREP_NT>::TOK; ++j) {
-        const int r = st.r0 + j;
-        *reinterpret_cast<float2*>(&Gs[r * GLD + st.c0]) = make_float2(st.g[j][0], st.g[j][1]);
-        *reinterpret_cast<bf16x2*>(&Ks[r * BLD + st.c0]) = (bf16x2){(__bf16)st.kk[j][0], (__bf16)st.kk[j][1]};
-        *reinterpret_cast<bf16x2*>(&Qs[r * BLD + st.c0]) = (bf16x2){(__bf16)st.qq[j][0], (__bf16)st.qq[j][1]};
+        for (int j = 0; j < Staged<PREP_NT>::TOK; ++j) {
+            const int r = st.r0 + j;
+            *reinterpret_cast<float2*>(&Gs[r * GLD + st.c0]) = make_float2(st.g[j][0], st.g[j][1]);
+            *reinterpret_cast<bf16x2*>(&Ks[r * BLD + st.c0]) = (bf16x2){(__bf16)st.kk[j][0], (__bf16)st.kk[j][1]};
+            *reinterpret_cast<bf16x2*>(&Qs[r * BLD + st.c0]) = (bf16x2){(__bf16)st.qq[j][0], (__bf16)st.qq[j][1]};
+        }
+    }
+    lds_sync();
+    if (t < kDim) {
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+            const float g0 = Gs[(16 * R) * GLD + t], gm = Gs[(16 * R + 7) * GLD + t],
+                        g1 = Gs[(16 * R + 15) * GLD + t];
+            unsafe_ch[R][t] = (g0 - gm > 96.f || gm - g1 > 96.f) ? 1 : 0;
+        }
     }
     lds_sync();
 
-    // ---- off-diagonal blocks on the matrix cores: rows r of block R carry
-    // 2^(G_r - rho), columns i of block I < R carry 2^(rho - G_i), with rho =
-    // G at the last token of block R - 1 (both factors <= 1).
-    for (int p = wave; p < 6; p += PREP_NT / 64) {
-        int R, I;
-        offdiag_block(p, R, I);
-        const int rr = 16 * R + (lane & 15), ii = 16 * I + (lane & 15), g = lane >> 4;
-        f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accP = accA;
+    // ---- A and P: block p = wave + 4 j; p < 4 the diagonal block p, else
+    // the off-diagonal block p - 4.  Accumulators stay in registers until
+    // every wave is done with G, k and q.
+    f32x4 accA[3], accP[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        accA[j] = accP[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        const int p = wave + 4 * j;
+        if (p >= 10) break;
+        int R = p, I = p;
+        if (p >= 4) offdiag_block(p - 4, R, I);
+        const bool diag = R == I;
+        const int rr = 16 * R + l16, ii = 16 * I + l16;
+        const int rho_row = diag ? 16 * R + 7 : 16 * R - 1;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int cc = 32 * s + 8 * g;
@@ -487,83 +532,85 @@ __global__ __launch_bounds__(PREP_NT) void chunk_prep_kernel(const ChunkBwdArgs 
             const bf16x8 kr = *reinterpret_cast<const bf16x8*>(&Ks[rr * BLD + cc]);
             const bf16x8 qr = *reinterpret_cast<const bf16x8*>(&Qs[rr * BLD + cc]);
             const bf16x8 ki = *reinterpret_cast<const bf16x8*>(&Ks[ii * BLD + cc]);
+            const uint2 us = *reinterpret_cast<const uint2*>(&unsafe_ch[R][cc]);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float rho = Gs[(16 * R - 1) * GLD + cc + j];
-                const float fr = ex2(Gs[rr * GLD + cc + j] - rho);
-                fk[j] = (float)kr[j] * fr;
-                fq[j] = (float)qr[j] * fr;
-                fh[j] = (float)ki[j] * ex2(rho - Gs[ii * GLD + cc + j]);
+            for (int jj = 0; jj < 8; ++jj) {
+                const bool ok = !diag || (((jj < 4 ? us.x : us.y) >> (8 * (jj & 3))) & 0xffu) == 0;
+                const float rho = Gs[rho_row * GLD + cc + jj];
+                const float fr = ok ? ex2(Gs[rr * GLD + cc + jj] - rho) : 0.f;
+                fk[jj] = (float)kr[jj] * fr;
+                fq[jj] = (float)qr[jj] * fr;
+                fh[jj] = ok ? (float)ki[jj] * ex2(rho - Gs[ii * GLD + cc + jj]) : 0.f;
             }
             bf16x8 kh, kl, qh, ql, hh, hl;
             split8(fk, kh, kl);
             split8(fq, qh, ql);
             split8(fh, hh, hl);
-            accA = mma3(kh, kl, hh, hl, accA);
-            accP = mma3(qh, ql, hh, hl, accP);
+            accA[j] = mma3(kh, kl, hh, hl, accA[j]);
+            accP[j] = mma3(qh, ql, hh, hl, accP[j]);
         }
+        if (diag) {
+            // the unsafe channels of this diagonal block, pairwise (i <= r)
+            const bool any = __any(unsafe_ch[R][lane] | unsafe_ch[R][lane + 64]);
+            if (any) {
+                for (int ch = 0; ch < kDim; ++ch) {
+                    if (!unsafe_ch[R][ch]) continue;   // the same for every lane
+                    const int i = 16 * R + l16;
+                    const float gi = Gs[i * GLD + ch], ki = (float)Ks[i * BLD + ch];
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        const int r = 16 * R + 4 * g + x;
+                        if (i <= r) {
+                            const float e = ki * ex2(Gs[r * GLD + ch] - gi);
+                            accA[j][x] += (float)Ks[r * BLD + ch] * e;
+                            accP[j][x] += (float)Qs[r * BLD + ch] * e;
+                        }
+                    }
+                }
+            }
+        }
+    }
+    lds_sync();   // G, k and q are dead: A, P and T take their bytes
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int p = wave + 4 * j;
+        if (p >= 10) break;
+        int R = p, I = p;
+        if (p >= 4) offdiag_block(p - 4, R, I);
+        const int i = 16 * I + l16;
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
             const int r = 16 * R + 4 * g + x;
-            As[r * TLD + ii] = accA[x];
-            Ps[r * TLD + ii] = accP[x];
-        }
-    }
-
-    // ---- diagonal blocks, pairwise: lane (i, channel quarter) of wave R
-    // sums over its 32 channels for every row r of the block, then over the
-    // four quarters.
-    for (int R = wave; R < 4; R += PREP_NT / 64) {
-        const int iloc = lane & 15, cq = lane >> 4;
-        const int i = 16 * R + iloc;
-        float gi[32], ki[32];
-#pragma unroll
-        for (int j = 0; j < 32; ++j) {
-            gi[j] = Gs[i * GLD + 32 * cq + j];
-            ki[j] = (float)Ks[i * BLD + 32 * cq + j];
-        }
-        for (int rl = 0; rl < 16; ++rl) {
-            const int r = 16 * R + rl;
-            float sa = 0.f, sp = 0.f;
-#pragma unroll
-            for (int j = 0; j < 32; ++j) {
-                const int cc = 32 * cq + j;
-                const float e = ex2(fminf(Gs[r * GLD + cc] - gi[j], 0.f));
-                const float ke = ki[j] * e;
-                sa += (float)Ks[r * BLD + cc] * ke;
-                sp += (float)Qs[r * BLD + cc] * ke;
-            }
-            sa += __shfl_xor(sa, 16);
-            sa += __shfl_xor(sa, 32);
-            sp += __shfl_xor(sp, 16);
-            sp += __shfl_xor(sp, 32);
-            if (cq == 0) {
-                As[r * TLD + i] = rl > iloc ? sa : 0.f;
-                Ps[r * TLD + i] = rl >= iloc ? sp : 0.f;
-            }
+            As[r * TLD + i] = i < r ? accA[j][x] : 0.f;
+            Ps[r * TLD + i] = i <= r ? accP[j][x] : 0.f;
         }
     }
     lds_sync();
 
-    // ---- T = (I + Diag(beta) A)^-1, unit lower triangular, by 16 x 16 blocks:
-    // the diagonal blocks by forward substitution (lane = column), then
-    // T_RI = -T_RR sum_{I <= J < R} N_RJ T_JI in order of R - I (N = Diag(beta) A).
-    if (lane < 16) {
-        const int R = wave, j = lane;
-        float x[16];
+    // ---- T = (I + N)^-1, N = B A (strictly lower).  Diagonal block R on wave
+    // R: lane (jc, p) holds rows 4p..4p+3 of column jc of T_RR.
+    {
+        const int R = wave, jc = lane >> 2, pq = lane & 3;
+        float4 nv[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float acc = r == j ? 1.f : 0.f;
-            if (r > j) {
-                const int gr = 16 * R + r;
+        for (int rr = 0; rr < 16; ++rr) {
+            const int r = 16 * R + rr;
+            const float br = bs[r];
+            const float* ar = &As[r * TLD + 16 * R + 4 * pq];
+            nv[rr] = make_float4(br * ar[0], br * ar[1], br * ar[2], br * ar[3]);
+        }
+        float tv[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int m = 0; m < 16; ++m)
-                    if (m < r) acc -= bs[gr] * As[gr * TLD + 16 * R + m] * x[m];
-            }
-            x[r] = acc;
+        for (int rr = 0; rr < 16; ++rr) {
+            // N is strictly lower and the rows of T not yet solved are zero
+            float sum = nv[rr].x * tv[0] + nv[rr].y * tv[1] + nv[rr].z * tv[2] + nv[rr].w * tv[3];
+            sum = quad_add<kQuadXor1>(sum);
+            sum = quad_add<kQuadXor2>(sum);
+            const float tr = (rr == jc ? 1.f : 0.f) - sum;
+            if (pq == (rr >> 2)) tv[rr & 3] = tr;
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) Ts[(16 * R + r) * TLD + 16 * R + j] = x[r];
+        for (int m = 0; m < 4; ++m) Ts[(16 * R + 4 * pq + m) * TLD + 16 * R + jc] = tv[m];
     }
     lds_sync();
     for (int d = 1; d < 4; ++d) {
@@ -575,8 +622,8 @@ __global__ __launch_bounds__(PREP_NT) void chunk_prep_kernel(const ChunkBwdArgs 
             for (int J = I; J < R; ++J)
 #pragma unroll
                 for (int m = 0; m < 16; ++m)
-                    y += bs[r] * As[r * TLD + 16 * J + m] * Ts[(16 * J + m) * TLD + 16 * I + il];
-            Ys[(R - d) * 256 + rl * 16 + il] = y;
+                    y += As[r * TLD + 16 * J + m] * Ts[(16 * J + m) * TLD + 16 * I + il];
+            Ys[(R - d) * 256 + rl * 16 + il] = bs[r] * y;
         }
         lds_sync();
         for (int R = d; R < 4; ++R) {
@@ -591,11 +638,22 @@ __global__ __launch_bounds__(PREP_NT) void chunk_prep_kernel(const ChunkBwdArgs 
 
     // ---- out: A (i < r), P (i <= r), T (i < r, unit diagonal), zeros elsewhere
     float* dst = a.ws_apt + (id * H + h) * (3 * TSZ);
-    for (int e = t; e < TSZ; e += PREP_NT) {
-        const int r = e >> 6, i = e & 63;
-        dst[e] = i < r ? As[r * TLD + i] : 0.f;
-        dst[TSZ + e] = i <= r ? Ps[r * TLD + i] : 0.f;
-        dst[2 * TSZ + e] = i < r ? Ts[r * TLD + i] : (i == r ? 1.f : 0.f);
+    for (int e = 4 * t; e < TSZ; e += 4 * PREP_NT) {
+        const int r = e >> 6, i0 = e & 63;
+        float4 va, vp, vt;
+        float* pa = &va.x;
+        float* pp = &vp.x;
+        float* pt = &vt.x;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = i0 + u;
+            pa[u] = i < r ? As[r * TLD + i] : 0.f;
+            pp[u] = i <= r ? Ps[r * TLD + i] : 0.f;
+            pt[u] = i < r ? Ts[r * TLD + i] : (i == r ? 1.f : 0.f);
+        }
+        *reinterpret_cast<float4*>(dst + e) = va;
+        *reinterpret_cast<float4*>(dst + TSZ + e) = vp;
+        *reinterpret_cast<float4*>(dst + 2 * TSZ + e) = vt;
     }
 }
 
@@ -928,9 +986,8 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_dstate_kernel(const ChunkBwdA
 // from LDS images of dO, -B dW' and U and the rows of S0 and dS1 read from
 // the workspaces as B operands):
 //   dQt = dO S0^T, dKt = -B dW' S0^T, dKe = U dS1^T, dgam_L = rowsum(dS1 (.) S0);
-//   writes dq = dQt gam, dk = dKt gam + dKe gam_L / gam and
-//   dL = Qt dQt + Kt dKt - Ke dKe (the intra kernel adds the rest), and the
-//   last-token terms sum_r Ke dKe + gam_L dgam_L; dP = dO U^T (lower blocks).
+//   writes dq = dQt gam, dk = dKt gam + dKe gam_L / gam and the S0 part of
+//   d log a (the intra kernel adds the cross sums); dP = dO U^T (lower blocks).
 // Phase C: dT = dU (B W)^T (lower blocks) from images of dU and B W.
 
 __global__ __launch_bounds__(SEQ_NT, 1) void chunk_grads_kernel(const ChunkBwdArgs a)
@@ -1153,8 +1210,8 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_grads_kernel(const ChunkBwdAr
             dg += __shfl_xor(dg, 32);
         }
         const float gLc = gLs[cw];
-        float keke = 0.f;  // sum over the rows of Ke dKe for channel cw
-        float first = 0.f;  // sum over the rows of Qt dQt + Kt dKt
+        // per row: Qt dQt + Kt dKt (av) and Ke dKe (bv), channel cw
+        float av[4][4], bv[4][4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             f32x4 dQt = {0.f, 0.f, 0.f, 0.f}, dKt = dQt, dKe = dQt;
@@ -1171,6 +1228,7 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_grads_kernel(const ChunkBwdAr
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 const int r = 16 * m + 4 * g + x;
+                av[m][x] = bv[m][x] = 0.f;
                 if (r < L) {
                     const int64_t e = ((row0c + r) * H + h) * kDim + cw;
                     const float G = Gs[r * GLD + cw];
@@ -1180,19 +1238,56 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_grads_kernel(const ChunkBwdAr
                     const float dkt = dKt[x] * gam, dke = dKe[x] * ge;
                     a.dq[e] = dq;
                     a.dk[e] = dkt + dke;
-                    a.dla[e] = q1 * dq + k1 * dkt - k1 * dke;
-                    keke += k1 * dke;
-                    first += q1 * dq + k1 * dkt;
+                    av[m][x] = q1 * dq + k1 * dkt;
+                    bv[m][x] = k1 * dke;
                 }
             }
         }
-        keke += __shfl_xor(keke, 16);
-        keke += __shfl_xor(keke, 32);
-        first += __shfl_xor(first, 16);
-        first += __shfl_xor(first, 32);
-        if (g == 0) {
-            dpt[2 * TSZ + cw] = keke + ex2(gLc) * dg;
-            dpt[2 * TSZ + kDim + cw] = first + ex2(gLc) * dg;
+        // The S0 part of d log a_j: sum_{r >= j} av_r + sum_{r < j} bv_r +
+        // gam_L dgam_L (suffix and prefix sums over the chunk's rows, held
+        // by the four lane groups g in blocks of 16: each term is as small as
+        // the decay it carries, with no cancellation between partial sums).
+        float pre_prev = 0.f;   // bv over the blocks before m
+        float sa_blk[4], sb_blk[4], sa_lane[4][4], sb_lane[4][4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float la_ = av[m][0] + av[m][1] + av[m][2] + av[m][3];
+            const float lb_ = bv[m][0] + bv[m][1] + bv[m][2] + bv[m][3];
+            sa_blk[m] = sb_blk[m] = 0.f;
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+                sa_lane[m][gg] = __shfl(la_, l16 + 16 * gg);
+                sb_lane[m][gg] = __shfl(lb_, l16 + 16 * gg);
+                sa_blk[m] += sa_lane[m][gg];
+                sb_blk[m] += sb_lane[m][gg];
+            }
+        }
+        const float glast = ex2(gLc) * dg;
+        float after[4];
+        after[3] = 0.f;
+#pragma unroll
+        for (int m = 2; m >= 0; --m) after[m] = after[m + 1] + sa_blk[m + 1];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            float sa = after[m], sb = pre_prev;
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+                if (gg > g) sa += sa_lane[m][gg];
+                if (gg < g) sb += sb_lane[m][gg];
+            }
+            // within this lane's four rows: suffix of av from x, prefix of bv before x
+            float suf[4];
+            suf[3] = sa + av[m][3];
+#pragma unroll
+            for (int x = 2; x >= 0; --x) suf[x] = suf[x + 1] + av[m][x];
+            float run_b = sb;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int r = 16 * m + 4 * g + x;
+                if (r < L) a.dla[((row0c + r) * H + h) * kDim + cw] = suf[x] + run_b + glast;
+                run_b += bv[m][x];
+            }
+            pre_prev += sb_blk[m];
         }
     }
     // dP = dO U^T on the 10 lower 16 x 16 blocks (2 per wave for waves 0, 1)
@@ -1305,6 +1400,7 @@ __global__ __launch_bounds__(INTRA_NT, 1) void chunk_intra_kernel(const ChunkBwd
     __shared__ __attribute__((aligned(16))) __bf16 Ks[CH * kDim];
     __shared__ __attribute__((aligned(16))) __bf16 Qs[CH * kDim];
     __shared__ float bs[CH], db2[CH], tot[(INTRA_NT / 64) * kDim];
+    __shared__ float DgS[16 * INTRA_NT];   // per thread: the cross sums inside the diagonal blocks
     static_assert(CH * kDim <= 2 * CH * PLD, "G fits where T and A were");
     float* Ts = U1;
     float* As = U1 + CH * PLD;
@@ -1403,11 +1499,101 @@ __global__ __launch_bounds__(INTRA_NT, 1) void chunk_intra_kernel(const ChunkBwd
     auto Gv = [&](int r) { return Gs[r * kDim + cc]; };
     auto Kv = [&](int r) { return (float)Ks[r * kDim + cc]; };
     auto Qv = [&](int r) { return (float)Qs[r * kDim + cc]; };
-    f32x4 dq[4], dkr[4], dkc[4];
+    const int64_t rs = static_cast<int64_t>(H) * kDim;
+    const int64_t e0 = (row0c * H + h) * kDim + cc;
+    // The cross sums C_j = sum_{r >= j > i} X_ri of the decay products
+    // X_ri = (dA_ri k_r + dP_ri q_r) k_i 2^(G_r - G_i) (this lane's channel)
+    // are the A/P part of d log a_j.  By blocks, for j in block J: Ab[J] the
+    // blocks entirely after and before J, Bc[J] the column sums over the row
+    // blocks after J (columns in J), the row sums over the column blocks
+    // before J (rows in J), and the pairs inside J (explicit).  Every term
+    // carries the decay over token j.  Row blocks run last to first, so that
+    // a block's dk column sums, Bc and Ab are complete when it is written.
+    // The pairs inside each diagonal block first (their cross sums, per row,
+    // into DgS): X_ri for rows r = 16R + 4g + x and the columns i < r of the
+    // block; c[j] gathers, over this lane's rows r >= j, the row sums over i < j.
+#pragma unroll 1
+    for (int R = 0; R < 4; ++R) {
+        const float rho = Gv(16 * R + 7);
+        const bool safe = Gv(16 * R) - rho <= 96.f && rho - Gv(16 * R + 15) <= 96.f;
+        float kh[4], qf[4], kf[4];
 #pragma unroll
-    for (int R = 0; R < 4; ++R) dq[R] = dkr[R] = dkc[R] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int x = 0; x < 4; ++x) {
+            const int r = 16 * R + 4 * g + x;   // also the column index of kh
+            const float f = safe ? ex2(Gv(r) - rho) : 0.f;
+            kh[x] = safe ? Kv(r) * ex2(rho - Gv(r)) : 0.f;
+            qf[x] = Qv(r) * f;
+            kf[x] = Kv(r) * f;
+        }
+        float khall[16];
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+            for (int xx = 0; xx < 4; ++xx) khall[4 * gg + xx] = __shfl(kh[xx], l16 + 16 * gg);
+        float c[16];
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) c[jj] = 0.f;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int rl = 4 * g + x;   // the row within the block
+            const int r = 16 * R + rl;
+            float run = 0.f;
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const float4 da = *reinterpret_cast<const float4*>(&Ad[r * PLD + 16 * R + 4 * i4]);
+                const float4 dp = *reinterpret_cast<const float4*>(&Pd[r * PLD + 16 * R + 4 * i4]);
+                const float dav[4] = {da.x, da.y, da.z, da.w};
+                const float dpv[4] = {dp.x, dp.y, dp.z, dp.w};
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int il = 4 * i4 + u;
+                    // (zero for an unsafe channel: kf, qf and kh are)
+                    const float xv = (dav[u] * kf[x] + dpv[u] * qf[x]) * khall[il];
+                    run += il < rl ? xv : 0.f;
+                    if (il + 1 < 16 && il + 1 <= rl) c[il + 1] += run;
+                }
+            }
+        }
+        if (__any(!safe)) {
+            // the unsafe channels' pairs, with pairwise factors
+            if (!safe) {
+                for (int x = 0; x < 4; ++x) {
+                    const int rl = 4 * g + x;
+                    const int r = 16 * R + rl;
+                    const float gr = Gv(r), kr = Kv(r), qr = Qv(r);
+                    float run = 0.f;
+#pragma unroll
+                    for (int il = 0; il + 1 < 16; ++il) {
+                        if (il < rl) {
+                            const int i = 16 * R + il;
+                            run += (Ad[r * PLD + i] * kr + Pd[r * PLD + i] * qr) * Kv(i) * ex2(gr - Gv(i));
+                        }
+                        if (il + 1 <= rl) c[il + 1] += run;
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int jj = 1; jj < 16; ++jj) {
+            c[jj] += __shfl_xor(c[jj], 16);
+            c[jj] += __shfl_xor(c[jj], 32);
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+            DgS[(4 * R + x) * INTRA_NT + t] = g == 0 ? c[x] : g == 1 ? c[4 + x] : g == 2 ? c[8 + x] : c[12 + x];
+    }
+
+    f32x4 dkc[4];
+    float Bc[4][4], Ab[4];
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
+        dkc[R] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        Ab[R] = 0.f;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) Bc[R][x] = 0.f;
+    }
+#pragma unroll
+    for (int R = 3; R >= 0; --R) {
         float gR[4], kR[4], qR[4];
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
@@ -1415,17 +1601,32 @@ __global__ __launch_bounds__(INTRA_NT, 1) void chunk_intra_kernel(const ChunkBwd
             kR[x] = Kv(16 * R + 4 * g + x);
             qR[x] = Qv(16 * R + 4 * g + x);
         }
+        f32x4 dqR = {0.f, 0.f, 0.f, 0.f}, dkrR = dqR;
+        float Cr[4] = {0.f, 0.f, 0.f, 0.f};
+        float pq[4], pk[4], pl[4];
 #pragma unroll
         for (int I = 0; I <= R; ++I) {
+            if (I == R) {
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const int r = 16 * R + 4 * g + x;
+                    const bool in = r < L;
+                    const int64_t e = e0 + (in ? r : 0) * rs;
+                    pq[x] = in ? a.dq[e] : 0.f;
+                    pk[x] = in ? a.dk[e] : 0.f;
+                    pl[x] = in ? a.dla[e] : 0.f;
+                }
+            }
             const float rho = I < R ? Gv(16 * R - 1) : Gv(16 * R + 7);
             const bool safe = I < R || (Gv(16 * R) - rho <= 96.f && rho - Gv(16 * R + 15) <= 96.f);
-            float f[4], hh[4], kh[4], qf[4], kf[4];
+            float f[4], hh[4], kI[4], kh[4], qf[4], kf[4];
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 const int i = 16 * I + 4 * g + x;
                 f[x] = safe ? ex2(gR[x] - rho) : 0.f;
                 hh[x] = safe ? ex2(rho - Gv(i)) : 0.f;
-                kh[x] = Kv(i) * hh[x];
+                kI[x] = Kv(i);
+                kh[x] = kI[x] * hh[x];
                 qf[x] = qR[x] * f[x];
                 kf[x] = kR[x] * f[x];
             }
@@ -1456,98 +1657,88 @@ __global__ __launch_bounds__(INTRA_NT, 1) void chunk_intra_kernel(const ChunkBwd
             sc = mma16(cah, cal, bfh, bfl, sc);
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
-                dq[R][x] += f[x] * sq[x];
-                dkr[R][x] += f[x] * sk[x];
+                dqR[x] += f[x] * sq[x];
+                dkrR[x] += f[x] * sk[x];
                 dkc[I][x] += hh[x] * sc[x];
             }
-            if (I == R && __any(!safe)) {
-                // pairwise on the vector ALUs for the unsafe channels
-                if (!safe) {
+            if (I < R) {
+                // an off-diagonal block: its row sums (rows in R), column sums
+                // (columns in I) and, when some block J lies between, its total
+                float tsum = 0.f;
 #pragma unroll
-                    for (int x = 0; x < 4; ++x) {
-                        const int r = 16 * R + 4 * g + x;
-                        float aq = 0.f, ak = 0.f, acc = 0.f;
-                        for (int i = 16 * R; i <= r; ++i) {
-                            const float kie = Kv(i) * ex2(gR[x] - Gv(i));
-                            aq += Pd[r * PLD + i] * kie;
-                            ak += Ad[r * PLD + i] * kie;
+                for (int x = 0; x < 4; ++x) {
+                    const float rx = f[x] * (qR[x] * sq[x] + kR[x] * sk[x]);
+                    Cr[x] += rx;
+                    tsum += rx;
+                    Bc[I][x] += kI[x] * hh[x] * sc[x];
+                }
+                if (I + 1 < R) {
+                    tsum += __shfl_xor(tsum, 16);
+                    tsum += __shfl_xor(tsum, 32);
+#pragma unroll
+                    for (int J = I + 1; J < R; ++J) Ab[J] += tsum;
+                }
+            } else {
+                if (__any(!safe)) {
+                    // pairwise on the vector ALUs for the unsafe channels
+                    if (!safe) {
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) {
+                            const int r = 16 * R + 4 * g + x;
+                            float aq = 0.f, ak = 0.f, acc = 0.f;
+                            for (int i = 16 * R; i <= r; ++i) {
+                                const float kie = Kv(i) * ex2(gR[x] - Gv(i));
+                                aq += Pd[r * PLD + i] * kie;
+                                ak += Ad[r * PLD + i] * kie;
+                            }
+                            const float gi = gR[x];  // row r as the column index i
+                            for (int rr = r; rr < 16 * R + 16; ++rr)
+                                acc += (Pd[rr * PLD + r] * Qv(rr) + Ad[rr * PLD + r] * Kv(rr)) * ex2(Gv(rr) - gi);
+                            dqR[x] += aq;
+                            dkrR[x] += ak;
+                            dkc[R][x] += acc;
                         }
-                        const float gi = gR[x];  // row r as the column index i
-                        for (int rr = r; rr < 16 * R + 16; ++rr)
-                            acc += (Pd[rr * PLD + r] * Qv(rr) + Ad[rr * PLD + r] * Kv(rr)) * ex2(Gv(rr) - gi);
-                        dq[R][x] += aq;
-                        dkr[R][x] += ak;
-                        dkc[R][x] += acc;
                     }
                 }
             }
         }
-    }
 
-    // ---- totals and the reverse cumulative sum of dL over the chunk's rows
-    // the grads kernel's terms of dq, dk and dL for this lane's rows: every
-    // load is issued before any store, so they share one memory round trip
-    const int64_t rs = static_cast<int64_t>(H) * kDim;
-    const int64_t e0 = (row0c * H + h) * kDim + cc;
-    float pq[4][4], pk[4][4], pl[4][4];
-#pragma unroll
-    for (int R = 0; R < 4; ++R)
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int r = 16 * R + 4 * g + x;
-            const bool in = r < L;
-            const int64_t e = e0 + (in ? r : 0) * rs;
-            pq[R][x] = in ? a.dq[e] : 0.f;
-            pk[R][x] = in ? a.dk[e] : 0.f;
-            pl[R][x] = in ? a.dla[e] : 0.f;
-        }
-    const float last = a.ws_dpt[wslot * kDptFloats + 2 * TSZ + cc];
-    const float first = a.ws_dpt[wslot * kDptFloats + 2 * TSZ + kDim + cc];
-    float dl[4][4], part[4];
-#pragma unroll
-    for (int R = 0; R < 4; ++R) {
-        part[R] = 0.f;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int r = 16 * R + 4 * g + x;
-            dl[R][x] = 0.f;
-            if (r < L) {
-                const float kv = Kv(r), qv = Qv(r);
-                const int64_t e = e0 + r * rs;
-                a.dq[e] = pq[R][x] + dq[R][x];
-                a.dk[e] = pk[R][x] + dkr[R][x] + dkc[R][x];
-                dl[R][x] = pl[R][x] + qv * dq[R][x] + kv * dkr[R][x] - kv * dkc[R][x] +
-                           (r == L - 1 ? last : 0.f);
-            }
-            part[R] += dl[R][x];
-        }
-    }
-    float carry = 0.f;   // sum of dL over the blocks after R
-#pragma unroll
-    for (int R = 3; R >= 0; --R) {
-        float above = 0.f, block = 0.f;   // later lane groups of this block; the whole block
+        // ---- block R is complete: dq, dk and d log a of its rows, added to
+        // the grads kernel's terms (requested before the diagonal block)
+        const float bl = Bc[R][0] + Bc[R][1] + Bc[R][2] + Bc[R][3];
+        const float cl = Cr[0] + Cr[1] + Cr[2] + Cr[3];
+        float bpre = 0.f, csuf = 0.f;   // over the lane groups before / after g
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
-            const float pg = __shfl(part[R], l16 + 16 * gg);
-            block += pg;
-            if (gg > g) above += pg;
+            const float bg = __shfl(bl, l16 + 16 * gg);
+            const float cg = __shfl(cl, l16 + 16 * gg);
+            if (gg < g) bpre += bg;
+            if (gg > g) csuf += cg;
         }
-        float run = carry + above;
+        float cs[4];   // suffix of the row sums from x
+        cs[3] = csuf + Cr[3];
 #pragma unroll
-        for (int x = 3; x >= 0; --x) {
+        for (int x = 2; x >= 0; --x) cs[x] = cs[x + 1] + Cr[x];
+        float bp = bpre;   // prefix of the column sums before x
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
             const int r = 16 * R + 4 * g + x;
-            run += dl[R][x];
-            if (r < L) a.dla[e0 + r * rs] = r == 0 ? first : run;
+            if (r < L) {
+                const int64_t e = e0 + r * rs;
+                a.dq[e] = pq[x] + dqR[x];
+                a.dk[e] = pk[x] + dkrR[x] + dkc[R][x];
+                a.dla[e] = pl[x] + Ab[R] + bp + cs[x] + DgS[(4 * R + x) * INTRA_NT + t];
+            }
+            bp += Bc[R][x];
         }
-        carry += block;
     }
     if (t < L) a.dbeta[(row0c + t) * H + h] += db2[t];
 }
 
 }  // namespace
 
-// the workspace the plan sizes: entering state, leaving-state gradient, A/P/T,
-// dP/dT and the first- and last-token terms, per (chunk id, head)
+// the workspace the plan sizes: entering state, leaving-state gradient, A/P/T
+// and dP/dT, per (chunk id, head)
 static_assert(kChunkBackwardFloats == 2 * static_cast<size_t>(SS) + 3 * TSZ + kDptFloats,
               "the workspace layout of the chunked backward");
 static_assert(CH == kChunk, "the plan's chunk length");

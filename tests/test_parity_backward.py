@@ -58,6 +58,31 @@ def test_backward_dense_bf16():
     _compare("backward dense bf16", got, ref)
 
 
+def test_backward_extreme_gates():
+    """Tokens whose every channel forgets completely (log_alpha = -200), some
+    of them inside a run of -20 on channels 20..39 (decays beyond 2^-96 over
+    half a 16-token block, so the diagonal blocks take those channels
+    pairwise), a run of -60 on half the channels of the other head, channels
+    that never forget (log_alpha = 0), beta at 0 and 1 (a token after a -200
+    one with beta = 0 enters from a vanishing state, so its d log alpha is of
+    order e^-200); resumed states, both loss gradients."""
+    inp = ki.dense_prefill(57, B=1, T=300, H=2, gated=True, initial_state=True)
+    r = np.random.default_rng(57)
+    la = inp.log_alpha
+    la[0, r.integers(0, 300, 40), 0, :] = -200.0
+    la[0, :, 1, :5] = 0.0
+    la[0, 100:140, 1, 64:] = -60.0
+    la[0, 150:230, 0, 20:40] = -20.0
+    bb = ki.bf16_to_f32(inp.beta)
+    bb[0, ::7, 0] = 0.0
+    bb[0, ::5, 1] = 1.0
+    inp.beta = ki.bf16_bits(bb)
+    d_o, d_s = ki.loss_gradients(57, (1, 300, 2, 128), 1, 2)
+    got = _dense(inp, d_o, d_s, device())
+    ref = oracle.backward(*inp.widened(), d_o, inp.initial_state, d_s)
+    _compare("backward extreme gates", got, ref)
+
+
 def test_backward_fp32_inputs_no_states():
     """fp32 inputs, no initial state and no final-state gradient (zeros)."""
     inp = ki.workload_single(T=256)
