@@ -392,9 +392,11 @@ struct TileRaw {
 template <bool TRANS, int NT>
 __device__ __forceinline__ void request_tile(const float* src, TileRaw<NT>& p)
 {
+    uint32_t tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));   // offsets recomputed per call, not kept across a loop
 #pragma unroll
     for (int j = 0; j < TileRaw<NT>::N; ++j) {
-        const uint32_t q = threadIdx.x + j * NT;
+        const uint32_t q = tid + j * NT;
         if (!TRANS) {
             const uint32_t r = q >> 5, i = 2 * (q & 31);
             p.x[j] = at(reinterpret_cast<const float2*>(src), (r * CH + i) >> 1);
@@ -410,9 +412,13 @@ template <bool TRANS, int NT>
 __device__ __forceinline__ void tile_put(const TileRaw<NT>& p, char* img)
 {
     constexpr int plane = CH * CH * 2;
+    // (the addresses are recomputed at every call rather than kept in
+    // registers across a caller's loop: the thread index is made opaque)
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
 #pragma unroll
     for (int j = 0; j < TileRaw<NT>::N; ++j) {
-        const int q = threadIdx.x + j * NT;
+        const int q = tid + j * NT;
         if (!TRANS) img_put2<true>(img, plane, q >> 5, 2 * (q & 31), 2, p.x[j].x, p.x[j].y);
         else img_put2<true>(img, plane, q & 63, 2 * (q >> 6), 2, p.x[j].x, p.x[j].y);
     }
@@ -718,6 +724,8 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_states_kernel(const ChunkBwdA
 
     for (int64_t c = 0; c < nch; ++c) {
         const int64_t id = chunk_id(row0, n, c);
+        const int64_t row0c = row0 + c * CH;
+        const int L = static_cast<int>(min<int64_t>(CH, len - c * CH));
         lds_sync();  // the previous chunk's products are done with the images
         tile_put<false, SEQ_NT>(traw, TI);
         VS[2 * t] = make_uint4(vraw[0] | (vraw[1] << 16), vraw[2] | (vraw[3] << 16),
@@ -766,17 +774,21 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_states_kernel(const ChunkBwdA
                 X[m] = mma3(ah, al, bh, bl, X[m]);
             }
         }
-        // B W = B (V - X)
+        // W = V - X (parked in dk for the grads kernel), then B W
         {
             const uint4 v0 = VS[2 * t], v1 = VS[2 * t + 1];
             const uint32_t vw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            float* wdst = a.dk + (row0c * H + h) * kDim;
+            const uint32_t rs = H * kDim, lo = col + 4 * g * rs;
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
-                    const int e = 4 * m + x;
+                    const int e = 4 * m + x, r = 16 * m + 4 * g + x;
                     const float v = (e & 1) ? bf_hi(vw[e >> 1]) : bf_lo(vw[e >> 1]);
-                    X[m][x] = bs[16 * m + 4 * g + x] * (v - X[m][x]);
+                    const float w = v - X[m][x];
+                    if (r < L) at(wdst + (16 * m + x) * rs, lo) = w;
+                    X[m][x] = bs[r] * w;
                 }
         }
         // U = T (B W) (sum over tokens: 2 steps)
@@ -794,7 +806,18 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_states_kernel(const ChunkBwdA
                 U[m] = mma3(ah, al, wh, wl, U[m]);
             }
         }
-        // S1 = Diag(gam_L) S0 + Ke^T U
+        // U (parked in dq for the grads kernel), then S1 = Diag(gam_L) S0 + Ke^T U
+        {
+            float* udst = a.dq + (row0c * H + h) * kDim;
+            const uint32_t rs = H * kDim, lo = col + 4 * g * rs;
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const int r = 16 * m + 4 * g + x;
+                    if (r < L) at(udst + (16 * m + x) * rs, lo) = U[m][x];
+                }
+        }
         bf16x8 uh[2], ul[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s) bfrag(U[2 * s], U[2 * s + 1], uh[s], ul[s]);
@@ -873,6 +896,8 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_dstate_kernel(const ChunkBwdA
 
     for (int64_t c = nch - 1; c >= 0; --c) {
         const int64_t id = chunk_id(row0, n, c);
+        const int64_t row0c = row0 + c * CH;
+        const int L = static_cast<int>(min<int64_t>(CH, len - c * CH));
         lds_sync();
         tile_put<true, SEQ_NT>(praw, PT);
         tile_put<true, SEQ_NT>(traw, TT);
@@ -883,6 +908,9 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_dstate_kernel(const ChunkBwdA
         for (int s = 0; s < 2; ++s) bfrag(oraw[2 * s], oraw[2 * s + 1], oh[s], ol[s]);
         Staged<SEQ_NT> st;
         stage_raw<SEQ_NT, true>(raw, tot, st);
+        // (the image addresses are recomputed every chunk rather than kept in
+        // registers across the loop: the channel index is made opaque here)
+        asm volatile("" : "+v"(st.c0));
 #pragma unroll
         for (int j = 0; j < Staged<SEQ_NT>::TOK; ++j) {
             const int r = st.r0 + j;
@@ -950,10 +978,24 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_dstate_kernel(const ChunkBwdA
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        // dU and dW' parked in d log alpha and dv for the grads kernel, then -B dW'
+        __builtin_amdgcn_sched_barrier(0);
+        {
+            const int64_t base = (row0c * H + h) * kDim;
+            const uint32_t rs = H * kDim, lo = col + 4 * g * rs;
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
+            for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int x = 0; x < 4; ++x) nW[m][x] *= -bs[16 * m + 4 * g + x];
+                for (int x = 0; x < 4; ++x) {
+                    const int r = 16 * m + 4 * g + x;
+                    if (r < L) {
+                        at(a.dla + base + (16 * m + x) * rs, lo) = dU[m][x];
+                        at(a.dv + base + (16 * m + x) * rs, lo) = nW[m][x];
+                    }
+                    nW[m][x] *= -bs[r];
+                }
+        }
+        __builtin_amdgcn_sched_barrier(0);
         // dS0 = Diag(gam_L) dS1 + Qt^T dO - Kt^T B dW'
         bf16x8 wh[2], wl[2];
 #pragma unroll
@@ -979,8 +1021,9 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_dstate_kernel(const ChunkBwdA
 // ================================================================ grads
 //
 // Per chunk of one head (grid: chunk ids x heads; 512 threads).
-// Phase A, wave w on value columns 16w..16w+15 (accumulator layout):
-//   X = Kt S0, W = V - X, U = T B W, dU = P^T dO + Ke dS1, dW' = T^T dU;
+// Phase A, wave w on value columns 16w..16w+15 (accumulator layout): U and
+// W = V - Kt S0 (parked in dq and dk by the states kernel), dU and dW' = T^T dU
+// (parked in d log alpha and dv by the dstate kernel), dO;
 //   writes dv = B dW' and the row sums of dW' (.) W (db, first term).
 // Phase B, wave w on channels 16w..16w+15 (sums over the value columns j,
 // from LDS images of dO, -B dW' and U and the rows of S0 and dS1 read from
@@ -992,12 +1035,9 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_dstate_kernel(const ChunkBwdA
 
 __global__ __launch_bounds__(SEQ_NT, 1) void chunk_grads_kernel(const ChunkBwdArgs a)
 {
-    constexpr int KT_PL = CH * kDim * 2, T_PL = CH * CH * 2;
-    // phase A: Kt | Ke | T | P^T | T^T;  phase B: dO | -B dW' | U;  phase C: dU | B W
-    constexpr int OFF_KT = 0, OFF_KE = 2 * KT_PL, OFF_TI = 4 * KT_PL, OFF_PT = OFF_TI + 2 * T_PL,
-                  OFF_TT = OFF_PT + 2 * T_PL, REGION = OFF_TT + 2 * T_PL;
-    constexpr int OFF_I0 = 0, OFF_I1 = 2 * KT_PL, OFF_I2 = 4 * KT_PL;
-    static_assert(6 * KT_PL <= REGION, "phase B images fit the phase A region");
+    constexpr int KT_PL = CH * kDim * 2;
+    // phase B: dO | -B dW' | U;  phase C: dU | B W
+    constexpr int OFF_I0 = 0, OFF_I1 = 2 * KT_PL, OFF_I2 = 4 * KT_PL, REGION = 6 * KT_PL;
     __shared__ __attribute__((aligned(16))) char img[REGION];
     __shared__ __attribute__((aligned(16))) float Gs[CH * GLD];
     __shared__ float tot[(SEQ_NT / 64) * kDim];
@@ -1015,12 +1055,9 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_grads_kernel(const ChunkBwdAr
     const int64_t rs = static_cast<int64_t>(H) * kDim;      // elements per token row
     const int64_t wslot = id * H + h;
 
-    // ---- staging: G tile, Kt and Ke images, T, P^T and T^T images
+    // ---- staging: G tile; this wave's columns of U, W, dU, dW' (parked in
+    // dq, dk, d log alpha and dv by the state sweeps) and dO
     {
-        const float* apt = a.ws_apt + wslot * (3 * TSZ);
-        tile_image<false, SEQ_NT>(apt + 2 * TSZ, img + OFF_TI);
-        tile_image<true, SEQ_NT>(apt + TSZ, img + OFF_PT);
-        tile_image<true, SEQ_NT>(apt + 2 * TSZ, img + OFF_TT);
         Staged<SEQ_NT> st;
         stage<SEQ_NT, false>(a, row0c, L, h, tot, st);
         stage_beta(a, row0c, L, h, bs);
@@ -1028,112 +1065,30 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_grads_kernel(const ChunkBwdAr
         for (int j = 0; j < Staged<SEQ_NT>::TOK; ++j) {
             const int r = st.r0 + j;
             *reinterpret_cast<float2*>(&Gs[r * GLD + st.c0]) = make_float2(st.g[j][0], st.g[j][1]);
-            img_put2<true>(img + OFF_KT, KT_PL, r, st.c0, 4, st.kk[j][0] * ex2(st.g[j][0]),
-                           st.kk[j][1] * ex2(st.g[j][1]));
-            img_put2<true>(img + OFF_KE, KT_PL, r, st.c0, 4, st.kk[j][0] * ex2(st.gl[0] - st.g[j][0]),
-                           st.kk[j][1] * ex2(st.gl[1] - st.g[j][1]));
         }
         if (st.r0 == 0) {
             gLs[st.c0] = st.gl[0];
             gLs[st.c0 + 1] = st.gl[1];
         }
     }
-    // ---- this wave's columns of S0, dS1, dO and V
-    f32x4 S[8], dS[8], dO[4], W[4];
+    f32x4 U[4], dU[4], dW[4], W[4], dO[4];
+    const int64_t e0 = (row0c * H + h) * kDim + col;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int r = 16 * m + 4 * g + x;
+            const bool in = r < L;
+            const int64_t e = e0 + (in ? r : 0) * rs;
+            U[m][x] = in ? a.dq[e] : 0.f;
+            W[m][x] = in ? a.dk[e] : 0.f;
+            dU[m][x] = in ? a.dla[e] : 0.f;
+            dW[m][x] = in ? a.dv[e] : 0.f;
+            dO[m][x] = in ? a.d_o[e] : 0.f;
+        }
+    lds_sync();   // G and beta
     {
-        const float* s0 = a.ws_s0 + wslot * SS;
-        const float* ds = a.ws_ds + wslot * SS;
-#pragma unroll
-        for (int tt = 0; tt < 8; ++tt)
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int e = (16 * tt + 4 * g + x) * kDim + col;
-                S[tt][x] = s0[e];
-                dS[tt][x] = ds[e];
-            }
-        const int64_t e0 = (row0c * H + h) * kDim + col;
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int r = 16 * m + 4 * g + x;
-                dO[m][x] = r < L ? a.d_o[e0 + r * rs] : 0.f;
-                W[m][x] = r < L ? widen(a.v[e0 + r * rs]) : 0.f;
-            }
-    }
-    lds_sync();
-
-    // ---- phase A
-    f32x4 U[4], dU[4], dW[4];
-    {
-        bf16x8 bh[4], bl[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) bfrag(S[2 * s], S[2 * s + 1], bh[s], bl[s]);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            f32x4 X = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                bf16x8 ah, al;
-                img_frag(img + OFF_KT, KT_PL, m * 4 + s, lane, ah, al);
-                X = mma3(ah, al, bh[s], bl[s], X);
-            }
-            W[m] -= X;  // W = V - X
-        }
-        f32x4 BW[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int x = 0; x < 4; ++x) BW[m][x] = bs[16 * m + 4 * g + x] * W[m][x];
-        bf16x8 wh[2], wl[2];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) bfrag(BW[2 * s], BW[2 * s + 1], wh[s], wl[s]);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            U[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                bf16x8 ah, al;
-                img_frag(img + OFF_TI, T_PL, m * 2 + s, lane, ah, al);
-                U[m] = mma3(ah, al, wh[s], wl[s], U[m]);
-            }
-        }
-        bf16x8 oh[2], ol[2];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) bfrag(dO[2 * s], dO[2 * s + 1], oh[s], ol[s]);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) bfrag(dS[2 * s], dS[2 * s + 1], bh[s], bl[s]);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            dU[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                bf16x8 ah, al;
-                img_frag(img + OFF_PT, T_PL, m * 2 + s, lane, ah, al);
-                dU[m] = mma3(ah, al, oh[s], ol[s], dU[m]);
-            }
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                bf16x8 ah, al;
-                img_frag(img + OFF_KE, KT_PL, m * 4 + s, lane, ah, al);
-                dU[m] = mma3(ah, al, bh[s], bl[s], dU[m]);
-            }
-        }
-        bf16x8 uh[2], ul[2];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) bfrag(dU[2 * s], dU[2 * s + 1], uh[s], ul[s]);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            dW[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                bf16x8 ah, al;
-                img_frag(img + OFF_TT, T_PL, m * 2 + s, lane, ah, al);
-                dW[m] = mma3(ah, al, uh[s], ul[s], dW[m]);
-            }
-        }
         // dv = B dW'; db (first term): row sums of dW' (.) W over this wave's columns
-        const int64_t e0 = (row0c * H + h) * kDim + col;
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -1153,7 +1108,7 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_grads_kernel(const ChunkBwdAr
                 }
             }
     }
-    lds_sync();  // every wave is done with the phase A images
+    lds_sync();
 
     // ---- phase B images (natural binding, rows = tokens, k = value columns):
     // dO, -B dW', U.  Even lanes store their value and the odd neighbour's.
