@@ -293,6 +293,7 @@ struct ChunkRaw {
     float2 la[TOK];
     uint32_t k[TOK];
     uint32_t q[WITHQ ? TOK : 1];
+    int L;                  // the chunk's rows; the rest are zeroed by stage_raw
 };
 
 template <int NT, bool WITHQ>
@@ -308,26 +309,36 @@ __device__ __forceinline__ void request(const ChunkBwdArgs& a, int64_t row0c, in
     const bf16_t* k = a.k + base;
     const bf16_t* q = a.q + base;
     const uint32_t rstride = static_cast<uint32_t>(a.H) * kDim;
+    // Rows past the chunk's end load row 0 (always present) and are zeroed
+    // at staging, not here: a load under a condition is compiled as a branch
+    // that waits for it, and so is a select right after the load.
+    p.L = L;
 #pragma unroll
     for (int j = 0; j < TOK; ++j) {
         const int r = r0 + j;
-        const bool in = r < L;
-        const uint32_t e = static_cast<uint32_t>(c0) + static_cast<uint32_t>(in ? r : 0) * rstride;
-        p.la[j] = in ? at(reinterpret_cast<const float2*>(la), e >> 1) : make_float2(0.f, 0.f);
-        p.k[j] = in ? at(reinterpret_cast<const uint32_t*>(k), e >> 1) : 0u;
-        if (WITHQ) p.q[j] = in ? at(reinterpret_cast<const uint32_t*>(q), e >> 1) : 0u;
+        const uint32_t e = static_cast<uint32_t>(c0) + static_cast<uint32_t>(r < L ? r : 0) * rstride;
+        p.la[j] = at(reinterpret_cast<const float2*>(la), e >> 1);
+        p.k[j] = at(reinterpret_cast<const uint32_t*>(k), e >> 1);
+        if (WITHQ) p.q[j] = at(reinterpret_cast<const uint32_t*>(q), e >> 1);
     }
 }
 
 // The cumulative log2-decay of the requested inputs (one barrier, for the
-// group prefix through `tot`).
+// group prefix through `tot`); rows from L on are zeroed in p first.
 template <int NT, bool WITHQ>
-__device__ __forceinline__ void stage_raw(const ChunkRaw<NT, WITHQ>& p, float* tot, Staged<NT>& s)
+__device__ __forceinline__ void stage_raw(ChunkRaw<NT, WITHQ>& p, float* tot, Staged<NT>& s)
 {
     constexpr int TG = Staged<NT>::TG, TOK = Staged<NT>::TOK;
     const int t = threadIdx.x;
     s.c0 = 2 * (t & 63);
     s.r0 = TOK * wave_id();
+#pragma unroll
+    for (int j = 0; j < TOK; ++j) {
+        const bool in = s.r0 + j < p.L;
+        p.la[j] = in ? p.la[j] : make_float2(0.f, 0.f);
+        p.k[j] = in ? p.k[j] : 0u;
+        if (WITHQ) p.q[j] = in ? p.q[j] : 0u;
+    }
     float run0 = 0.f, run1 = 0.f;
 #pragma unroll
     for (int j = 0; j < TOK; ++j) {
@@ -369,14 +380,23 @@ __device__ __forceinline__ void stage(const ChunkBwdArgs& a, int64_t row0c, int 
 {
     ChunkRaw<NT, WITHQ> p;
     request<NT, WITHQ>(a, row0c, L, h, p);
+    __builtin_amdgcn_sched_barrier(0);   // all requests issued before the first use
     stage_raw<NT, WITHQ>(p, tot, s);
 }
 
-// beta of the chunk's rows (zeros from L on) into LDS, by the first 64 threads
+// beta of the chunk's row t mod 64, loaded without a branch (a row from L on
+// reads row 0: its value is to be replaced by zero where it is used);
+// stage_beta stores the chunk's beta into LDS by the first 64 threads
+__device__ __forceinline__ float beta_raw(const ChunkBwdArgs& a, int64_t row0c, int L, int h)
+{
+    const int t = threadIdx.x & (CH - 1);
+    return widen(a.beta[(row0c + (t < L ? t : 0)) * a.H + h]);
+}
 __device__ __forceinline__ void stage_beta(const ChunkBwdArgs& a, int64_t row0c, int L, int h, float* bs)
 {
+    const float b = beta_raw(a, row0c, L, h);
     const int t = threadIdx.x;
-    if (t < CH) bs[t] = t < L ? widen(a.beta[(row0c + t) * a.H + h]) : 0.f;
+    if (t < CH) bs[t] = t < L ? b : 0.f;
 }
 
 // A 64 x 64 fp32 tile from global memory into an image: TRANS = false stores
@@ -706,7 +726,8 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_states_kernel(const ChunkBwdA
         const int64_t id = chunk_id(row0, n, c);
         request_tile<false, SEQ_NT>(a.ws_apt + (id * H + h) * (3 * TSZ) + 2 * TSZ, traw);
         request<SEQ_NT, false>(a, row0c, L, h, raw);
-        // rows from L on read row L - 1 and are replaced by zeros (no branches)
+        // rows from L on read row L - 1; they are replaced by zeros where the
+        // values are consumed (a select here would wait for the loads)
         const bf16_t* vb = a.v + (row0c * H + h) * kDim;
         const uint32_t rs = H * kDim;
 #pragma unroll
@@ -714,11 +735,9 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_states_kernel(const ChunkBwdA
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 const int r = 16 * m + 4 * g + x;
-                const uint32_t u = at(vb, col + static_cast<uint32_t>(min(r, L - 1)) * rs).bits;
-                vraw[4 * m + x] = r < L ? u : 0u;
+                vraw[4 * m + x] = at(vb, col + static_cast<uint32_t>(min(r, L - 1)) * rs).bits;
             }
-        const float b = widen(at(a.beta + row0c * H + h, static_cast<uint32_t>(min(t, L - 1)) * H));
-        braw = t < L ? b : 0.f;
+        braw = widen(at(a.beta + row0c * H + h, static_cast<uint32_t>(min(t, L - 1)) * H));
     };
     if (nch > 0) request_chunk(0);
 
@@ -728,11 +747,16 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_states_kernel(const ChunkBwdA
         const int L = static_cast<int>(min<int64_t>(CH, len - c * CH));
         lds_sync();  // the previous chunk's products are done with the images
         tile_put<false, SEQ_NT>(traw, TI);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+                if (16 * m + 4 * g + x >= L) vraw[4 * m + x] = 0u;
         VS[2 * t] = make_uint4(vraw[0] | (vraw[1] << 16), vraw[2] | (vraw[3] << 16),
                                vraw[4] | (vraw[5] << 16), vraw[6] | (vraw[7] << 16));
         VS[2 * t + 1] = make_uint4(vraw[8] | (vraw[9] << 16), vraw[10] | (vraw[11] << 16),
                                    vraw[12] | (vraw[13] << 16), vraw[14] | (vraw[15] << 16));
-        if (t < CH) bs[t] = braw;
+        if (t < CH) bs[t] = t < L ? braw : 0.f;
         Staged<SEQ_NT> st;
         stage_raw<SEQ_NT, false>(raw, tot, st);
 #pragma unroll
@@ -878,7 +902,8 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_dstate_kernel(const ChunkBwdA
         request_tile<true, SEQ_NT>(apt + TSZ, praw);
         request_tile<true, SEQ_NT>(apt + 2 * TSZ, traw);
         request<SEQ_NT, true>(a, row0c, L, h, raw);
-        // rows from L on read row L - 1 and are replaced by zeros (no branches)
+        // rows from L on read row L - 1; they are replaced by zeros where the
+        // values are consumed (a select here would wait for the loads)
         const float* ob = a.d_o + (row0c * H + h) * kDim;
         const uint32_t rs = H * kDim;
 #pragma unroll
@@ -886,11 +911,9 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_dstate_kernel(const ChunkBwdA
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 const int r = 16 * m + 4 * g + x;
-                const float o = at(ob, col + static_cast<uint32_t>(min(r, L - 1)) * rs);
-                oraw[m][x] = r < L ? o : 0.f;
+                oraw[m][x] = at(ob, col + static_cast<uint32_t>(min(r, L - 1)) * rs);
             }
-        const float b = widen(at(a.beta + row0c * H + h, static_cast<uint32_t>(min(t, L - 1)) * H));
-        braw = t < L ? b : 0.f;
+        braw = widen(at(a.beta + row0c * H + h, static_cast<uint32_t>(min(t, L - 1)) * H));
     };
     if (nch > 0) request_chunk(nch - 1);
 
@@ -901,7 +924,12 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_dstate_kernel(const ChunkBwdA
         lds_sync();
         tile_put<true, SEQ_NT>(praw, PT);
         tile_put<true, SEQ_NT>(traw, TT);
-        if (t < CH) bs[t] = braw;
+        if (t < CH) bs[t] = t < L ? braw : 0.f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+                if (16 * m + 4 * g + x >= L) oraw[m][x] = 0.f;
         // dO in accumulator layout (rows r = 16m + 4g + x of column col), split
         bf16x8 oh[2], ol[2];
 #pragma unroll
@@ -1055,22 +1083,13 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_grads_kernel(const ChunkBwdAr
     const int64_t rs = static_cast<int64_t>(H) * kDim;      // elements per token row
     const int64_t wslot = id * H + h;
 
-    // ---- staging: G tile; this wave's columns of U, W, dU, dW' (parked in
-    // dq, dk, d log alpha and dv by the state sweeps) and dO
-    {
-        Staged<SEQ_NT> st;
-        stage<SEQ_NT, false>(a, row0c, L, h, tot, st);
-        stage_beta(a, row0c, L, h, bs);
-#pragma unroll
-        for (int j = 0; j < Staged<SEQ_NT>::TOK; ++j) {
-            const int r = st.r0 + j;
-            *reinterpret_cast<float2*>(&Gs[r * GLD + st.c0]) = make_float2(st.g[j][0], st.g[j][1]);
-        }
-        if (st.r0 == 0) {
-            gLs[st.c0] = st.gl[0];
-            gLs[st.c0 + 1] = st.gl[1];
-        }
-    }
+    // ---- every global load of the chunk is issued here, before the first
+    // store: one round of latency, and no wait for a load also waits for
+    // earlier stores (loads and stores share one counter).  U, W, dU and dW'
+    // were parked in dq, dk, d log alpha and dv by the state sweeps.
+    ChunkRaw<SEQ_NT, true> raw;
+    request<SEQ_NT, true>(a, row0c, L, h, raw);
+    const float braw = beta_raw(a, row0c, L, h);
     f32x4 U[4], dU[4], dW[4], W[4], dO[4];
     const int64_t e0 = (row0c * H + h) * kDim + col;
 #pragma unroll
@@ -1080,13 +1099,65 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_grads_kernel(const ChunkBwdAr
             const int r = 16 * m + 4 * g + x;
             const bool in = r < L;
             const int64_t e = e0 + (in ? r : 0) * rs;
-            U[m][x] = in ? a.dq[e] : 0.f;
-            W[m][x] = in ? a.dk[e] : 0.f;
-            dU[m][x] = in ? a.dla[e] : 0.f;
-            dW[m][x] = in ? a.dv[e] : 0.f;
-            dO[m][x] = in ? a.d_o[e] : 0.f;
+            U[m][x] = a.dq[e];
+            W[m][x] = a.dk[e];
+            dU[m][x] = a.dla[e];
+            dW[m][x] = a.dv[e];
+            dO[m][x] = a.d_o[e];
         }
-    lds_sync();   // G and beta
+    // this lane's row cw = col of S0 and dS1, columns 32 s + 8 g .. + 7
+    float4 s0r[8], dsr[8];
+    {
+        const float* s0 = a.ws_s0 + wslot * SS + col * kDim;
+        const float* ds = a.ws_ds + wslot * SS + col * kDim;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int j0 = 32 * s + 8 * g;
+            s0r[2 * s] = *reinterpret_cast<const float4*>(s0 + j0);
+            s0r[2 * s + 1] = *reinterpret_cast<const float4*>(s0 + j0 + 4);
+            dsr[2 * s] = *reinterpret_cast<const float4*>(ds + j0);
+            dsr[2 * s + 1] = *reinterpret_cast<const float4*>(ds + j0 + 4);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+            if (16 * m + 4 * g + x >= L) U[m][x] = W[m][x] = dU[m][x] = dW[m][x] = dO[m][x] = 0.f;
+
+    // ---- staging: G and beta; k and q (bf16) into the image region, which
+    // is free until the phase B images
+    __bf16* Kb = reinterpret_cast<__bf16*>(img + OFF_I2);
+    __bf16* Qb = Kb + CH * kDim;
+    {
+        Staged<SEQ_NT> st;
+        stage_raw<SEQ_NT, true>(raw, tot, st);
+        if (t < CH) bs[t] = t < L ? braw : 0.f;
+#pragma unroll
+        for (int j = 0; j < Staged<SEQ_NT>::TOK; ++j) {
+            const int r = st.r0 + j;
+            *reinterpret_cast<float2*>(&Gs[r * GLD + st.c0]) = make_float2(st.g[j][0], st.g[j][1]);
+            *reinterpret_cast<uint32_t*>(&Kb[r * kDim + st.c0]) = raw.k[j];
+            *reinterpret_cast<uint32_t*>(&Qb[r * kDim + st.c0]) = raw.q[j];
+        }
+        if (st.r0 == 0) {
+            gLs[st.c0] = st.gl[0];
+            gLs[st.c0 + 1] = st.gl[1];
+        }
+    }
+    lds_sync();   // G, beta, k and q
+    // queries and keys of this lane's rows and channel (read before the
+    // barrier after which the images overwrite them)
+    float qv[4][4], kv[4][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int r = 16 * m + 4 * g + x;
+            qv[m][x] = (float)Qb[r * kDim + col];
+            kv[m][x] = (float)Kb[r * kDim + col];
+        }
     {
         // dv = B dW'; db (first term): row sums of dW' (.) W over this wave's columns
 #pragma unroll
@@ -1131,29 +1202,13 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_grads_kernel(const ChunkBwdAr
     float* dpt = a.ws_dpt + wslot * kDptFloats;
     {
         const int cw = col;
-        // queries and keys of this lane's rows and channel (all loads before the stores below)
-        float qv[4][4], kv[4][4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int r = 16 * m + 4 * g + x;
-                const int64_t e = ((row0c + (r < L ? r : 0)) * H + h) * kDim + cw;
-                qv[m][x] = r < L ? widen(a.q[e]) : 0.f;
-                kv[m][x] = r < L ? widen(a.k[e]) : 0.f;
-            }
         bf16x8 sh[4], sl[4], dh[4], dl[4];
         float dg = 0.f;
         {
-            const float* s0 = a.ws_s0 + wslot * SS + cw * kDim;
-            const float* ds = a.ws_ds + wslot * SS + cw * kDim;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const int j0 = 32 * s + 8 * g;
-                const float4 a0 = *reinterpret_cast<const float4*>(s0 + j0);
-                const float4 a1 = *reinterpret_cast<const float4*>(s0 + j0 + 4);
-                const float4 b0 = *reinterpret_cast<const float4*>(ds + j0);
-                const float4 b1 = *reinterpret_cast<const float4*>(ds + j0 + 4);
+                const float4 a0 = s0r[2 * s], a1 = s0r[2 * s + 1];
+                const float4 b0 = dsr[2 * s], b1 = dsr[2 * s + 1];
                 const float xs[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
                 const float xd[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
@@ -1371,19 +1426,54 @@ __global__ __launch_bounds__(INTRA_NT, 1) void chunk_intra_kernel(const ChunkBwd
     const int t = threadIdx.x, lane = t & 63, wave = wave_id(), g = lane >> 4, l16 = lane & 15;
     const int64_t wslot = id * H + h;
 
-    // ---- phase 1: T, A, dT (i < r), dP (i <= r)
+    // ---- the tiles, beta and the staging inputs are loaded first, without
+    // branches, so that their latencies overlap
+    constexpr int NE = TSZ / INTRA_NT;
+    float ar[NE], tr[NE], pr[NE], dr[NE];
     {
         const float* apt = a.ws_apt + wslot * (3 * TSZ);
         const float* dpt = a.ws_dpt + wslot * kDptFloats;
-        for (int e = t; e < TSZ; e += INTRA_NT) {
-            const int r = e >> 6, i = e & 63;
-            As[r * PLD + i] = apt[e];
-            Ts[r * PLD + i] = apt[2 * TSZ + e];
-            Pd[r * PLD + i] = i <= r ? dpt[e] : 0.f;
-            Ad[r * PLD + i] = i < r ? dpt[TSZ + e] : 0.f;
+#pragma unroll
+        for (int j = 0; j < NE; ++j) {
+            const int e = t + j * INTRA_NT;
+            ar[j] = apt[e];
+            tr[j] = apt[2 * TSZ + e];
+            pr[j] = dpt[e];
+            dr[j] = dpt[TSZ + e];
         }
-        stage_beta(a, row0c, L, h, bs);
     }
+    const float braw = beta_raw(a, row0c, L, h);
+    ChunkRaw<INTRA_NT, true> raw;
+    request<INTRA_NT, true>(a, row0c, L, h, raw);
+    // the grads kernel's terms of dq, dk and d log a for the rows of one
+    // 16-token block, channel cc = 16 w + l16; requested a block ahead, and
+    // before the previous block's stores (rows from L on are never stored)
+    const int cc = 16 * wave + l16;
+    const int64_t rs = static_cast<int64_t>(H) * kDim;
+    const int64_t e0 = (row0c * H + h) * kDim + cc;
+    float pq[4], pk[4], pl[4];
+    auto request_partials = [&](int R) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int r = 16 * R + 4 * g + x;
+            const int64_t e = e0 + (r < L ? r : 0) * rs;
+            pq[x] = a.dq[e];
+            pk[x] = a.dk[e];
+            pl[x] = a.dla[e];
+        }
+    };
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- phase 1: T, A, dT (i < r), dP (i <= r)
+#pragma unroll
+    for (int j = 0; j < NE; ++j) {
+        const int e = t + j * INTRA_NT, r = e >> 6, i = e & 63;
+        As[r * PLD + i] = ar[j];
+        Ts[r * PLD + i] = tr[j];
+        Pd[r * PLD + i] = i <= r ? pr[j] : 0.f;   // (only the lower blocks were written)
+        Ad[r * PLD + i] = i < r ? dr[j] : 0.f;
+    }
+    if (t < CH) bs[t] = t < L ? braw : 0.f;
     lds_sync();
     const int yi = t >> 3, y0 = 8 * (t & 7);   // this thread's row and first 8 columns
     {
@@ -1438,7 +1528,7 @@ __global__ __launch_bounds__(INTRA_NT, 1) void chunk_intra_kernel(const ChunkBwd
     // ---- phase 2 staging: G (over T and A), k, q
     {
         Staged<INTRA_NT> st;
-        stage<INTRA_NT, true>(a, row0c, L, h, tot, st);   // its barrier also ends phase 1
+        stage_raw<INTRA_NT, true>(raw, tot, st);   // its barrier also ends phase 1
 #pragma unroll
         for (int j = 0; j < Staged<INTRA_NT>::TOK; ++j) {
             const int r = st.r0 + j;
@@ -1450,12 +1540,9 @@ __global__ __launch_bounds__(INTRA_NT, 1) void chunk_intra_kernel(const ChunkBwd
     lds_sync();
 
     // ---- phase 2: wave w on channels cc = 16w + l16; rows 16R + 4g + x of each block R
-    const int cc = 16 * wave + l16;
     auto Gv = [&](int r) { return Gs[r * kDim + cc]; };
     auto Kv = [&](int r) { return (float)Ks[r * kDim + cc]; };
     auto Qv = [&](int r) { return (float)Qs[r * kDim + cc]; };
-    const int64_t rs = static_cast<int64_t>(H) * kDim;
-    const int64_t e0 = (row0c * H + h) * kDim + cc;
     // The cross sums C_j = sum_{r >= j > i} X_ri of the decay products
     // X_ri = (dA_ri k_r + dP_ri q_r) k_i 2^(G_r - G_i) (this lane's channel)
     // are the A/P part of d log a_j.  By blocks, for j in block J: Ab[J] the
@@ -1538,6 +1625,7 @@ __global__ __launch_bounds__(INTRA_NT, 1) void chunk_intra_kernel(const ChunkBwd
             DgS[(4 * R + x) * INTRA_NT + t] = g == 0 ? c[x] : g == 1 ? c[4 + x] : g == 2 ? c[8 + x] : c[12 + x];
     }
 
+    request_partials(3);
     f32x4 dkc[4];
     float Bc[4][4], Ab[4];
 #pragma unroll
@@ -1558,20 +1646,8 @@ __global__ __launch_bounds__(INTRA_NT, 1) void chunk_intra_kernel(const ChunkBwd
         }
         f32x4 dqR = {0.f, 0.f, 0.f, 0.f}, dkrR = dqR;
         float Cr[4] = {0.f, 0.f, 0.f, 0.f};
-        float pq[4], pk[4], pl[4];
 #pragma unroll
         for (int I = 0; I <= R; ++I) {
-            if (I == R) {
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const int r = 16 * R + 4 * g + x;
-                    const bool in = r < L;
-                    const int64_t e = e0 + (in ? r : 0) * rs;
-                    pq[x] = in ? a.dq[e] : 0.f;
-                    pk[x] = in ? a.dk[e] : 0.f;
-                    pl[x] = in ? a.dla[e] : 0.f;
-                }
-            }
             const float rho = I < R ? Gv(16 * R - 1) : Gv(16 * R + 7);
             const bool safe = I < R || (Gv(16 * R) - rho <= 96.f && rho - Gv(16 * R + 15) <= 96.f);
             float f[4], hh[4], kI[4], kh[4], qf[4], kf[4];
@@ -1659,7 +1735,7 @@ __global__ __launch_bounds__(INTRA_NT, 1) void chunk_intra_kernel(const ChunkBwd
         }
 
         // ---- block R is complete: dq, dk and d log a of its rows, added to
-        // the grads kernel's terms (requested before the diagonal block)
+        // the grads kernel's terms
         const float bl = Bc[R][0] + Bc[R][1] + Bc[R][2] + Bc[R][3];
         const float cl = Cr[0] + Cr[1] + Cr[2] + Cr[3];
         float bpre = 0.f, csuf = 0.f;   // over the lane groups before / after g
@@ -1675,16 +1751,25 @@ __global__ __launch_bounds__(INTRA_NT, 1) void chunk_intra_kernel(const ChunkBwd
 #pragma unroll
         for (int x = 2; x >= 0; --x) cs[x] = cs[x + 1] + Cr[x];
         float bp = bpre;   // prefix of the column sums before x
+        float fq[4], fk[4], fl[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            fq[x] = pq[x] + dqR[x];
+            fk[x] = pk[x] + dkrR[x] + dkc[R][x];
+            fl[x] = pl[x] + Ab[R] + bp + cs[x] + DgS[(4 * R + x) * INTRA_NT + t];
+            bp += Bc[R][x];
+        }
+        if (R > 0) request_partials(R - 1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
             const int r = 16 * R + 4 * g + x;
             if (r < L) {
                 const int64_t e = e0 + r * rs;
-                a.dq[e] = pq[x] + dqR[x];
-                a.dk[e] = pk[x] + dkrR[x] + dkc[R][x];
-                a.dla[e] = pl[x] + Ab[R] + bp + cs[x] + DgS[(4 * R + x) * INTRA_NT + t];
+                a.dq[e] = fq[x];
+                a.dk[e] = fk[x];
+                a.dla[e] = fl[x];
             }
-            bp += Bc[R][x];
         }
     }
     if (t < L) a.dbeta[(row0c + t) * H + h] += db2[t];
