@@ -166,44 +166,48 @@ __global__ __launch_bounds__(256) void decode_tokens_kernel(
     const int commit = n_commit ? min(max(n_commit[n], 0), K) : 0;
     auto rowvec = [&](int t) { return ((n * K + t) * H + h) * kDim; };  // token t's [*, 128] row
 
-    // all tokens' per-head inputs are requested first (independent loads), then
-    // the state; both are in flight together
-    float x0[KM], x1[KM], xb[KM];
+    // all tokens' per-head inputs are requested first, then the state; both
+    // are in flight together.  The loads have no branch around them (tokens
+    // from K on re-read token 0; every thread loads the gate, key and query
+    // element tid mod 128) and their raw values are converted only after all
+    // of them are issued: a conditional load, or one converted right away,
+    // is compiled to wait for its data on the spot.
+    const int e = tid & (kDim - 1);
+    float xa[KM];
+    InT xk[KM], xq[KM], xb[KM];
 #pragma unroll
     for (int t = 0; t < KM; ++t) {
-        if (t < K) {
-            const int64_t vec = rowvec(t);
-            if (tid < kDim) {
-                x0[t] = log_alpha[vec + tid];
-            } else {
-                x0[t] = widen(k[vec + tid - kDim]);
-                x1[t] = widen(q[vec + tid - kDim]);
-            }
-            if (tid == 0) xb[t] = widen(beta[(n * K + t) * H + h]);
-        }
+        const int tt = t < K ? t : 0;
+        const int64_t vec = rowvec(tt);
+        xa[t] = log_alpha[vec + e];
+        xk[t] = k[vec + e];
+        xq[t] = q[vec + e];
+        xb[t] = beta[(n * K + tt) * H + h];
     }
     float4 s[16];
 #pragma unroll
     for (int m = 0; m < 16; ++m)
         s[m] = *reinterpret_cast<const float4*>(S + (row0 + m) * kDim + col);
-    float4 vv = load4(v + rowvec(0) + col);
+    auto vrow = [&](int t) { return v + rowvec(t) + col; };
+    auto vraw = load4_raw(vrow(0));
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < KM; ++t) {
         if (t < K) {
             if (tid < kDim) {
-                sa[t][tid] = exp_gate(x0[t]);
+                sa[t][e] = exp_gate(xa[t]);
             } else {
-                sk[t][tid - kDim] = x0[t];
-                sq[t][tid - kDim] = x1[t];
+                sk[t][e] = widen(xk[t]);
+                sq[t][e] = widen(xq[t]);
             }
-            if (tid == 0) sb[t] = xb[t];
+            if (tid == 0) sb[t] = widen(xb[t]);
         }
     }
     __syncthreads();
 
     for (int t = 0; t < K; ++t) {
-        const float4 vt = vv;
-        if (t + 1 < K) vv = load4(v + rowvec(t + 1) + col);
+        const float4 vt = widen4(vraw);
+        vraw = load4_raw(vrow(t + 1 < K ? t + 1 : t));   // (the last token re-reads its own row)
         const float4 ot = token_update<InT, false>(s, &sa[t][row0], &sk[t][row0], &sq[t][row0], sb[t], vt);
         if (rg == 0) *reinterpret_cast<float4*>(o + rowvec(t) + col) = ot;
         if (t + 1 == commit) {

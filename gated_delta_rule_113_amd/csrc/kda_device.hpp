@@ -26,6 +26,17 @@ __device__ __forceinline__ float4 load4(const bf16_t* p)
                        __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
 }
 
+// The same four elements as raw storage (for a load issued ahead of its
+// use), and their widening.
+__device__ __forceinline__ float4 load4_raw(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ uint2 load4_raw(const bf16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+__device__ __forceinline__ float4 widen4(float4 r) { return r; }
+__device__ __forceinline__ float4 widen4(uint2 r)
+{
+    return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                       __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
+}
+
 // e^x as 2^(x log2 e) on the hardware exp2 (v_exp_f32).  For the gate values
 // used here (x <= 0, |x| up to a few hundred) the relative error is about
 // |x| * 2^-24, far below the fp32 state's own rounding over a sequence.

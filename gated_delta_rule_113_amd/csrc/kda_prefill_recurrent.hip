@@ -56,40 +56,42 @@ __global__ __launch_bounds__(256) void prefill_recurrent_kernel(
     }
     if (max_len > 0 && len > max_len) return;  // left to the chunked kernel
 
-    // this thread's staged element
+    // this thread's staged element.  The requests are plain loads with no
+    // branch around them (tokens past the end re-read the batch's first
+    // token, and every thread loads the four inputs of its element), and the
+    // raw values are converted only at staging: a load under a condition, or
+    // converted right away, is compiled to wait for its data on the spot.
     const int e = tid & (kDim - 1);
     const bool gate_value = tid < kDim;
-    float x0[TB], x1[TB], xb = 0.f;
+    float xa[TB];
+    InT xv[TB], xk[TB], xq[TB], xb;
     auto request = [&](int64_t t0) {
 #pragma unroll
         for (int t = 0; t < TB; ++t) {
-            if (t0 + t < len) {
-                const int64_t vec = ((first + t0 + t) * H + h) * kDim;
-                if (gate_value) {
-                    x0[t] = log_alpha[vec + e];
-                    x1[t] = widen(v[vec + e]);
-                } else {
-                    x0[t] = widen(k[vec + e]);
-                    x1[t] = widen(q[vec + e]);
-                }
-            }
+            const int64_t tt = t0 + t < len ? t0 + t : t0;
+            const int64_t vec = ((first + tt) * H + h) * kDim;
+            xa[t] = log_alpha[vec + e];
+            xv[t] = v[vec + e];
+            xk[t] = k[vec + e];
+            xq[t] = q[vec + e];
         }
-        if (tid < TB && t0 + tid < len) xb = widen(beta[(first + t0 + tid) * H + h]);
+        const int64_t tb = t0 + (tid & (TB - 1));
+        xb = beta[(first + (tb < len ? tb : t0)) * H + h];
     };
     auto stage = [&](int buf, int64_t t0) {
 #pragma unroll
         for (int t = 0; t < TB; ++t) {
             if (t0 + t < len) {
                 if (gate_value) {
-                    sa[buf][t][e] = RAW ? alpha_from_logit(x0[t]) : exp_gate(x0[t]);
-                    sv[buf][t][e] = x1[t];
+                    sa[buf][t][e] = RAW ? alpha_from_logit(xa[t]) : exp_gate(xa[t]);
+                    sv[buf][t][e] = widen(xv[t]);
                 } else {
-                    sk[buf][t][e] = x0[t];
-                    sq[buf][t][e] = x1[t];
+                    sk[buf][t][e] = widen(xk[t]);
+                    sq[buf][t][e] = widen(xq[t]);
                 }
             }
         }
-        if (tid < TB && t0 + tid < len) sb[buf][tid] = RAW ? sigmoid_gate(xb) : xb;
+        if (tid < TB && t0 + tid < len) sb[buf][tid] = RAW ? sigmoid_gate(widen(xb)) : widen(xb);
     };
 
     request(0);
