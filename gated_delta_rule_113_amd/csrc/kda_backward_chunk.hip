@@ -180,6 +180,35 @@ __device__ __forceinline__ void state_store(float* dst, uint32_t lo, const f32x4
 // The wave's index in the workgroup, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// x from another lane of the same row of 16, by a DPP control (a vector-ALU
+// operand modifier, no LDS traffic): quad_perm [1,0,3,2] swaps neighbours,
+// [2,3,0,1] pairs, row_half_mirror reverses each group of 8, row_ror:n
+// rotates the row by n.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppSwap1 = 0xB1, kDppSwap2 = 0x4E, kDppHalfMirror = 0x141;
+template <int N>
+__device__ __forceinline__ float row_ror(float x) { return dpp_mov<0x120 + N>(x); }
+
+// the sum over the 16 lanes of a row, in each of them
+__device__ __forceinline__ float row_sum16(float x)
+{
+    x += row_ror<8>(x);
+    x += row_ror<4>(x);
+    x += row_ror<2>(x);
+    return x + row_ror<1>(x);
+}
+// the sum over each aligned group of 8 lanes, in each of them
+__device__ __forceinline__ float group_sum8(float x)
+{
+    x += dpp_mov<kDppSwap1>(x);
+    x += dpp_mov<kDppSwap2>(x);
+    return x + dpp_mov<kDppHalfMirror>(x);
+}
+
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
@@ -1166,13 +1195,8 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_grads_kernel(const ChunkBwdAr
             for (int x = 0; x < 4; ++x) {
                 const int r = 16 * m + 4 * g + x;
                 if (r < L) a.dv[e0 + r * rs] = bs[r] * dW[m][x];
-                float p = dW[m][x] * W[m][x];
-                float d = dO[m][x] * U[m][x];  // the diagonal of dP in fp32
-#pragma unroll
-                for (int o = 8; o > 0; o >>= 1) {
-                    p += __shfl_xor(p, o);
-                    d += __shfl_xor(d, o);
-                }
+                const float p = row_sum16(dW[m][x] * W[m][x]);
+                const float d = row_sum16(dO[m][x] * U[m][x]);  // the diagonal of dP in fp32
                 if (l16 == 0) {
                     dbr[wave][r] = p;
                     dpd[wave][r] = d;
@@ -1184,7 +1208,7 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_grads_kernel(const ChunkBwdAr
     // ---- phase B images (natural binding, rows = tokens, k = value columns):
     // dO, -B dW', U.  Even lanes store their value and the odd neighbour's.
     auto put_pair = [&](int off, int r, float x) {
-        const float y = __shfl_xor(x, 1);
+        const float y = dpp_mov<kDppSwap1>(x);
         if ((l16 & 1) == 0) img_put2<false>(img + off, KT_PL, r, col, 4, x, y);
     };
 #pragma unroll
@@ -1475,38 +1499,64 @@ __global__ __launch_bounds__(INTRA_NT, 1) void chunk_intra_kernel(const ChunkBwd
     }
     if (t < CH) bs[t] = t < L ? braw : 0.f;
     lds_sync();
-    const int yi = t >> 3, y0 = 8 * (t & 7);   // this thread's row and first 8 columns
     {
-        // Y = T^T dT: Y_im = sum_{r >= i} T_ri dT_rm
-        float y[8] = {};
-        for (int r = yi; r < CH; ++r) {
-            const float tr = Ts[r * PLD + yi];
-            const float4 d0 = *reinterpret_cast<const float4*>(&Ad[r * PLD + y0]);
-            const float4 d1 = *reinterpret_cast<const float4*>(&Ad[r * PLD + y0 + 4]);
-            y[0] += tr * d0.x; y[1] += tr * d0.y; y[2] += tr * d0.z; y[3] += tr * d0.w;
-            y[4] += tr * d1.x; y[5] += tr * d1.y; y[6] += tr * d1.z; y[7] += tr * d1.w;
+        // Y = T^T dT (Y_im = sum_r T_ri dT_rm) on split-bf16 16x16x32 matrix
+        // instructions: wave w forms the tiles (I, M0) and (I, M0 + 1) with
+        // I = w / 2, M0 = 2 (w mod 2); the operands are read from the fp32
+        // tiles (T^T by columns of T, dT by columns), k = r.
+        const int I = wave >> 1, M0 = 2 * (wave & 1);
+        f32x4 y0 = {0.f, 0.f, 0.f, 0.f}, y1 = y0;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            float ta[8], b0[8], b1[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int r = 32 * ks + 8 * g + j;
+                ta[j] = Ts[r * PLD + 16 * I + l16];
+                b0[j] = Ad[r * PLD + 16 * M0 + l16];
+                b1[j] = Ad[r * PLD + 16 * M0 + 16 + l16];
+            }
+            bf16x8 ah, al, bh, bl;
+            split8(ta, ah, al);
+            split8(b0, bh, bl);
+            y0 = mma3(ah, al, bh, bl, y0);
+            split8(b1, bh, bl);
+            y1 = mma3(ah, al, bh, bl, y1);
         }
         lds_sync();
 #pragma unroll
-        for (int u = 0; u < 8; ++u) Ad[yi * PLD + y0 + u] = y[u];
+        for (int x = 0; x < 4; ++x) {
+            const int i = 16 * I + 4 * g + x;
+            Ad[i * PLD + 16 * M0 + l16] = y0[x];
+            Ad[i * PLD + 16 * M0 + 16 + l16] = y1[x];
+        }
     }
     lds_sync();
     {
-        // dM = -Y T^T: dM_ik = -sum_m Y_im T_km (only k < i is used)
-        float dm[8] = {};
-        if (y0 < yi) {
-            for (int m = 0; m < CH; m += 4) {
-                const float4 yv = *reinterpret_cast<const float4*>(&Ad[yi * PLD + m]);
+        // dM = -Y T^T (dM_ik = -sum_m Y_im T_km; only k < i is used later), the
+        // same tiling with (I, K0) and (I, K0 + 1): A = rows of Y, B = rows of T
+        const int I = wave >> 1, K0 = 2 * (wave & 1);
+        f32x4 m0 = {0.f, 0.f, 0.f, 0.f}, m1 = m0;
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const float4 tv = *reinterpret_cast<const float4*>(&Ts[(y0 + u) * PLD + m]);
-                    dm[u] -= yv.x * tv.x + yv.y * tv.y + yv.z * tv.z + yv.w * tv.w;
-                }
-            }
+        for (int ks = 0; ks < 2; ++ks) {
+            const int c = 32 * ks + 8 * g;
+            const f32x4* ya = reinterpret_cast<const f32x4*>(&Ad[(16 * I + l16) * PLD + c]);
+            const f32x4* t0 = reinterpret_cast<const f32x4*>(&Ts[(16 * K0 + l16) * PLD + c]);
+            const f32x4* t1 = reinterpret_cast<const f32x4*>(&Ts[(16 * K0 + 16 + l16) * PLD + c]);
+            bf16x8 ah, al, bh, bl;
+            bfrag(ya[0], ya[1], ah, al);
+            bfrag(t0[0], t0[1], bh, bl);
+            m0 = mma3(ah, al, bh, bl, m0);
+            bfrag(t1[0], t1[1], bh, bl);
+            m1 = mma3(ah, al, bh, bl, m1);
         }
         lds_sync();
 #pragma unroll
-        for (int u = 0; u < 8; ++u) Ad[yi * PLD + y0 + u] = dm[u];
+        for (int x = 0; x < 4; ++x) {
+            const int i = 16 * I + 4 * g + x;
+            Ad[i * PLD + 16 * K0 + l16] = -m0[x];
+            Ad[i * PLD + 16 * K0 + 16 + l16] = -m1[x];
+        }
     }
     lds_sync();
     {
@@ -1515,9 +1565,7 @@ __global__ __launch_bounds__(INTRA_NT, 1) void chunk_intra_kernel(const ChunkBwd
         float s2 = 0.f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) s2 += k0 + k < r ? Ad[r * PLD + k0 + k] * As[r * PLD + k0 + k] : 0.f;
-        s2 += __shfl_xor(s2, 4);
-        s2 += __shfl_xor(s2, 2);
-        s2 += __shfl_xor(s2, 1);
+        s2 = group_sum8(s2);
         if ((t & 7) == 0) db2[r] = s2;
     }
     lds_sync();
