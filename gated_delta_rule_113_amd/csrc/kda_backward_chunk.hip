@@ -592,10 +592,14 @@ __global__ __launch_bounds__(PREP_NT, 2) void chunk_prep_kernel(const ChunkBwdAr
             for (int jj = 0; jj < 8; ++jj) {
                 const bool ok = !diag || (((jj < 4 ? us.x : us.y) >> (8 * (jj & 3))) & 0xffu) == 0;
                 const float rho = Gs[rho_row * GLD + cc + jj];
-                const float fr = ok ? ex2(Gs[rr * GLD + cc + jj] - rho) : 0.f;
+                // (formed unconditionally, then selected: LDS reads under the
+                // condition would become branches)
+                const float fe = ex2(Gs[rr * GLD + cc + jj] - rho);
+                const float he = (float)ki[jj] * ex2(rho - Gs[ii * GLD + cc + jj]);
+                const float fr = ok ? fe : 0.f;
                 fk[jj] = (float)kr[jj] * fr;
                 fq[jj] = (float)qr[jj] * fr;
-                fh[jj] = ok ? (float)ki[jj] * ex2(rho - Gs[ii * GLD + cc + jj]) : 0.f;
+                fh[jj] = ok ? he : 0.f;
             }
             bf16x8 kh, kl, qh, ql, hh, hl;
             split8(fk, kh, kl);
@@ -1599,80 +1603,66 @@ __global__ __launch_bounds__(INTRA_NT, 1) void chunk_intra_kernel(const ChunkBwd
     // before J (rows in J), and the pairs inside J (explicit).  Every term
     // carries the decay over token j.  Row blocks run last to first, so that
     // a block's dk column sums, Bc and Ab are complete when it is written.
-    // The pairs inside each diagonal block first (their cross sums, per row,
-    // into DgS): X_ri for rows r = 16R + 4g + x and the columns i < r of the
-    // block; c[j] gathers, over this lane's rows r >= j, the row sums over i < j.
-#pragma unroll 1
-    for (int R = 0; R < 4; ++R) {
-        const float rho = Gv(16 * R + 7);
-        const bool safe = Gv(16 * R) - rho <= 96.f && rho - Gv(16 * R + 15) <= 96.f;
-        float kh[4], qf[4], kf[4];
+    // The pairs inside each diagonal block first, into DgS: lane group g takes
+    // the diagonal block R = g of channel cc, all 16 of its rows (no lane
+    // computes a pair above the diagonal, and no sum crosses lanes).  With
+    // a_r = k_r 2^(G_r - rho), c_r = q_r 2^(G_r - rho), b_i = k_i 2^(rho - G_i),
+    // X_ri = (dA_ri a_r + dP_ri c_r) b_i; cs[j] gathers, over the rows r >= j,
+    // the row sums over the columns i < j.
+    __builtin_amdgcn_sched_barrier(0);
+    {
+        const int R = g, r0 = 16 * g;
+        const float rho = Gv(r0 + 7);
+        const bool safe = Gv(r0) - rho <= 96.f && rho - Gv(r0 + 15) <= 96.f;
+        float bcol[16], cs[16];
+        // (values formed unconditionally and then selected: an LDS read under
+        // the condition would become a branch of its own)
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int r = 16 * R + 4 * g + x;   // also the column index of kh
-            const float f = safe ? ex2(Gv(r) - rho) : 0.f;
-            kh[x] = safe ? Kv(r) * ex2(rho - Gv(r)) : 0.f;
-            qf[x] = Qv(r) * f;
-            kf[x] = Kv(r) * f;
+        for (int il = 0; il < 16; ++il) {
+            const float b = Kv(r0 + il) * ex2(rho - Gv(r0 + il));
+            bcol[il] = safe ? b : 0.f;
+            cs[il] = 0.f;
         }
-        float khall[16];
 #pragma unroll
-        for (int gg = 0; gg < 4; ++gg)
-#pragma unroll
-            for (int xx = 0; xx < 4; ++xx) khall[4 * gg + xx] = __shfl(kh[xx], l16 + 16 * gg);
-        float c[16];
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) c[jj] = 0.f;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int rl = 4 * g + x;   // the row within the block
-            const int r = 16 * R + rl;
+        for (int rl = 1; rl < 16; ++rl) {
+            const int r = r0 + rl;
+            const float e = ex2(Gv(r) - rho);
+            const float f = safe ? e : 0.f;
+            const float ar = Kv(r) * f, cr = Qv(r) * f;
+            const float* da = &Ad[r * PLD + r0];
+            const float* dp = &Pd[r * PLD + r0];
             float run = 0.f;
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) {
-                const float4 da = *reinterpret_cast<const float4*>(&Ad[r * PLD + 16 * R + 4 * i4]);
-                const float4 dp = *reinterpret_cast<const float4*>(&Pd[r * PLD + 16 * R + 4 * i4]);
-                const float dav[4] = {da.x, da.y, da.z, da.w};
-                const float dpv[4] = {dp.x, dp.y, dp.z, dp.w};
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int il = 4 * i4 + u;
-                    // (zero for an unsafe channel: kf, qf and kh are)
-                    const float xv = (dav[u] * kf[x] + dpv[u] * qf[x]) * khall[il];
-                    run += il < rl ? xv : 0.f;
-                    if (il + 1 < 16 && il + 1 <= rl) c[il + 1] += run;
-                }
+            for (int il = 0; il < rl; ++il) {
+                run += (da[il] * ar + dp[il] * cr) * bcol[il];
+                cs[il + 1] += run;
             }
+            __builtin_amdgcn_sched_barrier(0);   // one row at a time: bounded register use
         }
         if (__any(!safe)) {
             // the unsafe channels' pairs, with pairwise factors
             if (!safe) {
-                for (int x = 0; x < 4; ++x) {
-                    const int rl = 4 * g + x;
-                    const int r = 16 * R + rl;
+                for (int rl = 1; rl < 16; ++rl) {
+                    const int r = r0 + rl;
                     const float gr = Gv(r), kr = Kv(r), qr = Qv(r);
                     float run = 0.f;
 #pragma unroll
-                    for (int il = 0; il + 1 < 16; ++il) {
+                    for (int il = 0; il < 15; ++il) {
                         if (il < rl) {
-                            const int i = 16 * R + il;
+                            const int i = r0 + il;
                             run += (Ad[r * PLD + i] * kr + Pd[r * PLD + i] * qr) * Kv(i) * ex2(gr - Gv(i));
+                            cs[il + 1] += run;
                         }
-                        if (il + 1 <= rl) c[il + 1] += run;
                     }
                 }
             }
         }
+        // to the thread that finalises row j = 16 R + jl: lane group jl / 4, slot 4 R + jl mod 4
 #pragma unroll
-        for (int jj = 1; jj < 16; ++jj) {
-            c[jj] += __shfl_xor(c[jj], 16);
-            c[jj] += __shfl_xor(c[jj], 32);
-        }
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-            DgS[(4 * R + x) * INTRA_NT + t] = g == 0 ? c[x] : g == 1 ? c[4 + x] : g == 2 ? c[8 + x] : c[12 + x];
+        for (int jl = 0; jl < 16; ++jl)
+            DgS[(4 * R + (jl & 3)) * INTRA_NT + 64 * wave + 16 * (jl >> 2) + l16] = cs[jl];
     }
-
+    __builtin_amdgcn_sched_barrier(0);
     request_partials(3);
     f32x4 dkc[4];
     float Bc[4][4], Ab[4];
@@ -1702,8 +1692,9 @@ __global__ __launch_bounds__(INTRA_NT, 1) void chunk_intra_kernel(const ChunkBwd
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 const int i = 16 * I + 4 * g + x;
-                f[x] = safe ? ex2(gR[x] - rho) : 0.f;
-                hh[x] = safe ? ex2(rho - Gv(i)) : 0.f;
+                const float fe = ex2(gR[x] - rho), he = ex2(rho - Gv(i));
+                f[x] = safe ? fe : 0.f;
+                hh[x] = safe ? he : 0.f;
                 kI[x] = Kv(i);
                 kh[x] = kI[x] * hh[x];
                 qf[x] = qR[x] * f[x];
