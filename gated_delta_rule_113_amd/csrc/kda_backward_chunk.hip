@@ -177,6 +177,56 @@ __device__ __forceinline__ void state_store(float* dst, uint32_t lo, const f32x4
         for (int x = 0; x < 4; ++x) at(dst + (16 * tt + x) * kDim, lo) = X[tt][x];
 }
 
+// Chunk intermediates parked by the state sweeps in a [rows][H][128] fp32
+// buffer, for lane (column col, lane group g) and row block m, rows
+// 16 m + 4 g + x.  In a full chunk the four values of one column go to one
+// 16-byte slot: rows 4q .. 4q + 3 (q = 4 m + g) of column c are kept at row
+// 4q + c / 32, columns 4 (c mod 32) .. + 3 (a permutation inside the four
+// rows, so one vector store or load per group instead of four).  A partial
+// chunk keeps every row r < L at its own place.  `base` points at the
+// chunk's first row for this head; rs is the row stride in floats.
+__device__ __forceinline__ void park4(float* base, uint32_t rs, int m, int g, int col, int L, f32x4 v)
+{
+    if (L == CH) {
+        const uint32_t lo = (4 * g + (col >> 5)) * rs + 4 * (col & 31);
+        at(reinterpret_cast<f32x4*>(base + 16 * m * rs), lo >> 2) = v;
+    } else {
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+            if (16 * m + 4 * g + x < L) at(base + (16 * m + x) * rs, 4 * g * rs + col) = v[x];
+    }
+}
+// All four row blocks of a lane (one branch for the four).
+__device__ __forceinline__ void park_all(float* base, uint32_t rs, int g, int col, int L, const f32x4 (&v)[4])
+{
+    if (L == CH) {
+        const uint32_t lo = ((4 * g + (col >> 5)) * rs + 4 * (col & 31)) >> 2;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) at(reinterpret_cast<f32x4*>(base + 16 * m * rs), lo) = v[m];
+    } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+                if (16 * m + 4 * g + x < L) at(base + (16 * m + x) * rs, 4 * g * rs + col) = v[m][x];
+    }
+}
+// The parked group back (rows from L on read row 0: to be replaced where used).
+__device__ __forceinline__ f32x4 unpark4(const float* base, uint32_t rs, int m, int g, int col, int L)
+{
+    if (L == CH) {
+        const uint32_t lo = (4 * g + (col >> 5)) * rs + 4 * (col & 31);
+        return at(reinterpret_cast<const f32x4*>(base + 16 * m * rs), lo >> 2);
+    }
+    f32x4 v;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        const int r = 16 * m + 4 * g + x;
+        v[x] = at(base, (r < L ? r : 0) * rs + col);
+    }
+    return v;
+}
+
 // The wave's index in the workgroup, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
@@ -413,19 +463,13 @@ __device__ __forceinline__ void stage(const ChunkBwdArgs& a, int64_t row0c, int 
     stage_raw<NT, WITHQ>(p, tot, s);
 }
 
-// beta of the chunk's row t mod 64, loaded without a branch (a row from L on
-// reads row 0: its value is to be replaced by zero where it is used);
-// stage_beta stores the chunk's beta into LDS by the first 64 threads
-__device__ __forceinline__ float beta_raw(const ChunkBwdArgs& a, int64_t row0c, int L, int h)
+// beta of the chunk's row t mod 64 as raw bits, loaded without a branch (a
+// row from L on reads row 0: its value is to be replaced by zero where it is
+// used), to be widened where it is staged
+__device__ __forceinline__ bf16_t beta_raw(const ChunkBwdArgs& a, int64_t row0c, int L, int h)
 {
     const int t = threadIdx.x & (CH - 1);
-    return widen(a.beta[(row0c + (t < L ? t : 0)) * a.H + h]);
-}
-__device__ __forceinline__ void stage_beta(const ChunkBwdArgs& a, int64_t row0c, int L, int h, float* bs)
-{
-    const float b = beta_raw(a, row0c, L, h);
-    const int t = threadIdx.x;
-    if (t < CH) bs[t] = t < L ? b : 0.f;
+    return a.beta[(row0c + (t < L ? t : 0)) * a.H + h];
 }
 
 // A 64 x 64 fp32 tile from global memory into an image: TRANS = false stores
@@ -544,9 +588,10 @@ __global__ __launch_bounds__(PREP_NT, 2) void chunk_prep_kernel(const ChunkBwdAr
     const int t = threadIdx.x, lane = t & 63, wave = wave_id(), g = lane >> 4, l16 = lane & 15;
 
     {
+        const bf16_t braw = beta_raw(a, row0c, L, h);   // in flight with the staging loads
         Staged<PREP_NT> st;
         stage<PREP_NT, true>(a, row0c, L, h, tot, st);
-        stage_beta(a, row0c, L, h, bs);
+        if (t < CH) bs[t] = t < L ? widen(braw) : 0.f;
 #pragma unroll
         for (int j = 0; j < Staged<PREP_NT>::TOK; ++j) {
             const int r = st.r0 + j;
@@ -752,7 +797,7 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_states_kernel(const ChunkBwdA
     ChunkRaw<SEQ_NT, false> raw;
     TileRaw<SEQ_NT> traw;
     uint32_t vraw[16];
-    float braw = 0.f;
+    bf16_t braw = {0};   // raw bits, widened where staged (widening here would wait for the load)
     auto request_chunk = [&](int64_t c) {
         const int64_t row0c = row0 + c * CH;
         const int L = static_cast<int>(min<int64_t>(CH, len - c * CH));
@@ -770,14 +815,17 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_states_kernel(const ChunkBwdA
                 const int r = 16 * m + 4 * g + x;
                 vraw[4 * m + x] = at(vb, col + static_cast<uint32_t>(min(r, L - 1)) * rs).bits;
             }
-        braw = widen(at(a.beta + row0c * H + h, static_cast<uint32_t>(min(t, L - 1)) * H));
+        braw = at(a.beta + row0c * H + h, static_cast<uint32_t>(min(t, L - 1)) * H);
     };
     if (nch > 0) request_chunk(0);
 
-    for (int64_t c = 0; c < nch; ++c) {
+    // one chunk step; FULL: a chunk of 64 rows (every chunk but a sequence's
+    // last), compiled apart so that its parking takes no branches
+    auto step = [&](const int64_t c, auto full) {
+        constexpr bool FULL = decltype(full)::value;
         const int64_t id = chunk_id(row0, n, c);
         const int64_t row0c = row0 + c * CH;
-        const int L = static_cast<int>(min<int64_t>(CH, len - c * CH));
+        const int L = FULL ? CH : static_cast<int>(min<int64_t>(CH, len - c * CH));
         lds_sync();  // the previous chunk's products are done with the images
         tile_put<false, SEQ_NT>(traw, TI);
 #pragma unroll
@@ -789,7 +837,7 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_states_kernel(const ChunkBwdA
                                vraw[4] | (vraw[5] << 16), vraw[6] | (vraw[7] << 16));
         VS[2 * t + 1] = make_uint4(vraw[8] | (vraw[9] << 16), vraw[10] | (vraw[11] << 16),
                                    vraw[12] | (vraw[13] << 16), vraw[14] | (vraw[15] << 16));
-        if (t < CH) bs[t] = t < L ? braw : 0.f;
+        if (t < CH) bs[t] = t < L ? widen(braw) : 0.f;
         Staged<SEQ_NT> st;
         stage_raw<SEQ_NT, false>(raw, tot, st);
 #pragma unroll
@@ -810,13 +858,14 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_states_kernel(const ChunkBwdA
             gls[st.c0] = ex2(st.gl[0]);
             gls[st.c0 + 1] = ex2(st.gl[1]);
         }
-        // checkpoint S0 (before the next chunk's requests, so that waiting for
-        // those does not wait for these stores)
-        state_store(a.ws_s0 + (id * H + h) * SS, slo, S);
         lds_sync();
         if (c + 1 < nch) request_chunk(c + 1);
 
-        // X = Kt S0 (sum over channels: B from S, 4 steps)
+        // X = Kt S0 (sum over channels: B from S, 4 steps).  The checkpoint of
+        // S0 is stored alongside, two row tiles per step, after the requests:
+        // the stores' issue overlaps the products, and waiting for the
+        // requests (loads and stores complete in order) does not wait for them.
+        float* s0dst = a.ws_s0 + (id * H + h) * SS;
         f32x4 X[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) X[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -830,23 +879,29 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_states_kernel(const ChunkBwdA
                 img_frag(KT, KT_PL, m * 4 + s, lane, ah, al);
                 X[m] = mma3(ah, al, bh, bl, X[m]);
             }
+#pragma unroll
+            for (int tt = 2 * s; tt < 2 * s + 2; ++tt)
+#pragma unroll
+                for (int x = 0; x < 4; ++x) at(s0dst + (16 * tt + x) * kDim, slo) = S[tt][x];
         }
         // W = V - X (parked in dk for the grads kernel), then B W
         {
             const uint4 v0 = VS[2 * t], v1 = VS[2 * t + 1];
             const uint32_t vw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
             float* wdst = a.dk + (row0c * H + h) * kDim;
-            const uint32_t rs = H * kDim, lo = col + 4 * g * rs;
+            const uint32_t rs = H * kDim;
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
+            for (int m = 0; m < 4; ++m) {
+                f32x4 w;
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
-                    const int e = 4 * m + x, r = 16 * m + 4 * g + x;
+                    const int e = 4 * m + x;
                     const float v = (e & 1) ? bf_hi(vw[e >> 1]) : bf_lo(vw[e >> 1]);
-                    const float w = v - X[m][x];
-                    if (r < L) at(wdst + (16 * m + x) * rs, lo) = w;
-                    X[m][x] = bs[r] * w;
+                    w[x] = v - X[m][x];
+                    X[m][x] = bs[16 * m + 4 * g + x] * w[x];
                 }
+                park4(wdst, rs, m, g, col, L, w);
+            }
         }
         // U = T (B W) (sum over tokens: 2 steps)
         f32x4 U[4];
@@ -866,14 +921,9 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_states_kernel(const ChunkBwdA
         // U (parked in dq for the grads kernel), then S1 = Diag(gam_L) S0 + Ke^T U
         {
             float* udst = a.dq + (row0c * H + h) * kDim;
-            const uint32_t rs = H * kDim, lo = col + 4 * g * rs;
+            const uint32_t rs = H * kDim;
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const int r = 16 * m + 4 * g + x;
-                    if (r < L) at(udst + (16 * m + x) * rs, lo) = U[m][x];
-                }
+            for (int m = 0; m < 4; ++m) park4(udst, rs, m, g, col, L, U[m]);
         }
         bf16x8 uh[2], ul[2];
 #pragma unroll
@@ -889,7 +939,11 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_states_kernel(const ChunkBwdA
                 S[tt] = mma3(ah, al, uh[s], ul[s], S[tt]);
             }
         }
-    }
+    };
+    // the full chunks in a loop of their own; a partial last chunk after it
+    const int64_t nfull = len / CH;
+    for (int64_t c = 0; c < nfull; ++c) step(c, std::true_type{});
+    if (nfull < nch) step(nfull, std::false_type{});
 }
 
 // ================================================================ dstate
@@ -927,7 +981,7 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_dstate_kernel(const ChunkBwdA
     ChunkRaw<SEQ_NT, true> raw;
     TileRaw<SEQ_NT> praw, traw;
     f32x4 oraw[4];
-    float braw = 0.f;
+    bf16_t braw = {0};   // raw bits, widened where staged (widening here would wait for the load)
     auto request_chunk = [&](int64_t c) {
         const int64_t row0c = row0 + c * CH;
         const int L = static_cast<int>(min<int64_t>(CH, len - c * CH));
@@ -946,18 +1000,21 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_dstate_kernel(const ChunkBwdA
                 const int r = 16 * m + 4 * g + x;
                 oraw[m][x] = at(ob, col + static_cast<uint32_t>(min(r, L - 1)) * rs);
             }
-        braw = widen(at(a.beta + row0c * H + h, static_cast<uint32_t>(min(t, L - 1)) * H));
+        braw = at(a.beta + row0c * H + h, static_cast<uint32_t>(min(t, L - 1)) * H);
     };
     if (nch > 0) request_chunk(nch - 1);
 
-    for (int64_t c = nch - 1; c >= 0; --c) {
+    // one chunk step; FULL: a chunk of 64 rows (every chunk but a sequence's
+    // last), compiled apart so that its parking takes no branches
+    auto step = [&](const int64_t c, auto full) {
+        constexpr bool FULL = decltype(full)::value;
         const int64_t id = chunk_id(row0, n, c);
         const int64_t row0c = row0 + c * CH;
-        const int L = static_cast<int>(min<int64_t>(CH, len - c * CH));
+        const int L = FULL ? CH : static_cast<int>(min<int64_t>(CH, len - c * CH));
         lds_sync();
         tile_put<true, SEQ_NT>(praw, PT);
         tile_put<true, SEQ_NT>(traw, TT);
-        if (t < CH) bs[t] = t < L ? braw : 0.f;
+        if (t < CH) bs[t] = t < L ? widen(braw) : 0.f;
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -992,8 +1049,10 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_dstate_kernel(const ChunkBwdA
             gls[st.c0] = ex2(st.gl[0]);
             gls[st.c0 + 1] = ex2(st.gl[1]);
         }
-        // the gradient in this chunk's leaving state (before the next requests,
-        // so that waiting for those does not wait for these stores)
+        // the gradient in this chunk's leaving state, stored before the next
+        // chunk's requests: a wave keeps at most 63 memory instructions in
+        // flight, and these stores issued after the requests would have to
+        // wait for the requests' data to make room
         state_store(a.ws_ds + (id * H + h) * SS, slo, dS);
         lds_sync();
         if (c > 0) request_chunk(c - 1);
@@ -1043,18 +1102,13 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_dstate_kernel(const ChunkBwdA
         __builtin_amdgcn_sched_barrier(0);
         {
             const int64_t base = (row0c * H + h) * kDim;
-            const uint32_t rs = H * kDim, lo = col + 4 * g * rs;
+            const uint32_t rs = H * kDim;
+            park_all(a.dla + base, rs, g, col, L, dU);
+            park_all(a.dv + base, rs, g, col, L, nW);
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const int r = 16 * m + 4 * g + x;
-                    if (r < L) {
-                        at(a.dla + base + (16 * m + x) * rs, lo) = dU[m][x];
-                        at(a.dv + base + (16 * m + x) * rs, lo) = nW[m][x];
-                    }
-                    nW[m][x] *= -bs[r];
-                }
+                for (int x = 0; x < 4; ++x) nW[m][x] *= -bs[16 * m + 4 * g + x];
         }
         __builtin_amdgcn_sched_barrier(0);
         // dS0 = Diag(gam_L) dS1 + Qt^T dO - Kt^T B dW'
@@ -1075,7 +1129,12 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_dstate_kernel(const ChunkBwdA
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-    }
+    };
+    // a partial last chunk (the first in this order) before the loop over
+    // the full ones
+    const int64_t nfull = len / CH;
+    if (nfull < nch) step(nfull, std::false_type{});
+    for (int64_t c = nfull - 1; c >= 0; --c) step(c, std::true_type{});
     if (a.ds0) state_store(a.ds0 + (n * H + h) * SS, slo, dS);
 }
 
@@ -1122,22 +1181,25 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_grads_kernel(const ChunkBwdAr
     // were parked in dq, dk, d log alpha and dv by the state sweeps.
     ChunkRaw<SEQ_NT, true> raw;
     request<SEQ_NT, true>(a, row0c, L, h, raw);
-    const float braw = beta_raw(a, row0c, L, h);
+    const bf16_t braw = beta_raw(a, row0c, L, h);
     f32x4 U[4], dU[4], dW[4], W[4], dO[4];
     const int64_t e0 = (row0c * H + h) * kDim + col;
+    {
+        const int64_t pb = (row0c * H + h) * kDim;
+        const uint32_t prs = static_cast<uint32_t>(rs);
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+        for (int m = 0; m < 4; ++m) {
+            U[m] = unpark4(a.dq + pb, prs, m, g, col, L);
+            W[m] = unpark4(a.dk + pb, prs, m, g, col, L);
+            dU[m] = unpark4(a.dla + pb, prs, m, g, col, L);
+            dW[m] = unpark4(a.dv + pb, prs, m, g, col, L);
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int r = 16 * m + 4 * g + x;
-            const bool in = r < L;
-            const int64_t e = e0 + (in ? r : 0) * rs;
-            U[m][x] = a.dq[e];
-            W[m][x] = a.dk[e];
-            dU[m][x] = a.dla[e];
-            dW[m][x] = a.dv[e];
-            dO[m][x] = a.d_o[e];
+            for (int x = 0; x < 4; ++x) {
+                const int r = 16 * m + 4 * g + x;
+                dO[m][x] = a.d_o[e0 + (r < L ? r : 0) * rs];
+            }
         }
+    }
     // this lane's row cw = col of S0 and dS1, columns 32 s + 8 g .. + 7
     float4 s0r[8], dsr[8];
     {
@@ -1166,7 +1228,7 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_grads_kernel(const ChunkBwdAr
     {
         Staged<SEQ_NT> st;
         stage_raw<SEQ_NT, true>(raw, tot, st);
-        if (t < CH) bs[t] = t < L ? braw : 0.f;
+        if (t < CH) bs[t] = t < L ? widen(braw) : 0.f;
 #pragma unroll
         for (int j = 0; j < Staged<SEQ_NT>::TOK; ++j) {
             const int r = st.r0 + j;
@@ -1470,7 +1532,7 @@ __global__ __launch_bounds__(INTRA_NT, 1) void chunk_intra_kernel(const ChunkBwd
             dr[j] = dpt[TSZ + e];
         }
     }
-    const float braw = beta_raw(a, row0c, L, h);
+    const bf16_t braw = beta_raw(a, row0c, L, h);
     ChunkRaw<INTRA_NT, true> raw;
     request<INTRA_NT, true>(a, row0c, L, h, raw);
     // the grads kernel's terms of dq, dk and d log a for the rows of one
@@ -1501,7 +1563,7 @@ __global__ __launch_bounds__(INTRA_NT, 1) void chunk_intra_kernel(const ChunkBwd
         Pd[r * PLD + i] = i <= r ? pr[j] : 0.f;   // (only the lower blocks were written)
         Ad[r * PLD + i] = i < r ? dr[j] : 0.f;
     }
-    if (t < CH) bs[t] = t < L ? braw : 0.f;
+    if (t < CH) bs[t] = t < L ? widen(braw) : 0.f;
     lds_sync();
     {
         // Y = T^T dT (Y_im = sum_r T_ri dT_rm) on split-bf16 16x16x32 matrix
