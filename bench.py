@@ -778,10 +778,12 @@ def time_backward(kda, ki, torch, np, dev, up, stream, reps, result):
         "forward_ms_same_inputs": fms,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_launch": nbytes,
+                     "traffic": measured_traffic("backward_B8_T4096_H32_hbm_traffic.json", "backward_call"),
                      "mfma_algorithmic_tflops": tf, "mfma_frac": tf / BF16_MFMA_PEAK_TFLOPS,
                      "algorithmic_flops_per_launch": flops,
                      "note": "the chunked backward (five kernels); algorithmic bytes = inputs read "
-                             "and gradients written once; the workspace round trips are not counted"},
+                             "and gradients written once; traffic = the measured HBM bytes of one call "
+                             "(its workspace round trips included)"},
     }
     del q, k, v, b, la, do, ds
 
