@@ -1153,15 +1153,27 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_dstate_kernel(const ChunkBwdA
 //   d log a (the intra kernel adds the cross sums); dP = dO U^T (lower blocks).
 // Phase C: dT = dU (B W)^T (lower blocks) from images of dU and B W.
 
-__global__ __launch_bounds__(SEQ_NT, 1) void chunk_grads_kernel(const ChunkBwdArgs a)
+constexpr int GR_KT_PL = CH * kDim * 2;
+// LDS of the gradient part (phase B: dO | -B dW' | U;  phase C: dU | B W)
+struct GradsLds {
+    char img[6 * GR_KT_PL];
+    float Gs[CH * GLD];
+    float tot[(SEQ_NT / 64) * kDim];
+    float bs[CH], gLs[kDim], dbr[SEQ_NT / 64][CH], dpd[SEQ_NT / 64][CH];
+};
+
+__device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm)
 {
-    constexpr int KT_PL = CH * kDim * 2;
-    // phase B: dO | -B dW' | U;  phase C: dU | B W
-    constexpr int OFF_I0 = 0, OFF_I1 = 2 * KT_PL, OFF_I2 = 4 * KT_PL, REGION = 6 * KT_PL;
-    __shared__ __attribute__((aligned(16))) char img[REGION];
-    __shared__ __attribute__((aligned(16))) float Gs[CH * GLD];
-    __shared__ float tot[(SEQ_NT / 64) * kDim];
-    __shared__ float bs[CH], gLs[kDim], dbr[SEQ_NT / 64][CH], dpd[SEQ_NT / 64][CH];
+    constexpr int KT_PL = GR_KT_PL;
+    constexpr int OFF_I0 = 0, OFF_I1 = 2 * KT_PL, OFF_I2 = 4 * KT_PL;
+    GradsLds& S_ = *reinterpret_cast<GradsLds*>(sm);
+    char* img = S_.img;
+    float* Gs = S_.Gs;
+    float* tot = S_.tot;
+    float* bs = S_.bs;
+    float* gLs = S_.gLs;
+    float (*dbr)[CH] = S_.dbr;
+    float (*dpd)[CH] = S_.dpd;
 
     const int H = a.H;
     const int64_t id = blockIdx.x / H;
@@ -1492,15 +1504,29 @@ __device__ __forceinline__ void split4(float x0, float x1, float x2, float x3, i
     l = __builtin_bit_cast(i16x4, (uint2){l0, l1});
 }
 
-__global__ __launch_bounds__(INTRA_NT, 1) void chunk_intra_kernel(const ChunkBwdArgs a)
+// LDS of the intra-chunk part
+struct IntraLds {
+    float Pd[CH * PLD];       // dP (i <= r)
+    float Ad[CH * PLD];       // dT, Y, dM, then dA
+    float U1[2 * CH * PLD];   // T and A, then G
+    __bf16 Ks[CH * kDim];
+    __bf16 Qs[CH * kDim];
+    float bs[CH], db2[CH], tot[(INTRA_NT / 64) * kDim];
+    float DgS[16 * INTRA_NT];   // per thread: the cross sums inside the diagonal blocks
+};
+
+__device__ __forceinline__ void intra_part(const ChunkBwdArgs& a, char* sm)
 {
-    __shared__ __attribute__((aligned(16))) float Pd[CH * PLD];       // dP (i <= r)
-    __shared__ __attribute__((aligned(16))) float Ad[CH * PLD];       // dT, Y, dM, then dA
-    __shared__ __attribute__((aligned(16))) float U1[2 * CH * PLD];   // T and A, then G
-    __shared__ __attribute__((aligned(16))) __bf16 Ks[CH * kDim];
-    __shared__ __attribute__((aligned(16))) __bf16 Qs[CH * kDim];
-    __shared__ float bs[CH], db2[CH], tot[(INTRA_NT / 64) * kDim];
-    __shared__ float DgS[16 * INTRA_NT];   // per thread: the cross sums inside the diagonal blocks
+    IntraLds& S_ = *reinterpret_cast<IntraLds*>(sm);
+    float* Pd = S_.Pd;
+    float* Ad = S_.Ad;
+    float* U1 = S_.U1;
+    __bf16* Ks = S_.Ks;
+    __bf16* Qs = S_.Qs;
+    float* bs = S_.bs;
+    float* db2 = S_.db2;
+    float* tot = S_.tot;
+    float* DgS = S_.DgS;
     static_assert(CH * kDim <= 2 * CH * PLD, "G fits where T and A were");
     float* Ts = U1;
     float* As = U1 + CH * PLD;
@@ -1876,6 +1902,23 @@ __global__ __launch_bounds__(INTRA_NT, 1) void chunk_intra_kernel(const ChunkBwd
     if (t < L) a.dbeta[(row0c + t) * H + h] += db2[t];
 }
 
+// The gradient part and then the intra-chunk part of one chunk of one head
+// (grid: chunk ids x heads; 512 threads).  The intra part reads back, from
+// global memory, what the gradient part of the same workgroup wrote there:
+// the partial dq, dk and d log alpha (each by the thread that wrote it) and
+// dP, dT (by other waves, after the barrier), which mostly hit in cache.
+constexpr size_t kGiLds = sizeof(GradsLds) > sizeof(IntraLds) ? sizeof(GradsLds) : sizeof(IntraLds);
+static_assert(kGiLds <= 160 * 1024, "LDS budget of one CU");
+static_assert(INTRA_NT == SEQ_NT, "one workgroup shape for both parts");
+
+__global__ __launch_bounds__(SEQ_NT, 1) void chunk_grads_kernel(const ChunkBwdArgs a)
+{
+    __shared__ __attribute__((aligned(16))) char sm[kGiLds];
+    grads_part(a, sm);
+    __syncthreads();   // global writes of the gradient part visible to the workgroup; LDS free
+    intra_part(a, sm);
+}
+
 }  // namespace
 
 // the workspace the plan sizes: entering state, leaving-state gradient, A/P/T
@@ -1938,10 +1981,6 @@ hipError_t launch_backward_chunked(const void* q, const void* k, const void* v, 
     hipLaunchKernelGGL(chunk_grads_kernel, chunks, dim3(SEQ_NT), 0, stream, a);
     e = hipGetLastError();
     report("backward gradient launch", e);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(chunk_intra_kernel, chunks, dim3(INTRA_NT), 0, stream, a);
-    e = hipGetLastError();
-    report("backward intra-chunk launch", e);
     return e;
 }
 
