@@ -40,14 +40,29 @@
 // by the id floor(row0 / 64) + sequence + chunk, unique and below rows / 64 +
 // sequences + 1, so dense and packed input share one workspace layout):
 //   prep   (one workgroup per chunk)  A, P and T of every chunk;
-//   states (one per unit, in order)   the entering state S0 of every chunk;
+//   states (one per unit, in order)   the entering state S0 of every chunk, and
+//                                     W and U, parked in dk and dq;
 //   dstate (one per unit, reversed)   the gradient dS1 in every chunk's leaving
-//                                     state, and the initial-state gradient;
-//   grads  (one per chunk)            dV, the S0/dS1 parts of dq, dk and dL,
-//                                     db's first term, dP and dT;
-//   intra  (one per chunk)            dM, dA, db's second term, the decay
-//                                     products and their cross sums, the
-//                                     A/P part of d log a.
+//                                     state, dU and dW' (parked in d log a and
+//                                     dv), and the initial-state gradient;
+//   grads  (one per chunk)            first the gradient part: dV, the S0/dS1
+//                                     parts of dq, dk and dL, db's first term,
+//                                     dP and dT; then the intra-chunk part: dM,
+//                                     dA, db's second term, the decay products
+//                                     and their cross sums, the A/P part of
+//                                     d log a, and the totals.
+// The parked intermediates use the gradient buffers as scratch: each chunk's
+// rows of its own head, written by a sweep and read back by the grads kernel
+// of the same chunk before it writes the gradients there.
+//
+// Memory instructions follow a few rules that the timings showed to matter on
+// this hardware: all global loads of a phase are issued before its first
+// store and before the first use of any of them (loads and stores retire in
+// order, so a wait for a load also waits for every earlier store); no load
+// sits under a condition and no loaded value is converted or selected right
+// after its load (either makes the compiler wait for the data on the spot);
+// and a wave keeps at most 63 memory instructions in flight, so stores that
+// would follow a chunk's requests are issued before them.
 //
 // Matrix products run on v_mfma_f32_16x16x32_bf16 with every operand split
 // into hi + lo bf16 (hi*hi + hi*lo + lo*hi, fp32 accumulation), as in the
@@ -60,10 +75,9 @@
 //
 // Decay factors never overflow: in the off-diagonal 16 x 16 blocks (rows r in
 // block R, columns i in an earlier block) 2^(G_r - G_i) is split at the last
-// token of block R - 1 into two factors <= 1.  Inside the diagonal blocks the
-// prep kernel forms it pairwise, 2^(G_r - G_i) <= 1; the intra kernel splits it
-// at the block's 8th token where both factors stay within 2^96 and forms it
-// pairwise for the other channels.
+// token of block R - 1 into two factors <= 1.  Inside the diagonal blocks it
+// is split at the block's 8th token where both factors stay within 2^96, and
+// formed pairwise on the vector ALUs for the other channels.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -1138,9 +1152,9 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_dstate_kernel(const ChunkBwdA
     if (a.ds0) state_store(a.ds0 + (n * H + h) * SS, slo, dS);
 }
 
-// ================================================================ grads
+// ================================================================ grads: gradient part
 //
-// Per chunk of one head (grid: chunk ids x heads; 512 threads).
+// Per chunk of one head (512 threads; the first part of the grads kernel).
 // Phase A, wave w on value columns 16w..16w+15 (accumulator layout): U and
 // W = V - Kt S0 (parked in dq and dk by the states kernel), dU and dW' = T^T dU
 // (parked in d log alpha and dv by the dstate kernel), dO;
@@ -1150,7 +1164,7 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_dstate_kernel(const ChunkBwdA
 // the workspaces as B operands):
 //   dQt = dO S0^T, dKt = -B dW' S0^T, dKe = U dS1^T, dgam_L = rowsum(dS1 (.) S0);
 //   writes dq = dQt gam, dk = dKt gam + dKe gam_L / gam and the S0 part of
-//   d log a (the intra kernel adds the cross sums); dP = dO U^T (lower blocks).
+//   d log a (the intra-chunk part adds the cross sums); dP = dO U^T (lower blocks).
 // Phase C: dT = dU (B W)^T (lower blocks) from images of dU and B W.
 
 constexpr int GR_KT_PL = CH * kDim * 2;
@@ -1466,10 +1480,10 @@ __device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm)
     }
 }
 
-// ================================================================ intra
+// ================================================================ grads: intra-chunk part
 //
-// Per chunk of one head (grid: chunk ids x heads; 512 threads).
-// Phase 1:  dM = -T^T dT T^T,  dA = B dM (i < r),  db_r += sum_{i<r} dM_ri A_ri.
+// Per chunk of one head (512 threads; the second part of the grads kernel).
+// Phase 1 (on split-bf16 matrix instructions):  dM = -T^T dT T^T,  dA = B dM (i < r),  db_r += sum_{i<r} dM_ri A_ri.
 // Phase 2, wave w on channels 16w..16w+15: the decay products of dP and dA,
 //   dq_r  = sum_{i<=r} dP_ri k_i 2^(G_r - G_i),   dk_r += sum_{i<r} dA_ri k_i 2^(G_r - G_i),
 //   dk_i += sum_{r>=i} (dP_ri q_r + dA_ri k_r) 2^(G_r - G_i),
