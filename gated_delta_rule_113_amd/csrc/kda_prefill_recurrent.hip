@@ -94,7 +94,7 @@ __global__ __launch_bounds__(256) void prefill_recurrent_kernel(
         if (tid < TB && t0 + tid < len) sb[buf][tid] = RAW ? sigmoid_gate(widen(xb)) : widen(xb);
     };
 
-    request(0);
+    if (len > 0) request(0);   // (its loads read token 0, which an empty sequence does not have)
     float4 s[16];
     if (const float* S0 = init_state_of(st, n, h, H)) {
 #pragma unroll
