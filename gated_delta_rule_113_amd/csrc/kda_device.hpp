@@ -65,8 +65,11 @@ __device__ __forceinline__ float log2_alpha_from_logit(float a)
     const float t = a * 1.4426950408889634f;
     const float y = __builtin_amdgcn_exp2f(-fabsf(t));
     const float u = 1.f + y;
-    const float l = u == 1.f ? y * 1.4426950408889634f
-                             : __builtin_amdgcn_logf(u) * (y * __builtin_amdgcn_rcpf(u - 1.f));
+    // both forms, then a select: a conditional expression with the logarithm
+    // in one arm is compiled as a branch around it
+    const float tiny = y * 1.4426950408889634f;
+    const float rest = __builtin_amdgcn_logf(u) * (y * __builtin_amdgcn_rcpf(u - 1.f));
+    const float l = u == 1.f ? tiny : rest;
     return -(fmaxf(t, 0.f) + l);
 }
 

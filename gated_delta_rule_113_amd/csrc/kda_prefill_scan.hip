@@ -612,9 +612,12 @@ __device__ __forceinline__ void scan_segment(const ScanArgs& a, char* sm, bool p
                 const float4 x = pla[m];
                 if (a.raw) {
                     // gate logits; rows past the chunk's end keep a zero log-decay
-                    if (4 * tg + m < L)
-                        run = make_float4(run.x + log2_alpha_from_logit(x.x), run.y + log2_alpha_from_logit(x.y),
-                                          run.z + log2_alpha_from_logit(x.z), run.w + log2_alpha_from_logit(x.w));
+                    // (formed for every row, then selected: no branch)
+                    const float4 ga = make_float4(log2_alpha_from_logit(x.x), log2_alpha_from_logit(x.y),
+                                                  log2_alpha_from_logit(x.z), log2_alpha_from_logit(x.w));
+                    const bool in = 4 * tg + m < L;
+                    run = make_float4(run.x + (in ? ga.x : 0.f), run.y + (in ? ga.y : 0.f),
+                                      run.z + (in ? ga.z : 0.f), run.w + (in ? ga.w : 0.f));
                 } else {
                     run = make_float4(run.x + x.x * kLog2e, run.y + x.y * kLog2e, run.z + x.z * kLog2e,
                                       run.w + x.w * kLog2e);
