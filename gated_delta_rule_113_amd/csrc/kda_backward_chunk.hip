@@ -539,6 +539,26 @@ __device__ __forceinline__ void tile_image(const float* src, char* img)
     tile_put<TRANS, NT>(p, img);
 }
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// hi*hi + hi*lo + lo*hi on the 16x16x16 bf16 instruction
+__device__ __forceinline__ f32x4 mma16(i16x4 ah, i16x4 al, i16x4 bh, i16x4 bl, f32x4 c)
+{
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, c, 0, 0, 0);
+    return c;
+}
+
+__device__ __forceinline__ void split4(float x0, float x1, float x2, float x3, i16x4& h, i16x4& l)
+{
+    uint32_t h0, l0, h1, l1;
+    split2(x0, x1, h0, l0);
+    split2(x2, x3, h1, l1);
+    h = __builtin_bit_cast(i16x4, (uint2){h0, h1});
+    l = __builtin_bit_cast(i16x4, (uint2){l0, l1});
+}
+
 // ================================================================ prep
 //
 // A, P and T of one chunk of one head (grid: chunk ids x heads; 256 threads,
@@ -551,8 +571,9 @@ __device__ __forceinline__ void tile_image(const float* src, char* img)
 // T = (I + B A)^-1: its diagonal blocks by forward substitution (one wave per
 // block, lane = (column, row quarter), quad sums over the lanes of a column),
 // its off-diagonal blocks as T_RI = -T_RR sum_{I <= J < R} N_RJ T_JI in order
-// of R - I (N = B A).  G, k and q live in LDS only until the A/P products are
-// done; A, P and T then take their place.
+// of R - I (N = B A), on split-bf16 16x16x16 matrix instructions.  G, k and q
+// live in LDS only until the A/P products are done; A, P and T then take their
+// place.
 
 constexpr int PREP_NT = 256;
 constexpr int GLD = 132;     // fp32 row stride of the G tile
@@ -576,10 +597,9 @@ constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E;
 
 __global__ __launch_bounds__(PREP_NT, 2) void chunk_prep_kernel(const ChunkBwdArgs a)
 {
-    // phase 1: G | k | q;  phase 2 (the same bytes): A | P | T | Y
+    // phase 1: G | k | q;  phase 2 (the same bytes): A | P | T
     constexpr int OFF_G = 0, OFF_K = CH * GLD * 4, OFF_Q = OFF_K + CH * BLD * 2, P1 = OFF_Q + CH * BLD * 2;
-    constexpr int OFF_A = 0, OFF_P = CH * TLD * 4, OFF_T = 2 * CH * TLD * 4, OFF_Y = 3 * CH * TLD * 4,
-                  P2 = OFF_Y + 3 * 256 * 4;
+    constexpr int OFF_A = 0, OFF_P = CH * TLD * 4, OFF_T = 2 * CH * TLD * 4, P2 = 3 * CH * TLD * 4;
     __shared__ __attribute__((aligned(16))) char sm[P1 > P2 ? P1 : P2];
     __shared__ float bs[CH];
     __shared__ float tot[(PREP_NT / 64) * kDim];
@@ -590,7 +610,6 @@ __global__ __launch_bounds__(PREP_NT, 2) void chunk_prep_kernel(const ChunkBwdAr
     float* As = reinterpret_cast<float*>(sm + OFF_A);
     float* Ps = reinterpret_cast<float*>(sm + OFF_P);
     float* Ts = reinterpret_cast<float*>(sm + OFF_T);
-    float* Ys = reinterpret_cast<float*>(sm + OFF_Y);
 
     const int H = a.H;
     const int64_t id = blockIdx.x / H;
@@ -731,25 +750,40 @@ __global__ __launch_bounds__(PREP_NT, 2) void chunk_prep_kernel(const ChunkBwdAr
         for (int m = 0; m < 4; ++m) Ts[(16 * R + 4 * pq + m) * TLD + 16 * R + jc] = tv[m];
     }
     lds_sync();
+    // Off-diagonal blocks by distance d = R - I (wave w < 4 - d takes R = d + w,
+    // I = w), on split-bf16 16x16x16 matrix instructions:
+    //   Y = B_R sum_{I <= J < R} A_RJ T_JI,   T_RI = -T_RR Y.
+    // Y comes out in accumulator layout, which is the B operand of the second
+    // product as it stands.
     for (int d = 1; d < 4; ++d) {
-        // Y = sum_J N_RJ T_JI for the 4 - d blocks of this distance
-        const int rl = t >> 4, il = t & 15;
-        for (int R = d; R < 4; ++R) {
-            const int I = R - d, r = 16 * R + rl;
-            float y = 0.f;
-            for (int J = I; J < R; ++J)
+        if (wave < 4 - d) {
+            const int R = d + wave, I = wave;
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            f32x4 y = z;
+            for (int J = I; J < R; ++J) {
+                float av[4], bv[4];
 #pragma unroll
-                for (int m = 0; m < 16; ++m)
-                    y += As[r * TLD + 16 * J + m] * Ts[(16 * J + m) * TLD + 16 * I + il];
-            Ys[(R - d) * 256 + rl * 16 + il] = bs[r] * y;
-        }
-        lds_sync();
-        for (int R = d; R < 4; ++R) {
-            const int I = R - d, r = 16 * R + rl;
-            float x = 0.f;
+                for (int x = 0; x < 4; ++x) {
+                    av[x] = As[(16 * R + l16) * TLD + 16 * J + 4 * g + x];
+                    bv[x] = Ts[(16 * J + 4 * g + x) * TLD + 16 * I + l16];
+                }
+                i16x4 ah, al, bh, bl;
+                split4(av[0], av[1], av[2], av[3], ah, al);
+                split4(bv[0], bv[1], bv[2], bv[3], bh, bl);
+                y = mma16(ah, al, bh, bl, y);
+            }
+            float by[4], tv[4];
 #pragma unroll
-            for (int m = 0; m < 16; ++m) x -= Ts[r * TLD + 16 * R + m] * Ys[(R - d) * 256 + m * 16 + il];
-            Ts[r * TLD + 16 * I + il] = x;
+            for (int x = 0; x < 4; ++x) {
+                by[x] = bs[16 * R + 4 * g + x] * y[x];
+                tv[x] = Ts[(16 * R + l16) * TLD + 16 * R + 4 * g + x];
+            }
+            i16x4 ah, al, bh, bl;
+            split4(tv[0], tv[1], tv[2], tv[3], ah, al);
+            split4(by[0], by[1], by[2], by[3], bh, bl);
+            const f32x4 tr = mma16(ah, al, bh, bl, z);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) Ts[(16 * R + 4 * g + x) * TLD + 16 * I + l16] = -tr[x];
         }
         lds_sync();
     }
@@ -765,9 +799,12 @@ __global__ __launch_bounds__(PREP_NT, 2) void chunk_prep_kernel(const ChunkBwdAr
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int i = i0 + u;
-            pa[u] = i < r ? As[r * TLD + i] : 0.f;
-            pp[u] = i <= r ? Ps[r * TLD + i] : 0.f;
-            pt[u] = i < r ? Ts[r * TLD + i] : (i == r ? 1.f : 0.f);
+            // (read unconditionally, then selected: reads under the condition
+            // would become branches)
+            const float xa = As[r * TLD + i], xp = Ps[r * TLD + i], xt = Ts[r * TLD + i];
+            pa[u] = i < r ? xa : 0.f;
+            pp[u] = i <= r ? xp : 0.f;
+            pt[u] = i < r ? xt : (i == r ? 1.f : 0.f);
         }
         *reinterpret_cast<float4*>(dst + e) = va;
         *reinterpret_cast<float4*>(dst + TSZ + e) = vp;
@@ -1498,25 +1535,6 @@ __device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm)
 constexpr int INTRA_NT = 512;
 constexpr int PLD = 68;   // fp32 row stride of the 64 x 64 tiles
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-
-// hi*hi + hi*lo + lo*hi on the 16x16x16 bf16 instruction
-__device__ __forceinline__ f32x4 mma16(i16x4 ah, i16x4 al, i16x4 bh, i16x4 bl, f32x4 c)
-{
-    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, c, 0, 0, 0);
-    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, c, 0, 0, 0);
-    return c;
-}
-
-__device__ __forceinline__ void split4(float x0, float x1, float x2, float x3, i16x4& h, i16x4& l)
-{
-    uint32_t h0, l0, h1, l1;
-    split2(x0, x1, h0, l0);
-    split2(x2, x3, h1, l1);
-    h = __builtin_bit_cast(i16x4, (uint2){h0, h1});
-    l = __builtin_bit_cast(i16x4, (uint2){l0, l1});
-}
 
 // LDS of the intra-chunk part
 struct IntraLds {
