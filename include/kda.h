@@ -336,7 +336,9 @@ kda_status kda_varlen_prefill_slots(const void *q, const void *k, const void *v,
  *                 state, or NULL for zeros
  * Outputs, fp32, all written:
  *   dq, dk, dlog_alpha : the layout of q;  dv : the layout of v;  dbeta : the
- *                 layout of beta
+ *                 layout of beta.  With bf16 inputs dq, dk, dv and dlog_alpha
+ *                 also hold intermediate values of the call before their final
+ *                 ones, so they must not overlap any input or each other
  *   d_initial_state : [B or N, H, d_k, d_v], or NULL to skip; it MAY be the same
  *                 pointer as d_final_state
  * bf16 inputs take the chunked form on the matrix cores (64-token chunks;
