@@ -16,11 +16,11 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(PKG, "libkda.so")
 
 KDA_F32, KDA_BF16 = 0, 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 STATUS_NAMES = {
     0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
     4: "KDA_ERR_ALIGN", 5: "KDA_ERR_UNSUPPORTED", 6: "KDA_ERR_HIP",
-    7: "KDA_ERR_WORKSPACE", 8: "KDA_ERR_PRECONDITION",
+    7: "KDA_ERR_WORKSPACE", 8: "KDA_ERR_PRECONDITION", 9: "KDA_ERR_OVERLAP",
 }
 # workspace_bytes value asking the library to allocate the workspace itself
 KDA_WORKSPACE_AUTO = -1

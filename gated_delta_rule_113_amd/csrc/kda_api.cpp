@@ -52,6 +52,18 @@ kda_status check_ptrs(std::initializer_list<const void*> required,
     return KDA_OK;
 }
 
+// Byte ranges [p, p + n) of device buffers; NULL or empty ranges overlap nothing.
+struct Span {
+    const void* p;
+    uint64_t n;
+};
+bool overlap(Span a, Span b)
+{
+    if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a.p), y = reinterpret_cast<uintptr_t>(b.p);
+    return x < y + b.n && y < x + a.n;
+}
+
 // A caller-owned workspace is `bytes` bytes at a 256-byte aligned `ws` (NULL
 // when bytes is 0); KDA_WORKSPACE_AUTO asks the library for one (ws NULL).
 kda_status check_workspace(const void* ws, int64_t bytes)
@@ -289,6 +301,25 @@ kda_status backward_impl(const void* q, const void* k, const void* v, const void
         if ((st = check_ptrs({q, k, v, beta, log_alpha, d_o, dq, dk, dv, dbeta, dlog_alpha},
                              {initial_state, d_final_state, d_initial_state})) != KDA_OK)
             return st;
+        // the gradient buffers are written while the inputs are still read (and
+        // hold intermediates): no output may overlap an input or another output,
+        // except d_initial_state == d_final_state
+        const uint64_t ie = in_dtype == KDA_BF16 ? 2 : 4;
+        const uint64_t vec = static_cast<uint64_t>(rows) * H * kda::kDim, sc = static_cast<uint64_t>(rows) * H;
+        const uint64_t stb = static_cast<uint64_t>(n_seq) * H * kda::kStateFloats * 4;
+        const Span outs[] = {{dq, vec * 4}, {dk, vec * 4}, {dv, vec * 4}, {dlog_alpha, vec * 4},
+                             {dbeta, sc * 4}, {d_initial_state, stb}};
+        const Span ins[] = {{q, vec * ie}, {k, vec * ie}, {v, vec * ie}, {beta, sc * ie},
+                            {log_alpha, vec * 4}, {d_o, vec * 4}, {initial_state, stb},
+                            {d_final_state, stb}};
+        for (size_t i = 0; i < 6; ++i) {
+            for (size_t j = 0; j < i; ++j)
+                if (overlap(outs[i], outs[j])) return KDA_ERR_OVERLAP;
+            for (const Span& in : ins) {
+                if (i == 5 && in.p == d_final_state && d_initial_state == d_final_state) continue;
+                if (overlap(outs[i], in)) return KDA_ERR_OVERLAP;
+            }
+        }
     } else if ((st = check_ptrs({}, {initial_state, d_final_state, d_initial_state})) != KDA_OK) {
         return st;
     }
@@ -580,6 +611,7 @@ const char* kda_status_str(kda_status status)
         case KDA_ERR_HIP: return "KDA_ERR_HIP: the HIP runtime rejected a launch, or an earlier HIP error is pending";
         case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: the workspace is too small, or the library could not allocate one";
         case KDA_ERR_PRECONDITION: return "KDA_ERR_PRECONDITION: (KDA_DEBUG) log_alpha not finite or > 0, or cu_seqlens not 0..T_total non-decreasing";
+        case KDA_ERR_OVERLAP: return "KDA_ERR_OVERLAP: an output buffer overlaps an input or another output";
     }
     return "KDA_ERR_UNKNOWN: not a kda_status value";
 }

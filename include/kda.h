@@ -98,7 +98,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 typedef enum kda_status {
     KDA_OK = 0,
@@ -109,7 +109,8 @@ typedef enum kda_status {
     KDA_ERR_UNSUPPORTED = 5,  /* d_k or d_v other than 128                      */
     KDA_ERR_HIP = 6,          /* the HIP runtime rejected a launch, or a HIP error is pending */
     KDA_ERR_WORKSPACE = 7,    /* workspace too small or misused, or none could be allocated */
-    KDA_ERR_PRECONDITION = 8  /* KDA_DEBUG: a device-data precondition does not hold */
+    KDA_ERR_PRECONDITION = 8, /* KDA_DEBUG: a device-data precondition does not hold */
+    KDA_ERR_OVERLAP = 9       /* output buffers overlap each other or an input  */
 } kda_status;
 
 /* workspace_bytes value asking the library to allocate the workspace itself */
@@ -338,7 +339,8 @@ kda_status kda_varlen_prefill_slots(const void *q, const void *k, const void *v,
  *   dq, dk, dlog_alpha : the layout of q;  dv : the layout of v;  dbeta : the
  *                 layout of beta.  With bf16 inputs dq, dk, dv and dlog_alpha
  *                 also hold intermediate values of the call before their final
- *                 ones, so they must not overlap any input or each other
+ *                 ones, so no output may overlap an input or another output
+ *                 (KDA_ERR_OVERLAP, checked on the host from the sizes)
  *   d_initial_state : [B or N, H, d_k, d_v], or NULL to skip; it MAY be the same
  *                 pointer as d_final_state
  * bf16 inputs take the chunked form on the matrix cores (64-token chunks;

@@ -15,7 +15,7 @@ import gated_delta_rule_113_amd as kda
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "kda.h")
 
-OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, HIP, WORKSPACE, PRECONDITION = range(9)
+OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, HIP, WORKSPACE, PRECONDITION, OVERLAP = range(10)
 AUTO = -1            # KDA_WORKSPACE_AUTO
 P = 0x10000          # a 16-byte aligned fake device address
 MIS = 0x10008        # 8-byte aligned only
@@ -55,8 +55,8 @@ def test_exports_match_header(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 2
-    for code in range(9):
+    assert lib.kda_abi_version() == 3
+    for code in range(10):
         s = lib.kda_status_str(code).decode()
         assert s.startswith(kda._binding.STATUS_NAMES[code])
     assert lib.kda_status_str(99).decode().startswith("KDA_ERR_UNKNOWN")
@@ -250,6 +250,24 @@ def test_backward_validation(lib):
                 dv_=None, db=None, dla=None, ds0=None)
     assert backward(lib, T=0, **none) == OK
     assert varlen_backward(lib, Tt=0, **none) == OK
+
+
+def test_backward_overlap(lib):
+    # buffers 1 MiB apart (B=1, T=4, H=2 needs at most 128 KiB each); with no
+    # overlap the call still stops before any launch: no workspace was given
+    # (KDA_ERR_WORKSPACE), or without a GPU the runtime check (KDA_ERR_HIP)
+    names = ("q", "k", "v", "beta", "la", "s0", "do", "dsT", "dq", "dk_", "dv_", "db", "dla", "ds0")
+    apart = {n: (i + 1) << 20 for i, n in enumerate(names)}
+    assert backward(lib, **apart) in (WORKSPACE, HIP)
+    assert backward(lib, **dict(apart, ds0=apart["dsT"])) in (WORKSPACE, HIP)   # allowed alias
+    assert backward(lib, **dict(apart, dq=apart["q"])) == OVERLAP
+    assert backward(lib, **dict(apart, dv_=apart["v"] + 1024)) == OVERLAP   # partly over v (2 KiB of bf16)
+    assert backward(lib, **dict(apart, dla=apart["dk_"])) == OVERLAP
+    assert backward(lib, **dict(apart, db=apart["do"] + 4096 - 16)) == OVERLAP
+    assert backward(lib, **dict(apart, ds0=apart["s0"])) == OVERLAP
+    assert backward(lib, **dict(apart, dq=apart["q"] + 2048)) in (WORKSPACE, HIP)  # just past bf16 q
+    vb = {n: (i + 1) << 20 for i, n in enumerate(names) if n not in ("s0", "dsT", "ds0")}
+    assert varlen_backward(lib, **dict(vb, cu=P, s0=None, dsT=None, ds0=None, dq=vb["la"])) == OVERLAP
 
 
 def test_binding_rejects_cpu_tensors(lib):
