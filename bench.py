@@ -781,7 +781,7 @@ def time_backward(kda, ki, torch, np, dev, up, stream, reps, result):
                      "traffic": measured_traffic("backward_B8_T4096_H32_hbm_traffic.json", "backward_call"),
                      "mfma_algorithmic_tflops": tf, "mfma_frac": tf / BF16_MFMA_PEAK_TFLOPS,
                      "algorithmic_flops_per_launch": flops,
-                     "note": "the chunked backward (five kernels); algorithmic bytes = inputs read "
+                     "note": "the chunked backward (four kernels); algorithmic bytes = inputs read "
                              "and gradients written once; traffic = the measured HBM bytes of one call "
                              "(its workspace round trips included)"},
     }

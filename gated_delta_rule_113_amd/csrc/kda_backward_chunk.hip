@@ -1938,7 +1938,7 @@ __device__ __forceinline__ void intra_part(const ChunkBwdArgs& a, char* sm)
 // (grid: chunk ids x heads; 512 threads).  The intra part reads back, from
 // global memory, what the gradient part of the same workgroup wrote there:
 // the partial dq, dk and d log alpha (each by the thread that wrote it) and
-// dP, dT (by other waves, after the barrier), which mostly hit in cache.
+// dP, dT (by other waves, after the barrier).
 constexpr size_t kGiLds = sizeof(GradsLds) > sizeof(IntraLds) ? sizeof(GradsLds) : sizeof(IntraLds);
 static_assert(kGiLds <= 160 * 1024, "LDS budget of one CU");
 static_assert(INTRA_NT == SEQ_NT, "one workgroup shape for both parts");
