@@ -72,7 +72,7 @@ def parse():
     ap.add_argument("--heads", type=int, default=32)
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
-    ap.add_argument("--backward-reps", type=int, default=3)
+    ap.add_argument("--backward-reps", type=int, default=5)
     ap.add_argument("--no-raw", action="store_true",
                     help="skip the prefill from raw projections (same kernels: keeps kernel traces to one kind)")
     ap.add_argument("--no-tokens", action="store_true",
@@ -743,8 +743,13 @@ def time_backward(kda, ki, torch, np, dev, up, stream, reps, result):
     la, do, ds = up(inp.log_alpha, False), up(d_o, False), up(d_s, False)
     del inp, d_o, d_s
 
+    # the first calls after the prefill section run up to 15% slower while the
+    # GPU settles: five untimed calls first
+    warm = 5
+
     def med(fn):
-        fn()
+        for _ in range(warm):
+            fn()
         torch.cuda.synchronize()
         ts = []
         for _ in range(reps):
@@ -770,7 +775,7 @@ def time_backward(kda, ki, torch, np, dev, up, stream, reps, result):
         "workload": f"gradients of a prefill: B={B} x T={T} tokens, H={H}, bf16 q/k/v/beta, fp32 "
                     "log_alpha/d_o/d_final_state, gated channel mix, zero initial state",
         "ms": bms,
-        "timing": f"median of {reps} calls, each between two HIP events, after one untimed call; "
+        "timing": f"median of {reps} calls, each between two HIP events, after {warm} untimed calls; "
                   "caller-provided workspace",
         "workspace_bytes": ws.numel(),
         "tokens_per_s": B * T / (bms / 1e3),
