@@ -1204,6 +1204,32 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_dstate_kernel(const ChunkBwdA
 //   d log a (the intra-chunk part adds the cross sums); dP = dO U^T (lower blocks).
 // Phase C: dT = dU (B W)^T (lower blocks) from images of dU and B W.
 
+constexpr int INTRA_NT = SEQ_NT;   // the intra-chunk part runs in the same workgroup
+
+// The intra-chunk part's inputs that do not depend on the gradient part (A and T
+// tiles, log alpha, k, q, beta), requested while the gradient part still runs.
+struct IntraReq {
+    static constexpr int NE = TSZ / INTRA_NT;
+    float ar[NE], tr[NE];
+    bf16_t braw;
+    ChunkRaw<INTRA_NT, true> raw;
+};
+
+__device__ __forceinline__ void intra_request(const ChunkBwdArgs& a, int64_t id, int h, int64_t row0c, int L,
+                                              IntraReq& rq)
+{
+    const int t = threadIdx.x;
+    const float* apt = a.ws_apt + (id * a.H + h) * (3 * TSZ);
+#pragma unroll
+    for (int j = 0; j < IntraReq::NE; ++j) {
+        const int e = t + j * INTRA_NT;
+        rq.ar[j] = apt[e];
+        rq.tr[j] = apt[2 * TSZ + e];
+    }
+    rq.braw = beta_raw(a, row0c, L, h);
+    request<INTRA_NT, true>(a, row0c, L, h, rq.raw);
+}
+
 constexpr int GR_KT_PL = CH * kDim * 2;
 // LDS of the gradient part (phase B: dO | -B dW' | U;  phase C: dU | B W)
 struct GradsLds {
@@ -1213,7 +1239,7 @@ struct GradsLds {
     float bs[CH], gLs[kDim], dbr[SEQ_NT / 64][CH], dpd[SEQ_NT / 64][CH];
 };
 
-__device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm)
+__device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm, IntraReq& rq)
 {
     constexpr int KT_PL = GR_KT_PL;
     constexpr int OFF_I0 = 0, OFF_I1 = 2 * KT_PL, OFF_I2 = 4 * KT_PL;
@@ -1482,6 +1508,8 @@ __device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm)
         }
     }
     lds_sync();  // phase B images are dead
+    // the intra-chunk part's independent inputs, in flight during phase C
+    intra_request(a, id, h, row0c, L, rq);
 
     // ---- phase C: images of dU and B W, then dT = dU (B W)^T on the lower blocks
 #pragma unroll
@@ -1532,7 +1560,6 @@ __device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm)
 // block exceeds 2^-96) get that block pairwise on the vector ALUs.  Then dL,
 // its reverse cumulative sum over the chunk, and the totals of dq and dk.
 
-constexpr int INTRA_NT = 512;
 constexpr int PLD = 68;   // fp32 row stride of the 64 x 64 tiles
 
 
@@ -1547,7 +1574,7 @@ struct IntraLds {
     float DgS[16 * INTRA_NT];   // per thread: the cross sums inside the diagonal blocks
 };
 
-__device__ __forceinline__ void intra_part(const ChunkBwdArgs& a, char* sm)
+__device__ __forceinline__ void intra_part(const ChunkBwdArgs& a, char* sm, IntraReq& rq)
 {
     IntraLds& S_ = *reinterpret_cast<IntraLds*>(sm);
     float* Pd = S_.Pd;
@@ -1574,25 +1601,24 @@ __device__ __forceinline__ void intra_part(const ChunkBwdArgs& a, char* sm)
     const int t = threadIdx.x, lane = t & 63, wave = wave_id(), g = lane >> 4, l16 = lane & 15;
     const int64_t wslot = id * H + h;
 
-    // ---- the tiles, beta and the staging inputs are loaded first, without
-    // branches, so that their latencies overlap
-    constexpr int NE = TSZ / INTRA_NT;
-    float ar[NE], tr[NE], pr[NE], dr[NE];
+    // ---- dP and dT (written by the gradient part) are loaded first, without
+    // branches; the A and T tiles, beta and the staging inputs were requested
+    // during the gradient part (rq)
+    constexpr int NE = IntraReq::NE;
+    float pr[NE], dr[NE];
     {
-        const float* apt = a.ws_apt + wslot * (3 * TSZ);
         const float* dpt = a.ws_dpt + wslot * kDptFloats;
 #pragma unroll
         for (int j = 0; j < NE; ++j) {
             const int e = t + j * INTRA_NT;
-            ar[j] = apt[e];
-            tr[j] = apt[2 * TSZ + e];
             pr[j] = dpt[e];
             dr[j] = dpt[TSZ + e];
         }
     }
-    const bf16_t braw = beta_raw(a, row0c, L, h);
-    ChunkRaw<INTRA_NT, true> raw;
-    request<INTRA_NT, true>(a, row0c, L, h, raw);
+    const float (&ar)[NE] = rq.ar;
+    const float (&tr)[NE] = rq.tr;
+    const bf16_t braw = rq.braw;
+    ChunkRaw<INTRA_NT, true>& raw = rq.raw;
     // the grads kernel's terms of dq, dk and d log a for the rows of one
     // 16-token block, channel cc = 16 w + l16; requested a block ahead, and
     // before the previous block's stores (rows from L on are never stored)
@@ -1946,9 +1972,10 @@ static_assert(INTRA_NT == SEQ_NT, "one workgroup shape for both parts");
 __global__ __launch_bounds__(SEQ_NT, 1) void chunk_grads_kernel(const ChunkBwdArgs a)
 {
     __shared__ __attribute__((aligned(16))) char sm[kGiLds];
-    grads_part(a, sm);
+    IntraReq rq;
+    grads_part(a, sm, rq);
     __syncthreads();   // global writes of the gradient part visible to the workgroup; LDS free
-    intra_part(a, sm);
+    intra_part(a, sm, rq);
 }
 
 }  // namespace
