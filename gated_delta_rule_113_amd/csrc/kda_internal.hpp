@@ -74,7 +74,7 @@ constexpr int64_t kShortPrefill = 16;
 // workspace.  A tier that would not cut any sequence comes back as tier 2.
 // The plans are host arithmetic only (kda_plan.cpp).
 constexpr int64_t kMinSegment = 1024;   // shortest automatic segment
-constexpr size_t kTpBytes = 4 * 8192;   // the split T and P of one chunk (T hi, T lo, P hi, P lo)
+constexpr size_t kTpBytes = 4 * 336 * 16;   // the kept chunks of the split T and P of one chunk (T hi, T lo, P hi, P lo)
 // The fastest plan keeps the T/P images only while one call needs at most
 // this many bytes of them: the million-token workload (32 heads) would need
 // 17 GB of them for about 1% less time.

@@ -126,8 +126,23 @@ constexpr int LDS_BYTES = OFF_TD + 4 * 16 * TD_LD * 4;
 // and P, between a chunk's state products and the next chunk's staging
 constexpr int OFF_OT = OFF_T_HI;
 static_assert(OFF_P_LO + 8192 - OFF_T_HI == CH * kDim * 4, "output tile fits T and P exactly");
-constexpr int TP_BYTES = 4 * 8192;  // the split T and P of one chunk (T hi, T lo, P hi, P lo)
-static_assert(TP_BYTES == 16 * NT * 4, "four 16-byte pieces per thread");
+static_assert(4 * 8192 == 16 * NT * 4, "the T/P image: four 16-byte pieces per thread");
+// In the workspace each of the four planes of the T/P image (T hi, T lo, P hi,
+// P lo; 64 rows of eight 16-byte chunks) keeps only the chunks that can hold a
+// nonzero entry: T and P are lower triangular, and logical chunk c of a row
+// holds the natural columns 32 (c / 4) + 4 (c mod 4) + {0..3, 16..19}, so it is
+// kept in row r when its first column 32 (c / 4) + 4 (c mod 4) <= r.  Kept
+// chunks are numbered row by row: 336 per plane instead of 512.
+constexpr int kTpChunks = 336;
+constexpr int TP_BYTES = 4 * kTpChunks * 16;   // workspace bytes per (chunk, head)
+__device__ __forceinline__ bool tp_kept(int r, int c) { return 32 * (c >> 2) + 4 * (c & 3) <= r; }
+// the number of kept chunks in the rows before r
+__device__ __forceinline__ int tp_row_base(int r)
+{
+    return r <= 4 ? r : r <= 8 ? 4 + 2 * (r - 4) : r <= 12 ? 12 + 3 * (r - 8) : r <= 32 ? 24 + 4 * (r - 12)
+         : r <= 36 ? 104 + 5 * (r - 32) : r <= 40 ? 124 + 6 * (r - 36) : r <= 44 ? 148 + 7 * (r - 40)
+         : 176 + 8 * (r - 44);
+}
 static_assert(R1_BYTES >= 32768, "Ke^T must fit in R1");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CU");
 
@@ -135,10 +150,6 @@ static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CU");
 __device__ __forceinline__ int perm(int x)
 {
     return (x & ~31) | ((x & 12) << 1) | ((x & 16) >> 2) | (x & 3);
-}
-__device__ __forceinline__ int unperm(int p)
-{
-    return (p & ~31) | ((p & 24) >> 1) | ((p & 4) << 2) | (p & 3);
 }
 // Byte offsets in bf16 tiles of 128 (256 B rows) and 64 (128 B rows) entries.
 __device__ __forceinline__ int a256(int row, int pos)
@@ -156,7 +167,7 @@ __device__ __forceinline__ int a128(int row, int pos)
 // apart hit distinct banks at one chunk position.
 __device__ __forceinline__ int g_off(int row, int pos)
 {
-    return OFF_G + (row << 9) + ((((pos >> 2) ^ (row ^ (row >> 4))) & 15 | ((pos >> 2) & 16)) << 4) + ((pos & 3) << 2);
+    return OFF_G + (row << 9) + (((((pos >> 2) ^ (row ^ (row >> 4))) & 15) | ((pos >> 2) & 16)) << 4) + ((pos & 3) << 2);
 }
 // Byte offset in the transposed tile Ke^T (channel rows of 64 tokens): like
 // a128, with the chunk index XOR-ed with (row >> 1 ^ row >> 3) & 7, which
@@ -331,7 +342,7 @@ struct ScanArgs {
     int64_t short_max;  // sequences of at most this many tokens are skipped (0: none)
     float* ws_maps;   // [slots][H][2][d_k][d_v]: M and R of each segment but the last
     float* ws_start;  // [slots][H][d_k][d_v]: entering state of each segment
-    char* ws_tp;      // or null: LDS images (32 KiB) of the split T and P of every chunk of the
+    char* ws_tp;      // or null: the kept chunks (21 KiB) of the split T and P images of every chunk of the
                       // segments that pass 1 maps, for pass 3 to reuse; block (chunk id, head), with
                       // chunk id = (first row of the segment) / 64 + sequence + chunk within the segment
                       // (segments start at multiples of 64 within their sequence, so ids are unique
@@ -563,11 +574,17 @@ __device__ __forceinline__ void scan_segment(const ScanArgs& a, char* sm, bool p
         char* tpg = TP ? a.ws_tp + (((sg.row0 + sg.begin) / CH + sg.n + ci) * H + h) * static_cast<int64_t>(TP_BYTES)
                        : nullptr;
         uint4 tp0, tp1, tp2, tp3;  // (named registers: an array here ended up in scratch memory)
+        // this thread's 16-byte chunk of each image plane: row tid / 8, slot tid
+        // mod 8, logical chunk slot ^ (row / 2 mod 8) (the a128 swizzle); a
+        // chunk not kept reads chunk 0 and is replaced by zeros when staged
+        const int tp_r = tid >> 3, tp_c = (tid & 7) ^ ((tp_r >> 1) & 7);
+        const bool tp_in = tp_kept(tp_r, tp_c);
         if (LOADTP) {
-            tp0 = *gat<const uint4>(tpg, 16 * tid);
-            tp1 = *gat<const uint4>(tpg, 16 * (tid + NT));
-            tp2 = *gat<const uint4>(tpg, 16 * (tid + 2 * NT));
-            tp3 = *gat<const uint4>(tpg, 16 * (tid + 3 * NT));
+            const uint32_t ci = tp_in ? tp_row_base(tp_r) + tp_c : 0;
+            tp0 = *gat<const uint4>(tpg, 16 * ci);
+            tp1 = *gat<const uint4>(tpg, 16 * (ci + kTpChunks));
+            tp2 = *gat<const uint4>(tpg, 16 * (ci + 2 * kTpChunks));
+            tp3 = *gat<const uint4>(tpg, 16 * (ci + 3 * kTpChunks));
         }
 
         // ======== 0: stage the chunk; scan of the log2-decay in registers.
@@ -845,11 +862,18 @@ __device__ __forceinline__ void scan_segment(const ScanArgs& a, char* sm, bool p
         };
 
         if constexpr (LOADTP) {
-            // the output tile over T and P was written out in phase 0
+            // the output tile over T and P was written out in phase 0.  A chunk
+            // not kept is overwritten with zeros after its (dummy) copy: a select
+            // on the loaded value would be compiled to wait for the load at once
             at<uint4>(sm, OFF_T_HI + 16 * tid) = tp0;
             at<uint4>(sm, OFF_T_HI + 16 * (tid + NT)) = tp1;
             at<uint4>(sm, OFF_T_HI + 16 * (tid + 2 * NT)) = tp2;
             at<uint4>(sm, OFF_T_HI + 16 * (tid + 3 * NT)) = tp3;
+            if (!tp_in) {
+                const uint4 z4 = make_uint4(0, 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) at<uint4>(sm, OFF_T_HI + 16 * (tid + NT * j)) = z4;
+            }
         } else if (kh == 0) {
             const int r = 16 * rb + l16;
             const float br = at<float>(sm, OFF_BETA + 4 * r);
@@ -1109,9 +1133,12 @@ __device__ __forceinline__ void scan_segment(const ScanArgs& a, char* sm, bool p
                 // T and P are complete and only read from here on: their image
                 // goes to the workspace for pass 3 (here, after the X pass,
                 // rather than before it: 2% per call)
+                if (tp_in) {
+                    const uint32_t ci = tp_row_base(tp_r) + tp_c;
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    *gat<uint4>(tpg, 16 * (tid + NT * j)) = at<uint4>(sm, OFF_T_HI + 16 * (tid + NT * j));
+                    for (int j = 0; j < 4; ++j)
+                        *gat<uint4>(tpg, 16 * (ci + kTpChunks * j)) = at<uint4>(sm, OFF_T_HI + 16 * (tid + NT * j));
+                }
             }
             if (!OUT) {
 #pragma unroll

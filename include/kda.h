@@ -120,8 +120,9 @@ typedef enum kda_status {
 typedef enum kda_plan {
     KDA_PLAN_FULL = 0,        /* segments; pass 1 also keeps the split UT transform
                                  T and query-key matrix P of every chunk it maps
-                                 (32 KiB per chunk and head) for pass 3, while
-                                 those stay under 8 GiB per call */
+                                 (their lower-triangular parts, 21 KiB per chunk
+                                 and head) for pass 3, while those stay under
+                                 8 GiB per call */
     KDA_PLAN_SEGMENTS = 1,    /* segments, without the T/P images */
     KDA_PLAN_UNSEGMENTED = 2  /* one workgroup per (sequence, head); no workspace */
 } kda_plan;
