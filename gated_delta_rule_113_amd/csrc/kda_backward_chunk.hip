@@ -80,6 +80,7 @@
 // formed pairwise on the vector ALUs for the other channels.
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
 #include <cstdint>
 #include <type_traits>
 
@@ -121,11 +122,7 @@ struct ChunkBwdArgs {
     float* ws_s0;        // [ids][H][128][128]  entering state of every chunk
     float* ws_ds;        // [ids][H][128][128]  gradient in every chunk's leaving state
     float* ws_apt;       // [ids][H][3][64][64] A, P, T
-    float* ws_dpt;       // [ids][H][kDptFloats] dP, dT
 };
-
-// dP and dT (64 x 64 each)
-constexpr int kDptFloats = 2 * TSZ;
 
 __device__ __forceinline__ int64_t seq_row0(const ChunkBwdArgs& a, int64_t n)
 {
@@ -579,6 +576,7 @@ constexpr int PREP_NT = 256;
 constexpr int GLD = 132;     // fp32 row stride of the G tile
 constexpr int BLD = 136;     // bf16 row stride of the k and q tiles
 constexpr int TLD = 65;      // fp32 row stride of 64 x 64 tiles
+constexpr int PLD = 68;      // fp32 row stride of the grads kernel's 64 x 64 tiles
 
 // The six off-diagonal 16 x 16 blocks (row block, column block).
 __device__ __forceinline__ void offdiag_block(int p, int& R, int& I)
@@ -1230,16 +1228,27 @@ __device__ __forceinline__ void intra_request(const ChunkBwdArgs& a, int64_t id,
     request<INTRA_NT, true>(a, row0c, L, h, rq.raw);
 }
 
+// The gradient part's terms of dq, dk and d log alpha, held in registers for
+// the intra-chunk part: row 16 m + 4 g + x, channel 16 w + l16 (the same
+// thread owns the same elements in both parts).
+struct Partials {
+    float q[4][4], k[4][4], l[4][4];
+};
+
 constexpr int GR_KT_PL = CH * kDim * 2;
-// LDS of the gradient part (phase B: dO | -B dW' | U;  phase C: dU | B W)
+// LDS of the gradient part (phase B: dO | -B dW' | U;  phase C: dU | B W, and
+// dT where U was).  dP and dT stay in LDS for the intra-chunk part.
 struct GradsLds {
     char img[6 * GR_KT_PL];
     float Gs[CH * GLD];
     float tot[(SEQ_NT / 64) * kDim];
     float bs[CH], gLs[kDim], dbr[SEQ_NT / 64][CH], dpd[SEQ_NT / 64][CH];
+    float Pd[CH * PLD];   // dP (i <= r; the blocks above the diagonal are not written)
 };
+constexpr int GR_DT_OFF = 4 * GR_KT_PL;   // dT (fp32, row stride PLD) over the image of U
+static_assert(CH * PLD * 4 <= 2 * GR_KT_PL, "dT fits where the image of U was");
 
-__device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm, IntraReq& rq)
+__device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm, IntraReq& rq, Partials& pp)
 {
     constexpr int KT_PL = GR_KT_PL;
     constexpr int OFF_I0 = 0, OFF_I1 = 2 * KT_PL, OFF_I2 = 4 * KT_PL;
@@ -1251,6 +1260,8 @@ __device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm, Intr
     float* gLs = S_.gLs;
     float (*dbr)[CH] = S_.dbr;
     float (*dpd)[CH] = S_.dpd;
+    float* Pd = S_.Pd;
+    float* Dt = reinterpret_cast<float*>(img + GR_DT_OFF);
 
     const int H = a.H;
     const int64_t id = blockIdx.x / H;
@@ -1343,13 +1354,12 @@ __device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm, Intr
             kv[m][x] = (float)Kb[r * kDim + col];
         }
     {
-        // dv = B dW'; db (first term): row sums of dW' (.) W over this wave's columns
+        // db (first term): row sums of dW' (.) W over this wave's columns
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 const int r = 16 * m + 4 * g + x;
-                if (r < L) a.dv[e0 + r * rs] = bs[r] * dW[m][x];
                 const float p = row_sum16(dW[m][x] * W[m][x]);
                 const float d = row_sum16(dO[m][x] * U[m][x]);  // the diagonal of dP in fp32
                 if (l16 == 0) {
@@ -1359,6 +1369,15 @@ __device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm, Intr
             }
     }
     lds_sync();
+    // dv = B dW', stored only now: dv held parked dW' rows that other lanes
+    // read, and every wave has used all its parked values before this barrier
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int r = 16 * m + 4 * g + x;
+            if (r < L) a.dv[e0 + r * rs] = bs[r] * dW[m][x];
+        }
 
     // ---- phase B images (natural binding, rows = tokens, k = value columns):
     // dO, -B dW', U.  Even lanes store their value and the odd neighbour's.
@@ -1378,7 +1397,6 @@ __device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm, Intr
     lds_sync();
 
     // ---- phase B: wave w on channels cw = 16w + l16; rows of S0 and dS1 as B operands
-    float* dpt = a.ws_dpt + wslot * kDptFloats;
     {
         const int cw = col;
         bf16x8 sh[4], sl[4], dh[4], dl[4];
@@ -1417,19 +1435,16 @@ __device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm, Intr
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 const int r = 16 * m + 4 * g + x;
-                av[m][x] = bv[m][x] = 0.f;
-                if (r < L) {
-                    const int64_t e = ((row0c + r) * H + h) * kDim + cw;
-                    const float G = Gs[r * GLD + cw];
-                    const float gam = ex2(G), ge = ex2(gLc - G);
-                    const float q1 = qv[m][x], k1 = kv[m][x];
-                    const float dq = dQt[x] * gam;
-                    const float dkt = dKt[x] * gam, dke = dKe[x] * ge;
-                    a.dq[e] = dq;
-                    a.dk[e] = dkt + dke;
-                    av[m][x] = q1 * dq + k1 * dkt;
-                    bv[m][x] = k1 * dke;
-                }
+                const float G = Gs[r * GLD + cw];
+                const float gam = ex2(G), ge = ex2(gLc - G);
+                const float q1 = qv[m][x], k1 = kv[m][x];
+                const float dq = dQt[x] * gam;
+                const float dkt = dKt[x] * gam, dke = dKe[x] * ge;
+                const bool in = r < L;
+                pp.q[m][x] = dq;
+                pp.k[m][x] = dkt + dke;
+                av[m][x] = in ? q1 * dq + k1 * dkt : 0.f;
+                bv[m][x] = in ? k1 * dke : 0.f;
             }
         }
         // The S0 part of d log a_j: sum_{r >= j} av_r + sum_{r < j} bv_r +
@@ -1472,14 +1487,14 @@ __device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm, Intr
             float run_b = sb;
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
-                const int r = 16 * m + 4 * g + x;
-                if (r < L) a.dla[((row0c + r) * H + h) * kDim + cw] = suf[x] + run_b + glast;
+                pp.l[m][x] = suf[x] + run_b + glast;
                 run_b += bv[m][x];
             }
             pre_prev += sb_blk[m];
         }
     }
-    // dP = dO U^T on the 10 lower 16 x 16 blocks (2 per wave for waves 0, 1)
+    // dP = dO U^T on the 10 lower 16 x 16 blocks (2 per wave for waves 0, 1),
+    // zero above the diagonal inside the diagonal blocks
     for (int b = wave; b < 10; b += SEQ_NT / 64) {
         int mr = 0;
         while ((mr + 1) * (mr + 2) / 2 <= b) ++mr;
@@ -1495,21 +1510,21 @@ __device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm, Intr
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
             const int r = 16 * mr + 4 * g + x, i = 16 * mi + l16;
-            float val = acc[x];
-            if (r == i) {
-                // dP_rr = dO_r . U_r carries the first token of a sequence from a
-                // zero state (dq = dP_rr k_r there); its sum can cancel far below
-                // its terms, so it is summed in fp32 rather than on split bf16
-                val = 0.f;
-#pragma unroll
-                for (int w = 0; w < SEQ_NT / 64; ++w) val += dpd[w][r];
-            }
-            dpt[r * CH + i] = val;
+            Pd[r * PLD + i] = i <= r ? acc[x] : 0.f;
         }
     }
     lds_sync();  // phase B images are dead
     // the intra-chunk part's independent inputs, in flight during phase C
     intra_request(a, id, h, row0c, L, rq);
+    // dP_rr = dO_r . U_r carries the first token of a sequence from a zero
+    // state (dq = dP_rr k_r there); its sum can cancel far below its terms, so
+    // it is summed in fp32 rather than on split bf16
+    if (t < CH) {
+        float d = 0.f;
+#pragma unroll
+        for (int w = 0; w < SEQ_NT / 64; ++w) d += dpd[w][t];
+        Pd[t * PLD + t] = d;
+    }
 
     // ---- phase C: images of dU and B W, then dT = dU (B W)^T on the lower blocks
 #pragma unroll
@@ -1521,6 +1536,8 @@ __device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm, Intr
             put_pair(OFF_I1, r, bs[r] * W[m][x]);
         }
     lds_sync();
+    // dT (i < r) into LDS over the image of U, zero elsewhere: the 10 lower
+    // blocks from the products, the 6 upper ones as zeros
     for (int b = wave; b < 10; b += SEQ_NT / 64) {
         int mr = 0;
         while ((mr + 1) * (mr + 2) / 2 <= b) ++mr;
@@ -1534,7 +1551,16 @@ __device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm, Intr
             acc = mma3(ah, al, bh2, bl2, acc);
         }
 #pragma unroll
-        for (int x = 0; x < 4; ++x) dpt[TSZ + (16 * mr + 4 * g + x) * CH + 16 * mi + l16] = acc[x];
+        for (int x = 0; x < 4; ++x) {
+            const int r = 16 * mr + 4 * g + x, i = 16 * mi + l16;
+            Dt[r * PLD + i] = i < r ? acc[x] : 0.f;
+        }
+    }
+#pragma unroll
+    for (int e = t; e < 6 * 256; e += SEQ_NT) {
+        int R, I;
+        offdiag_block(e >> 8, R, I);   // (R, I) below the diagonal; (I, R) above it
+        Dt[(16 * I + ((e >> 4) & 15)) * PLD + 16 * R + (e & 15)] = 0.f;
     }
     // db, first term
     if (t < L) {
@@ -1560,21 +1586,23 @@ __device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm, Intr
 // block exceeds 2^-96) get that block pairwise on the vector ALUs.  Then dL,
 // its reverse cumulative sum over the chunk, and the totals of dq and dk.
 
-constexpr int PLD = 68;   // fp32 row stride of the 64 x 64 tiles
-
-
-// LDS of the intra-chunk part
+// LDS of the intra-chunk part.  dP and dT are where the gradient part left
+// them; everything else overlays the gradient part's dead regions.
 struct IntraLds {
-    float Pd[CH * PLD];       // dP (i <= r)
-    float Ad[CH * PLD];       // dT, Y, dM, then dA
     float U1[2 * CH * PLD];   // T and A, then G
     __bf16 Ks[CH * kDim];
-    __bf16 Qs[CH * kDim];
     float bs[CH], db2[CH], tot[(INTRA_NT / 64) * kDim];
+    char pad0[GR_DT_OFF - 2 * CH * PLD * 4 - CH * kDim * 2 - (2 * CH + (INTRA_NT / 64) * kDim) * 4];
+    float Ad[CH * PLD];       // dT, Y, dM, then dA
+    __bf16 Qs[CH * kDim];
     float DgS[16 * INTRA_NT];   // per thread: the cross sums inside the diagonal blocks
+    char pad1[offsetof(GradsLds, Pd) - GR_DT_OFF - CH * PLD * 4 - CH * kDim * 2 - 16 * INTRA_NT * 4];
+    float Pd[CH * PLD];       // dP (i <= r)
 };
+static_assert(offsetof(IntraLds, Ad) == GR_DT_OFF, "dT where the gradient part wrote it");
+static_assert(offsetof(IntraLds, Pd) == offsetof(GradsLds, Pd), "dP where the gradient part wrote it");
 
-__device__ __forceinline__ void intra_part(const ChunkBwdArgs& a, char* sm, IntraReq& rq)
+__device__ __forceinline__ void intra_part(const ChunkBwdArgs& a, char* sm, IntraReq& rq, const Partials& pp)
 {
     IntraLds& S_ = *reinterpret_cast<IntraLds*>(sm);
     float* Pd = S_.Pd;
@@ -1599,53 +1627,26 @@ __device__ __forceinline__ void intra_part(const ChunkBwdArgs& a, char* sm, Intr
     const int64_t row0c = seq_row0(a, n) + c * CH;
     const int L = static_cast<int>(min<int64_t>(CH, seq_len(a, n) - c * CH));
     const int t = threadIdx.x, lane = t & 63, wave = wave_id(), g = lane >> 4, l16 = lane & 15;
-    const int64_t wslot = id * H + h;
 
-    // ---- dP and dT (written by the gradient part) are loaded first, without
-    // branches; the A and T tiles, beta and the staging inputs were requested
-    // during the gradient part (rq)
+    // ---- dP and dT are in LDS (from the gradient part); the A and T tiles,
+    // beta and the staging inputs were requested during the gradient part (rq)
     constexpr int NE = IntraReq::NE;
-    float pr[NE], dr[NE];
-    {
-        const float* dpt = a.ws_dpt + wslot * kDptFloats;
-#pragma unroll
-        for (int j = 0; j < NE; ++j) {
-            const int e = t + j * INTRA_NT;
-            pr[j] = dpt[e];
-            dr[j] = dpt[TSZ + e];
-        }
-    }
     const float (&ar)[NE] = rq.ar;
     const float (&tr)[NE] = rq.tr;
     const bf16_t braw = rq.braw;
     ChunkRaw<INTRA_NT, true>& raw = rq.raw;
-    // the grads kernel's terms of dq, dk and d log a for the rows of one
-    // 16-token block, channel cc = 16 w + l16; requested a block ahead, and
-    // before the previous block's stores (rows from L on are never stored)
+    // channel cc = 16 w + l16 of the rows 16 R + 4 g + x (as the gradient part's terms)
     const int cc = 16 * wave + l16;
     const int64_t rs = static_cast<int64_t>(H) * kDim;
     const int64_t e0 = (row0c * H + h) * kDim + cc;
-    float pq[4], pk[4], pl[4];
-    auto request_partials = [&](int R) {
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int r = 16 * R + 4 * g + x;
-            const int64_t e = e0 + (r < L ? r : 0) * rs;
-            pq[x] = a.dq[e];
-            pk[x] = a.dk[e];
-            pl[x] = a.dla[e];
-        }
-    };
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- phase 1: T, A, dT (i < r), dP (i <= r)
+    // ---- phase 1: T and A
 #pragma unroll
     for (int j = 0; j < NE; ++j) {
         const int e = t + j * INTRA_NT, r = e >> 6, i = e & 63;
         As[r * PLD + i] = ar[j];
         Ts[r * PLD + i] = tr[j];
-        Pd[r * PLD + i] = i <= r ? pr[j] : 0.f;   // (only the lower blocks were written)
-        Ad[r * PLD + i] = i < r ? dr[j] : 0.f;
     }
     if (t < CH) bs[t] = t < L ? widen(braw) : 0.f;
     lds_sync();
@@ -1809,7 +1810,6 @@ __device__ __forceinline__ void intra_part(const ChunkBwdArgs& a, char* sm, Intr
             DgS[(4 * R + (jl & 3)) * INTRA_NT + 64 * wave + 16 * (jl >> 2) + l16] = cs[jl];
     }
     __builtin_amdgcn_sched_barrier(0);
-    request_partials(3);
     f32x4 dkc[4];
     float Bc[4][4], Ab[4];
 #pragma unroll
@@ -1939,13 +1939,11 @@ __device__ __forceinline__ void intra_part(const ChunkBwdArgs& a, char* sm, Intr
         float fq[4], fk[4], fl[4];
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-            fq[x] = pq[x] + dqR[x];
-            fk[x] = pk[x] + dkrR[x] + dkc[R][x];
-            fl[x] = pl[x] + Ab[R] + bp + cs[x] + DgS[(4 * R + x) * INTRA_NT + t];
+            fq[x] = pp.q[R][x] + dqR[x];
+            fk[x] = pp.k[R][x] + dkrR[x] + dkc[R][x];
+            fl[x] = pp.l[R][x] + Ab[R] + bp + cs[x] + DgS[(4 * R + x) * INTRA_NT + t];
             bp += Bc[R][x];
         }
-        if (R > 0) request_partials(R - 1);
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
             const int r = 16 * R + 4 * g + x;
@@ -1961,10 +1959,9 @@ __device__ __forceinline__ void intra_part(const ChunkBwdArgs& a, char* sm, Intr
 }
 
 // The gradient part and then the intra-chunk part of one chunk of one head
-// (grid: chunk ids x heads; 512 threads).  The intra part reads back, from
-// global memory, what the gradient part of the same workgroup wrote there:
-// the partial dq, dk and d log alpha (each by the thread that wrote it) and
-// dP, dT (by other waves, after the barrier).
+// (grid: chunk ids x heads; 512 threads).  The intra part takes the partial
+// dq, dk and d log alpha of the gradient part in registers and dP, dT from LDS
+// (written by other waves, before the barrier).
 constexpr size_t kGiLds = sizeof(GradsLds) > sizeof(IntraLds) ? sizeof(GradsLds) : sizeof(IntraLds);
 static_assert(kGiLds <= 160 * 1024, "LDS budget of one CU");
 static_assert(INTRA_NT == SEQ_NT, "one workgroup shape for both parts");
@@ -1973,16 +1970,17 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_grads_kernel(const ChunkBwdAr
 {
     __shared__ __attribute__((aligned(16))) char sm[kGiLds];
     IntraReq rq;
-    grads_part(a, sm, rq);
-    __syncthreads();   // global writes of the gradient part visible to the workgroup; LDS free
-    intra_part(a, sm, rq);
+    Partials pp;
+    grads_part(a, sm, rq, pp);
+    __syncthreads();   // dP and dT complete; the rest of the LDS free
+    intra_part(a, sm, rq, pp);
 }
 
 }  // namespace
 
-// the workspace the plan sizes: entering state, leaving-state gradient, A/P/T
-// and dP/dT, per (chunk id, head)
-static_assert(kChunkBackwardFloats == 2 * static_cast<size_t>(SS) + 3 * TSZ + kDptFloats,
+// the workspace the plan sizes: entering state, leaving-state gradient and
+// A/P/T, per (chunk id, head)
+static_assert(kChunkBackwardFloats == 2 * static_cast<size_t>(SS) + 3 * TSZ,
               "the workspace layout of the chunked backward");
 static_assert(CH == kChunk, "the plan's chunk length");
 
@@ -2019,7 +2017,6 @@ hipError_t launch_backward_chunked(const void* q, const void* k, const void* v, 
     a.ws_s0 = w;
     a.ws_ds = a.ws_s0 + slots * SS;
     a.ws_apt = a.ws_ds + slots * SS;
-    a.ws_dpt = a.ws_apt + slots * 3 * TSZ;
 
     const dim3 chunks(static_cast<unsigned>(n_ids * H)), seqs(static_cast<unsigned>(units));
     hipError_t e;

@@ -112,8 +112,8 @@ hipError_t launch_prefill_scan(const void* q, const void* k, const void* v, cons
 // checkpoint state every kBackwardBlock tokens (8 KiB per head-token) in the
 // workspace, and the reverse sweep recomputes each block from its checkpoint.
 constexpr int kBackwardBlock = 8;
-// per (chunk, head): entering state, leaving-state gradient, A / P / T, dP / dT
-constexpr size_t kChunkBackwardFloats = 2 * kStateFloats + 5 * kChunk * kChunk;
+// per (chunk, head): entering state, leaving-state gradient, A / P / T
+constexpr size_t kChunkBackwardFloats = 2 * kStateFloats + 3 * kChunk * kChunk;
 struct BackwardPlan {
     bool chunked = false;       // bf16 inputs: the chunked matrix-core backward
     int64_t n_ids = 0;          // chunked: chunk ids per head

@@ -347,9 +347,9 @@ kda_status kda_varlen_prefill_slots(const void *q, const void *k, const void *v,
  * bf16 inputs take the chunked form on the matrix cores (64-token chunks;
  * operands split into hi + lo bf16 as in the prefill, fp32 accumulation): the
  * workspace keeps, per (64-token chunk, head), the chunk's entering state and
- * the gradient in its leaving state, its UT transform, A and P matrices and
- * their gradients, about 208 KiB, i.e. 3.3 KiB per head-token (3.3 GiB for
- * 8 x 4096 tokens x 32 heads, 104 GiB for 1,048,576 tokens x 32 heads).  fp32
+ * the gradient in its leaving state, its UT transform, A and P matrices,
+ * 176 KiB, i.e. 2.75 KiB per head-token (2.8 GiB for 8 x 4096 tokens x 32
+ * heads, 88 GiB for 1,048,576 tokens x 32 heads).  fp32
  * inputs take the token-by-token chain rule with a state checkpoint every 8
  * tokens (8 KiB per head-token).  kda_backward_workspace_size gives the bytes;
  * a smaller workspace is KDA_ERR_WORKSPACE.  B or N = 0 is a no-op; with no
