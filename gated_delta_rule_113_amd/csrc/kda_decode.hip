@@ -136,6 +136,21 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     }
 }
 
+constexpr float kLog2e = 1.4426950408889634f;
+
+// The sum over the 64 lanes of a wave, in every lane.
+__device__ __forceinline__ float wave_sum(float x)
+{
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));  // lane ^ 1
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));  // lane ^ 2
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false)); // row_ror 4
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false)); // row_ror 8
+    const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+    const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+}
+
 // K consecutive tokens of each sequence from its current state (speculative
 // decoding: verify K draft tokens, then keep the accepted prefix).  The same
 // per-token arithmetic and lane mapping as decode_step_kernel, with the state
@@ -217,6 +232,166 @@ __global__ __launch_bounds__(256) void decode_tokens_kernel(
     }
 }
 
+// Verify only (no commit) for K <= 4: the K tokens as one chunk of the
+// blockwise form ("Kimi K3 -- the architecture and infrastructure,
+// explained", section "Kimi Delta Attention: the load-bearing choice": the
+// delta rule regrouped per block of tokens), in fp32 on the vector ALUs.
+// With G_t the cumulative log2-decay of each channel over tokens 0..t and S
+// the entering state:
+//     A_ri = sum_c k_rc k_ic 2^(G_rc - G_ic) (i < r),  P_ri = sum_c q_rc k_ic 2^(G_rc - G_ic) (i <= r)
+//     X_r = S^T (k_r (.) 2^G_r),   Y_r = S^T (q_r (.) 2^G_r)
+//     U_r = b_r (v_r - X_r - sum_{i<r} A_ri U_i),   o_r = Y_r + sum_{i<=r} P_ri U_i
+// (all exponents <= 0).  Per token a lane does 128 multiply-adds per 64
+// state elements (X and Y) instead of the 256 of a state update and readout,
+// and the state is only read, so it is streamed through registers in blocks
+// of 4 rows instead of held: a lane needs few registers and every head of a
+// decode batch can be resident at once (8 waves per SIMD), the loads of later
+// blocks overlapping the arithmetic of earlier ones.  The pair sums grow as
+// K^2, so longer drafts and commits keep the token-by-token kernel above.  Lane mapping: wave w owns columns 32w..32w+31,
+// lane l the columns 32w + 2 (l & 15) .. +1 of the 32 rows 32 (l >> 4) .. +31
+// (one load instruction of a wave covers 4 rows x 128 contiguous bytes).
+template <typename InT>
+__global__ __launch_bounds__(256, 8) void decode_verify4_kernel(
+    const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
+    const InT* __restrict__ beta, const float* __restrict__ log_alpha,
+    const float* __restrict__ state, int K, int H, float* __restrict__ o)
+{
+    constexpr int KM = 4, NP = KM * (KM + 1) / 2, NB = 8;   // tokens, pairs, 4-row blocks per lane
+    __shared__ __attribute__((aligned(16))) float sKt[KM][kDim], sQt[KM][kDim];
+    __shared__ float pA[NP][2], pP[NP][2];
+    const int64_t unit = blockIdx.x;  // n * H + h
+    const int64_t n = unit / H;
+    const int h = static_cast<int>(unit - n * H);
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int r0 = 32 * (lane >> 4);
+    const int col = 32 * wave + 2 * (lane & 15);
+    const float* S = state + unit * (kDim * kDim) + col;
+    auto rowvec = [&](int t) { return ((n * K + t) * H + h) * kDim; };
+
+    // inputs first (no branch around a load: tokens from K on re-read token 0),
+    // then the first two blocks of the state
+    const int e = tid & (kDim - 1);
+    float xa[KM];
+    InT xk[KM], xq[KM], xb[KM];
+    decltype(load2_raw(v)) vr[KM];
+#pragma unroll
+    for (int t = 0; t < KM; ++t) {
+        const int tt = t < K ? t : 0;
+        const int64_t vec = rowvec(tt);
+        xa[t] = log_alpha[vec + e];
+        xk[t] = k[vec + e];
+        xq[t] = q[vec + e];
+        xb[t] = beta[(n * K + tt) * H + h];
+        vr[t] = load2_raw(v + vec + col);
+    }
+    float2 blk[2][4];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) blk[b][i] = *reinterpret_cast<const float2*>(S + (r0 + 4 * b + i) * kDim);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // per channel e: G, the decayed keys and queries (first half), the pairs'
+    // terms of A and P (both halves, by parity)
+    const int half = wave >> 1;
+    float g[KM], kv[KM], qv[KM];
+    {
+        float run = 0.f;
+#pragma unroll
+        for (int t = 0; t < KM; ++t) {
+            run += t < K ? xa[t] * kLog2e : 0.f;
+            g[t] = run;
+            kv[t] = widen(xk[t]);
+            qv[t] = widen(xq[t]);
+        }
+    }
+    if (half == 0) {
+#pragma unroll
+        for (int t = 0; t < KM; ++t) {
+            if (t < K) {
+                const float gm = __builtin_amdgcn_exp2f(g[t]);
+                sKt[t][e] = kv[t] * gm;
+                sQt[t][e] = qv[t] * gm;
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < KM; ++r)
+#pragma unroll
+        for (int i = 0; i <= r; ++i) {
+            const int p = r * (r + 1) / 2 + i;
+            if (r < K && (p & 1) == half) {
+                const float f = kv[i] * __builtin_amdgcn_exp2f(g[r] - g[i]);
+                const float av = i < r ? wave_sum(kv[r] * f) : 0.f;
+                const float pv = wave_sum(qv[r] * f);
+                if (lane == 0) {
+                    pA[p][wave & 1] = av;
+                    pP[p][wave & 1] = pv;
+                }
+            }
+        }
+    __syncthreads();
+
+    // ---- X_t and Y_t over the lane's 32 rows, block by block, two blocks in flight
+    float2 X[KM], Y[KM];
+#pragma unroll
+    for (int t = 0; t < KM; ++t) X[t] = Y[t] = make_float2(0.f, 0.f);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        float2 (&cur)[4] = blk[b & 1];
+#pragma unroll
+        for (int t = 0; t < KM; ++t) {
+            if (t >= K) continue;
+            const float4 k4 = *reinterpret_cast<const float4*>(&sKt[t][r0 + 4 * b]);
+            const float4 q4 = *reinterpret_cast<const float4*>(&sQt[t][r0 + 4 * b]);
+            const float kt[4] = {k4.x, k4.y, k4.z, k4.w}, qt[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                X[t].x += kt[i] * cur[i].x; X[t].y += kt[i] * cur[i].y;
+                Y[t].x += qt[i] * cur[i].x; Y[t].y += qt[i] * cur[i].y;
+            }
+        }
+        if (b + 2 < NB) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) cur[i] = *reinterpret_cast<const float2*>(S + (r0 + 4 * (b + 2) + i) * kDim);
+        }
+    }
+    // sums over the four row quarters (lanes l, l ^ 16, l ^ 32, l ^ 48)
+    auto quarters = [](float x) {
+        const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+        const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+    };
+    float2 U[KM];
+#pragma unroll
+    for (int r = 0; r < KM; ++r) {
+        if (r >= K) continue;
+        const float2 x = make_float2(quarters(X[r].x), quarters(X[r].y));
+        const float2 y = make_float2(quarters(Y[r].x), quarters(Y[r].y));
+        const float2 vt = widen2(vr[r]);
+        float2 u = make_float2(vt.x - x.x, vt.y - x.y);
+#pragma unroll
+        for (int i = 0; i < r; ++i) {
+            const int p = r * (r + 1) / 2 + i;
+            const float a_ = pA[p][0] + pA[p][1];
+            u.x -= a_ * U[i].x; u.y -= a_ * U[i].y;
+        }
+        const float br = widen(xb[r]);
+        U[r] = make_float2(br * u.x, br * u.y);
+        float2 ot = y;
+#pragma unroll
+        for (int i = 0; i <= r; ++i) {
+            const int p = r * (r + 1) / 2 + i;
+            const float p_ = pP[p][0] + pP[p][1];
+            ot.x += p_ * U[i].x; ot.y += p_ * U[i].y;
+        }
+        if (r0 == 0) *reinterpret_cast<float2*>(o + rowvec(r) + col) = ot;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_decode_tokens(const void* q, const void* k, const void* v, const void* beta,
@@ -236,8 +411,15 @@ hipError_t launch_decode_tokens(const void* q, const void* k, const void* v, con
                            static_cast<const T*>(v), static_cast<const T*>(beta), log_alpha,
                            state, n_commit, static_cast<int>(K), static_cast<int>(H), o);
     };
+    auto verify4 = [&](auto tag) {
+        using T = decltype(tag);
+        hipLaunchKernelGGL(decode_verify4_kernel<T>, grid, block, 0, stream, static_cast<const T*>(q),
+                           static_cast<const T*>(k), static_cast<const T*>(v), static_cast<const T*>(beta),
+                           log_alpha, state, static_cast<int>(K), static_cast<int>(H), o);
+    };
     auto pick = [&](auto tag) {
-        if (K <= 4) go(std::integral_constant<int, 4>{}, tag);
+        if (K <= 4 && !n_commit) verify4(tag);
+        else if (K <= 4) go(std::integral_constant<int, 4>{}, tag);
         else if (K <= 8) go(std::integral_constant<int, 8>{}, tag);
         else go(std::integral_constant<int, 16>{}, tag);
     };

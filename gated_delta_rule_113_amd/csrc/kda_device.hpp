@@ -36,6 +36,15 @@ __device__ __forceinline__ float4 widen4(uint2 r)
     return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
                        __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u));
 }
+// Two consecutive elements as raw storage (p 4-byte aligned for bf16, 8-byte
+// aligned for fp32), and their widening.
+__device__ __forceinline__ float2 load2_raw(const float* p) { return *reinterpret_cast<const float2*>(p); }
+__device__ __forceinline__ uint32_t load2_raw(const bf16_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+__device__ __forceinline__ float2 widen2(float2 r) { return r; }
+__device__ __forceinline__ float2 widen2(uint32_t r)
+{
+    return make_float2(__uint_as_float(r << 16), __uint_as_float(r & 0xffff0000u));
+}
 
 // e^x as 2^(x log2 e) on the hardware exp2 (v_exp_f32).  For the gate values
 // used here (x <= 0, |x| up to a few hundred) the relative error is about

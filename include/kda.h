@@ -255,7 +255,9 @@ kda_status kda_decode_step_raw(const void *q, const void *k, const void *v, cons
  * keep the accepted prefix.  The pages describe a draft layer that guesses
  * several tokens which the main model then checks in one pass (the
  * marketersindex.com Kimi K3 article, section "Optimization for Inference:
- * 4-Bit and Speculative Decoding"); the per-token update is the decode step's.
+ * 4-Bit and Speculative Decoding"); the per-token update is the decode step's
+ * (a verify of K <= 4 tokens evaluates the same recurrence as one block, equal
+ * to it up to fp32 rounding).
  *   q, k, log_alpha : [N, K, H, d_k];  v : [N, K, H, d_v];  beta : [N, K, H]
  *   o      : [N, K, H, d_v] fp32, written for all K tokens
  *   state  : [N, H, d_k, d_v] fp32.  Without n_commit it is only read (verify).
