@@ -316,6 +316,30 @@ def size_query(lib, fn, *args):
     return code, out.value
 
 
+def test_backward_workspace_bytes(lib):
+    """The backward's workspace as the header states it: bf16, 176 KiB per
+    (64-token chunk id, head) -- the entering state and the leaving-state
+    gradient (2 x 64 KiB) and A, P, T (3 x 16 KiB) -- with ids below
+    rows / 64 + sequences + 1; fp32, one 64 KiB state per 8 tokens of each
+    sequence (dense) or fewer than T_total / 8 + N blocks (packed)."""
+    per_chunk = (2 * 128 * 128 + 3 * 64 * 64) * 4
+    assert per_chunk == 176 * 1024
+    for B, T, H in ((8, 4096, 32), (1, 1048576, 32), (3, 100, 5), (1, 17, 1)):
+        ids = B * T // 64 + B + 1
+        assert size_query(lib, "kda_backward_workspace_size", B, T, H, 128, 128, 1) == (OK, ids * H * per_chunk)
+        blocks = B * ((T + 7) // 8)
+        assert size_query(lib, "kda_backward_workspace_size", B, T, H, 128, 128, 0) == (OK, blocks * H * 65536)
+    for N, Tt, H in ((16, 360769, 32), (2000, 2000 * 37, 4)):
+        ids = Tt // 64 + N + 1
+        assert size_query(lib, "kda_varlen_backward_workspace_size", N, Tt, H, 128, 128, 1) == \
+            (OK, ids * H * per_chunk)
+        assert size_query(lib, "kda_varlen_backward_workspace_size", N, Tt, H, 128, 128, 0) == \
+            (OK, (Tt // 8 + N) * H * 65536)
+    # the training shape and the million-token shape of the header's figures
+    assert size_query(lib, "kda_backward_workspace_size", 8, 4096, 32, 128, 128, 1)[1] / 2 ** 30 < 2.8
+    assert size_query(lib, "kda_backward_workspace_size", 1, 1 << 20, 32, 128, 128, 1)[1] / 2 ** 30 < 88.1
+
+
 def test_workspace_size_validation(lib):
     """The size queries validate like the calls and report 0 bytes then;
     fp32 inputs and bf16 sequences of at most 16 tokens (token-by-token
