@@ -528,14 +528,6 @@ __device__ __forceinline__ void tile_put(const TileRaw<NT>& p, char* img)
     }
 }
 
-template <bool TRANS, int NT>
-__device__ __forceinline__ void tile_image(const float* src, char* img)
-{
-    TileRaw<NT> p;
-    request_tile<TRANS, NT>(src, p);
-    tile_put<TRANS, NT>(p, img);
-}
-
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 // hi*hi + hi*lo + lo*hi on the 16x16x16 bf16 instruction
