@@ -1190,9 +1190,10 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_dstate_kernel(const ChunkBwdA
 // from LDS images of dO, -B dW' and U and the rows of S0 and dS1 read from
 // the workspaces as B operands):
 //   dQt = dO S0^T, dKt = -B dW' S0^T, dKe = U dS1^T, dgam_L = rowsum(dS1 (.) S0);
-//   writes dq = dQt gam, dk = dKt gam + dKe gam_L / gam and the S0 part of
-//   d log a (the intra-chunk part adds the cross sums); dP = dO U^T (lower blocks).
-// Phase C: dT = dU (B W)^T (lower blocks) from images of dU and B W.
+//   forms dq = dQt gam, dk = dKt gam + dKe gam_L / gam and the S0 part of
+//   d log a, kept in registers for the intra-chunk part (which adds its
+//   terms and writes the totals); dP = dO U^T (lower blocks) into LDS.
+// Phase C: dT = dU (B W)^T (lower blocks) from images of dU and B W, into LDS.
 
 constexpr int INTRA_NT = SEQ_NT;   // the intra-chunk part runs in the same workgroup
 
