@@ -486,11 +486,13 @@ __device__ __forceinline__ bf16_t beta_raw(const ChunkBwdArgs& a, int64_t row0c,
 // A 64 x 64 fp32 tile from global memory into an image: TRANS = false stores
 // Z[r][i] at (row r, k i), TRANS = true at (row i, k r); PERM binding.  The
 // loads (request_tile) come apart from the stores (tile_put) so that they can
-// be issued a chunk ahead.
+// be issued a chunk ahead.  Each thread loads two 16-byte pieces: rows r and
+// r + 32 (TRANS = false) or the rows 2p, 2p + 1 of one row pair p (TRANS =
+// true), columns 4 (t mod 16) .. +3.
 template <int NT>
 struct TileRaw {
-    static constexpr int N = TSZ / 2 / NT;
-    float2 x[N];
+    static_assert(NT == 512, "two 16-byte pieces per thread");
+    float4 x[2];
 };
 
 template <bool TRANS, int NT>
@@ -498,17 +500,11 @@ __device__ __forceinline__ void request_tile(const float* src, TileRaw<NT>& p)
 {
     uint32_t tid = threadIdx.x;
     asm volatile("" : "+v"(tid));   // offsets recomputed per call, not kept across a loop
+    const uint32_t i = 4 * (tid & 15);
 #pragma unroll
-    for (int j = 0; j < TileRaw<NT>::N; ++j) {
-        const uint32_t q = tid + j * NT;
-        if (!TRANS) {
-            const uint32_t r = q >> 5, i = 2 * (q & 31);
-            p.x[j] = at(reinterpret_cast<const float2*>(src), (r * CH + i) >> 1);
-        } else {
-            // consecutive threads take consecutive columns i of one pair of rows
-            const uint32_t i = q & 63, r = 2 * (q >> 6);
-            p.x[j] = make_float2(at(src, r * CH + i), at(src, (r + 1) * CH + i));
-        }
+    for (int j = 0; j < 2; ++j) {
+        const uint32_t r = TRANS ? 2 * (tid >> 4) + j : (tid >> 4) + 32 * j;
+        p.x[j] = at(reinterpret_cast<const float4*>(src), (r * CH + i) >> 2);
     }
 }
 
@@ -520,12 +516,39 @@ __device__ __forceinline__ void tile_put(const TileRaw<NT>& p, char* img)
     // registers across a caller's loop: the thread index is made opaque)
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
+    const int i = 4 * (tid & 15);
+    if (!TRANS) {
 #pragma unroll
-    for (int j = 0; j < TileRaw<NT>::N; ++j) {
-        const int q = tid + j * NT;
-        if (!TRANS) img_put2<true>(img, plane, q >> 5, 2 * (q & 31), 2, p.x[j].x, p.x[j].y);
-        else img_put2<true>(img, plane, q & 63, 2 * (q >> 6), 2, p.x[j].x, p.x[j].y);
+        for (int j = 0; j < 2; ++j) {
+            const int r = (tid >> 4) + 32 * j;
+            img_put2<true>(img, plane, r, i, 2, p.x[j].x, p.x[j].y);
+            img_put2<true>(img, plane, r, i + 2, 2, p.x[j].z, p.x[j].w);
+        }
+    } else {
+        // the pair (Z[r][i + u], Z[r + 1][i + u]) is k = r, r + 1 of row i + u
+        const int r = 2 * (tid >> 4);
+        img_put2<true>(img, plane, i, r, 2, p.x[0].x, p.x[1].x);
+        img_put2<true>(img, plane, i + 1, r, 2, p.x[0].y, p.x[1].y);
+        img_put2<true>(img, plane, i + 2, r, 2, p.x[0].z, p.x[1].z);
+        img_put2<true>(img, plane, i + 3, r, 2, p.x[0].w, p.x[1].w);
     }
+}
+
+// The 4 x 4 transpose of the float4 values of the four lanes of a quad: lane y
+// holds row y (its four columns) and ends with column y (four rows), by two
+// exchanges on DPP quad permutations.
+__device__ __forceinline__ f32x4 quad_transpose(f32x4 a)
+{
+    const int y = threadIdx.x & 3;
+    const bool e = (y & 1) == 0, f = (y & 2) == 0;
+    // lanes y and y ^ 1 swap the off-diagonal entries of their 2 x 2 blocks
+    float r0 = dpp_mov<kDppSwap1>(e ? a[1] : a[0]);
+    float r1 = dpp_mov<kDppSwap1>(e ? a[3] : a[2]);
+    const f32x4 b = e ? (f32x4){a[0], r0, a[2], r1} : (f32x4){r0, a[1], r1, a[3]};
+    // lanes y and y ^ 2 swap the off-diagonal 2 x 2 blocks
+    r0 = dpp_mov<kDppSwap2>(f ? b[2] : b[0]);
+    r1 = dpp_mov<kDppSwap2>(f ? b[3] : b[1]);
+    return f ? (f32x4){b[0], b[1], r0, r1} : (f32x4){r0, r1, b[2], b[3]};
 }
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -817,7 +840,10 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_states_kernel(const ChunkBwdA
     __shared__ __attribute__((aligned(16))) char KT[2 * KT_PL];   // Kt: rows r, k = channels
     __shared__ __attribute__((aligned(16))) char KE[2 * KE_PL];   // Ke^T: rows c, k = tokens
     __shared__ __attribute__((aligned(16))) char TI[2 * T_PL];    // T: rows r, k = i
-    __shared__ __attribute__((aligned(16))) uint4 VS[2 * SEQ_NT]; // each thread's own V rows
+    // V rows (bf16) at a row stride of VLD elements: the four lane groups of a
+    // wave read rows 4 apart, which then fall in disjoint banks
+    constexpr int VLD = kDim + 8;
+    __shared__ __attribute__((aligned(16))) __bf16 VS[CH * VLD];
     __shared__ float tot[(SEQ_NT / 64) * kDim];
     __shared__ float bs[CH], gls[kDim];
 
@@ -834,10 +860,11 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_states_kernel(const ChunkBwdA
     state_load(a.s0 ? a.s0 + (n * H + h) * SS : nullptr, slo, S);
 
     // The inputs of chunk c + 1 are requested while chunk c's products run:
-    // log alpha and k, the T tile, this thread's V rows and beta.
+    // log alpha and k, the T tile, V (row t / 8, columns 16 (t mod 8) .. +15)
+    // and beta.
     ChunkRaw<SEQ_NT, false> raw;
     TileRaw<SEQ_NT> traw;
-    uint32_t vraw[16];
+    uint4 vraw0, vraw1;   // (named registers: an array of two ended up in scratch memory)
     bf16_t braw = {0};   // raw bits, widened where staged (widening here would wait for the load)
     auto request_chunk = [&](int64_t c) {
         const int64_t row0c = row0 + c * CH;
@@ -849,13 +876,9 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_states_kernel(const ChunkBwdA
         // values are consumed (a select here would wait for the loads)
         const bf16_t* vb = a.v + (row0c * H + h) * kDim;
         const uint32_t rs = H * kDim;
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int r = 16 * m + 4 * g + x;
-                vraw[4 * m + x] = at(vb, col + static_cast<uint32_t>(min(r, L - 1)) * rs).bits;
-            }
+        const uint32_t ve = static_cast<uint32_t>(min(t >> 3, L - 1)) * rs + 16 * (t & 7);
+        vraw0 = at(reinterpret_cast<const uint4*>(vb), ve >> 3);
+        vraw1 = at(reinterpret_cast<const uint4*>(vb), (ve >> 3) + 1);
         braw = at(a.beta + row0c * H + h, static_cast<uint32_t>(min(t, L - 1)) * H);
     };
     if (nch > 0) request_chunk(0);
@@ -869,15 +892,11 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_states_kernel(const ChunkBwdA
         const int L = FULL ? CH : static_cast<int>(min<int64_t>(CH, len - c * CH));
         lds_sync();  // the previous chunk's products are done with the images
         tile_put<false, SEQ_NT>(traw, TI);
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int x = 0; x < 4; ++x)
-                if (16 * m + 4 * g + x >= L) vraw[4 * m + x] = 0u;
-        VS[2 * t] = make_uint4(vraw[0] | (vraw[1] << 16), vraw[2] | (vraw[3] << 16),
-                               vraw[4] | (vraw[5] << 16), vraw[6] | (vraw[7] << 16));
-        VS[2 * t + 1] = make_uint4(vraw[8] | (vraw[9] << 16), vraw[10] | (vraw[11] << 16),
-                                   vraw[12] | (vraw[13] << 16), vraw[14] | (vraw[15] << 16));
+        {
+            uint4* vs = reinterpret_cast<uint4*>(&VS[(t >> 3) * VLD + 16 * (t & 7)]);
+            vs[0] = vraw0;
+            vs[1] = vraw1;
+        }
         if (t < CH) bs[t] = t < L ? widen(braw) : 0.f;
         Staged<SEQ_NT> st;
         stage_raw<SEQ_NT, false>(raw, tot, st);
@@ -925,10 +944,9 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_states_kernel(const ChunkBwdA
 #pragma unroll
                 for (int x = 0; x < 4; ++x) at(s0dst + (16 * tt + x) * kDim, slo) = S[tt][x];
         }
-        // W = V - X (parked in dk for the grads kernel), then B W
+        // W = V - X (parked in dk for the grads kernel), then B W; rows from
+        // L on hold row L - 1 of V and are taken as zeros
         {
-            const uint4 v0 = VS[2 * t], v1 = VS[2 * t + 1];
-            const uint32_t vw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
             float* wdst = a.dk + (row0c * H + h) * kDim;
             const uint32_t rs = H * kDim;
 #pragma unroll
@@ -936,10 +954,10 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_states_kernel(const ChunkBwdA
                 f32x4 w;
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
-                    const int e = 4 * m + x;
-                    const float v = (e & 1) ? bf_hi(vw[e >> 1]) : bf_lo(vw[e >> 1]);
-                    w[x] = v - X[m][x];
-                    X[m][x] = bs[16 * m + 4 * g + x] * w[x];
+                    const int r = 16 * m + 4 * g + x;
+                    const float v = (float)VS[r * VLD + col];
+                    w[x] = (FULL || r < L ? v : 0.f) - X[m][x];
+                    X[m][x] = bs[r] * w[x];
                 }
                 park4(wdst, rs, m, g, col, L, w);
             }
@@ -1031,16 +1049,18 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_dstate_kernel(const ChunkBwdA
         request_tile<true, SEQ_NT>(apt + 2 * TSZ, traw);
         request<SEQ_NT, true>(a, row0c, L, h, raw);
         // rows from L on read row L - 1; they are replaced by zeros where the
-        // values are consumed (a select here would wait for the loads)
+        // values are consumed (a select here would wait for the loads).  Lane
+        // (g, 4 q + y) loads row 16 m + 4 g + y, columns 16 w + 4 q .. +3; a
+        // quad transpose at staging gives it column 16 w + 4 q + y of the
+        // four rows 16 m + 4 g + x.
         const float* ob = a.d_o + (row0c * H + h) * kDim;
         const uint32_t rs = H * kDim;
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int r = 16 * m + 4 * g + x;
-                oraw[m][x] = at(ob, col + static_cast<uint32_t>(min(r, L - 1)) * rs);
-            }
+        for (int m = 0; m < 4; ++m) {
+            const int r = 16 * m + 4 * g + (lane & 3);
+            oraw[m] = at(reinterpret_cast<const f32x4*>(ob),
+                         (16 * wave + 4 * ((lane & 15) >> 2) + static_cast<uint32_t>(min(r, L - 1)) * rs) >> 2);
+        }
         braw = at(a.beta + row0c * H + h, static_cast<uint32_t>(min(t, L - 1)) * H);
     };
     if (nch > 0) request_chunk(nch - 1);
@@ -1057,10 +1077,12 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_dstate_kernel(const ChunkBwdA
         tile_put<true, SEQ_NT>(traw, TT);
         if (t < CH) bs[t] = t < L ? widen(braw) : 0.f;
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
+        for (int m = 0; m < 4; ++m) {
+            oraw[m] = quad_transpose(oraw[m]);
 #pragma unroll
             for (int x = 0; x < 4; ++x)
                 if (16 * m + 4 * g + x >= L) oraw[m][x] = 0.f;
+        }
         // dO in accumulator layout (rows r = 16m + 4g + x of column col), split
         bf16x8 oh[2], ol[2];
 #pragma unroll
@@ -1200,8 +1222,8 @@ constexpr int INTRA_NT = SEQ_NT;   // the intra-chunk part runs in the same work
 // The intra-chunk part's inputs that do not depend on the gradient part (A and T
 // tiles, log alpha, k, q, beta), requested while the gradient part still runs.
 struct IntraReq {
-    static constexpr int NE = TSZ / INTRA_NT;
-    float ar[NE], tr[NE];
+    static constexpr int NE = TSZ / INTRA_NT / 4;   // 16-byte pieces per thread and tile
+    f32x4 ar[NE], tr[NE];
     bf16_t braw;
     ChunkRaw<INTRA_NT, true> raw;
 };
@@ -1210,12 +1232,12 @@ __device__ __forceinline__ void intra_request(const ChunkBwdArgs& a, int64_t id,
                                               IntraReq& rq)
 {
     const int t = threadIdx.x;
-    const float* apt = a.ws_apt + (id * a.H + h) * (3 * TSZ);
+    const f32x4* apt = reinterpret_cast<const f32x4*>(a.ws_apt + (id * a.H + h) * (3 * TSZ));
 #pragma unroll
     for (int j = 0; j < IntraReq::NE; ++j) {
-        const int e = t + j * INTRA_NT;
+        const int e = t + j * INTRA_NT;   // 16-byte piece: row e / 16, columns 4 (e mod 16) .. +3
         rq.ar[j] = apt[e];
-        rq.tr[j] = apt[2 * TSZ + e];
+        rq.tr[j] = apt[2 * TSZ / 4 + e];
     }
     rq.braw = beta_raw(a, row0c, L, h);
     request<INTRA_NT, true>(a, row0c, L, h, rq.raw);
@@ -1624,8 +1646,8 @@ __device__ __forceinline__ void intra_part(const ChunkBwdArgs& a, char* sm, Intr
     // ---- dP and dT are in LDS (from the gradient part); the A and T tiles,
     // beta and the staging inputs were requested during the gradient part (rq)
     constexpr int NE = IntraReq::NE;
-    const float (&ar)[NE] = rq.ar;
-    const float (&tr)[NE] = rq.tr;
+    const f32x4 (&ar)[NE] = rq.ar;
+    const f32x4 (&tr)[NE] = rq.tr;
     const bf16_t braw = rq.braw;
     ChunkRaw<INTRA_NT, true>& raw = rq.raw;
     // channel cc = 16 w + l16 of the rows 16 R + 4 g + x (as the gradient part's terms)
@@ -1637,9 +1659,9 @@ __device__ __forceinline__ void intra_part(const ChunkBwdArgs& a, char* sm, Intr
     // ---- phase 1: T and A
 #pragma unroll
     for (int j = 0; j < NE; ++j) {
-        const int e = t + j * INTRA_NT, r = e >> 6, i = e & 63;
-        As[r * PLD + i] = ar[j];
-        Ts[r * PLD + i] = tr[j];
+        const int e = t + j * INTRA_NT, r = e >> 4, i = 4 * (e & 15);
+        *reinterpret_cast<f32x4*>(&As[r * PLD + i]) = ar[j];
+        *reinterpret_cast<f32x4*>(&Ts[r * PLD + i]) = tr[j];
     }
     if (t < CH) bs[t] = t < L ? widen(braw) : 0.f;
     lds_sync();
