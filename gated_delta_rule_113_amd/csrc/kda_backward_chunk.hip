@@ -464,16 +464,6 @@ __device__ __forceinline__ void stage_raw(ChunkRaw<NT, WITHQ>& p, float* tot, St
     s.gl[1] = a1;
 }
 
-template <int NT, bool WITHQ>
-__device__ __forceinline__ void stage(const ChunkBwdArgs& a, int64_t row0c, int L, int h, float* tot,
-                                      Staged<NT>& s)
-{
-    ChunkRaw<NT, WITHQ> p;
-    request<NT, WITHQ>(a, row0c, L, h, p);
-    __builtin_amdgcn_sched_barrier(0);   // all requests issued before the first use
-    stage_raw<NT, WITHQ>(p, tot, s);
-}
-
 // beta of the chunk's row t mod 64 as raw bits, loaded without a branch (a
 // row from L on reads row 0: its value is to be replaced by zero where it is
 // used), to be widened where it is staged
@@ -481,6 +471,80 @@ __device__ __forceinline__ bf16_t beta_raw(const ChunkBwdArgs& a, int64_t row0c,
 {
     const int t = threadIdx.x & (CH - 1);
     return a.beta[(row0c + (t < L ? t : 0)) * a.H + h];
+}
+
+// log alpha, k and q of one chunk, four channels per thread: thread t takes
+// channels 4 (t mod 32) .. +3 of the TOK tokens TOK (t / 32) .. +TOK-1, so
+// that each token is one 16-byte load of log alpha and one 8-byte load each
+// of k and q.  Rows from L on load row 0 and are zeroed when staged.
+template <int NT>
+struct Raw4 {
+    static constexpr int TOK = 32 * CH / NT;
+    float4 la[TOK];
+    uint2 k[TOK], q[TOK];
+    int L;
+};
+
+template <int NT>
+__device__ __forceinline__ void request4(const ChunkBwdArgs& a, int64_t row0c, int L, int h, Raw4<NT>& p)
+{
+    constexpr int TOK = Raw4<NT>::TOK;
+    const int t = threadIdx.x;
+    const int c0 = 4 * (t & 31), r0 = TOK * (t >> 5);
+    const int64_t base = (row0c * a.H + h) * kDim;
+    const uint32_t rstride = static_cast<uint32_t>(a.H) * kDim;
+    p.L = L;
+#pragma unroll
+    for (int j = 0; j < TOK; ++j) {
+        const int r = r0 + j;
+        const uint32_t e4 = (static_cast<uint32_t>(c0) + static_cast<uint32_t>(r < L ? r : 0) * rstride) >> 2;
+        p.la[j] = at(reinterpret_cast<const float4*>(a.la + base), e4);
+        p.k[j] = at(reinterpret_cast<const uint2*>(a.k + base), e4);
+        p.q[j] = at(reinterpret_cast<const uint2*>(a.q + base), e4);
+    }
+}
+
+// The cumulative log2-decay G of the thread's elements (rows from L on zeroed
+// in p first: they decay nothing) and G at the chunk's last token; one
+// barrier, for the prefix over the waves through tot (NT / 64 x 128 floats).
+// The two halves of a wave hold neighbouring token groups.
+template <int NT>
+__device__ __forceinline__ void stage4(Raw4<NT>& p, float* tot, float4 (&gv)[Raw4<NT>::TOK], float4& gl)
+{
+    constexpr int TOK = Raw4<NT>::TOK;
+    const int t = threadIdx.x, c0 = 4 * (t & 31), r0 = TOK * (t >> 5);
+    float4 run = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < TOK; ++j) {
+        const bool in = r0 + j < p.L;
+        const float4 x = p.la[j];
+        p.k[j] = in ? p.k[j] : make_uint2(0u, 0u);
+        p.q[j] = in ? p.q[j] : make_uint2(0u, 0u);
+        run.x += in ? x.x * kLog2e : 0.f;
+        run.y += in ? x.y * kLog2e : 0.f;
+        run.z += in ? x.z * kLog2e : 0.f;
+        run.w += in ? x.w * kLog2e : 0.f;
+        gv[j] = run;
+    }
+    const float4 other = make_float4(__shfl_xor(run.x, 32), __shfl_xor(run.y, 32), __shfl_xor(run.z, 32),
+                                     __shfl_xor(run.w, 32));
+    const int w = wave_id();
+    const bool upper = (t & 32) != 0;
+    if (!upper)
+        *reinterpret_cast<float4*>(&tot[w * kDim + c0]) =
+            make_float4(run.x + other.x, run.y + other.y, run.z + other.z, run.w + other.w);
+    lds_sync();
+    float4 pre = upper ? other : make_float4(0.f, 0.f, 0.f, 0.f), all = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < NT / 64; ++u) {
+        const float4 x = *reinterpret_cast<const float4*>(&tot[u * kDim + c0]);
+        if (u < w) pre = make_float4(pre.x + x.x, pre.y + x.y, pre.z + x.z, pre.w + x.w);
+        all = make_float4(all.x + x.x, all.y + x.y, all.z + x.z, all.w + x.w);
+    }
+#pragma unroll
+    for (int j = 0; j < TOK; ++j)
+        gv[j] = make_float4(gv[j].x + pre.x, gv[j].y + pre.y, gv[j].z + pre.z, gv[j].w + pre.w);
+    gl = all;
 }
 
 // A 64 x 64 fp32 tile from global memory into an image: TRANS = false stores
@@ -634,16 +698,20 @@ __global__ __launch_bounds__(PREP_NT, 2) void chunk_prep_kernel(const ChunkBwdAr
     const int t = threadIdx.x, lane = t & 63, wave = wave_id(), g = lane >> 4, l16 = lane & 15;
 
     {
+        Raw4<PREP_NT> raw;
+        request4<PREP_NT>(a, row0c, L, h, raw);
         const bf16_t braw = beta_raw(a, row0c, L, h);   // in flight with the staging loads
-        Staged<PREP_NT> st;
-        stage<PREP_NT, true>(a, row0c, L, h, tot, st);
+        __builtin_amdgcn_sched_barrier(0);              // all requests issued before the first use
+        float4 gv[Raw4<PREP_NT>::TOK], gl;
+        stage4<PREP_NT>(raw, tot, gv, gl);
         if (t < CH) bs[t] = t < L ? widen(braw) : 0.f;
+        const int c0 = 4 * (t & 31), r0 = Raw4<PREP_NT>::TOK * (t >> 5);
 #pragma unroll
-        for (int j = 0; j < Staged<PREP_NT>::TOK; ++j) {
-            const int r = st.r0 + j;
-            *reinterpret_cast<float2*>(&Gs[r * GLD + st.c0]) = make_float2(st.g[j][0], st.g[j][1]);
-            *reinterpret_cast<bf16x2*>(&Ks[r * BLD + st.c0]) = (bf16x2){(__bf16)st.kk[j][0], (__bf16)st.kk[j][1]};
-            *reinterpret_cast<bf16x2*>(&Qs[r * BLD + st.c0]) = (bf16x2){(__bf16)st.qq[j][0], (__bf16)st.qq[j][1]};
+        for (int j = 0; j < Raw4<PREP_NT>::TOK; ++j) {
+            const int r = r0 + j;
+            *reinterpret_cast<float4*>(&Gs[r * GLD + c0]) = gv[j];
+            *reinterpret_cast<uint2*>(&Ks[r * BLD + c0]) = raw.k[j];
+            *reinterpret_cast<uint2*>(&Qs[r * BLD + c0]) = raw.q[j];
         }
     }
     lds_sync();
