@@ -1287,8 +1287,10 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_dstate_kernel(const ChunkBwdA
 
 constexpr int INTRA_NT = SEQ_NT;   // the intra-chunk part runs in the same workgroup
 
-// The intra-chunk part's inputs that do not depend on the gradient part (A and T
-// tiles, log alpha, k, q, beta), requested while the gradient part still runs.
+// The intra-chunk part's inputs: the A and T tiles, requested while the
+// gradient part still runs, and from the gradient part's staging the raw
+// keys, queries (rows from L on zeroed) and beta.  G stays in the gradient
+// part's LDS tile.
 struct IntraReq {
     static constexpr int NE = TSZ / INTRA_NT / 4;   // 16-byte pieces per thread and tile
     f32x4 ar[NE], tr[NE];
@@ -1307,8 +1309,6 @@ __device__ __forceinline__ void intra_request(const ChunkBwdArgs& a, int64_t id,
         rq.ar[j] = apt[e];
         rq.tr[j] = apt[2 * TSZ / 4 + e];
     }
-    rq.braw = beta_raw(a, row0c, L, h);
-    request<INTRA_NT, true>(a, row0c, L, h, rq.raw);
 }
 
 // The gradient part's terms of dq, dk and d log alpha, held in registers for
@@ -1328,7 +1328,8 @@ struct GradsLds {
     float bs[CH], gLs[kDim], dbr[SEQ_NT / 64][CH], dpd[SEQ_NT / 64][CH];
     float Pd[CH * PLD];   // dP (i <= r; the blocks above the diagonal are not written)
 };
-constexpr int GR_DT_OFF = 4 * GR_KT_PL;   // dT (fp32, row stride PLD) over the image of U
+// dT (fp32, row stride PLD) at the end of the image of U
+constexpr int GR_DT_OFF = 6 * GR_KT_PL - CH * PLD * 4;
 static_assert(CH * PLD * 4 <= 2 * GR_KT_PL, "dT fits where the image of U was");
 
 __device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm, IntraReq& rq, Partials& pp)
@@ -1362,9 +1363,10 @@ __device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm, Intr
     // store: one round of latency, and no wait for a load also waits for
     // earlier stores (loads and stores share one counter).  U, W, dU and dW'
     // were parked in dq, dk, d log alpha and dv by the state sweeps.
-    ChunkRaw<SEQ_NT, true> raw;
+    ChunkRaw<SEQ_NT, true>& raw = rq.raw;   // kept: the intra-chunk part stages its k and q
     request<SEQ_NT, true>(a, row0c, L, h, raw);
-    const bf16_t braw = beta_raw(a, row0c, L, h);
+    rq.braw = beta_raw(a, row0c, L, h);
+    const bf16_t& braw = rq.braw;
     f32x4 U[4], dU[4], dW[4], W[4], dO[4];
     const int64_t e0 = (row0c * H + h) * kDim + col;
     {
@@ -1669,21 +1671,23 @@ __device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm, Intr
 // block exceeds 2^-96) get that block pairwise on the vector ALUs.  Then dL,
 // its reverse cumulative sum over the chunk, and the totals of dq and dk.
 
-// LDS of the intra-chunk part.  dP and dT are where the gradient part left
+// LDS of the intra-chunk part.  dP, dT and G are where the gradient part left
 // them; everything else overlays the gradient part's dead regions.
 struct IntraLds {
-    float U1[2 * CH * PLD];   // T and A, then G
+    float U1[2 * CH * PLD];   // T and A, then (phase 2) the diagonal blocks' cross sums
     __bf16 Ks[CH * kDim];
-    float bs[CH], db2[CH], tot[(INTRA_NT / 64) * kDim];
-    char pad0[GR_DT_OFF - 2 * CH * PLD * 4 - CH * kDim * 2 - (2 * CH + (INTRA_NT / 64) * kDim) * 4];
-    float Ad[CH * PLD];       // dT, Y, dM, then dA
     __bf16 Qs[CH * kDim];
-    float DgS[16 * INTRA_NT];   // per thread: the cross sums inside the diagonal blocks
-    char pad1[offsetof(GradsLds, Pd) - GR_DT_OFF - CH * PLD * 4 - CH * kDim * 2 - 16 * INTRA_NT * 4];
+    float bs[CH], db2[CH];
+    char pad0[GR_DT_OFF - 2 * CH * PLD * 4 - 2 * CH * kDim * 2 - 2 * CH * 4];
+    float Ad[CH * PLD];       // dT, Y, dM, then dA
+    float Gs[CH * GLD];       // G (the gradient part's tile)
+    char pad1[offsetof(GradsLds, Pd) - offsetof(GradsLds, Gs) - CH * GLD * 4];
     float Pd[CH * PLD];       // dP (i <= r)
 };
 static_assert(offsetof(IntraLds, Ad) == GR_DT_OFF, "dT where the gradient part wrote it");
+static_assert(offsetof(IntraLds, Gs) == offsetof(GradsLds, Gs), "G where the gradient part staged it");
 static_assert(offsetof(IntraLds, Pd) == offsetof(GradsLds, Pd), "dP where the gradient part wrote it");
+static_assert(16 * INTRA_NT * 4 <= 2 * CH * PLD * 4, "the cross sums fit where T and A were");
 
 __device__ __forceinline__ void intra_part(const ChunkBwdArgs& a, char* sm, IntraReq& rq, const Partials& pp)
 {
@@ -1695,12 +1699,10 @@ __device__ __forceinline__ void intra_part(const ChunkBwdArgs& a, char* sm, Intr
     __bf16* Qs = S_.Qs;
     float* bs = S_.bs;
     float* db2 = S_.db2;
-    float* tot = S_.tot;
-    float* DgS = S_.DgS;
-    static_assert(CH * kDim <= 2 * CH * PLD, "G fits where T and A were");
+    const float* Gs = S_.Gs;
     float* Ts = U1;
     float* As = U1 + CH * PLD;
-    float* Gs = U1;
+    float* DgS = U1;   // after phase 1
 
     const int H = a.H;
     const int64_t id = blockIdx.x / H;
@@ -1711,25 +1713,36 @@ __device__ __forceinline__ void intra_part(const ChunkBwdArgs& a, char* sm, Intr
     const int L = static_cast<int>(min<int64_t>(CH, seq_len(a, n) - c * CH));
     const int t = threadIdx.x, lane = t & 63, wave = wave_id(), g = lane >> 4, l16 = lane & 15;
 
-    // ---- dP and dT are in LDS (from the gradient part); the A and T tiles,
-    // beta and the staging inputs were requested during the gradient part (rq)
+    // ---- dP, dT and G are in LDS (from the gradient part); the A and T
+    // tiles were requested during the gradient part, k, q and beta kept from
+    // its staging (rq)
     constexpr int NE = IntraReq::NE;
     const f32x4 (&ar)[NE] = rq.ar;
     const f32x4 (&tr)[NE] = rq.tr;
     const bf16_t braw = rq.braw;
-    ChunkRaw<INTRA_NT, true>& raw = rq.raw;
+    const ChunkRaw<INTRA_NT, true>& raw = rq.raw;
     // channel cc = 16 w + l16 of the rows 16 R + 4 g + x (as the gradient part's terms)
     const int cc = 16 * wave + l16;
     const int64_t rs = static_cast<int64_t>(H) * kDim;
     const int64_t e0 = (row0c * H + h) * kDim + cc;
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- phase 1: T and A
+    // ---- phase 1: T and A; k and q for phase 2 (the gradient part's
+    // staging mapping: channels 2 (t mod 64), +1 of tokens TOK (t / 64) ..)
 #pragma unroll
     for (int j = 0; j < NE; ++j) {
         const int e = t + j * INTRA_NT, r = e >> 4, i = 4 * (e & 15);
         *reinterpret_cast<f32x4*>(&As[r * PLD + i]) = ar[j];
         *reinterpret_cast<f32x4*>(&Ts[r * PLD + i]) = tr[j];
+    }
+    {
+        constexpr int TOK = Staged<INTRA_NT>::TOK;
+        const int c0 = 2 * (t & 63), r0 = TOK * wave;
+#pragma unroll
+        for (int j = 0; j < TOK; ++j) {
+            *reinterpret_cast<uint32_t*>(&Ks[(r0 + j) * kDim + c0]) = raw.k[j];
+            *reinterpret_cast<uint32_t*>(&Qs[(r0 + j) * kDim + c0]) = raw.q[j];
+        }
     }
     if (t < CH) bs[t] = t < L ? widen(braw) : 0.f;
     lds_sync();
@@ -1807,22 +1820,10 @@ __device__ __forceinline__ void intra_part(const ChunkBwdArgs& a, char* sm, Intr
         const int r = e >> 6, i = e & 63;
         Ad[r * PLD + i] = i < r ? bs[r] * Ad[r * PLD + i] : 0.f;   // dA
     }
-    // ---- phase 2 staging: G (over T and A), k, q
-    {
-        Staged<INTRA_NT> st;
-        stage_raw<INTRA_NT, true>(raw, tot, st);   // its barrier also ends phase 1
-#pragma unroll
-        for (int j = 0; j < Staged<INTRA_NT>::TOK; ++j) {
-            const int r = st.r0 + j;
-            *reinterpret_cast<float2*>(&Gs[r * kDim + st.c0]) = make_float2(st.g[j][0], st.g[j][1]);
-            *reinterpret_cast<bf16x2*>(&Ks[r * kDim + st.c0]) = (bf16x2){(__bf16)st.kk[j][0], (__bf16)st.kk[j][1]};
-            *reinterpret_cast<bf16x2*>(&Qs[r * kDim + st.c0]) = (bf16x2){(__bf16)st.qq[j][0], (__bf16)st.qq[j][1]};
-        }
-    }
-    lds_sync();
+    lds_sync();   // phase 1 is done with T and A: the cross sums take their place
 
     // ---- phase 2: wave w on channels cc = 16w + l16; rows 16R + 4g + x of each block R
-    auto Gv = [&](int r) { return Gs[r * kDim + cc]; };
+    auto Gv = [&](int r) { return Gs[r * GLD + cc]; };
     auto Kv = [&](int r) { return (float)Ks[r * kDim + cc]; };
     auto Qv = [&](int r) { return (float)Qs[r * kDim + cc]; };
     // The cross sums C_j = sum_{r >= j > i} X_ri of the decay products
