@@ -1465,20 +1465,28 @@ __device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm, Intr
         }
 
     // ---- phase B images (natural binding, rows = tokens, k = value columns):
-    // dO, -B dW', U.  Even lanes store their value and the odd neighbour's.
-    auto put_pair = [&](int off, int r, float x) {
-        const float y = dpp_mov<kDppSwap1>(x);
-        if ((l16 & 1) == 0) img_put2<false>(img + off, KT_PL, r, col, 4, x, y);
+    // dO, -B dW', U.  An image element pair is two neighbouring columns held
+    // by the lanes col and col ^ 1 (l16 even / odd): of the four rows 4g + x
+    // of row block m, the even lane stores rows x = 0, 1 and the odd lane rows
+    // x = 2, 3, each after taking the neighbour's two values (DPP).
+    const bool even = (l16 & 1) == 0;
+    const int kc = col & ~1;
+    auto put_quad = [&](int off, int m, f32x4 v) {
+        const float s0 = dpp_mov<kDppSwap1>(even ? v[2] : v[0]);
+        const float s1 = dpp_mov<kDppSwap1>(even ? v[3] : v[1]);
+        const int ra = 16 * m + 4 * g + (even ? 0 : 2);
+        img_put2<false>(img + off, KT_PL, ra, kc, 4, even ? v[0] : s0, even ? s0 : v[2]);
+        img_put2<false>(img + off, KT_PL, ra + 1, kc, 4, even ? v[1] : s1, even ? s1 : v[3]);
     };
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < 4; ++m) {
+        f32x4 nw;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int r = 16 * m + 4 * g + x;
-            put_pair(OFF_I0, r, dO[m][x]);
-            put_pair(OFF_I1, r, -bs[r] * dW[m][x]);
-            put_pair(OFF_I2, r, U[m][x]);
-        }
+        for (int x = 0; x < 4; ++x) nw[x] = -bs[16 * m + 4 * g + x] * dW[m][x];
+        put_quad(OFF_I0, m, dO[m]);
+        put_quad(OFF_I1, m, nw);
+        put_quad(OFF_I2, m, U[m]);
+    }
     lds_sync();
 
     // ---- phase B: wave w on channels cw = 16w + l16; rows of S0 and dS1 as B operands
@@ -1613,13 +1621,13 @@ __device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm, Intr
 
     // ---- phase C: images of dU and B W, then dT = dU (B W)^T on the lower blocks
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < 4; ++m) {
+        f32x4 bw;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int r = 16 * m + 4 * g + x;
-            put_pair(OFF_I0, r, dU[m][x]);
-            put_pair(OFF_I1, r, bs[r] * W[m][x]);
-        }
+        for (int x = 0; x < 4; ++x) bw[x] = bs[16 * m + 4 * g + x] * W[m][x];
+        put_quad(OFF_I0, m, dU[m]);
+        put_quad(OFF_I1, m, bw);
+    }
     lds_sync();
     // dT (i < r) into LDS over the image of U, zero elsewhere: the 10 lower
     // blocks from the products, the 6 upper ones as zeros
