@@ -1681,12 +1681,15 @@ __device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm, Intr
 
 // LDS of the intra-chunk part.  dP, dT and G are where the gradient part left
 // them; everything else overlays the gradient part's dead regions.
+// k and q are kept channel-major (row stride KLD tokens), so that the rows a
+// lane reads for its channel are contiguous.
+constexpr int KLD = CH + 8;
 struct IntraLds {
     float U1[2 * CH * PLD];   // T and A, then (phase 2) the diagonal blocks' cross sums
-    __bf16 Ks[CH * kDim];
-    __bf16 Qs[CH * kDim];
+    __bf16 Ks[kDim * KLD];
+    __bf16 Qs[kDim * KLD];
     float bs[CH], db2[CH];
-    char pad0[GR_DT_OFF - 2 * CH * PLD * 4 - 2 * CH * kDim * 2 - 2 * CH * 4];
+    char pad0[GR_DT_OFF - 2 * CH * PLD * 4 - 2 * kDim * KLD * 2 - 2 * CH * 4];
     float Ad[CH * PLD];       // dT, Y, dM, then dA
     float Gs[CH * GLD];       // G (the gradient part's tile)
     char pad1[offsetof(GradsLds, Pd) - offsetof(GradsLds, Gs) - CH * GLD * 4];
@@ -1746,10 +1749,14 @@ __device__ __forceinline__ void intra_part(const ChunkBwdArgs& a, char* sm, Intr
     {
         constexpr int TOK = Staged<INTRA_NT>::TOK;
         const int c0 = 2 * (t & 63), r0 = TOK * wave;
+        // (pairs of tokens per channel: the raw pairs hold two channels of one token)
 #pragma unroll
-        for (int j = 0; j < TOK; ++j) {
-            *reinterpret_cast<uint32_t*>(&Ks[(r0 + j) * kDim + c0]) = raw.k[j];
-            *reinterpret_cast<uint32_t*>(&Qs[(r0 + j) * kDim + c0]) = raw.q[j];
+        for (int j = 0; j < TOK; j += 2) {
+            const uint32_t k0 = raw.k[j], k1 = raw.k[j + 1], q0 = raw.q[j], q1 = raw.q[j + 1];
+            *reinterpret_cast<uint32_t*>(&Ks[c0 * KLD + r0 + j]) = (k0 & 0xffffu) | (k1 << 16);
+            *reinterpret_cast<uint32_t*>(&Ks[(c0 + 1) * KLD + r0 + j]) = (k0 >> 16) | (k1 & 0xffff0000u);
+            *reinterpret_cast<uint32_t*>(&Qs[c0 * KLD + r0 + j]) = (q0 & 0xffffu) | (q1 << 16);
+            *reinterpret_cast<uint32_t*>(&Qs[(c0 + 1) * KLD + r0 + j]) = (q0 >> 16) | (q1 & 0xffff0000u);
         }
     }
     if (t < CH) bs[t] = t < L ? widen(braw) : 0.f;
@@ -1832,8 +1839,8 @@ __device__ __forceinline__ void intra_part(const ChunkBwdArgs& a, char* sm, Intr
 
     // ---- phase 2: wave w on channels cc = 16w + l16; rows 16R + 4g + x of each block R
     auto Gv = [&](int r) { return Gs[r * GLD + cc]; };
-    auto Kv = [&](int r) { return (float)Ks[r * kDim + cc]; };
-    auto Qv = [&](int r) { return (float)Qs[r * kDim + cc]; };
+    auto Kv = [&](int r) { return (float)Ks[cc * KLD + r]; };
+    auto Qv = [&](int r) { return (float)Qs[cc * KLD + r]; };
     // The cross sums C_j = sum_{r >= j > i} X_ri of the decay products
     // X_ri = (dA_ri k_r + dP_ri q_r) k_i 2^(G_r - G_i) (this lane's channel)
     // are the A/P part of d log a_j.  By blocks, for j in block J: Ab[J] the
