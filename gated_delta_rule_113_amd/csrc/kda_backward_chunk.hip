@@ -41,10 +41,10 @@
 // sequences + 1, so dense and packed input share one workspace layout):
 //   prep   (one workgroup per chunk)  A, P and T of every chunk;
 //   states (one per unit, in order)   the entering state S0 of every chunk, and
-//                                     W and U, parked in dk and dq;
+//                                     W, parked in dk;
 //   dstate (one per unit, reversed)   the gradient dS1 in every chunk's leaving
-//                                     state, dU and dW' (parked in d log a and
-//                                     dv), and the initial-state gradient;
+//                                     state, dU (parked in d log a), and the
+//                                     initial-state gradient;
 //   grads  (one per chunk)            first the gradient part: dV, the S0/dS1
 //                                     parts of dq, dk and dL, db's first term,
 //                                     dP and dT; then the intra-chunk part: dM,
@@ -1045,13 +1045,7 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_states_kernel(const ChunkBwdA
                 U[m] = mma3(ah, al, wh, wl, U[m]);
             }
         }
-        // U (parked in dq for the grads kernel), then S1 = Diag(gam_L) S0 + Ke^T U
-        {
-            float* udst = a.dq + (row0c * H + h) * kDim;
-            const uint32_t rs = H * kDim;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) park4(udst, rs, m, g, col, L, U[m]);
-        }
+        // S1 = Diag(gam_L) S0 + Ke^T U
         bf16x8 uh[2], ul[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s) bfrag(U[2 * s], U[2 * s + 1], uh[s], ul[s]);
@@ -1229,13 +1223,12 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_dstate_kernel(const ChunkBwdA
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        // dU and dW' parked in d log alpha and dv for the grads kernel, then -B dW'
+        // dU parked in d log alpha for the grads kernel, then -B dW'
         __builtin_amdgcn_sched_barrier(0);
         {
             const int64_t base = (row0c * H + h) * kDim;
             const uint32_t rs = H * kDim;
             park_all(a.dla + base, rs, g, col, L, dU);
-            park_all(a.dv + base, rs, g, col, L, nW);
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -1272,9 +1265,10 @@ __global__ __launch_bounds__(SEQ_NT, 1) void chunk_dstate_kernel(const ChunkBwdA
 // ================================================================ grads: gradient part
 //
 // Per chunk of one head (512 threads; the first part of the grads kernel).
-// Phase A, wave w on value columns 16w..16w+15 (accumulator layout): U and
-// W = V - Kt S0 (parked in dq and dk by the states kernel), dU and dW' = T^T dU
-// (parked in d log alpha and dv by the dstate kernel), dO;
+// Phase A, wave w on value columns 16w..16w+15 (accumulator layout):
+// W = V - Kt S0 (parked in dk by the states kernel), dU (parked in d log alpha
+// by the dstate kernel), dO; U = T B W and dW' = T^T dU formed again from the
+// T tile;
 //   writes dv = B dW' and the row sums of dW' (.) W (db, first term).
 // Phase B, wave w on channels 16w..16w+15 (sums over the value columns j,
 // from LDS images of dO, -B dW' and U and the rows of S0 and dS1 read from
@@ -1361,12 +1355,16 @@ __device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm, Intr
 
     // ---- every global load of the chunk is issued here, before the first
     // store: one round of latency, and no wait for a load also waits for
-    // earlier stores (loads and stores share one counter).  U, W, dU and dW'
-    // were parked in dq, dk, d log alpha and dv by the state sweeps.
+    // earlier stores (loads and stores share one counter).  W and dU were
+    // parked in dk and d log alpha by the state sweeps; U = T (B W) and
+    // dW' = T^T dU are formed again here from the T tile, on the same
+    // products the sweeps used.
     ChunkRaw<SEQ_NT, true>& raw = rq.raw;   // kept: the intra-chunk part stages its k and q
     request<SEQ_NT, true>(a, row0c, L, h, raw);
     rq.braw = beta_raw(a, row0c, L, h);
     const bf16_t& braw = rq.braw;
+    TileRaw<SEQ_NT> traw;   // T, rows 2p and 2p + 1: both images from one load
+    request_tile<true, SEQ_NT>(a.ws_apt + wslot * (3 * TSZ) + 2 * TSZ, traw);
     f32x4 U[4], dU[4], dW[4], W[4], dO[4];
     const int64_t e0 = (row0c * H + h) * kDim + col;
     {
@@ -1374,10 +1372,8 @@ __device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm, Intr
         const uint32_t prs = static_cast<uint32_t>(rs);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            U[m] = unpark4(a.dq + pb, prs, m, g, col, L);
             W[m] = unpark4(a.dk + pb, prs, m, g, col, L);
             dU[m] = unpark4(a.dla + pb, prs, m, g, col, L);
-            dW[m] = unpark4(a.dv + pb, prs, m, g, col, L);
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 const int r = 16 * m + 4 * g + x;
@@ -1404,12 +1400,25 @@ __device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm, Intr
     for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int x = 0; x < 4; ++x)
-            if (16 * m + 4 * g + x >= L) U[m][x] = W[m][x] = dU[m][x] = dW[m][x] = dO[m][x] = 0.f;
+            if (16 * m + 4 * g + x >= L) W[m][x] = dU[m][x] = dO[m][x] = 0.f;
 
-    // ---- staging: G and beta; k and q (bf16) into the image region, which
-    // is free until the phase B images
+    // ---- staging: G and beta; k and q (bf16) and the images of T and T^T
+    // into the image region, which is free until the phase B images
     __bf16* Kb = reinterpret_cast<__bf16*>(img + OFF_I2);
     __bf16* Qb = Kb + CH * kDim;
+    constexpr int T_PL = CH * CH * 2;
+    char* TIm = img + OFF_I0;            // T: rows r, k = i
+    char* TTm = img + OFF_I0 + 2 * T_PL; // T^T: rows i, k = r
+    tile_put<true, SEQ_NT>(traw, TTm);
+    {
+        // the same pieces as rows r = 2p, 2p + 1 of T, k = 4 (t mod 16) .. +3
+        const int r = 2 * (t >> 4), i = 4 * (t & 15);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            img_put2<true>(TIm, T_PL, r + j, i, 2, traw.x[j].x, traw.x[j].y);
+            img_put2<true>(TIm, T_PL, r + j, i + 2, 2, traw.x[j].z, traw.x[j].w);
+        }
+    }
     {
         Staged<SEQ_NT> st;
         stage_raw<SEQ_NT, true>(raw, tot, st);
@@ -1426,7 +1435,35 @@ __device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm, Intr
             gLs[st.c0 + 1] = st.gl[1];
         }
     }
-    lds_sync();   // G, beta, k and q
+    lds_sync();   // G, beta, k, q and the images of T
+    // U = T (B W) and dW' = T^T dU (sums over tokens, 2 steps each)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) U[m] = dW[m] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        f32x4 b0, b1;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            b0[x] = bs[16 * (2 * s) + 4 * g + x] * W[2 * s][x];
+            b1[x] = bs[16 * (2 * s + 1) + 4 * g + x] * W[2 * s + 1][x];
+        }
+        bf16x8 wh, wl, uh, ul;
+        bfrag(b0, b1, wh, wl);
+        bfrag(dU[2 * s], dU[2 * s + 1], uh, ul);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            bf16x8 ah, al;
+            img_frag(TIm, T_PL, m * 2 + s, lane, ah, al);
+            U[m] = mma3(ah, al, wh, wl, U[m]);
+            img_frag(TTm, T_PL, m * 2 + s, lane, ah, al);
+            dW[m] = mma3(ah, al, uh, ul, dW[m]);
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+            if (16 * m + 4 * g + x >= L) U[m][x] = dW[m][x] = 0.f;
     // queries and keys of this lane's rows and channel (read before the
     // barrier after which the images overwrite them)
     float qv[4][4], kv[4][4];
@@ -1454,8 +1491,7 @@ __device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm, Intr
             }
     }
     lds_sync();
-    // dv = B dW', stored only now: dv held parked dW' rows that other lanes
-    // read, and every wave has used all its parked values before this barrier
+    // dv = B dW'
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll

@@ -340,8 +340,8 @@ kda_status kda_varlen_prefill_slots(const void *q, const void *k, const void *v,
  *                 state, or NULL for zeros
  * Outputs, fp32, all written:
  *   dq, dk, dlog_alpha : the layout of q;  dv : the layout of v;  dbeta : the
- *                 layout of beta.  With bf16 inputs dq, dk, dv and dlog_alpha
- *                 also hold intermediate values of the call before their final
+ *                 layout of beta.  With bf16 inputs dk and dlog_alpha also
+ *                 hold intermediate values of the call before their final
  *                 ones, so no output may overlap an input or another output
  *                 (KDA_ERR_OVERLAP, checked on the host from the sizes)
  *   d_initial_state : [B or N, H, d_k, d_v], or NULL to skip; it MAY be the same
