@@ -1719,22 +1719,34 @@ __device__ __forceinline__ void grads_part(const ChunkBwdArgs& a, char* sm, Intr
 // them; everything else overlays the gradient part's dead regions.
 // k and q are kept channel-major (row stride KLD tokens), so that the rows a
 // lane reads for its channel are contiguous.
+// Phase 2 reads dP and dA as split-bf16 fragments formed once per workgroup
+// (4 per pair of blocks (R, I <= R): rows of dP, rows of dA, columns of dP,
+// columns of dA; 16 bytes per lane: high pair, low pair), the first NFR0 of
+// them where T and A were, the rest where the gradient part's row sums were;
+// the diagonal blocks also in fp32 (block stride DGB floats), and the cross
+// sums of the diagonal blocks (16 slots of INTRA_NT) where dA and dP were.
 constexpr int KLD = CH + 8;
+constexpr int NFR = 4 * 10;
+constexpr int NFR0 = 2 * CH * PLD * 4 / (64 * 16);
+constexpr int DGB = 16 * 16 + 16;   // (+16: the four blocks start on different banks)
 struct IntraLds {
-    float U1[2 * CH * PLD];   // T and A, then (phase 2) the diagonal blocks' cross sums
+    float U1[2 * CH * PLD];   // T and A, then (phase 2) fragments 0 .. NFR0 - 1
     __bf16 Ks[kDim * KLD];
     __bf16 Qs[kDim * KLD];
     float bs[CH], db2[CH];
-    char pad0[GR_DT_OFF - 2 * CH * PLD * 4 - 2 * kDim * KLD * 2 - 2 * CH * 4];
-    float Ad[CH * PLD];       // dT, Y, dM, then dA
+    float Dg[2][4 * DGB];     // (phase 2) the diagonal blocks of dP and dA
+    float Ad[CH * PLD];       // dT, Y, dM, dA, then (phase 2) cross sums, slots 0..7
     float Gs[CH * GLD];       // G (the gradient part's tile)
-    char pad1[offsetof(GradsLds, Pd) - offsetof(GradsLds, Gs) - CH * GLD * 4];
-    float Pd[CH * PLD];       // dP (i <= r)
+    uint4 Fr1[(NFR - NFR0) * 64];   // fragments NFR0 ..
+    char pad1[offsetof(GradsLds, Pd) - offsetof(GradsLds, Gs) - CH * GLD * 4 - (NFR - NFR0) * 64 * 16];
+    float Pd[CH * PLD];       // dP (i <= r), then (phase 2) cross sums, slots 8..15
 };
 static_assert(offsetof(IntraLds, Ad) == GR_DT_OFF, "dT where the gradient part wrote it");
 static_assert(offsetof(IntraLds, Gs) == offsetof(GradsLds, Gs), "G where the gradient part staged it");
 static_assert(offsetof(IntraLds, Pd) == offsetof(GradsLds, Pd), "dP where the gradient part wrote it");
-static_assert(16 * INTRA_NT * 4 <= 2 * CH * PLD * 4, "the cross sums fit where T and A were");
+static_assert(NFR0 * 64 * 16 == sizeof(IntraLds::U1), "whole fragments where T and A were");
+static_assert(8 * INTRA_NT <= CH * PLD, "eight slots of cross sums fit in each of dA and dP");
+static_assert(NFR % (INTRA_NT / 64) == 0, "the waves form the fragments in whole rounds");
 
 __device__ __forceinline__ void intra_part(const ChunkBwdArgs& a, char* sm, IntraReq& rq, const Partials& pp)
 {
@@ -1749,7 +1761,9 @@ __device__ __forceinline__ void intra_part(const ChunkBwdArgs& a, char* sm, Intr
     const float* Gs = S_.Gs;
     float* Ts = U1;
     float* As = U1 + CH * PLD;
-    float* DgS = U1;   // after phase 1
+    // phase 2: fragment f of the split dP and dA, and the cross sums' slot s
+    auto frag = [&](int f) { return f < NFR0 ? reinterpret_cast<uint4*>(U1) + 64 * f : S_.Fr1 + 64 * (f - NFR0); };
+    auto slot = [&](int s) { return s < 8 ? Ad + s * INTRA_NT : Pd + (s - 8) * INTRA_NT; };
 
     const int H = a.H;
     const int64_t id = blockIdx.x / H;
@@ -1871,7 +1885,41 @@ __device__ __forceinline__ void intra_part(const ChunkBwdArgs& a, char* sm, Intr
         const int r = e >> 6, i = e & 63;
         Ad[r * PLD + i] = i < r ? bs[r] * Ad[r * PLD + i] : 0.f;   // dA
     }
-    lds_sync();   // phase 1 is done with T and A: the cross sums take their place
+    lds_sync();
+    // ---- the operands of phase 2, split once for all waves (T and A are
+    // dead): wave w forms the fragments w, w + 8, ..; fragment 4 p + m of the
+    // p-th pair of blocks (R, I <= R) in the order (0,0), (1,0), (1,1), (2,0) ..
+    // holds, for lane (g, l16), m = 0, 1: dP, dA at row 16 R + l16, columns
+    // 16 I + 4 g ..; m = 2, 3: dP, dA at rows 16 R + 4 g .., column 16 I + l16
+#pragma unroll
+    for (int j = 0; j < NFR / (INTRA_NT / 64); ++j) {
+        const int f = wave + (INTRA_NT / 64) * j, p = f >> 2, m = f & 3;
+        const int R = p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3, I = p - R * (R + 1) / 2;
+        const float* src = (m & 1) ? Ad : Pd;
+        float v[4];
+        if (m < 2) {
+            const float4 w = *reinterpret_cast<const float4*>(&src[(16 * R + l16) * PLD + 16 * I + 4 * g]);
+            v[0] = w.x, v[1] = w.y, v[2] = w.z, v[3] = w.w;
+        } else {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) v[x] = src[(16 * R + 4 * g + x) * PLD + 16 * I + l16];
+        }
+        i16x4 hi, lo;
+        split4(v[0], v[1], v[2], v[3], hi, lo);
+        const uint2 h2 = __builtin_bit_cast(uint2, hi), l2 = __builtin_bit_cast(uint2, lo);
+        frag(f)[lane] = (uint4){h2.x, h2.y, l2.x, l2.y};
+    }
+    {
+        // the diagonal blocks in fp32: thread t takes 4 values of one row
+        static_assert(INTRA_NT == 2 * 4 * 16 * 4, "one float4 per thread");
+        const int m = t >> 8, R = (t >> 6) & 3, rl = (t >> 2) & 15, c4 = 4 * (t & 3);
+        const float* src = m ? Ad : Pd;
+        *reinterpret_cast<float4*>(&S_.Dg[m][R * DGB + 16 * rl + c4]) =
+            *reinterpret_cast<const float4*>(&src[(16 * R + rl) * PLD + 16 * R + c4]);
+    }
+    lds_sync();   // dP and dA are read: the cross sums take their place
+    const float* DgP = S_.Dg[0];
+    const float* DgA = S_.Dg[1];
 
     // ---- phase 2: wave w on channels cc = 16w + l16; rows 16R + 4g + x of each block R
     auto Gv = [&](int r) { return Gs[r * GLD + cc]; };
@@ -1885,7 +1933,7 @@ __device__ __forceinline__ void intra_part(const ChunkBwdArgs& a, char* sm, Intr
     // before J (rows in J), and the pairs inside J (explicit).  Every term
     // carries the decay over token j.  Row blocks run last to first, so that
     // a block's dk column sums, Bc and Ab are complete when it is written.
-    // The pairs inside each diagonal block first, into DgS: lane group g takes
+    // The pairs inside each diagonal block first, into the slots: lane group g takes
     // the diagonal block R = g of channel cc, all 16 of its rows (no lane
     // computes a pair above the diagonal, and no sum crosses lanes).  With
     // a_r = k_r 2^(G_r - rho), c_r = q_r 2^(G_r - rho), b_i = k_i 2^(rho - G_i),
@@ -1911,8 +1959,8 @@ __device__ __forceinline__ void intra_part(const ChunkBwdArgs& a, char* sm, Intr
             const float e = ex2(Gv(r) - rho);
             const float f = safe ? e : 0.f;
             const float ar = Kv(r) * f, cr = Qv(r) * f;
-            const float* da = &Ad[r * PLD + r0];
-            const float* dp = &Pd[r * PLD + r0];
+            const float* da = &DgA[R * DGB + 16 * rl];
+            const float* dp = &DgP[R * DGB + 16 * rl];
             float run = 0.f;
 #pragma unroll
             for (int il = 0; il < rl; ++il) {
@@ -1932,7 +1980,7 @@ __device__ __forceinline__ void intra_part(const ChunkBwdArgs& a, char* sm, Intr
                     for (int il = 0; il < 15; ++il) {
                         if (il < rl) {
                             const int i = r0 + il;
-                            run += (Ad[r * PLD + i] * kr + Pd[r * PLD + i] * qr) * Kv(i) * ex2(gr - Gv(i));
+                            run += (DgA[R * DGB + 16 * rl + il] * kr + DgP[R * DGB + 16 * rl + il] * qr) * Kv(i) * ex2(gr - Gv(i));
                             cs[il + 1] += run;
                         }
                     }
@@ -1940,9 +1988,10 @@ __device__ __forceinline__ void intra_part(const ChunkBwdArgs& a, char* sm, Intr
             }
         }
         // to the thread that finalises row j = 16 R + jl: lane group jl / 4, slot 4 R + jl mod 4
+        float* dgs = g < 2 ? Ad + 4 * g * INTRA_NT : Pd + (4 * g - 8) * INTRA_NT;   // slots 4 R ..
 #pragma unroll
         for (int jl = 0; jl < 16; ++jl)
-            DgS[(4 * R + (jl & 3)) * INTRA_NT + 64 * wave + 16 * (jl >> 2) + l16] = cs[jl];
+            dgs[(jl & 3) * INTRA_NT + 64 * wave + 16 * (jl >> 2) + l16] = cs[jl];
     }
     __builtin_amdgcn_sched_barrier(0);
     f32x4 dkc[4];
@@ -1986,24 +2035,21 @@ __device__ __forceinline__ void intra_part(const ChunkBwdArgs& a, char* sm, Intr
             split4(qf[0], qf[1], qf[2], qf[3], bqh, bql);
             split4(kf[0], kf[1], kf[2], kf[3], bfh, bfl);
             // row side: A = dP_RI, dA_RI (row l16 of block R, columns 4g.. of block I)
-            const float4 p4 = *reinterpret_cast<const float4*>(&Pd[(16 * R + l16) * PLD + 16 * I + 4 * g]);
-            const float4 a4 = *reinterpret_cast<const float4*>(&Ad[(16 * R + l16) * PLD + 16 * I + 4 * g]);
-            i16x4 aph, apl, aah, aal;
-            split4(p4.x, p4.y, p4.z, p4.w, aph, apl);
-            split4(a4.x, a4.y, a4.z, a4.w, aah, aal);
+            const int f0 = 4 * (R * (R + 1) / 2 + I);
+            const uint4 frp = frag(f0)[lane], fra = frag(f0 + 1)[lane];
+            const uint4 fcp = frag(f0 + 2)[lane], fca = frag(f0 + 3)[lane];
+            const i16x4 aph = __builtin_bit_cast(i16x4, (uint2){frp.x, frp.y});
+            const i16x4 apl = __builtin_bit_cast(i16x4, (uint2){frp.z, frp.w});
+            const i16x4 aah = __builtin_bit_cast(i16x4, (uint2){fra.x, fra.y});
+            const i16x4 aal = __builtin_bit_cast(i16x4, (uint2){fra.z, fra.w});
             const f32x4 z = {0.f, 0.f, 0.f, 0.f};
             const f32x4 sq = mma16(aph, apl, bkh, bkl, z);
             const f32x4 sk = mma16(aah, aal, bkh, bkl, z);
             // column side: A = dP_RI^T, dA_RI^T (row l16 of block I, columns 4g.. of block R)
-            float pc[4], ac[4];
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                pc[x] = Pd[(16 * R + 4 * g + x) * PLD + 16 * I + l16];
-                ac[x] = Ad[(16 * R + 4 * g + x) * PLD + 16 * I + l16];
-            }
-            i16x4 cph, cpl, cah, cal;
-            split4(pc[0], pc[1], pc[2], pc[3], cph, cpl);
-            split4(ac[0], ac[1], ac[2], ac[3], cah, cal);
+            const i16x4 cph = __builtin_bit_cast(i16x4, (uint2){fcp.x, fcp.y});
+            const i16x4 cpl = __builtin_bit_cast(i16x4, (uint2){fcp.z, fcp.w});
+            const i16x4 cah = __builtin_bit_cast(i16x4, (uint2){fca.x, fca.y});
+            const i16x4 cal = __builtin_bit_cast(i16x4, (uint2){fca.z, fca.w});
             f32x4 sc = mma16(cph, cpl, bqh, bql, z);
             sc = mma16(cah, cal, bfh, bfl, sc);
 #pragma unroll
@@ -2037,14 +2083,16 @@ __device__ __forceinline__ void intra_part(const ChunkBwdArgs& a, char* sm, Intr
                         for (int x = 0; x < 4; ++x) {
                             const int r = 16 * R + 4 * g + x;
                             float aq = 0.f, ak = 0.f, acc = 0.f;
+                            const int d = R * DGB, rl = 4 * g + x;   // the diagonal block, row rl
                             for (int i = 16 * R; i <= r; ++i) {
                                 const float kie = Kv(i) * ex2(gR[x] - Gv(i));
-                                aq += Pd[r * PLD + i] * kie;
-                                ak += Ad[r * PLD + i] * kie;
+                                aq += DgP[d + 16 * rl + i - 16 * R] * kie;
+                                ak += DgA[d + 16 * rl + i - 16 * R] * kie;
                             }
                             const float gi = gR[x];  // row r as the column index i
                             for (int rr = r; rr < 16 * R + 16; ++rr)
-                                acc += (Pd[rr * PLD + r] * Qv(rr) + Ad[rr * PLD + r] * Kv(rr)) * ex2(Gv(rr) - gi);
+                                acc += (DgP[d + 16 * (rr - 16 * R) + rl] * Qv(rr) + DgA[d + 16 * (rr - 16 * R) + rl] * Kv(rr)) *
+                                       ex2(Gv(rr) - gi);
                             dqR[x] += aq;
                             dkrR[x] += ak;
                             dkc[R][x] += acc;
@@ -2076,7 +2124,7 @@ __device__ __forceinline__ void intra_part(const ChunkBwdArgs& a, char* sm, Intr
         for (int x = 0; x < 4; ++x) {
             fq[x] = pp.q[R][x] + dqR[x];
             fk[x] = pp.k[R][x] + dkrR[x] + dkc[R][x];
-            fl[x] = pp.l[R][x] + Ab[R] + bp + cs[x] + DgS[(4 * R + x) * INTRA_NT + t];
+            fl[x] = pp.l[R][x] + Ab[R] + bp + cs[x] + slot(4 * R + x)[t];
             bp += Bc[R][x];
         }
 #pragma unroll
