@@ -1953,20 +1953,27 @@ __device__ __forceinline__ void intra_part(const ChunkBwdArgs& a, char* sm, Intr
             bcol[il] = safe ? b : 0.f;
             cs[il] = 0.f;
         }
+        // rows last to first: col[i] is the sum of dA_ri a_r + dP_ri c_r over
+        // the rows r >= rl taken so far, so that cs[rl] = sum_{i < rl} b_i col[i]
+        float colv[15];
 #pragma unroll
-        for (int rl = 1; rl < 16; ++rl) {
+        for (int il = 0; il < 15; ++il) colv[il] = 0.f;
+#pragma unroll
+        for (int rl = 15; rl >= 1; --rl) {
             const int r = r0 + rl;
             const float e = ex2(Gv(r) - rho);
             const float f = safe ? e : 0.f;
             const float ar = Kv(r) * f, cr = Qv(r) * f;
             const float* da = &DgA[R * DGB + 16 * rl];
             const float* dp = &DgP[R * DGB + 16 * rl];
-            float run = 0.f;
+            float acc = 0.f;
 #pragma unroll
             for (int il = 0; il < rl; ++il) {
-                run += (da[il] * ar + dp[il] * cr) * bcol[il];
-                cs[il + 1] += run;
+                colv[il] = fmaf(da[il], ar, colv[il]);
+                colv[il] = fmaf(dp[il], cr, colv[il]);
+                acc = fmaf(bcol[il], colv[il], acc);
             }
+            cs[rl] = acc;
             __builtin_amdgcn_sched_barrier(0);   // one row at a time: bounded register use
         }
         if (__any(!safe)) {
