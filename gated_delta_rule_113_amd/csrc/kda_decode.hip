@@ -29,7 +29,28 @@
 namespace kda {
 namespace {
 
-template <typename InT, bool RAW>
+// A state row piece of 4 floats.  STREAM: with the nontemporal hint, for
+// states that do not fit the last-level cache (then nothing is reused from it
+// by the next step, and the hint keeps the stream from evicting what is);
+// without it, a state that fits is read back from that cache at the next step.
+typedef float nt4 __attribute__((ext_vector_type(4)));
+template <bool STREAM>
+__device__ __forceinline__ float4 state_ld(const float* p)
+{
+    if (STREAM) {
+        const nt4 x = __builtin_nontemporal_load(reinterpret_cast<const nt4*>(p));
+        return make_float4(x[0], x[1], x[2], x[3]);
+    }
+    return *reinterpret_cast<const float4*>(p);
+}
+template <bool STREAM>
+__device__ __forceinline__ void state_st(float* p, float4 t)
+{
+    if (STREAM) __builtin_nontemporal_store((nt4){t.x, t.y, t.z, t.w}, reinterpret_cast<nt4*>(p));
+    else *reinterpret_cast<float4*>(p) = t;
+}
+
+template <typename InT, bool RAW, bool STREAM>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
     const InT* __restrict__ beta, const float* __restrict__ log_alpha,
@@ -70,8 +91,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     float bt = widen(beta[unit]);
     float4 s[16];
 #pragma unroll
-    for (int m = 0; m < 16; ++m)
-        s[m] = *reinterpret_cast<const float4*>(S + (row0 + m) * kDim + col);
+    for (int m = 0; m < 16; ++m) s[m] = state_ld<STREAM>(S + (row0 + m) * kDim + col);
 
     if (tid < kDim) {
         sa[tid] = RAW ? alpha_from_logit(x0) : exp_gate(x0);
@@ -132,7 +152,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     for (int m = 0; m < 16; ++m) {
         float4 t = s[m];
         t.x += kk[m] * u0; t.y += kk[m] * u1; t.z += kk[m] * u2; t.w += kk[m] * u3;
-        *reinterpret_cast<float4*>(S + (row0 + m) * kDim + col) = t;
+        state_st<STREAM>(S + (row0 + m) * kDim + col, t);
     }
 }
 
@@ -442,13 +462,22 @@ hipError_t launch_decode_step(const void* q, const void* k, const void* v, const
                            static_cast<const T*>(beta), log_alpha, state, slots, n_pool,
                            static_cast<int>(H), o);
     };
-    if (bf16) {
-        if (raw) go(decode_step_kernel<bf16_t, true>, bf16_t{});
-        else go(decode_step_kernel<bf16_t, false>, bf16_t{});
-    } else {
-        if (raw) go(decode_step_kernel<float, true>, 0.f);
-        else go(decode_step_kernel<float, false>, 0.f);
-    }
+    // the states this step reads and writes, against the 256 MB last-level
+    // cache: larger ones are streamed with the nontemporal hint
+    constexpr int64_t kDecodeStreamBytes = int64_t(256) << 20;
+    const bool stream_state = units * static_cast<int64_t>(kDim * kDim * sizeof(float)) > kDecodeStreamBytes;
+    auto pick = [&](auto str) {
+        constexpr bool ST = decltype(str)::value;
+        if (bf16) {
+            if (raw) go(decode_step_kernel<bf16_t, true, ST>, bf16_t{});
+            else go(decode_step_kernel<bf16_t, false, ST>, bf16_t{});
+        } else {
+            if (raw) go(decode_step_kernel<float, true, ST>, 0.f);
+            else go(decode_step_kernel<float, false, ST>, 0.f);
+        }
+    };
+    if (stream_state) pick(std::true_type{});
+    else pick(std::false_type{});
     return hipGetLastError();
 }
 

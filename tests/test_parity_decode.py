@@ -53,6 +53,18 @@ def test_decode_full_size_every_head():
     gc.finish()
 
 
+def test_decode_streamed_state_every_head():
+    """A batch whose states (136 sequences x 32 heads, 272 MiB) exceed the
+    256 MB last-level cache, which the step streams with the nontemporal
+    hint: two steps, every head's outputs and final state against the oracle."""
+    inp = ki.decode_steps(7, steps=2, N=136, H=32)
+    o, S = _run_chain(inp, device())
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(S))
+    q, k, v, b, la = inp.widened()
+    o_ref, S_ref = oracle.decode_chain(q, k, v, b, la, inp.initial_state)
+    check("decode streamed state, 136 x 32 heads", rel_err_vectors(o, o_ref), rel_err_states(S, S_ref))
+
+
 def test_decode_in_place_and_zero_beta():
     """beta = 0 and log_alpha = 0 leave the state bit-for-bit unchanged; the
     output is then S^T q."""
