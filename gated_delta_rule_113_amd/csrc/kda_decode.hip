@@ -43,6 +43,16 @@ __device__ __forceinline__ float4 state_ld(const float* p)
     }
     return *reinterpret_cast<const float4*>(p);
 }
+typedef float nt2 __attribute__((ext_vector_type(2)));
+template <bool STREAM>
+__device__ __forceinline__ float2 state_ld2(const float* p)
+{
+    if (STREAM) {
+        const nt2 x = __builtin_nontemporal_load(reinterpret_cast<const nt2*>(p));
+        return make_float2(x[0], x[1]);
+    }
+    return *reinterpret_cast<const float2*>(p);
+}
 template <bool STREAM>
 __device__ __forceinline__ void state_st(float* p, float4 t)
 {
@@ -179,7 +189,7 @@ __device__ __forceinline__ float wave_sum(float x)
 // n_commit at all, leaves it unchanged).  Every token's output is written.
 // The K tokens' gates, keys, queries and write strengths are staged in LDS
 // together before the state loads complete.
-template <typename InT, int KM>
+template <typename InT, int KM, bool STREAM>
 __global__ __launch_bounds__(256) void decode_tokens_kernel(
     const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
     const InT* __restrict__ beta, const float* __restrict__ log_alpha,
@@ -222,7 +232,7 @@ __global__ __launch_bounds__(256) void decode_tokens_kernel(
     float4 s[16];
 #pragma unroll
     for (int m = 0; m < 16; ++m)
-        s[m] = *reinterpret_cast<const float4*>(S + (row0 + m) * kDim + col);
+        s[m] = state_ld<STREAM>(S + (row0 + m) * kDim + col);
     auto vrow = [&](int t) { return v + rowvec(t) + col; };
     auto vraw = load4_raw(vrow(0));
     __builtin_amdgcn_sched_barrier(0);
@@ -247,7 +257,7 @@ __global__ __launch_bounds__(256) void decode_tokens_kernel(
         if (rg == 0) *reinterpret_cast<float4*>(o + rowvec(t) + col) = ot;
         if (t + 1 == commit) {
 #pragma unroll
-            for (int m = 0; m < 16; ++m) *reinterpret_cast<float4*>(S + (row0 + m) * kDim + col) = s[m];
+            for (int m = 0; m < 16; ++m) state_st<STREAM>(S + (row0 + m) * kDim + col, s[m]);
         }
     }
 }
@@ -270,7 +280,7 @@ __global__ __launch_bounds__(256) void decode_tokens_kernel(
 // K^2, so longer drafts and commits keep the token-by-token kernel above.  Lane mapping: wave w owns columns 32w..32w+31,
 // lane l the columns 32w + 2 (l & 15) .. +1 of the 32 rows 32 (l >> 4) .. +31
 // (one load instruction of a wave covers 4 rows x 128 contiguous bytes).
-template <typename InT>
+template <typename InT, bool STREAM>
 __global__ __launch_bounds__(256, 8) void decode_verify4_kernel(
     const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
     const InT* __restrict__ beta, const float* __restrict__ log_alpha,
@@ -310,7 +320,7 @@ __global__ __launch_bounds__(256, 8) void decode_verify4_kernel(
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) blk[b][i] = *reinterpret_cast<const float2*>(S + (r0 + 4 * b + i) * kDim);
+        for (int i = 0; i < 4; ++i) blk[b][i] = state_ld2<STREAM>(S + (r0 + 4 * b + i) * kDim);
     __builtin_amdgcn_sched_barrier(0);
 
     // per channel e: G, the decayed keys and queries (first half), the pairs'
@@ -375,7 +385,7 @@ __global__ __launch_bounds__(256, 8) void decode_verify4_kernel(
         }
         if (b + 2 < NB) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) cur[i] = *reinterpret_cast<const float2*>(S + (r0 + 4 * (b + 2) + i) * kDim);
+            for (int i = 0; i < 4; ++i) cur[i] = state_ld2<STREAM>(S + (r0 + 4 * (b + 2) + i) * kDim);
         }
     }
     // sums over the four row quarters (lanes l, l ^ 16, l ^ 32, l ^ 48)
@@ -414,6 +424,14 @@ __global__ __launch_bounds__(256, 8) void decode_verify4_kernel(
 
 }  // namespace
 
+// Whether a call's states (64 KiB per head) exceed the 256 MB last-level
+// cache: then its kernels stream them with the nontemporal hint.
+static bool streams_state(int64_t units)
+{
+    constexpr int64_t kStreamBytes = int64_t(256) << 20;
+    return units * static_cast<int64_t>(kDim * kDim * sizeof(float)) > kStreamBytes;
+}
+
 hipError_t launch_decode_tokens(const void* q, const void* k, const void* v, const void* beta,
                                 const float* log_alpha, float* state, const int32_t* n_commit,
                                 float* o, int64_t N, int64_t K, int64_t H, bool bf16,
@@ -423,28 +441,31 @@ hipError_t launch_decode_tokens(const void* q, const void* k, const void* v, con
     if (units <= 0 || K <= 0) return hipSuccess;
     if (K > kMaxDraft) return hipErrorInvalidValue;
     const dim3 grid(static_cast<unsigned>(units)), block(256);
-    auto go = [&](auto km, auto tag) {
+    auto go = [&](auto km, auto tag, auto str) {
         using T = decltype(tag);
         constexpr int KMV = decltype(km)::value;
-        hipLaunchKernelGGL((decode_tokens_kernel<T, KMV>), grid, block, 0, stream,
+        constexpr bool ST = decltype(str)::value;
+        hipLaunchKernelGGL((decode_tokens_kernel<T, KMV, ST>), grid, block, 0, stream,
                            static_cast<const T*>(q), static_cast<const T*>(k),
                            static_cast<const T*>(v), static_cast<const T*>(beta), log_alpha,
                            state, n_commit, static_cast<int>(K), static_cast<int>(H), o);
     };
-    auto verify4 = [&](auto tag) {
+    auto verify4 = [&](auto tag, auto str) {
         using T = decltype(tag);
-        hipLaunchKernelGGL(decode_verify4_kernel<T>, grid, block, 0, stream, static_cast<const T*>(q),
+        constexpr bool ST = decltype(str)::value;
+        hipLaunchKernelGGL((decode_verify4_kernel<T, ST>), grid, block, 0, stream, static_cast<const T*>(q),
                            static_cast<const T*>(k), static_cast<const T*>(v), static_cast<const T*>(beta),
                            log_alpha, state, static_cast<int>(K), static_cast<int>(H), o);
     };
-    auto pick = [&](auto tag) {
-        if (K <= 4 && !n_commit) verify4(tag);
-        else if (K <= 4) go(std::integral_constant<int, 4>{}, tag);
-        else if (K <= 8) go(std::integral_constant<int, 8>{}, tag);
-        else go(std::integral_constant<int, 16>{}, tag);
+    auto pick = [&](auto tag, auto str) {
+        if (K <= 4 && !n_commit) verify4(tag, str);
+        else if (K <= 4) go(std::integral_constant<int, 4>{}, tag, str);
+        else if (K <= 8) go(std::integral_constant<int, 8>{}, tag, str);
+        else go(std::integral_constant<int, 16>{}, tag, str);
     };
-    if (bf16) pick(bf16_t{});
-    else pick(0.f);
+    const bool st = streams_state(units);
+    if (bf16) st ? pick(bf16_t{}, std::true_type{}) : pick(bf16_t{}, std::false_type{});
+    else st ? pick(0.f, std::true_type{}) : pick(0.f, std::false_type{});
     return hipGetLastError();
 }
 
@@ -462,10 +483,6 @@ hipError_t launch_decode_step(const void* q, const void* k, const void* v, const
                            static_cast<const T*>(beta), log_alpha, state, slots, n_pool,
                            static_cast<int>(H), o);
     };
-    // the states this step reads and writes, against the 256 MB last-level
-    // cache: larger ones are streamed with the nontemporal hint
-    constexpr int64_t kDecodeStreamBytes = int64_t(256) << 20;
-    const bool stream_state = units * static_cast<int64_t>(kDim * kDim * sizeof(float)) > kDecodeStreamBytes;
     auto pick = [&](auto str) {
         constexpr bool ST = decltype(str)::value;
         if (bf16) {
@@ -476,7 +493,7 @@ hipError_t launch_decode_step(const void* q, const void* k, const void* v, const
             else go(decode_step_kernel<float, false, ST>, 0.f);
         }
     };
-    if (stream_state) pick(std::true_type{});
+    if (streams_state(units)) pick(std::true_type{});
     else pick(std::false_type{});
     return hipGetLastError();
 }

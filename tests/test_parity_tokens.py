@@ -118,3 +118,30 @@ def test_tokens_match_single_steps_full_size():
     o_ref, S_ref = _oracle(sub, N, K, np.full(N, K))
     check("decode tokens full size, heads 0 and 31", rel_err_vectors(o[:, :, heads], o_ref),
           rel_err_states(S[:, heads], S_ref))
+
+
+@pytest.mark.parametrize("K", [4, 6])
+def test_tokens_streamed_state_every_head(K):
+    """A batch whose states (136 sequences x 32 heads, 272 MiB) exceed the
+    256 MB last-level cache, which the kernels stream with the nontemporal
+    hint: verify (K = 4 takes the streaming verify kernel), then commit of
+    per-sequence prefixes of 0..K tokens; every head against the oracle."""
+    torch = _torch()
+    dev = device()
+    N, H = 136, 32
+    inp, arrs = _inputs(33, N, K, H, "bf16")
+    t = _upload(arrs, "bf16", dev)
+    s0 = to_dev(inp.initial_state, "f32", dev)
+    state = s0.clone()
+    o = kda.kda_decode_tokens(t["q"], t["k"], t["v"], t["beta"], t["log_alpha"], state)
+    torch.cuda.synchronize()
+    assert torch.equal(state, s0)
+    del s0
+    accepted = (np.arange(N) % (K + 1)).astype(np.int32)
+    o2 = kda.kda_decode_tokens(t["q"], t["k"], t["v"], t["beta"], t["log_alpha"], state,
+                               torch.from_numpy(accepted).to(dev))
+    torch.cuda.synchronize()
+    o, o2, S = o.cpu().numpy(), o2.cpu().numpy(), state.cpu().numpy()
+    o_ref, S_ref = _oracle(inp, N, K, accepted)
+    check(f"decode tokens streamed state K={K}, verify", rel_err_vectors(o, o_ref), rel_err_states(S, S_ref))
+    check(f"decode tokens streamed state K={K}, commit", rel_err_vectors(o2, o_ref), rel_err_states(S, S_ref))
